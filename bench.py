@@ -1,0 +1,230 @@
+#!/usr/bin/env python
+"""LoopVQ hot-path benchmark on one MI355X.
+
+One step = the whole hot path over one batch of synthetic, HBM-resident input:
+encode the layer's K cache, encode its V cache (loop-axis VQ, nearest
+codeword), then one fused decode-attention call that serves every loop step
+of every block.  The default workload is the 0.5-bit looped-model slice
+(B=32, 16 kv-heads / 16 q-heads, D=128, T=T_c=4, G=16, K=256, 8192 context
+tokens + 4 bf16 sinks).
+
+Prints one JSON line.  `value` is whole-step throughput in context tokens per
+second per loop block (B * N * n_blk / step time); per-kernel rates, the
+roofline of the dominant kernel (and of the decode kernel) and the CPU
+oracle's rate on a bounded sample are attached.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "decode-attn context tokens/s per loop block + % HBM peak; encode codes/s"
+UNIT = "context tokens/s per loop block"
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("encode.hip", "decode.hip", "common.h", "kernels.h"):
+        with open(os.path.join(ROOT, "sub_bit_loop_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel, workload):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel sources; else None."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        d = json.load(f)
+    if d.get("source_hash") != kernel_source_hash():
+        return None
+    e = d.get("kernels", {}).get(kernel)
+    if not e or e.get("workload") != workload:
+        return None
+    return e.get("bytes_per_launch")
+
+
+# ----------------------------------------------------------------------------- CPU oracle leg
+
+def _oracle_head(args):
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    import oracle as ref
+    kx, vx, kc, vc, sk, sv, qs, T_c, theta = args
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        ki, _ = ref.encode(kx, kc, T_c)
+        vi, _ = ref.encode(vx, vc, T_c)
+        for t in range(qs.shape[0]):
+            ref.decode_attn_row(qs[t], t, ki, vi, kc, vc, sk, sv, T_c, theta)
+        return time.perf_counter() - t0, ki.size + vi.size
+
+
+def cpu_baseline(cfg, inp, n_tok):
+    """Oracle on batch entry 0, every kv-head, the first n_tok context tokens:
+    K and V encode plus decode of every loop step over those tokens."""
+    from concurrent.futures import ProcessPoolExecutor
+    import multiprocessing as mp
+    import torch
+    f = lambda t: t.float().cpu().double().numpy()
+    jobs = []
+    for h in range(cfg.H_kv):
+        hq = h * (cfg.H_q // cfg.H_kv)
+        jobs.append((f(inp["k"][0, h, :, :n_tok]), f(inp["v"][0, h, :, :n_tok]), f(inp["k_cb"][h]),
+                     f(inp["v_cb"][h]), f(inp["sink_k"][0, h]), f(inp["sink_v"][0, h]),
+                     f(inp["q"][0, hq]), cfg.T_c, cfg.theta))
+    cores = len(os.sched_getaffinity(0))
+    workers = max(1, min(cores, len(jobs), 16))
+    t0 = time.perf_counter()
+    with ProcessPoolExecutor(max_workers=workers, mp_context=mp.get_context("spawn")) as ex:
+        res = list(ex.map(_oracle_head, jobs))
+    wall = time.perf_counter() - t0
+    codes = sum(r[1] for r in res)
+    # GQA heads beyond the first of each group are not re-run: count them as served
+    # only when the group size is 1 (the default workload).
+    tokens_blocks = n_tok * cfg.n_blk
+    return {
+        "value": tokens_blocks / wall,
+        "unit": UNIT,
+        "cores": workers,
+        "kind": "oracle",
+        "sample": "batch entry 0, all %d kv-heads, first %d context tokens: fp64 NumPy encode of K and V "
+                  "(%d codes) + decode attention of every loop step over those tokens and the %d sinks; "
+                  "one process per kv-head, %d processes, 1 BLAS thread each; wall %.1f s"
+                  % (cfg.H_kv, n_tok, codes, cfg.n_s, workers, wall),
+        "encode_codes_per_s": codes / wall,
+    }
+
+
+# ----------------------------------------------------------------------------- GPU leg
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=2, help="workload index 1-4 (single layer)")
+    ap.add_argument("--cpu-tokens", type=int, default=1024, help="context tokens in the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the LoopVQ path has no multi-GPU step in this build "
+              "(decode shards over batch x kv-heads with no communication); run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import sub_bit_loop_amd as lv
+    from synth import config_by_index
+    from tests.helpers import build_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    lv.lib()
+    cfg = config_by_index(args.config)
+    if cfg.layers != 1:
+        print("bench.py times single-layer workloads (1-4)", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    t_gen = time.time()
+    inp = build_inputs(cfg, 0, "cuda")
+    torch.cuda.synchronize()
+    t_gen = time.time() - t_gen
+    g = lv.geom(cfg.D, cfg.T, cfg.T_c, cfg.G, cfg.K, cfg.H_kv, cfg.H_q, cfg.theta)
+    shp = (cfg.B, cfg.H_kv, cfg.n_blk, cfg.N, cfg.chunks)
+    kidx = torch.empty(shp, dtype=torch.uint8, device="cuda")
+    vidx = torch.empty(shp, dtype=torch.uint8, device="cuda")
+    rope = lv.rope_table(cfg.n_s + cfg.N, cfg.D, cfg.theta)
+    out = torch.empty((cfg.B, cfg.H_q, cfg.T, cfg.D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((cfg.B, cfg.H_q, cfg.T), dtype=torch.float32, device="cuda")
+    ws = torch.empty(lv.decode_workspace_bytes(g, cfg.B, cfg.N, 0, cfg.T), dtype=torch.uint8, device="cuda")
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        lv.encode(g, inp["k"], inp["k_cb"], kidx)
+        if ev is not None:
+            ev[1].record()
+        lv.encode(g, inp["v"], inp["v_cb"], vidx)
+        if ev is not None:
+            ev[2].record()
+        lv.decode_attn(g, inp["q"], kidx, vidx, inp["k_cb"], inp["v_cb"], inp["sink_k"], inp["sink_v"], rope,
+                       out=out, lse=lse, workspace=ws)
+        if ev is not None:
+            ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(args.steps):
+        step(evs[i])
+    t1.record()
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    ms_step = total_ms / args.steps
+    enc_ms = sum(e[0].elapsed_time(e[1]) + e[1].elapsed_time(e[2]) for e in evs) / (2 * args.steps)
+    dec_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
+
+    units = cfg.B * cfg.H_kv * cfg.N * cfg.n_blk                  # decode units per call
+    codes_per_call = cfg.B * cfg.H_kv * cfg.n_blk * cfg.N * cfg.chunks
+    idx_bytes = 2 * cfg.chunks                                     # K + V index bytes per unit
+    dec_bytes = units * idx_bytes
+    enc_bytes = codes_per_call * (2 * cfg.G + 1)                   # bf16 joint vector in, 1 byte out
+    dec_gbs = dec_bytes / (dec_ms * 1e-3) / 1e9
+    enc_gbs = enc_bytes / (enc_ms * 1e-3) / 1e9
+    workload = ("config %d (%s): B=%d, %d kv-heads / %d q-heads, D=%d, T=%d, T_c=%d, G=%d, K=%d, N=%d + %d sinks"
+                % (cfg.index, cfg.name, cfg.B, cfg.H_kv, cfg.H_q, cfg.D, cfg.T, cfg.T_c, cfg.G, cfg.K, cfg.N, cfg.n_s))
+    roof_dec = {"kernel": "loopvq decode_attn call (decode_kernel + merge_kernel)", "bound": "hbm",
+                "achieved": dec_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dec_gbs / HBM_PEAK_GBS,
+                "traffic": load_traffic("decode", workload),
+                "algorithmic_bytes_per_launch": dec_bytes, "avg_launch_ms": dec_ms}
+    roof_enc = {"kernel": "loopvq encode call (encode_kernel)", "bound": "hbm",
+                "achieved": enc_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": enc_gbs / HBM_PEAK_GBS,
+                "traffic": load_traffic("encode", workload),
+                "algorithmic_bytes_per_launch": enc_bytes, "avg_launch_ms": enc_ms,
+                "mfma_tflops": 2.0 * cfg.K * cfg.G * codes_per_call / (enc_ms * 1e-3) / 1e12,
+                "mfma_frac_of_bf16_peak": 2.0 * cfg.K * cfg.G * codes_per_call / (enc_ms * 1e-3) / 2.5e15}
+    dominant = roof_enc if 2 * enc_ms >= dec_ms else roof_dec
+    res = {
+        "metric": METRIC,
+        "value": cfg.B * cfg.N * cfg.n_blk / (ms_step * 1e-3),
+        "unit": UNIT,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": workload, "global_batch": cfg.B, "seq_len": cfg.N + cfg.n_s,
+                   "step": "encode K + encode V + decode attention of all %d loop steps" % cfg.T},
+        "decode": {"ms_per_call": dec_ms, "context_tokens_per_s_per_block": cfg.B * cfg.N * cfg.n_blk / (dec_ms * 1e-3),
+                   "units_per_s": units / (dec_ms * 1e-3), "index_GBps": dec_gbs,
+                   "hbm_frac_index_bytes": dec_gbs / HBM_PEAK_GBS},
+        "encode": {"ms_per_call": enc_ms, "codes_per_s": codes_per_call / (enc_ms * 1e-3), "GBps": enc_gbs},
+        "roofline": dominant,
+        "roofline_decode": roof_dec,
+        "input_generation_s": t_gen,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(cfg, inp, min(args.cpu_tokens, cfg.N))
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,177 @@
+/*
+ * loopvq.h -- C ABI of the LoopVQ hot path on MI355X (gfx950).
+ *
+ * LoopVQ (review of arXiv 2611.05304 on jaehun.me, "paper-2611-05304v1") stores
+ * a looped transformer's per-step KV cache as one b-bit code per joint vector
+ * that spans c = G/T_c channels at each of T_c consecutive loop steps
+ * (section 3.1, eq. 4/5).  Two calls mirror the two things a user of the method
+ * does (section 3.4): encode a block of per-step K or V into index rows, and
+ * run decode attention over the index rows with codebooks resident on chip.
+ *
+ * Conventions shared by every entry point
+ *   - Pointers named "device" point to GPU memory of the current HIP device;
+ *     the geometry / pre-transform structs are host memory, read during the
+ *     call only.  The caller owns every buffer; the library allocates no device
+ *     memory in these calls (decode scratch comes from the caller's workspace).
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls are
+ *     stream-ordered and asynchronous; they never synchronize.  Faults raised
+ *     while kernels run surface at the caller's next synchronization.
+ *   - All argument checks happen on the host before any HIP call.  A failed
+ *     check returns LOOPVQ_EINVAL (bad value) or LOOPVQ_ENOTSUP (legal but not
+ *     built, e.g. D != 128); a failed launch returns LOOPVQ_EHIP.  The message
+ *     is available from loopvq_last_error() (thread-local).  No C++ exception
+ *     crosses this boundary.
+ *   - bf16 and fp16 tensors are passed as raw 16-bit storage.
+ *   - Multi-dimensional buffers are dense, row-major, in the order given.
+ */
+#ifndef LOOPVQ_H
+#define LOOPVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LOOPVQ_ABI_VERSION 1
+
+typedef enum {
+  LOOPVQ_OK = 0,
+  LOOPVQ_EINVAL = -1,
+  LOOPVQ_ENOTSUP = -2,
+  LOOPVQ_EHIP = -3,
+  LOOPVQ_EWORKSPACE = -4
+} loopvq_status;
+
+/* Geometry of one attention layer (section 3.1 notation).
+ *   D          head dim (even; this build supports D = 128)
+ *   T          loop steps; T_c steps per block, T % T_c == 0, n_blk = T / T_c
+ *   G          joint-vector length, G % T_c == 0, c = G / T_c, D % c == 0;
+ *              this build supports G in {16, 32} with D/2 % c == 0
+ *   K          codebook entries, 2 <= K <= 256 (one uint8 index per code)
+ *   n_kv_heads, n_q_heads   n_q_heads % n_kv_heads == 0; q-head hq reads
+ *              kv-head hq / (n_q_heads / n_kv_heads)
+ *   rope_theta RoPE base (rotate-half pairs (d, d + D/2), angle
+ *              pos * theta^(-2d/D)) */
+typedef struct {
+  int32_t D, T, T_c, G, K, n_kv_heads, n_q_heads;
+  float rope_theta;
+} loopvq_geom;
+
+/* Channel pre-transform for keys (section 3.3, appendix B eq. 10).
+ *   w      device fp32 [n_kv_heads][D], every entry > 0
+ *   perm   device int16 [n_kv_heads][D], a permutation of 0..D-1 per head;
+ *          transformed channel d' holds raw channel perm[d']
+ *   sigma  device fp16 [B][N_cap][T]: per-(token, step) RMS of the layer's raw
+ *          pre-RoPE key over all n_kv_heads * D channels, rounded to fp16
+ *          (round to nearest even).  loopvq_encode writes it for the tokens it
+ *          encodes; loopvq_decode_attn reads it.
+ *   N_cap  token capacity of sigma
+ * The transformed key is z[d'] = (w[perm[d']] * k[perm[d']]) / sigma. */
+typedef struct {
+  const float* w;
+  const int16_t* perm;
+  uint16_t* sigma;
+  int32_t N_cap;
+} loopvq_pretransform;
+
+/* loopvq_encode -- nearest-codeword encode of loop-axis joint vectors
+ * (section "terms" eq. 2 with the joint vector of section 3.1 eq. 4).
+ *
+ * For every batch b < B, kv-head h, block beta < n_blk, token j < N and chunk
+ * q < D/c, the joint vector is z[i*T_c + m] = x[b][h][beta*T_c + m][j][q*c + i]
+ * (i < c, m < T_c), or its pre-transformed value when pt != NULL, and
+ *   idx[b][h][beta][tok0 + j][q] = argmin_r ||z - e_r||^2
+ * over the entries e_r = codebook[h][beta][r][0..G) (lowest r on exact ties).
+ * Distances are screened with bf16 MFMA tiles and every code whose best two
+ * candidates lie within the screening error bound is re-scored in fp64, so the
+ * result equals the exact argmin.
+ *
+ *   g          geometry (host)
+ *   x          device bf16, element (b, h, t, j, d) at
+ *              b*xs[0] + h*xs[1] + t*xs[2] + j*xs[3] + d   (xs = x_strides,
+ *              in elements; each row of D channels is contiguous)
+ *   codebook   device bf16 [n_kv_heads][n_blk][K][G], coordinate i*T_c + m
+ *   B, N, tok0 batch size, tokens to encode, first destination token
+ *   idx        device uint8 [B][n_kv_heads][n_blk][N_cap][D/c]
+ *   N_cap      token capacity of idx, tok0 + N <= N_cap
+ *   pt         NULL for values and plain keys; for pre-transformed keys also
+ *              writes pt->sigma[b][tok0 + j][t] for every step t < T
+ * Errors: EINVAL for NULL pointers, bad geometry, N < 0, tok0 < 0,
+ * tok0 + N > N_cap (or > pt->N_cap), non-positive strides; ENOTSUP for D != 128
+ * or G not in {16, 32}.  N == 0 is a no-op returning LOOPVQ_OK. */
+loopvq_status loopvq_encode(const loopvq_geom* g, const void* x, const int64_t x_strides[4],
+                            const void* codebook, int32_t B, int32_t N, int32_t tok0,
+                            uint8_t* idx, int32_t N_cap, const loopvq_pretransform* pt,
+                            void* stream);
+
+/* loopvq_rope_table -- the per-position sin/cos table the decode kernel reads
+ * (section 3.4, step 3).  table[p][d] = (cos(phi), sin(phi)) with
+ * phi = p * theta^(-2d/D) evaluated in fp64 on the GPU and rounded to fp32.
+ *   table   device fp32 [n_pos][D/2][2]
+ * Errors: EINVAL for NULL table, n_pos < 1, odd D or D < 2, theta <= 0. */
+loopvq_status loopvq_rope_table(float theta, int32_t D, int32_t n_pos, float* table,
+                                void* stream);
+
+/* loopvq_decode_attn_workspace -- bytes of scratch loopvq_decode_attn needs
+ * for this shape (split-context partials).  Same argument rules as
+ * loopvq_decode_attn; *bytes may be 0. */
+loopvq_status loopvq_decode_attn_workspace(const loopvq_geom* g, int32_t B, int32_t N,
+                                           int32_t step0, int32_t n_steps, size_t* bytes);
+
+/* loopvq_decode_attn -- fused decode attention over the compressed cache
+ * (section 3.4 step 3; RoPE after dequant, section 3.1).
+ *
+ * For every batch b, q-head hq and loop step t in [step0, step0 + n_steps):
+ * with kv-head h = hq / (n_q_heads / n_kv_heads), block beta = t / T_c and
+ * m = t % T_c, the keys are the n_s bf16 sinks sink_k[b][h][t][s] at position
+ * s and the dequantized tokens j < N_b, whose channel q*c + i is
+ * k_cb[h][beta][k_idx[b][h][beta][j][q]][i*T_c + m] (inverse pre-transform
+ * applied when pt != NULL), at position n_s + j; every key is rotated (RoPE)
+ * at its position; values likewise from v_idx / v_cb / sink_v (no RoPE).
+ * The result is softmax attention with scale 1/sqrt(D):
+ *   out[b][hq][t - step0][0..D)  (fp32)
+ *   lse[b][hq][t - step0]        (fp32, natural log-sum-exp of the scaled
+ *                                 scores; may be NULL)
+ * so a caller can merge it with attention over other keys (Flash-Decoding
+ * log-sum-exp combine).  Each index row is decoded once for every step of its
+ * block that lies in the requested range.
+ *
+ *   q          device bf16 [B][n_q_heads][n_steps][D], already rotated
+ *   k_idx, v_idx  device uint8 [B][n_kv_heads][n_blk][N_cap][D/c]
+ *   k_cb, v_cb device bf16 [n_kv_heads][n_blk][K][G]
+ *   sink_k, sink_v  device bf16 [B][n_kv_heads][T][n_s][D], pre-RoPE; may be
+ *              NULL when n_s == 0
+ *   N          quantized tokens in the cache (N <= N_cap)
+ *   seq_len    device int32 [B] or NULL; batch b attends min(seq_len[b], N)
+ *              quantized tokens (negative values count as 0)
+ *   pt         keys' pre-transform (reads w, perm, sigma) or NULL
+ *   rope_table device fp32 [n_pos][D/2][2] from loopvq_rope_table, with
+ *              n_pos >= n_s + N
+ *   workspace  device scratch of at least loopvq_decode_attn_workspace() bytes
+ * A row with no keys at all (n_s == 0 and N_b == 0) yields out = 0 and
+ * lse = -inf.
+ * Errors: EINVAL for NULL pointers, bad geometry, step range outside [0, T),
+ * N > N_cap, n_pos too small; EWORKSPACE for a short workspace; ENOTSUP as for
+ * loopvq_encode. */
+loopvq_status loopvq_decode_attn(const loopvq_geom* g, const void* q, int32_t step0,
+                                 int32_t n_steps, const uint8_t* k_idx, const uint8_t* v_idx,
+                                 int32_t N_cap, const void* k_cb, const void* v_cb,
+                                 const void* sink_k, const void* sink_v, int32_t n_s,
+                                 int32_t B, int32_t N, const int32_t* seq_len,
+                                 const loopvq_pretransform* pt, const float* rope_table,
+                                 int32_t n_pos, float* out, float* lse, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/* Thread-local text of the last non-OK status ("" if none). */
+const char* loopvq_last_error(void);
+
+/* LOOPVQ_ABI_VERSION of the built library. */
+int32_t loopvq_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LOOPVQ_H */

@@ -1,0 +1,8 @@
+"""LoopVQ hot path on MI355X: loop-axis VQ encode and fused decode attention.
+
+The compute lives in libloopvq.so (hand-written HIP for gfx950) behind a C ABI
+(include/loopvq.h); this package only marshals torch tensors into it.
+"""
+from ._lib import LoopVQError, lib  # noqa: F401
+from .api import (decode_attn, decode_workspace_bytes, encode, geom,  # noqa: F401
+                  pretransform, rope_table)

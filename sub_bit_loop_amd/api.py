@@ -1,0 +1,114 @@
+"""Thin torch-facing binding of the LoopVQ C ABI (argument marshalling only).
+
+Every tensor must already live on the current HIP device with the documented
+dtype and layout; the calls are enqueued on torch's current stream.
+"""
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import Geom, PreTransform, check
+
+
+def geom(D, T, T_c, G, K, n_kv_heads, n_q_heads, rope_theta=1.0e4) -> Geom:
+    return Geom(D, T, T_c, G, K, n_kv_heads, n_q_heads, rope_theta)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _need(t, dtype, name):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s (got %s)" % (name, dtype, t.dtype))
+    if t.device.type != "cuda":
+        raise ValueError("%s must be a device tensor" % name)
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def pretransform(w, perm, sigma):
+    """Keys' channel pre-transform: w fp32 [H][D], perm int16 [H][D], sigma fp16 [B][N_cap][T]."""
+    _need(w, torch.float32, "w")
+    _need(perm, torch.int16, "perm")
+    _need(sigma, torch.float16, "sigma")
+    pt = PreTransform(w.data_ptr(), perm.data_ptr(), sigma.data_ptr(), sigma.shape[1])
+    pt._keep = (w, perm, sigma)
+    return pt
+
+
+def encode(g: Geom, x, codebook, idx, tok0=0, pt=None, stream=None):
+    """x bf16 [B][H][T][N][D] (any strides with D contiguous), codebook bf16
+    [H][n_blk][K][G], idx uint8 [B][H][n_blk][N_cap][D/c] (written)."""
+    _need(x, torch.bfloat16, "x")
+    _need(codebook, torch.bfloat16, "codebook")
+    _need(idx, torch.uint8, "idx")
+    if x.dim() != 5 or x.stride(4) != 1:
+        raise ValueError("x must be [B][H][T][N][D] with contiguous rows")
+    if not codebook.is_contiguous() or not idx.is_contiguous():
+        raise ValueError("codebook and idx must be contiguous")
+    B, _, _, N, _ = x.shape
+    strides = (ctypes.c_int64 * 4)(*[x.stride(i) for i in range(4)])
+    st = _lib.lib().loopvq_encode(ctypes.byref(g), _ptr(x), strides, _ptr(codebook), B, N, tok0,
+                                  _ptr(idx), idx.shape[3], ctypes.byref(pt) if pt is not None else None,
+                                  _stream(stream))
+    check(st)
+    return idx
+
+
+def rope_table(n_pos, D=128, theta=1.0e4, device="cuda", stream=None):
+    t = torch.empty((n_pos, D // 2, 2), dtype=torch.float32, device=device)
+    check(_lib.lib().loopvq_rope_table(theta, D, n_pos, _ptr(t), _stream(stream)))
+    return t
+
+
+def decode_workspace_bytes(g: Geom, B, N, step0, n_steps):
+    out = ctypes.c_size_t(0)
+    check(_lib.lib().loopvq_decode_attn_workspace(ctypes.byref(g), B, N, step0, n_steps, ctypes.byref(out)))
+    return out.value
+
+
+def decode_attn(g: Geom, q, k_idx, v_idx, k_cb, v_cb, sink_k, sink_v, rope, N=None, step0=0,
+                seq_len=None, pt=None, out=None, lse=None, workspace=None, stream=None):
+    """q bf16 [B][Hq][n_steps][D] (post-RoPE); k_idx/v_idx uint8 [B][H][n_blk][N_cap][D/c];
+    k_cb/v_cb bf16 [H][n_blk][K][G]; sinks bf16 [B][H][T][n_s][D] or None;
+    rope fp32 [n_pos][D/2][2].  Returns (out fp32 [B][Hq][n_steps][D], lse fp32 [B][Hq][n_steps])."""
+    _need(q, torch.bfloat16, "q")
+    _need(k_idx, torch.uint8, "k_idx")
+    _need(v_idx, torch.uint8, "v_idx")
+    _need(k_cb, torch.bfloat16, "k_cb")
+    _need(v_cb, torch.bfloat16, "v_cb")
+    _need(rope, torch.float32, "rope")
+    for t, n in ((q, "q"), (k_idx, "k_idx"), (v_idx, "v_idx"), (k_cb, "k_cb"), (v_cb, "v_cb"), (rope, "rope")):
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % n)
+    B, Hq, n_steps, D = q.shape
+    N_cap = k_idx.shape[3]
+    N = N_cap if N is None else N
+    n_s = 0
+    if sink_k is not None:
+        _need(sink_k, torch.bfloat16, "sink_k")
+        _need(sink_v, torch.bfloat16, "sink_v")
+        n_s = sink_k.shape[3]
+    if seq_len is not None:
+        _need(seq_len, torch.int32, "seq_len")
+    if out is None:
+        out = torch.empty((B, Hq, n_steps, D), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, n_steps), dtype=torch.float32, device=q.device)
+    need = decode_workspace_bytes(g, B, N, step0, n_steps)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=q.device)
+    st = _lib.lib().loopvq_decode_attn(
+        ctypes.byref(g), _ptr(q), step0, n_steps, _ptr(k_idx), _ptr(v_idx), N_cap, _ptr(k_cb), _ptr(v_cb),
+        _ptr(sink_k), _ptr(sink_v), n_s, B, N, _ptr(seq_len), ctypes.byref(pt) if pt is not None else None,
+        _ptr(rope), rope.shape[0], _ptr(out), _ptr(lse), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    check(st)
+    return out, lse

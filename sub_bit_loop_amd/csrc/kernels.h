@@ -1,0 +1,67 @@
+// Kernel argument blocks and launchers shared by the LoopVQ host API and the
+// HIP kernels.  Internal to the library.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace loopvq {
+
+struct EncodeArgs {
+  const uint16_t* x;          // bf16 rows of D, strides in elements
+  int64_t xs0, xs1, xs2, xs3;
+  const uint16_t* cb;         // bf16 [H][n_blk][K][G]
+  uint8_t* idx;               // [B][H][n_blk][N_cap][D/c]
+  int32_t H, n_blk, K, T, N, tok0, N_cap;
+  const float* w;             // pre-transform (keys) or null
+  const int16_t* perm;
+  const uint16_t* sigma;      // fp16 [B][sig_cap][T]
+  int32_t sig_cap;
+};
+
+struct SigmaArgs {
+  const uint16_t* x;
+  int64_t xs0, xs1, xs2, xs3;
+  int32_t H, T, N, tok0, sig_cap;
+  uint16_t* sigma;            // fp16 [B][sig_cap][T]
+};
+
+struct DecodeArgs {
+  const uint16_t* q;          // bf16 [B][Hq][n_steps][D]
+  const uint8_t* kidx;        // [B][H][n_blk][N_cap][D/c]
+  const uint8_t* vidx;
+  const uint16_t* kcb;        // bf16 [H][n_blk][K][G]
+  const uint16_t* vcb;
+  const uint16_t* sk;         // bf16 [B][H][T][n_s][D]
+  const uint16_t* sv;
+  const int32_t* seq_len;     // [B] or null
+  const float* w;             // pre-transform or null
+  const int16_t* perm;
+  const uint16_t* sigma;      // fp16 [B][sig_cap][T]
+  int32_t sig_cap;
+  const float* rope;          // fp32 [n_pos][D/2][2]
+  float* ws;                  // partials [B][Hq][n_steps][n_split][D+1]
+  int32_t B, H, Hq, T, n_blk, K, N, N_cap, n_s, step0, n_steps, n_split, gqa, blk0, n_blk_serv;
+  int32_t tok_per_split;
+  float qscale;               // log2(e) / sqrt(D)
+};
+
+struct MergeArgs {
+  const float* ws;
+  float* out;
+  float* lse;
+  int32_t rows, n_split;
+};
+
+// Launchers return hipSuccess or the launch error.  G in {16, 32},
+// T_c in {1, 2, 4, 8}; the caller validates.
+hipError_t launch_encode(int G, int TC, bool tasq, const EncodeArgs& a, int B, hipStream_t s);
+hipError_t launch_sigma(const SigmaArgs& a, int B, hipStream_t s);
+hipError_t launch_decode(int G, int TC, bool tasq, const DecodeArgs& a, hipStream_t s);
+hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
+hipError_t launch_rope_table(double theta, int D, int n_pos, float* table, hipStream_t s);
+
+constexpr int kDecodeThreads = 256;
+constexpr int kEncodeThreads = 256;
+constexpr int kEncodeTokens = 64;  // tokens per encode workgroup
+
+}  // namespace loopvq

@@ -1,0 +1,261 @@
+// Host side of the LoopVQ C ABI: argument checks, launch geometry, errors.
+// Every check runs before the first HIP call; no C++ exception leaves here.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/loopvq.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+loopvq_status fail(loopvq_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+loopvq_status hip_fail(hipError_t e, const char* what) {
+  return fail(LOOPVQ_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+
+// Geometry shared by both calls.
+loopvq_status check_geom(const loopvq_geom* g) {
+  if (!g) return fail(LOOPVQ_EINVAL, "geometry pointer is NULL");
+  if (g->D < 2 || g->D % 2) return fail(LOOPVQ_EINVAL, "D=%d must be even and >= 2", g->D);
+  if (g->T < 1 || g->T_c < 1 || g->T % g->T_c)
+    return fail(LOOPVQ_EINVAL, "T=%d must be a positive multiple of T_c=%d", g->T, g->T_c);
+  if (g->G < 1 || g->G % g->T_c)
+    return fail(LOOPVQ_EINVAL, "G=%d must be a positive multiple of T_c=%d", g->G, g->T_c);
+  const int c = g->G / g->T_c;
+  if (g->D % c) return fail(LOOPVQ_EINVAL, "D=%d must be a multiple of c=G/T_c=%d", g->D, c);
+  if (g->K < 2 || g->K > 256) return fail(LOOPVQ_EINVAL, "K=%d must be in [2, 256]", g->K);
+  if (g->n_kv_heads < 1 || g->n_q_heads < 1 || g->n_q_heads % g->n_kv_heads)
+    return fail(LOOPVQ_EINVAL, "n_q_heads=%d must be a positive multiple of n_kv_heads=%d",
+                g->n_q_heads, g->n_kv_heads);
+  if (!(g->rope_theta > 0.f) || !std::isfinite(g->rope_theta))
+    return fail(LOOPVQ_EINVAL, "rope_theta must be positive and finite");
+  if (g->D != 128) return fail(LOOPVQ_ENOTSUP, "this build supports D=128 only (got %d)", g->D);
+  if (g->G != 16 && g->G != 32) return fail(LOOPVQ_ENOTSUP, "this build supports G in {16, 32} (got %d)", g->G);
+  if (!pow2(g->T_c) || g->T_c > 8) return fail(LOOPVQ_ENOTSUP, "this build supports T_c in {1,2,4,8} (got %d)", g->T_c);
+  if ((g->D / 2) % c) return fail(LOOPVQ_ENOTSUP, "c=%d must divide D/2", c);
+  return LOOPVQ_OK;
+}
+
+loopvq_status check_pt(const loopvq_pretransform* pt, int B, int tok_end, bool need_sigma_write) {
+  if (!pt) return LOOPVQ_OK;
+  if (!pt->w || !pt->perm || !pt->sigma) return fail(LOOPVQ_EINVAL, "pre-transform has a NULL pointer");
+  if (pt->N_cap < tok_end)
+    return fail(LOOPVQ_EINVAL, "pre-transform sigma capacity %d < %d tokens", pt->N_cap, tok_end);
+  (void)B;
+  (void)need_sigma_write;
+  return LOOPVQ_OK;
+}
+
+struct DecodePlan {
+  int n_blk_serv, blk0, n_split, tok_per_split;
+  size_t ws_bytes;
+};
+
+DecodePlan plan_decode(const loopvq_geom* g, int B, int N, int step0, int n_steps) {
+  DecodePlan p;
+  p.blk0 = step0 / g->T_c;
+  const int blk1 = (step0 + n_steps - 1) / g->T_c;
+  p.n_blk_serv = blk1 - p.blk0 + 1;
+  const long long wgs = (long long)B * g->n_q_heads * p.n_blk_serv;
+  const int target = 2048;
+  long long ns = (target + wgs - 1) / wgs;
+  const long long max_by_tokens = N > 0 ? (N + 255) / 256 : 1;
+  if (ns > max_by_tokens) ns = max_by_tokens;
+  if (ns < 1) ns = 1;
+  p.n_split = (int)ns;
+  p.tok_per_split = N > 0 ? (N + p.n_split - 1) / p.n_split : 0;
+  p.ws_bytes = (size_t)B * g->n_q_heads * n_steps * p.n_split * (g->D + 1) * sizeof(float);
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* loopvq_last_error(void) { return g_err; }
+
+int32_t loopvq_abi_version(void) { return LOOPVQ_ABI_VERSION; }
+
+loopvq_status loopvq_encode(const loopvq_geom* g, const void* x, const int64_t x_strides[4],
+                            const void* codebook, int32_t B, int32_t N, int32_t tok0,
+                            uint8_t* idx, int32_t N_cap, const loopvq_pretransform* pt,
+                            void* stream) {
+  g_err[0] = 0;
+  loopvq_status st = check_geom(g);
+  if (st != LOOPVQ_OK) return st;
+  if (B < 0 || N < 0 || tok0 < 0) return fail(LOOPVQ_EINVAL, "B=%d, N=%d, tok0=%d must be >= 0", B, N, tok0);
+  if ((long long)tok0 + N > N_cap) return fail(LOOPVQ_EINVAL, "tok0 + N = %lld exceeds N_cap=%d", (long long)tok0 + N, N_cap);
+  if (N == 0 || B == 0) return LOOPVQ_OK;
+  if (!x || !x_strides || !codebook || !idx) return fail(LOOPVQ_EINVAL, "NULL tensor pointer");
+  for (int i = 0; i < 4; ++i)
+    if (x_strides[i] <= 0 || x_strides[i] % 8)
+      return fail(LOOPVQ_EINVAL, "x_strides[%d]=%lld must be a positive multiple of 8", i, (long long)x_strides[i]);
+  if (x_strides[3] < g->D) return fail(LOOPVQ_EINVAL, "token stride %lld < D", (long long)x_strides[3]);
+  if (reinterpret_cast<uintptr_t>(x) % 16 || reinterpret_cast<uintptr_t>(codebook) % 16)
+    return fail(LOOPVQ_EINVAL, "x and codebook must be 16-byte aligned");
+  st = check_pt(pt, B, tok0 + N, true);
+  if (st != LOOPVQ_OK) return st;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  loopvq::EncodeArgs a{};
+  a.x = static_cast<const uint16_t*>(x);
+  a.xs0 = x_strides[0];
+  a.xs1 = x_strides[1];
+  a.xs2 = x_strides[2];
+  a.xs3 = x_strides[3];
+  a.cb = static_cast<const uint16_t*>(codebook);
+  a.idx = idx;
+  a.H = g->n_kv_heads;
+  a.n_blk = g->T / g->T_c;
+  a.K = g->K;
+  a.T = g->T;
+  a.N = N;
+  a.tok0 = tok0;
+  a.N_cap = N_cap;
+  if (pt) {
+    loopvq::SigmaArgs sa{};
+    sa.x = a.x;
+    sa.xs0 = a.xs0;
+    sa.xs1 = a.xs1;
+    sa.xs2 = a.xs2;
+    sa.xs3 = a.xs3;
+    sa.H = a.H;
+    sa.T = a.T;
+    sa.N = N;
+    sa.tok0 = tok0;
+    sa.sig_cap = pt->N_cap;
+    sa.sigma = pt->sigma;
+    hipError_t e = loopvq::launch_sigma(sa, B, s);
+    if (e != hipSuccess) return hip_fail(e, "sigma launch");
+    a.w = pt->w;
+    a.perm = pt->perm;
+    a.sigma = pt->sigma;
+    a.sig_cap = pt->N_cap;
+  }
+  hipError_t e = loopvq::launch_encode(g->G, g->T_c, pt != nullptr, a, B, s);
+  if (e != hipSuccess) return hip_fail(e, "encode launch");
+  return LOOPVQ_OK;
+}
+
+loopvq_status loopvq_rope_table(float theta, int32_t D, int32_t n_pos, float* table, void* stream) {
+  g_err[0] = 0;
+  if (!table) return fail(LOOPVQ_EINVAL, "table is NULL");
+  if (n_pos < 1) return fail(LOOPVQ_EINVAL, "n_pos=%d must be >= 1", n_pos);
+  if (D < 2 || D % 2) return fail(LOOPVQ_EINVAL, "D=%d must be even and >= 2", D);
+  if (!(theta > 0.f) || !std::isfinite(theta)) return fail(LOOPVQ_EINVAL, "theta must be positive");
+  hipError_t e = loopvq::launch_rope_table((double)theta, D, n_pos, table, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "rope table launch");
+  return LOOPVQ_OK;
+}
+
+static loopvq_status check_decode_shape(const loopvq_geom* g, int32_t B, int32_t N, int32_t step0,
+                                        int32_t n_steps) {
+  loopvq_status st = check_geom(g);
+  if (st != LOOPVQ_OK) return st;
+  if (B < 0 || N < 0) return fail(LOOPVQ_EINVAL, "B=%d and N=%d must be >= 0", B, N);
+  if (n_steps < 1 || step0 < 0 || step0 + n_steps > g->T)
+    return fail(LOOPVQ_EINVAL, "step range [%d, %d) must lie in [0, T=%d)", step0, step0 + n_steps, g->T);
+  return LOOPVQ_OK;
+}
+
+loopvq_status loopvq_decode_attn_workspace(const loopvq_geom* g, int32_t B, int32_t N,
+                                           int32_t step0, int32_t n_steps, size_t* bytes) {
+  g_err[0] = 0;
+  loopvq_status st = check_decode_shape(g, B, N, step0, n_steps);
+  if (st != LOOPVQ_OK) return st;
+  if (!bytes) return fail(LOOPVQ_EINVAL, "bytes is NULL");
+  *bytes = B > 0 ? plan_decode(g, B, N, step0, n_steps).ws_bytes : 0;
+  return LOOPVQ_OK;
+}
+
+loopvq_status loopvq_decode_attn(const loopvq_geom* g, const void* q, int32_t step0,
+                                 int32_t n_steps, const uint8_t* k_idx, const uint8_t* v_idx,
+                                 int32_t N_cap, const void* k_cb, const void* v_cb,
+                                 const void* sink_k, const void* sink_v, int32_t n_s,
+                                 int32_t B, int32_t N, const int32_t* seq_len,
+                                 const loopvq_pretransform* pt, const float* rope_table,
+                                 int32_t n_pos, float* out, float* lse, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  loopvq_status st = check_decode_shape(g, B, N, step0, n_steps);
+  if (st != LOOPVQ_OK) return st;
+  if (n_s < 0) return fail(LOOPVQ_EINVAL, "n_s=%d must be >= 0", n_s);
+  if (N > N_cap) return fail(LOOPVQ_EINVAL, "N=%d exceeds N_cap=%d", N, N_cap);
+  if (B == 0) return LOOPVQ_OK;
+  if (!q || !k_cb || !v_cb || !rope_table || !out) return fail(LOOPVQ_EINVAL, "NULL tensor pointer");
+  if (N > 0 && (!k_idx || !v_idx)) return fail(LOOPVQ_EINVAL, "NULL index pointer");
+  if (n_s > 0 && (!sink_k || !sink_v)) return fail(LOOPVQ_EINVAL, "NULL sink pointer with n_s=%d", n_s);
+  if ((long long)n_s + N > n_pos)
+    return fail(LOOPVQ_EINVAL, "rope table has %d positions, need n_s + N = %lld", n_pos, (long long)n_s + N);
+  if (reinterpret_cast<uintptr_t>(k_cb) % 16 || reinterpret_cast<uintptr_t>(v_cb) % 16)
+    return fail(LOOPVQ_EINVAL, "codebooks must be 16-byte aligned");
+  st = check_pt(pt, B, N, false);
+  if (st != LOOPVQ_OK) return st;
+  const DecodePlan p = plan_decode(g, B, N, step0, n_steps);
+  if (!workspace || workspace_bytes < p.ws_bytes)
+    return fail(LOOPVQ_EWORKSPACE, "workspace of %zu bytes needed (got %zu)", p.ws_bytes, workspace_bytes);
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  loopvq::DecodeArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.kidx = k_idx;
+  a.vidx = v_idx;
+  a.kcb = static_cast<const uint16_t*>(k_cb);
+  a.vcb = static_cast<const uint16_t*>(v_cb);
+  a.sk = static_cast<const uint16_t*>(sink_k);
+  a.sv = static_cast<const uint16_t*>(sink_v);
+  a.seq_len = seq_len;
+  if (pt) {
+    a.w = pt->w;
+    a.perm = pt->perm;
+    a.sigma = pt->sigma;
+    a.sig_cap = pt->N_cap;
+  }
+  a.rope = rope_table;
+  a.ws = static_cast<float*>(workspace);
+  a.B = B;
+  a.H = g->n_kv_heads;
+  a.Hq = g->n_q_heads;
+  a.T = g->T;
+  a.n_blk = g->T / g->T_c;
+  a.K = g->K;
+  a.N = N;
+  a.N_cap = N_cap;
+  a.n_s = n_s;
+  a.step0 = step0;
+  a.n_steps = n_steps;
+  a.n_split = p.n_split;
+  a.gqa = g->n_q_heads / g->n_kv_heads;
+  a.blk0 = p.blk0;
+  a.n_blk_serv = p.n_blk_serv;
+  a.tok_per_split = p.tok_per_split;
+  a.qscale = (float)(1.4426950408889634 / std::sqrt((double)g->D));
+  hipError_t e = loopvq::launch_decode(g->G, g->T_c, pt != nullptr, a, s);
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  loopvq::MergeArgs ma{};
+  ma.ws = a.ws;
+  ma.out = out;
+  ma.lse = lse;
+  ma.rows = B * g->n_q_heads * n_steps;
+  ma.n_split = p.n_split;
+  e = loopvq::launch_merge(ma, s);
+  if (e != hipSuccess) return hip_fail(e, "merge launch");
+  return LOOPVQ_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,236 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Indices must equal the oracle's wherever the oracle's tie set has one element
+and lie in the tie set elsewhere; decode outputs must satisfy
+max_d |o_gpu - o_ref| <= 2e-3 * ||o_ref||_2 per (batch, q-head, step) row.
+Decode parity feeds both sides the GPU's own index tensors.
+"""
+import dataclasses
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as ref
+from synth import config_by_index
+from tests.helpers import (OUT_TOL, build_inputs, check_indices, np64, row_error, small_cfg)
+
+pytestmark = pytest.mark.gpu
+
+
+def _lib():
+    import sub_bit_loop_amd as s
+    s.lib()
+    return s
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _geom(s, cfg):
+    return s.geom(cfg.D, cfg.T, cfg.T_c, cfg.G, cfg.K, cfg.H_kv, cfg.H_q, cfg.theta)
+
+
+def _encode_all(s, cfg, inp, N_cap=None, pt_sigma=None):
+    g = _geom(s, cfg)
+    N = inp["k"].shape[3]
+    B = inp["k"].shape[0]
+    N_cap = N if N_cap is None else N_cap
+    shp = (B, cfg.H_kv, cfg.n_blk, N_cap, cfg.chunks)
+    kidx = torch.zeros(shp, dtype=torch.uint8, device="cuda")
+    vidx = torch.zeros(shp, dtype=torch.uint8, device="cuda")
+    pt = None
+    sigma = None
+    if cfg.tasq:
+        sigma = torch.zeros((B, N_cap, cfg.T), dtype=torch.float16, device="cuda")
+        pt = s.pretransform(inp["w"], inp["perm"], sigma)
+    s.encode(g, inp["k"], inp["k_cb"], kidx, pt=pt)
+    s.encode(g, inp["v"], inp["v_cb"], vidx)
+    return kidx, vidx, sigma, pt
+
+
+def _check_encode_slice(cfg, inp, kidx, vidx, sigma, b, h, toks):
+    """Oracle check of one (batch, kv-head) over a token subset."""
+    kx = np64(inp["k"][b, h][:, toks])
+    vx = np64(inp["v"][b, h][:, toks])
+    kc = np64(inp["k_cb"][h])
+    vc = np64(inp["v_cb"][h])
+    gk = kidx[b, h][:, toks].cpu().numpy()
+    gv = vidx[b, h][:, toks].cpu().numpy()
+    tasq = None
+    if cfg.tasq:
+        klayer = np64(inp["k"][b][:, :, toks])           # [H, T, n, D]
+        sig_ref = ref.tasq_sigma(klayer)                  # [n, T]
+        sbar = ref.fp16_round(sig_ref)
+        sg = sigma[b, toks].double().cpu().numpy()
+        # fp16 rounding must agree except within 1e-6 relative of a midpoint
+        mism = sg != sbar
+        if mism.any():
+            lo = ref.fp16_round(sig_ref * (1 - 1e-6))
+            hi = ref.fp16_round(sig_ref * (1 + 1e-6))
+            assert np.all((lo != hi)[mism]), "sigma differs from the oracle's fp16 rounding"
+        w = inp["w"][h].double().cpu().numpy()
+        perm = inp["perm"][h].long().cpu().numpy()
+        tasq = (w, perm, sg)
+    rk = check_indices(gk, kx, kc, cfg.T_c, tasq)
+    rv = check_indices(gv, vx, vc, cfg.T_c)
+    return rk, rv
+
+
+def _check_rows(cfg, inp, kidx, vidx, sigma, out, lse, rows, step0=0, N=None, seq=None):
+    """rows: list of (b, hq, t) with t absolute step; out/lse hold steps from step0."""
+    worst = 0.0
+    gqa = cfg.H_q // cfg.H_kv
+    for (b, hq, t) in rows:
+        h = hq // gqa
+        Nb = kidx.shape[3] if N is None else N
+        if seq is not None:
+            Nb = max(0, min(int(seq[b]), Nb))
+        ki = kidx[b, h].cpu().numpy()
+        vi = vidx[b, h].cpu().numpy()
+        tasq = None
+        if cfg.tasq:
+            tasq = (inp["w"][h].double().cpu().numpy(), inp["perm"][h].long().cpu().numpy(),
+                    sigma[b].double().cpu().numpy())
+        q = np64(inp["q"][b, hq, t])            # inp["q"] holds every step
+        n_s = inp["sink_k"].shape[3] if inp["sink_k"] is not None else 0
+        sk = np64(inp["sink_k"][b, h]) if n_s else np.zeros((cfg.T, 0, cfg.D))
+        sv = np64(inp["sink_v"][b, h]) if n_s else np.zeros((cfg.T, 0, cfg.D))
+        o_gpu = out[b, hq, t - step0].double().cpu().numpy()
+        if Nb + n_s == 0:
+            assert np.all(o_gpu == 0) and lse[b, hq, t - step0].item() == -math.inf
+            continue
+        o_ref, l_ref = ref.decode_attn_row(q, t, ki, vi, np64(inp["k_cb"][h]), np64(inp["v_cb"][h]),
+                                           sk, sv, cfg.T_c, cfg.theta, n_tokens=Nb, tasq=tasq)
+        err = row_error(o_gpu, o_ref)
+        worst = max(worst, err)
+        assert err <= OUT_TOL, "row %s: err %.3g" % ((b, hq, t), err)
+        assert abs(lse[b, hq, t - step0].item() - l_ref) < 1e-3 * max(1.0, abs(l_ref))
+    return worst
+
+
+def _decode(s, cfg, inp, kidx, vidx, pt, N=None, step0=0, n_steps=None, seq=None, n_s=None):
+    g = _geom(s, cfg)
+    n_steps = cfg.T if n_steps is None else n_steps
+    N = kidx.shape[3] if N is None else N
+    ns = inp["sink_k"].shape[3] if n_s is None else n_s
+    rope = s.rope_table(ns + kidx.shape[3] + 8, cfg.D, cfg.theta)
+    q = inp["q"][:, :, step0:step0 + n_steps].contiguous()
+    sk = inp["sink_k"] if ns else None
+    sv = inp["sink_v"] if ns else None
+    return s.decode_attn(g, q, kidx, vidx, inp["k_cb"], inp["v_cb"], sk, sv, rope, N=N, step0=step0,
+                         seq_len=seq, pt=pt)
+
+
+def test_config1_full():
+    s = _lib()
+    cfg = config_by_index(1)
+    _say("config 1: building inputs")
+    inp = build_inputs(cfg, 0, "cuda")
+    kidx, vidx, sigma, pt = _encode_all(s, cfg, inp)
+    out, lse = _decode(s, cfg, inp, kidx, vidx, pt)
+    torch.cuda.synchronize()
+    rk, rv = _check_encode_slice(cfg, inp, kidx, vidx, sigma, 0, 0, slice(None))
+    _say("config 1 encode K exact/tie/fail", rk, "V", rv)
+    assert rk[2] == 0 and rv[2] == 0
+    rows = [(0, 0, t) for t in range(cfg.T)]
+    worst = _check_rows(cfg, inp, kidx, vidx, sigma, out, lse, rows)
+    _say("config 1 decode worst rel err %.3g" % worst)
+
+
+GEOMS = [
+    # name, G, T_c, T, H_kv, H_q, B, N, n_s, K, tasq
+    ("two-blocks-gqa2", 16, 4, 8, 2, 4, 2, 1000, 4, 256, False),
+    ("quarter-bit-gqa4", 32, 4, 4, 2, 8, 2, 700, 4, 256, False),
+    ("pretransform", 16, 4, 4, 2, 2, 2, 777, 4, 256, True),
+    ("tc2-k200-nosink", 16, 2, 4, 1, 1, 1, 300, 0, 200, False),
+    ("tc1-channel-vq", 16, 1, 2, 1, 2, 1, 129, 3, 64, False),
+    ("tc8", 32, 8, 8, 1, 1, 1, 200, 2, 256, False),
+]
+
+
+@pytest.mark.parametrize("geo", GEOMS, ids=[x[0] for x in GEOMS])
+def test_small_geometries(geo):
+    s = _lib()
+    name, G, T_c, T, H, Hq, B, N, n_s, K, tasq = geo
+    _say("geometry", name)
+    cfg = small_cfg(1, G=G, T_c=T_c, T=T, H_kv=H, H_q=Hq, B=B, N=N, n_s=n_s, K=K, tasq=tasq,
+                    rho_k=(0.85,) * (T - 1), rho_v=(0.9,) * (T - 1), n_calib=1024, kmeans_iters=8)
+    inp = build_inputs(cfg, 0, "cuda", kmeans=True)
+    # plant exact codewords (and a duplicate codeword) to exercise exact ties
+    kc = inp["k_cb"]
+    kc[:, :, K - 1] = kc[:, :, 3]
+    c = cfg.c
+    for j in range(0, min(N, 40), 7):
+        if tasq:
+            break
+        r = (j * 37) % K
+        for beta in range(cfg.n_blk):
+            for m in range(T_c):
+                for i in range(c):
+                    val = kc[:, beta, r, i * T_c + m].view(1, H, 1).expand(B, H, cfg.D // c)
+                    inp["k"][:, :, beta * T_c + m, j, i::c] = val
+    kidx, vidx, sigma, pt = _encode_all(s, cfg, inp)
+    out, lse = _decode(s, cfg, inp, kidx, vidx, pt, n_s=n_s)
+    torch.cuda.synchronize()
+    fails = 0
+    for b in range(B):
+        for h in range(H):
+            rk, rv = _check_encode_slice(cfg, inp, kidx, vidx, sigma, b, h, slice(None))
+            fails += rk[2] + rv[2]
+            _say("  b%d h%d K exact/tie/fail %s V %s" % (b, h, rk, rv))
+    assert fails == 0
+    rows = [(b, hq, t) for b in range(B) for hq in range(Hq) for t in range(T)]
+    worst = _check_rows(cfg, inp, kidx, vidx, sigma, out, lse, rows)
+    _say("  decode worst rel err %.3g over %d rows" % (worst, len(rows)))
+
+
+def test_edge_cases():
+    s = _lib()
+    cfg = small_cfg(1, B=3, N=300, H_kv=1, H_q=1, n_calib=1024, kmeans_iters=5)
+    inp = build_inputs(cfg, 0, "cuda")
+    kidx, vidx, sigma, pt = _encode_all(s, cfg, inp)
+    # only sinks (N = 0)
+    out, lse = _decode(s, cfg, inp, kidx, vidx, pt, N=0)
+    torch.cuda.synchronize()
+    _check_rows(cfg, inp, kidx, vidx, sigma, out, lse, [(b, 0, t) for b in range(3) for t in range(4)], N=0)
+    # per-batch lengths, one row with no keys at all
+    seq = torch.tensor([0, 5, 1000], dtype=torch.int32, device="cuda")
+    out, lse = _decode(s, cfg, inp, kidx, vidx, pt, seq=seq, n_s=0)
+    torch.cuda.synchronize()
+    inp0 = dict(inp, sink_k=None, sink_v=None)
+    _check_rows(cfg, inp0, kidx, vidx, sigma, out, lse, [(b, 0, t) for b in range(3) for t in range(4)],
+                seq=seq.cpu().numpy())
+    # step sub-ranges: one step, and a middle pair
+    for step0, n_steps in ((2, 1), (1, 2)):
+        out, lse = _decode(s, cfg, inp, kidx, vidx, pt, step0=step0, n_steps=n_steps)
+        torch.cuda.synchronize()
+        _check_rows(cfg, inp, kidx, vidx, sigma, out, lse,
+                    [(b, 0, t) for b in range(3) for t in range(step0, step0 + n_steps)], step0=step0)
+    # append: encode tokens [200, 300) at tok0 = 200 into a fresh buffer
+    g = _geom(s, cfg)
+    idx2 = torch.zeros_like(kidx)
+    idx2[:, :, :, :200] = kidx[:, :, :, :200]
+    s.encode(g, inp["k"][:, :, :, 200:], inp["k_cb"], idx2, tok0=200)
+    torch.cuda.synchronize()
+    assert torch.equal(idx2, kidx)
+    # determinism: identical bytes on a second run
+    k2, v2, _, _ = _encode_all(s, cfg, inp)
+    o2, l2 = _decode(s, cfg, inp, k2, v2, pt)
+    o1, l1 = _decode(s, cfg, inp, kidx, vidx, pt)
+    torch.cuda.synchronize()
+    assert torch.equal(k2, kidx) and torch.equal(v2, vidx)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_rope_table_matches_oracle():
+    s = _lib()
+    t = s.rope_table(65800, 128, 1.0e4)
+    torch.cuda.synchronize()
+    tab = ref.rope_table(65800, 128)
+    got = t.double().cpu().numpy()
+    assert np.max(np.abs(got - tab)) <= 6e-8
