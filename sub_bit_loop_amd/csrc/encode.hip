@@ -62,14 +62,34 @@ __global__ __launch_bounds__(256) void sigma_kernel(SigmaArgs a) {
   }
 }
 
+// Split an fp32 value into three bf16 terms whose sum is exact (RNE splits).
+__device__ __forceinline__ void split3(float x, uint16_t& h, uint16_t& m, uint16_t& l) {
+  uint32_t a = f32_to_bf16_rne(x);
+  float r1 = x - bf16_to_f32(a);
+  uint32_t b = f32_to_bf16_rne(r1);
+  float r2 = r1 - bf16_to_f32(b);
+  h = (uint16_t)a;
+  m = (uint16_t)b;
+  l = (uint16_t)f32_to_bf16_rne(r2);
+}
+
+// bf16 bits of the smallest bf16 >= x (x > 0 finite).
+__device__ __forceinline__ uint16_t bf16_ceil(float x) {
+  uint32_t u = __float_as_uint(x);
+  uint32_t hi = u >> 16;
+  if (u & 0xffffu) ++hi;
+  return (uint16_t)hi;
+}
+
 template <int G, int TC, bool TASQ>
 __global__ __launch_bounds__(kEncodeThreads) void encode_kernel(EncodeArgs a) {
   constexpr int D = 128;
   constexpr int C = G / TC;        // channels per step per code
   constexpr int CPT = D / C;       // codes per token
   constexpr int KK = G / 16;       // MFMA k-chunks of 16
+  // Per codebook row: -2*e (G bf16) and the norm row [nh, nm, nl, 1, 1, 1, 1, 0].
   __shared__ __attribute__((aligned(16))) uint16_t s_cb[256 * G];
-  __shared__ __attribute__((aligned(16))) float s_nrm[256];
+  __shared__ __attribute__((aligned(16))) uint16_t s_nb[256 * 8];
   __shared__ float s_wmax[kEncodeThreads / kWave];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -78,25 +98,31 @@ __global__ __launch_bounds__(kEncodeThreads) void encode_kernel(EncodeArgs a) {
   const int b = blockIdx.z;
   const uint16_t* cb = a.cb + (int64_t)hb * a.K * G;
 
-  for (int e = tid; e < 256 * G; e += kEncodeThreads) {
-    uint16_t v = 0;
-    if (e < a.K * G) v = (uint16_t)f32_to_bf16_rne(-2.f * bf16_to_f32(cb[e]));
-    s_cb[e] = v;
-  }
   float nmax = 0.f;
   {
-    const int r = tid;
-    float nrm = INFINITY;
+    const int r = tid;   // one codebook row per thread
+    uint16_t nh = 0, nm = 0, nl = 0;
+    uint16_t one = 0;
     if (r < a.K) {
-      float s = 0.f;
+      double s = 0.0;
+#pragma unroll
       for (int u = 0; u < G; ++u) {
-        float f = bf16_to_f32(cb[r * G + u]);
-        s = fmaf(f, f, s);
+        const float f = bf16_to_f32(cb[r * G + u]);
+        s += (double)f * (double)f;
+        s_cb[r * G + u] = (uint16_t)f32_to_bf16_rne(-2.f * f);
       }
-      nrm = s;
-      nmax = s;
+      const float nf = (float)s;
+      split3(nf, nh, nm, nl);
+      nmax = nf;
+      one = 0x3f80;
+    } else {
+      // Padding rows never win: a huge norm, zero codeword.
+#pragma unroll
+      for (int u = 0; u < G; ++u) s_cb[r * G + u] = 0;
+      nh = 0x7f00;   // 2^127
     }
-    s_nrm[r] = nrm;
+    uint16_t* nb = s_nb + r * 8;
+    nb[0] = nh; nb[1] = nm; nb[2] = nl; nb[3] = one; nb[4] = one; nb[5] = one; nb[6] = 0x3f80; nb[7] = 0;
   }
   for (int off = 32; off >= 1; off >>= 1) nmax = fmaxf(nmax, __shfl_xor(nmax, off));
   if (lane == 0) s_wmax[wave] = nmax;
@@ -114,6 +140,7 @@ __global__ __launch_bounds__(kEncodeThreads) void encode_kernel(EncodeArgs a) {
   const float* wh = TASQ ? a.w + h * D : nullptr;
   const int16_t* ph = TASQ ? a.perm + h * D : nullptr;
   const uint16_t* sgb = TASQ ? a.sigma + ((int64_t)b * a.sig_cap + a.tok0) * a.T + beta * TC : nullptr;
+  const uint32_t kmask = 0xffffff00u;   // the low byte carries the lane-local candidate number
 
   for (int grp = wave; grp < ngroups; grp += kEncodeThreads / kWave) {
     const int g = grp * 32 + n;
@@ -123,7 +150,7 @@ __global__ __launch_bounds__(kEncodeThreads) void encode_kernel(EncodeArgs a) {
     const int j = j0 + jl;
     const uint16_t* xr = xbase + (int64_t)j * a.xs3;
 
-    // B operand: this lane's 8 joint coordinates per k-chunk.
+    // B operand: this lane's 8 joint coordinates per k-chunk (code n, coordinates 16kk+8hh..+7).
     bf16x8_t bz[KK];
     bf16x8_t bzlo[KK];
     float zz = 0.f;
@@ -135,78 +162,92 @@ __global__ __launch_bounds__(kEncodeThreads) void encode_kernel(EncodeArgs a) {
         const int i = u / TC, m = u - (u / TC) * TC;
         const int d = q * C + i;
         if constexpr (!TASQ) {
-          uint16_t v = xr[m * a.xs2 + d];
-          float f = bf16_to_f32(v);
+          const uint16_t v = xr[m * a.xs2 + d];
+          const float f = bf16_to_f32(v);
           zz = fmaf(f, f, zz);
           bz[kk][e] = __builtin_bit_cast(__bf16, v);
         } else {
           const int o = ph[d] & (D - 1);
-          float kv = bf16_to_f32(xr[m * a.xs2 + o]);
+          const float kv = bf16_to_f32(xr[m * a.xs2 + o]);
           _Float16 sh;
-          uint16_t sb = sgb[(int64_t)j * a.T + m];
+          const uint16_t sb = sgb[(int64_t)j * a.T + m];
           __builtin_memcpy(&sh, &sb, 2);
-          float zf = (wh[o] * kv) / (float)sh;
-          uint32_t hb16 = f32_to_bf16_rne(zf);
-          uint32_t lb16 = f32_to_bf16_rne(zf - bf16_to_f32(hb16));
+          const float zf = (wh[o] * kv) / (float)sh;
+          const uint32_t hb16 = f32_to_bf16_rne(zf);
+          const uint32_t lb16 = f32_to_bf16_rne(zf - bf16_to_f32(hb16));
           zz = fmaf(zf, zf, zz);
           bz[kk][e] = __builtin_bit_cast(__bf16, (uint16_t)hb16);
           bzlo[kk][e] = __builtin_bit_cast(__bf16, (uint16_t)lb16);
         }
       }
     }
+    zz += __shfl_xor(zz, 32);   // ||z||^2 of code n (both halves)
+    // Error bound of the screened distance, and a margin that keeps every
+    // screened value positive so its bit pattern orders like the value.
+    float eps = (float)(G + 24) * 5.9604645e-08f * (2.f * emax + 2.f * zz);
+    if constexpr (TASQ) eps = 2.f * eps + 3.0517578e-05f * (zz + emax);
+    const uint16_t beta_b = bf16_ceil(2.f * eps + 1e-30f);
+    bf16x8_t bn;
+    {
+      uint16_t zh, zm, zl;
+      split3(zz, zh, zm, zl);
+      const uint16_t one = hh == 0 ? 0x3f80 : 0;
+      bn[0] = __builtin_bit_cast(__bf16, one);
+      bn[1] = __builtin_bit_cast(__bf16, one);
+      bn[2] = __builtin_bit_cast(__bf16, one);
+      bn[3] = __builtin_bit_cast(__bf16, (uint16_t)(hh == 0 ? zh : 0));
+      bn[4] = __builtin_bit_cast(__bf16, (uint16_t)(hh == 0 ? zm : 0));
+      bn[5] = __builtin_bit_cast(__bf16, (uint16_t)(hh == 0 ? zl : 0));
+      bn[6] = __builtin_bit_cast(__bf16, (uint16_t)(hh == 0 ? beta_b : 0));
+      bn[7] = __builtin_bit_cast(__bf16, (uint16_t)0);
+    }
 
-    float b1 = INFINITY, b2 = INFINITY;
-    int i1 = 0;
-#pragma unroll 1
+    // Screening: every value is ||z - e_r||^2 + margin (fp32 MFMA); the key
+    // replaces the low mantissa byte with the lane-local candidate number.
+    // Keys are positive finite floats whose low byte is the candidate number,
+    // so float min / median order them exactly like the screened values.
+    float k1 = INFINITY, k2 = INFINITY;
+#pragma unroll 2
     for (int t = 0; t < 8; ++t) {
-      f32x16_t acc;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        f32x4_t nv = *reinterpret_cast<const f32x4_t*>(&s_nrm[32 * t + 8 * v + 4 * hh]);
-        acc[4 * v + 0] = nv[0];
-        acc[4 * v + 1] = nv[1];
-        acc[4 * v + 2] = nv[2];
-        acc[4 * v + 3] = nv[3];
-      }
+      f32x16_t acc = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      const bf16x8_t an = *reinterpret_cast<const bf16x8_t*>(&s_nb[(32 * t + n) * 8 + 0]);
+      bf16x8_t anz;
+      if (hh == 0) anz = an; else anz = bf16x8_t{};
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(anz, bn, acc, 0, 0, 0);
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
-        bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(&s_cb[(32 * t + n) * G + 16 * kk + 8 * hh]);
+        const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(&s_cb[(32 * t + n) * G + 16 * kk + 8 * hh]);
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bz[kk], acc, 0, 0, 0);
         if constexpr (TASQ) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bzlo[kk], acc, 0, 0, 0);
       }
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float v = acc[i];
-        const int r = 32 * t + 8 * (i >> 2) + 4 * hh + (i & 3);
-        b2 = fminf(b2, fmaxf(b1, v));
-        if (v < b1) {
-          b1 = v;
-          i1 = r;
-        }
+        const float key = __uint_as_float(__builtin_amdgcn_perm(__float_as_uint(acc[i]), (uint32_t)(16 * t + i), 0x07060500u));
+        k2 = __builtin_amdgcn_fmed3f(k1, k2, key);
+        k1 = fminf(k1, key);
       }
     }
-    // Combine the two half-waves (lanes n and n+32 hold different codewords).
-    const float ob1 = __shfl_xor(b1, 32), ob2 = __shfl_xor(b2, 32);
-    const int oi1 = __shfl_xor(i1, 32);
-    zz += __shfl_xor(zz, 32);
-    float nb1;
-    int ni1;
-    if (ob1 < b1 || (ob1 == b1 && oi1 < i1)) {
-      nb1 = ob1;
-      ni1 = oi1;
-    } else {
-      nb1 = b1;
-      ni1 = i1;
-    }
-    const float nb2 = fminf(fmaxf(b1, ob1), fminf(b2, ob2));
-    if (hh == 0 && valid) {
-      // Screening error bound on dt (fp32 sums of G+1 terms plus the norm).
-      float eps = (float)(2 * G + 2) * 5.9604645e-08f * (2.f * emax + zz);
-      if constexpr (TASQ) eps = 2.f * eps + 1.5258789e-05f * (zz + emax);
-      int res = ni1;
-      if (!(nb2 > nb1 + 2.f * eps)) {
-        // Exact re-score in fp64, direct form, lowest index wins.
-        double zd[G];
+    // Merge the two half-waves (lanes n and n+32 screen different codewords).
+    const uint32_t uk1 = __float_as_uint(k1), uk2 = __float_as_uint(k2);
+    const uint32_t ok1 = __shfl_xor(uk1, 32), ok2 = __shfl_xor(uk2, 32);
+    const float v1 = __uint_as_float(uk1 & kmask), ov1 = __uint_as_float(ok1 & kmask);
+    const bool mine = v1 < ov1 || (v1 == ov1 && hh == 0);
+    const uint32_t wkey = mine ? uk1 : ok1;
+    const int whalf = mine ? hh : hh ^ 1;
+    const float t1 = __uint_as_float(wkey & kmask);
+    // second smallest screened value over both halves
+    const float s_own2 = __uint_as_float(uk2 & kmask), s_oth2 = __uint_as_float(ok2 & kmask);
+    const float t2 = mine ? fminf(s_own2, ov1) : fminf(s_oth2, v1);
+    const float thr = t1 * (1.f + 6.1035156e-05f) + 2.f * eps;
+    const bool tie = valid && !(t2 > thr);
+    const int loc = (int)(wkey & 0xffu);
+    int res = 32 * (loc >> 4) + 8 * ((loc & 15) >> 2) + 4 * whalf + (loc & 3);
+
+    if (__builtin_expect(__ballot(tie) != 0, 0)) {
+      // Rare path: re-screen and score every candidate inside the band exactly
+      // in fp64 (direct form); lowest index wins exact ties.
+      double zd[G];
+      if (tie) {
 #pragma unroll
         for (int u = 0; u < G; ++u) {
           const int i = u / TC, m = u - (u / TC) * TC;
@@ -215,30 +256,56 @@ __global__ __launch_bounds__(kEncodeThreads) void encode_kernel(EncodeArgs a) {
             zd[u] = (double)bf16_to_f32(xr[m * a.xs2 + d]);
           } else {
             const int o = ph[d] & (D - 1);
-            double kv = (double)bf16_to_f32(xr[m * a.xs2 + o]);
-            double sg = f16_bits_to_f64(sgb[(int64_t)j * a.T + m]);
+            const double kv = (double)bf16_to_f32(xr[m * a.xs2 + o]);
+            const double sg = f16_bits_to_f64(sgb[(int64_t)j * a.T + m]);
             zd[u] = ((double)wh[o] * kv) / sg;
           }
         }
-        double best = INFINITY;
-        int bi = 0;
-        for (int r = 0; r < a.K; ++r) {
-          double dist = 0.0;
+      }
+      const float lim = tie ? thr : -1.f;
+      double best = INFINITY;
+      int bi = 0x7fffffff;
+#pragma unroll 1
+      for (int t = 0; t < 8; ++t) {
+        f32x16_t acc = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        const bf16x8_t an = *reinterpret_cast<const bf16x8_t*>(&s_nb[(32 * t + n) * 8 + 0]);
+        bf16x8_t anz;
+        if (hh == 0) anz = an; else anz = bf16x8_t{};
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(anz, bn, acc, 0, 0, 0);
 #pragma unroll
-          for (int u = 0; u < G; ++u) {
-            double e = -0.5 * (double)bf16_to_f32(s_cb[r * G + u]);
-            double df = zd[u] - e;
-            dist += df * df;
-          }
-          if (dist < best) {
-            best = dist;
-            bi = r;
+        for (int kk = 0; kk < KK; ++kk) {
+          const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(&s_cb[(32 * t + n) * G + 16 * kk + 8 * hh]);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bz[kk], acc, 0, 0, 0);
+          if constexpr (TASQ) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bzlo[kk], acc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float tv = __uint_as_float(__float_as_uint(acc[i]) & kmask);
+          if (tv <= lim) {
+            const int r = 32 * t + 8 * (i >> 2) + 4 * hh + (i & 3);
+            double dist = 0.0;
+            for (int u = 0; u < G; ++u) {
+              const double e = -0.5 * (double)bf16_to_f32(s_cb[r * G + u]);
+              const double df = zd[u] - e;
+              dist += df * df;
+            }
+            if (r < a.K && (dist < best || (dist == best && r < bi))) {
+              best = dist;
+              bi = r;
+            }
           }
         }
-        res = bi;
       }
-      ibase[g] = (uint8_t)res;
+      // combine the halves: smallest distance, then lowest index
+      const double obest = __shfl_xor(best, 32);
+      const int obi = __shfl_xor(bi, 32);
+      if (obest < best || (obest == best && obi < bi)) {
+        best = obest;
+        bi = obi;
+      }
+      if (tie) res = bi;
     }
+    if (hh == 0 && valid) ibase[g] = (uint8_t)res;
   }
 }
 
