@@ -107,11 +107,14 @@ loopvq_status loopvq_encode(const loopvq_geom* g, const void* x, const int64_t x
                             void* stream);
 
 /* loopvq_rope_table -- the per-position sin/cos table the decode kernel reads
- * (section 3.4, step 3).  table[p][d] = (cos(phi), sin(phi)) with
- * phi = p * theta^(-2d/D) evaluated in fp64 on the GPU and rounded to fp32.
- *   table   device fp32 [n_pos][D/2][2]
- * Errors: EINVAL for NULL table, n_pos < 1, odd D or D < 2, theta <= 0. */
-loopvq_status loopvq_rope_table(float theta, int32_t D, int32_t n_pos, float* table,
+ * (section 3.4, step 3).  For position p and frequency f < D/2 the angle is
+ * phi = p * theta^(-2f/D), evaluated in fp64 on the GPU; cos(phi) and sin(phi)
+ * are rounded once to fp16 (round to nearest even).
+ *   table   device fp16 [n_pos][D/8][8]: entry [p][f/4] holds
+ *           cos of frequencies 4*(f/4) .. +3, then their sines
+ * Errors: EINVAL for NULL table, n_pos < 1, D not a positive multiple of 8,
+ * theta <= 0. */
+loopvq_status loopvq_rope_table(float theta, int32_t D, int32_t n_pos, void* table,
                                 void* stream);
 
 /* loopvq_decode_attn_workspace -- bytes of scratch loopvq_decode_attn needs
@@ -147,9 +150,11 @@ loopvq_status loopvq_decode_attn_workspace(const loopvq_geom* g, int32_t B, int3
  *   seq_len    device int32 [B] or NULL; batch b attends min(seq_len[b], N)
  *              quantized tokens (negative values count as 0)
  *   pt         keys' pre-transform (reads w, perm, sigma) or NULL
- *   rope_table device fp32 [n_pos][D/2][2] from loopvq_rope_table, with
- *              n_pos >= n_s + N
+ *   rope_table device fp16 table written by loopvq_rope_table for this D and
+ *              theta, with n_pos >= n_s + N positions
  *   workspace  device scratch of at least loopvq_decode_attn_workspace() bytes
+ * Alignment: q, k_idx, v_idx, k_cb, v_cb, sink_k, sink_v, rope_table and
+ * workspace must be 16-byte aligned.
  * A row with no keys at all (n_s == 0 and N_b == 0) yields out = 0 and
  * lse = -inf.
  * Errors: EINVAL for NULL pointers, bad geometry, step range outside [0, T),
@@ -160,7 +165,7 @@ loopvq_status loopvq_decode_attn(const loopvq_geom* g, const void* q, int32_t st
                                  int32_t N_cap, const void* k_cb, const void* v_cb,
                                  const void* sink_k, const void* sink_v, int32_t n_s,
                                  int32_t B, int32_t N, const int32_t* seq_len,
-                                 const loopvq_pretransform* pt, const float* rope_table,
+                                 const loopvq_pretransform* pt, const void* rope_table,
                                  int32_t n_pos, float* out, float* lse, void* workspace,
                                  size_t workspace_bytes, void* stream);
 

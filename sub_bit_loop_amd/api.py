@@ -63,7 +63,8 @@ def encode(g: Geom, x, codebook, idx, tok0=0, pt=None, stream=None):
 
 
 def rope_table(n_pos, D=128, theta=1.0e4, device="cuda", stream=None):
-    t = torch.empty((n_pos, D // 2, 2), dtype=torch.float32, device=device)
+    """fp16 [n_pos][D/8][8]: per 4 frequencies, their cosines then sines."""
+    t = torch.empty((n_pos, D // 8, 8), dtype=torch.float16, device=device)
     check(_lib.lib().loopvq_rope_table(theta, D, n_pos, _ptr(t), _stream(stream)))
     return t
 
@@ -78,13 +79,13 @@ def decode_attn(g: Geom, q, k_idx, v_idx, k_cb, v_cb, sink_k, sink_v, rope, N=No
                 seq_len=None, pt=None, out=None, lse=None, workspace=None, stream=None):
     """q bf16 [B][Hq][n_steps][D] (post-RoPE); k_idx/v_idx uint8 [B][H][n_blk][N_cap][D/c];
     k_cb/v_cb bf16 [H][n_blk][K][G]; sinks bf16 [B][H][T][n_s][D] or None;
-    rope fp32 [n_pos][D/2][2].  Returns (out fp32 [B][Hq][n_steps][D], lse fp32 [B][Hq][n_steps])."""
+    rope fp16 table from rope_table().  Returns (out fp32 [B][Hq][n_steps][D], lse fp32 [B][Hq][n_steps])."""
     _need(q, torch.bfloat16, "q")
     _need(k_idx, torch.uint8, "k_idx")
     _need(v_idx, torch.uint8, "v_idx")
     _need(k_cb, torch.bfloat16, "k_cb")
     _need(v_cb, torch.bfloat16, "v_cb")
-    _need(rope, torch.float32, "rope")
+    _need(rope, torch.float16, "rope")
     for t, n in ((q, "q"), (k_idx, "k_idx"), (v_idx, "v_idx"), (k_cb, "k_cb"), (v_cb, "v_cb"), (rope, "rope")):
         if not t.is_contiguous():
             raise ValueError("%s must be contiguous" % n)

@@ -31,6 +31,29 @@ __device__ __forceinline__ double f16_bits_to_f64(uint16_t h) {
   return (double)(float)v;
 }
 
+// fp64 -> fp16 bits, round to nearest even (finite inputs; overflow saturates
+// to the largest finite value).
+__device__ __forceinline__ uint16_t f64_to_f16_rne(double v) {
+  const uint16_t sign = v < 0.0 ? 0x8000 : 0;
+  const double av = fabs(v);
+  const _Float16 h0 = (_Float16)(float)av;
+  uint16_t b0;
+  __builtin_memcpy(&b0, &h0, 2);
+  if (b0 >= 0x7c00) b0 = 0x7bff;
+  uint16_t best = b0;
+  double bestd = fabs(av - f16_bits_to_f64(b0));
+  for (int k = -1; k <= 1; k += 2) {
+    const int c = (int)b0 + k;
+    if (c < 0 || c >= 0x7c00) continue;
+    const double d = fabs(av - f16_bits_to_f64((uint16_t)c));
+    if (d < bestd || (d == bestd && (c & 1) == 0 && (best & 1) != 0)) {
+      best = (uint16_t)c;
+      bestd = d;
+    }
+  }
+  return (uint16_t)(best | sign);
+}
+
 // DPP all-reduce sum over aligned groups of L lanes (L in {1,2,4,8,16}).
 // quad_perm [1,0,3,2] = 0xB1, [2,3,0,1] = 0x4E, row_half_mirror = 0x141,
 // row_mirror = 0x140: each pairs every lane with a partner inside the group.

@@ -184,25 +184,15 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
       }
     }
 
-    // cos/sin of the token position for this lane's frequencies.
+    // cos/sin of the token position for this lane's frequencies (fp16 table:
+    // per position 16 quads of [cos f..f+3, sin f..f+3]).
     float cs[NE], sn[NE];
-    const float* rp = a.rope + (int64_t)pos * D;
+    const _Float16* rp = reinterpret_cast<const _Float16*>(a.rope) + (int64_t)pos * D;
 #pragma unroll
     for (int e = 0; e < NE; ++e) {
-      if constexpr (!TASQ) {
-        if (e < C) {
-          const float2 v = *reinterpret_cast<const float2*>(rp + 2 * freq[e]);
-          cs[e] = v.x;
-          sn[e] = v.y;
-        } else {
-          cs[e] = cs[e - C];
-          sn[e] = sn[e - C];
-        }
-      } else {
-        const float2 v = *reinterpret_cast<const float2*>(rp + 2 * freq[e]);
-        cs[e] = v.x;
-        sn[e] = v.y;
-      }
+      const int f = freq[e];
+      cs[e] = (float)rp[(f >> 2) * 8 + (f & 3)];
+      sn[e] = (float)rp[(f >> 2) * 8 + 4 + (f & 3)];
     }
 
     float sc[R];
@@ -357,23 +347,26 @@ hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// fp64 angles, rounded once to fp32 (review section 3.4: precomputed table).
-__global__ void rope_table_kernel(double theta, int D, int n_pos, float* table) {
+// fp64 angles rounded once to fp16 (review section 3.4: a precomputed
+// per-position sin/cos table).  Layout per position: D/8 quads, each
+// [cos f, cos f+1, cos f+2, cos f+3, sin f, ..., sin f+3] with f = 4 * quad.
+__global__ void rope_table_kernel(double theta, int D, int n_pos, uint16_t* table) {
   const int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int half = D / 2;
   if (x >= (int64_t)n_pos * half) return;
-  const int p = (int)(x / half), d = (int)(x - (int64_t)p * half);
-  const double omega = pow(theta, -2.0 * (double)d / (double)D);
+  const int p = (int)(x / half), f = (int)(x - (int64_t)p * half);
+  const double omega = pow(theta, -2.0 * (double)f / (double)D);
   const double phi = (double)p * omega;
-  table[2 * x] = (float)cos(phi);
-  table[2 * x + 1] = (float)sin(phi);
+  uint16_t* row = table + (int64_t)p * D + (f >> 2) * 8;
+  row[f & 3] = f64_to_f16_rne(cos(phi));
+  row[4 + (f & 3)] = f64_to_f16_rne(sin(phi));
 }
 
-hipError_t launch_rope_table(double theta, int D, int n_pos, float* table, hipStream_t s) {
+hipError_t launch_rope_table(double theta, int D, int n_pos, void* table, hipStream_t s) {
   const int64_t n = (int64_t)n_pos * (D / 2);
   const int threads = 256;
   hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((n + threads - 1) / threads)), dim3(threads), 0, s,
-                     theta, D, n_pos, table);
+                     theta, D, n_pos, static_cast<uint16_t*>(table));
   return hipGetLastError();
 }
 

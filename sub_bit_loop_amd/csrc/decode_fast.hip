@@ -1,0 +1,394 @@
+// LoopVQ fused decode attention, specialised for the 0.5-bit loop layout:
+// G = 16, T_c = 4 (c = 4 channels per step per code), D = 128, no channel
+// pre-transform.
+//
+// LoopVQ review (arXiv 2611.05304), section 3.4 step 3 (codebook on chip,
+// lookup by index, RoPE from a precomputed table after dequant, Flash-
+// Decoding split merge) and section 3.1 eq. (5) (step m reads coordinate
+// i*T_c + m of the shared codeword).
+//
+// Layout choices for gfx950:
+//   * Both codebooks sit in LDS as fp16, step-major inside a codeword:
+//     word (m, i) at 8m + 2i bytes, 32 bytes per codeword.  Bytes [16h, 16h+16)
+//     hold steps 2h and 2h+1 for all four channels, so one ds_read_b128
+//     returns what one lane needs for two steps.
+//   * A token is served by 8 lanes: lane (h, g) takes steps {2h, 2h+1} and
+//     chunk pairs (q, q + 16) for q = g, g+4, g+8, g+12, i.e. the channel
+//     pairs that RoPE rotates together.  Every index byte is decoded once for
+//     all four steps.
+//   * Rotation runs on packed fp16 pairs of adjacent channels, scores are
+//     v_dot2_f32_f16 sums in fp32, the four same-step lanes reduce with DPP
+//     inside a quad, the softmax is online (base 2), and P*V accumulates in
+//     fp32 from fp16 codeword values.
+//   * Codebooks are rescaled by a power of two on load when their values would
+//     not fit fp16, and the scale is folded back into scores and outputs.
+#include "common.h"
+#include "kernels.h"
+
+namespace loopvq {
+
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ h2_t as_h2(uint32_t w) { return __builtin_bit_cast(h2_t, w); }
+
+// Power-of-two exponent s >= 0 with max_abs * 2^-s <= 2^lim.
+__device__ __forceinline__ int pow2_shift(float max_abs, int lim) {
+  if (!(max_abs > 0.f)) return 0;
+  const int e = ilogbf(max_abs) + 1;    // max_abs < 2^e
+  return e > lim ? e - lim : 0;
+}
+
+__device__ __forceinline__ uint32_t pack_h2(float a, float b) {
+  const _Float16 x = (_Float16)a, y = (_Float16)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
+
+__global__ __launch_bounds__(kDecodeThreads) void decode_g16t4_kernel(DecodeArgs a) {
+  constexpr int D = 128, HD = 64, G = 16, TC = 4, CPT = 32;
+  constexpr int LPT = 8, SPW = kWave / LPT, NW = kDecodeThreads / kWave;
+  __shared__ __attribute__((aligned(16))) uint4 s_k[256 * 2];
+  __shared__ __attribute__((aligned(16))) uint4 s_v[256 * 2];
+  __shared__ float s_red[NW][TC][D + 2];
+  __shared__ float s_amax[2][NW];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int sl = lane & 7, slot = lane >> 3;
+  const int hs = sl >> 2, g = sl & 3;           // step half, chunk group
+  const int split = blockIdx.x;
+  const int hq = blockIdx.y;
+  const int h = hq / a.gqa;
+  const int b = blockIdx.z / a.n_blk_serv;
+  const int beta = a.blk0 + (blockIdx.z - b * a.n_blk_serv);
+
+  // ---- codebooks -> LDS (fp16, step-major), with power-of-two range scaling
+  const int64_t cbo = ((int64_t)h * a.n_blk + beta) * a.K * G;
+  const uint16_t* gk = a.kcb + cbo;
+  const uint16_t* gv = a.vcb + cbo;
+  const int r = tid;   // one row per thread
+  float kx[G], vx[G];
+  float mk = 0.f, mv = 0.f;
+  if (r < a.K) {
+    const uint4* pk = reinterpret_cast<const uint4*>(gk + r * G);
+    const uint4* pv = reinterpret_cast<const uint4*>(gv + r * G);
+#pragma unroll
+    for (int c4 = 0; c4 < 2; ++c4) {
+      const uint4 x = pk[c4], y = pv[c4];
+      const uint32_t xw[4] = {x.x, x.y, x.z, x.w}, yw[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        kx[8 * c4 + 2 * w] = bf16lo(xw[w]);
+        kx[8 * c4 + 2 * w + 1] = bf16hi(xw[w]);
+        vx[8 * c4 + 2 * w] = bf16lo(yw[w]);
+        vx[8 * c4 + 2 * w + 1] = bf16hi(yw[w]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      mk = fmaxf(mk, fabsf(kx[u]));
+      mv = fmaxf(mv, fabsf(vx[u]));
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < G; ++u) kx[u] = vx[u] = 0.f;
+  }
+  for (int off = 32; off >= 1; off >>= 1) {
+    mk = fmaxf(mk, __shfl_xor(mk, off));
+    mv = fmaxf(mv, __shfl_xor(mv, off));
+  }
+  if (lane == 0) {
+    s_amax[0][wave] = mk;
+    s_amax[1][wave] = mv;
+  }
+  __syncthreads();
+  mk = fmaxf(fmaxf(s_amax[0][0], s_amax[0][1]), fmaxf(s_amax[0][2], s_amax[0][3]));
+  mv = fmaxf(fmaxf(s_amax[1][0], s_amax[1][1]), fmaxf(s_amax[1][2], s_amax[1][3]));
+  const int shk = pow2_shift(mk, 14), shv = pow2_shift(mv, 15);
+  {
+    const float sk = ldexpf(1.f, -shk), sv = ldexpf(1.f, -shv);
+    uint32_t kw[8], vw[8];
+#pragma unroll
+    for (int m = 0; m < TC; ++m) {
+#pragma unroll
+      for (int ip = 0; ip < 2; ++ip) {
+        // joint coordinate of channel i at step m is i*T_c + m
+        kw[2 * m + ip] = pack_h2(kx[(2 * ip) * TC + m] * sk, kx[(2 * ip + 1) * TC + m] * sk);
+        vw[2 * m + ip] = pack_h2(vx[(2 * ip) * TC + m] * sv, vx[(2 * ip + 1) * TC + m] * sv);
+      }
+    }
+    s_k[2 * r] = make_uint4(kw[0], kw[1], kw[2], kw[3]);
+    s_k[2 * r + 1] = make_uint4(kw[4], kw[5], kw[6], kw[7]);
+    s_v[2 * r] = make_uint4(vw[0], vw[1], vw[2], vw[3]);
+    s_v[2 * r + 1] = make_uint4(vw[4], vw[5], vw[6], vw[7]);
+  }
+
+  // ---- queries of this lane: steps 2hs+ml, chunk pairs k, partner p, channel pair ip
+  const int t_lo = max(a.step0, beta * TC), t_hi = min(a.step0 + a.n_steps, (beta + 1) * TC);
+  uint32_t qv[2][4][2][2];
+#pragma unroll
+  for (int ml = 0; ml < 2; ++ml) {
+    const int t = beta * TC + 2 * hs + ml;
+    const bool act = t >= t_lo && t < t_hi;
+    const uint16_t* qr = a.q + (((int64_t)b * a.Hq + hq) * a.n_steps + (act ? t - a.step0 : 0)) * D;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const int d0 = p * HD + 4 * (g + 4 * k);
+        const uint2 w = *reinterpret_cast<const uint2*>(qr + d0);
+        qv[ml][k][p][0] = act ? pack_h2(bf16lo(w.x), bf16hi(w.x)) : 0u;
+        qv[ml][k][p][1] = act ? pack_h2(bf16lo(w.y), bf16hi(w.y)) : 0u;
+      }
+    }
+  }
+  const float sscale = a.qscale * ldexpf(1.f, shk);
+
+  float mrow[2] = {-INFINITY, -INFINITY}, lrow[2] = {0.f, 0.f};
+  float acc[2][4][2][4];
+#pragma unroll
+  for (int ml = 0; ml < 2; ++ml)
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[ml][k][p][c] = 0.f;
+  __syncthreads();
+
+  int nb = a.N;
+  if (a.seq_len) nb = max(0, min(a.seq_len[b], a.N));
+  const int tok_lo = split * a.tok_per_split;
+  const int tok_hi = min(nb, tok_lo + a.tok_per_split);
+  const int n_sink = split == 0 ? a.n_s : 0;
+  const int64_t irow0 = (((int64_t)b * a.H + h) * a.n_blk + beta) * (int64_t)a.N_cap;
+  const int64_t sink0 = (((int64_t)b * a.H + h) * a.T + beta * TC) * (int64_t)a.n_s;
+  const uint16_t* rope16 = reinterpret_cast<const uint16_t*>(a.rope);
+  const float ksc = ldexpf(1.f, -shk), vsc = ldexpf(1.f, -shv);
+
+  // One token (or sink) of this lane's slot: scores, online softmax, P*V.
+  // Kw: the 8 K codeword halves (chunks g+4k, then their RoPE partners);
+  // vi: V codeword byte offsets (or sink values when vsink is set).
+  // Scores of one token (or sink) for this lane's two steps: RoPE on packed
+  // fp16 channel pairs, v_dot2 into fp32, sum over the four same-step lanes.
+  auto scores = [&](const uint4 (&Kw)[8], const uint4 (&CS)[4], float (&sc)[2]) {
+    sc[0] = sc[1] = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t cw[2] = {CS[k].x, CS[k].y}, sw[2] = {CS[k].z, CS[k].w};
+      const uint32_t k1w[4] = {Kw[k].x, Kw[k].y, Kw[k].z, Kw[k].w};
+      const uint32_t k2w[4] = {Kw[k + 4].x, Kw[k + 4].y, Kw[k + 4].z, Kw[k + 4].w};
+#pragma unroll
+      for (int ml = 0; ml < 2; ++ml) {
+#pragma unroll
+        for (int ip = 0; ip < 2; ++ip) {
+          const h2_t c2 = as_h2(cw[ip]), s2 = as_h2(sw[ip]);
+          const h2_t x1 = as_h2(k1w[2 * ml + ip]), x2 = as_h2(k2w[2 * ml + ip]);
+          const h2_t r1 = x1 * c2 - x2 * s2;
+          const h2_t r2 = x2 * c2 + x1 * s2;
+          sc[ml] = __builtin_amdgcn_fdot2(r1, as_h2(qv[ml][k][0][ip]), sc[ml], false);
+          sc[ml] = __builtin_amdgcn_fdot2(r2, as_h2(qv[ml][k][1][ip]), sc[ml], false);
+        }
+      }
+    }
+#pragma unroll
+    for (int ml = 0; ml < 2; ++ml) sc[ml] = group_sum<4>(sc[ml]) * sscale;
+  };
+  // Online softmax (base 2) and P*V.  The running maximum is only moved when a
+  // score exceeds it by more than 8 (a factor 256): the weights stay within
+  // fp32 range and the rescale of the accumulators becomes rare.
+  auto accumulate = [&](const float (&sc)[2], const uint4 (&V)[8], bool valid) {
+    if (!valid) return;
+#pragma unroll
+    for (int ml = 0; ml < 2; ++ml) {
+      const float s = sc[ml];
+      if (s > mrow[ml] + 8.f) {
+        const float alpha = __builtin_amdgcn_exp2f(mrow[ml] - s);
+        lrow[ml] *= alpha;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+#pragma unroll
+          for (int p = 0; p < 2; ++p)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc[ml][k][p][c] *= alpha;
+        mrow[ml] = s;
+      }
+      const float pr = __builtin_amdgcn_exp2f(s - mrow[ml]);
+      lrow[ml] += pr;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          const uint4 vq = V[k + 4 * p];
+          const uint32_t vw[4] = {vq.x, vq.y, vq.z, vq.w};
+#pragma unroll
+          for (int ip = 0; ip < 2; ++ip) {
+            const h2_t v2 = as_h2(vw[2 * ml + ip]);
+            acc[ml][k][p][2 * ip] = fmaf(pr, (float)v2.x, acc[ml][k][p][2 * ip]);
+            acc[ml][k][p][2 * ip + 1] = fmaf(pr, (float)v2.y, acc[ml][k][p][2 * ip + 1]);
+          }
+        }
+      }
+    }
+  };
+  auto load_cs = [&](int pos, uint4 (&CS)[4]) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) CS[k] = reinterpret_cast<const uint4*>(rope16 + (int64_t)pos * D)[g + 4 * k];
+  };
+
+  // Sinks (split 0 only): values straight from the bf16 rows, scaled like the codebooks.
+  for (int base = 0; base < n_sink; base += NW * SPW) {
+    const int item = base + wave * SPW + slot;
+    const bool valid = item < n_sink;
+    const int it = valid ? item : 0;
+    uint4 Kw[8], Vs[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int k = c & 3, p = c >> 2;
+      const int d0 = p * HD + 4 * (g + 4 * k);
+      uint32_t kw[4], vw[4];
+#pragma unroll
+      for (int ml = 0; ml < 2; ++ml) {
+        const int m = 2 * hs + ml;
+        const uint2 x = *reinterpret_cast<const uint2*>(a.sk + (sink0 + (int64_t)m * a.n_s + it) * D + d0);
+        const uint2 y = *reinterpret_cast<const uint2*>(a.sv + (sink0 + (int64_t)m * a.n_s + it) * D + d0);
+        kw[2 * ml + 0] = pack_h2(bf16lo(x.x) * ksc, bf16hi(x.x) * ksc);
+        kw[2 * ml + 1] = pack_h2(bf16lo(x.y) * ksc, bf16hi(x.y) * ksc);
+        vw[2 * ml + 0] = pack_h2(bf16lo(y.x) * vsc, bf16hi(y.x) * vsc);
+        vw[2 * ml + 1] = pack_h2(bf16lo(y.y) * vsc, bf16hi(y.y) * vsc);
+      }
+      Kw[c] = make_uint4(kw[0], kw[1], kw[2], kw[3]);
+      Vs[c] = make_uint4(vw[0], vw[1], vw[2], vw[3]);
+    }
+    uint4 CS[4];
+    load_cs(it, CS);
+    float sc[2];
+    scores(Kw, CS, sc);
+    accumulate(sc, Vs, valid);
+  }
+
+  // Context tokens.  The index rows and the sin/cos quads of the next
+  // iteration are loaded as soon as the current ones are consumed.
+  const int n_tok = max(0, tok_hi - tok_lo);
+  const int my = wave * SPW + slot;
+  auto row_ptrs = [&](int base, const uint4*& kr, const uint4*& vr, int& jj) {
+    const int it = base + my;
+    jj = tok_lo + (it < n_tok ? it : n_tok - 1);   // always a real row
+    kr = reinterpret_cast<const uint4*>(a.kidx + (irow0 + jj) * CPT);
+    vr = reinterpret_cast<const uint4*>(a.vidx + (irow0 + jj) * CPT);
+  };
+  uint4 rows[4];
+  uint4 CS[4];
+  if (n_tok > 0) {
+    const uint4 *kr, *vr;
+    int jj;
+    row_ptrs(0, kr, vr, jj);
+    rows[0] = kr[0];
+    rows[1] = kr[1];
+    rows[2] = vr[0];
+    rows[3] = vr[1];
+    load_cs(a.n_s + jj, CS);
+  }
+  for (int base = 0; base < n_tok; base += NW * SPW) {
+    const bool valid = base + my < n_tok;
+    uint32_t ka[8], va[8];
+    {
+      const uint32_t kd[8] = {rows[0].x, rows[0].y, rows[0].z, rows[0].w, rows[1].x, rows[1].y, rows[1].z, rows[1].w};
+      const uint32_t vd[8] = {rows[2].x, rows[2].y, rows[2].z, rows[2].w, rows[3].x, rows[3].y, rows[3].z, rows[3].w};
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        // chunk g + 4c (c < 4) or the RoPE partner g + 4(c-4) + 16 is byte g of word c
+        ka[c] = 2 * __builtin_amdgcn_ubfe(kd[c], 8 * g, 8) + hs;
+        va[c] = 2 * __builtin_amdgcn_ubfe(vd[c], 8 * g, 8) + hs;
+      }
+    }
+    // Unconditional (clamped) next loads keep the prefetch in place without copies.
+    int jn = 0;
+    {
+      const uint4 *kr, *vr;
+      row_ptrs(base + NW * SPW, kr, vr, jn);
+      rows[0] = kr[0];
+      rows[1] = kr[1];
+      rows[2] = vr[0];
+      rows[3] = vr[1];
+    }
+    uint4 Kw[8], V[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) Kw[c] = s_k[ka[c]];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) V[c] = s_v[va[c]];
+    float sc[2];
+    scores(Kw, CS, sc);
+    load_cs(a.n_s + jn, CS);
+    accumulate(sc, V, valid);
+  }
+
+  // ---- merge the 8 slots of the wave (lanes with equal sl)
+#pragma unroll
+  for (int off = LPT; off < kWave; off <<= 1) {
+#pragma unroll
+    for (int ml = 0; ml < 2; ++ml) {
+      const float om = __shfl_xor(mrow[ml], off);
+      const float ol = __shfl_xor(lrow[ml], off);
+      const float mm = fmaxf(mrow[ml], om);
+      const float a1 = mrow[ml] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mrow[ml] - mm);
+      const float a2 = om == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(om - mm);
+      lrow[ml] = lrow[ml] * a1 + ol * a2;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const float oa = __shfl_xor(acc[ml][k][p][c], off);
+            acc[ml][k][p][c] = acc[ml][k][p][c] * a1 + oa * a2;
+          }
+      mrow[ml] = mm;
+    }
+  }
+  if (slot == 0) {
+#pragma unroll
+    for (int ml = 0; ml < 2; ++ml) {
+      const int m = 2 * hs + ml;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) s_red[wave][m][p * HD + 4 * (g + 4 * k) + c] = acc[ml][k][p][c];
+      if (g == 0) {
+        s_red[wave][m][D] = mrow[ml];
+        s_red[wave][m][D + 1] = lrow[ml];
+      }
+    }
+  }
+  __syncthreads();
+  const float osc = ldexpf(1.f, shv);
+  for (int x = tid; x < TC * D; x += kDecodeThreads) {
+    const int m = x / D, d = x - m * D;
+    const int t = beta * TC + m;
+    if (t < t_lo || t >= t_hi) continue;
+    float mm = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) mm = fmaxf(mm, s_red[w][m][D]);
+    float num = 0.f, den = 0.f;
+    if (mm != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float mw = s_red[w][m][D];
+        const float f = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - mm);
+        num += f * s_red[w][m][d];
+        den += f * s_red[w][m][D + 1];
+      }
+    }
+    float* dst = a.ws + ((((int64_t)b * a.Hq + hq) * a.n_steps + (t - a.step0)) * a.n_split + split) * (D + 1);
+    dst[d] = den > 0.f ? num / den * osc : 0.f;
+    if (d == 0) dst[D] = den > 0.f ? (mm + __log2f(den)) * 0.69314718055994531f : -INFINITY;
+  }
+}
+
+hipError_t launch_decode_g16t4(const DecodeArgs& a, hipStream_t s) {
+  dim3 grid(a.n_split, a.Hq, a.B * a.n_blk_serv);
+  hipLaunchKernelGGL(decode_g16t4_kernel, grid, dim3(kDecodeThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace loopvq

@@ -19,25 +19,6 @@
 
 namespace loopvq {
 
-// fp64 -> fp16 bits, round to nearest even, for non-negative finite v.
-__device__ __forceinline__ uint16_t f64_to_f16_rne(double v) {
-  _Float16 h0 = (_Float16)(float)v;
-  uint16_t b0;
-  __builtin_memcpy(&b0, &h0, 2);
-  uint16_t best = b0;
-  double bestd = fabs(v - f16_bits_to_f64(b0));
-  for (int k = -1; k <= 1; k += 2) {
-    int c = (int)b0 + k;
-    if (c < 0 || c >= 0x7c00) continue;
-    double d = fabs(v - f16_bits_to_f64((uint16_t)c));
-    if (d < bestd || (d == bestd && (c & 1) == 0 && (best & 1) != 0)) {
-      best = (uint16_t)c;
-      bestd = d;
-    }
-  }
-  return best;
-}
-
 // Per-(token, step) RMS of the layer's raw keys over all heads and channels,
 // in fp64, rounded to fp16 (review section 3.3 / appendix B).  One wave per
 // token; lane l covers channels 2l, 2l+1 of every head.

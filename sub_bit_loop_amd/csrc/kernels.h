@@ -38,7 +38,7 @@ struct DecodeArgs {
   const int16_t* perm;
   const uint16_t* sigma;      // fp16 [B][sig_cap][T]
   int32_t sig_cap;
-  const float* rope;          // fp32 [n_pos][D/2][2]
+  const void* rope;           // fp16 [n_pos][D/8][8] quads (cos x4, sin x4)
   float* ws;                  // partials [B][Hq][n_steps][n_split][D+1]
   int32_t B, H, Hq, T, n_blk, K, N, N_cap, n_s, step0, n_steps, n_split, gqa, blk0, n_blk_serv;
   int32_t tok_per_split;
@@ -58,7 +58,8 @@ hipError_t launch_encode(int G, int TC, bool tasq, const EncodeArgs& a, int B, h
 hipError_t launch_sigma(const SigmaArgs& a, int B, hipStream_t s);
 hipError_t launch_decode(int G, int TC, bool tasq, const DecodeArgs& a, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
-hipError_t launch_rope_table(double theta, int D, int n_pos, float* table, hipStream_t s);
+hipError_t launch_rope_table(double theta, int D, int n_pos, void* table, hipStream_t s);
+hipError_t launch_decode_g16t4(const DecodeArgs& a, hipStream_t s);
 
 constexpr int kDecodeThreads = 256;
 constexpr int kEncodeThreads = 256;

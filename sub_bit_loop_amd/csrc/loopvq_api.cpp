@@ -152,11 +152,11 @@ loopvq_status loopvq_encode(const loopvq_geom* g, const void* x, const int64_t x
   return LOOPVQ_OK;
 }
 
-loopvq_status loopvq_rope_table(float theta, int32_t D, int32_t n_pos, float* table, void* stream) {
+loopvq_status loopvq_rope_table(float theta, int32_t D, int32_t n_pos, void* table, void* stream) {
   g_err[0] = 0;
   if (!table) return fail(LOOPVQ_EINVAL, "table is NULL");
   if (n_pos < 1) return fail(LOOPVQ_EINVAL, "n_pos=%d must be >= 1", n_pos);
-  if (D < 2 || D % 2) return fail(LOOPVQ_EINVAL, "D=%d must be even and >= 2", D);
+  if (D < 8 || D % 8) return fail(LOOPVQ_EINVAL, "D=%d must be a positive multiple of 8", D);
   if (!(theta > 0.f) || !std::isfinite(theta)) return fail(LOOPVQ_EINVAL, "theta must be positive");
   hipError_t e = loopvq::launch_rope_table((double)theta, D, n_pos, table, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "rope table launch");
@@ -188,7 +188,7 @@ loopvq_status loopvq_decode_attn(const loopvq_geom* g, const void* q, int32_t st
                                  int32_t N_cap, const void* k_cb, const void* v_cb,
                                  const void* sink_k, const void* sink_v, int32_t n_s,
                                  int32_t B, int32_t N, const int32_t* seq_len,
-                                 const loopvq_pretransform* pt, const float* rope_table,
+                                 const loopvq_pretransform* pt, const void* rope_table,
                                  int32_t n_pos, float* out, float* lse, void* workspace,
                                  size_t workspace_bytes, void* stream) {
   g_err[0] = 0;
@@ -202,8 +202,12 @@ loopvq_status loopvq_decode_attn(const loopvq_geom* g, const void* q, int32_t st
   if (n_s > 0 && (!sink_k || !sink_v)) return fail(LOOPVQ_EINVAL, "NULL sink pointer with n_s=%d", n_s);
   if ((long long)n_s + N > n_pos)
     return fail(LOOPVQ_EINVAL, "rope table has %d positions, need n_s + N = %lld", n_pos, (long long)n_s + N);
-  if (reinterpret_cast<uintptr_t>(k_cb) % 16 || reinterpret_cast<uintptr_t>(v_cb) % 16)
-    return fail(LOOPVQ_EINVAL, "codebooks must be 16-byte aligned");
+  {
+    const void* al[] = {q, k_idx, v_idx, k_cb, v_cb, sink_k, sink_v, rope_table, workspace};
+    for (const void* p : al)
+      if (reinterpret_cast<uintptr_t>(p) % 16)
+        return fail(LOOPVQ_EINVAL, "tensor pointers must be 16-byte aligned");
+  }
   st = check_pt(pt, B, N, false);
   if (st != LOOPVQ_OK) return st;
   const DecodePlan p = plan_decode(g, B, N, step0, n_steps);
@@ -245,7 +249,11 @@ loopvq_status loopvq_decode_attn(const loopvq_geom* g, const void* q, int32_t st
   a.n_blk_serv = p.n_blk_serv;
   a.tok_per_split = p.tok_per_split;
   a.qscale = (float)(1.4426950408889634 / std::sqrt((double)g->D));
-  hipError_t e = loopvq::launch_decode(g->G, g->T_c, pt != nullptr, a, s);
+  // 0.5-bit loop layout without pre-transform: the specialised kernel;
+  // every other geometry: the generic one.
+  hipError_t e = (g->G == 16 && g->T_c == 4 && pt == nullptr)
+                     ? loopvq::launch_decode_g16t4(a, s)
+                     : loopvq::launch_decode(g->G, g->T_c, pt != nullptr, a, s);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   loopvq::MergeArgs ma{};
   ma.ws = a.ws;

@@ -82,6 +82,7 @@ def test_rope_table_argument_errors():
     P = ctypes.c_void_p
     assert lib.loopvq_rope_table(1e4, 128, 10, P(0), None) == -1
     assert lib.loopvq_rope_table(1e4, 127, 10, P(16), None) == -1
+    assert lib.loopvq_rope_table(1e4, 132, 10, P(16), None) == -1
     assert lib.loopvq_rope_table(1e4, 128, 0, P(16), None) == -1
     assert lib.loopvq_rope_table(-1.0, 128, 10, P(16), None) == -1
 
