@@ -30,7 +30,7 @@ UNIT = "context tokens/s per loop block"
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in ("encode.hip", "decode.hip", "common.h", "kernels.h"):
+    for f in ("encode.hip", "decode.hip", "decode_fast.hip", "common.h", "kernels.h"):
         with open(os.path.join(ROOT, "sub_bit_loop_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -114,6 +114,8 @@ def main():
     ap.add_argument("--config", type=int, default=2, help="workload index 1-4 (single layer)")
     ap.add_argument("--cpu-tokens", type=int, default=1024, help="context tokens in the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the LoopVQ path has no multi-GPU step in this build "
@@ -161,6 +163,14 @@ def main():
         if ev is not None:
             ev[3].record()
 
+    if args.copy_calibration:
+        # one elementwise kernel that reads 1 GiB and writes 1 GiB
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
