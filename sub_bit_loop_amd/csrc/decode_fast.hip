@@ -43,6 +43,11 @@ __device__ __forceinline__ uint32_t pack_h2(float a, float b) {
   return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
 }
 
+// P*V accumulates in packed fp16 for kFlush tokens per lane and is then added
+// into fp32.  With the running max allowed to lag by at most kLag (weights
+// <= 2^kLag) and |v| <= 2^kVLim, a partial sum stays below 2^(3+7+4) = 16384.
+constexpr int kFlush = 16, kLag = 3, kVLim = 7;
+
 __global__ __launch_bounds__(kDecodeThreads) void decode_g16t4_kernel(DecodeArgs a) {
   constexpr int D = 128, HD = 64, G = 16, TC = 4, CPT = 32;
   constexpr int LPT = 8, SPW = kWave / LPT, NW = kDecodeThreads / kWave;
@@ -102,7 +107,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_g16t4_kernel(DecodeArgs
   __syncthreads();
   mk = fmaxf(fmaxf(s_amax[0][0], s_amax[0][1]), fmaxf(s_amax[0][2], s_amax[0][3]));
   mv = fmaxf(fmaxf(s_amax[1][0], s_amax[1][1]), fmaxf(s_amax[1][2], s_amax[1][3]));
-  const int shk = pow2_shift(mk, 14), shv = pow2_shift(mv, 15);
+  const int shk = pow2_shift(mk, 14), shv = pow2_shift(mv, kVLim);
   {
     const float sk = ldexpf(1.f, -shk), sv = ldexpf(1.f, -shv);
     uint32_t kw[8], vw[8];
@@ -192,27 +197,54 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_g16t4_kernel(DecodeArgs
 #pragma unroll
     for (int ml = 0; ml < 2; ++ml) sc[ml] = group_sum<4>(sc[ml]) * sscale;
   };
-  // Online softmax (base 2) and P*V.  The running maximum is only moved when a
-  // score exceeds it by more than 8 (a factor 256): the weights stay within
-  // fp32 range and the rescale of the accumulators becomes rare.
+  // Online softmax (base 2) and P*V.  The running maximum moves only when a
+  // score exceeds it by more than kLag, which keeps rescaling rare.
+  uint32_t acc16[2][4][2][2];
+#pragma unroll
+  for (int ml = 0; ml < 2; ++ml)
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) acc16[ml][k][p][0] = acc16[ml][k][p][1] = 0u;
+  auto flush = [&]() {
+#pragma unroll
+    for (int ml = 0; ml < 2; ++ml)
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+#pragma unroll
+          for (int ip = 0; ip < 2; ++ip) {
+            const h2_t v = as_h2(acc16[ml][k][p][ip]);
+            acc[ml][k][p][2 * ip] += (float)v.x;
+            acc[ml][k][p][2 * ip + 1] += (float)v.y;
+            acc16[ml][k][p][ip] = 0u;
+          }
+  };
   auto accumulate = [&](const float (&sc)[2], const uint4 (&V)[8], bool valid) {
     if (!valid) return;
 #pragma unroll
     for (int ml = 0; ml < 2; ++ml) {
       const float s = sc[ml];
-      if (s > mrow[ml] + 8.f) {
+      if (s > mrow[ml] + (float)kLag) {
         const float alpha = __builtin_amdgcn_exp2f(mrow[ml] - s);
+        const h2_t a2 = {(_Float16)alpha, (_Float16)alpha};
         lrow[ml] *= alpha;
 #pragma unroll
         for (int k = 0; k < 4; ++k)
 #pragma unroll
-          for (int p = 0; p < 2; ++p)
+          for (int p = 0; p < 2; ++p) {
 #pragma unroll
             for (int c = 0; c < 4; ++c) acc[ml][k][p][c] *= alpha;
+#pragma unroll
+            for (int ip = 0; ip < 2; ++ip)
+              acc16[ml][k][p][ip] = __builtin_bit_cast(uint32_t, as_h2(acc16[ml][k][p][ip]) * a2);
+          }
         mrow[ml] = s;
       }
       const float pr = __builtin_amdgcn_exp2f(s - mrow[ml]);
       lrow[ml] += pr;
+      const h2_t p2 = {(_Float16)pr, (_Float16)pr};
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
 #pragma unroll
@@ -222,8 +254,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_g16t4_kernel(DecodeArgs
 #pragma unroll
           for (int ip = 0; ip < 2; ++ip) {
             const h2_t v2 = as_h2(vw[2 * ml + ip]);
-            acc[ml][k][p][2 * ip] = fmaf(pr, (float)v2.x, acc[ml][k][p][2 * ip]);
-            acc[ml][k][p][2 * ip + 1] = fmaf(pr, (float)v2.y, acc[ml][k][p][2 * ip + 1]);
+            acc16[ml][k][p][ip] = __builtin_bit_cast(uint32_t, v2 * p2 + as_h2(acc16[ml][k][p][ip]));
           }
         }
       }
@@ -263,6 +294,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_g16t4_kernel(DecodeArgs
     float sc[2];
     scores(Kw, CS, sc);
     accumulate(sc, Vs, valid);
+    flush();
   }
 
   // Context tokens.  The index rows and the sin/cos quads of the next
@@ -287,6 +319,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_g16t4_kernel(DecodeArgs
     rows[3] = vr[1];
     load_cs(a.n_s + jj, CS);
   }
+  int since_flush = 0;
   for (int base = 0; base < n_tok; base += NW * SPW) {
     const bool valid = base + my < n_tok;
     uint32_t ka[8], va[8];
@@ -319,7 +352,12 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_g16t4_kernel(DecodeArgs
     scores(Kw, CS, sc);
     load_cs(a.n_s + jn, CS);
     accumulate(sc, V, valid);
+    if (++since_flush == kFlush) {
+      flush();
+      since_flush = 0;
+    }
   }
+  flush();
 
   // ---- merge the 8 slots of the wave (lanes with equal sl)
 #pragma unroll

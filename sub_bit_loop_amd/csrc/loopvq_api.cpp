@@ -72,7 +72,7 @@ DecodePlan plan_decode(const loopvq_geom* g, int B, int N, int step0, int n_step
   const int blk1 = (step0 + n_steps - 1) / g->T_c;
   p.n_blk_serv = blk1 - p.blk0 + 1;
   const long long wgs = (long long)B * g->n_q_heads * p.n_blk_serv;
-  const int target = 2048;
+  const int target = 512;   // about one resident round of workgroups (2 per CU)
   long long ns = (target + wgs - 1) / wgs;
   const long long max_by_tokens = N > 0 ? (N + 255) / 256 : 1;
   if (ns > max_by_tokens) ns = max_by_tokens;
