@@ -1,6 +1,6 @@
-// LoopVQ fused decode attention, specialised for the 0.5-bit loop layout:
-// G = 16, T_c = 4 (c = 4 channels per step per code), D = 128, no channel
-// pre-transform.
+// LoopVQ fused decode attention, specialised for blocks of T_c = 4 loop steps
+// with c = 4 (G = 16, 0.5 bit) or c = 8 (G = 32, 0.25 bit) channels per step
+// per code, D = 128, no channel pre-transform.
 //
 // LoopVQ review (arXiv 2611.05304), section 3.4 step 3 (codebook on chip,
 // lookup by index, RoPE from a precomputed table after dequant, Flash-
@@ -8,20 +8,23 @@
 // i*T_c + m of the shared codeword).
 //
 // Layout choices for gfx950:
-//   * Both codebooks sit in LDS as fp16, step-major inside a codeword:
-//     word (m, i) at 8m + 2i bytes, 32 bytes per codeword.  Bytes [16h, 16h+16)
-//     hold steps 2h and 2h+1 for all four channels, so one ds_read_b128
-//     returns what one lane needs for two steps.
-//   * A token is served by 8 lanes: lane (h, g) takes steps {2h, 2h+1} and
-//     chunk pairs (q, q + 16) for q = g, g+4, g+8, g+12, i.e. the channel
-//     pairs that RoPE rotates together.  Every index byte is decoded once for
-//     all four steps.
+//   * Both codebooks sit in LDS as fp16, step-major inside a codeword (word
+//     (m, channel pair) at m*2c + 4*pair bytes).  The first half of a codeword
+//     holds steps 0-1, the second steps 2-3; a lane reads the half of its two
+//     steps with c/4 ds_read_b128.
+//   * A token is served by 8 lanes: lane (h, g) takes steps {2h, 2h+1} and the
+//     chunk pairs (q, q + D/(2c)) for q = g, g+4, ..., i.e. exactly the
+//     channel pairs that RoPE rotates together.  Every index byte is decoded
+//     once for all four steps.
 //   * Rotation runs on packed fp16 pairs of adjacent channels, scores are
 //     v_dot2_f32_f16 sums in fp32, the four same-step lanes reduce with DPP
-//     inside a quad, the softmax is online (base 2), and P*V accumulates in
-//     fp32 from fp16 codeword values.
-//   * Codebooks are rescaled by a power of two on load when their values would
-//     not fit fp16, and the scale is folded back into scores and outputs.
+//     inside a quad, the softmax is online (base 2) and P*V accumulates packed
+//     fp16 pairs that are flushed into fp32 every kFlush tokens.
+//   * Codebooks are rescaled by a power of two on load so that keys fit fp16
+//     and values stay below 2^kVLim; the scales are folded back into scores and
+//     outputs.
+// One workgroup serves one (batch, q-head, block, context split); q-heads of a
+// GQA group gather the same rows in separate workgroups.
 #include "common.h"
 #include "kernels.h"
 
@@ -48,11 +51,18 @@ __device__ __forceinline__ uint32_t pack_h2(float a, float b) {
 // <= 2^kLag) and |v| <= 2^kVLim, a partial sum stays below 2^(3+7+4) = 16384.
 constexpr int kFlush = 16, kLag = 3, kVLim = 7;
 
-__global__ __launch_bounds__(kDecodeThreads) void decode_g16t4_kernel(DecodeArgs a) {
-  constexpr int D = 128, HD = 64, G = 16, TC = 4, CPT = 32;
+template <int C>
+__global__ __launch_bounds__(kDecodeThreads) void decode_fast_kernel(DecodeArgs a) {
+  constexpr int D = 128, HD = 64, TC = 4, G = C * TC, CPT = D / C;
+  constexpr int NP = HD / C;          // RoPE chunk pairs per token (16 or 8)
+  constexpr int NPL = NP / 4;         // chunk pairs per lane (4 or 2)
+  constexpr int NCW = 2 * NPL;        // codewords gathered per lane per token
+  constexpr int QW = C / 4;           // uint4 per codeword half (two steps)
+  constexpr int DW = C / 2;           // dwords per step of a codeword
+  constexpr int RW = CPT / 16;        // uint4 per index row
   constexpr int LPT = 8, SPW = kWave / LPT, NW = kDecodeThreads / kWave;
-  __shared__ __attribute__((aligned(16))) uint4 s_k[256 * 2];
-  __shared__ __attribute__((aligned(16))) uint4 s_v[256 * 2];
+  __shared__ __attribute__((aligned(16))) uint4 s_k[256 * 2 * QW];
+  __shared__ __attribute__((aligned(16))) uint4 s_v[256 * 2 * QW];
   __shared__ float s_red[NW][TC][D + 2];
   __shared__ float s_amax[2][NW];
 
@@ -67,16 +77,14 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_g16t4_kernel(DecodeArgs
 
   // ---- codebooks -> LDS (fp16, step-major), with power-of-two range scaling
   const int64_t cbo = ((int64_t)h * a.n_blk + beta) * a.K * G;
-  const uint16_t* gk = a.kcb + cbo;
-  const uint16_t* gv = a.vcb + cbo;
   const int r = tid;   // one row per thread
   float kx[G], vx[G];
   float mk = 0.f, mv = 0.f;
   if (r < a.K) {
-    const uint4* pk = reinterpret_cast<const uint4*>(gk + r * G);
-    const uint4* pv = reinterpret_cast<const uint4*>(gv + r * G);
+    const uint4* pk = reinterpret_cast<const uint4*>(a.kcb + cbo + r * G);
+    const uint4* pv = reinterpret_cast<const uint4*>(a.vcb + cbo + r * G);
 #pragma unroll
-    for (int c4 = 0; c4 < 2; ++c4) {
+    for (int c4 = 0; c4 < G / 8; ++c4) {
       const uint4 x = pk[c4], y = pv[c4];
       const uint32_t xw[4] = {x.x, x.y, x.z, x.w}, yw[4] = {y.x, y.y, y.z, y.w};
 #pragma unroll
@@ -110,53 +118,60 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_g16t4_kernel(DecodeArgs
   const int shk = pow2_shift(mk, 14), shv = pow2_shift(mv, kVLim);
   {
     const float sk = ldexpf(1.f, -shk), sv = ldexpf(1.f, -shv);
-    uint32_t kw[8], vw[8];
+    uint32_t kw[2 * C], vw[2 * C];   // [m][pair]: step m, channels (2*pair, 2*pair+1)
 #pragma unroll
     for (int m = 0; m < TC; ++m) {
 #pragma unroll
-      for (int ip = 0; ip < 2; ++ip) {
+      for (int ip = 0; ip < DW; ++ip) {
         // joint coordinate of channel i at step m is i*T_c + m
-        kw[2 * m + ip] = pack_h2(kx[(2 * ip) * TC + m] * sk, kx[(2 * ip + 1) * TC + m] * sk);
-        vw[2 * m + ip] = pack_h2(vx[(2 * ip) * TC + m] * sv, vx[(2 * ip + 1) * TC + m] * sv);
+        kw[m * DW + ip] = pack_h2(kx[(2 * ip) * TC + m] * sk, kx[(2 * ip + 1) * TC + m] * sk);
+        vw[m * DW + ip] = pack_h2(vx[(2 * ip) * TC + m] * sv, vx[(2 * ip + 1) * TC + m] * sv);
       }
     }
-    s_k[2 * r] = make_uint4(kw[0], kw[1], kw[2], kw[3]);
-    s_k[2 * r + 1] = make_uint4(kw[4], kw[5], kw[6], kw[7]);
-    s_v[2 * r] = make_uint4(vw[0], vw[1], vw[2], vw[3]);
-    s_v[2 * r + 1] = make_uint4(vw[4], vw[5], vw[6], vw[7]);
+#pragma unroll
+    for (int u = 0; u < 2 * QW; ++u) {
+      s_k[r * 2 * QW + u] = make_uint4(kw[4 * u], kw[4 * u + 1], kw[4 * u + 2], kw[4 * u + 3]);
+      s_v[r * 2 * QW + u] = make_uint4(vw[4 * u], vw[4 * u + 1], vw[4 * u + 2], vw[4 * u + 3]);
+    }
   }
 
   // ---- queries of this lane: steps 2hs+ml, chunk pairs k, partner p, channel pair ip
   const int t_lo = max(a.step0, beta * TC), t_hi = min(a.step0 + a.n_steps, (beta + 1) * TC);
-  uint32_t qv[2][4][2][2];
+  uint32_t qv[2][NPL][2][DW];
 #pragma unroll
   for (int ml = 0; ml < 2; ++ml) {
     const int t = beta * TC + 2 * hs + ml;
     const bool act = t >= t_lo && t < t_hi;
     const uint16_t* qr = a.q + (((int64_t)b * a.Hq + hq) * a.n_steps + (act ? t - a.step0 : 0)) * D;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < NPL; ++k) {
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
-        const int d0 = p * HD + 4 * (g + 4 * k);
-        const uint2 w = *reinterpret_cast<const uint2*>(qr + d0);
-        qv[ml][k][p][0] = act ? pack_h2(bf16lo(w.x), bf16hi(w.x)) : 0u;
-        qv[ml][k][p][1] = act ? pack_h2(bf16lo(w.y), bf16hi(w.y)) : 0u;
+        const int d0 = p * HD + C * (g + 4 * k);
+#pragma unroll
+        for (int ip = 0; ip < DW; ++ip) {
+          const uint32_t w = *reinterpret_cast<const uint32_t*>(qr + d0 + 2 * ip);
+          qv[ml][k][p][ip] = act ? pack_h2(bf16lo(w), bf16hi(w)) : 0u;
+        }
       }
     }
   }
   const float sscale = a.qscale * ldexpf(1.f, shk);
 
   float mrow[2] = {-INFINITY, -INFINITY}, lrow[2] = {0.f, 0.f};
-  float acc[2][4][2][4];
+  float acc[2][NPL][2][C];
+  uint32_t acc16[2][NPL][2][DW];
 #pragma unroll
   for (int ml = 0; ml < 2; ++ml)
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
+    for (int k = 0; k < NPL; ++k)
 #pragma unroll
-      for (int p = 0; p < 2; ++p)
+      for (int p = 0; p < 2; ++p) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) acc[ml][k][p][c] = 0.f;
+        for (int c = 0; c < C; ++c) acc[ml][k][p][c] = 0.f;
+#pragma unroll
+        for (int ip = 0; ip < DW; ++ip) acc16[ml][k][p][ip] = 0u;
+      }
   __syncthreads();
 
   int nb = a.N;
@@ -169,24 +184,20 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_g16t4_kernel(DecodeArgs
   const uint16_t* rope16 = reinterpret_cast<const uint16_t*>(a.rope);
   const float ksc = ldexpf(1.f, -shk), vsc = ldexpf(1.f, -shv);
 
-  // One token (or sink) of this lane's slot: scores, online softmax, P*V.
-  // Kw: the 8 K codeword halves (chunks g+4k, then their RoPE partners);
-  // vi: V codeword byte offsets (or sink values when vsink is set).
-  // Scores of one token (or sink) for this lane's two steps: RoPE on packed
-  // fp16 channel pairs, v_dot2 into fp32, sum over the four same-step lanes.
-  auto scores = [&](const uint4 (&Kw)[8], const uint4 (&CS)[4], float (&sc)[2]) {
+  // Codeword halves of one token: Kw[c] for c < NPL are chunks g + 4c, the
+  // rest their RoPE partners; each half is C dwords (two steps x DW words).
+  // CS[k][u]: sin/cos quads of chunk g + 4k (quad u covers 4 frequencies).
+  auto scores = [&](const uint32_t (&Kw)[NCW][C], const uint4 (&CS)[NPL][QW], float (&sc)[2]) {
     sc[0] = sc[1] = 0.f;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t cw[2] = {CS[k].x, CS[k].y}, sw[2] = {CS[k].z, CS[k].w};
-      const uint32_t k1w[4] = {Kw[k].x, Kw[k].y, Kw[k].z, Kw[k].w};
-      const uint32_t k2w[4] = {Kw[k + 4].x, Kw[k + 4].y, Kw[k + 4].z, Kw[k + 4].w};
+    for (int k = 0; k < NPL; ++k) {
 #pragma unroll
       for (int ml = 0; ml < 2; ++ml) {
 #pragma unroll
-        for (int ip = 0; ip < 2; ++ip) {
-          const h2_t c2 = as_h2(cw[ip]), s2 = as_h2(sw[ip]);
-          const h2_t x1 = as_h2(k1w[2 * ml + ip]), x2 = as_h2(k2w[2 * ml + ip]);
+        for (int ip = 0; ip < DW; ++ip) {
+          const uint4 q4 = CS[k][ip >> 1];
+          const h2_t c2 = as_h2((ip & 1) ? q4.y : q4.x), s2 = as_h2((ip & 1) ? q4.w : q4.z);
+          const h2_t x1 = as_h2(Kw[k][ml * DW + ip]), x2 = as_h2(Kw[k + NPL][ml * DW + ip]);
           const h2_t r1 = x1 * c2 - x2 * s2;
           const h2_t r2 = x2 * c2 + x1 * s2;
           sc[ml] = __builtin_amdgcn_fdot2(r1, as_h2(qv[ml][k][0][ip]), sc[ml], false);
@@ -197,31 +208,24 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_g16t4_kernel(DecodeArgs
 #pragma unroll
     for (int ml = 0; ml < 2; ++ml) sc[ml] = group_sum<4>(sc[ml]) * sscale;
   };
-  // Online softmax (base 2) and P*V.  The running maximum moves only when a
-  // score exceeds it by more than kLag, which keeps rescaling rare.
-  uint32_t acc16[2][4][2][2];
-#pragma unroll
-  for (int ml = 0; ml < 2; ++ml)
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-#pragma unroll
-      for (int p = 0; p < 2; ++p) acc16[ml][k][p][0] = acc16[ml][k][p][1] = 0u;
   auto flush = [&]() {
 #pragma unroll
     for (int ml = 0; ml < 2; ++ml)
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
+      for (int k = 0; k < NPL; ++k)
 #pragma unroll
         for (int p = 0; p < 2; ++p)
 #pragma unroll
-          for (int ip = 0; ip < 2; ++ip) {
+          for (int ip = 0; ip < DW; ++ip) {
             const h2_t v = as_h2(acc16[ml][k][p][ip]);
             acc[ml][k][p][2 * ip] += (float)v.x;
             acc[ml][k][p][2 * ip + 1] += (float)v.y;
             acc16[ml][k][p][ip] = 0u;
           }
   };
-  auto accumulate = [&](const float (&sc)[2], const uint4 (&V)[8], bool valid) {
+  // Online softmax (base 2) and P*V.  The running maximum moves only when a
+  // score exceeds it by more than kLag, which keeps rescaling rare.
+  auto accumulate = [&](const float (&sc)[2], const uint32_t (&Vw)[NCW][C], bool valid) {
     if (!valid) return;
 #pragma unroll
     for (int ml = 0; ml < 2; ++ml) {
@@ -231,13 +235,13 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_g16t4_kernel(DecodeArgs
         const h2_t a2 = {(_Float16)alpha, (_Float16)alpha};
         lrow[ml] *= alpha;
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
+        for (int k = 0; k < NPL; ++k)
 #pragma unroll
           for (int p = 0; p < 2; ++p) {
 #pragma unroll
-            for (int c = 0; c < 4; ++c) acc[ml][k][p][c] *= alpha;
+            for (int c = 0; c < C; ++c) acc[ml][k][p][c] *= alpha;
 #pragma unroll
-            for (int ip = 0; ip < 2; ++ip)
+            for (int ip = 0; ip < DW; ++ip)
               acc16[ml][k][p][ip] = __builtin_bit_cast(uint32_t, as_h2(acc16[ml][k][p][ip]) * a2);
           }
         mrow[ml] = s;
@@ -246,54 +250,63 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_g16t4_kernel(DecodeArgs
       lrow[ml] += pr;
       const h2_t p2 = {(_Float16)pr, (_Float16)pr};
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
+      for (int k = 0; k < NPL; ++k)
 #pragma unroll
-        for (int p = 0; p < 2; ++p) {
-          const uint4 vq = V[k + 4 * p];
-          const uint32_t vw[4] = {vq.x, vq.y, vq.z, vq.w};
+        for (int p = 0; p < 2; ++p)
 #pragma unroll
-          for (int ip = 0; ip < 2; ++ip) {
-            const h2_t v2 = as_h2(vw[2 * ml + ip]);
+          for (int ip = 0; ip < DW; ++ip) {
+            const h2_t v2 = as_h2(Vw[k + NPL * p][ml * DW + ip]);
             acc16[ml][k][p][ip] = __builtin_bit_cast(uint32_t, v2 * p2 + as_h2(acc16[ml][k][p][ip]));
           }
-        }
-      }
     }
   };
-  auto load_cs = [&](int pos, uint4 (&CS)[4]) {
+  auto load_cs = [&](int pos, uint4 (&CS)[NPL][QW]) {
+    const uint4* row = reinterpret_cast<const uint4*>(rope16 + (int64_t)pos * D);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) CS[k] = reinterpret_cast<const uint4*>(rope16 + (int64_t)pos * D)[g + 4 * k];
+    for (int k = 0; k < NPL; ++k)
+#pragma unroll
+      for (int u = 0; u < QW; ++u) CS[k][u] = row[(C / 4) * (g + 4 * k) + u];
+  };
+  auto gather = [&](const uint4* tab, uint32_t cw, uint32_t (&out)[C]) {
+#pragma unroll
+    for (int u = 0; u < QW; ++u) {
+      const uint4 x = tab[(2 * cw + hs) * QW + u];
+      out[4 * u] = x.x;
+      out[4 * u + 1] = x.y;
+      out[4 * u + 2] = x.z;
+      out[4 * u + 3] = x.w;
+    }
   };
 
-  // Sinks (split 0 only): values straight from the bf16 rows, scaled like the codebooks.
+  // Sinks (split 0 only): straight from the bf16 rows, scaled like the codebooks.
   for (int base = 0; base < n_sink; base += NW * SPW) {
     const int item = base + wave * SPW + slot;
     const bool valid = item < n_sink;
     const int it = valid ? item : 0;
-    uint4 Kw[8], Vs[8];
+    uint32_t Kw[NCW][C], Vw[NCW][C];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int k = c & 3, p = c >> 2;
-      const int d0 = p * HD + 4 * (g + 4 * k);
-      uint32_t kw[4], vw[4];
+    for (int c = 0; c < NCW; ++c) {
+      const int k = c % NPL, p = c / NPL;
+      const int d0 = p * HD + C * (g + 4 * k);
 #pragma unroll
       for (int ml = 0; ml < 2; ++ml) {
         const int m = 2 * hs + ml;
-        const uint2 x = *reinterpret_cast<const uint2*>(a.sk + (sink0 + (int64_t)m * a.n_s + it) * D + d0);
-        const uint2 y = *reinterpret_cast<const uint2*>(a.sv + (sink0 + (int64_t)m * a.n_s + it) * D + d0);
-        kw[2 * ml + 0] = pack_h2(bf16lo(x.x) * ksc, bf16hi(x.x) * ksc);
-        kw[2 * ml + 1] = pack_h2(bf16lo(x.y) * ksc, bf16hi(x.y) * ksc);
-        vw[2 * ml + 0] = pack_h2(bf16lo(y.x) * vsc, bf16hi(y.x) * vsc);
-        vw[2 * ml + 1] = pack_h2(bf16lo(y.y) * vsc, bf16hi(y.y) * vsc);
+        const uint16_t* kr = a.sk + (sink0 + (int64_t)m * a.n_s + it) * D + d0;
+        const uint16_t* vr = a.sv + (sink0 + (int64_t)m * a.n_s + it) * D + d0;
+#pragma unroll
+        for (int ip = 0; ip < DW; ++ip) {
+          const uint32_t x = *reinterpret_cast<const uint32_t*>(kr + 2 * ip);
+          const uint32_t y = *reinterpret_cast<const uint32_t*>(vr + 2 * ip);
+          Kw[c][ml * DW + ip] = pack_h2(bf16lo(x) * ksc, bf16hi(x) * ksc);
+          Vw[c][ml * DW + ip] = pack_h2(bf16lo(y) * vsc, bf16hi(y) * vsc);
+        }
       }
-      Kw[c] = make_uint4(kw[0], kw[1], kw[2], kw[3]);
-      Vs[c] = make_uint4(vw[0], vw[1], vw[2], vw[3]);
     }
-    uint4 CS[4];
+    uint4 CS[NPL][QW];
     load_cs(it, CS);
     float sc[2];
     scores(Kw, CS, sc);
-    accumulate(sc, Vs, valid);
+    accumulate(sc, Vw, valid);
     flush();
   }
 
@@ -301,57 +314,54 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_g16t4_kernel(DecodeArgs
   // iteration are loaded as soon as the current ones are consumed.
   const int n_tok = max(0, tok_hi - tok_lo);
   const int my = wave * SPW + slot;
-  auto row_ptrs = [&](int base, const uint4*& kr, const uint4*& vr, int& jj) {
+  uint4 krow[RW], vrow[RW];
+  uint4 CS[NPL][QW];
+  auto load_rows = [&](int base, int& jj) {
     const int it = base + my;
     jj = tok_lo + (it < n_tok ? it : n_tok - 1);   // always a real row
-    kr = reinterpret_cast<const uint4*>(a.kidx + (irow0 + jj) * CPT);
-    vr = reinterpret_cast<const uint4*>(a.vidx + (irow0 + jj) * CPT);
+    const uint4* kr = reinterpret_cast<const uint4*>(a.kidx + (irow0 + jj) * CPT);
+    const uint4* vr = reinterpret_cast<const uint4*>(a.vidx + (irow0 + jj) * CPT);
+#pragma unroll
+    for (int u = 0; u < RW; ++u) {
+      krow[u] = kr[u];
+      vrow[u] = vr[u];
+    }
   };
-  uint4 rows[4];
-  uint4 CS[4];
   if (n_tok > 0) {
-    const uint4 *kr, *vr;
     int jj;
-    row_ptrs(0, kr, vr, jj);
-    rows[0] = kr[0];
-    rows[1] = kr[1];
-    rows[2] = vr[0];
-    rows[3] = vr[1];
+    load_rows(0, jj);
     load_cs(a.n_s + jj, CS);
   }
   int since_flush = 0;
   for (int base = 0; base < n_tok; base += NW * SPW) {
     const bool valid = base + my < n_tok;
-    uint32_t ka[8], va[8];
+    uint32_t ka[NCW], va[NCW];
     {
-      const uint32_t kd[8] = {rows[0].x, rows[0].y, rows[0].z, rows[0].w, rows[1].x, rows[1].y, rows[1].z, rows[1].w};
-      const uint32_t vd[8] = {rows[2].x, rows[2].y, rows[2].z, rows[2].w, rows[3].x, rows[3].y, rows[3].z, rows[3].w};
+      uint32_t kd[4 * RW], vd[4 * RW];
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        // chunk g + 4c (c < 4) or the RoPE partner g + 4(c-4) + 16 is byte g of word c
-        ka[c] = 2 * __builtin_amdgcn_ubfe(kd[c], 8 * g, 8) + hs;
-        va[c] = 2 * __builtin_amdgcn_ubfe(vd[c], 8 * g, 8) + hs;
+      for (int u = 0; u < RW; ++u) {
+        kd[4 * u] = krow[u].x; kd[4 * u + 1] = krow[u].y; kd[4 * u + 2] = krow[u].z; kd[4 * u + 3] = krow[u].w;
+        vd[4 * u] = vrow[u].x; vd[4 * u + 1] = vrow[u].y; vd[4 * u + 2] = vrow[u].z; vd[4 * u + 3] = vrow[u].w;
+      }
+#pragma unroll
+      for (int c = 0; c < NCW; ++c) {
+        // chunk g + 4c (c < NPL) or the RoPE partner g + 4(c - NPL) + NP is byte g of word c
+        ka[c] = __builtin_amdgcn_ubfe(kd[c], 8 * g, 8);
+        va[c] = __builtin_amdgcn_ubfe(vd[c], 8 * g, 8);
       }
     }
     // Unconditional (clamped) next loads keep the prefetch in place without copies.
-    int jn = 0;
-    {
-      const uint4 *kr, *vr;
-      row_ptrs(base + NW * SPW, kr, vr, jn);
-      rows[0] = kr[0];
-      rows[1] = kr[1];
-      rows[2] = vr[0];
-      rows[3] = vr[1];
-    }
-    uint4 Kw[8], V[8];
+    int jn;
+    load_rows(base + NW * SPW, jn);
+    uint32_t Kw[NCW][C], Vw[NCW][C];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) Kw[c] = s_k[ka[c]];
+    for (int c = 0; c < NCW; ++c) gather(s_k, ka[c], Kw[c]);
 #pragma unroll
-    for (int c = 0; c < 8; ++c) V[c] = s_v[va[c]];
+    for (int c = 0; c < NCW; ++c) gather(s_v, va[c], Vw[c]);
     float sc[2];
     scores(Kw, CS, sc);
     load_cs(a.n_s + jn, CS);
-    accumulate(sc, V, valid);
+    accumulate(sc, Vw, valid);
     if (++since_flush == kFlush) {
       flush();
       since_flush = 0;
@@ -371,11 +381,11 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_g16t4_kernel(DecodeArgs
       const float a2 = om == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(om - mm);
       lrow[ml] = lrow[ml] * a1 + ol * a2;
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
+      for (int k = 0; k < NPL; ++k)
 #pragma unroll
         for (int p = 0; p < 2; ++p)
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
+          for (int c = 0; c < C; ++c) {
             const float oa = __shfl_xor(acc[ml][k][p][c], off);
             acc[ml][k][p][c] = acc[ml][k][p][c] * a1 + oa * a2;
           }
@@ -387,11 +397,11 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_g16t4_kernel(DecodeArgs
     for (int ml = 0; ml < 2; ++ml) {
       const int m = 2 * hs + ml;
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
+      for (int k = 0; k < NPL; ++k)
 #pragma unroll
         for (int p = 0; p < 2; ++p)
 #pragma unroll
-          for (int c = 0; c < 4; ++c) s_red[wave][m][p * HD + 4 * (g + 4 * k) + c] = acc[ml][k][p][c];
+          for (int c = 0; c < C; ++c) s_red[wave][m][p * HD + C * (g + 4 * k) + c] = acc[ml][k][p][c];
       if (g == 0) {
         s_red[wave][m][D] = mrow[ml];
         s_red[wave][m][D + 1] = lrow[ml];
@@ -423,9 +433,14 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_g16t4_kernel(DecodeArgs
   }
 }
 
-hipError_t launch_decode_g16t4(const DecodeArgs& a, hipStream_t s) {
+hipError_t launch_decode_fast(int G, const DecodeArgs& a, hipStream_t s) {
   dim3 grid(a.n_split, a.Hq, a.B * a.n_blk_serv);
-  hipLaunchKernelGGL(decode_g16t4_kernel, grid, dim3(kDecodeThreads), 0, s, a);
+  if (G == 16)
+    hipLaunchKernelGGL(decode_fast_kernel<4>, grid, dim3(kDecodeThreads), 0, s, a);
+  else if (G == 32)
+    hipLaunchKernelGGL(decode_fast_kernel<8>, grid, dim3(kDecodeThreads), 0, s, a);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

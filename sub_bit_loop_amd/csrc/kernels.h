@@ -59,7 +59,7 @@ hipError_t launch_sigma(const SigmaArgs& a, int B, hipStream_t s);
 hipError_t launch_decode(int G, int TC, bool tasq, const DecodeArgs& a, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
 hipError_t launch_rope_table(double theta, int D, int n_pos, void* table, hipStream_t s);
-hipError_t launch_decode_g16t4(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_decode_fast(int G, const DecodeArgs& a, hipStream_t s);
 
 constexpr int kDecodeThreads = 256;
 constexpr int kEncodeThreads = 256;

@@ -249,10 +249,10 @@ loopvq_status loopvq_decode_attn(const loopvq_geom* g, const void* q, int32_t st
   a.n_blk_serv = p.n_blk_serv;
   a.tok_per_split = p.tok_per_split;
   a.qscale = (float)(1.4426950408889634 / std::sqrt((double)g->D));
-  // 0.5-bit loop layout without pre-transform: the specialised kernel;
-  // every other geometry: the generic one.
-  hipError_t e = (g->G == 16 && g->T_c == 4 && pt == nullptr)
-                     ? loopvq::launch_decode_g16t4(a, s)
+  // Blocks of four steps without pre-transform (0.5 and 0.25 bit): the
+  // specialised kernel; every other geometry: the generic one.
+  hipError_t e = (g->T_c == 4 && pt == nullptr)
+                     ? loopvq::launch_decode_fast(g->G, a, s)
                      : loopvq::launch_decode(g->G, g->T_c, pt != nullptr, a, s);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   loopvq::MergeArgs ma{};
