@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define LOOPVQ_ABI_VERSION 1
+#define LOOPVQ_ABI_VERSION 2
 
 typedef enum {
   LOOPVQ_OK = 0,
@@ -129,10 +129,13 @@ loopvq_status loopvq_decode_attn_workspace(const loopvq_geom* g, int32_t B, int3
  * For every batch b, q-head hq and loop step t in [step0, step0 + n_steps):
  * with kv-head h = hq / (n_q_heads / n_kv_heads), block beta = t / T_c and
  * m = t % T_c, the keys are the n_s bf16 sinks sink_k[b][h][t][s] at position
- * s and the dequantized tokens j < N_b, whose channel q*c + i is
+ * s, the dequantized tokens j < N_b, whose channel q*c + i is
  * k_cb[h][beta][k_idx[b][h][beta][j][q]][i*T_c + m] (inverse pre-transform
- * applied when pt != NULL), at position n_s + j; every key is rotated (RoPE)
- * at its position; values likewise from v_idx / v_cb / sink_v (no RoPE).
+ * applied when pt != NULL), at position n_s + j, and the n_r bf16 tokens of
+ * the recent window recent_k[b][h][t][r] at position n_s + N_b + r (section
+ * 3.4 step 1: sinks and the newest tokens stay bf16); every key is rotated
+ * (RoPE) at its position; values likewise from v_idx / v_cb / sink_v /
+ * recent_v (no RoPE).
  * The result is softmax attention with scale 1/sqrt(D):
  *   out[b][hq][t - step0][0..D)  (fp32)
  *   lse[b][hq][t - step0]        (fp32, natural log-sum-exp of the scaled
@@ -146,25 +149,29 @@ loopvq_status loopvq_decode_attn_workspace(const loopvq_geom* g, int32_t B, int3
  *   k_cb, v_cb device bf16 [n_kv_heads][n_blk][K][G]
  *   sink_k, sink_v  device bf16 [B][n_kv_heads][T][n_s][D], pre-RoPE; may be
  *              NULL when n_s == 0
+ *   recent_k, recent_v  device bf16 [B][n_kv_heads][T][R_cap][D], pre-RoPE;
+ *              the first n_r tokens are attended; may be NULL when n_r == 0
  *   N          quantized tokens in the cache (N <= N_cap)
  *   seq_len    device int32 [B] or NULL; batch b attends min(seq_len[b], N)
  *              quantized tokens (negative values count as 0)
  *   pt         keys' pre-transform (reads w, perm, sigma) or NULL
  *   rope_table device fp16 table written by loopvq_rope_table for this D and
- *              theta, with n_pos >= n_s + N positions
+ *              theta, with n_pos >= n_s + N + n_r positions
  *   workspace  device scratch of at least loopvq_decode_attn_workspace() bytes
- * Alignment: q, k_idx, v_idx, k_cb, v_cb, sink_k, sink_v, rope_table and
+ * Alignment: q, k_idx, v_idx, k_cb, v_cb, sink_k, sink_v, recent_k, recent_v,
+ * rope_table and
  * workspace must be 16-byte aligned.
- * A row with no keys at all (n_s == 0 and N_b == 0) yields out = 0 and
+ * A row with no keys at all (n_s == 0, N_b == 0 and n_r == 0) yields out = 0 and
  * lse = -inf.
  * Errors: EINVAL for NULL pointers, bad geometry, step range outside [0, T),
- * N > N_cap, n_pos too small; EWORKSPACE for a short workspace; ENOTSUP as for
+ * N > N_cap, n_r > R_cap, n_pos too small; EWORKSPACE for a short workspace; ENOTSUP as for
  * loopvq_encode. */
 loopvq_status loopvq_decode_attn(const loopvq_geom* g, const void* q, int32_t step0,
                                  int32_t n_steps, const uint8_t* k_idx, const uint8_t* v_idx,
                                  int32_t N_cap, const void* k_cb, const void* v_cb,
                                  const void* sink_k, const void* sink_v, int32_t n_s,
-                                 int32_t B, int32_t N, const int32_t* seq_len,
+                                 const void* recent_k, const void* recent_v, int32_t n_r,
+                                 int32_t R_cap, int32_t B, int32_t N, const int32_t* seq_len,
                                  const loopvq_pretransform* pt, const void* rope_table,
                                  int32_t n_pos, float* out, float* lse, void* workspace,
                                  size_t workspace_bytes, void* stream);

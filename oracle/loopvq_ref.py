@@ -205,13 +205,16 @@ def lse_merge(parts):
 
 def decode_attn_row(q_t: np.ndarray, t: int, k_idx, v_idx, k_cb, v_cb,
                     sink_k, sink_v, T_c: int, theta: float = 1.0e4,
-                    n_tokens=None, tasq=None):
+                    n_tokens=None, tasq=None, recent_k=None, recent_v=None):
     """Decode attention of one query row (one batch entry, one q-head, step t).
 
     q_t: [D] post-RoPE query.  k_idx, v_idx: [n_blk, N, D/c] for the kv-head.
     k_cb, v_cb: [n_blk, K, G].  sink_k, sink_v: [T, n_s, D] pre-RoPE bf16 values.
     n_tokens: quantized tokens attended (default all N).
     tasq: None or (w [D], perm [D], sigma [N, T]) for keys of this kv-head.
+    recent_k, recent_v: None or [T, n_r, D] pre-RoPE bf16 values of the recent
+    window (section 3.4 step 1: the newest tokens stay bf16), at positions
+    n_s + n_tokens .. n_s + n_tokens + n_r - 1.
     Returns (out [D], lse).
     """
     D = q_t.shape[-1]
@@ -223,9 +226,14 @@ def decode_attn_row(q_t: np.ndarray, t: int, k_idx, v_idx, k_cb, v_cb,
     if tasq is not None:
         w, perm, sigma = tasq
         kq = tasq_inverse(kq, w, perm, sigma[:N, t])
-    keys = np.concatenate([np.asarray(sink_k[t], dtype=np.float64), kq], axis=0)
-    vals = np.concatenate([np.asarray(sink_v[t], dtype=np.float64), vq], axis=0)
-    pos = np.arange(n_s + N)
+    ks = [np.asarray(sink_k[t], dtype=np.float64), kq]
+    vs = [np.asarray(sink_v[t], dtype=np.float64), vq]
+    if recent_k is not None:
+        ks.append(np.asarray(recent_k[t], dtype=np.float64))
+        vs.append(np.asarray(recent_v[t], dtype=np.float64))
+    keys = np.concatenate(ks, axis=0)
+    vals = np.concatenate(vs, axis=0)
+    pos = np.arange(keys.shape[0])
     return attention(q_t, apply_rope(keys, pos, theta), vals)
 
 

@@ -52,8 +52,8 @@ def lib():
     L.loopvq_rope_table.restype = ctypes.c_int
     L.loopvq_decode_attn_workspace.argtypes = [GP, I32, I32, I32, I32, ctypes.POINTER(SZ)]
     L.loopvq_decode_attn_workspace.restype = ctypes.c_int
-    L.loopvq_decode_attn.argtypes = [GP, P, I32, I32, P, P, I32, P, P, P, P, I32, I32, I32, P,
-                                     PTP, P, I32, P, P, P, SZ, P]
+    L.loopvq_decode_attn.argtypes = [GP, P, I32, I32, P, P, I32, P, P, P, P, I32, P, P, I32, I32,
+                                     I32, I32, P, PTP, P, I32, P, P, P, SZ, P]
     L.loopvq_decode_attn.restype = ctypes.c_int
     L.loopvq_last_error.argtypes = []
     L.loopvq_last_error.restype = ctypes.c_char_p

@@ -76,9 +76,11 @@ def decode_workspace_bytes(g: Geom, B, N, step0, n_steps):
 
 
 def decode_attn(g: Geom, q, k_idx, v_idx, k_cb, v_cb, sink_k, sink_v, rope, N=None, step0=0,
-                seq_len=None, pt=None, out=None, lse=None, workspace=None, stream=None):
+                seq_len=None, pt=None, out=None, lse=None, workspace=None, stream=None,
+                recent_k=None, recent_v=None, n_r=None):
     """q bf16 [B][Hq][n_steps][D] (post-RoPE); k_idx/v_idx uint8 [B][H][n_blk][N_cap][D/c];
     k_cb/v_cb bf16 [H][n_blk][K][G]; sinks bf16 [B][H][T][n_s][D] or None;
+    recent window bf16 [B][H][T][R_cap][D] or None (first n_r tokens attended);
     rope fp16 table from rope_table().  Returns (out fp32 [B][Hq][n_steps][D], lse fp32 [B][Hq][n_steps])."""
     _need(q, torch.bfloat16, "q")
     _need(k_idx, torch.uint8, "k_idx")
@@ -99,6 +101,12 @@ def decode_attn(g: Geom, q, k_idx, v_idx, k_cb, v_cb, sink_k, sink_v, rope, N=No
         n_s = sink_k.shape[3]
     if seq_len is not None:
         _need(seq_len, torch.int32, "seq_len")
+    R_cap = 0
+    if recent_k is not None:
+        _need(recent_k, torch.bfloat16, "recent_k")
+        _need(recent_v, torch.bfloat16, "recent_v")
+        R_cap = recent_k.shape[3]
+    n_r = R_cap if n_r is None else n_r
     if out is None:
         out = torch.empty((B, Hq, n_steps, D), dtype=torch.float32, device=q.device)
     if lse is None:
@@ -108,7 +116,8 @@ def decode_attn(g: Geom, q, k_idx, v_idx, k_cb, v_cb, sink_k, sink_v, rope, N=No
         workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=q.device)
     st = _lib.lib().loopvq_decode_attn(
         ctypes.byref(g), _ptr(q), step0, n_steps, _ptr(k_idx), _ptr(v_idx), N_cap, _ptr(k_cb), _ptr(v_cb),
-        _ptr(sink_k), _ptr(sink_v), n_s, B, N, _ptr(seq_len), ctypes.byref(pt) if pt is not None else None,
+        _ptr(sink_k), _ptr(sink_v), n_s, _ptr(recent_k), _ptr(recent_v), n_r, R_cap, B, N, _ptr(seq_len),
+        ctypes.byref(pt) if pt is not None else None,
         _ptr(rope), rope.shape[0], _ptr(out), _ptr(lse), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream))
     check(st)

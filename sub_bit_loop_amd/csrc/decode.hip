@@ -119,25 +119,31 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
   if (a.seq_len) nb = max(0, min(a.seq_len[b], a.N));
   const int tok_lo = split * a.tok_per_split;
   const int tok_hi = min(nb, tok_lo + a.tok_per_split);
+  // bf16 items (sinks, then the recent window) are served by split 0.
   const int n_sink = split == 0 ? a.n_s : 0;
-  const int n_items = n_sink + max(0, tok_hi - tok_lo);
+  const int n_bf = n_sink + (split == 0 ? a.n_r : 0);
+  const int n_items = n_bf + max(0, tok_hi - tok_lo);
   const int64_t irow0 = (((int64_t)b * a.H + h) * a.n_blk + beta) * (int64_t)a.N_cap;
   const int64_t sink0 = (((int64_t)b * a.H + h) * a.T + beta * TC) * (int64_t)a.n_s;
+  const int64_t rec0 = (((int64_t)b * a.H + h) * a.T + beta * TC) * (int64_t)a.r_cap;
 
   for (int base = 0; base < n_items; base += NW * SPW) {
     const int item = base + wave * SPW + slot;
     const bool valid = item < n_items;
     const int it = valid ? item : 0;
-    const bool is_sink = it < n_sink;
-    const int j = is_sink ? 0 : tok_lo + it - n_sink;
-    const int pos = is_sink ? it : a.n_s + j;
+    const bool is_sink = it < n_bf;
+    const bool is_rec = is_sink && it >= n_sink;
+    const int j = is_sink ? 0 : tok_lo + it - n_bf;
+    const int pos = !is_sink ? a.n_s + j : (is_rec ? a.n_s + nb + (it - n_sink) : it);
 
     float kv[NE][TC], vv[NE][TC], sg[TC];
     if (is_sink) {
 #pragma unroll
       for (int m = 0; m < TC; ++m) {
-        const uint16_t* kr = a.sk + (sink0 + (int64_t)m * a.n_s + it) * D;
-        const uint16_t* vr = a.sv + (sink0 + (int64_t)m * a.n_s + it) * D;
+        const uint16_t* kr = is_rec ? a.rk + (rec0 + (int64_t)m * a.r_cap + (it - n_sink)) * D
+                                    : a.sk + (sink0 + (int64_t)m * a.n_s + it) * D;
+        const uint16_t* vr = is_rec ? a.rv + (rec0 + (int64_t)m * a.r_cap + (it - n_sink)) * D
+                                    : a.sv + (sink0 + (int64_t)m * a.n_s + it) * D;
 #pragma unroll
         for (int e = 0; e < NE; ++e) {
           const int p = e / C, i = e % C;

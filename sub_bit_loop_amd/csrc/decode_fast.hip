@@ -178,9 +178,12 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_fast_kernel(DecodeArgs 
   if (a.seq_len) nb = max(0, min(a.seq_len[b], a.N));
   const int tok_lo = split * a.tok_per_split;
   const int tok_hi = min(nb, tok_lo + a.tok_per_split);
+  // bf16 items (sinks, then the recent window) are served by split 0.
   const int n_sink = split == 0 ? a.n_s : 0;
+  const int n_bf = n_sink + (split == 0 ? a.n_r : 0);
   const int64_t irow0 = (((int64_t)b * a.H + h) * a.n_blk + beta) * (int64_t)a.N_cap;
   const int64_t sink0 = (((int64_t)b * a.H + h) * a.T + beta * TC) * (int64_t)a.n_s;
+  const int64_t rec0 = (((int64_t)b * a.H + h) * a.T + beta * TC) * (int64_t)a.r_cap;
   const uint16_t* rope16 = reinterpret_cast<const uint16_t*>(a.rope);
   const float ksc = ldexpf(1.f, -shk), vsc = ldexpf(1.f, -shv);
 
@@ -278,11 +281,15 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_fast_kernel(DecodeArgs 
     }
   };
 
-  // Sinks (split 0 only): straight from the bf16 rows, scaled like the codebooks.
-  for (int base = 0; base < n_sink; base += NW * SPW) {
+  // Sinks and the recent window (split 0 only): straight from the bf16 rows,
+  // scaled like the codebooks.  Sink s sits at position s, recent token r at
+  // n_s + N_b + r.
+  for (int base = 0; base < n_bf; base += NW * SPW) {
     const int item = base + wave * SPW + slot;
-    const bool valid = item < n_sink;
+    const bool valid = item < n_bf;
     const int it = valid ? item : 0;
+    const bool is_rec = it >= n_sink;
+    const int pos = is_rec ? a.n_s + nb + (it - n_sink) : it;
     uint32_t Kw[NCW][C], Vw[NCW][C];
 #pragma unroll
     for (int c = 0; c < NCW; ++c) {
@@ -291,8 +298,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_fast_kernel(DecodeArgs 
 #pragma unroll
       for (int ml = 0; ml < 2; ++ml) {
         const int m = 2 * hs + ml;
-        const uint16_t* kr = a.sk + (sink0 + (int64_t)m * a.n_s + it) * D + d0;
-        const uint16_t* vr = a.sv + (sink0 + (int64_t)m * a.n_s + it) * D + d0;
+        const uint16_t* kr = (is_rec ? a.rk + (rec0 + (int64_t)m * a.r_cap + (it - n_sink)) * D
+                                     : a.sk + (sink0 + (int64_t)m * a.n_s + it) * D) + d0;
+        const uint16_t* vr = (is_rec ? a.rv + (rec0 + (int64_t)m * a.r_cap + (it - n_sink)) * D
+                                     : a.sv + (sink0 + (int64_t)m * a.n_s + it) * D) + d0;
 #pragma unroll
         for (int ip = 0; ip < DW; ++ip) {
           const uint32_t x = *reinterpret_cast<const uint32_t*>(kr + 2 * ip);
@@ -303,7 +312,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_fast_kernel(DecodeArgs 
       }
     }
     uint4 CS[NPL][QW];
-    load_cs(it, CS);
+    load_cs(pos, CS);
     float sc[2];
     scores(Kw, CS, sc);
     accumulate(sc, Vw, valid);

@@ -33,6 +33,9 @@ struct DecodeArgs {
   const uint16_t* vcb;
   const uint16_t* sk;         // bf16 [B][H][T][n_s][D]
   const uint16_t* sv;
+  const uint16_t* rk;         // bf16 [B][H][T][r_cap][D] recent window or null
+  const uint16_t* rv;
+  int32_t n_r, r_cap;
   const int32_t* seq_len;     // [B] or null
   const float* w;             // pre-transform or null
   const int16_t* perm;

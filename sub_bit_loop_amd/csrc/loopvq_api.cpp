@@ -187,7 +187,8 @@ loopvq_status loopvq_decode_attn(const loopvq_geom* g, const void* q, int32_t st
                                  int32_t n_steps, const uint8_t* k_idx, const uint8_t* v_idx,
                                  int32_t N_cap, const void* k_cb, const void* v_cb,
                                  const void* sink_k, const void* sink_v, int32_t n_s,
-                                 int32_t B, int32_t N, const int32_t* seq_len,
+                                 const void* recent_k, const void* recent_v, int32_t n_r,
+                                 int32_t R_cap, int32_t B, int32_t N, const int32_t* seq_len,
                                  const loopvq_pretransform* pt, const void* rope_table,
                                  int32_t n_pos, float* out, float* lse, void* workspace,
                                  size_t workspace_bytes, void* stream) {
@@ -195,15 +196,18 @@ loopvq_status loopvq_decode_attn(const loopvq_geom* g, const void* q, int32_t st
   loopvq_status st = check_decode_shape(g, B, N, step0, n_steps);
   if (st != LOOPVQ_OK) return st;
   if (n_s < 0) return fail(LOOPVQ_EINVAL, "n_s=%d must be >= 0", n_s);
+  if (n_r < 0 || n_r > R_cap) return fail(LOOPVQ_EINVAL, "n_r=%d must lie in [0, R_cap=%d]", n_r, R_cap);
   if (N > N_cap) return fail(LOOPVQ_EINVAL, "N=%d exceeds N_cap=%d", N, N_cap);
   if (B == 0) return LOOPVQ_OK;
   if (!q || !k_cb || !v_cb || !rope_table || !out) return fail(LOOPVQ_EINVAL, "NULL tensor pointer");
   if (N > 0 && (!k_idx || !v_idx)) return fail(LOOPVQ_EINVAL, "NULL index pointer");
   if (n_s > 0 && (!sink_k || !sink_v)) return fail(LOOPVQ_EINVAL, "NULL sink pointer with n_s=%d", n_s);
-  if ((long long)n_s + N > n_pos)
-    return fail(LOOPVQ_EINVAL, "rope table has %d positions, need n_s + N = %lld", n_pos, (long long)n_s + N);
+  if (n_r > 0 && (!recent_k || !recent_v)) return fail(LOOPVQ_EINVAL, "NULL recent-window pointer with n_r=%d", n_r);
+  if ((long long)n_s + N + n_r > n_pos)
+    return fail(LOOPVQ_EINVAL, "rope table has %d positions, need n_s + N + n_r = %lld", n_pos,
+                (long long)n_s + N + n_r);
   {
-    const void* al[] = {q, k_idx, v_idx, k_cb, v_cb, sink_k, sink_v, rope_table, workspace};
+    const void* al[] = {q, k_idx, v_idx, k_cb, v_cb, sink_k, sink_v, recent_k, recent_v, rope_table, workspace};
     for (const void* p : al)
       if (reinterpret_cast<uintptr_t>(p) % 16)
         return fail(LOOPVQ_EINVAL, "tensor pointers must be 16-byte aligned");
@@ -223,6 +227,10 @@ loopvq_status loopvq_decode_attn(const loopvq_geom* g, const void* q, int32_t st
   a.vcb = static_cast<const uint16_t*>(v_cb);
   a.sk = static_cast<const uint16_t*>(sink_k);
   a.sv = static_cast<const uint16_t*>(sink_v);
+  a.rk = static_cast<const uint16_t*>(recent_k);
+  a.rv = static_cast<const uint16_t*>(recent_v);
+  a.n_r = n_r;
+  a.r_cap = R_cap;
   a.seq_len = seq_len;
   if (pt) {
     a.w = pt->w;

@@ -27,7 +27,7 @@ def test_exports_match_header():
     assert set(names) == set(L.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.loopvq_abi_version() == 1
+    assert lib.loopvq_abi_version() == 2
 
 
 def _geom(L, **kw):
@@ -101,16 +101,20 @@ def test_decode_workspace_and_errors():
 
     def call(**kw):
         a = dict(q=P(16), step0=0, n_steps=4, k_idx=P(16), v_idx=P(16), N_cap=100, k_cb=P(16), v_cb=P(16),
-                 sink_k=P(16), sink_v=P(16), n_s=4, B=2, N=100, seq_len=None, pt=None, rope=P(16), n_pos=104,
-                 out=P(16), lse=P(16), ws=P(16), ws_bytes=need.value)
+                 sink_k=P(16), sink_v=P(16), n_s=4, rk=P(16), rv=P(16), n_r=8, R_cap=8, B=2, N=100,
+                 seq_len=None, pt=None, rope=P(16), n_pos=112, out=P(16), lse=P(16), ws=P(16),
+                 ws_bytes=need.value)
         a.update(kw)
         return lib.loopvq_decode_attn(ctypes.byref(g), a["q"], a["step0"], a["n_steps"], a["k_idx"], a["v_idx"],
                                       a["N_cap"], a["k_cb"], a["v_cb"], a["sink_k"], a["sink_v"], a["n_s"],
-                                      a["B"], a["N"], a["seq_len"], a["pt"], a["rope"], a["n_pos"], a["out"],
-                                      a["lse"], a["ws"], a["ws_bytes"], None)
+                                      a["rk"], a["rv"], a["n_r"], a["R_cap"], a["B"], a["N"], a["seq_len"],
+                                      a["pt"], a["rope"], a["n_pos"], a["out"], a["lse"], a["ws"],
+                                      a["ws_bytes"], None)
     assert call(q=P(0)) == -1
     assert call(N=101) == -1                  # N > N_cap
-    assert call(n_pos=103) == -1              # table too short
+    assert call(n_pos=111) == -1              # table too short for sinks + N + recent
+    assert call(n_r=9) == -1                  # n_r > R_cap
+    assert call(rk=P(0)) == -1                # recent window missing with n_r > 0
     assert call(sink_k=P(0)) == -1            # sinks missing with n_s > 0
     assert call(k_cb=P(8)) == -1              # misaligned codebook
     assert call(step0=2, n_steps=3) == -1     # step range outside [0, T)

@@ -81,7 +81,7 @@ def _check_encode_slice(cfg, inp, kidx, vidx, sigma, b, h, toks):
     return rk, rv
 
 
-def _check_rows(cfg, inp, kidx, vidx, sigma, out, lse, rows, step0=0, N=None, seq=None):
+def _check_rows(cfg, inp, kidx, vidx, sigma, out, lse, rows, step0=0, N=None, seq=None, recent=None):
     """rows: list of (b, hq, t) with t absolute step; out/lse hold steps from step0."""
     worst = 0.0
     gqa = cfg.H_q // cfg.H_kv
@@ -104,8 +104,12 @@ def _check_rows(cfg, inp, kidx, vidx, sigma, out, lse, rows, step0=0, N=None, se
         if Nb + n_s == 0:
             assert np.all(o_gpu == 0) and lse[b, hq, t - step0].item() == -math.inf
             continue
+        rk = rv = None
+        if recent is not None:
+            rk, rv = np64(recent[0][b, h]), np64(recent[1][b, h])
         o_ref, l_ref = ref.decode_attn_row(q, t, ki, vi, np64(inp["k_cb"][h]), np64(inp["v_cb"][h]),
-                                           sk, sv, cfg.T_c, cfg.theta, n_tokens=Nb, tasq=tasq)
+                                           sk, sv, cfg.T_c, cfg.theta, n_tokens=Nb, tasq=tasq,
+                                           recent_k=rk, recent_v=rv)
         err = row_error(o_gpu, o_ref)
         worst = max(worst, err)
         assert err <= OUT_TOL, "row %s: err %.3g" % ((b, hq, t), err)
@@ -113,17 +117,19 @@ def _check_rows(cfg, inp, kidx, vidx, sigma, out, lse, rows, step0=0, N=None, se
     return worst
 
 
-def _decode(s, cfg, inp, kidx, vidx, pt, N=None, step0=0, n_steps=None, seq=None, n_s=None):
+def _decode(s, cfg, inp, kidx, vidx, pt, N=None, step0=0, n_steps=None, seq=None, n_s=None, recent=None):
     g = _geom(s, cfg)
     n_steps = cfg.T if n_steps is None else n_steps
     N = kidx.shape[3] if N is None else N
     ns = inp["sink_k"].shape[3] if n_s is None else n_s
-    rope = s.rope_table(ns + kidx.shape[3] + 8, cfg.D, cfg.theta)
+    n_r = 0 if recent is None else recent[0].shape[3]
+    rope = s.rope_table(ns + kidx.shape[3] + n_r + 8, cfg.D, cfg.theta)
     q = inp["q"][:, :, step0:step0 + n_steps].contiguous()
     sk = inp["sink_k"] if ns else None
     sv = inp["sink_v"] if ns else None
+    rk, rv = (None, None) if recent is None else recent
     return s.decode_attn(g, q, kidx, vidx, inp["k_cb"], inp["v_cb"], sk, sv, rope, N=N, step0=step0,
-                         seq_len=seq, pt=pt)
+                         seq_len=seq, pt=pt, recent_k=rk, recent_v=rv)
 
 
 def test_config1_full():
@@ -240,3 +246,50 @@ def test_rope_table_matches_oracle():
     assert np.max(np.abs(sin - tab[:, :, 1])) <= 2.0 ** -12
     want = ref.fp16_round(tab[:, :, 0])
     assert np.mean(cos == want) > 0.999
+
+
+RECENT = [
+    # name, G, T_c, T, H_kv, H_q, B, N, n_r, pretransform
+    ("half-bit", 16, 4, 4, 2, 2, 2, 600, 64, False),
+    ("quarter-bit-gqa", 32, 4, 4, 1, 4, 2, 500, 64, False),
+    ("generic-tc2", 16, 2, 4, 1, 1, 2, 300, 24, False),
+    ("pretransform", 16, 4, 4, 2, 2, 1, 400, 32, True),
+]
+
+
+@pytest.mark.parametrize("geo", RECENT, ids=[x[0] for x in RECENT])
+def test_recent_window_and_page_conversion(geo):
+    """bf16 recent window in the same softmax, then one 8-token page moved from
+    the window into the compressed cache (encode at tok0 = N)."""
+    s = _lib()
+    name, G, T_c, T, H, Hq, B, N, n_r, tasq = geo
+    _say("recent window", name)
+    cfg = small_cfg(1, G=G, T_c=T_c, T=T, H_kv=H, H_q=Hq, B=B, N=N + n_r, n_s=4, tasq=tasq,
+                    rho_k=(0.85,) * (T - 1), rho_v=(0.9,) * (T - 1), n_calib=1024, kmeans_iters=8)
+    inp = build_inputs(cfg, 0, "cuda")
+    g = _geom(s, cfg)
+    cap = N + n_r
+    shp = (B, H, cfg.n_blk, cap, cfg.chunks)
+    kidx = torch.zeros(shp, dtype=torch.uint8, device="cuda")
+    vidx = torch.zeros(shp, dtype=torch.uint8, device="cuda")
+    sigma = None
+    pt = None
+    if tasq:
+        sigma = torch.zeros((B, cap, T), dtype=torch.float16, device="cuda")
+        pt = s.pretransform(inp["w"], inp["perm"], sigma)
+    s.encode(g, inp["k"][:, :, :, :N], inp["k_cb"], kidx, pt=pt)
+    s.encode(g, inp["v"][:, :, :, :N], inp["v_cb"], vidx)
+    rk = inp["k"][:, :, :, N:].contiguous()
+    rv = inp["v"][:, :, :, N:].contiguous()
+    rows = [(b, hq, t) for b in range(B) for hq in range(Hq) for t in range(T)]
+    out, lse = _decode(s, cfg, inp, kidx, vidx, pt, N=N, recent=(rk, rv))
+    torch.cuda.synchronize()
+    w1 = _check_rows(cfg, inp, kidx, vidx, sigma, out, lse, rows, N=N, recent=(rk, rv))
+    # page conversion: the oldest 8 recent tokens become codes at tok0 = N
+    s.encode(g, rk[:, :, :, :8], inp["k_cb"], kidx, tok0=N, pt=pt)
+    s.encode(g, rv[:, :, :, :8], inp["v_cb"], vidx, tok0=N)
+    rk2, rv2 = rk[:, :, :, 8:].contiguous(), rv[:, :, :, 8:].contiguous()
+    out, lse = _decode(s, cfg, inp, kidx, vidx, pt, N=N + 8, recent=(rk2, rv2))
+    torch.cuda.synchronize()
+    w2 = _check_rows(cfg, inp, kidx, vidx, sigma, out, lse, rows, N=N + 8, recent=(rk2, rv2))
+    _say("  worst rel err %.3g before, %.3g after the page conversion" % (w1, w2))

@@ -243,6 +243,34 @@ def test_attention_matches_sdpa_with_sinks():
         assert abs(lse - float(torch.logsumexp(torch.from_numpy(s), 0))) < 1e-12
 
 
+def test_recent_window_is_the_same_softmax():
+    """Section 3.4: the newest tokens stay bf16 and are attended in the same
+    softmax; their positions follow the quantized tokens.  Equivalent to
+    Flash-Decoding merge of the compressed part with a bf16 segment."""
+    rng = np.random.default_rng(31)
+    T, T_c, D, G, K, N, n_s, n_r = 4, 4, 128, 16, 32, 20, 3, 5
+    cb_k, cb_v = _bf16(rng, (1, K, G)), _bf16(rng, (1, K, G))
+    ki = rng.integers(0, K, size=(1, N, D // 4))
+    vi = rng.integers(0, K, size=(1, N, D // 4))
+    sk, sv = _bf16(rng, (T, n_s, D)), _bf16(rng, (T, n_s, D))
+    rk, rv = _bf16(rng, (T, n_r, D)), _bf16(rng, (T, n_r, D))
+    for t in range(T):
+        q = rng.standard_normal(D)
+        full = ref.decode_attn_row(q, t, ki, vi, cb_k, cb_v, sk, sv, T_c, recent_k=rk, recent_v=rv)
+        base = ref.decode_attn_row(q, t, ki, vi, cb_k, cb_v, sk, sv, T_c)
+        seg = ref.attention(q, ref.apply_rope(rk[t], np.arange(n_s + N, n_s + N + n_r)), rv[t])
+        out, lse = ref.lse_merge([base, seg])
+        assert np.allclose(full[0], out, atol=1e-12) and abs(full[1] - lse) < 1e-12
+        # and equals SDPA over the explicit key sequence sinks | codes | recent
+        keys = np.concatenate([sk[t], ref.dequant(ki, cb_k, T_c, D)[t], rk[t]])
+        pos = np.arange(keys.shape[0])
+        vals = np.concatenate([sv[t], ref.dequant(vi, cb_v, T_c, D)[t], rv[t]])
+        sd = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q)[None, None, None], torch.from_numpy(ref.apply_rope(keys, pos))[None, None],
+            torch.from_numpy(vals)[None, None])
+        assert np.allclose(full[0], sd[0, 0, 0].numpy(), atol=1e-12)
+
+
 def test_attention_special_cases():
     rng = np.random.default_rng(17)
     D, P = 16, 9
