@@ -68,19 +68,20 @@ def _oracle_head(args):
         return time.perf_counter() - t0, ki.size + vi.size
 
 
-def cpu_baseline(cfg, inp, n_tok):
-    """Oracle on batch entry 0, every kv-head, the first n_tok context tokens:
-    K and V encode plus decode of every loop step over those tokens."""
+def cpu_baseline(cfg, inp, n_tok, n_b):
+    """Oracle on batch entries 0..n_b-1, every kv-head, the first n_tok context
+    tokens: K and V encode plus decode of every loop step over those tokens."""
     from concurrent.futures import ProcessPoolExecutor
     import multiprocessing as mp
     import torch
     f = lambda t: t.float().cpu().double().numpy()
     jobs = []
-    for h in range(cfg.H_kv):
-        hq = h * (cfg.H_q // cfg.H_kv)
-        jobs.append((f(inp["k"][0, h, :, :n_tok]), f(inp["v"][0, h, :, :n_tok]), f(inp["k_cb"][h]),
-                     f(inp["v_cb"][h]), f(inp["sink_k"][0, h]), f(inp["sink_v"][0, h]),
-                     f(inp["q"][0, hq]), cfg.T_c, cfg.theta))
+    for b in range(n_b):
+        for h in range(cfg.H_kv):
+            hq = h * (cfg.H_q // cfg.H_kv)
+            jobs.append((f(inp["k"][b, h, :, :n_tok]), f(inp["v"][b, h, :, :n_tok]), f(inp["k_cb"][h]),
+                         f(inp["v_cb"][h]), f(inp["sink_k"][b, h]), f(inp["sink_v"][b, h]),
+                         f(inp["q"][b, hq]), cfg.T_c, cfg.theta))
     cores = len(os.sched_getaffinity(0))
     workers = max(1, min(cores, len(jobs), 16))
     t0 = time.perf_counter()
@@ -88,18 +89,18 @@ def cpu_baseline(cfg, inp, n_tok):
         res = list(ex.map(_oracle_head, jobs))
     wall = time.perf_counter() - t0
     codes = sum(r[1] for r in res)
-    # GQA heads beyond the first of each group are not re-run: count them as served
-    # only when the group size is 1 (the default workload).
-    tokens_blocks = n_tok * cfg.n_blk
+    # One q-head per kv-head is decoded; with GQA the other heads of a group
+    # are not re-run (the default workload has none).
+    tokens_blocks = n_b * n_tok * cfg.n_blk
     return {
         "value": tokens_blocks / wall,
         "unit": UNIT,
         "cores": workers,
         "kind": "oracle",
-        "sample": "batch entry 0, all %d kv-heads, first %d context tokens: fp64 NumPy encode of K and V "
+        "sample": "batch entries 0..%d, all %d kv-heads, first %d context tokens: fp64 NumPy encode of K and V "
                   "(%d codes) + decode attention of every loop step over those tokens and the %d sinks; "
-                  "one process per kv-head, %d processes, 1 BLAS thread each; wall %.1f s"
-                  % (cfg.H_kv, n_tok, codes, cfg.n_s, workers, wall),
+                  "one process per (batch entry, kv-head), %d at a time, 1 BLAS thread each; wall %.1f s"
+                  % (n_b - 1, cfg.H_kv, n_tok, codes, cfg.n_s, workers, wall),
         "encode_codes_per_s": codes / wall,
     }
 
@@ -112,7 +113,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=2, help="workload index 1-4 (single layer)")
-    ap.add_argument("--cpu-tokens", type=int, default=1024, help="context tokens in the oracle sample")
+    ap.add_argument("--cpu-tokens", type=int, default=8192, help="context tokens in the oracle sample")
+    ap.add_argument("--cpu-batch", type=int, default=2, help="batch entries in the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
@@ -125,7 +127,7 @@ def main():
     import torch
     import sub_bit_loop_amd as lv
     from synth import config_by_index
-    from tests.helpers import build_inputs
+    from synth import build_inputs
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -188,6 +190,32 @@ def main():
     enc_ms = sum(e[0].elapsed_time(e[1]) + e[1].elapsed_time(e[2]) for e in evs) / (2 * args.steps)
     dec_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
 
+    # Per-step usage (the review's kernel serves one loop step per call and
+    # re-reads the index rows every step): T calls with n_steps = 1.
+    ps_ms = None
+    if cfg.T > 1:
+        qs = [inp["q"][:, :, t:t + 1].contiguous() for t in range(cfg.T)]
+        outs = torch.empty((cfg.B, cfg.H_q, 1, cfg.D), dtype=torch.float32, device="cuda")
+        lses = torch.empty((cfg.B, cfg.H_q, 1), dtype=torch.float32, device="cuda")
+        ws1 = torch.empty(max(4, lv.decode_workspace_bytes(g, cfg.B, cfg.N, 0, 1)), dtype=torch.uint8,
+                          device="cuda")
+
+        def per_step():
+            for t in range(cfg.T):
+                lv.decode_attn(g, qs[t], kidx, vidx, inp["k_cb"], inp["v_cb"], inp["sink_k"], inp["sink_v"],
+                               rope, step0=t, out=outs, lse=lses, workspace=ws1)
+        per_step()
+        torch.cuda.synchronize()
+        p0 = torch.cuda.Event(enable_timing=True)
+        p1 = torch.cuda.Event(enable_timing=True)
+        reps = max(1, min(args.steps, 10))
+        p0.record()
+        for _ in range(reps):
+            per_step()
+        p1.record()
+        torch.cuda.synchronize()
+        ps_ms = p0.elapsed_time(p1) / reps
+
     units = cfg.B * cfg.H_kv * cfg.N * cfg.n_blk                  # decode units per call
     codes_per_call = cfg.B * cfg.H_kv * cfg.n_blk * cfg.N * cfg.chunks
     idx_bytes = 2 * cfg.chunks                                     # K + V index bytes per unit
@@ -227,12 +255,15 @@ def main():
                    "units_per_s": units / (dec_ms * 1e-3), "index_GBps": dec_gbs,
                    "hbm_frac_index_bytes": dec_gbs / HBM_PEAK_GBS},
         "encode": {"ms_per_call": enc_ms, "codes_per_s": codes_per_call / (enc_ms * 1e-3), "GBps": enc_gbs},
+        "decode_per_step": None if ps_ms is None else {
+            "ms_all_steps": ps_ms, "calls": cfg.T, "vs_fused": ps_ms / dec_ms,
+            "note": "one call per loop step (n_steps = 1), each re-reading the index rows"},
         "roofline": dominant,
         "roofline_decode": roof_dec,
         "input_generation_s": t_gen,
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(cfg, inp, min(args.cpu_tokens, cfg.N))
+        res["cpu_baseline"] = cpu_baseline(cfg, inp, min(args.cpu_tokens, cfg.N), max(1, min(args.cpu_batch, cfg.B)))
     print(json.dumps(res), flush=True)
 
 

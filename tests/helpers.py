@@ -10,38 +10,13 @@ import numpy as np
 import torch
 
 import oracle as ref
-from synth import config_by_index, gen_kv_layer, gen_queries, gen_sinks, gen_tasq_params, train_codebooks
+from synth import build_inputs, config_by_index, random_codebooks  # noqa: F401 (re-exported)
 
 OUT_TOL = 2e-3          # max-abs error relative to the row's output L2 norm
 
 
 def small_cfg(idx, **over):
     return dataclasses.replace(config_by_index(idx), **over)
-
-
-def random_codebooks(cfg, seed, device, scale=1.0):
-    g = torch.Generator(device="cpu").manual_seed(seed)
-    shp = (cfg.H_kv, cfg.n_blk, cfg.K, cfg.G)
-    kc = (torch.randn(shp, generator=g) * scale).to(torch.bfloat16)
-    vc = (torch.randn(shp, generator=g) * scale).to(torch.bfloat16)
-    return kc.to(device), vc.to(device)
-
-
-def build_inputs(cfg, layer=0, device="cuda", kmeans=True, cb_seed=1):
-    """All inputs of one layer on `device`."""
-    k = gen_kv_layer(cfg, layer, "k", device)
-    v = gen_kv_layer(cfg, layer, "v", device)
-    sk, sv = gen_sinks(cfg, layer, device)
-    q = gen_queries(cfg, layer, device)
-    if kmeans:
-        kc, vc = train_codebooks(cfg, layer, device, dtype=torch.float32 if device != "cpu" else torch.float64)
-    else:
-        kc, vc = random_codebooks(cfg, cb_seed, device)
-    d = dict(k=k, v=v, sink_k=sk, sink_v=sv, q=q, k_cb=kc, v_cb=vc)
-    if cfg.tasq:
-        w, perm = gen_tasq_params(cfg, layer, device)
-        d.update(w=w, perm=perm)
-    return d
 
 
 def np64(t):
