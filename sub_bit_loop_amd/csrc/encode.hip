@@ -5,15 +5,20 @@
 // joint vector is channel q*c + i of block step m; section 3.4 step 2: the
 // distances to every codebook entry are a dense matrix product.
 //
-// Each workgroup owns one (batch, kv-head, block) and 64 tokens.  The block's
-// codebook is staged in LDS as -2*e (bf16, exact) with ||e||^2 (fp32); a wave
-// takes 32 codes at a time and evaluates
-//     dt_r = ||e_r||^2 - 2 z.e_r    (= ||z - e_r||^2 - ||z||^2)
-// for 32 codewords per v_mfma_f32_32x32x16_bf16 (codewords on M, codes on N,
-// ||e||^2 preloaded in the accumulator), keeping a per-lane best/second-best.
-// A code whose two best screened values lie within twice the fp32 error bound
-// is re-scored exactly in fp64 (direct form, lowest index on ties), so the
-// written index is the exact argmin.
+// Each workgroup owns one (batch, kv-head, block) and 128 tokens.  The
+// block's codebook is staged once as -2*e (bf16, exact) with ||e||^2 split
+// into three bf16 terms; each wave then keeps the A operands of all 8
+// codeword tiles in registers.  A wave takes 32 codes at a time (two 8-byte
+// loads per lane: joint coordinates are taken in step-major order, so each
+// lane reads contiguous channels of two steps) and evaluates
+//     s_r = ||e_r||^2 + u - 2 z.e_r    (u ~ ||z||^2, common to all r)
+// for 32 codewords per tile: a v_mfma_f32_32x32x8 for the norm terms and a
+// v_mfma_f32_32x32x16_bf16 for the products (codewords on M, codes on N).
+// Each lane keeps its best and second-best keys (value with the candidate
+// number in the low mantissa byte) with one min3, one med3 and one min per
+// two candidates.  A code whose two best screened values lie within the
+// fp32 error band is re-scored exactly in fp64 (direct form, lowest index on
+// ties), so the written index is the exact argmin.
 #include "common.h"
 #include "kernels.h"
 
@@ -65,13 +70,17 @@ __device__ __forceinline__ uint16_t bf16_ceil(float x) {
 template <int G, int TC, bool TASQ>
 __global__ __launch_bounds__(kEncodeThreads) void encode_kernel(EncodeArgs a) {
   constexpr int D = 128;
-  constexpr int C = G / TC;        // channels per step per code
-  constexpr int CPT = D / C;       // codes per token
-  constexpr int KK = G / 16;       // MFMA k-chunks of 16
-  // Per codebook row: -2*e (G bf16) and the norm row [nh, nm, nl, 1, 1, 1, 1, 0].
+  constexpr int C = G / TC;          // channels per step per code
+  constexpr int CPT = D / C;         // codes per token
+  constexpr int LOG_CPT = __builtin_ctz(CPT);
+  constexpr int KK = G / 16;         // MFMA k-chunks of 16
+  constexpr int CW = C < 8 ? C : 8;  // contiguous channels per load
+  constexpr int NL = 8 / CW;         // loads per 8-position slot
+  static_assert(C >= 2 && (CPT & (CPT - 1)) == 0, "unsupported code shape");
+  // Per codebook row: -2*e in step-major order (G bf16) and the norm row
+  // [nh, nm, nl, 1] (||e||^2 split into three bf16 terms).
   __shared__ __attribute__((aligned(16))) uint16_t s_cb[256 * G];
-  __shared__ __attribute__((aligned(16))) uint16_t s_nb[256 * 8];
-  __shared__ float s_wmax[kEncodeThreads / kWave];
+  __shared__ __attribute__((aligned(16))) uint16_t s_nb[256 * 4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hb = blockIdx.y;
@@ -79,134 +88,192 @@ __global__ __launch_bounds__(kEncodeThreads) void encode_kernel(EncodeArgs a) {
   const int b = blockIdx.z;
   const uint16_t* cb = a.cb + (int64_t)hb * a.K * G;
 
-  float nmax = 0.f;
   {
     const int r = tid;   // one codebook row per thread
-    uint16_t nh = 0, nm = 0, nl = 0;
-    uint16_t one = 0;
+    uint16_t nh = 0, nm = 0, nl = 0, one = 0;
     if (r < a.K) {
       double s = 0.0;
 #pragma unroll
-      for (int u = 0; u < G; ++u) {
-        const float f = bf16_to_f32(cb[r * G + u]);
+      for (int p = 0; p < G; ++p) {
+        // position p = m*C + i holds joint coordinate i*T_c + m
+        const float f = bf16_to_f32(cb[r * G + (p % C) * TC + p / C]);
         s += (double)f * (double)f;
-        s_cb[r * G + u] = (uint16_t)f32_to_bf16_rne(-2.f * f);
+        s_cb[r * G + p] = (uint16_t)f32_to_bf16_rne(-2.f * f);
       }
       const float nf = (float)s;
       split3(nf, nh, nm, nl);
-      nmax = nf;
       one = 0x3f80;
     } else {
       // Padding rows never win: a huge norm, zero codeword.
 #pragma unroll
-      for (int u = 0; u < G; ++u) s_cb[r * G + u] = 0;
+      for (int p = 0; p < G; ++p) s_cb[r * G + p] = 0;
       nh = 0x7f00;   // 2^127
     }
-    uint16_t* nb = s_nb + r * 8;
-    nb[0] = nh; nb[1] = nm; nb[2] = nl; nb[3] = one; nb[4] = one; nb[5] = one; nb[6] = 0x3f80; nb[7] = 0;
+    uint16_t* nb = s_nb + r * 4;
+    nb[0] = nh; nb[1] = nm; nb[2] = nl; nb[3] = one;
   }
-  for (int off = 32; off >= 1; off >>= 1) nmax = fmaxf(nmax, __shfl_xor(nmax, off));
-  if (lane == 0) s_wmax[wave] = nmax;
   __syncthreads();
-  const float emax = fmaxf(fmaxf(s_wmax[0], s_wmax[1]), fmaxf(s_wmax[2], s_wmax[3]));
+
+  const int n = lane & 31, hh = lane >> 5;
+  // The A operands of all 8 codeword tiles stay in registers: row n of tile
+  // t is codeword 32t + n; this half-wave holds positions 16kk + 8hh .. +7.
+  // The norm rows are the A operand of a 32x32x8 product whose k = 4..7
+  // half (second half-wave) meets zeros in B.
+  s16x4_t an[8];
+  bf16x8_t av[8][KK];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    an[t] = *reinterpret_cast<const s16x4_t*>(&s_nb[(32 * t + n) * 4]);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      av[t][kk] = *reinterpret_cast<const bf16x8_t*>(&s_cb[(32 * t + n) * G + 16 * kk + 8 * hh]);
+  }
 
   const int j0 = blockIdx.x * kEncodeTokens;
   const int j1 = min(j0 + kEncodeTokens, a.N);
   const int ncodes = (j1 - j0) * CPT;
   const int ngroups = (ncodes + 31) >> 5;
-  const int n = lane & 31, hh = lane >> 5;
-  const uint16_t* xbase = a.x + b * a.xs0 + h * a.xs1 + (int64_t)(beta * TC) * a.xs2;
+  const int64_t xs2 = a.xs2, xs3 = a.xs3;
+  const uint16_t* xbase = a.x + b * a.xs0 + h * a.xs1 + (int64_t)(beta * TC) * xs2 + (int64_t)j0 * xs3;
   uint8_t* ibase = a.idx + (((int64_t)b * a.H + h) * a.n_blk + beta) * (int64_t)a.N_cap * CPT +
                    (int64_t)(a.tok0 + j0) * CPT;
   const float* wh = TASQ ? a.w + h * D : nullptr;
   const int16_t* ph = TASQ ? a.perm + h * D : nullptr;
-  const uint16_t* sgb = TASQ ? a.sigma + ((int64_t)b * a.sig_cap + a.tok0) * a.T + beta * TC : nullptr;
+  const uint16_t* sgb = TASQ ? a.sigma + ((int64_t)b * a.sig_cap + a.tok0 + j0) * a.T + beta * TC : nullptr;
   const uint32_t kmask = 0xffffff00u;   // the low byte carries the lane-local candidate number
 
-  for (int grp = wave; grp < ngroups; grp += kEncodeThreads / kWave) {
-    const int g = grp * 32 + n;
-    const bool valid = g < ncodes;
-    const int gg = valid ? g : ncodes - 1;
-    const int jl = gg / CPT, q = gg - jl * CPT;
-    const int j = j0 + jl;
-    const uint16_t* xr = xbase + (int64_t)j * a.xs3;
+  // Lane-constant part of the load address: slot s = 2kk + hh covers
+  // positions 8s .. 8s+7, i.e. steps 8s/C .. and channels (8s % C) ...
+  int64_t loff[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    const int p0 = 8 * (2 * kk + hh);
+    loff[kk] = (int64_t)(p0 / C) * xs2 + (p0 % C);
+  }
 
-    // B operand: this lane's 8 joint coordinates per k-chunk (code n, coordinates 16kk+8hh..+7).
-    bf16x8_t bz[KK];
-    bf16x8_t bzlo[KK];
-    float zz = 0.f;
+  // Loads (and, for pre-transformed keys, transforms) the joint vectors of
+  // group grp: code g = 32*grp + n is token g / CPT, chunk g % CPT.
+  auto fetch = [&](int grp, bf16x8_t (&zh)[KK], bf16x8_t (&zl)[KK], float& zz) {
+    const int g = min(grp * 32 + n, ncodes - 1);
+    const int jl = g >> LOG_CPT, q = g & (CPT - 1);
+    zz = 0.f;
+    if constexpr (!TASQ) {
+      const uint16_t* xr = xbase + (int64_t)jl * xs3 + q * C;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int u = 16 * kk + 8 * hh + e;
-        const int i = u / TC, m = u - (u / TC) * TC;
-        const int d = q * C + i;
-        if constexpr (!TASQ) {
-          const uint16_t v = xr[m * a.xs2 + d];
-          const float f = bf16_to_f32(v);
-          zz = fmaf(f, f, zz);
-          bz[kk][e] = __builtin_bit_cast(__bf16, v);
+      for (int kk = 0; kk < KK; ++kk) {
+        const uint16_t* pz = xr + loff[kk];
+        if constexpr (CW == 8) {
+          zh[kk] = *reinterpret_cast<const bf16x8_t*>(pz);
         } else {
+          uint32_t w[4];
+#pragma unroll
+          for (int l = 0; l < NL; ++l) {
+            if constexpr (CW == 4) {
+              const uint2 v = *reinterpret_cast<const uint2*>(pz + l * xs2);
+              w[2 * l] = v.x;
+              w[2 * l + 1] = v.y;
+            } else {
+              w[l] = *reinterpret_cast<const uint32_t*>(pz + l * xs2);
+            }
+          }
+          zh[kk] = __builtin_bit_cast(bf16x8_t, (uint4){w[0], w[1], w[2], w[3]});
+        }
+      }
+    } else {
+      const uint16_t* xr = xbase + (int64_t)jl * xs3;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int p = 16 * kk + 8 * hh + e;
+          const int m = p / C, d = q * C + (p % C);
           const int o = ph[d] & (D - 1);
-          const float kv = bf16_to_f32(xr[m * a.xs2 + o]);
+          const float kv = bf16_to_f32(xr[m * xs2 + o]);
           _Float16 sh;
-          const uint16_t sb = sgb[(int64_t)j * a.T + m];
+          const uint16_t sb = sgb[(int64_t)jl * a.T + m];
           __builtin_memcpy(&sh, &sb, 2);
           const float zf = (wh[o] * kv) / (float)sh;
           const uint32_t hb16 = f32_to_bf16_rne(zf);
           const uint32_t lb16 = f32_to_bf16_rne(zf - bf16_to_f32(hb16));
           zz = fmaf(zf, zf, zz);
-          bz[kk][e] = __builtin_bit_cast(__bf16, (uint16_t)hb16);
-          bzlo[kk][e] = __builtin_bit_cast(__bf16, (uint16_t)lb16);
+          zh[kk][e] = __builtin_bit_cast(__bf16, (uint16_t)hb16);
+          zl[kk][e] = __builtin_bit_cast(__bf16, (uint16_t)lb16);
         }
       }
     }
-    zz += __shfl_xor(zz, 32);   // ||z||^2 of code n (both halves)
-    // Error bound of the screened distance, and a margin that keeps every
-    // screened value positive so its bit pattern orders like the value.
-    float eps = (float)(G + 24) * 5.9604645e-08f * (2.f * emax + 2.f * zz);
-    if constexpr (TASQ) eps = 2.f * eps + 3.0517578e-05f * (zz + emax);
-    const uint16_t beta_b = bf16_ceil(2.f * eps + 1e-30f);
-    bf16x8_t bn;
-    {
-      uint16_t zh, zm, zl;
-      split3(zz, zh, zm, zl);
-      const uint16_t one = hh == 0 ? 0x3f80 : 0;
-      bn[0] = __builtin_bit_cast(__bf16, one);
-      bn[1] = __builtin_bit_cast(__bf16, one);
-      bn[2] = __builtin_bit_cast(__bf16, one);
-      bn[3] = __builtin_bit_cast(__bf16, (uint16_t)(hh == 0 ? zh : 0));
-      bn[4] = __builtin_bit_cast(__bf16, (uint16_t)(hh == 0 ? zm : 0));
-      bn[5] = __builtin_bit_cast(__bf16, (uint16_t)(hh == 0 ? zl : 0));
-      bn[6] = __builtin_bit_cast(__bf16, (uint16_t)(hh == 0 ? beta_b : 0));
-      bn[7] = __builtin_bit_cast(__bf16, (uint16_t)0);
+  };
+
+  // The next group's loads are issued before the current group is screened.
+  constexpr int WS = kEncodeThreads / kWave;
+  bf16x8_t bz[KK], bzlo[KK];
+  float zzp;
+  fetch(wave, bz, bzlo, zzp);
+  for (int grp = wave; grp < ngroups; grp += WS) {
+    bf16x8_t cz[KK], czlo[KK];
+    float zz = zzp;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      cz[kk] = bz[kk];
+      if constexpr (TASQ) czlo[kk] = bzlo[kk];
     }
+    fetch(min(grp + WS, ngroups - 1), bz, bzlo, zzp);
+    const int g = grp * 32 + n;
+    const bool valid = g < ncodes;
+
+    if constexpr (!TASQ) {
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const uint4 w = __builtin_bit_cast(uint4, cz[kk]);
+        zz = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.x), __builtin_bit_cast(bf16x2_t, w.x), zz, false);
+        zz = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.y), __builtin_bit_cast(bf16x2_t, w.y), zz, false);
+        zz = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.z), __builtin_bit_cast(bf16x2_t, w.z), zz, false);
+        zz = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.w), __builtin_bit_cast(bf16x2_t, w.w), zz, false);
+      }
+    }
+    zz += __shfl_xor(zz, 32);   // ||z||^2 of code n (both halves)
+    // B operand of the norm product: [1, 1, 1, u] in the first half-wave,
+    // zero in the second.  u >= ||z||^2 (1 + 2^-8) keeps the screened values
+    // of every candidate that can come near the minimum positive, so their
+    // bit patterns order like the values.
+    const uint32_t zzb = bf16_ceil(zz * (1.f + 0x1p-8f) + 1e-30f);
+    const uint2 bnw = hh == 0 ? (uint2){0x3f803f80u, 0x3f80u | (zzb << 16)} : (uint2){0u, 0u};
+    const s16x4_t bn = __builtin_bit_cast(s16x4_t, bnw);
 
     // Screening: every value is ||z - e_r||^2 + margin (fp32 MFMA); the key
     // replaces the low mantissa byte with the lane-local candidate number.
-    // Keys are positive finite floats whose low byte is the candidate number,
-    // so float min / median order them exactly like the screened values.
+    // Keys are positive finite floats, so float min / median order them like
+    // the screened values.  Two candidates per step: k1 = min3, and the new
+    // second best is min(k2, median(k1_old, a, b)).
     float k1 = INFINITY, k2 = INFINITY;
-#pragma unroll 2
-    for (int t = 0; t < 8; ++t) {
-      f32x16_t acc = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      const bf16x8_t an = *reinterpret_cast<const bf16x8_t*>(&s_nb[(32 * t + n) * 8 + 0]);
-      bf16x8_t anz;
-      if (hh == 0) anz = an; else anz = bf16x8_t{};
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(anz, bn, acc, 0, 0, 0);
+    auto norms = [&](int t) {
+      const f32x16_t z16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      return __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(an[t], bn, z16, 0, 0, 0);
+    };
+    auto screen = [&](f32x16_t acc, int t) {
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
-        const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(&s_cb[(32 * t + n) * G + 16 * kk + 8 * hh]);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bz[kk], acc, 0, 0, 0);
-        if constexpr (TASQ) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bzlo[kk], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[t][kk], cz[kk], acc, 0, 0, 0);
+        if constexpr (TASQ) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[t][kk], czlo[kk], acc, 0, 0, 0);
       }
+      return acc;
+    };
+    auto select = [&](const f32x16_t& acc, int t) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float key = __uint_as_float(__builtin_amdgcn_perm(__float_as_uint(acc[i]), (uint32_t)(16 * t + i), 0x07060500u));
-        k2 = __builtin_amdgcn_fmed3f(k1, k2, key);
-        k1 = fminf(k1, key);
+      for (int i = 0; i < 16; i += 2) {
+        const float ka = __uint_as_float(__builtin_amdgcn_perm(__float_as_uint(acc[i]), (uint32_t)(16 * t + i), 0x07060500u));
+        const float kb = __uint_as_float(__builtin_amdgcn_perm(__float_as_uint(acc[i + 1]), (uint32_t)(16 * t + i + 1), 0x07060500u));
+        const float md = __builtin_amdgcn_fmed3f(k1, ka, kb);
+        k1 = fminf(k1, fminf(ka, kb));
+        k2 = fminf(k2, md);
       }
+    };
+    // The norm product of tile t+1 is issued before tile t's selection.
+    f32x16_t accn = norms(0);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const f32x16_t acc = screen(accn, t);
+      if (t + 1 < 8) accn = norms(t + 1);
+      select(acc, t);
     }
     // Merge the two half-waves (lanes n and n+32 screen different codewords).
     const uint32_t uk1 = __float_as_uint(k1), uk2 = __float_as_uint(k2);
@@ -219,27 +286,40 @@ __global__ __launch_bounds__(kEncodeThreads) void encode_kernel(EncodeArgs a) {
     // second smallest screened value over both halves
     const float s_own2 = __uint_as_float(uk2 & kmask), s_oth2 = __uint_as_float(ok2 & kmask);
     const float t2 = mine ? fminf(s_own2, ov1) : fminf(s_oth2, v1);
-    const float thr = t1 * (1.f + 6.1035156e-05f) + 2.f * eps;
+    // Exactness band.  A screened value carries at most kErr * (||e||^2 +
+    // u) of fp32 rounding (the MFMA sums 4 + G exact bf16 products; |partial
+    // sums| <= 2 (||e||^2 + u)).  Only candidates whose screened value can
+    // reach the band matter; their distance is below Tb, so their norm is
+    // below (||z|| + sqrt(Tb))^2 <= 2 (||z||^2 + Tb).  The key's low byte
+    // adds < 2^-15 t1.
+    constexpr float kErr = (float)(2 * G + 16) * 0x1p-24f;
+    const float Tb = t1 * 1.0625f + zz * 0x1p-6f;
+    const float nb = 2.f * (zz + Tb);
+    float eps = kErr * (nb + 1.02f * zz);
+    if constexpr (TASQ) eps = 2.f * eps + 0x1p-15f * (zz + nb);
+    const float thr = t1 * (1.f + 0x1p-14f) + 2.f * eps;
     const bool tie = valid && !(t2 > thr);
     const int loc = (int)(wkey & 0xffu);
     int res = 32 * (loc >> 4) + 8 * ((loc & 15) >> 2) + 4 * whalf + (loc & 3);
 
     if (__builtin_expect(__ballot(tie) != 0, 0)) {
       // Rare path: re-screen and score every candidate inside the band exactly
-      // in fp64 (direct form); lowest index wins exact ties.
+      // in fp64 (direct form, step-major positions); lowest index wins exact ties.
+      const int gc = min(g, ncodes - 1);
+      const int jl = gc >> LOG_CPT, q = gc & (CPT - 1);
+      const uint16_t* xr = xbase + (int64_t)jl * xs3;
       double zd[G];
       if (tie) {
 #pragma unroll
-        for (int u = 0; u < G; ++u) {
-          const int i = u / TC, m = u - (u / TC) * TC;
-          const int d = q * C + i;
+        for (int p = 0; p < G; ++p) {
+          const int m = p / C, d = q * C + (p % C);
           if constexpr (!TASQ) {
-            zd[u] = (double)bf16_to_f32(xr[m * a.xs2 + d]);
+            zd[p] = (double)bf16_to_f32(xr[m * xs2 + d]);
           } else {
             const int o = ph[d] & (D - 1);
-            const double kv = (double)bf16_to_f32(xr[m * a.xs2 + o]);
-            const double sg = f16_bits_to_f64(sgb[(int64_t)j * a.T + m]);
-            zd[u] = ((double)wh[o] * kv) / sg;
+            const double kv = (double)bf16_to_f32(xr[m * xs2 + o]);
+            const double sg = f16_bits_to_f64(sgb[(int64_t)jl * a.T + m]);
+            zd[p] = ((double)wh[o] * kv) / sg;
           }
         }
       }
@@ -249,15 +329,13 @@ __global__ __launch_bounds__(kEncodeThreads) void encode_kernel(EncodeArgs a) {
 #pragma unroll 1
       for (int t = 0; t < 8; ++t) {
         f32x16_t acc = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        const bf16x8_t an = *reinterpret_cast<const bf16x8_t*>(&s_nb[(32 * t + n) * 8 + 0]);
-        bf16x8_t anz;
-        if (hh == 0) anz = an; else anz = bf16x8_t{};
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(anz, bn, acc, 0, 0, 0);
+        const s16x4_t rn = *reinterpret_cast<const s16x4_t*>(&s_nb[(32 * t + n) * 4]);
+        acc = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(rn, bn, acc, 0, 0, 0);
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-          const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(&s_cb[(32 * t + n) * G + 16 * kk + 8 * hh]);
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bz[kk], acc, 0, 0, 0);
-          if constexpr (TASQ) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bzlo[kk], acc, 0, 0, 0);
+          const bf16x8_t rv = *reinterpret_cast<const bf16x8_t*>(&s_cb[(32 * t + n) * G + 16 * kk + 8 * hh]);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rv, cz[kk], acc, 0, 0, 0);
+          if constexpr (TASQ) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rv, czlo[kk], acc, 0, 0, 0);
         }
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -265,9 +343,9 @@ __global__ __launch_bounds__(kEncodeThreads) void encode_kernel(EncodeArgs a) {
           if (tv <= lim) {
             const int r = 32 * t + 8 * (i >> 2) + 4 * hh + (i & 3);
             double dist = 0.0;
-            for (int u = 0; u < G; ++u) {
-              const double e = -0.5 * (double)bf16_to_f32(s_cb[r * G + u]);
-              const double df = zd[u] - e;
+            for (int p = 0; p < G; ++p) {
+              const double e = -0.5 * (double)bf16_to_f32(s_cb[r * G + p]);
+              const double df = zd[p] - e;
               dist += df * df;
             }
             if (r < a.K && (dist < best || (dist == best && r < bi))) {

@@ -66,6 +66,6 @@ hipError_t launch_decode_fast(int G, const DecodeArgs& a, hipStream_t s);
 
 constexpr int kDecodeThreads = 256;
 constexpr int kEncodeThreads = 256;
-constexpr int kEncodeTokens = 64;  // tokens per encode workgroup
+constexpr int kEncodeTokens = 128;  // tokens per encode workgroup
 
 }  // namespace loopvq
