@@ -82,7 +82,8 @@ __global__ __launch_bounds__(kEncodeThreads) void encode_kernel(EncodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t s_cb[256 * G];
   __shared__ __attribute__((aligned(16))) uint16_t s_nb[256 * 4];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hb = blockIdx.y;
   const int h = hb / a.n_blk, beta = hb - h * a.n_blk;
   const int b = blockIdx.z;
@@ -144,21 +145,36 @@ __global__ __launch_bounds__(kEncodeThreads) void encode_kernel(EncodeArgs a) {
 
   // Lane-constant part of the load address: slot s = 2kk + hh covers
   // positions 8s .. 8s+7, i.e. steps 8s/C .. and channels (8s % C) ...
+  // With CPT >= 32 a group of 32 codes lies in one token (chunks n + a
+  // group-uniform offset); otherwise it spans 32/CPT tokens.
+  const int ntok = j1 - j0;
   int64_t loff[KK];
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) {
     const int p0 = 8 * (2 * kk + hh);
-    loff[kk] = (int64_t)(p0 / C) * xs2 + (p0 % C);
+    loff[kk] = (int64_t)(p0 / C) * xs2 + (p0 % C) + (CPT >= 32 ? n * C : (n & (CPT - 1)) * C);
   }
+  // token (relative to j0) and chunk of this lane's code in group grp
+  auto code_pos = [&](int grp, int& jl, int& q) {
+    const int g0 = grp * 32;
+    if constexpr (CPT >= 32) {
+      jl = g0 >> LOG_CPT;
+      q = (g0 & (CPT - 1)) + n;
+    } else {
+      jl = min((g0 >> LOG_CPT) + (n >> LOG_CPT), ntok - 1);
+      q = n & (CPT - 1);
+    }
+  };
 
   // Loads (and, for pre-transformed keys, transforms) the joint vectors of
   // group grp: code g = 32*grp + n is token g / CPT, chunk g % CPT.
   auto fetch = [&](int grp, bf16x8_t (&zh)[KK], bf16x8_t (&zl)[KK], float& zz) {
-    const int g = min(grp * 32 + n, ncodes - 1);
-    const int jl = g >> LOG_CPT, q = g & (CPT - 1);
+    int jl, q;
+    code_pos(grp, jl, q);
     zz = 0.f;
     if constexpr (!TASQ) {
-      const uint16_t* xr = xbase + (int64_t)jl * xs3 + q * C;
+      // group-uniform part of the address (the lane part is in loff)
+      const uint16_t* xr = xbase + (int64_t)jl * xs3 + (CPT >= 32 ? (q - n) * C : 0);
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
         const uint16_t* pz = xr + loff[kk];
@@ -218,7 +234,7 @@ __global__ __launch_bounds__(kEncodeThreads) void encode_kernel(EncodeArgs a) {
     }
     fetch(min(grp + WS, ngroups - 1), bz, bzlo, zzp);
     const int g = grp * 32 + n;
-    const bool valid = g < ncodes;
+    const bool valid = CPT >= 32 || g < ncodes;
 
     if constexpr (!TASQ) {
 #pragma unroll
@@ -275,17 +291,19 @@ __global__ __launch_bounds__(kEncodeThreads) void encode_kernel(EncodeArgs a) {
       if (t + 1 < 8) accn = norms(t + 1);
       select(acc, t);
     }
-    // Merge the two half-waves (lanes n and n+32 screen different codewords).
-    const uint32_t uk1 = __float_as_uint(k1), uk2 = __float_as_uint(k2);
-    const uint32_t ok1 = __shfl_xor(uk1, 32), ok2 = __shfl_xor(uk2, 32);
-    const float v1 = __uint_as_float(uk1 & kmask), ov1 = __uint_as_float(ok1 & kmask);
-    const bool mine = v1 < ov1 || (v1 == ov1 && hh == 0);
-    const uint32_t wkey = mine ? uk1 : ok1;
-    const int whalf = mine ? hh : hh ^ 1;
-    const float t1 = __uint_as_float(wkey & kmask);
+    // Merge the two half-waves (lanes n and n+32 screen different codewords):
+    // after the swaps both lanes of a code hold the first half's keys (a*)
+    // and the second half's keys (b*) and take the same decision.
+    const auto s1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(k1), __float_as_uint(k1), false, false);
+    const auto s2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(k2), __float_as_uint(k2), false, false);
+    const uint32_t a1 = s1[0], b1 = s1[1], a2 = s2[0], b2 = s2[1];
+    const float va1 = __uint_as_float(a1 & kmask), vb1 = __uint_as_float(b1 & kmask);
+    const bool first = va1 <= vb1;
+    const uint32_t wkey = first ? a1 : b1;
+    const int whalf = first ? 0 : 1;
+    const float t1 = first ? va1 : vb1;
     // second smallest screened value over both halves
-    const float s_own2 = __uint_as_float(uk2 & kmask), s_oth2 = __uint_as_float(ok2 & kmask);
-    const float t2 = mine ? fminf(s_own2, ov1) : fminf(s_oth2, v1);
+    const float t2 = first ? fminf(__uint_as_float(a2 & kmask), vb1) : fminf(__uint_as_float(b2 & kmask), va1);
     // Exactness band.  A screened value carries at most kErr * (||e||^2 +
     // u) of fp32 rounding (the MFMA sums 4 + G exact bf16 products; |partial
     // sums| <= 2 (||e||^2 + u)).  Only candidates whose screened value can
@@ -305,8 +323,8 @@ __global__ __launch_bounds__(kEncodeThreads) void encode_kernel(EncodeArgs a) {
     if (__builtin_expect(__ballot(tie) != 0, 0)) {
       // Rare path: re-screen and score every candidate inside the band exactly
       // in fp64 (direct form, step-major positions); lowest index wins exact ties.
-      const int gc = min(g, ncodes - 1);
-      const int jl = gc >> LOG_CPT, q = gc & (CPT - 1);
+      int jl, q;
+      code_pos(grp, jl, q);
       const uint16_t* xr = xbase + (int64_t)jl * xs3;
       double zd[G];
       if (tie) {
