@@ -28,9 +28,16 @@ METRIC = "decode-attn context tokens/s per loop block + % HBM peak; encode codes
 UNIT = "context tokens/s per loop block"
 
 
-def kernel_source_hash():
+# Sources whose change invalidates a kernel's committed HBM-traffic figure.
+KERNEL_SOURCES = {
+    "encode": ("encode.hip", "common.h", "kernels.h", "loopvq_api.cpp", "calib.hip"),
+    "decode": ("decode.hip", "decode_fast.hip", "common.h", "kernels.h", "loopvq_api.cpp", "calib.hip"),
+}
+
+
+def kernel_source_hash(kernel):
     h = hashlib.sha256()
-    for f in ("encode.hip", "decode.hip", "decode_fast.hip", "common.h", "kernels.h"):
+    for f in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, "sub_bit_loop_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -38,16 +45,14 @@ def kernel_source_hash():
 
 def load_traffic(kernel, workload):
     """HBM bytes per launch from the committed counter summary, if it was taken
-    on the current kernel sources; else None."""
+    on the current sources of that kernel and on this workload; else None."""
     p = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(p):
         return None
     with open(p) as f:
         d = json.load(f)
-    if d.get("source_hash") != kernel_source_hash():
-        return None
     e = d.get("kernels", {}).get(kernel)
-    if not e or e.get("workload") != workload:
+    if not e or e.get("workload") != workload or e.get("source_hash") != kernel_source_hash(kernel):
         return None
     return e.get("bytes_per_launch")
 
@@ -105,6 +110,48 @@ def cpu_baseline(cfg, inp, n_tok, n_b):
     }
 
 
+# ----------------------------------------------------------------------------- HBM stream rates
+
+def hbm_stream(torch, nbytes=1 << 30):
+    """Time a plain 16-byte-per-lane streaming read and device copy of nbytes
+    (libloopvq_calib.so).  Returns GB/s of bytes read, and of bytes read +
+    written for the copy.  Their counter readings also calibrate FETCH_SIZE
+    and WRITE_SIZE for kernels with the same access width."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "sub_bit_loop_amd", "libloopvq_calib.so"))
+    lib.loopvq_calib_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p]
+    lib.loopvq_calib_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p]
+    lib.loopvq_calib_read_sink_words.argtypes = [ctypes.c_uint64]
+    lib.loopvq_calib_read_sink_words.restype = ctypes.c_uint64
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    sink = torch.empty(int(lib.loopvq_calib_read_sink_words(nbytes)), dtype=torch.int32, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+
+    def timed(fn, reps):
+        fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    def rd():
+        if lib.loopvq_calib_read(src.data_ptr(), nbytes, sink.data_ptr(), st) != 0:
+            raise RuntimeError("calib read launch failed")
+
+    def cp():
+        if lib.loopvq_calib_copy(src.data_ptr(), dst.data_ptr(), nbytes, st) != 0:
+            raise RuntimeError("calib copy launch failed")
+    r_ms = timed(rd, 10)
+    c_ms = timed(cp, 5)
+    del src, dst, sink
+    return {"read_GBps": nbytes / r_ms / 1e6, "copy_GBps": 2 * nbytes / c_ms / 1e6, "bytes": nbytes,
+            "note": "calib_read_kernel / calib_copy_kernel, 16 B per lane, grid-stride"}
+
+
 # ----------------------------------------------------------------------------- GPU leg
 
 def main():
@@ -116,8 +163,6 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=8192, help="context tokens in the oracle sample")
     ap.add_argument("--cpu-batch", type=int, default=2, help="batch entries in the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the LoopVQ path has no multi-GPU step in this build "
@@ -165,14 +210,7 @@ def main():
         if ev is not None:
             ev[3].record()
 
-    if args.copy_calibration:
-        # one elementwise kernel that reads 1 GiB and writes 1 GiB
-        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            torch.mul(src, 1.0, out=dst)
-        torch.cuda.synchronize()
-        del src, dst
+    stream = hbm_stream(torch)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -228,11 +266,13 @@ def main():
     roof_dec = {"kernel": "loopvq decode_attn call (decode_kernel + merge_kernel)", "bound": "hbm",
                 "achieved": dec_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dec_gbs / HBM_PEAK_GBS,
                 "traffic": load_traffic("decode", workload),
-                "algorithmic_bytes_per_launch": dec_bytes, "avg_launch_ms": dec_ms}
+                "algorithmic_bytes_per_launch": dec_bytes, "avg_launch_ms": dec_ms,
+                "frac_of_measured_read": dec_gbs / stream["read_GBps"]}
     roof_enc = {"kernel": "loopvq encode call (encode_kernel)", "bound": "hbm",
                 "achieved": enc_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": enc_gbs / HBM_PEAK_GBS,
                 "traffic": load_traffic("encode", workload),
                 "algorithmic_bytes_per_launch": enc_bytes, "avg_launch_ms": enc_ms,
+                "frac_of_measured_read": enc_gbs / stream["read_GBps"],
                 "mfma_tflops": 2.0 * cfg.K * cfg.G * codes_per_call / (enc_ms * 1e-3) / 1e12,
                 "mfma_frac_of_bf16_peak": 2.0 * cfg.K * cfg.G * codes_per_call / (enc_ms * 1e-3) / 2.5e15}
     dominant = roof_enc if 2 * enc_ms >= dec_ms else roof_dec
@@ -260,6 +300,7 @@ def main():
             "note": "one call per loop step (n_steps = 1), each re-reading the index rows"},
         "roofline": dominant,
         "roofline_decode": roof_dec,
+        "hbm_stream": stream,
         "input_generation_s": t_gen,
     }
     if not args.no_cpu_baseline:
