@@ -59,14 +59,6 @@ __device__ __forceinline__ void split3(float x, uint16_t& h, uint16_t& m, uint16
   l = (uint16_t)f32_to_bf16_rne(r2);
 }
 
-// bf16 bits of the smallest bf16 >= x (x > 0 finite).
-__device__ __forceinline__ uint16_t bf16_ceil(float x) {
-  uint32_t u = __float_as_uint(x);
-  uint32_t hi = u >> 16;
-  if (u & 0xffffu) ++hi;
-  return (uint16_t)hi;
-}
-
 template <int G, int TC, bool TASQ>
 __global__ __launch_bounds__(kEncodeThreads) void encode_kernel(EncodeArgs a) {
   constexpr int D = 128;
@@ -133,7 +125,7 @@ __global__ __launch_bounds__(kEncodeThreads) void encode_kernel(EncodeArgs a) {
   const int j0 = blockIdx.x * kEncodeTokens;
   const int j1 = min(j0 + kEncodeTokens, a.N);
   const int ncodes = (j1 - j0) * CPT;
-  const int ngroups = (ncodes + 31) >> 5;
+  const int ngroups = __builtin_amdgcn_readfirstlane((ncodes + 31) >> 5);
   const int64_t xs2 = a.xs2, xs3 = a.xs3;
   const uint16_t* xbase = a.x + b * a.xs0 + h * a.xs1 + (int64_t)(beta * TC) * xs2 + (int64_t)j0 * xs3;
   uint8_t* ibase = a.idx + (((int64_t)b * a.H + h) * a.n_blk + beta) * (int64_t)a.N_cap * CPT +
@@ -219,6 +211,12 @@ __global__ __launch_bounds__(kEncodeThreads) void encode_kernel(EncodeArgs a) {
     }
   };
 
+  // Lane constants of the norm product's B operand (zero in the second
+  // half-wave).
+  const uint32_t bn_lo = hh == 0 ? 0x3f803f80u : 0u;
+  const uint32_t bn_hmask = hh == 0 ? 0xffff0000u : 0u;
+  const uint32_t bn_one = hh == 0 ? 0x3f80u : 0u;
+
   // The next group's loads are issued before the current group is screened.
   constexpr int WS = kEncodeThreads / kWave;
   bf16x8_t bz[KK], bzlo[KK];
@@ -246,13 +244,18 @@ __global__ __launch_bounds__(kEncodeThreads) void encode_kernel(EncodeArgs a) {
         zz = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.w), __builtin_bit_cast(bf16x2_t, w.w), zz, false);
       }
     }
-    zz += __shfl_xor(zz, 32);   // ||z||^2 of code n (both halves)
+    {
+      // ||z||^2 of code n (both halves)
+      const auto zs = __builtin_amdgcn_permlane32_swap(__float_as_uint(zz), __float_as_uint(zz), false, false);
+      zz = __uint_as_float(zs[0]) + __uint_as_float(zs[1]);
+    }
     // B operand of the norm product: [1, 1, 1, u] in the first half-wave,
     // zero in the second.  u >= ||z||^2 (1 + 2^-8) keeps the screened values
     // of every candidate that can come near the minimum positive, so their
     // bit patterns order like the values.
-    const uint32_t zzb = bf16_ceil(zz * (1.f + 0x1p-8f) + 1e-30f);
-    const uint2 bnw = hh == 0 ? (uint2){0x3f803f80u, 0x3f80u | (zzb << 16)} : (uint2){0u, 0u};
+    // (bits + 0xffff) & 0xffff0000 rounds a positive float up to bf16.
+    const uint32_t zzu = __float_as_uint(fmaf(zz, 1.f + 0x1p-8f, 1e-30f));
+    const uint2 bnw = {bn_lo, ((zzu + 0xffffu) & bn_hmask) | bn_one};
     const s16x4_t bn = __builtin_bit_cast(s16x4_t, bnw);
 
     // Screening: every value is ||z - e_r||^2 + margin (fp32 MFMA); the key
@@ -276,6 +279,7 @@ __global__ __launch_bounds__(kEncodeThreads) void encode_kernel(EncodeArgs a) {
     auto select = [&](const f32x16_t& acc, int t) {
 #pragma unroll
       for (int i = 0; i < 16; i += 2) {
+        // low byte: the lane-local candidate number 16t + i
         const float ka = __uint_as_float(__builtin_amdgcn_perm(__float_as_uint(acc[i]), (uint32_t)(16 * t + i), 0x07060500u));
         const float kb = __uint_as_float(__builtin_amdgcn_perm(__float_as_uint(acc[i + 1]), (uint32_t)(16 * t + i + 1), 0x07060500u));
         const float md = __builtin_amdgcn_fmed3f(k1, ka, kb);
@@ -310,15 +314,17 @@ __global__ __launch_bounds__(kEncodeThreads) void encode_kernel(EncodeArgs a) {
     // reach the band matter; their distance is below Tb, so their norm is
     // below (||z|| + sqrt(Tb))^2 <= 2 (||z||^2 + Tb).  The key's low byte
     // adds < 2^-15 t1.
+    // With Tb = 1.0625 t1 + ||z||^2 / 64 and nb = 2 (||z||^2 + Tb):
+    //   eps = kErr (nb + 1.02 ||z||^2)  [+ for pre-transformed keys: doubled,
+    //         plus 2^-15 (||z||^2 + nb) for the two-term bf16 split of z],
+    //   thr = t1 (1 + 2^-14) + 2 eps  =  kA t1 + kB ||z||^2.
     constexpr float kErr = (float)(2 * G + 16) * 0x1p-24f;
-    const float Tb = t1 * 1.0625f + zz * 0x1p-6f;
-    const float nb = 2.f * (zz + Tb);
-    float eps = kErr * (nb + 1.02f * zz);
-    if constexpr (TASQ) eps = 2.f * eps + 0x1p-15f * (zz + nb);
-    const float thr = t1 * (1.f + 0x1p-14f) + 2.f * eps;
+    constexpr float kA = TASQ ? 1.f + 0x1p-14f + 8.5f * kErr + 2.125f * 0x1p-14f : 1.f + 0x1p-14f + 4.25f * kErr;
+    constexpr float kB = TASQ ? 12.21f * kErr + 3.04f * 0x1p-14f : 6.11f * kErr;
+    const float thr = fmaf(kA, t1, kB * zz);
     const bool tie = valid && !(t2 > thr);
-    const int loc = (int)(wkey & 0xffu);
-    int res = 32 * (loc >> 4) + 8 * ((loc & 15) >> 2) + 4 * whalf + (loc & 3);
+    // candidate 16t + i of half-wave hh is codebook entry 32t + 8(i/4) + 4hh + i%4
+    int res = (int)(((wkey & 0x7cu) << 1) | (wkey & 3u)) | (whalf << 2);
 
     if (__builtin_expect(__ballot(tie) != 0, 0)) {
       // Rare path: re-screen and score every candidate inside the band exactly
