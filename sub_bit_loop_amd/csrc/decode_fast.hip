@@ -442,12 +442,351 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_fast_kernel(DecodeArgs 
   }
 }
 
+// Single-step variant (n_steps = 1, the per-step use of the review's own
+// kernel): only the served step's slice of each codeword is staged (C fp16 per
+// entry), and the eight lanes of a token split the channels alone, so no work
+// is spent on the other steps of the block.  Lane (g4, s2) owns the chunk
+// pairs (q, q + D/(2c)) for q = g4 + 4 (s2 + 2k).
+template <int C>
+__global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(DecodeArgs a) {
+  constexpr int D = 128, HD = 64, TC = 4, G = C * TC, CPT = D / C;
+  constexpr int NP = HD / C;          // RoPE chunk pairs per token (16 or 8)
+  constexpr int NPL = NP / 8;         // chunk pairs per lane (2 or 1)
+  constexpr int DW = C / 2;           // dwords of one step of a codeword
+  constexpr int QW = C / 4;           // sin/cos quads per chunk
+  constexpr int RW = CPT / 16;        // uint4 per index row
+  constexpr int PO = NP / 8;          // word-pair offset of the RoPE partner chunks
+  constexpr int LPT = 8, SPW = kWave / LPT, NW = kDecodeThreads / kWave;
+  __shared__ __attribute__((aligned(16))) uint32_t s_k[256 * DW];
+  __shared__ __attribute__((aligned(16))) uint32_t s_v[256 * DW];
+  __shared__ float s_red[NW][D + 2];
+  __shared__ float s_amax[2][NW];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int sl = lane & 7, slot = lane >> 3;
+  const int g4 = sl & 3, s2 = sl >> 2;
+  const int split = blockIdx.x;
+  const int hq = blockIdx.y;
+  const int h = hq / a.gqa;
+  const int b = blockIdx.z;
+  const int t = a.step0;              // the one served step
+  const int beta = t / TC, m = t - beta * TC;
+
+  // ---- step m of both codebooks -> LDS (fp16), power-of-two range scaling
+  const int64_t cbo = ((int64_t)h * a.n_blk + beta) * a.K * G;
+  const int r = tid;   // one row per thread
+  float kx[C], vx[C];
+  float mk = 0.f, mv = 0.f;
+#pragma unroll
+  for (int i = 0; i < C; ++i) kx[i] = vx[i] = 0.f;
+  if (r < a.K) {
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+      // joint coordinate of channel i at step m is i*T_c + m
+      kx[i] = bf16_to_f32(a.kcb[cbo + r * G + i * TC + m]);
+      vx[i] = bf16_to_f32(a.vcb[cbo + r * G + i * TC + m]);
+      mk = fmaxf(mk, fabsf(kx[i]));
+      mv = fmaxf(mv, fabsf(vx[i]));
+    }
+  }
+  for (int off = 32; off >= 1; off >>= 1) {
+    mk = fmaxf(mk, __shfl_xor(mk, off));
+    mv = fmaxf(mv, __shfl_xor(mv, off));
+  }
+  if (lane == 0) {
+    s_amax[0][wave] = mk;
+    s_amax[1][wave] = mv;
+  }
+  __syncthreads();
+  mk = fmaxf(fmaxf(s_amax[0][0], s_amax[0][1]), fmaxf(s_amax[0][2], s_amax[0][3]));
+  mv = fmaxf(fmaxf(s_amax[1][0], s_amax[1][1]), fmaxf(s_amax[1][2], s_amax[1][3]));
+  const int shk = pow2_shift(mk, 14), shv = pow2_shift(mv, kVLim);
+  {
+    const float sk = ldexpf(1.f, -shk), sv = ldexpf(1.f, -shv);
+#pragma unroll
+    for (int ip = 0; ip < DW; ++ip) {
+      s_k[r * DW + ip] = pack_h2(kx[2 * ip] * sk, kx[2 * ip + 1] * sk);
+      s_v[r * DW + ip] = pack_h2(vx[2 * ip] * sv, vx[2 * ip + 1] * sv);
+    }
+  }
+
+  // ---- this lane's query words: chunk pairs k, partner p, channel pair ip
+  uint32_t qv[NPL][2][DW];
+  {
+    const uint16_t* qr = a.q + ((int64_t)b * a.Hq + hq) * a.n_steps * D;
+#pragma unroll
+    for (int k = 0; k < NPL; ++k)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const int d0 = p * HD + C * (g4 + 4 * (s2 + 2 * k));
+#pragma unroll
+        for (int ip = 0; ip < DW; ++ip) {
+          const uint32_t w = *reinterpret_cast<const uint32_t*>(qr + d0 + 2 * ip);
+          qv[k][p][ip] = pack_h2(bf16lo(w), bf16hi(w));
+        }
+      }
+  }
+  const float sscale = a.qscale * ldexpf(1.f, shk);
+
+  float mrow = -INFINITY, lrow = 0.f;
+  float acc[NPL][2][C];
+  uint32_t acc16[NPL][2][DW];
+#pragma unroll
+  for (int k = 0; k < NPL; ++k)
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+#pragma unroll
+      for (int c = 0; c < C; ++c) acc[k][p][c] = 0.f;
+#pragma unroll
+      for (int ip = 0; ip < DW; ++ip) acc16[k][p][ip] = 0u;
+    }
+  __syncthreads();
+
+  int nb = a.N;
+  if (a.seq_len) nb = max(0, min(a.seq_len[b], a.N));
+  const int tok_lo = split * a.tok_per_split;
+  const int tok_hi = min(nb, tok_lo + a.tok_per_split);
+  const int n_sink = split == 0 ? a.n_s : 0;
+  const int n_bf = n_sink + (split == 0 ? a.n_r : 0);
+  const int64_t irow0 = (((int64_t)b * a.H + h) * a.n_blk + beta) * (int64_t)a.N_cap;
+  const int64_t sink0 = (((int64_t)b * a.H + h) * a.T + t) * (int64_t)a.n_s;
+  const int64_t rec0 = (((int64_t)b * a.H + h) * a.T + t) * (int64_t)a.r_cap;
+  const uint16_t* rope16 = reinterpret_cast<const uint16_t*>(a.rope);
+  const float ksc = ldexpf(1.f, -shk), vsc = ldexpf(1.f, -shv);
+
+  // Kw[k] / Kw[NPL + k]: this step's words of chunk pair k and of its partner.
+  auto score = [&](const uint32_t (&Kw)[2 * NPL][DW], const uint4 (&CS)[NPL][QW]) {
+    float sc = 0.f;
+#pragma unroll
+    for (int k = 0; k < NPL; ++k)
+#pragma unroll
+      for (int ip = 0; ip < DW; ++ip) {
+        const uint4 q4 = CS[k][ip >> 1];
+        const h2_t c2 = as_h2((ip & 1) ? q4.y : q4.x), s2v = as_h2((ip & 1) ? q4.w : q4.z);
+        const h2_t x1 = as_h2(Kw[k][ip]), x2 = as_h2(Kw[NPL + k][ip]);
+        const h2_t r1 = x1 * c2 - x2 * s2v;
+        const h2_t r2 = x2 * c2 + x1 * s2v;
+        sc = __builtin_amdgcn_fdot2(r1, as_h2(qv[k][0][ip]), sc, false);
+        sc = __builtin_amdgcn_fdot2(r2, as_h2(qv[k][1][ip]), sc, false);
+      }
+    return group_sum<8>(sc) * sscale;
+  };
+  auto flush = [&]() {
+#pragma unroll
+    for (int k = 0; k < NPL; ++k)
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+#pragma unroll
+        for (int ip = 0; ip < DW; ++ip) {
+          const h2_t v = as_h2(acc16[k][p][ip]);
+          acc[k][p][2 * ip] += (float)v.x;
+          acc[k][p][2 * ip + 1] += (float)v.y;
+          acc16[k][p][ip] = 0u;
+        }
+  };
+  // Online softmax (base 2; the running maximum lags by at most kLag) and P*V.
+  auto accumulate = [&](float s, const uint32_t (&Vw)[2 * NPL][DW], bool valid) {
+    if (!valid) return;
+    if (s > mrow + (float)kLag) {
+      const float alpha = __builtin_amdgcn_exp2f(mrow - s);
+      const h2_t a2 = {(_Float16)alpha, (_Float16)alpha};
+      lrow *= alpha;
+#pragma unroll
+      for (int k = 0; k < NPL; ++k)
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+#pragma unroll
+          for (int c = 0; c < C; ++c) acc[k][p][c] *= alpha;
+#pragma unroll
+          for (int ip = 0; ip < DW; ++ip)
+            acc16[k][p][ip] = __builtin_bit_cast(uint32_t, as_h2(acc16[k][p][ip]) * a2);
+        }
+      mrow = s;
+    }
+    const float pr = __builtin_amdgcn_exp2f(s - mrow);
+    lrow += pr;
+    const h2_t p2 = {(_Float16)pr, (_Float16)pr};
+#pragma unroll
+    for (int k = 0; k < NPL; ++k)
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+#pragma unroll
+        for (int ip = 0; ip < DW; ++ip) {
+          const h2_t v2 = as_h2(Vw[p * NPL + k][ip]);
+          acc16[k][p][ip] = __builtin_bit_cast(uint32_t, v2 * p2 + as_h2(acc16[k][p][ip]));
+        }
+  };
+  auto load_cs = [&](int pos, uint4 (&CS)[NPL][QW]) {
+    const uint4* row = reinterpret_cast<const uint4*>(rope16 + (int64_t)pos * D);
+#pragma unroll
+    for (int k = 0; k < NPL; ++k)
+#pragma unroll
+      for (int u = 0; u < QW; ++u) CS[k][u] = row[QW * (g4 + 4 * (s2 + 2 * k)) + u];
+  };
+
+  // Sinks and the recent window (split 0 only), straight from the bf16 rows.
+  for (int base = 0; base < n_bf; base += NW * SPW) {
+    const int item = base + wave * SPW + slot;
+    const bool valid = item < n_bf;
+    const int it = valid ? item : 0;
+    const bool is_rec = it >= n_sink;
+    const int pos = is_rec ? a.n_s + nb + (it - n_sink) : it;
+    const uint16_t* kr = is_rec ? a.rk + (rec0 + (it - n_sink)) * D : a.sk + (sink0 + it) * D;
+    const uint16_t* vr = is_rec ? a.rv + (rec0 + (it - n_sink)) * D : a.sv + (sink0 + it) * D;
+    uint32_t Kw[2 * NPL][DW], Vw[2 * NPL][DW];
+#pragma unroll
+    for (int c = 0; c < 2 * NPL; ++c) {
+      const int k = c % NPL, p = c / NPL;
+      const int d0 = p * HD + C * (g4 + 4 * (s2 + 2 * k));
+#pragma unroll
+      for (int ip = 0; ip < DW; ++ip) {
+        const uint32_t x = *reinterpret_cast<const uint32_t*>(kr + d0 + 2 * ip);
+        const uint32_t y = *reinterpret_cast<const uint32_t*>(vr + d0 + 2 * ip);
+        Kw[c][ip] = pack_h2(bf16lo(x) * ksc, bf16hi(x) * ksc);
+        Vw[c][ip] = pack_h2(bf16lo(y) * vsc, bf16hi(y) * vsc);
+      }
+    }
+    uint4 CS[NPL][QW];
+    load_cs(pos, CS);
+    accumulate(score(Kw, CS), Vw, valid);
+    flush();
+  }
+
+  // Context tokens; index rows and sin/cos quads are prefetched one token ahead.
+  // Index byte of chunk c is byte c % 4 of word c / 4; this lane's chunks sit
+  // in word pairs (k, and k + PO for the partners) at byte 4*s2 + g4.
+  const uint32_t psel = 0x0c0c0c00u | (uint32_t)(4 * s2 + g4);
+  const int n_tok = max(0, tok_hi - tok_lo);
+  const int my = wave * SPW + slot;
+  uint4 krow[RW], vrow[RW];
+  uint4 CS[NPL][QW];
+  auto load_rows = [&](int base, int& jj) {
+    const int it = base + my;
+    jj = tok_lo + (it < n_tok ? it : n_tok - 1);   // always a real row
+    const uint4* kr = reinterpret_cast<const uint4*>(a.kidx + (irow0 + jj) * CPT);
+    const uint4* vr = reinterpret_cast<const uint4*>(a.vidx + (irow0 + jj) * CPT);
+#pragma unroll
+    for (int u = 0; u < RW; ++u) {
+      krow[u] = kr[u];
+      vrow[u] = vr[u];
+    }
+  };
+  if (n_tok > 0) {
+    int jj;
+    load_rows(0, jj);
+    load_cs(a.n_s + jj, CS);
+  }
+  int since_flush = 0;
+  for (int base = 0; base < n_tok; base += NW * SPW) {
+    const bool valid = base + my < n_tok;
+    uint32_t kd[4 * RW], vd[4 * RW];
+#pragma unroll
+    for (int u = 0; u < RW; ++u) {
+      kd[4 * u] = krow[u].x; kd[4 * u + 1] = krow[u].y; kd[4 * u + 2] = krow[u].z; kd[4 * u + 3] = krow[u].w;
+      vd[4 * u] = vrow[u].x; vd[4 * u + 1] = vrow[u].y; vd[4 * u + 2] = vrow[u].z; vd[4 * u + 3] = vrow[u].w;
+    }
+    int jn;
+    load_rows(base + NW * SPW, jn);
+    uint32_t Kw[2 * NPL][DW], Vw[2 * NPL][DW];
+#pragma unroll
+    for (int c = 0; c < 2 * NPL; ++c) {
+      const int wp = (c % NPL) + (c / NPL) * PO;     // word pair of chunk c
+      const uint32_t ik = __builtin_amdgcn_perm(kd[2 * wp + 1], kd[2 * wp], psel);
+      const uint32_t iv = __builtin_amdgcn_perm(vd[2 * wp + 1], vd[2 * wp], psel);
+      if constexpr (DW == 2) {
+        const uint2 x = *reinterpret_cast<const uint2*>(&s_k[ik * DW]);
+        const uint2 y = *reinterpret_cast<const uint2*>(&s_v[iv * DW]);
+        Kw[c][0] = x.x; Kw[c][1] = x.y;
+        Vw[c][0] = y.x; Vw[c][1] = y.y;
+      } else {
+        const uint4 x = *reinterpret_cast<const uint4*>(&s_k[ik * DW]);
+        const uint4 y = *reinterpret_cast<const uint4*>(&s_v[iv * DW]);
+        Kw[c][0] = x.x; Kw[c][1] = x.y; Kw[c][2] = x.z; Kw[c][3] = x.w;
+        Vw[c][0] = y.x; Vw[c][1] = y.y; Vw[c][2] = y.z; Vw[c][3] = y.w;
+      }
+    }
+    const float sc = score(Kw, CS);
+    load_cs(a.n_s + jn, CS);
+    accumulate(sc, Vw, valid);
+    if (++since_flush == kFlush) {
+      flush();
+      since_flush = 0;
+    }
+  }
+  flush();
+
+  // ---- merge the 8 slots of the wave (lanes with equal sl), then the waves
+#pragma unroll
+  for (int off = LPT; off < kWave; off <<= 1) {
+    const float om = __shfl_xor(mrow, off);
+    const float ol = __shfl_xor(lrow, off);
+    const float mm = fmaxf(mrow, om);
+    const float a1 = mrow == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mrow - mm);
+    const float a2 = om == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(om - mm);
+    lrow = lrow * a1 + ol * a2;
+#pragma unroll
+    for (int k = 0; k < NPL; ++k)
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+          const float oa = __shfl_xor(acc[k][p][c], off);
+          acc[k][p][c] = acc[k][p][c] * a1 + oa * a2;
+        }
+    mrow = mm;
+  }
+  if (slot == 0) {
+#pragma unroll
+    for (int k = 0; k < NPL; ++k)
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+#pragma unroll
+        for (int c = 0; c < C; ++c) s_red[wave][p * HD + C * (g4 + 4 * (s2 + 2 * k)) + c] = acc[k][p][c];
+    if (sl == 0) {
+      s_red[wave][D] = mrow;
+      s_red[wave][D + 1] = lrow;
+    }
+  }
+  __syncthreads();
+  const float osc = ldexpf(1.f, shv);
+  if (tid < D) {
+    const int d = tid;
+    float mm = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) mm = fmaxf(mm, s_red[w][D]);
+    float num = 0.f, den = 0.f;
+    if (mm != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float mw = s_red[w][D];
+        const float f = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - mm);
+        num += f * s_red[w][d];
+        den += f * s_red[w][D + 1];
+      }
+    }
+    float* dst = a.ws + (((int64_t)b * a.Hq + hq) * a.n_split + split) * (D + 1);
+    dst[d] = den > 0.f ? num / den * osc : 0.f;
+    if (d == 0) dst[D] = den > 0.f ? (mm + __log2f(den)) * 0.69314718055994531f : -INFINITY;
+  }
+}
+
 hipError_t launch_decode_fast(int G, const DecodeArgs& a, hipStream_t s) {
   dim3 grid(a.n_split, a.Hq, a.B * a.n_blk_serv);
   if (G == 16)
     hipLaunchKernelGGL(decode_fast_kernel<4>, grid, dim3(kDecodeThreads), 0, s, a);
   else if (G == 32)
     hipLaunchKernelGGL(decode_fast_kernel<8>, grid, dim3(kDecodeThreads), 0, s, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_step(int G, const DecodeArgs& a, hipStream_t s) {
+  dim3 grid(a.n_split, a.Hq, a.B);
+  if (G == 16)
+    hipLaunchKernelGGL(decode_step_kernel<4>, grid, dim3(kDecodeThreads), 0, s, a);
+  else if (G == 32)
+    hipLaunchKernelGGL(decode_step_kernel<8>, grid, dim3(kDecodeThreads), 0, s, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

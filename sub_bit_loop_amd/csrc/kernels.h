@@ -63,6 +63,8 @@ hipError_t launch_decode(int G, int TC, bool tasq, const DecodeArgs& a, hipStrea
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
 hipError_t launch_rope_table(double theta, int D, int n_pos, void* table, hipStream_t s);
 hipError_t launch_decode_fast(int G, const DecodeArgs& a, hipStream_t s);
+// n_steps == 1, T_c = 4, no pre-transform; grid (n_split, Hq, B)
+hipError_t launch_decode_step(int G, const DecodeArgs& a, hipStream_t s);
 
 constexpr int kDecodeThreads = 256;
 constexpr int kEncodeThreads = 256;

@@ -72,7 +72,9 @@ DecodePlan plan_decode(const loopvq_geom* g, int B, int N, int step0, int n_step
   const int blk1 = (step0 + n_steps - 1) / g->T_c;
   p.n_blk_serv = blk1 - p.blk0 + 1;
   const long long wgs = (long long)B * g->n_q_heads * p.n_blk_serv;
-  const int target = 512;   // about one resident round of workgroups (2 per CU)
+  // About one resident round of workgroups: 2 per CU for the multi-step
+  // kernel (255 VGPRs); the single-step kernel (95 VGPRs) fits 4.
+  const int target = n_steps == 1 ? 1024 : 512;
   long long ns = (target + wgs - 1) / wgs;
   const long long max_by_tokens = N > 0 ? (N + 255) / 256 : 1;
   if (ns > max_by_tokens) ns = max_by_tokens;
@@ -258,10 +260,13 @@ loopvq_status loopvq_decode_attn(const loopvq_geom* g, const void* q, int32_t st
   a.tok_per_split = p.tok_per_split;
   a.qscale = (float)(1.4426950408889634 / std::sqrt((double)g->D));
   // Blocks of four steps without pre-transform (0.5 and 0.25 bit): the
-  // specialised kernel; every other geometry: the generic one.
-  hipError_t e = (g->T_c == 4 && pt == nullptr)
-                     ? loopvq::launch_decode_fast(g->G, a, s)
-                     : loopvq::launch_decode(g->G, g->T_c, pt != nullptr, a, s);
+  // specialised kernels (one for a single served step, one for several);
+  // every other geometry: the generic one.
+  hipError_t e;
+  if (g->T_c == 4 && pt == nullptr)
+    e = n_steps == 1 ? loopvq::launch_decode_step(g->G, a, s) : loopvq::launch_decode_fast(g->G, a, s);
+  else
+    e = loopvq::launch_decode(g->G, g->T_c, pt != nullptr, a, s);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   loopvq::MergeArgs ma{};
   ma.ws = a.ws;

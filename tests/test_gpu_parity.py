@@ -101,7 +101,8 @@ def _check_rows(cfg, inp, kidx, vidx, sigma, out, lse, rows, step0=0, N=None, se
         sk = np64(inp["sink_k"][b, h]) if n_s else np.zeros((cfg.T, 0, cfg.D))
         sv = np64(inp["sink_v"][b, h]) if n_s else np.zeros((cfg.T, 0, cfg.D))
         o_gpu = out[b, hq, t - step0].double().cpu().numpy()
-        if Nb + n_s == 0:
+        n_r = 0 if recent is None else recent[0].shape[3]
+        if Nb + n_s + n_r == 0:
             assert np.all(o_gpu == 0) and lse[b, hq, t - step0].item() == -math.inf
             continue
         rk = rv = None
@@ -293,3 +294,52 @@ def test_recent_window_and_page_conversion(geo):
     torch.cuda.synchronize()
     w2 = _check_rows(cfg, inp, kidx, vidx, sigma, out, lse, rows, N=N + 8, recent=(rk2, rv2))
     _say("  worst rel err %.3g before, %.3g after the page conversion" % (w1, w2))
+
+
+STEP_GEOMS = [
+    # name, G, T, H_kv, H_q, B, N, n_s, n_r
+    ("half-bit-2blk-gqa2", 16, 8, 2, 4, 2, 700, 4, 0),
+    ("quarter-bit-gqa4-recent", 32, 4, 2, 8, 2, 513, 4, 40),
+    ("half-bit-nosink-recent", 16, 4, 1, 1, 3, 300, 0, 24),
+]
+
+
+@pytest.mark.parametrize("geo", STEP_GEOMS, ids=[x[0] for x in STEP_GEOMS])
+def test_per_step_decode(geo):
+    """One call per loop step (n_steps = 1), as a looped model runs its steps
+    in sequence: every row against the oracle, with per-batch lengths (one
+    batch entry with no quantized tokens), and against the fused call."""
+    s = _lib()
+    name, G, T, H, Hq, B, N, n_s, n_r = geo
+    _say("per-step decode", name)
+    cfg = small_cfg(1, G=G, T_c=4, T=T, H_kv=H, H_q=Hq, B=B, N=N + n_r, n_s=n_s,
+                    rho_k=(0.85,) * (T - 1), rho_v=(0.9,) * (T - 1), n_calib=1024, kmeans_iters=8)
+    inp = build_inputs(cfg, 0, "cuda")
+    g = _geom(s, cfg)
+    shp = (B, H, cfg.n_blk, N, cfg.chunks)
+    kidx = torch.zeros(shp, dtype=torch.uint8, device="cuda")
+    vidx = torch.zeros(shp, dtype=torch.uint8, device="cuda")
+    s.encode(g, inp["k"][:, :, :, :N], inp["k_cb"], kidx)
+    s.encode(g, inp["v"][:, :, :, :N], inp["v_cb"], vidx)
+    recent = None
+    if n_r:
+        recent = (inp["k"][:, :, :, N:].contiguous(), inp["v"][:, :, :, N:].contiguous())
+    seq = torch.tensor([N, 0, N - 77][:B], dtype=torch.int32, device="cuda")
+    fused, fused_lse = _decode(s, cfg, inp, kidx, vidx, None, N=N, seq=seq, n_s=n_s, recent=recent)
+    worst = 0.0
+    for t in range(T):
+        out, lse = _decode(s, cfg, inp, kidx, vidx, None, N=N, step0=t, n_steps=1, seq=seq, n_s=n_s,
+                           recent=recent)
+        torch.cuda.synchronize()
+        rows = [(b, hq, t) for b in range(B) for hq in range(Hq)]
+        inp_rows = inp if n_s else dict(inp, sink_k=None, sink_v=None)
+        worst = max(worst, _check_rows(cfg, inp_rows, kidx, vidx, None, out, lse, rows, step0=t,
+                                       seq=seq.cpu().numpy(), recent=recent))
+        # the single-step and the fused kernels agree within their fp16 rounding
+        d = (out[:, :, 0] - fused[:, :, t]).abs().max().item()
+        scale = fused[:, :, t].abs().max().item()
+        assert d <= 4 * OUT_TOL * max(scale, 1e-30), (t, d, scale)
+        fin = torch.isfinite(fused_lse[:, :, t])
+        assert torch.equal(fin, torch.isfinite(lse[:, :, 0]))
+        assert torch.allclose(lse[:, :, 0][fin], fused_lse[:, :, t][fin], atol=1e-3, rtol=1e-4)
+    _say("  decode worst rel err %.3g over %d steps" % (worst, T))
