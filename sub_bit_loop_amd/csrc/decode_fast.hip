@@ -442,12 +442,15 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_fast_kernel(DecodeArgs 
   }
 }
 
-// Single-step variant (n_steps = 1, the per-step use of the review's own
-// kernel): only the served step's slice of each codeword is staged (C fp16 per
-// entry), and the eight lanes of a token split the channels alone, so no work
-// is spent on the other steps of the block.  Lane (g4, s2) owns the chunk
-// pairs (q, q + D/(2c)) for q = g4 + 4 (s2 + 2k).
-template <int C>
+// Single-step variant: one workgroup serves one loop step of one (batch,
+// kv-head) for HPW q-heads of its GQA group.  Only the served step's slice of
+// each codeword is staged (C fp16 per entry) and the eight lanes of a token
+// split the channels, so no work is spent on the other steps of the block,
+// and the codeword gathers and the RoPE rotation of a key are shared by the
+// HPW heads.  Lane (g4, s2) owns the chunk pairs (q, q + D/(2c)) for
+// q = g4 + 4 (s2 + 2k).  Used for per-step calls (n_steps = 1, the review's
+// own per-step use) and, one workgroup per step, for GQA groups.
+template <int C, int HPW>
 __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(DecodeArgs a) {
   constexpr int D = 128, HD = 64, TC = 4, G = C * TC, CPT = D / C;
   constexpr int NP = HD / C;          // RoPE chunk pairs per token (16 or 8)
@@ -459,17 +462,18 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(DecodeArgs 
   constexpr int LPT = 8, SPW = kWave / LPT, NW = kDecodeThreads / kWave;
   __shared__ __attribute__((aligned(16))) uint32_t s_k[256 * DW];
   __shared__ __attribute__((aligned(16))) uint32_t s_v[256 * DW];
-  __shared__ float s_red[NW][D + 2];
+  __shared__ float s_red[NW][HPW][D + 2];
   __shared__ float s_amax[2][NW];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int sl = lane & 7, slot = lane >> 3;
   const int g4 = sl & 3, s2 = sl >> 2;
   const int split = blockIdx.x;
-  const int hq = blockIdx.y;
-  const int h = hq / a.gqa;
-  const int b = blockIdx.z;
-  const int t = a.step0;              // the one served step
+  const int hq0 = blockIdx.y * HPW;   // first q-head served (HPW divides the GQA group)
+  const int h = hq0 / a.gqa;
+  const int b = blockIdx.z / a.n_steps;
+  const int tl = blockIdx.z - b * a.n_steps;   // step within the served range
+  const int t = a.step0 + tl;
   const int beta = t / TC, m = t - beta * TC;
 
   // ---- step m of both codebooks -> LDS (fp16), power-of-two range scaling
@@ -510,10 +514,11 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(DecodeArgs 
     }
   }
 
-  // ---- this lane's query words: chunk pairs k, partner p, channel pair ip
-  uint32_t qv[NPL][2][DW];
-  {
-    const uint16_t* qr = a.q + ((int64_t)b * a.Hq + hq) * a.n_steps * D;
+  // ---- query words of the served heads: head hh, chunk pairs k, partner p, channel pair ip
+  uint32_t qv[HPW][NPL][2][DW];
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) {
+    const uint16_t* qr = a.q + (((int64_t)b * a.Hq + hq0 + hh) * a.n_steps + tl) * D;
 #pragma unroll
     for (int k = 0; k < NPL; ++k)
 #pragma unroll
@@ -522,24 +527,29 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(DecodeArgs 
 #pragma unroll
         for (int ip = 0; ip < DW; ++ip) {
           const uint32_t w = *reinterpret_cast<const uint32_t*>(qr + d0 + 2 * ip);
-          qv[k][p][ip] = pack_h2(bf16lo(w), bf16hi(w));
+          qv[hh][k][p][ip] = pack_h2(bf16lo(w), bf16hi(w));
         }
       }
   }
   const float sscale = a.qscale * ldexpf(1.f, shk);
 
-  float mrow = -INFINITY, lrow = 0.f;
-  float acc[NPL][2][C];
-  uint32_t acc16[NPL][2][DW];
+  float mrow[HPW], lrow[HPW];
+  float acc[HPW][NPL][2][C];
+  uint32_t acc16[HPW][NPL][2][DW];
 #pragma unroll
-  for (int k = 0; k < NPL; ++k)
+  for (int hh = 0; hh < HPW; ++hh) {
+    mrow[hh] = -INFINITY;
+    lrow[hh] = 0.f;
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
+    for (int k = 0; k < NPL; ++k)
 #pragma unroll
-      for (int c = 0; c < C; ++c) acc[k][p][c] = 0.f;
+      for (int p = 0; p < 2; ++p) {
 #pragma unroll
-      for (int ip = 0; ip < DW; ++ip) acc16[k][p][ip] = 0u;
-    }
+        for (int c = 0; c < C; ++c) acc[hh][k][p][c] = 0.f;
+#pragma unroll
+        for (int ip = 0; ip < DW; ++ip) acc16[hh][k][p][ip] = 0u;
+      }
+  }
   __syncthreads();
 
   int nb = a.N;
@@ -555,8 +565,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(DecodeArgs 
   const float ksc = ldexpf(1.f, -shk), vsc = ldexpf(1.f, -shv);
 
   // Kw[k] / Kw[NPL + k]: this step's words of chunk pair k and of its partner.
-  auto score = [&](const uint32_t (&Kw)[2 * NPL][DW], const uint4 (&CS)[NPL][QW]) {
-    float sc = 0.f;
+  // The key is rotated once and scored against every served head.
+  auto scores = [&](const uint32_t (&Kw)[2 * NPL][DW], const uint4 (&CS)[NPL][QW], float (&sc)[HPW]) {
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) sc[hh] = 0.f;
 #pragma unroll
     for (int k = 0; k < NPL; ++k)
 #pragma unroll
@@ -566,55 +578,66 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(DecodeArgs 
         const h2_t x1 = as_h2(Kw[k][ip]), x2 = as_h2(Kw[NPL + k][ip]);
         const h2_t r1 = x1 * c2 - x2 * s2v;
         const h2_t r2 = x2 * c2 + x1 * s2v;
-        sc = __builtin_amdgcn_fdot2(r1, as_h2(qv[k][0][ip]), sc, false);
-        sc = __builtin_amdgcn_fdot2(r2, as_h2(qv[k][1][ip]), sc, false);
+#pragma unroll
+        for (int hh = 0; hh < HPW; ++hh) {
+          sc[hh] = __builtin_amdgcn_fdot2(r1, as_h2(qv[hh][k][0][ip]), sc[hh], false);
+          sc[hh] = __builtin_amdgcn_fdot2(r2, as_h2(qv[hh][k][1][ip]), sc[hh], false);
+        }
       }
-    return group_sum<8>(sc) * sscale;
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) sc[hh] = group_sum<8>(sc[hh]) * sscale;
   };
   auto flush = [&]() {
 #pragma unroll
-    for (int k = 0; k < NPL; ++k)
-#pragma unroll
-      for (int p = 0; p < 2; ++p)
-#pragma unroll
-        for (int ip = 0; ip < DW; ++ip) {
-          const h2_t v = as_h2(acc16[k][p][ip]);
-          acc[k][p][2 * ip] += (float)v.x;
-          acc[k][p][2 * ip + 1] += (float)v.y;
-          acc16[k][p][ip] = 0u;
-        }
-  };
-  // Online softmax (base 2; the running maximum lags by at most kLag) and P*V.
-  auto accumulate = [&](float s, const uint32_t (&Vw)[2 * NPL][DW], bool valid) {
-    if (!valid) return;
-    if (s > mrow + (float)kLag) {
-      const float alpha = __builtin_amdgcn_exp2f(mrow - s);
-      const h2_t a2 = {(_Float16)alpha, (_Float16)alpha};
-      lrow *= alpha;
+    for (int hh = 0; hh < HPW; ++hh)
 #pragma unroll
       for (int k = 0; k < NPL; ++k)
 #pragma unroll
-        for (int p = 0; p < 2; ++p) {
+        for (int p = 0; p < 2; ++p)
 #pragma unroll
-          for (int c = 0; c < C; ++c) acc[k][p][c] *= alpha;
+          for (int ip = 0; ip < DW; ++ip) {
+            const h2_t v = as_h2(acc16[hh][k][p][ip]);
+            acc[hh][k][p][2 * ip] += (float)v.x;
+            acc[hh][k][p][2 * ip + 1] += (float)v.y;
+            acc16[hh][k][p][ip] = 0u;
+          }
+  };
+  // Online softmax per head (base 2; the running maximum lags by at most
+  // kLag) and P*V.
+  auto accumulate = [&](const float (&sc)[HPW], const uint32_t (&Vw)[2 * NPL][DW], bool valid) {
+    if (!valid) return;
 #pragma unroll
-          for (int ip = 0; ip < DW; ++ip)
-            acc16[k][p][ip] = __builtin_bit_cast(uint32_t, as_h2(acc16[k][p][ip]) * a2);
-        }
-      mrow = s;
+    for (int hh = 0; hh < HPW; ++hh) {
+      const float s = sc[hh];
+      if (s > mrow[hh] + (float)kLag) {
+        const float alpha = __builtin_amdgcn_exp2f(mrow[hh] - s);
+        const h2_t a2 = {(_Float16)alpha, (_Float16)alpha};
+        lrow[hh] *= alpha;
+#pragma unroll
+        for (int k = 0; k < NPL; ++k)
+#pragma unroll
+          for (int p = 0; p < 2; ++p) {
+#pragma unroll
+            for (int c = 0; c < C; ++c) acc[hh][k][p][c] *= alpha;
+#pragma unroll
+            for (int ip = 0; ip < DW; ++ip)
+              acc16[hh][k][p][ip] = __builtin_bit_cast(uint32_t, as_h2(acc16[hh][k][p][ip]) * a2);
+          }
+        mrow[hh] = s;
+      }
+      const float pr = __builtin_amdgcn_exp2f(s - mrow[hh]);
+      lrow[hh] += pr;
+      const h2_t p2 = {(_Float16)pr, (_Float16)pr};
+#pragma unroll
+      for (int k = 0; k < NPL; ++k)
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+#pragma unroll
+          for (int ip = 0; ip < DW; ++ip) {
+            const h2_t v2 = as_h2(Vw[p * NPL + k][ip]);
+            acc16[hh][k][p][ip] = __builtin_bit_cast(uint32_t, v2 * p2 + as_h2(acc16[hh][k][p][ip]));
+          }
     }
-    const float pr = __builtin_amdgcn_exp2f(s - mrow);
-    lrow += pr;
-    const h2_t p2 = {(_Float16)pr, (_Float16)pr};
-#pragma unroll
-    for (int k = 0; k < NPL; ++k)
-#pragma unroll
-      for (int p = 0; p < 2; ++p)
-#pragma unroll
-        for (int ip = 0; ip < DW; ++ip) {
-          const h2_t v2 = as_h2(Vw[p * NPL + k][ip]);
-          acc16[k][p][ip] = __builtin_bit_cast(uint32_t, v2 * p2 + as_h2(acc16[k][p][ip]));
-        }
   };
   auto load_cs = [&](int pos, uint4 (&CS)[NPL][QW]) {
     const uint4* row = reinterpret_cast<const uint4*>(rope16 + (int64_t)pos * D);
@@ -648,7 +671,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(DecodeArgs 
     }
     uint4 CS[NPL][QW];
     load_cs(pos, CS);
-    accumulate(score(Kw, CS), Vw, valid);
+    float sc[HPW];
+    scores(Kw, CS, sc);
+    accumulate(sc, Vw, valid);
     flush();
   }
 
@@ -705,7 +730,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(DecodeArgs 
         Vw[c][0] = y.x; Vw[c][1] = y.y; Vw[c][2] = y.z; Vw[c][3] = y.w;
       }
     }
-    const float sc = score(Kw, CS);
+    float sc[HPW];
+    scores(Kw, CS, sc);
     load_cs(a.n_s + jn, CS);
     accumulate(sc, Vw, valid);
     if (++since_flush == kFlush) {
@@ -718,53 +744,60 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(DecodeArgs 
   // ---- merge the 8 slots of the wave (lanes with equal sl), then the waves
 #pragma unroll
   for (int off = LPT; off < kWave; off <<= 1) {
-    const float om = __shfl_xor(mrow, off);
-    const float ol = __shfl_xor(lrow, off);
-    const float mm = fmaxf(mrow, om);
-    const float a1 = mrow == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mrow - mm);
-    const float a2 = om == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(om - mm);
-    lrow = lrow * a1 + ol * a2;
 #pragma unroll
-    for (int k = 0; k < NPL; ++k)
+    for (int hh = 0; hh < HPW; ++hh) {
+      const float om = __shfl_xor(mrow[hh], off);
+      const float ol = __shfl_xor(lrow[hh], off);
+      const float mm = fmaxf(mrow[hh], om);
+      const float a1 = mrow[hh] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mrow[hh] - mm);
+      const float a2 = om == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(om - mm);
+      lrow[hh] = lrow[hh] * a1 + ol * a2;
 #pragma unroll
-      for (int p = 0; p < 2; ++p)
+      for (int k = 0; k < NPL; ++k)
 #pragma unroll
-        for (int c = 0; c < C; ++c) {
-          const float oa = __shfl_xor(acc[k][p][c], off);
-          acc[k][p][c] = acc[k][p][c] * a1 + oa * a2;
-        }
-    mrow = mm;
+        for (int p = 0; p < 2; ++p)
+#pragma unroll
+          for (int c = 0; c < C; ++c) {
+            const float oa = __shfl_xor(acc[hh][k][p][c], off);
+            acc[hh][k][p][c] = acc[hh][k][p][c] * a1 + oa * a2;
+          }
+      mrow[hh] = mm;
+    }
   }
   if (slot == 0) {
 #pragma unroll
-    for (int k = 0; k < NPL; ++k)
+    for (int hh = 0; hh < HPW; ++hh) {
 #pragma unroll
-      for (int p = 0; p < 2; ++p)
+      for (int k = 0; k < NPL; ++k)
 #pragma unroll
-        for (int c = 0; c < C; ++c) s_red[wave][p * HD + C * (g4 + 4 * (s2 + 2 * k)) + c] = acc[k][p][c];
-    if (sl == 0) {
-      s_red[wave][D] = mrow;
-      s_red[wave][D + 1] = lrow;
+        for (int p = 0; p < 2; ++p)
+#pragma unroll
+          for (int c = 0; c < C; ++c)
+            s_red[wave][hh][p * HD + C * (g4 + 4 * (s2 + 2 * k)) + c] = acc[hh][k][p][c];
+      if (sl == 0) {
+        s_red[wave][hh][D] = mrow[hh];
+        s_red[wave][hh][D + 1] = lrow[hh];
+      }
     }
   }
   __syncthreads();
   const float osc = ldexpf(1.f, shv);
-  if (tid < D) {
-    const int d = tid;
+  for (int x = tid; x < HPW * D; x += kDecodeThreads) {
+    const int hh = x / D, d = x - hh * D;
     float mm = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) mm = fmaxf(mm, s_red[w][D]);
+    for (int w = 0; w < NW; ++w) mm = fmaxf(mm, s_red[w][hh][D]);
     float num = 0.f, den = 0.f;
     if (mm != -INFINITY) {
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
-        const float mw = s_red[w][D];
+        const float mw = s_red[w][hh][D];
         const float f = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - mm);
-        num += f * s_red[w][d];
-        den += f * s_red[w][D + 1];
+        num += f * s_red[w][hh][d];
+        den += f * s_red[w][hh][D + 1];
       }
     }
-    float* dst = a.ws + (((int64_t)b * a.Hq + hq) * a.n_split + split) * (D + 1);
+    float* dst = a.ws + ((((int64_t)b * a.Hq + hq0 + hh) * a.n_steps + tl) * a.n_split + split) * (D + 1);
     dst[d] = den > 0.f ? num / den * osc : 0.f;
     if (d == 0) dst[D] = den > 0.f ? (mm + __log2f(den)) * 0.69314718055994531f : -INFINITY;
   }
@@ -781,15 +814,22 @@ hipError_t launch_decode_fast(int G, const DecodeArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_decode_step(int G, const DecodeArgs& a, hipStream_t s) {
-  dim3 grid(a.n_split, a.Hq, a.B);
-  if (G == 16)
-    hipLaunchKernelGGL(decode_step_kernel<4>, grid, dim3(kDecodeThreads), 0, s, a);
-  else if (G == 32)
-    hipLaunchKernelGGL(decode_step_kernel<8>, grid, dim3(kDecodeThreads), 0, s, a);
-  else
-    return hipErrorInvalidValue;
+template <int C>
+static hipError_t step_launch(int hpw, const DecodeArgs& a, hipStream_t s) {
+  dim3 grid(a.n_split, a.Hq / hpw, a.B * a.n_steps);
+  switch (hpw) {
+    case 1: hipLaunchKernelGGL((decode_step_kernel<C, 1>), grid, dim3(kDecodeThreads), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((decode_step_kernel<C, 2>), grid, dim3(kDecodeThreads), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((decode_step_kernel<C, 4>), grid, dim3(kDecodeThreads), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
+}
+
+hipError_t launch_decode_step(int G, int hpw, const DecodeArgs& a, hipStream_t s) {
+  if (G == 16) return step_launch<4>(hpw, a, s);
+  if (G == 32) return step_launch<8>(hpw, a, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace loopvq

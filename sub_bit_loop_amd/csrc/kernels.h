@@ -63,8 +63,9 @@ hipError_t launch_decode(int G, int TC, bool tasq, const DecodeArgs& a, hipStrea
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
 hipError_t launch_rope_table(double theta, int D, int n_pos, void* table, hipStream_t s);
 hipError_t launch_decode_fast(int G, const DecodeArgs& a, hipStream_t s);
-// n_steps == 1, T_c = 4, no pre-transform; grid (n_split, Hq, B)
-hipError_t launch_decode_step(int G, const DecodeArgs& a, hipStream_t s);
+// T_c = 4, no pre-transform; one workgroup per (split, group of hpw q-heads,
+// batch x served step); hpw in {1, 2, 4} divides the GQA group size.
+hipError_t launch_decode_step(int G, int hpw, const DecodeArgs& a, hipStream_t s);
 
 constexpr int kDecodeThreads = 256;
 constexpr int kEncodeThreads = 256;

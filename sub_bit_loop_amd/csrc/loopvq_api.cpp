@@ -63,6 +63,8 @@ loopvq_status check_pt(const loopvq_pretransform* pt, int B, int tok_end, bool n
 
 struct DecodePlan {
   int n_blk_serv, blk0, n_split, tok_per_split;
+  int hpw;            // q-heads per workgroup of the single-step kernel
+  bool step_kernel;   // T_c = 4 without pre-transform: single-step kernel
   size_t ws_bytes;
 };
 
@@ -71,10 +73,22 @@ DecodePlan plan_decode(const loopvq_geom* g, int B, int N, int step0, int n_step
   p.blk0 = step0 / g->T_c;
   const int blk1 = (step0 + n_steps - 1) / g->T_c;
   p.n_blk_serv = blk1 - p.blk0 + 1;
-  const long long wgs = (long long)B * g->n_q_heads * p.n_blk_serv;
-  // About one resident round of workgroups: 2 per CU for the multi-step
-  // kernel (255 VGPRs); the single-step kernel (95 VGPRs) fits 4.
-  const int target = n_steps == 1 ? 1024 : 512;
+  const int gqa = g->n_q_heads / g->n_kv_heads;
+  p.hpw = gqa % 4 == 0 ? 4 : (gqa % 2 == 0 ? 2 : 1);
+  // Blocks of four steps use the single-step kernel (one workgroup per served
+  // step) when a call serves one step, or when the q-heads of a GQA group can
+  // share its codeword gathers and key rotation; otherwise the multi-step
+  // kernel, which decodes each index row once for all steps of its block.
+  p.step_kernel = g->T_c == 4 && (n_steps == 1 || p.hpw > 1);
+  long long wgs;
+  int target;   // about one resident round of workgroups
+  if (p.step_kernel) {
+    wgs = (long long)B * (g->n_q_heads / p.hpw) * n_steps;
+    target = p.hpw == 1 ? 1024 : 512;   // 95 VGPRs: 4 per CU; more heads: 2
+  } else {
+    wgs = (long long)B * g->n_q_heads * p.n_blk_serv;
+    target = 512;                        // 255 VGPRs: 2 per CU
+  }
   long long ns = (target + wgs - 1) / wgs;
   const long long max_by_tokens = N > 0 ? (N + 255) / 256 : 1;
   if (ns > max_by_tokens) ns = max_by_tokens;
@@ -260,11 +274,11 @@ loopvq_status loopvq_decode_attn(const loopvq_geom* g, const void* q, int32_t st
   a.tok_per_split = p.tok_per_split;
   a.qscale = (float)(1.4426950408889634 / std::sqrt((double)g->D));
   // Blocks of four steps without pre-transform (0.5 and 0.25 bit): the
-  // specialised kernels (one for a single served step, one for several);
-  // every other geometry: the generic one.
+  // specialised kernels chosen by the plan; every other geometry: the
+  // generic one.
   hipError_t e;
   if (g->T_c == 4 && pt == nullptr)
-    e = n_steps == 1 ? loopvq::launch_decode_step(g->G, a, s) : loopvq::launch_decode_fast(g->G, a, s);
+    e = p.step_kernel ? loopvq::launch_decode_step(g->G, p.hpw, a, s) : loopvq::launch_decode_fast(g->G, a, s);
   else
     e = loopvq::launch_decode(g->G, g->T_c, pt != nullptr, a, s);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
