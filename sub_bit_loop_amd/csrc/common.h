@@ -58,17 +58,19 @@ __device__ __forceinline__ uint16_t f64_to_f16_rne(double v) {
 
 // DPP all-reduce sum over aligned groups of L lanes (L in {1,2,4,8,16}).
 // quad_perm [1,0,3,2] = 0xB1, [2,3,0,1] = 0x4E, row_half_mirror = 0x141,
-// row_mirror = 0x140: each pairs every lane with a partner inside the group.
+// row_mirror = 0x140: each pairs every lane with a partner inside the group,
+// so no source lane is ever out of range and bound_ctrl (which lets the
+// compiler fold the move into a v_add_f32_dpp) changes nothing.
 template <int L>
 __device__ __forceinline__ float group_sum(float v) {
   if constexpr (L >= 2)
-    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
   if constexpr (L >= 4)
-    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));
   if constexpr (L >= 8)
-    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, true));
   if constexpr (L >= 16)
-    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, true));
   if constexpr (L >= 32) v += __shfl_xor(v, 16);
   if constexpr (L >= 64) v += __shfl_xor(v, 32);
   return v;
