@@ -31,7 +31,8 @@ UNIT = "context tokens/s per loop block"
 # Sources whose change invalidates a kernel's committed HBM-traffic figure.
 KERNEL_SOURCES = {
     "encode": ("encode.hip", "common.h", "kernels.h", "loopvq_api.cpp", "calib.hip"),
-    "decode": ("decode.hip", "decode_fast.hip", "common.h", "kernels.h", "loopvq_api.cpp", "calib.hip"),
+    "decode": ("decode.hip", "decode_fast.hip", "decode_gqa.hip", "common.h", "kernels.h", "loopvq_api.cpp",
+               "calib.hip"),
 }
 
 

@@ -15,7 +15,7 @@ LIB = os.path.join(HERE, "libloopvq.so")
 CALIB_LIB = os.path.join(HERE, "libloopvq_calib.so")
 CALIB_SOURCES = ["calib.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["encode.hip", "decode.hip", "decode_fast.hip", "loopvq_api.cpp"]
+SOURCES = ["encode.hip", "decode.hip", "decode_fast.hip", "decode_gqa.hip", "loopvq_api.cpp"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wno-unused-command-line-argument"]
@@ -23,7 +23,10 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
 
 # The encode kernel orders float keys with v_min/v_med3; with IEEE mode off
 # those need no NaN canonicalisation (its inputs are finite by contract).
-EXTRA = {"encode.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee", "-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# The GQA decode kernel keeps its MFMA accumulators in ordinary VGPRs so that
+# it fits two waves per SIMD.
+EXTRA = {"encode.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee", "-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "decode_gqa.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src):

@@ -66,6 +66,8 @@ hipError_t launch_decode_fast(int G, const DecodeArgs& a, hipStream_t s);
 // T_c = 4, no pre-transform; one workgroup per (split, group of hpw q-heads,
 // batch x served step); hpw in {1, 2, 4} divides the GQA group size.
 hipError_t launch_decode_step(int G, int hpw, const DecodeArgs& a, hipStream_t s);
+// T_c = 4, no pre-transform, groups of 4 q-heads; grid (n_split, Hq/4, B x blocks)
+hipError_t launch_decode_gqa(int G, const DecodeArgs& a, hipStream_t s);
 
 constexpr int kDecodeThreads = 256;
 constexpr int kEncodeThreads = 256;

@@ -61,10 +61,12 @@ loopvq_status check_pt(const loopvq_pretransform* pt, int B, int tok_end, bool n
   return LOOPVQ_OK;
 }
 
+enum class DecodeKernel { kGeneric, kFast, kStep, kGqa };
+
 struct DecodePlan {
   int n_blk_serv, blk0, n_split, tok_per_split;
-  int hpw;            // q-heads per workgroup of the single-step kernel
-  bool step_kernel;   // T_c = 4 without pre-transform: single-step kernel
+  int hpw;              // q-heads per workgroup of the single-step kernel
+  DecodeKernel kernel;  // for T_c = 4 without pre-transform (else the generic one)
   size_t ws_bytes;
 };
 
@@ -75,19 +77,33 @@ DecodePlan plan_decode(const loopvq_geom* g, int B, int N, int step0, int n_step
   p.n_blk_serv = blk1 - p.blk0 + 1;
   const int gqa = g->n_q_heads / g->n_kv_heads;
   p.hpw = gqa % 4 == 0 ? 4 : (gqa % 2 == 0 ? 2 : 1);
-  // Blocks of four steps use the single-step kernel (one workgroup per served
-  // step) when a call serves one step, or when the q-heads of a GQA group can
-  // share its codeword gathers and key rotation; otherwise the multi-step
-  // kernel, which decodes each index row once for all steps of its block.
-  p.step_kernel = g->T_c == 4 && (n_steps == 1 || p.hpw > 1);
+  // Blocks of four steps: GQA groups of four q-heads with several steps served
+  // use the MFMA kernel (16 score rows per token); a single served step, or
+  // other GQA groups, use the single-step kernel (one workgroup per step,
+  // q-heads sharing gathers and rotation); otherwise the multi-step kernel,
+  // which decodes each index row once for all steps of its block.
+  if (g->T_c != 4)
+    p.kernel = DecodeKernel::kGeneric;
+  else if (gqa % 4 == 0 && n_steps > 1)
+    p.kernel = DecodeKernel::kGqa;
+  else if (n_steps == 1 || p.hpw > 1)
+    p.kernel = DecodeKernel::kStep;
+  else
+    p.kernel = DecodeKernel::kFast;
   long long wgs;
   int target;   // about one resident round of workgroups
-  if (p.step_kernel) {
-    wgs = (long long)B * (g->n_q_heads / p.hpw) * n_steps;
-    target = p.hpw == 1 ? 1024 : 512;   // 95 VGPRs: 4 per CU; more heads: 2
-  } else {
-    wgs = (long long)B * g->n_q_heads * p.n_blk_serv;
-    target = 512;                        // 255 VGPRs: 2 per CU
+  switch (p.kernel) {
+    case DecodeKernel::kStep:
+      wgs = (long long)B * (g->n_q_heads / p.hpw) * n_steps;
+      target = p.hpw == 1 ? 1024 : 512;   // 95 VGPRs: 4 per CU; more heads: 2
+      break;
+    case DecodeKernel::kGqa:
+      wgs = (long long)B * (g->n_q_heads / 4) * p.n_blk_serv;
+      target = 512;
+      break;
+    default:
+      wgs = (long long)B * g->n_q_heads * p.n_blk_serv;
+      target = 512;                        // 255 VGPRs: 2 per CU
   }
   long long ns = (target + wgs - 1) / wgs;
   const long long max_by_tokens = N > 0 ? (N + 255) / 256 : 1;
@@ -277,10 +293,14 @@ loopvq_status loopvq_decode_attn(const loopvq_geom* g, const void* q, int32_t st
   // specialised kernels chosen by the plan; every other geometry: the
   // generic one.
   hipError_t e;
-  if (g->T_c == 4 && pt == nullptr)
-    e = p.step_kernel ? loopvq::launch_decode_step(g->G, p.hpw, a, s) : loopvq::launch_decode_fast(g->G, a, s);
-  else
+  if (pt != nullptr || p.kernel == DecodeKernel::kGeneric)
     e = loopvq::launch_decode(g->G, g->T_c, pt != nullptr, a, s);
+  else if (p.kernel == DecodeKernel::kGqa)
+    e = loopvq::launch_decode_gqa(g->G, a, s);
+  else if (p.kernel == DecodeKernel::kStep)
+    e = loopvq::launch_decode_step(g->G, p.hpw, a, s);
+  else
+    e = loopvq::launch_decode_fast(g->G, a, s);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   loopvq::MergeArgs ma{};
   ma.ws = a.ws;
