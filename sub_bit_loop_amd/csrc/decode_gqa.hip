@@ -73,16 +73,24 @@ template <int C>
 __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(2))) void decode_gqa_kernel(DecodeArgs a) {
   constexpr int D = 128, HD = 64, TC = 4, G = C * TC, CPT = D / C;
   constexpr int CW = G / 8;           // uint4 per codeword (fp16, step-major)
+  // Codeword stride in uint4: one pad slot makes it odd, so the step-m slices
+  // of random codewords spread over all LDS bank groups (a stride of 4 slots
+  // would put every step-m read of a wave in the same 4 of 16 groups).
+  constexpr int CWS = CW + 1;
   constexpr int DW = C / 2;           // dwords of one step of a codeword
   constexpr int RW = CPT / 16;        // uint4 per index row
   constexpr int NW = kDecodeThreads / kWave;
   constexpr int TOK = 16;             // tokens per wave iteration
-  __shared__ __attribute__((aligned(16))) uint4 s_k[256 * CW];
-  __shared__ __attribute__((aligned(16))) uint4 s_v[256 * CW];
+  // K and V codebooks; after the token loops the same memory holds the
+  // per-wave partial rows of the final merge.
+  constexpr int KV_U4 = 2 * 256 * CWS, RED_U4 = (NW * 16 * (D + 2) * 4 + 15) / 16;
+  __shared__ __attribute__((aligned(16))) uint4 s_kv[KV_U4 > RED_U4 ? KV_U4 : RED_U4];
+  uint4* const s_k = s_kv;
+  uint4* const s_v = s_kv + 256 * CWS;
+  float (*const s_red)[16][D + 2] = reinterpret_cast<float (*)[16][D + 2]>(s_kv);
   __shared__ __attribute__((aligned(16))) uint32_t s_p[NW][TOK][4][4];      // [t][m][h] fp16 pairs (p, p)
   __shared__ float s_alpha[NW][4][4];                                        // [m][h]
   __shared__ __attribute__((aligned(16))) uint8_t s_vix[NW][CPT][TOK];      // V index bytes, transposed
-  __shared__ float s_red[NW][16][D + 2];
   __shared__ float s_amax[2][NW];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -148,8 +156,8 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
       }
 #pragma unroll
     for (int u = 0; u < CW; ++u) {
-      s_k[r * CW + u] = make_uint4(kw[4 * u], kw[4 * u + 1], kw[4 * u + 2], kw[4 * u + 3]);
-      s_v[r * CW + u] = make_uint4(vw[4 * u], vw[4 * u + 1], vw[4 * u + 2], vw[4 * u + 3]);
+      s_k[r * CWS + u] = make_uint4(kw[4 * u], kw[4 * u + 1], kw[4 * u + 2], kw[4 * u + 3]);
+      s_v[r * CWS + u] = make_uint4(vw[4 * u], vw[4 * u + 1], vw[4 * u + 2], vw[4 * u + 3]);
     }
   }
 
@@ -396,7 +404,7 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
       if constexpr (C == 8) {
         const int c = 4 * rp + q4;                          // chunk = channels 8c .. 8c+7
         const uint32_t ik = __builtin_amdgcn_ubfe(kd[c >> 2], 8 * (c & 3), 8);
-        const uint4* cw = &s_k[ik * CW];
+        const uint4* cw = &s_k[ik * CWS];
 #pragma unroll
         for (int m = 0; m < TC; ++m) {
           const uint4 x = cw[m];                            // step m: 8 channels
@@ -407,7 +415,7 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
         for (int half = 0; half < 2; ++half) {
           const int c = 8 * rp + 2 * q4 + half;             // chunk = channels 4c .. 4c+3
           const uint32_t ik = __builtin_amdgcn_ubfe(kd[c >> 2], 8 * (c & 3), 8);
-          const uint4* cw = &s_k[ik * CW];
+          const uint4* cw = &s_k[ik * CWS];
           const uint4 x0 = cw[0], x1 = cw[1];               // steps 0-1, 2-3
           Kc[0][rp][2 * half] = x0.x; Kc[0][rp][2 * half + 1] = x0.y;
           Kc[1][rp][2 * half] = x0.z; Kc[1][rp][2 * half + 1] = x0.w;
@@ -429,7 +437,7 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
       for (int t = 0; t < TOK; ++t) {
         const uint32_t iv = __builtin_amdgcn_ubfe(iw[t >> 2], 8 * (t & 3), 8);
-        const uint4 y = s_v[iv * CW + ms];
+        const uint4 y = s_v[iv * CWS + ms];
         const uint32_t Vw[4] = {y.x, y.y, y.z, y.w};
         pv(t, Vw);
       }
@@ -442,8 +450,8 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
         const uint32_t va = __builtin_amdgcn_ubfe(wa[t >> 2], 8 * (t & 3), 8);
         const uint32_t vb = __builtin_amdgcn_ubfe(wb[t >> 2], 8 * (t & 3), 8);
         // step ms of a 4-channel codeword: dwords 2ms, 2ms+1
-        const uint2 ya = reinterpret_cast<const uint2*>(&s_v[va * CW])[ms];
-        const uint2 yb = reinterpret_cast<const uint2*>(&s_v[vb * CW])[ms];
+        const uint2 ya = reinterpret_cast<const uint2*>(&s_v[va * CWS])[ms];
+        const uint2 yb = reinterpret_cast<const uint2*>(&s_v[vb * CWS])[ms];
         const uint32_t Vw[4] = {ya.x, ya.y, yb.x, yb.y};
         pv(t, Vw);
       }
@@ -452,7 +460,9 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
     wave_sync();
   }
 
-  // ---- per-wave row totals, then merge the waves through LDS
+  // ---- per-wave row totals, then merge the waves through LDS (the codebook
+  // memory, once every wave is done with it)
+  __syncthreads();
 #pragma unroll
   for (int i = 0; i < TC; ++i) {
     float l = Lr[i];
