@@ -66,7 +66,8 @@ typedef struct {
  *   sigma  device fp16 [B][N_cap][T]: per-(token, step) RMS of the layer's raw
  *          pre-RoPE key over all n_kv_heads * D channels, rounded to fp16
  *          (round to nearest even).  loopvq_encode writes it for the tokens it
- *          encodes; loopvq_decode_attn reads it.
+ *          encodes; loopvq_decode_attn reads it.  4-byte aligned (decode
+ *          reads the two steps of a half block as one word; EINVAL otherwise)
  *   N_cap  token capacity of sigma
  * The transformed key is z[d'] = (w[perm[d']] * k[perm[d']]) / sigma. */
 typedef struct {

@@ -1,0 +1,445 @@
+// LoopVQ fused decode attention for keys stored with the channel
+// pre-transform (TaSQ), blocks of T_c = 4 loop steps, c = 4 or 8 channels per
+// step per code, D = 128.
+//
+// LoopVQ review (arXiv 2611.05304), section 3.3 eq. (10) (keys multiplied by
+// per-channel weights, divided by the token's scale sigma and permuted before
+// grouping; the inverse is applied at dequant), section 3.4 step 3 (codebook
+// on chip, lookup by index, RoPE from a precomputed table after dequant,
+// Flash-Decoding split merge) and section 3.1 eq. (5) (step m reads
+// coordinate i*T_c + m of the shared codeword).
+//
+// The restored key is k[p(d')] = sigma * z[d'] / w[p(d')] (p = permutation,
+// z = codeword slice in the transformed space), rotated by RoPE at the token
+// position.  Since q . R_pos k = (R_-pos q) . k, a key is scored in the
+// transformed space against an effective query
+//     e[d'] = a[d'] cos(pos w_f) + b[d'] sin(pos w_f),   f = p(d') mod D/2,
+//     a[d'] = q[p(d')] / w[p(d')],
+//     b[d'] = +-q[p(d') +- D/2] / w[p(d')]   (+ for p(d') < D/2),
+// and the dot product is multiplied by the token's sigma.  The permutation
+// separates RoPE partners, so unlike the plain kernels no lane rotates a key:
+// every lane owns contiguous transformed channels and takes the cos/sin of
+// their (scattered) frequencies from a per-wave LDS copy of the token's table
+// row.
+//
+// Layout choices:
+//   * Codebooks in LDS as fp16, step-major inside a codeword, first half
+//     steps 0-1, second half steps 2-3 (as in the plain multi-step kernel).
+//   * 16 lanes serve a token: lane (hs, g) takes steps {2hs, 2hs+1} and the
+//     chunks D/c/8 * g .. +D/c/8-1, i.e. the 16 transformed channels
+//     16g .. 16g+15, whose index bytes are one aligned 4-byte word (c = 4) or
+//     half of one (c = 8).
+//   * Per wave iteration each lane copies one quad of its token's RoPE row
+//     into the wave's LDS tile as (cos f, sin f) fp16 pairs; lanes then read
+//     the pairs of their 16 frequencies from it.
+//   * Effective queries, scores and P*V run on packed fp16 (scores summed in
+//     fp32 by v_dot2_f32_f16); P*V partials are flushed into fp32 every
+//     kFlush tokens, with the same range bounds as the plain kernels.
+// One workgroup serves one (batch, q-head, block, context split).
+#include "common.h"
+#include "kernels.h"
+
+namespace loopvq {
+
+namespace {
+
+typedef _Float16 h2t_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ h2t_t as_h2t(uint32_t w) { return __builtin_bit_cast(h2t_t, w); }
+
+__device__ __forceinline__ uint32_t pack_h2t(float a, float b) {
+  const _Float16 x = (_Float16)a, y = (_Float16)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
+
+__device__ __forceinline__ int pow2_shift_t(float max_abs, int lim) {
+  if (!(max_abs > 0.f)) return 0;
+  const int e = ilogbf(max_abs) + 1;
+  return e > lim ? e - lim : 0;
+}
+
+// Orders this wave's LDS traffic: writes before it are visible to the wave's
+// reads after it, and reads before it complete before later writes.
+__device__ __forceinline__ void wave_sync_t() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+constexpr int kTFlush = 16, kTLag = 3, kTVLim = 7;
+constexpr uint32_t kSelLo = 0x05040100u;   // v_perm: low halves of (src1, src0)
+constexpr uint32_t kSelHi = 0x07060302u;   // v_perm: high halves of (src1, src0)
+
+}  // namespace
+
+template <int C>
+__global__ __launch_bounds__(kDecodeThreads) void decode_tasq_kernel(DecodeArgs a) {
+  constexpr int D = 128, HD = 64, TC = 4, G = C * TC, CPT = D / C;
+  constexpr int QW = C / 4;           // uint4 per codeword half (two steps)
+  constexpr int DW = C / 2;           // dwords per step of a codeword
+  constexpr int LPT = 16, SPW = kWave / LPT, NW = kDecodeThreads / kWave;
+  constexpr int NCK = CPT / 8;        // chunks per lane (4 or 2)
+  constexpr int NCH = NCK * C;        // transformed channels per lane (16)
+  constexpr int NPR = NCH / 2;        // channel pairs per lane (8)
+  constexpr int CSR = HD + 4;         // dwords per RoPE tile row (pad spreads the slots over banks)
+  __shared__ __attribute__((aligned(16))) uint4 s_k[256 * 2 * QW];
+  __shared__ __attribute__((aligned(16))) uint4 s_v[256 * 2 * QW];
+  __shared__ __attribute__((aligned(16))) uint32_t s_cs[NW][SPW][CSR];   // (cos f, sin f) fp16 pairs
+  __shared__ float s_red[NW][TC][D + 2];
+  __shared__ float s_amax[2][NW];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int sl = lane & 15, slot = lane >> 4;
+  const int hs = sl >> 3, g = sl & 7;
+  const int split = blockIdx.x;
+  const int hq = blockIdx.y;
+  const int h = hq / a.gqa;
+  const int b = blockIdx.z / a.n_blk_serv;
+  const int beta = a.blk0 + (blockIdx.z - b * a.n_blk_serv);
+
+  // ---- codebooks -> LDS (fp16, step-major), power-of-two range scaling
+  const int64_t cbo = ((int64_t)h * a.n_blk + beta) * a.K * G;
+  const int r = tid;
+  float kx[G], vx[G];
+  float mk = 0.f, mv = 0.f;
+  if (r < a.K) {
+    const uint4* pk = reinterpret_cast<const uint4*>(a.kcb + cbo + r * G);
+    const uint4* pv = reinterpret_cast<const uint4*>(a.vcb + cbo + r * G);
+#pragma unroll
+    for (int c4 = 0; c4 < G / 8; ++c4) {
+      const uint4 x = pk[c4], y = pv[c4];
+      const uint32_t xw[4] = {x.x, x.y, x.z, x.w}, yw[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        kx[8 * c4 + 2 * w] = bf16lo(xw[w]);
+        kx[8 * c4 + 2 * w + 1] = bf16hi(xw[w]);
+        vx[8 * c4 + 2 * w] = bf16lo(yw[w]);
+        vx[8 * c4 + 2 * w + 1] = bf16hi(yw[w]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      mk = fmaxf(mk, fabsf(kx[u]));
+      mv = fmaxf(mv, fabsf(vx[u]));
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < G; ++u) kx[u] = vx[u] = 0.f;
+  }
+  for (int off = 32; off >= 1; off >>= 1) {
+    mk = fmaxf(mk, __shfl_xor(mk, off));
+    mv = fmaxf(mv, __shfl_xor(mv, off));
+  }
+  if (lane == 0) {
+    s_amax[0][wave] = mk;
+    s_amax[1][wave] = mv;
+  }
+  __syncthreads();
+  mk = fmaxf(fmaxf(s_amax[0][0], s_amax[0][1]), fmaxf(s_amax[0][2], s_amax[0][3]));
+  mv = fmaxf(fmaxf(s_amax[1][0], s_amax[1][1]), fmaxf(s_amax[1][2], s_amax[1][3]));
+  const int shk = pow2_shift_t(mk, 14), shv = pow2_shift_t(mv, kTVLim);
+  {
+    const float sk = ldexpf(1.f, -shk), sv = ldexpf(1.f, -shv);
+    uint32_t kw[2 * C], vw[2 * C];   // [m][pair]
+#pragma unroll
+    for (int m = 0; m < TC; ++m)
+#pragma unroll
+      for (int ip = 0; ip < DW; ++ip) {
+        kw[m * DW + ip] = pack_h2t(kx[(2 * ip) * TC + m] * sk, kx[(2 * ip + 1) * TC + m] * sk);
+        vw[m * DW + ip] = pack_h2t(vx[(2 * ip) * TC + m] * sv, vx[(2 * ip + 1) * TC + m] * sv);
+      }
+#pragma unroll
+    for (int u = 0; u < 2 * QW; ++u) {
+      s_k[r * 2 * QW + u] = make_uint4(kw[4 * u], kw[4 * u + 1], kw[4 * u + 2], kw[4 * u + 3]);
+      s_v[r * 2 * QW + u] = make_uint4(vw[4 * u], vw[4 * u + 1], vw[4 * u + 2], vw[4 * u + 3]);
+    }
+  }
+
+  // ---- effective-query coefficients of this lane's channels d' = 16g + j
+  // for steps 2hs + ml, and the LDS addresses of their (cos, sin) pairs.
+  const int t_lo = max(a.step0, beta * TC), t_hi = min(a.step0 + a.n_steps, (beta + 1) * TC);
+  uint32_t A2[2][NPR], B2[2][NPR];
+  const uint32_t* cs_addr[NCH];
+  {
+    int och[NCH];
+    float rw[NCH];
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      const int o = a.perm[h * D + NCH * g + j] & (D - 1);   // stays in bounds for any input
+      och[j] = o;
+      rw[j] = 1.f / a.w[h * D + o];
+      cs_addr[j] = &s_cs[wave][slot][o & (HD - 1)];
+    }
+#pragma unroll
+    for (int ml = 0; ml < 2; ++ml) {
+      const int t = beta * TC + 2 * hs + ml;
+      const bool act = t >= t_lo && t < t_hi;
+      const uint16_t* qr = a.q + (((int64_t)b * a.Hq + hq) * a.n_steps + (act ? t - a.step0 : 0)) * D;
+#pragma unroll
+      for (int p = 0; p < NPR; ++p) {
+        float av[2], bv[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int o = och[2 * p + u];
+          const float qo = bf16_to_f32(qr[o]);
+          const float qp = bf16_to_f32(qr[o ^ HD]);
+          av[u] = act ? qo * rw[2 * p + u] : 0.f;
+          bv[u] = act ? (o < HD ? qp : -qp) * rw[2 * p + u] : 0.f;
+        }
+        A2[ml][p] = pack_h2t(av[0], av[1]);
+        B2[ml][p] = pack_h2t(bv[0], bv[1]);
+      }
+    }
+  }
+  const float sscale = a.qscale * ldexpf(1.f, shk);
+
+  float mrow[2] = {-INFINITY, -INFINITY}, lrow[2] = {0.f, 0.f};
+  float acc[2][NCH];
+  uint32_t acc16[2][NPR];
+#pragma unroll
+  for (int ml = 0; ml < 2; ++ml) {
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) acc[ml][j] = 0.f;
+#pragma unroll
+    for (int p = 0; p < NPR; ++p) acc16[ml][p] = 0u;
+  }
+  __syncthreads();
+
+  int nb = a.N;
+  if (a.seq_len) nb = max(0, min(a.seq_len[b], a.N));
+  const int tok_lo = split * a.tok_per_split;
+  const int tok_hi = min(nb, tok_lo + a.tok_per_split);
+  const int n_sink = split == 0 ? a.n_s : 0;
+  const int n_bf = n_sink + (split == 0 ? a.n_r : 0);
+  const int64_t irow0 = (((int64_t)b * a.H + h) * a.n_blk + beta) * (int64_t)a.N_cap;
+  const int64_t sink0 = (((int64_t)b * a.H + h) * a.T + beta * TC) * (int64_t)a.n_s;
+  const int64_t rec0 = (((int64_t)b * a.H + h) * a.T + beta * TC) * (int64_t)a.r_cap;
+  const uint16_t* rope16 = reinterpret_cast<const uint16_t*>(a.rope);
+  const float ksc = ldexpf(1.f, -shk), vsc = ldexpf(1.f, -shv);
+
+  // RoPE quad sl of position pos (4 frequencies) -> the slot's tile row.
+  auto load_quad = [&](int pos) { return reinterpret_cast<const uint4*>(rope16 + (int64_t)pos * D)[sl]; };
+  auto fill = [&](const uint4& qd) {
+    uint4 o;
+    o.x = __builtin_amdgcn_perm(qd.z, qd.x, kSelLo);
+    o.y = __builtin_amdgcn_perm(qd.z, qd.x, kSelHi);
+    o.z = __builtin_amdgcn_perm(qd.w, qd.y, kSelLo);
+    o.w = __builtin_amdgcn_perm(qd.w, qd.y, kSelHi);
+    *reinterpret_cast<uint4*>(&s_cs[wave][slot][4 * sl]) = o;
+  };
+  // Scores of the lane's two steps (summed over the 8 lanes of the token's
+  // step half); Kw[k][ml*DW + ip] = channel pair (2ip, 2ip+1) of chunk k.
+  auto scores = [&](const uint32_t (&Kw)[NCK][C], const float (&sg)[2], float (&sc)[2]) {
+    uint32_t cs2[NPR], sn2[NPR];
+#pragma unroll
+    for (int p = 0; p < NPR; ++p) {
+      const uint32_t d0 = *cs_addr[2 * p], d1 = *cs_addr[2 * p + 1];
+      cs2[p] = __builtin_amdgcn_perm(d1, d0, kSelLo);
+      sn2[p] = __builtin_amdgcn_perm(d1, d0, kSelHi);
+    }
+#pragma unroll
+    for (int ml = 0; ml < 2; ++ml) {
+      float part = 0.f;
+#pragma unroll
+      for (int p = 0; p < NPR; ++p) {
+        const h2t_t e2 = as_h2t(A2[ml][p]) * as_h2t(cs2[p]) + as_h2t(B2[ml][p]) * as_h2t(sn2[p]);
+        part = __builtin_amdgcn_fdot2(e2, as_h2t(Kw[p / DW][ml * DW + p % DW]), part, false);
+      }
+      sc[ml] = group_sum<8>(part) * sg[ml] * sscale;
+    }
+  };
+  auto flush = [&]() {
+#pragma unroll
+    for (int ml = 0; ml < 2; ++ml)
+#pragma unroll
+      for (int p = 0; p < NPR; ++p) {
+        const h2t_t v = as_h2t(acc16[ml][p]);
+        acc[ml][2 * p] += (float)v.x;
+        acc[ml][2 * p + 1] += (float)v.y;
+        acc16[ml][p] = 0u;
+      }
+  };
+  auto accumulate = [&](const float (&sc)[2], const uint32_t (&Vw)[NCK][C], bool valid) {
+    if (!valid) return;
+#pragma unroll
+    for (int ml = 0; ml < 2; ++ml) {
+      const float s = sc[ml];
+      if (s > mrow[ml] + (float)kTLag) {
+        const float alpha = __builtin_amdgcn_exp2f(mrow[ml] - s);
+        const h2t_t a2 = {(_Float16)alpha, (_Float16)alpha};
+        lrow[ml] *= alpha;
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) acc[ml][j] *= alpha;
+#pragma unroll
+        for (int p = 0; p < NPR; ++p) acc16[ml][p] = __builtin_bit_cast(uint32_t, as_h2t(acc16[ml][p]) * a2);
+        mrow[ml] = s;
+      }
+      const float pr = __builtin_amdgcn_exp2f(s - mrow[ml]);
+      lrow[ml] += pr;
+      const h2t_t p2 = {(_Float16)pr, (_Float16)pr};
+#pragma unroll
+      for (int p = 0; p < NPR; ++p)
+        acc16[ml][p] = __builtin_bit_cast(uint32_t,
+                                          as_h2t(Vw[p / DW][ml * DW + p % DW]) * p2 + as_h2t(acc16[ml][p]));
+    }
+  };
+
+  // ---- bf16 items (split 0): sinks at positions 0..n_s-1, the recent window
+  // at n_s + N_b + r.  Their keys are raw, so they enter the transformed
+  // space as w[p(d')] * k[p(d')] with sigma = 1.
+  for (int base = 0; base < n_bf; base += NW * SPW) {
+    const int item = base + wave * SPW + slot;
+    const bool valid = item < n_bf;
+    const int it = valid ? item : 0;
+    const bool is_rec = it >= n_sink;
+    const int pos = is_rec ? a.n_s + nb + (it - n_sink) : it;
+    fill(load_quad(pos));
+    wave_sync_t();
+    uint32_t Kw[NCK][C], Vw[NCK][C];
+#pragma unroll
+    for (int ml = 0; ml < 2; ++ml) {
+      const int m = 2 * hs + ml;
+      const uint16_t* kr = is_rec ? a.rk + (rec0 + (int64_t)m * a.r_cap + (it - n_sink)) * D
+                                  : a.sk + (sink0 + (int64_t)m * a.n_s + it) * D;
+      const uint16_t* vr = is_rec ? a.rv + (rec0 + (int64_t)m * a.r_cap + (it - n_sink)) * D
+                                  : a.sv + (sink0 + (int64_t)m * a.n_s + it) * D;
+#pragma unroll
+      for (int p = 0; p < NPR; ++p) {
+        float z[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int o = a.perm[h * D + NCH * g + 2 * p + u] & (D - 1);
+          z[u] = bf16_to_f32(kr[o]) * a.w[h * D + o] * ksc;
+        }
+        const uint32_t vv = *reinterpret_cast<const uint32_t*>(vr + NCH * g + 2 * p);
+        Kw[p / DW][ml * DW + p % DW] = pack_h2t(z[0], z[1]);
+        Vw[p / DW][ml * DW + p % DW] = pack_h2t(bf16lo(vv) * vsc, bf16hi(vv) * vsc);
+      }
+    }
+    const float sg[2] = {1.f, 1.f};
+    float sc[2];
+    scores(Kw, sg, sc);
+    accumulate(sc, Vw, valid);
+    flush();
+    wave_sync_t();
+  }
+
+  // ---- quantized tokens, one per lane slot per iteration; index words, sigma
+  // and the RoPE quad of the next iteration are loaded one iteration ahead.
+  const int n_tok = max(0, tok_hi - tok_lo);
+  const int my = wave * SPW + slot;
+  // word of the index row holding this lane's index bytes, and their bit offset
+  const int kwo = C == 4 ? g : (g >> 1);
+  const int kbit = C == 4 ? 0 : 16 * (g & 1);
+  uint32_t kwn = 0, vwn = 0, sgn = 0;
+  uint4 rqn = make_uint4(0, 0, 0, 0);
+  auto load_next = [&](int base) {
+    const int it = base + my;
+    const int jj = tok_lo + (it < n_tok ? it : n_tok - 1);   // always a real row
+    kwn = reinterpret_cast<const uint32_t*>(a.kidx + (irow0 + jj) * CPT)[kwo];
+    vwn = reinterpret_cast<const uint32_t*>(a.vidx + (irow0 + jj) * CPT)[kwo];
+    sgn = *reinterpret_cast<const uint32_t*>(a.sigma + ((int64_t)b * a.sig_cap + jj) * a.T + beta * TC + 2 * hs);
+    rqn = load_quad(a.n_s + jj);
+  };
+  if (n_tok > 0) load_next(0);
+  int since_flush = 0;
+  for (int base = 0; base < n_tok; base += NW * SPW) {
+    const bool valid = base + my < n_tok;
+    const uint32_t kwc = kwn, vwc = vwn, sgc = sgn;
+    fill(rqn);
+    load_next(base + NW * SPW);
+    wave_sync_t();
+    uint32_t Kw[NCK][C], Vw[NCK][C];
+#pragma unroll
+    for (int k = 0; k < NCK; ++k) {
+      const uint32_t ik = __builtin_amdgcn_ubfe(kwc, kbit + 8 * k, 8);
+      const uint32_t iv = __builtin_amdgcn_ubfe(vwc, kbit + 8 * k, 8);
+#pragma unroll
+      for (int u = 0; u < QW; ++u) {
+        const uint4 x = s_k[(2 * ik + hs) * QW + u];
+        const uint4 y = s_v[(2 * iv + hs) * QW + u];
+        Kw[k][4 * u] = x.x; Kw[k][4 * u + 1] = x.y; Kw[k][4 * u + 2] = x.z; Kw[k][4 * u + 3] = x.w;
+        Vw[k][4 * u] = y.x; Vw[k][4 * u + 1] = y.y; Vw[k][4 * u + 2] = y.z; Vw[k][4 * u + 3] = y.w;
+      }
+    }
+    const h2t_t s16 = as_h2t(sgc);
+    const float sg[2] = {(float)s16.x, (float)s16.y};
+    float sc[2];
+    scores(Kw, sg, sc);
+    accumulate(sc, Vw, valid);
+    if (++since_flush == kTFlush) {
+      flush();
+      since_flush = 0;
+    }
+    wave_sync_t();
+  }
+  flush();
+
+  // ---- merge the SPW slots of the wave (lanes with equal sl)
+#pragma unroll
+  for (int off = LPT; off < kWave; off <<= 1) {
+#pragma unroll
+    for (int ml = 0; ml < 2; ++ml) {
+      const float om = __shfl_xor(mrow[ml], off);
+      const float ol = __shfl_xor(lrow[ml], off);
+      const float mm = fmaxf(mrow[ml], om);
+      const float a1 = mrow[ml] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mrow[ml] - mm);
+      const float a2 = om == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(om - mm);
+      lrow[ml] = lrow[ml] * a1 + ol * a2;
+#pragma unroll
+      for (int j = 0; j < NCH; ++j) {
+        const float oa = __shfl_xor(acc[ml][j], off);
+        acc[ml][j] = acc[ml][j] * a1 + oa * a2;
+      }
+      mrow[ml] = mm;
+    }
+  }
+  if (slot == 0) {
+#pragma unroll
+    for (int ml = 0; ml < 2; ++ml) {
+      const int m = 2 * hs + ml;
+#pragma unroll
+      for (int j = 0; j < NCH; ++j) s_red[wave][m][NCH * g + j] = acc[ml][j];
+      if (g == 0) {
+        s_red[wave][m][D] = mrow[ml];
+        s_red[wave][m][D + 1] = lrow[ml];
+      }
+    }
+  }
+  __syncthreads();
+  const float osc = ldexpf(1.f, shv);
+  for (int x = tid; x < TC * D; x += kDecodeThreads) {
+    const int m = x / D, d = x - m * D;
+    const int t = beta * TC + m;
+    if (t < t_lo || t >= t_hi) continue;
+    float mm = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) mm = fmaxf(mm, s_red[w][m][D]);
+    float num = 0.f, den = 0.f;
+    if (mm != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float mw = s_red[w][m][D];
+        const float f = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - mm);
+        num += f * s_red[w][m][d];
+        den += f * s_red[w][m][D + 1];
+      }
+    }
+    float* dst = a.ws + ((((int64_t)b * a.Hq + hq) * a.n_steps + (t - a.step0)) * a.n_split + split) * (D + 1);
+    dst[d] = den > 0.f ? num / den * osc : 0.f;
+    if (d == 0) dst[D] = den > 0.f ? (mm + __log2f(den)) * 0.69314718055994531f : -INFINITY;
+  }
+}
+
+hipError_t launch_decode_tasq(int G, const DecodeArgs& a, hipStream_t s) {
+  dim3 grid(a.n_split, a.Hq, a.B * a.n_blk_serv);
+  if (G == 16)
+    hipLaunchKernelGGL(decode_tasq_kernel<4>, grid, dim3(kDecodeThreads), 0, s, a);
+  else if (G == 32)
+    hipLaunchKernelGGL(decode_tasq_kernel<8>, grid, dim3(kDecodeThreads), 0, s, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace loopvq

@@ -2,6 +2,7 @@
 // Every check runs before the first HIP call; no C++ exception leaves here.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -61,16 +62,16 @@ loopvq_status check_pt(const loopvq_pretransform* pt, int B, int tok_end, bool n
   return LOOPVQ_OK;
 }
 
-enum class DecodeKernel { kGeneric, kFast, kStep, kGqa };
+enum class DecodeKernel { kGeneric, kFast, kStep, kGqa, kTasq };
 
 struct DecodePlan {
   int n_blk_serv, blk0, n_split, tok_per_split;
   int hpw;              // q-heads per workgroup of the single-step kernel
-  DecodeKernel kernel;  // for T_c = 4 without pre-transform (else the generic one)
+  DecodeKernel kernel;
   size_t ws_bytes;
 };
 
-DecodePlan plan_decode(const loopvq_geom* g, int B, int N, int step0, int n_steps) {
+DecodePlan plan_decode(const loopvq_geom* g, int B, int N, int step0, int n_steps, bool tasq) {
   DecodePlan p;
   p.blk0 = step0 / g->T_c;
   const int blk1 = (step0 + n_steps - 1) / g->T_c;
@@ -82,8 +83,12 @@ DecodePlan plan_decode(const loopvq_geom* g, int B, int N, int step0, int n_step
   // other GQA groups, use the single-step kernel (one workgroup per step,
   // q-heads sharing gathers and rotation); otherwise the multi-step kernel,
   // which decodes each index row once for all steps of its block.
+  // Pre-transformed keys in blocks of four steps have their own kernel (one
+  // q-head per workgroup); other block lengths use the generic kernel.
   if (g->T_c != 4)
     p.kernel = DecodeKernel::kGeneric;
+  else if (tasq)
+    p.kernel = DecodeKernel::kTasq;
   else if (gqa % 4 == 0 && n_steps > 1)
     p.kernel = DecodeKernel::kGqa;
   else if (n_steps == 1 || p.hpw > 1)
@@ -211,7 +216,10 @@ loopvq_status loopvq_decode_attn_workspace(const loopvq_geom* g, int32_t B, int3
   loopvq_status st = check_decode_shape(g, B, N, step0, n_steps);
   if (st != LOOPVQ_OK) return st;
   if (!bytes) return fail(LOOPVQ_EINVAL, "bytes is NULL");
-  *bytes = B > 0 ? plan_decode(g, B, N, step0, n_steps).ws_bytes : 0;
+  // the caller may or may not pass a pre-transform: cover both plans
+  *bytes = B > 0 ? std::max(plan_decode(g, B, N, step0, n_steps, false).ws_bytes,
+                            plan_decode(g, B, N, step0, n_steps, true).ws_bytes)
+                 : 0;
   return LOOPVQ_OK;
 }
 
@@ -246,7 +254,9 @@ loopvq_status loopvq_decode_attn(const loopvq_geom* g, const void* q, int32_t st
   }
   st = check_pt(pt, B, N, false);
   if (st != LOOPVQ_OK) return st;
-  const DecodePlan p = plan_decode(g, B, N, step0, n_steps);
+  const DecodePlan p = plan_decode(g, B, N, step0, n_steps, pt != nullptr);
+  if (p.kernel == DecodeKernel::kTasq && reinterpret_cast<uintptr_t>(pt->sigma) % 4)
+    return fail(LOOPVQ_EINVAL, "pre-transform sigma must be 4-byte aligned");
   if (!workspace || workspace_bytes < p.ws_bytes)
     return fail(LOOPVQ_EWORKSPACE, "workspace of %zu bytes needed (got %zu)", p.ws_bytes, workspace_bytes);
 
@@ -289,12 +299,14 @@ loopvq_status loopvq_decode_attn(const loopvq_geom* g, const void* q, int32_t st
   a.n_blk_serv = p.n_blk_serv;
   a.tok_per_split = p.tok_per_split;
   a.qscale = (float)(1.4426950408889634 / std::sqrt((double)g->D));
-  // Blocks of four steps without pre-transform (0.5 and 0.25 bit): the
-  // specialised kernels chosen by the plan; every other geometry: the
-  // generic one.
+  // Blocks of four steps (0.5 and 0.25 bit, with or without the key
+  // pre-transform): the specialised kernels chosen by the plan; every other
+  // geometry: the generic one.
   hipError_t e;
-  if (pt != nullptr || p.kernel == DecodeKernel::kGeneric)
+  if (p.kernel == DecodeKernel::kGeneric)
     e = loopvq::launch_decode(g->G, g->T_c, pt != nullptr, a, s);
+  else if (p.kernel == DecodeKernel::kTasq)
+    e = loopvq::launch_decode_tasq(g->G, a, s);
   else if (p.kernel == DecodeKernel::kGqa)
     e = loopvq::launch_decode_gqa(g->G, a, s);
   else if (p.kernel == DecodeKernel::kStep)

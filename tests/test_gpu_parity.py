@@ -157,6 +157,8 @@ GEOMS = [
     ("quarter-bit-mha", 32, 4, 4, 2, 2, 2, 650, 4, 256, False),
     ("quarter-bit-2blk-gqa2", 32, 4, 8, 1, 2, 1, 480, 4, 256, False),
     ("pretransform", 16, 4, 4, 2, 2, 2, 777, 4, 256, True),
+    ("pretransform-quarter-bit", 32, 4, 4, 2, 2, 1, 600, 4, 256, True),
+    ("pretransform-2blk-gqa2", 16, 4, 8, 1, 2, 2, 500, 4, 256, True),
     ("tc2-k200-nosink", 16, 2, 4, 1, 1, 1, 300, 0, 200, False),
     ("tc1-channel-vq", 16, 1, 2, 1, 2, 1, 129, 3, 64, False),
     ("tc8", 32, 8, 8, 1, 1, 1, 200, 2, 256, False),
@@ -300,10 +302,11 @@ def test_recent_window_and_page_conversion(geo):
 
 
 STEP_GEOMS = [
-    # name, G, T, H_kv, H_q, B, N, n_s, n_r
-    ("half-bit-2blk-gqa2", 16, 8, 2, 4, 2, 700, 4, 0),
-    ("quarter-bit-gqa4-recent", 32, 4, 2, 8, 2, 513, 4, 40),
-    ("half-bit-nosink-recent", 16, 4, 1, 1, 3, 300, 0, 24),
+    # name, G, T, H_kv, H_q, B, N, n_s, n_r, pretransform
+    ("half-bit-2blk-gqa2", 16, 8, 2, 4, 2, 700, 4, 0, False),
+    ("quarter-bit-gqa4-recent", 32, 4, 2, 8, 2, 513, 4, 40, False),
+    ("half-bit-nosink-recent", 16, 4, 1, 1, 3, 300, 0, 24, False),
+    ("pretransform-recent", 16, 4, 2, 2, 2, 450, 4, 16, True),
 ]
 
 
@@ -313,30 +316,34 @@ def test_per_step_decode(geo):
     in sequence: every row against the oracle, with per-batch lengths (one
     batch entry with no quantized tokens), and against the fused call."""
     s = _lib()
-    name, G, T, H, Hq, B, N, n_s, n_r = geo
+    name, G, T, H, Hq, B, N, n_s, n_r, tasq = geo
     _say("per-step decode", name)
-    cfg = small_cfg(1, G=G, T_c=4, T=T, H_kv=H, H_q=Hq, B=B, N=N + n_r, n_s=n_s,
+    cfg = small_cfg(1, G=G, T_c=4, T=T, H_kv=H, H_q=Hq, B=B, N=N + n_r, n_s=n_s, tasq=tasq,
                     rho_k=(0.85,) * (T - 1), rho_v=(0.9,) * (T - 1), n_calib=1024, kmeans_iters=8)
     inp = build_inputs(cfg, 0, "cuda")
     g = _geom(s, cfg)
     shp = (B, H, cfg.n_blk, N, cfg.chunks)
     kidx = torch.zeros(shp, dtype=torch.uint8, device="cuda")
     vidx = torch.zeros(shp, dtype=torch.uint8, device="cuda")
-    s.encode(g, inp["k"][:, :, :, :N], inp["k_cb"], kidx)
+    pt = sigma = None
+    if tasq:
+        sigma = torch.zeros((B, N, T), dtype=torch.float16, device="cuda")
+        pt = s.pretransform(inp["w"], inp["perm"], sigma)
+    s.encode(g, inp["k"][:, :, :, :N], inp["k_cb"], kidx, pt=pt)
     s.encode(g, inp["v"][:, :, :, :N], inp["v_cb"], vidx)
     recent = None
     if n_r:
         recent = (inp["k"][:, :, :, N:].contiguous(), inp["v"][:, :, :, N:].contiguous())
     seq = torch.tensor([N, 0, N - 77][:B], dtype=torch.int32, device="cuda")
-    fused, fused_lse = _decode(s, cfg, inp, kidx, vidx, None, N=N, seq=seq, n_s=n_s, recent=recent)
+    fused, fused_lse = _decode(s, cfg, inp, kidx, vidx, pt, N=N, seq=seq, n_s=n_s, recent=recent)
     worst = 0.0
     for t in range(T):
-        out, lse = _decode(s, cfg, inp, kidx, vidx, None, N=N, step0=t, n_steps=1, seq=seq, n_s=n_s,
+        out, lse = _decode(s, cfg, inp, kidx, vidx, pt, N=N, step0=t, n_steps=1, seq=seq, n_s=n_s,
                            recent=recent)
         torch.cuda.synchronize()
         rows = [(b, hq, t) for b in range(B) for hq in range(Hq)]
         inp_rows = inp if n_s else dict(inp, sink_k=None, sink_v=None)
-        worst = max(worst, _check_rows(cfg, inp_rows, kidx, vidx, None, out, lse, rows, step0=t,
+        worst = max(worst, _check_rows(cfg, inp_rows, kidx, vidx, sigma, out, lse, rows, step0=t,
                                        seq=seq.cpu().numpy(), recent=recent))
         # the single-step and the fused kernels agree within their fp16 rounding
         d = (out[:, :, 0] - fused[:, :, t]).abs().max().item()
