@@ -12,6 +12,10 @@ Prints one JSON line.  `value` is whole-step throughput in context tokens per
 second per loop block (B * N * n_blk / step time); per-kernel rates, the
 roofline of the dominant kernel (and of the decode kernel) and the CPU
 oracle's rate on a bounded sample are attached.
+
+`--config 5` instead runs the 24-layer workload as one flow (prefill encode of
+every layer, then 256 decode calls over all layers with an 8-token page
+encoded per layer every 8 calls) and prints its own JSON line.
 """
 import argparse
 import hashlib
@@ -155,6 +159,128 @@ def hbm_stream(torch, nbytes=1 << 30):
             "note": "calib_read_kernel / calib_copy_kernel, 16 B per lane, grid-stride"}
 
 
+# ----------------------------------------------------------------------------- workload 5 flow
+
+def workload5(args, torch, lv, cfg):
+    """The 24-layer workload as one flow: prefill-encode every layer (inputs
+    generated untimed, one layer at a time), then `decode_steps` decode calls
+    over all layers, each serving every loop step, with one 8-token page per
+    layer encoded after every `page` calls (the page conversion of the
+    review's section 3.4 step 2).  Prints one JSON line."""
+    from synth import build_inputs
+    B, H, L = cfg.B, cfg.H_kv, cfg.layers
+    g = lv.geom(cfg.D, cfg.T, cfg.T_c, cfg.G, cfg.K, cfg.H_kv, cfg.H_q, cfg.theta)
+    n_pages = cfg.decode_steps // cfg.page
+    N_cap = cfg.N + cfg.page * n_pages
+    rope = lv.rope_table(cfg.n_s + N_cap, cfg.D, cfg.theta)
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    layers, enc_ms, gen_s = [], 0.0, 0.0
+    for layer in range(L):
+        t = time.time()
+        inp = build_inputs(cfg, layer, "cuda")
+        torch.cuda.synchronize()
+        gen_s += time.time() - t
+        shp = (B, H, cfg.n_blk, N_cap, cfg.chunks)
+        lay = dict(q=inp["q"], k_cb=inp["k_cb"], v_cb=inp["v_cb"], sk=inp["sink_k"], sv=inp["sink_v"],
+                   w=inp["w"], perm=inp["perm"],
+                   kidx=torch.zeros(shp, dtype=torch.uint8, device="cuda"),
+                   vidx=torch.zeros(shp, dtype=torch.uint8, device="cuda"),
+                   sigma=torch.zeros((B, N_cap, cfg.T), dtype=torch.float16, device="cuda"))
+        lay["pt"] = lv.pretransform(lay["w"], lay["perm"], lay["sigma"])
+        e0, e1 = ev(), ev()
+        e0.record()
+        lv.encode(g, inp["k"], lay["k_cb"], lay["kidx"], pt=lay["pt"])
+        lv.encode(g, inp["v"], lay["v_cb"], lay["vidx"])
+        e1.record()
+        torch.cuda.synchronize()
+        enc_ms += e0.elapsed_time(e1)
+        # the page source: the layer's last 8 tokens (their content does not change the timing)
+        lay["page_k"] = inp["k"][:, :, :, -cfg.page:].clone()
+        lay["page_v"] = inp["v"][:, :, :, -cfg.page:].clone()
+        del inp
+        torch.cuda.empty_cache()
+        layers.append(lay)
+        print("layer %d encoded (%.1f ms); generation so far %.0f s" % (layer, e0.elapsed_time(e1), gen_s),
+              file=sys.stderr, flush=True)
+
+    ws = torch.empty(max(4, lv.decode_workspace_bytes(g, B, N_cap, 0, cfg.T)), dtype=torch.uint8, device="cuda")
+    out = torch.empty((B, cfg.H_q, cfg.T, cfg.D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, cfg.H_q, cfg.T), dtype=torch.float32, device="cuda")
+
+    def decode_all(N):
+        for lay in layers:
+            lv.decode_attn(g, lay["q"], lay["kidx"], lay["vidx"], lay["k_cb"], lay["v_cb"], lay["sk"], lay["sv"],
+                           rope, N=N, pt=lay["pt"], out=out, lse=lse, workspace=ws)
+
+    decode_all(cfg.N)                       # warm-up
+    torch.cuda.synchronize()
+    N, tok_blocks = cfg.N, 0
+    dec_ev, page_ev = [], []
+    t0, t1 = ev(), ev()
+    t0.record()
+    for call in range(cfg.decode_steps):
+        a, b = ev(), ev()
+        a.record()
+        decode_all(N)
+        b.record()
+        dec_ev.append((a, b))
+        tok_blocks += B * N * cfg.n_blk * L
+        if (call + 1) % cfg.page == 0:
+            a, b = ev(), ev()
+            a.record()
+            for lay in layers:
+                lv.encode(g, lay["page_k"], lay["k_cb"], lay["kidx"], tok0=N, pt=lay["pt"])
+                lv.encode(g, lay["page_v"], lay["v_cb"], lay["vidx"], tok0=N)
+            b.record()
+            page_ev.append((a, b))
+            N += cfg.page
+        if (call + 1) % 64 == 0:
+            torch.cuda.synchronize()
+            print("decode call %d done" % (call + 1), file=sys.stderr, flush=True)
+    t1.record()
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    dec_ms = sum(a.elapsed_time(b) for a, b in dec_ev)
+    page_ms = sum(a.elapsed_time(b) for a, b in page_ev)
+    idx_bytes = sum(B * H * cfg.n_blk * (cfg.N + cfg.page * (c // cfg.page)) * 2 * cfg.chunks * L
+                    for c in range(cfg.decode_steps))
+    codes_prefill = 2 * B * H * cfg.n_blk * cfg.N * cfg.chunks * L
+    workload = ("config 5 (%s): %d layers x B=%d, %d kv-heads / %d q-heads, D=%d, T=T_c=%d, G=%d, K=%d, "
+                "keys pre-transformed; prefill %d tokens + %d sinks, then %d decode calls with an %d-token "
+                "page encoded every %d calls" % (cfg.name, L, B, H, cfg.H_q, cfg.D, cfg.T, cfg.G, cfg.K, cfg.N,
+                                                 cfg.n_s, cfg.decode_steps, cfg.page, cfg.page))
+    dec_gbs = idx_bytes / (dec_ms * 1e-3) / 1e9
+    res = {
+        "metric": METRIC,
+        "value": tok_blocks / (dec_ms * 1e-3),
+        "unit": UNIT,
+        "n_gpus": 1,
+        "steps": cfg.decode_steps,
+        "warmup": 1,
+        "ms_per_step": total_ms / cfg.decode_steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": workload, "global_batch": B, "seq_len": cfg.N + cfg.n_s,
+                   "step": "one decode call over all %d layers (every loop step) plus, every %d calls, a page "
+                           "encode per layer" % (L, cfg.page)},
+        "prefill_encode": {"ms_per_layer": enc_ms / L, "codes_per_s": codes_prefill / (enc_ms * 1e-3),
+                           "note": "K (pre-transform, sigma) + V of one layer, %d codes" % (codes_prefill // L)},
+        "decode": {"ms_per_call_per_layer": dec_ms / (cfg.decode_steps * L), "index_GBps": dec_gbs,
+                   "hbm_frac_index_bytes": dec_gbs / HBM_PEAK_GBS},
+        "page_encode": {"events": len(page_ev), "ms_per_event_all_layers": page_ms / max(1, len(page_ev)),
+                        "ms_per_layer": page_ms / max(1, len(page_ev) * L)},
+        "timed_flow_s": total_ms / 1e3,
+        "input_generation_s": gen_s,
+    }
+    print(json.dumps(res), flush=True)
+
+
 # ----------------------------------------------------------------------------- GPU leg
 
 def main():
@@ -162,7 +288,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=2, help="workload index 1-4 (single layer)")
+    ap.add_argument("--config", type=int, default=2,
+                    help="workload index: 1-4 single layer, 5 the 24-layer prefill + decode flow")
     ap.add_argument("--cpu-tokens", type=int, default=8192, help="context tokens in the oracle sample")
     ap.add_argument("--cpu-batch", type=int, default=2, help="batch entries in the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -182,10 +309,10 @@ def main():
         sys.exit(1)
     lv.lib()
     cfg = config_by_index(args.config)
-    if cfg.layers != 1:
-        print("bench.py times single-layer workloads (1-4)", file=sys.stderr)
-        sys.exit(2)
     torch.cuda.set_device(0)
+    if cfg.layers != 1:
+        workload5(args, torch, lv, cfg)
+        return
     t_gen = time.time()
     inp = build_inputs(cfg, 0, "cuda")
     torch.cuda.synchronize()
