@@ -158,6 +158,23 @@ __global__ __launch_bounds__(kEncodeThreads) void encode_kernel(EncodeArgs a) {
     }
   };
 
+  // Pre-transformed keys: this lane's code is always chunk n mod CPT of its
+  // token, so the raw channel p(d) and weight w[p(d)] of each of its joint
+  // positions are lane constants.
+  int tof[TASQ ? KK : 1][8];
+  float twt[TASQ ? KK : 1][8];
+  if constexpr (TASQ && CPT <= 32) {
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int p = 16 * kk + 8 * hh + e;
+        const int o = ph[(n & (CPT - 1)) * C + (p % C)] & (D - 1);
+        tof[kk][e] = o;
+        twt[kk][e] = wh[o];
+      }
+  }
+
   // Loads (and, for pre-transformed keys, transforms) the joint vectors of
   // group grp: code g = 32*grp + n is token g / CPT, chunk g % CPT.
   auto fetch = [&](int grp, bf16x8_t (&zh)[KK], bf16x8_t (&zl)[KK], float& zz) {
@@ -188,24 +205,36 @@ __global__ __launch_bounds__(kEncodeThreads) void encode_kernel(EncodeArgs a) {
         }
       }
     } else {
+      // z = w[p(d)] * k[p(d)] / sigma, split into two bf16 terms for an
+      // exact-enough contraction (the band below covers the split; near
+      // ties are re-scored from the inputs in fp64).
       const uint16_t* xr = xbase + (int64_t)jl * xs3;
+      const uint16_t* sg = sgb + (int64_t)jl * a.T;
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int p = 16 * kk + 8 * hh + e;
-          const int m = p / C, d = q * C + (p % C);
-          const int o = ph[d] & (D - 1);
-          const float kv = bf16_to_f32(xr[m * xs2 + o]);
+          const int m = (16 * kk + 8 * hh) / C + (C <= 8 ? e / C : 0);   // = p / C
+          int o;
+          float wv;
+          if constexpr (CPT <= 32) {
+            o = tof[kk][e];
+            wv = twt[kk][e];
+          } else {
+            // c = 2: the lane's chunk changes between groups
+            o = ph[q * C + (p % C)] & (D - 1);
+            wv = wh[o];
+          }
           _Float16 sh;
-          const uint16_t sb = sgb[(int64_t)jl * a.T + m];
+          const uint16_t sb = sg[m];
           __builtin_memcpy(&sh, &sb, 2);
-          const float zf = (wh[o] * kv) / (float)sh;
-          const uint32_t hb16 = f32_to_bf16_rne(zf);
-          const uint32_t lb16 = f32_to_bf16_rne(zf - bf16_to_f32(hb16));
+          const float kv = bf16_to_f32(xr[m * xs2 + o]);
+          const float zf = (wv * kv) * __builtin_amdgcn_rcpf((float)sh);
+          const __bf16 zhi = (__bf16)zf;
           zz = fmaf(zf, zf, zz);
-          zh[kk][e] = __builtin_bit_cast(__bf16, (uint16_t)hb16);
-          zl[kk][e] = __builtin_bit_cast(__bf16, (uint16_t)lb16);
+          zh[kk][e] = zhi;
+          zl[kk][e] = (__bf16)(zf - (float)zhi);
         }
       }
     }
