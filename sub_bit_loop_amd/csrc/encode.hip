@@ -175,69 +175,81 @@ __global__ __launch_bounds__(kEncodeThreads) void encode_kernel(EncodeArgs a) {
       }
   }
 
-  // Loads (and, for pre-transformed keys, transforms) the joint vectors of
-  // group grp: code g = 32*grp + n is token g / CPT, chunk g % CPT.
-  auto fetch = [&](int grp, bf16x8_t (&zh)[KK], bf16x8_t (&zl)[KK], float& zz) {
+  // Loads the joint vectors of group grp: code g = 32*grp + n is token
+  // g / CPT, chunk g % CPT.
+  auto fetch = [&](int grp, bf16x8_t (&zh)[KK]) {
+    int jl, q;
+    code_pos(grp, jl, q);
+    // group-uniform part of the address (the lane part is in loff)
+    const uint16_t* xr = xbase + (int64_t)jl * xs3 + (CPT >= 32 ? (q - n) * C : 0);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const uint16_t* pz = xr + loff[kk];
+      if constexpr (CW == 8) {
+        zh[kk] = *reinterpret_cast<const bf16x8_t*>(pz);
+      } else {
+        uint32_t w[4];
+#pragma unroll
+        for (int l = 0; l < NL; ++l) {
+          if constexpr (CW == 4) {
+            const uint2 v = *reinterpret_cast<const uint2*>(pz + l * xs2);
+            w[2 * l] = v.x;
+            w[2 * l + 1] = v.y;
+          } else {
+            w[l] = *reinterpret_cast<const uint32_t*>(pz + l * xs2);
+          }
+        }
+        zh[kk] = __builtin_bit_cast(bf16x8_t, (uint4){w[0], w[1], w[2], w[3]});
+      }
+    }
+  };
+  // Pre-transformed keys, in two parts so that the loads of the next group
+  // are in flight while the current one is screened: the raw bf16 bits of
+  // k[p(d)] and the fp16 bits of sigma for each joint position of the lane,
+  // then z = w[p(d)] * k[p(d)] / sigma split into three bf16 terms (the
+  // residuals are exact in fp32, the sum is within 2^-24 |z|; the band below
+  // covers the split, near ties are re-scored from the inputs in fp64).
+  auto raw_channel = [&](int kk, int e, int q) {
+    if constexpr (CPT <= 32) return tof[kk][e];
+    // c = 2: the lane's chunk changes between groups
+    return ph[q * C + ((16 * kk + 8 * hh + e) % C)] & (D - 1);
+  };
+  auto fetch_raw = [&](int grp, uint32_t (&rk)[KK][8], uint32_t (&rs)[KK][8]) {
+    int jl, q;
+    code_pos(grp, jl, q);
+    const uint16_t* xr = xbase + (int64_t)jl * xs3;
+    const uint16_t* sg = sgb + (int64_t)jl * a.T;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int m = (16 * kk + 8 * hh) / C + (C <= 8 ? e / C : 0);   // step of position 16kk + 8hh + e
+        rk[kk][e] = xr[m * xs2 + raw_channel(kk, e, q)];
+        rs[kk][e] = sg[m];
+      }
+  };
+  auto transform = [&](int grp, const uint32_t (&rk)[KK][8], const uint32_t (&rs)[KK][8], bf16x8_t (&zh)[KK],
+                       bf16x8_t (&zl)[KK], bf16x8_t (&zl2)[KK], float& zz) {
     int jl, q;
     code_pos(grp, jl, q);
     zz = 0.f;
-    if constexpr (!TASQ) {
-      // group-uniform part of the address (the lane part is in loff)
-      const uint16_t* xr = xbase + (int64_t)jl * xs3 + (CPT >= 32 ? (q - n) * C : 0);
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        const uint16_t* pz = xr + loff[kk];
-        if constexpr (CW == 8) {
-          zh[kk] = *reinterpret_cast<const bf16x8_t*>(pz);
-        } else {
-          uint32_t w[4];
+    for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
-          for (int l = 0; l < NL; ++l) {
-            if constexpr (CW == 4) {
-              const uint2 v = *reinterpret_cast<const uint2*>(pz + l * xs2);
-              w[2 * l] = v.x;
-              w[2 * l + 1] = v.y;
-            } else {
-              w[l] = *reinterpret_cast<const uint32_t*>(pz + l * xs2);
-            }
-          }
-          zh[kk] = __builtin_bit_cast(bf16x8_t, (uint4){w[0], w[1], w[2], w[3]});
-        }
+      for (int e = 0; e < 8; ++e) {
+        const float wv = CPT <= 32 ? twt[kk][e] : wh[raw_channel(kk, e, q)];
+        _Float16 sh;
+        const uint16_t sb = (uint16_t)rs[kk][e];
+        __builtin_memcpy(&sh, &sb, 2);
+        const float zf = (wv * bf16_to_f32(rk[kk][e])) * __builtin_amdgcn_rcpf((float)sh);
+        const __bf16 z1 = (__bf16)zf;
+        const float r1 = zf - (float)z1;
+        const __bf16 z2 = (__bf16)r1;
+        zz = fmaf(zf, zf, zz);
+        zh[kk][e] = z1;
+        zl[kk][e] = z2;
+        zl2[kk][e] = (__bf16)(r1 - (float)z2);
       }
-    } else {
-      // z = w[p(d)] * k[p(d)] / sigma, split into two bf16 terms for an
-      // exact-enough contraction (the band below covers the split; near
-      // ties are re-scored from the inputs in fp64).
-      const uint16_t* xr = xbase + (int64_t)jl * xs3;
-      const uint16_t* sg = sgb + (int64_t)jl * a.T;
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int p = 16 * kk + 8 * hh + e;
-          const int m = (16 * kk + 8 * hh) / C + (C <= 8 ? e / C : 0);   // = p / C
-          int o;
-          float wv;
-          if constexpr (CPT <= 32) {
-            o = tof[kk][e];
-            wv = twt[kk][e];
-          } else {
-            // c = 2: the lane's chunk changes between groups
-            o = ph[q * C + (p % C)] & (D - 1);
-            wv = wh[o];
-          }
-          _Float16 sh;
-          const uint16_t sb = sg[m];
-          __builtin_memcpy(&sh, &sb, 2);
-          const float kv = bf16_to_f32(xr[m * xs2 + o]);
-          const float zf = (wv * kv) * __builtin_amdgcn_rcpf((float)sh);
-          const __bf16 zhi = (__bf16)zf;
-          zz = fmaf(zf, zf, zz);
-          zh[kk][e] = zhi;
-          zl[kk][e] = (__bf16)(zf - (float)zhi);
-        }
-      }
-    }
   };
 
   // Lane constants of the norm product's B operand (zero in the second
@@ -248,18 +260,23 @@ __global__ __launch_bounds__(kEncodeThreads) void encode_kernel(EncodeArgs a) {
 
   // The next group's loads are issued before the current group is screened.
   constexpr int WS = kEncodeThreads / kWave;
-  bf16x8_t bz[KK], bzlo[KK];
-  float zzp;
-  fetch(wave, bz, bzlo, zzp);
+  bf16x8_t bz[KK];
+  uint32_t brk[TASQ ? KK : 1][8], brs[TASQ ? KK : 1][8];
+  if constexpr (TASQ)
+    fetch_raw(wave, brk, brs);
+  else
+    fetch(wave, bz);
   for (int grp = wave; grp < ngroups; grp += WS) {
-    bf16x8_t cz[KK], czlo[KK];
-    float zz = zzp;
+    bf16x8_t cz[KK], czlo[KK], czlo2[KK];
+    float zz = 0.f;
+    if constexpr (TASQ) {
+      transform(grp, brk, brs, cz, czlo, czlo2, zz);
+      fetch_raw(min(grp + WS, ngroups - 1), brk, brs);
+    } else {
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      cz[kk] = bz[kk];
-      if constexpr (TASQ) czlo[kk] = bzlo[kk];
+      for (int kk = 0; kk < KK; ++kk) cz[kk] = bz[kk];
+      fetch(min(grp + WS, ngroups - 1), bz);
     }
-    fetch(min(grp + WS, ngroups - 1), bz, bzlo, zzp);
     const int g = grp * 32 + n;
     const bool valid = CPT >= 32 || g < ncodes;
 
@@ -301,7 +318,10 @@ __global__ __launch_bounds__(kEncodeThreads) void encode_kernel(EncodeArgs a) {
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[t][kk], cz[kk], acc, 0, 0, 0);
-        if constexpr (TASQ) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[t][kk], czlo[kk], acc, 0, 0, 0);
+        if constexpr (TASQ) {
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[t][kk], czlo[kk], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[t][kk], czlo2[kk], acc, 0, 0, 0);
+        }
       }
       return acc;
     };
@@ -344,12 +364,17 @@ __global__ __launch_bounds__(kEncodeThreads) void encode_kernel(EncodeArgs a) {
     // below (||z|| + sqrt(Tb))^2 <= 2 (||z||^2 + Tb).  The key's low byte
     // adds < 2^-15 t1.
     // With Tb = 1.0625 t1 + ||z||^2 / 64 and nb = 2 (||z||^2 + Tb):
-    //   eps = kErr (nb + 1.02 ||z||^2)  [+ for pre-transformed keys: doubled,
-    //         plus 2^-15 (||z||^2 + nb) for the two-term bf16 split of z],
+    //   eps = kErr (nb + 1.02 ||z||^2),
     //   thr = t1 (1 + 2^-14) + 2 eps  =  kA t1 + kB ||z||^2.
+    // Pre-transformed keys: the MFMA sums 4 + 3G products (three split
+    // terms), so kErr triples; and the split sum differs from the exact
+    // transformed value by < 2^-21 |z| (2^-24 from the split, ~2^-22 from
+    // the fp32 product with the reciprocal of sigma), which moves a screened
+    // value by < 2^-21 (||z||^2 + nb):
+    //   eps = 3 kErr (nb + 1.02 ||z||^2) + 2^-21 (||z||^2 + nb).
     constexpr float kErr = (float)(2 * G + 16) * 0x1p-24f;
-    constexpr float kA = TASQ ? 1.f + 0x1p-14f + 8.5f * kErr + 2.125f * 0x1p-14f : 1.f + 0x1p-14f + 4.25f * kErr;
-    constexpr float kB = TASQ ? 12.21f * kErr + 3.04f * 0x1p-14f : 6.11f * kErr;
+    constexpr float kA = TASQ ? 1.f + 0x1p-14f + 12.75f * kErr + 4.25f * 0x1p-21f : 1.f + 0x1p-14f + 4.25f * kErr;
+    constexpr float kB = TASQ ? 18.31f * kErr + 6.07f * 0x1p-21f : 6.11f * kErr;
     const float thr = fmaf(kA, t1, kB * zz);
     const bool tie = valid && !(t2 > thr);
     // candidate 16t + i of half-wave hh is codebook entry 32t + 8(i/4) + 4hh + i%4
@@ -388,7 +413,10 @@ __global__ __launch_bounds__(kEncodeThreads) void encode_kernel(EncodeArgs a) {
         for (int kk = 0; kk < KK; ++kk) {
           const bf16x8_t rv = *reinterpret_cast<const bf16x8_t*>(&s_cb[(32 * t + n) * G + 16 * kk + 8 * hh]);
           acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rv, cz[kk], acc, 0, 0, 0);
-          if constexpr (TASQ) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rv, czlo[kk], acc, 0, 0, 0);
+          if constexpr (TASQ) {
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rv, czlo[kk], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rv, czlo2[kk], acc, 0, 0, 0);
+          }
         }
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
