@@ -8,3 +8,4 @@ Every function is the plain definition from the LoopVQ review (arXiv
 2611.05304), written in NumPy float64, with no blocking or fusion.
 """
 from .loopvq_ref import *  # noqa: F401,F403
+from .tasq_perm import *  # noqa: F401,F403,E402
