@@ -17,7 +17,8 @@ design notes of the repository):
     before its permutation), centred, normalised by the token count n;
   * pairs are grouped by the magnitude of their correlation: the affinity of
     pairs u and v is the sum of |corr| over both channels of each pair and
-    every (step, step) combination of the block;
+    every (step, step) combination of the block, evaluated for u < v and used
+    for both orders;
   * groups are formed greedily, one at a time: the seed is the free pair with
     the largest affinity to all other free pairs, then the free pair with the
     largest summed affinity to the group's members joins, until the group has
@@ -59,6 +60,10 @@ def pair_affinity(cov: np.ndarray, T_c: int, D: int) -> np.ndarray:
     # fold the steps and the two channels of each pair
     a = a.sum(axis=(0, 2))                                  # [D, D]
     A = a[:HD, :HD] + a[:HD, HD:] + a[HD:, :HD] + a[HD:, HD:]
+    # defined once per unordered pair (from u < v), so that ties which are
+    # exact in real arithmetic stay exact
+    iu = np.triu_indices(HD, 1)
+    A[(iu[1], iu[0])] = A[iu]
     np.fill_diagonal(A, 0.0)
     return A
 
