@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define LOOPVQ_ABI_VERSION 2
+#define LOOPVQ_ABI_VERSION 3
 
 typedef enum {
   LOOPVQ_OK = 0,
@@ -176,6 +176,42 @@ loopvq_status loopvq_decode_attn(const loopvq_geom* g, const void* q, int32_t st
                                  const loopvq_pretransform* pt, const void* rope_table,
                                  int32_t n_pos, float* out, float* lse, void* workspace,
                                  size_t workspace_bytes, void* stream);
+
+/* loopvq_tasq_covariance -- statistics for deriving the keys' channel
+ * permutation (section 3.3: the permutation is taken from the T_c*D x T_c*D
+ * covariance of a block's stacked step keys).  For every (kv-head, block) it
+ * computes, in fp64, the mean and the covariance (centred, divided by B*N) of
+ * the scaled keys y[s*D + d] = w[h][d] * k[d] / sigma at block step s, over
+ * the B*N (batch entry, token) pairs.  sigma is the same per-(token, step) RMS
+ * as in loopvq_encode and is written here first.
+ *   x, x_strides  raw bf16 pre-RoPE keys [B][H_kv][T][N] rows of D (as encode)
+ *   w             device fp32 [H_kv][D], entries > 0
+ *   sigma         device fp16 [B][sig_cap][T], written for tokens 0..N-1
+ *   mean          device fp64 [H_kv][T/T_c][T_c*D], written
+ *   cov           device fp64 [H_kv][T/T_c][T_c*D][T_c*D], written
+ * Errors: EINVAL for NULL pointers, B < 1, N < 1, sig_cap < N, bad strides or
+ * geometry; ENOTSUP for D != 128 or T_c*D > 1024.  Stream-ordered, does not
+ * synchronize; the result does not depend on launch order (no atomics). */
+loopvq_status loopvq_tasq_covariance(const loopvq_geom* g, const void* x, const int64_t x_strides[4],
+                                     int32_t B, int32_t N, const float* w, uint16_t* sigma, int32_t sig_cap,
+                                     double* mean, double* cov, void* stream);
+
+/* loopvq_tasq_pair_permutation -- host-side grouping of one block's
+ * covariance (as written by loopvq_tasq_covariance, copied to host memory)
+ * into a channel permutation whose chunks of c channels each hold c/2 whole
+ * RoPE pairs {u, u + D/2} (section 3.3).  Pairs u, v < D/2 are scored by the
+ * sum of |correlation| over their two channels each and every (step, step)
+ * combination; groups are built one at a time: the free pair with the largest
+ * score to all free pairs seeds a group, then the free pair with the largest
+ * summed score to the group's members joins, until c/2 pairs; ties go to the
+ * lowest pair number.  Chunk q is the q-th group, its pairs in joining order,
+ * each as (u, u + D/2).
+ *   cov   host fp64 [T_c*D][T_c*D]
+ *   perm  host int16 [D], written: transformed channel d' holds raw channel
+ *         perm[d'] (the loopvq_pretransform convention)
+ * Errors: EINVAL for NULL pointers, T_c < 1, odd D, odd c or c not dividing D. */
+loopvq_status loopvq_tasq_pair_permutation(const double* cov, int32_t T_c, int32_t D, int32_t c,
+                                           int16_t* perm);
 
 /* Thread-local text of the last non-OK status ("" if none). */
 const char* loopvq_last_error(void);

@@ -62,6 +62,43 @@ def encode(g: Geom, x, codebook, idx, tok0=0, pt=None, stream=None):
     return idx
 
 
+def tasq_covariance(g: Geom, x, w, sigma, mean=None, cov=None, stream=None):
+    """Mean and covariance (fp64) of the block-stacked scaled keys w*k/sigma for
+    the pre-transform's permutation.  x bf16 [B][H][T][N][D] raw keys (rows
+    contiguous), w fp32 [H][D], sigma fp16 [B][N_cap][T] (written).
+    Returns (mean [H][n_blk][T_c*D], cov [H][n_blk][T_c*D][T_c*D])."""
+    _need(x, torch.bfloat16, "x")
+    _need(w, torch.float32, "w")
+    _need(sigma, torch.float16, "sigma")
+    if x.dim() != 5 or x.stride(4) != 1:
+        raise ValueError("x must be [B][H][T][N][D] with contiguous rows")
+    B, H, T, N, D = x.shape
+    F = g.T_c * g.D
+    n_blk = g.T // g.T_c
+    if mean is None:
+        mean = torch.empty((H, n_blk, F), dtype=torch.float64, device=x.device)
+    if cov is None:
+        cov = torch.empty((H, n_blk, F, F), dtype=torch.float64, device=x.device)
+    _need(mean, torch.float64, "mean")
+    _need(cov, torch.float64, "cov")
+    strides = (ctypes.c_int64 * 4)(*[x.stride(i) for i in range(4)])
+    check(_lib.lib().loopvq_tasq_covariance(ctypes.byref(g), _ptr(x), strides, B, N, _ptr(w), _ptr(sigma),
+                                            sigma.shape[1], _ptr(mean), _ptr(cov), _stream(stream)))
+    return mean, cov
+
+
+def tasq_pair_permutation(cov_host, T_c, D, c):
+    """Channel permutation (int16 [D], host) from one block's covariance
+    (fp64 [T_c*D][T_c*D], host tensor)."""
+    if not isinstance(cov_host, torch.Tensor) or cov_host.dtype != torch.float64 or cov_host.device.type != "cpu":
+        raise TypeError("cov_host must be a host float64 tensor")
+    cov_host = cov_host.contiguous()
+    perm = torch.empty(D, dtype=torch.int16)
+    check(_lib.lib().loopvq_tasq_pair_permutation(ctypes.c_void_p(cov_host.data_ptr()), T_c, D, c,
+                                                  ctypes.c_void_p(perm.data_ptr())))
+    return perm
+
+
 def rope_table(n_pos, D=128, theta=1.0e4, device="cuda", stream=None):
     """fp16 [n_pos][D/8][8]: per 4 frequencies, their cosines then sines."""
     t = torch.empty((n_pos, D // 8, 8), dtype=torch.float16, device=device)

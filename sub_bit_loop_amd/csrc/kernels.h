@@ -48,6 +48,17 @@ struct DecodeArgs {
   float qscale;               // log2(e) / sqrt(D)
 };
 
+struct TasqStatsArgs {
+  const uint16_t* x;          // bf16 rows of D (raw pre-RoPE keys), strides in elements
+  int64_t xs0, xs1, xs2, xs3;
+  const float* w;             // [H][D]
+  const uint16_t* sigma;      // fp16 [B][sig_cap][T]
+  int32_t sig_cap;
+  double* mean;               // [H][n_blk][T_c*D]
+  double* cov;                // [H][n_blk][T_c*D][T_c*D]
+  int32_t B, H, T, T_c, n_blk, N, D;
+};
+
 struct MergeArgs {
   const float* ws;
   float* out;
@@ -62,6 +73,9 @@ hipError_t launch_sigma(const SigmaArgs& a, int B, hipStream_t s);
 hipError_t launch_decode(int G, int TC, bool tasq, const DecodeArgs& a, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
 hipError_t launch_rope_table(double theta, int D, int n_pos, void* table, hipStream_t s);
+// Mean, then covariance, of the block-stacked scaled keys (needs sigma
+// written first); T_c*D a multiple of 64 and at most 1024.
+hipError_t launch_tasq_stats(const TasqStatsArgs& a, hipStream_t s);
 hipError_t launch_decode_fast(int G, const DecodeArgs& a, hipStream_t s);
 // T_c = 4, no pre-transform; one workgroup per (split, group of hpw q-heads,
 // batch x served step); hpw in {1, 2, 4} divides the GQA group size.

@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <vector>
 
 #include "../../include/loopvq.h"
 #include "kernels.h"
@@ -197,6 +198,131 @@ loopvq_status loopvq_rope_table(float theta, int32_t D, int32_t n_pos, void* tab
   if (!(theta > 0.f) || !std::isfinite(theta)) return fail(LOOPVQ_EINVAL, "theta must be positive");
   hipError_t e = loopvq::launch_rope_table((double)theta, D, n_pos, table, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "rope table launch");
+  return LOOPVQ_OK;
+}
+
+loopvq_status loopvq_tasq_covariance(const loopvq_geom* g, const void* x, const int64_t x_strides[4],
+                                     int32_t B, int32_t N, const float* w, uint16_t* sigma, int32_t sig_cap,
+                                     double* mean, double* cov, void* stream) {
+  g_err[0] = 0;
+  loopvq_status st = check_geom(g);
+  if (st != LOOPVQ_OK) return st;
+  if (B < 1 || N < 1) return fail(LOOPVQ_EINVAL, "B=%d and N=%d must be >= 1", B, N);
+  if (!x || !x_strides || !w || !sigma || !mean || !cov) return fail(LOOPVQ_EINVAL, "NULL pointer");
+  if (sig_cap < N) return fail(LOOPVQ_EINVAL, "sigma capacity %d < N=%d", sig_cap, N);
+  for (int i = 0; i < 4; ++i)
+    if (x_strides[i] <= 0 || x_strides[i] % 8)
+      return fail(LOOPVQ_EINVAL, "x_strides[%d]=%lld must be a positive multiple of 8", i, (long long)x_strides[i]);
+  if (x_strides[3] < g->D) return fail(LOOPVQ_EINVAL, "token stride %lld < D", (long long)x_strides[3]);
+  if (reinterpret_cast<uintptr_t>(x) % 16) return fail(LOOPVQ_EINVAL, "x must be 16-byte aligned");
+  if (g->T_c * g->D > 1024) return fail(LOOPVQ_ENOTSUP, "T_c*D=%d exceeds 1024", g->T_c * g->D);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  loopvq::SigmaArgs sa{};
+  sa.x = static_cast<const uint16_t*>(x);
+  sa.xs0 = x_strides[0];
+  sa.xs1 = x_strides[1];
+  sa.xs2 = x_strides[2];
+  sa.xs3 = x_strides[3];
+  sa.H = g->n_kv_heads;
+  sa.T = g->T;
+  sa.N = N;
+  sa.tok0 = 0;
+  sa.sig_cap = sig_cap;
+  sa.sigma = sigma;
+  hipError_t e = loopvq::launch_sigma(sa, B, s);
+  if (e != hipSuccess) return hip_fail(e, "sigma launch");
+  loopvq::TasqStatsArgs a{};
+  a.x = sa.x;
+  a.xs0 = sa.xs0;
+  a.xs1 = sa.xs1;
+  a.xs2 = sa.xs2;
+  a.xs3 = sa.xs3;
+  a.w = w;
+  a.sigma = sigma;
+  a.sig_cap = sig_cap;
+  a.mean = mean;
+  a.cov = cov;
+  a.B = B;
+  a.H = g->n_kv_heads;
+  a.T = g->T;
+  a.T_c = g->T_c;
+  a.n_blk = g->T / g->T_c;
+  a.N = N;
+  a.D = g->D;
+  e = loopvq::launch_tasq_stats(a, s);
+  if (e != hipSuccess) return hip_fail(e, "covariance launch");
+  return LOOPVQ_OK;
+}
+
+loopvq_status loopvq_tasq_pair_permutation(const double* cov, int32_t T_c, int32_t D, int32_t c, int16_t* perm) {
+  g_err[0] = 0;
+  if (!cov || !perm) return fail(LOOPVQ_EINVAL, "NULL pointer");
+  if (T_c < 1 || D < 2 || D % 2 || c < 2 || c % 2 || D % c)
+    return fail(LOOPVQ_EINVAL, "need T_c >= 1, even D, even c dividing D (T_c=%d, D=%d, c=%d)", T_c, D, c);
+  if (D > 32767) return fail(LOOPVQ_EINVAL, "D=%d does not fit int16 channel numbers", D);
+  const int F = T_c * D, HD = D / 2, per = c / 2;
+  // correlation magnitudes folded over (step, step) and the two channels of
+  // each RoPE pair
+  std::vector<double> sd(F);
+  for (int f = 0; f < F; ++f) {
+    const double v = cov[(size_t)f * F + f];
+    sd[f] = v > 0.0 ? std::sqrt(v) : 0.0;
+  }
+  std::vector<double> A((size_t)HD * HD, 0.0);
+  for (int u = 0; u < HD; ++u)
+    for (int v = u + 1; v < HD; ++v) {   // one value per unordered pair keeps exact ties exact
+      double acc = 0.0;
+      for (int si = 0; si < T_c; ++si)
+        for (int sj = 0; sj < T_c; ++sj)
+          for (int ca = 0; ca < 2; ++ca)
+            for (int cb = 0; cb < 2; ++cb) {
+              const int fa = si * D + u + ca * HD, fb = sj * D + v + cb * HD;
+              const double den = sd[fa] * sd[fb];
+              if (den > 0.0) acc += std::fabs(cov[(size_t)fa * F + fb] / den);
+            }
+      A[(size_t)u * HD + v] = acc;
+      A[(size_t)v * HD + u] = acc;
+    }
+  // greedy groups of `per` pairs: seed = free pair with the largest affinity
+  // to the other free pairs, then the free pair closest to the group; ties
+  // go to the lowest pair number
+  std::vector<char> used(HD, 0);
+  int out = 0;
+  for (int left = HD; left > 0; left -= per) {
+    int seed = -1;
+    double best = -1.0;
+    for (int u = 0; u < HD; ++u) {
+      if (used[u]) continue;
+      double tot = 0.0;
+      for (int v = 0; v < HD; ++v)
+        if (!used[v]) tot += A[(size_t)u * HD + v];
+      if (tot > best) {
+        best = tot;
+        seed = u;
+      }
+    }
+    std::vector<int> group{seed};
+    used[seed] = 1;
+    while ((int)group.size() < per) {
+      int nxt = -1;
+      double bg = -1.0;
+      for (int v = 0; v < HD; ++v) {
+        if (used[v]) continue;
+        double gsum = 0.0;
+        for (int u : group) gsum += A[(size_t)v * HD + u];
+        if (gsum > bg) {
+          bg = gsum;
+          nxt = v;
+        }
+      }
+      group.push_back(nxt);
+      used[nxt] = 1;
+    }
+    for (int u : group) {
+      perm[out++] = (int16_t)u;
+      perm[out++] = (int16_t)(u + HD);
+    }
+  }
   return LOOPVQ_OK;
 }
 

@@ -27,7 +27,7 @@ def test_exports_match_header():
     assert set(names) == set(L.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.loopvq_abi_version() == 2
+    assert lib.loopvq_abi_version() == 3
 
 
 def _geom(L, **kw):
