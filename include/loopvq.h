@@ -213,6 +213,39 @@ loopvq_status loopvq_tasq_covariance(const loopvq_geom* g, const void* x, const 
 loopvq_status loopvq_tasq_pair_permutation(const double* cov, int32_t T_c, int32_t D, int32_t c,
                                            int16_t* perm);
 
+/* loopvq_kmeans_accumulate -- the update half of one step of the
+ * importance-weighted k-means that builds the codebooks ("codebook and
+ * calibration", eq. 3: joint vector n weighs omega_n = ||dL/dz_n||^2, summed
+ * over the T_c steps it covers).  The assignment is loopvq_encode's exact
+ * argmin of the same vectors.  For every joint vector n of the B x N tokens
+ * with index r = idx[n] < K it adds, in fp64,
+ *     sums[h][beta][r][u] += omega_n * z_n[u]   (u = i*T_c + m, eq. 4 layout)
+ *     wsum[h][beta][r]    += omega_n
+ * where z_n is the bf16 joint vector, or with pt the pre-transformed key
+ * w[p(d')] * k[p(d')] / sigma in fp64 (sigma as written by loopvq_encode).
+ *   x, x_strides  the encoded bf16 cache [B][H_kv][T][N] rows of D (as encode)
+ *   idx, N_cap    indices written by loopvq_encode for the same x
+ *   weight        device fp32 [B][H_kv][T/T_c][N][D/c] (omega per joint
+ *                 vector) or NULL for all ones
+ *   sums, wsum    device fp64 [H_kv][T/T_c][K][G] and [H_kv][T/T_c][K];
+ *                 accumulated (zero them before the first call of a step)
+ * The fp64 sums are accumulated with atomics, so their last bits depend on
+ * the order of execution.  Errors: EINVAL for NULL pointers, negative B or N,
+ * N > N_cap, bad strides, an undersized pt->N_cap; ENOTSUP for D != 128 or G
+ * not in {16, 32}.  N == 0 or B == 0 is a no-op. */
+loopvq_status loopvq_kmeans_accumulate(const loopvq_geom* g, const void* x, const int64_t x_strides[4],
+                                      int32_t B, int32_t N, const uint8_t* idx, int32_t N_cap,
+                                      const float* weight, const loopvq_pretransform* pt, double* sums,
+                                      double* wsum, void* stream);
+
+/* loopvq_kmeans_finalize -- the new codebook of the step: every entry with
+ * wsum > 0 becomes sums / wsum rounded to bf16 (to nearest, ties to even,
+ * from the fp64 quotient); entries with zero weight keep their value.
+ *   codebook  device bf16 [H_kv][T/T_c][K][G], updated in place
+ * Errors: EINVAL for NULL pointers; ENOTSUP as for the geometry. */
+loopvq_status loopvq_kmeans_finalize(const loopvq_geom* g, const double* sums, const double* wsum,
+                                    void* codebook, void* stream);
+
 /* Thread-local text of the last non-OK status ("" if none). */
 const char* loopvq_last_error(void);
 

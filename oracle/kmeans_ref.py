@@ -33,12 +33,14 @@ def fisher_weights(grad_joint: np.ndarray) -> np.ndarray:
     return (g * g).sum(axis=-1)
 
 
-def weighted_kmeans_sums(z: np.ndarray, omega: np.ndarray, cb: np.ndarray):
+def weighted_kmeans_sums(z: np.ndarray, omega: np.ndarray, cb: np.ndarray, assign=None):
     """z [n, G], omega [n] >= 0, cb [K, G] -> (assignment [n],
-    sums [K, G] = sum of omega z per codeword, wsum [K] = sum of omega)."""
+    sums [K, G] = sum of omega z per codeword, wsum [K] = sum of omega).
+    `assign`, when given, replaces the argmin (to compare an update made
+    from the same assignment)."""
     z = np.asarray(z, dtype=np.float64)
     om = np.asarray(omega, dtype=np.float64)
-    a, _ = nearest_codeword(z, cb)
+    a = nearest_codeword(z, cb)[0] if assign is None else np.asarray(assign, dtype=np.int64)
     K, G = np.asarray(cb).shape
     sums = np.zeros((K, G))
     wsum = np.zeros(K)

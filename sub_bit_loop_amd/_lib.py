@@ -14,7 +14,7 @@ STATUS_NAME = {OK: "OK", EINVAL: "EINVAL", ENOTSUP: "ENOTSUP", EHIP: "EHIP", EWO
 # Names the C header declares; tests check that every one is exported.
 EXPORTS = ("loopvq_encode", "loopvq_rope_table", "loopvq_decode_attn_workspace",
            "loopvq_decode_attn", "loopvq_tasq_covariance", "loopvq_tasq_pair_permutation",
-           "loopvq_last_error", "loopvq_abi_version")
+           "loopvq_kmeans_accumulate", "loopvq_kmeans_finalize", "loopvq_last_error", "loopvq_abi_version")
 
 
 class Geom(ctypes.Structure):
@@ -60,6 +60,10 @@ def lib():
     L.loopvq_tasq_covariance.restype = ctypes.c_int
     L.loopvq_tasq_pair_permutation.argtypes = [P, I32, I32, I32, P]
     L.loopvq_tasq_pair_permutation.restype = ctypes.c_int
+    L.loopvq_kmeans_accumulate.argtypes = [GP, P, I64P, I32, I32, P, I32, P, PTP, P, P, P]
+    L.loopvq_kmeans_accumulate.restype = ctypes.c_int
+    L.loopvq_kmeans_finalize.argtypes = [GP, P, P, P, P]
+    L.loopvq_kmeans_finalize.restype = ctypes.c_int
     L.loopvq_last_error.argtypes = []
     L.loopvq_last_error.restype = ctypes.c_char_p
     L.loopvq_abi_version.argtypes = []

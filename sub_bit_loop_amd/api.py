@@ -99,6 +99,44 @@ def tasq_pair_permutation(cov_host, T_c, D, c):
     return perm
 
 
+def kmeans_accumulate(g: Geom, x, idx, sums, wsum, weight=None, pt=None, stream=None):
+    """Adds omega*z and omega of every joint vector of x into its codeword's
+    sums fp64 [H][n_blk][K][G] and wsum fp64 [H][n_blk][K].  x bf16
+    [B][H][T][N][D] (rows contiguous), idx uint8 from encode(x),
+    weight fp32 [B][H][n_blk][N][D/c] or None."""
+    _need(x, torch.bfloat16, "x")
+    _need(idx, torch.uint8, "idx")
+    _need(sums, torch.float64, "sums")
+    _need(wsum, torch.float64, "wsum")
+    if weight is not None:
+        _need(weight, torch.float32, "weight")
+        if not weight.is_contiguous():
+            raise ValueError("weight must be contiguous")
+    if x.dim() != 5 or x.stride(4) != 1:
+        raise ValueError("x must be [B][H][T][N][D] with contiguous rows")
+    for t, n in ((idx, "idx"), (sums, "sums"), (wsum, "wsum")):
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % n)
+    B, _, _, N, _ = x.shape
+    strides = (ctypes.c_int64 * 4)(*[x.stride(i) for i in range(4)])
+    check(_lib.lib().loopvq_kmeans_accumulate(ctypes.byref(g), _ptr(x), strides, B, N, _ptr(idx), idx.shape[3],
+                                              _ptr(weight), ctypes.byref(pt) if pt is not None else None,
+                                              _ptr(sums), _ptr(wsum), _stream(stream)))
+
+
+def kmeans_finalize(g: Geom, sums, wsum, codebook, stream=None):
+    """codebook bf16 [H][n_blk][K][G] <- bf16(sums / wsum) where wsum > 0."""
+    _need(sums, torch.float64, "sums")
+    _need(wsum, torch.float64, "wsum")
+    _need(codebook, torch.bfloat16, "codebook")
+    for t, n in ((sums, "sums"), (wsum, "wsum"), (codebook, "codebook")):
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % n)
+    check(_lib.lib().loopvq_kmeans_finalize(ctypes.byref(g), _ptr(sums), _ptr(wsum), _ptr(codebook),
+                                            _stream(stream)))
+    return codebook
+
+
 def rope_table(n_pos, D=128, theta=1.0e4, device="cuda", stream=None):
     """fp16 [n_pos][D/8][8]: per 4 frequencies, their cosines then sines."""
     t = torch.empty((n_pos, D // 8, 8), dtype=torch.float16, device=device)

@@ -59,6 +59,20 @@ struct TasqStatsArgs {
   int32_t B, H, T, T_c, n_blk, N, D;
 };
 
+struct KmeansArgs {
+  const uint16_t* x;          // bf16 rows of D (the encoded K or V cache), strides in elements
+  int64_t xs0, xs1, xs2, xs3;
+  const uint8_t* idx;         // [B][H][n_blk][N_cap][D/c] assignments (loopvq_encode)
+  const float* weight;        // [B][H][n_blk][N][D/c] importance per joint vector, or null (all 1)
+  const float* w;             // pre-transform (keys) or null
+  const int16_t* perm;
+  const uint16_t* sigma;      // fp16 [B][sig_cap][T]
+  int32_t sig_cap;
+  double* sums;               // [H][n_blk][K][G], accumulated
+  double* wsum;               // [H][n_blk][K], accumulated
+  int32_t H, T, T_c, n_blk, K, G, N, N_cap, D;
+};
+
 struct MergeArgs {
   const float* ws;
   float* out;
@@ -76,6 +90,11 @@ hipError_t launch_rope_table(double theta, int D, int n_pos, void* table, hipStr
 // Mean, then covariance, of the block-stacked scaled keys (needs sigma
 // written first); T_c*D a multiple of 64 and at most 1024.
 hipError_t launch_tasq_stats(const TasqStatsArgs& a, hipStream_t s);
+// Weighted k-means update: accumulate (G in {16, 32}, K <= 256), then
+// e = bf16(sums / wsum) for the n = H*n_blk*K*G codebook entries with wsum > 0.
+hipError_t launch_kmeans_accumulate(const KmeansArgs& a, int B, bool tasq, hipStream_t s);
+hipError_t launch_kmeans_finalize(const double* sums, const double* wsum, uint16_t* cb, int64_t n, int G,
+                                  hipStream_t s);
 hipError_t launch_decode_fast(int G, const DecodeArgs& a, hipStream_t s);
 // T_c = 4, no pre-transform; one workgroup per (split, group of hpw q-heads,
 // batch x served step); hpw in {1, 2, 4} divides the GQA group size.

@@ -326,6 +326,65 @@ loopvq_status loopvq_tasq_pair_permutation(const double* cov, int32_t T_c, int32
   return LOOPVQ_OK;
 }
 
+loopvq_status loopvq_kmeans_accumulate(const loopvq_geom* g, const void* x, const int64_t x_strides[4],
+                                      int32_t B, int32_t N, const uint8_t* idx, int32_t N_cap,
+                                      const float* weight, const loopvq_pretransform* pt, double* sums,
+                                      double* wsum, void* stream) {
+  g_err[0] = 0;
+  loopvq_status st = check_geom(g);
+  if (st != LOOPVQ_OK) return st;
+  if (B < 0 || N < 0) return fail(LOOPVQ_EINVAL, "B=%d and N=%d must be >= 0", B, N);
+  if (N > N_cap) return fail(LOOPVQ_EINVAL, "N=%d exceeds N_cap=%d", N, N_cap);
+  if (N == 0 || B == 0) return LOOPVQ_OK;
+  if (!x || !x_strides || !idx || !sums || !wsum) return fail(LOOPVQ_EINVAL, "NULL pointer");
+  for (int i = 0; i < 4; ++i)
+    if (x_strides[i] <= 0) return fail(LOOPVQ_EINVAL, "x_strides[%d]=%lld must be positive", i, (long long)x_strides[i]);
+  if (x_strides[3] < g->D) return fail(LOOPVQ_EINVAL, "token stride %lld < D", (long long)x_strides[3]);
+  st = check_pt(pt, B, N, false);
+  if (st != LOOPVQ_OK) return st;
+  loopvq::KmeansArgs a{};
+  a.x = static_cast<const uint16_t*>(x);
+  a.xs0 = x_strides[0];
+  a.xs1 = x_strides[1];
+  a.xs2 = x_strides[2];
+  a.xs3 = x_strides[3];
+  a.idx = idx;
+  a.weight = weight;
+  if (pt) {
+    a.w = pt->w;
+    a.perm = pt->perm;
+    a.sigma = pt->sigma;
+    a.sig_cap = pt->N_cap;
+  }
+  a.sums = sums;
+  a.wsum = wsum;
+  a.H = g->n_kv_heads;
+  a.T = g->T;
+  a.T_c = g->T_c;
+  a.n_blk = g->T / g->T_c;
+  a.K = g->K;
+  a.G = g->G;
+  a.N = N;
+  a.N_cap = N_cap;
+  a.D = g->D;
+  hipError_t e = loopvq::launch_kmeans_accumulate(a, B, pt != nullptr, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "k-means accumulate launch");
+  return LOOPVQ_OK;
+}
+
+loopvq_status loopvq_kmeans_finalize(const loopvq_geom* g, const double* sums, const double* wsum,
+                                    void* codebook, void* stream) {
+  g_err[0] = 0;
+  loopvq_status st = check_geom(g);
+  if (st != LOOPVQ_OK) return st;
+  if (!sums || !wsum || !codebook) return fail(LOOPVQ_EINVAL, "NULL pointer");
+  const int64_t n = (int64_t)g->n_kv_heads * (g->T / g->T_c) * g->K * g->G;
+  hipError_t e = loopvq::launch_kmeans_finalize(sums, wsum, static_cast<uint16_t*>(codebook), n, g->G,
+                                                reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "k-means finalize launch");
+  return LOOPVQ_OK;
+}
+
 static loopvq_status check_decode_shape(const loopvq_geom* g, int32_t B, int32_t N, int32_t step0,
                                         int32_t n_steps) {
   loopvq_status st = check_geom(g);

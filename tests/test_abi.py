@@ -122,3 +122,21 @@ def test_decode_workspace_and_errors():
     assert call(ws_bytes=need.value - 1) == -4
     assert call(ws=P(0)) == -4
     assert call(B=0) == 0                     # nothing to do
+
+
+def test_kmeans_entry_points_reject_bad_arguments():
+    import sub_bit_loop_amd as lv
+    _, lib = _lib()
+    g = lv.geom(128, 4, 4, 16, 256, 1, 1)
+    P = ctypes.c_void_p
+    st = (ctypes.c_int64 * 4)(4 * 8 * 128, 4 * 8 * 128, 8 * 128, 128)
+    P16 = P(16)
+    # N > N_cap, negative B, NULL outputs: all refused on the host
+    assert lib.loopvq_kmeans_accumulate(ctypes.byref(g), P16, st, 1, 9, P16, 8, None, None, P16, P16, None) == -1
+    assert lib.loopvq_kmeans_accumulate(ctypes.byref(g), P16, st, -1, 8, P16, 8, None, None, P16, P16, None) == -1
+    assert lib.loopvq_kmeans_accumulate(ctypes.byref(g), P16, st, 1, 8, P16, 8, None, None, None, P16, None) == -1
+    # nothing to do
+    assert lib.loopvq_kmeans_accumulate(ctypes.byref(g), None, None, 1, 0, None, 8, None, None, None, None, None) == 0
+    assert lib.loopvq_kmeans_finalize(ctypes.byref(g), None, P16, P16, None) == -1
+    bad = lv.geom(128, 4, 4, 24, 256, 1, 1)
+    assert lib.loopvq_kmeans_finalize(ctypes.byref(bad), P16, P16, P16, None) != 0
