@@ -201,33 +201,48 @@ def test_small_geometries(geo):
     _say("  decode worst rel err %.3g over %d rows" % (worst, len(rows)))
 
 
-def test_edge_cases():
+EDGE_GEOMS = [
+    # name, G, T, H_kv, H_q, pretransform  (the plain multi-step, the GQA MFMA and the
+    # pre-transform kernels; T = 8 gives ranges that cross a block boundary)
+    ("mha", 16, 4, 1, 1, False),
+    ("gqa4-2blk", 32, 8, 1, 4, False),
+    ("pretransform-2blk", 16, 8, 1, 1, True),
+]
+
+
+@pytest.mark.parametrize("geo", EDGE_GEOMS, ids=[x[0] for x in EDGE_GEOMS])
+def test_edge_cases(geo):
     s = _lib()
-    cfg = small_cfg(1, B=3, N=300, H_kv=1, H_q=1, n_calib=1024, kmeans_iters=5)
+    name, G, T, H, Hq, tasq = geo
+    _say("edge cases", name)
+    cfg = small_cfg(1, G=G, T=T, B=3, N=300, H_kv=H, H_q=Hq, tasq=tasq, rho_k=(0.85,) * (T - 1),
+                    rho_v=(0.9,) * (T - 1), n_calib=1024, kmeans_iters=5)
     inp = build_inputs(cfg, 0, "cuda")
     kidx, vidx, sigma, pt = _encode_all(s, cfg, inp)
+    all_rows = [(b, hq, t) for b in range(3) for hq in range(Hq) for t in range(T)]
     # only sinks (N = 0)
     out, lse = _decode(s, cfg, inp, kidx, vidx, pt, N=0)
     torch.cuda.synchronize()
-    _check_rows(cfg, inp, kidx, vidx, sigma, out, lse, [(b, 0, t) for b in range(3) for t in range(4)], N=0)
+    _check_rows(cfg, inp, kidx, vidx, sigma, out, lse, all_rows, N=0)
     # per-batch lengths, one row with no keys at all
     seq = torch.tensor([0, 5, 1000], dtype=torch.int32, device="cuda")
     out, lse = _decode(s, cfg, inp, kidx, vidx, pt, seq=seq, n_s=0)
     torch.cuda.synchronize()
     inp0 = dict(inp, sink_k=None, sink_v=None)
-    _check_rows(cfg, inp0, kidx, vidx, sigma, out, lse, [(b, 0, t) for b in range(3) for t in range(4)],
-                seq=seq.cpu().numpy())
-    # step sub-ranges: one step, and a middle pair
-    for step0, n_steps in ((2, 1), (1, 2)):
+    _check_rows(cfg, inp0, kidx, vidx, sigma, out, lse, all_rows, seq=seq.cpu().numpy())
+    # step sub-ranges: one step, a middle pair, and (T = 8) ranges across the block boundary
+    ranges = [(2, 1), (1, 2)] + ([(3, 2), (2, 5), (5, 3)] if T == 8 else [])
+    for step0, n_steps in ranges:
         out, lse = _decode(s, cfg, inp, kidx, vidx, pt, step0=step0, n_steps=n_steps)
         torch.cuda.synchronize()
         _check_rows(cfg, inp, kidx, vidx, sigma, out, lse,
-                    [(b, 0, t) for b in range(3) for t in range(step0, step0 + n_steps)], step0=step0)
+                    [(b, hq, t) for b in range(3) for hq in range(Hq) for t in range(step0, step0 + n_steps)],
+                    step0=step0)
     # append: encode tokens [200, 300) at tok0 = 200 into a fresh buffer
     g = _geom(s, cfg)
     idx2 = torch.zeros_like(kidx)
     idx2[:, :, :, :200] = kidx[:, :, :, :200]
-    s.encode(g, inp["k"][:, :, :, 200:], inp["k_cb"], idx2, tok0=200)
+    s.encode(g, inp["k"][:, :, :, 200:], inp["k_cb"], idx2, tok0=200, pt=pt)
     torch.cuda.synchronize()
     assert torch.equal(idx2, kidx)
     # determinism: identical bytes on a second run
