@@ -44,6 +44,10 @@ def _run_config(idx, n_enc=3, n_rows=8, layer=0):
     return s, cfg, inp, kidx, vidx, sigma, pt
 
 
+def test_config1_full():
+    _run_config(1, n_rows=4)
+
+
 def test_config2_full():
     _run_config(2)
 
