@@ -380,6 +380,7 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
     load_rows(0, jj);
     load_cs(a.n_s + jj, CS);
   }
+  int tiles = 0;
   for (int base = 0; base < n_tok; base += NW * TOK) {
     const bool valid = base + wave * TOK + t16 < n_tok;
     uint32_t kd[4 * RW], vd[4 * RW];
@@ -456,9 +457,15 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
         pv(t, Vw);
       }
     }
-    flush();
+    // fp16 partials over two tiles (32 tokens): |p| <= 2^kGLag, |v| <= 2^kGVLim,
+    // so a partial stays below 2^15
+    if (++tiles == 2) {
+      flush();
+      tiles = 0;
+    }
     wave_sync();
   }
+  flush();
 
   // ---- per-wave row totals, then merge the waves through LDS (the codebook
   // memory, once every wave is done with it)
