@@ -10,3 +10,4 @@ Every function is the plain definition from the LoopVQ review (arXiv
 from .loopvq_ref import *  # noqa: F401,F403
 from .tasq_perm import *  # noqa: F401,F403,E402
 from .kmeans_ref import *  # noqa: F401,F403,E402
+from .finetune_ref import *  # noqa: F401,F403,E402
