@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define LOOPVQ_ABI_VERSION 3
+#define LOOPVQ_ABI_VERSION 4
 
 typedef enum {
   LOOPVQ_OK = 0,
@@ -245,6 +245,78 @@ loopvq_status loopvq_kmeans_accumulate(const loopvq_geom* g, const void* x, cons
  * Errors: EINVAL for NULL pointers; ENOTSUP as for the geometry. */
 loopvq_status loopvq_kmeans_finalize(const loopvq_geom* g, const double* sums, const double* wsum,
                                     void* codebook, void* stream);
+
+/* ---- loop-aware codebook fine-tuning (section 3.2, eq. 6) ----
+ * The objective compares the model's outputs with the precise cache and with
+ * the cache rebuilt from the codebooks at every position after the sinks,
+ * with all loop steps reading the rebuilt cache; the codebook entries get
+ * exact gradients by backpropagation (the assignment is a constant of each
+ * iteration).  The two calls below are that attention and its backward pass;
+ * the model around them and the optimizer are the caller's. */
+
+/* loopvq_rope_table_f32 -- fp32 RoPE table for the calls below.
+ *   table  device fp32 [n_pos][D/2][2]: cos and sin of p * theta^(-2f/D),
+ *          evaluated in fp64 on the GPU, rounded once to fp32
+ * Errors: EINVAL for NULL table, n_pos < 1, odd D, theta <= 0. */
+loopvq_status loopvq_rope_table_f32(float theta, int32_t D, int32_t n_pos, float* table, void* stream);
+
+/* loopvq_prefill_attn -- causal attention of the N positions after the sinks
+ * over the compressed cache of those N tokens.
+ *
+ * For every batch b, q-head hq and loop step t in [step0, step0 + n_steps),
+ * with kv-head h = hq / (n_q_heads / n_kv_heads), block beta = t / T_c and
+ * m = t % T_c: query i (i < N) sits at position n_s + i and attends to the
+ * n_s bf16 sinks sink_k[b][h][t][s] (position s) and to the tokens j <= i,
+ * whose channel q*c + i' is k_cb[h][beta][k_idx[b][h][beta][j][q]][i'*T_c + m]
+ * (section 3.1 eq. 5) at position n_s + j; keys are rotated (RoPE) at their
+ * positions, values come from v_idx / v_cb / sink_v; scale 1/sqrt(D).
+ *   q          device fp32 [B][n_q_heads][n_steps][N][D], already rotated
+ *   k_idx, v_idx  device uint8 [B][n_kv_heads][n_blk][N_cap][D/c]
+ *   k_cb, v_cb device bf16 [n_kv_heads][n_blk][K][G]
+ *   sink_k, sink_v  device bf16 [B][n_kv_heads][T][n_s][D], pre-RoPE; may be
+ *              NULL when n_s == 0
+ *   rope_table device fp32 table of loopvq_rope_table_f32 with
+ *              n_pos >= n_s + N positions
+ *   out        device fp32 [B][n_q_heads][n_steps][N][D], written
+ *   lse        device fp32 [B][n_q_heads][n_steps][N], written (natural log)
+ * Alignment: q, sinks, rope_table and out 16-byte aligned.
+ * Errors: EINVAL for NULL pointers, bad geometry, step range outside [0, T),
+ * N > N_cap, n_pos too small, misalignment; ENOTSUP as for loopvq_encode.
+ * B == 0 or N == 0 is a no-op (the tensor pointers may then be NULL).
+ * Deterministic. */
+loopvq_status loopvq_prefill_attn(const loopvq_geom* g, const float* q, int32_t step0, int32_t n_steps,
+                                  int32_t B, int32_t N, const uint8_t* k_idx, const uint8_t* v_idx,
+                                  int32_t N_cap, const void* k_cb, const void* v_cb, const void* sink_k,
+                                  const void* sink_v, int32_t n_s, const float* rope_table, int32_t n_pos,
+                                  float* out, float* lse, void* stream);
+
+/* loopvq_prefill_attn_backward_workspace -- bytes of scratch the backward
+ * needs: B * n_q_heads * n_steps * N floats. */
+loopvq_status loopvq_prefill_attn_backward_workspace(const loopvq_geom* g, int32_t B, int32_t N,
+                                                     int32_t step0, int32_t n_steps, size_t* bytes);
+
+/* loopvq_prefill_attn_backward -- gradients of loopvq_prefill_attn for a
+ * given d_out (same arguments as the forward, plus its out and lse):
+ *   d_q        device fp32 like q, written
+ *   d_k_cb, d_v_cb  device fp32 [n_kv_heads][n_blk][K][G], overwritten with
+ *              the gradient with respect to the bf16 codebook entries the
+ *              forward read (summed over every batch entry, q-head, step and
+ *              token of the call; keys pass back through the rotation)
+ *   workspace  device scratch of loopvq_prefill_attn_backward_workspace()
+ *              bytes, 16-byte aligned
+ * Alignment: as the forward, plus out, d_out and d_q 16-byte aligned.
+ * Errors: as the forward; EWORKSPACE for a short workspace.  The codebook
+ * gradients are summed with fp32 atomics, so their last bits depend on the
+ * order of execution; d_q is deterministic.  B == 0 or N == 0 zeroes
+ * d_k_cb and d_v_cb (which must not be NULL; the other tensors may be). */
+loopvq_status loopvq_prefill_attn_backward(const loopvq_geom* g, const float* q, int32_t step0,
+                                           int32_t n_steps, int32_t B, int32_t N, const uint8_t* k_idx,
+                                           const uint8_t* v_idx, int32_t N_cap, const void* k_cb,
+                                           const void* v_cb, const void* sink_k, const void* sink_v,
+                                           int32_t n_s, const float* rope_table, int32_t n_pos,
+                                           const float* out, const float* lse, const float* d_out, float* d_q,
+                                           float* d_k_cb, float* d_v_cb, void* workspace,
+                                           size_t workspace_bytes, void* stream);
 
 /* Thread-local text of the last non-OK status ("" if none). */
 const char* loopvq_last_error(void);

@@ -14,7 +14,9 @@ STATUS_NAME = {OK: "OK", EINVAL: "EINVAL", ENOTSUP: "ENOTSUP", EHIP: "EHIP", EWO
 # Names the C header declares; tests check that every one is exported.
 EXPORTS = ("loopvq_encode", "loopvq_rope_table", "loopvq_decode_attn_workspace",
            "loopvq_decode_attn", "loopvq_tasq_covariance", "loopvq_tasq_pair_permutation",
-           "loopvq_kmeans_accumulate", "loopvq_kmeans_finalize", "loopvq_last_error", "loopvq_abi_version")
+           "loopvq_kmeans_accumulate", "loopvq_kmeans_finalize", "loopvq_rope_table_f32",
+           "loopvq_prefill_attn", "loopvq_prefill_attn_backward_workspace", "loopvq_prefill_attn_backward",
+           "loopvq_last_error", "loopvq_abi_version")
 
 
 class Geom(ctypes.Structure):
@@ -64,6 +66,15 @@ def lib():
     L.loopvq_kmeans_accumulate.restype = ctypes.c_int
     L.loopvq_kmeans_finalize.argtypes = [GP, P, P, P, P]
     L.loopvq_kmeans_finalize.restype = ctypes.c_int
+    L.loopvq_rope_table_f32.argtypes = [ctypes.c_float, I32, I32, P, P]
+    L.loopvq_rope_table_f32.restype = ctypes.c_int
+    L.loopvq_prefill_attn.argtypes = [GP, P, I32, I32, I32, I32, P, P, I32, P, P, P, P, I32, P, I32, P, P, P]
+    L.loopvq_prefill_attn.restype = ctypes.c_int
+    L.loopvq_prefill_attn_backward_workspace.argtypes = [GP, I32, I32, I32, I32, ctypes.POINTER(SZ)]
+    L.loopvq_prefill_attn_backward_workspace.restype = ctypes.c_int
+    L.loopvq_prefill_attn_backward.argtypes = [GP, P, I32, I32, I32, I32, P, P, I32, P, P, P, P, I32, P, I32,
+                                               P, P, P, P, P, P, P, SZ, P]
+    L.loopvq_prefill_attn_backward.restype = ctypes.c_int
     L.loopvq_last_error.argtypes = []
     L.loopvq_last_error.restype = ctypes.c_char_p
     L.loopvq_abi_version.argtypes = []

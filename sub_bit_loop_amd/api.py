@@ -197,3 +197,76 @@ def decode_attn(g: Geom, q, k_idx, v_idx, k_cb, v_cb, sink_k, sink_v, rope, N=No
         workspace.numel() * workspace.element_size(), _stream(stream))
     check(st)
     return out, lse
+
+
+def rope_table_f32(n_pos, D=128, theta=1.0e4, device="cuda", stream=None):
+    """fp32 [n_pos][D/2][2]: (cos, sin) of angle p * theta^(-2f/D), computed in fp64."""
+    t = torch.empty((n_pos, D // 2, 2), dtype=torch.float32, device=device)
+    check(_lib.lib().loopvq_rope_table_f32(theta, D, n_pos, _ptr(t), _stream(stream)))
+    return t
+
+
+def _prefill_common(q, k_idx, v_idx, k_cb, v_cb, sink_k, sink_v, rope):
+    _need(q, torch.float32, "q")
+    _need(k_idx, torch.uint8, "k_idx")
+    _need(v_idx, torch.uint8, "v_idx")
+    _need(k_cb, torch.bfloat16, "k_cb")
+    _need(v_cb, torch.bfloat16, "v_cb")
+    _need(rope, torch.float32, "rope")
+    for t, n in ((q, "q"), (k_idx, "k_idx"), (v_idx, "v_idx"), (k_cb, "k_cb"), (v_cb, "v_cb"), (rope, "rope")):
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % n)
+    n_s = 0
+    if sink_k is not None:
+        _need(sink_k, torch.bfloat16, "sink_k")
+        _need(sink_v, torch.bfloat16, "sink_v")
+        n_s = sink_k.shape[3]
+    return n_s
+
+
+def prefill_attn(g: Geom, q, k_idx, v_idx, k_cb, v_cb, sink_k, sink_v, rope, step0=0, out=None, lse=None,
+                 stream=None):
+    """Causal attention of the N positions after the sinks over the compressed cache.
+    q fp32 [B][Hq][n_steps][N][D] (post-RoPE, query i at position n_s + i); k_idx/v_idx uint8
+    [B][H][n_blk][N_cap][D/c]; k_cb/v_cb bf16 [H][n_blk][K][G]; sinks bf16 [B][H][T][n_s][D] or
+    None; rope fp32 table from rope_table_f32().  Returns (out fp32 like q, lse fp32 [B][Hq][n_steps][N])."""
+    n_s = _prefill_common(q, k_idx, v_idx, k_cb, v_cb, sink_k, sink_v, rope)
+    B, Hq, n_steps, N, D = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, n_steps, N), dtype=torch.float32, device=q.device)
+    check(_lib.lib().loopvq_prefill_attn(
+        ctypes.byref(g), _ptr(q), step0, n_steps, B, N, _ptr(k_idx), _ptr(v_idx), k_idx.shape[3], _ptr(k_cb),
+        _ptr(v_cb), _ptr(sink_k), _ptr(sink_v), n_s, _ptr(rope), rope.shape[0], _ptr(out), _ptr(lse),
+        _stream(stream)))
+    return out, lse
+
+
+def prefill_attn_backward(g: Geom, q, k_idx, v_idx, k_cb, v_cb, sink_k, sink_v, rope, out, lse, d_out,
+                          step0=0, d_q=None, d_k_cb=None, d_v_cb=None, workspace=None, stream=None):
+    """Gradients of prefill_attn: returns (d_q fp32 like q, d_k_cb, d_v_cb fp32 [H][n_blk][K][G]).
+    The codebook gradients are overwritten (sums over every q-head, step and token in the call)."""
+    n_s = _prefill_common(q, k_idx, v_idx, k_cb, v_cb, sink_k, sink_v, rope)
+    for t, n in ((out, "out"), (lse, "lse"), (d_out, "d_out")):
+        _need(t, torch.float32, n)
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % n)
+    B, Hq, n_steps, N, D = q.shape
+    if d_q is None:
+        d_q = torch.empty_like(q)
+    if d_k_cb is None:
+        d_k_cb = torch.empty(k_cb.shape, dtype=torch.float32, device=q.device)
+    if d_v_cb is None:
+        d_v_cb = torch.empty(v_cb.shape, dtype=torch.float32, device=q.device)
+    need = ctypes.c_size_t(0)
+    check(_lib.lib().loopvq_prefill_attn_backward_workspace(ctypes.byref(g), B, N, step0, n_steps,
+                                                            ctypes.byref(need)))
+    if workspace is None or workspace.numel() * workspace.element_size() < need.value:
+        workspace = torch.empty(max(need.value, 16), dtype=torch.uint8, device=q.device)
+    check(_lib.lib().loopvq_prefill_attn_backward(
+        ctypes.byref(g), _ptr(q), step0, n_steps, B, N, _ptr(k_idx), _ptr(v_idx), k_idx.shape[3], _ptr(k_cb),
+        _ptr(v_cb), _ptr(sink_k), _ptr(sink_v), n_s, _ptr(rope), rope.shape[0], _ptr(out), _ptr(lse),
+        _ptr(d_out), _ptr(d_q), _ptr(d_k_cb), _ptr(d_v_cb), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return d_q, d_k_cb, d_v_cb

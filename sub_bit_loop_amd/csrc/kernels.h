@@ -73,6 +73,26 @@ struct KmeansArgs {
   int32_t H, T, T_c, n_blk, K, G, N, N_cap, D;
 };
 
+struct PrefillArgs {
+  const float* q;             // fp32 [B][Hq][n_steps][N][D], post-RoPE
+  const uint8_t* kidx;        // [B][H][n_blk][N_cap][D/c]
+  const uint8_t* vidx;
+  const uint16_t* kcb;        // bf16 [H][n_blk][K][G]
+  const uint16_t* vcb;
+  const uint16_t* sk;         // bf16 [B][H][T][n_s][D], pre-RoPE
+  const uint16_t* sv;
+  const float* rope;          // fp32 [n_pos][D/2][2] (cos, sin)
+  float* out;                 // fp32 [B][Hq][n_steps][N][D] (written forward, read backward)
+  float* lse;                 // fp32 [B][Hq][n_steps][N], natural log
+  const float* dout;          // backward: gradient of out
+  float* dq;                  // backward: fp32 like q
+  float* dkcb;                // backward: fp32 [H][n_blk][K][G]
+  float* dvcb;
+  float* delta;               // backward scratch: [B][Hq][n_steps][N]
+  int32_t B, H, Hq, T, T_c, n_blk, K, G, N, N_cap, n_s, step0, n_steps, gqa;
+  float scale;                // 1 / sqrt(D)
+};
+
 struct MergeArgs {
   const float* ws;
   float* out;
@@ -108,5 +128,11 @@ hipError_t launch_decode_tasq(int G, const DecodeArgs& a, hipStream_t s);
 constexpr int kDecodeThreads = 256;
 constexpr int kEncodeThreads = 256;
 constexpr int kEncodeTokens = 128;  // tokens per encode workgroup
+
+hipError_t launch_fill_f32(float* p, int64_t n, hipStream_t s);   // p[0..n) = 0
+hipError_t launch_rope_table_f32(float* tab, int n_pos, int D, double theta, hipStream_t s);
+// forward (out, lse) or backward (delta, zeroed then accumulated codebook
+// gradients, dq); C = G / T_c in {2, 4, 8, 16, 32}
+hipError_t launch_prefill(const PrefillArgs& a, int C, bool backward, hipStream_t s);
 
 }  // namespace loopvq

@@ -510,4 +510,132 @@ loopvq_status loopvq_decode_attn(const loopvq_geom* g, const void* q, int32_t st
   return LOOPVQ_OK;
 }
 
+loopvq_status loopvq_rope_table_f32(float theta, int32_t D, int32_t n_pos, float* table, void* stream) {
+  g_err[0] = 0;
+  if (!table) return fail(LOOPVQ_EINVAL, "table is NULL");
+  if (n_pos < 1) return fail(LOOPVQ_EINVAL, "n_pos=%d must be >= 1", n_pos);
+  if (D < 2 || D % 2) return fail(LOOPVQ_EINVAL, "D=%d must be even and >= 2", D);
+  if (!(theta > 0.f) || !std::isfinite(theta)) return fail(LOOPVQ_EINVAL, "theta must be positive");
+  hipError_t e = loopvq::launch_rope_table_f32(table, n_pos, D, (double)theta, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "rope table launch");
+  return LOOPVQ_OK;
+}
+
+static loopvq_status prefill_args(const loopvq_geom* g, const float* q, int32_t step0, int32_t n_steps,
+                                  int32_t B, int32_t N, const uint8_t* k_idx, const uint8_t* v_idx,
+                                  int32_t N_cap, const void* k_cb, const void* v_cb, const void* sink_k,
+                                  const void* sink_v, int32_t n_s, const float* rope_table, int32_t n_pos,
+                                  loopvq::PrefillArgs& a) {
+  loopvq_status st = check_decode_shape(g, B, N, step0, n_steps);
+  if (st != LOOPVQ_OK) return st;
+  if (n_s < 0) return fail(LOOPVQ_EINVAL, "n_s=%d must be >= 0", n_s);
+  if (N > N_cap) return fail(LOOPVQ_EINVAL, "N=%d exceeds N_cap=%d", N, N_cap);
+  if (B > 0 && N > 0) {   // an empty call may pass NULL tensors
+    if (!q || !k_idx || !v_idx || !k_cb || !v_cb || !rope_table)
+      return fail(LOOPVQ_EINVAL, "NULL tensor pointer");
+    if (n_s > 0 && (!sink_k || !sink_v)) return fail(LOOPVQ_EINVAL, "sinks are NULL with n_s=%d", n_s);
+    if ((long long)n_s + N > n_pos) return fail(LOOPVQ_EINVAL, "rope table has %d positions, need %lld", n_pos,
+                                                 (long long)n_s + N);
+  }
+  for (const void* p : {(const void*)q, (const void*)rope_table, sink_k, sink_v})
+    if (reinterpret_cast<uintptr_t>(p) % 16) return fail(LOOPVQ_EINVAL, "q, rope_table and sinks must be 16-byte aligned");
+  a = loopvq::PrefillArgs{};
+  a.q = q;
+  a.kidx = k_idx;
+  a.vidx = v_idx;
+  a.kcb = static_cast<const uint16_t*>(k_cb);
+  a.vcb = static_cast<const uint16_t*>(v_cb);
+  a.sk = static_cast<const uint16_t*>(sink_k);
+  a.sv = static_cast<const uint16_t*>(sink_v);
+  a.rope = rope_table;
+  a.B = B;
+  a.H = g->n_kv_heads;
+  a.Hq = g->n_q_heads;
+  a.T = g->T;
+  a.T_c = g->T_c;
+  a.n_blk = g->T / g->T_c;
+  a.K = g->K;
+  a.G = g->G;
+  a.N = N;
+  a.N_cap = N_cap;
+  a.n_s = n_s;
+  a.step0 = step0;
+  a.n_steps = n_steps;
+  a.gqa = g->n_q_heads / g->n_kv_heads;
+  a.scale = (float)(1.0 / std::sqrt((double)g->D));
+  return LOOPVQ_OK;
+}
+
+loopvq_status loopvq_prefill_attn(const loopvq_geom* g, const float* q, int32_t step0, int32_t n_steps,
+                                  int32_t B, int32_t N, const uint8_t* k_idx, const uint8_t* v_idx,
+                                  int32_t N_cap, const void* k_cb, const void* v_cb, const void* sink_k,
+                                  const void* sink_v, int32_t n_s, const float* rope_table, int32_t n_pos,
+                                  float* out, float* lse, void* stream) {
+  g_err[0] = 0;
+  loopvq::PrefillArgs a;
+  loopvq_status st = prefill_args(g, q, step0, n_steps, B, N, k_idx, v_idx, N_cap, k_cb, v_cb, sink_k, sink_v,
+                                  n_s, rope_table, n_pos, a);
+  if (st != LOOPVQ_OK) return st;
+  if (B == 0 || N == 0) return LOOPVQ_OK;
+  if (!out || !lse) return fail(LOOPVQ_EINVAL, "out and lse must not be NULL");
+  if (reinterpret_cast<uintptr_t>(out) % 16) return fail(LOOPVQ_EINVAL, "out must be 16-byte aligned");
+  a.out = out;
+  a.lse = lse;
+  hipError_t e = loopvq::launch_prefill(a, g->G / g->T_c, false, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "prefill attention launch");
+  return LOOPVQ_OK;
+}
+
+loopvq_status loopvq_prefill_attn_backward_workspace(const loopvq_geom* g, int32_t B, int32_t N,
+                                                     int32_t step0, int32_t n_steps, size_t* bytes) {
+  g_err[0] = 0;
+  loopvq_status st = check_decode_shape(g, B, N, step0, n_steps);
+  if (st != LOOPVQ_OK) return st;
+  if (!bytes) return fail(LOOPVQ_EINVAL, "bytes is NULL");
+  *bytes = (size_t)B * g->n_q_heads * n_steps * N * sizeof(float);
+  return LOOPVQ_OK;
+}
+
+loopvq_status loopvq_prefill_attn_backward(const loopvq_geom* g, const float* q, int32_t step0,
+                                           int32_t n_steps, int32_t B, int32_t N, const uint8_t* k_idx,
+                                           const uint8_t* v_idx, int32_t N_cap, const void* k_cb,
+                                           const void* v_cb, const void* sink_k, const void* sink_v,
+                                           int32_t n_s, const float* rope_table, int32_t n_pos,
+                                           const float* out, const float* lse, const float* d_out, float* d_q,
+                                           float* d_k_cb, float* d_v_cb, void* workspace,
+                                           size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  loopvq::PrefillArgs a;
+  loopvq_status st = prefill_args(g, q, step0, n_steps, B, N, k_idx, v_idx, N_cap, k_cb, v_cb, sink_k, sink_v,
+                                  n_s, rope_table, n_pos, a);
+  if (st != LOOPVQ_OK) return st;
+  if (!d_k_cb || !d_v_cb) return fail(LOOPVQ_EINVAL, "NULL codebook gradient");
+  if (B > 0 && N > 0 && (!out || !lse || !d_out || !d_q)) return fail(LOOPVQ_EINVAL, "NULL tensor pointer");
+  for (const void* p : {(const void*)out, (const void*)d_out, (const void*)d_q})
+    if (reinterpret_cast<uintptr_t>(p) % 16) return fail(LOOPVQ_EINVAL, "out, d_out and d_q must be 16-byte aligned");
+  const size_t need = (size_t)B * g->n_q_heads * n_steps * N * sizeof(float);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(LOOPVQ_EWORKSPACE, "workspace of %zu bytes < %zu", workspace_bytes, need);
+  if (reinterpret_cast<uintptr_t>(workspace) % 16) return fail(LOOPVQ_EINVAL, "workspace must be 16-byte aligned");
+  a.out = const_cast<float*>(out);
+  a.lse = const_cast<float*>(lse);
+  a.dout = d_out;
+  a.dq = d_q;
+  a.dkcb = d_k_cb;
+  a.dvcb = d_v_cb;
+  a.delta = static_cast<float*>(workspace);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (B == 0 || N == 0) {
+    // nothing attends: the codebook gradients are zero
+    const int64_t ncb = (int64_t)g->n_kv_heads * (g->T / g->T_c) * g->K * g->G;
+    e = loopvq::launch_fill_f32(d_k_cb, ncb, s);
+    if (e == hipSuccess) e = loopvq::launch_fill_f32(d_v_cb, ncb, s);
+  } else {
+    e = loopvq::launch_prefill(a, g->G / g->T_c, true, s);
+  }
+  if (e != hipSuccess) return hip_fail(e, "prefill attention backward launch");
+  return LOOPVQ_OK;
+}
+
 }  // extern "C"

@@ -1,0 +1,490 @@
+// Causal attention of every position after the sinks over the compressed
+// cache, and its backward pass into the queries and the codebook entries:
+// the hot part of loop-aware codebook fine-tuning.
+//
+// LoopVQ review (arXiv 2611.05304), section 3.2 eq. (6): the objective is the
+// KL between the model's outputs with the precise cache and with the cache
+// rebuilt from the codebooks, over the N positions after the bf16 sinks, with
+// all T_c steps reading the rebuilt cache; the codebook entries get exact
+// gradients by backpropagation (the argmin itself is not differentiated).
+// Section 3.1 eq. (5): step m of a block reads coordinate i*T_c + m of the
+// shared codeword; RoPE is applied after the dequant (section "terms").
+//
+// Query i of step t sits at position n_s + i and attends to the n_s sinks
+// (positions 0..n_s-1, bf16, pre-RoPE) and to the tokens j <= i (position
+// n_s + j).  Everything is fp32; the RoPE table is fp32 (cos, sin) per
+// (position, frequency), computed in fp64.
+//
+// Thread layout (256 threads): a row (a query, or a key in the key-side
+// backward) is served by four lanes; lane `sub` owns the 16 frequencies
+// 16*sub .. 16*sub + 15 and both channels of each RoPE pair (f and f + 64),
+// so rotations stay inside a lane and a dot product is a 4-lane sum.
+#include "common.h"
+#include "kernels.h"
+
+namespace loopvq {
+
+namespace {
+
+constexpr int kPD = 128;              // head dimension
+constexpr int kPH = 64;               // RoPE pairs
+constexpr int kRows = 64;             // rows per workgroup (queries or keys)
+constexpr int kTile = 32;             // keys (or queries) staged per LDS tile
+constexpr int kLds = kPD + 4;         // padded LDS row
+
+__device__ __forceinline__ float quad_sum(float v) {
+  v += __shfl_xor(v, 1);
+  v += __shfl_xor(v, 2);
+  return v;
+}
+
+// Stage step m's slice of the K and V codebooks of (kv-head h, block beta)
+// as fp32 [K][C].
+template <int C>
+__device__ void stage_codebooks(const PrefillArgs& a, int h, int beta, int m, float* s_cbk, float* s_cbv) {
+  const int64_t base = ((int64_t)h * a.n_blk + beta) * a.K * a.G;
+  // all 256 byte values get a row (zero past K), so any index byte stays in bounds
+  for (int e = threadIdx.x; e < 256 * C; e += blockDim.x) {
+    const int r = e / C, i = e - r * C;
+    const int64_t o = base + (int64_t)r * a.G + i * a.T_c + m;
+    s_cbk[e] = r < a.K ? bf16_to_f32(a.kcb[o]) : 0.f;
+    s_cbv[e] = r < a.K ? bf16_to_f32(a.vcb[o]) : 0.f;
+  }
+}
+
+// Fill an LDS tile with cnt keys (rotated) and values: sinks j0.. (positions
+// j) when `sinks`, else tokens j0.. (positions n_s + j).  Thread (kk, fs)
+// writes frequencies 8*fs .. 8*fs + 7 of key kk and their partners.
+template <int C>
+__device__ void fill_tile(const PrefillArgs& a, int b, int h, int t, int beta, bool sinks, int j0, int cnt,
+                          const float* s_cbk, const float* s_cbv, float (*s_k)[kLds], float (*s_v)[kLds]) {
+  const int kk = threadIdx.x >> 3, fs = threadIdx.x & 7;
+  float klo[8], khi[8], vlo[8], vhi[8];
+  int pos = 0;
+  if (kk < cnt) {
+    const int j = j0 + kk;
+    if (sinks) {
+      pos = j;
+      const int64_t ro = ((((int64_t)b * a.H + h) * a.T + t) * a.n_s + j) * kPD;
+      const uint4 xl = *reinterpret_cast<const uint4*>(a.sk + ro + 8 * fs);
+      const uint4 xh = *reinterpret_cast<const uint4*>(a.sk + ro + kPH + 8 * fs);
+      const uint4 yl = *reinterpret_cast<const uint4*>(a.sv + ro + 8 * fs);
+      const uint4 yh = *reinterpret_cast<const uint4*>(a.sv + ro + kPH + 8 * fs);
+      const uint32_t wxl[4] = {xl.x, xl.y, xl.z, xl.w}, wxh[4] = {xh.x, xh.y, xh.z, xh.w};
+      const uint32_t wyl[4] = {yl.x, yl.y, yl.z, yl.w}, wyh[4] = {yh.x, yh.y, yh.z, yh.w};
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        klo[2 * w] = bf16lo(wxl[w]); klo[2 * w + 1] = bf16hi(wxl[w]);
+        khi[2 * w] = bf16lo(wxh[w]); khi[2 * w + 1] = bf16hi(wxh[w]);
+        vlo[2 * w] = bf16lo(wyl[w]); vlo[2 * w + 1] = bf16hi(wyl[w]);
+        vhi[2 * w] = bf16lo(wyh[w]); vhi[2 * w + 1] = bf16hi(wyh[w]);
+      }
+    } else {
+      pos = a.n_s + j;
+      const int64_t ir = ((((int64_t)b * a.H + h) * a.n_blk + beta) * a.N_cap + j) * (kPD / C);
+      const uint8_t* kr = a.kidx + ir;
+      const uint8_t* vr = a.vidx + ir;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int dl = 8 * fs + e, dh = kPH + 8 * fs + e;
+        klo[e] = s_cbk[kr[dl / C] * C + dl % C];
+        khi[e] = s_cbk[kr[dh / C] * C + dh % C];
+        vlo[e] = s_cbv[vr[dl / C] * C + dl % C];
+        vhi[e] = s_cbv[vr[dh / C] * C + dh % C];
+      }
+    }
+    const float4* cs = reinterpret_cast<const float4*>(a.rope + ((int64_t)pos * kPH + 8 * fs) * 2);
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+      const float4 w = cs[e2];     // (cos, sin) of two frequencies
+      const float c0 = w.x, s0 = w.y, c1 = w.z, s1 = w.w;
+      const float a0 = klo[2 * e2], b0 = khi[2 * e2], a1 = klo[2 * e2 + 1], b1 = khi[2 * e2 + 1];
+      klo[2 * e2] = a0 * c0 - b0 * s0;
+      khi[2 * e2] = b0 * c0 + a0 * s0;
+      klo[2 * e2 + 1] = a1 * c1 - b1 * s1;
+      khi[2 * e2 + 1] = b1 * c1 + a1 * s1;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) klo[e] = khi[e] = vlo[e] = vhi[e] = 0.f;
+  }
+#pragma unroll
+  for (int e4 = 0; e4 < 2; ++e4) {
+    *reinterpret_cast<float4*>(&s_k[kk][8 * fs + 4 * e4]) =
+        make_float4(klo[4 * e4], klo[4 * e4 + 1], klo[4 * e4 + 2], klo[4 * e4 + 3]);
+    *reinterpret_cast<float4*>(&s_k[kk][kPH + 8 * fs + 4 * e4]) =
+        make_float4(khi[4 * e4], khi[4 * e4 + 1], khi[4 * e4 + 2], khi[4 * e4 + 3]);
+    *reinterpret_cast<float4*>(&s_v[kk][8 * fs + 4 * e4]) =
+        make_float4(vlo[4 * e4], vlo[4 * e4 + 1], vlo[4 * e4 + 2], vlo[4 * e4 + 3]);
+    *reinterpret_cast<float4*>(&s_v[kk][kPH + 8 * fs + 4 * e4]) =
+        make_float4(vhi[4 * e4], vhi[4 * e4 + 1], vhi[4 * e4 + 2], vhi[4 * e4 + 3]);
+  }
+}
+
+// Row-local load / dot / axpy over a lane's 32 channels of a 128-wide row.
+struct Row32 {
+  float lo[16], hi[16];
+};
+
+__device__ __forceinline__ void load_row(Row32& r, const float* p, int sub, float scale) {
+  const float4* l = reinterpret_cast<const float4*>(p + 16 * sub);
+  const float4* hh = reinterpret_cast<const float4*>(p + kPH + 16 * sub);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const float4 x = l[u], y = hh[u];
+    r.lo[4 * u] = x.x * scale; r.lo[4 * u + 1] = x.y * scale; r.lo[4 * u + 2] = x.z * scale; r.lo[4 * u + 3] = x.w * scale;
+    r.hi[4 * u] = y.x * scale; r.hi[4 * u + 1] = y.y * scale; r.hi[4 * u + 2] = y.z * scale; r.hi[4 * u + 3] = y.w * scale;
+  }
+}
+
+__device__ __forceinline__ float dot_lds(const Row32& r, const float* row, int sub) {
+  const float4* l = reinterpret_cast<const float4*>(row + 16 * sub);
+  const float4* hh = reinterpret_cast<const float4*>(row + kPH + 16 * sub);
+  float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const float4 x = l[u], y = hh[u];
+    s0 = fmaf(r.lo[4 * u], x.x, s0); s1 = fmaf(r.lo[4 * u + 1], x.y, s1);
+    s0 = fmaf(r.lo[4 * u + 2], x.z, s0); s1 = fmaf(r.lo[4 * u + 3], x.w, s1);
+    s0 = fmaf(r.hi[4 * u], y.x, s0); s1 = fmaf(r.hi[4 * u + 1], y.y, s1);
+    s0 = fmaf(r.hi[4 * u + 2], y.z, s0); s1 = fmaf(r.hi[4 * u + 3], y.w, s1);
+  }
+  return s0 + s1;
+}
+
+__device__ __forceinline__ void axpy_lds(Row32& acc, float p, const float* row, int sub) {
+  const float4* l = reinterpret_cast<const float4*>(row + 16 * sub);
+  const float4* hh = reinterpret_cast<const float4*>(row + kPH + 16 * sub);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const float4 x = l[u], y = hh[u];
+    acc.lo[4 * u] = fmaf(p, x.x, acc.lo[4 * u]); acc.lo[4 * u + 1] = fmaf(p, x.y, acc.lo[4 * u + 1]);
+    acc.lo[4 * u + 2] = fmaf(p, x.z, acc.lo[4 * u + 2]); acc.lo[4 * u + 3] = fmaf(p, x.w, acc.lo[4 * u + 3]);
+    acc.hi[4 * u] = fmaf(p, y.x, acc.hi[4 * u]); acc.hi[4 * u + 1] = fmaf(p, y.y, acc.hi[4 * u + 1]);
+    acc.hi[4 * u + 2] = fmaf(p, y.z, acc.hi[4 * u + 2]); acc.hi[4 * u + 3] = fmaf(p, y.w, acc.hi[4 * u + 3]);
+  }
+}
+
+__device__ __forceinline__ void store_row(const Row32& r, float* p, int sub, float scale) {
+  float4* l = reinterpret_cast<float4*>(p + 16 * sub);
+  float4* hh = reinterpret_cast<float4*>(p + kPH + 16 * sub);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    l[u] = make_float4(r.lo[4 * u] * scale, r.lo[4 * u + 1] * scale, r.lo[4 * u + 2] * scale, r.lo[4 * u + 3] * scale);
+    hh[u] = make_float4(r.hi[4 * u] * scale, r.hi[4 * u + 1] * scale, r.hi[4 * u + 2] * scale, r.hi[4 * u + 3] * scale);
+  }
+}
+
+__device__ __forceinline__ void zero_row(Row32& r) {
+#pragma unroll
+  for (int e = 0; e < 16; ++e) r.lo[e] = r.hi[e] = 0.f;
+}
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.69314718055994531f;
+
+}  // namespace
+
+// fp32 (cos, sin) per (position, frequency): angle p * theta^(-2f/D) in fp64.
+__global__ __launch_bounds__(256) void rope_table_f32_kernel(float* tab, int n_pos, int D, double theta) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int H = D / 2;
+  if (e >= (int64_t)n_pos * H) return;
+  const int p = (int)(e / H), f = (int)(e - (int64_t)p * H);
+  const double om = pow(theta, -2.0 * (double)f / (double)D);
+  double s, c;
+  sincos((double)p * om, &s, &c);
+  tab[2 * e] = (float)c;
+  tab[2 * e + 1] = (float)s;
+}
+
+// Forward: out[b][hq][tl][i] and lse (natural log).  Grid (query tiles of 64,
+// H_q, B * n_steps).
+template <int C>
+__global__ __launch_bounds__(256) void prefill_fwd_kernel(PrefillArgs a) {
+  extern __shared__ float s_cb[];                    // [2][K*C] step slices
+  __shared__ __attribute__((aligned(16))) float s_k[kTile][kLds];
+  __shared__ __attribute__((aligned(16))) float s_v[kTile][kLds];
+  const int row = threadIdx.x >> 2, sub = threadIdx.x & 3;
+  const int hq = blockIdx.y, h = hq / a.gqa;
+  const int b = blockIdx.z / a.n_steps, tl = blockIdx.z - b * a.n_steps;
+  const int t = a.step0 + tl, beta = t / a.T_c, m = t - beta * a.T_c;
+  const int q0 = blockIdx.x * kRows;
+  const int i = q0 + row;
+  const bool vq = i < a.N;
+  float* s_cbk = s_cb;
+  float* s_cbv = s_cb + 256 * C;
+  stage_codebooks<C>(a, h, beta, m, s_cbk, s_cbv);
+
+  const int64_t qrow = ((((int64_t)b * a.Hq + hq) * a.n_steps + tl) * a.N + (vq ? i : 0)) * kPD;
+  Row32 q, o;
+  load_row(q, a.q + qrow, sub, a.scale * kLog2e);
+  zero_row(o);
+  float mx = -INFINITY, l = 0.f;
+
+  auto consume = [&](int cnt, int jbase, bool causal) {
+    for (int kk = 0; kk < cnt; ++kk) {
+      const float s = quad_sum(dot_lds(q, s_k[kk], sub));
+      if (!vq || (causal && jbase + kk > i)) continue;
+      if (s > mx) {
+        const float al = __builtin_amdgcn_exp2f(mx - s);
+        l *= al;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) { o.lo[e] *= al; o.hi[e] *= al; }
+        mx = s;
+      }
+      const float p = __builtin_amdgcn_exp2f(s - mx);
+      l += p;
+      axpy_lds(o, p, s_v[kk], sub);
+    }
+  };
+  for (int j0 = 0; j0 < a.n_s; j0 += kTile) {
+    const int cnt = min(kTile, a.n_s - j0);
+    __syncthreads();
+    fill_tile<C>(a, b, h, t, beta, true, j0, cnt, s_cbk, s_cbv, s_k, s_v);
+    __syncthreads();
+    consume(cnt, 0, false);
+  }
+  const int jend = min(a.N, q0 + kRows);
+  for (int j0 = 0; j0 < jend; j0 += kTile) {
+    const int cnt = min(kTile, jend - j0);
+    __syncthreads();
+    fill_tile<C>(a, b, h, t, beta, false, j0, cnt, s_cbk, s_cbv, s_k, s_v);
+    __syncthreads();
+    consume(cnt, j0, true);
+  }
+  if (vq) {
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    store_row(o, a.out + qrow, sub, inv);
+    if (sub == 0) a.lse[qrow / kPD] = l > 0.f ? (mx + __log2f(l)) * kLn2 : -INFINITY;
+  }
+}
+
+// delta[row] = sum_d dout[row][d] * out[row][d]; one wave per row.
+__global__ __launch_bounds__(256) void prefill_delta_kernel(const float* __restrict__ out,
+                                                            const float* __restrict__ dout,
+                                                            float* __restrict__ delta, int64_t rows) {
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (r >= rows) return;
+  const float2 x = reinterpret_cast<const float2*>(out + r * kPD)[lane];
+  const float2 y = reinterpret_cast<const float2*>(dout + r * kPD)[lane];
+  float s = x.x * y.x + x.y * y.y;
+  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+  if (lane == 0) delta[r] = s;
+}
+
+__global__ __launch_bounds__(256) void prefill_zero_kernel(float* __restrict__ p, int64_t n) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e < n) p[e] = 0.f;
+}
+
+// Key-side backward: for 64 tokens of one (b, q-head, step), accumulate the
+// gradients of their rotated keys and values over every query that sees
+// them, undo the rotation, and add them into the codeword entries the
+// tokens use (fp32 atomics).  Grid (token tiles of 64, H_q, B * n_steps).
+template <int C>
+__global__ __launch_bounds__(256) void prefill_bwd_kv_kernel(PrefillArgs a) {
+  extern __shared__ float s_gd[];                    // [2][K*C] gradient accumulators
+  __shared__ __attribute__((aligned(16))) float s_q[kTile][kLds];
+  __shared__ __attribute__((aligned(16))) float s_do[kTile][kLds];
+  __shared__ float s_l2[kTile], s_dl[kTile];
+  const int row = threadIdx.x >> 2, sub = threadIdx.x & 3;
+  const int hq = blockIdx.y, h = hq / a.gqa;
+  const int b = blockIdx.z / a.n_steps, tl = blockIdx.z - b * a.n_steps;
+  const int t = a.step0 + tl, beta = t / a.T_c, m = t - beta * a.T_c;
+  const int k0 = blockIdx.x * kRows;
+  const int j = k0 + row;
+  const bool vk = j < a.N;
+  float* s_gk = s_gd;
+  float* s_gv = s_gd + 256 * C;
+  for (int e = threadIdx.x; e < 2 * 256 * C; e += blockDim.x) s_gd[e] = 0.f;
+  __syncthreads();
+
+  // this lane's key (rotated) and value channels, straight from the codebooks
+  const int64_t ir = ((((int64_t)b * a.H + h) * a.n_blk + beta) * a.N_cap + (vk ? j : 0)) * (kPD / C);
+  const int64_t cbo = ((int64_t)h * a.n_blk + beta) * a.K * a.G;
+  Row32 kr, vv, dk, dv;
+  float cs[16], sn[16];
+  {
+    const int pos = a.n_s + (vk ? j : 0);
+    const float2* rp = reinterpret_cast<const float2*>(a.rope + ((int64_t)pos * kPH + 16 * sub) * 2);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int dl = 16 * sub + e, dh = kPH + dl;
+      // an index byte >= K (never written by the encode) reads the last entry
+      const int rkl = min((int)a.kidx[ir + dl / C], a.K - 1), rkh = min((int)a.kidx[ir + dh / C], a.K - 1);
+      const int rvl = min((int)a.vidx[ir + dl / C], a.K - 1), rvh = min((int)a.vidx[ir + dh / C], a.K - 1);
+      const float xl = bf16_to_f32(a.kcb[cbo + (int64_t)rkl * a.G + (dl % C) * a.T_c + m]);
+      const float xh = bf16_to_f32(a.kcb[cbo + (int64_t)rkh * a.G + (dh % C) * a.T_c + m]);
+      vv.lo[e] = bf16_to_f32(a.vcb[cbo + (int64_t)rvl * a.G + (dl % C) * a.T_c + m]);
+      vv.hi[e] = bf16_to_f32(a.vcb[cbo + (int64_t)rvh * a.G + (dh % C) * a.T_c + m]);
+      const float2 w = rp[e];
+      cs[e] = w.x;
+      sn[e] = w.y;
+      kr.lo[e] = xl * w.x - xh * w.y;
+      kr.hi[e] = xh * w.x + xl * w.y;
+    }
+  }
+  zero_row(dk);
+  zero_row(dv);
+  const float sc2 = a.scale * kLog2e;
+
+  // queries i >= k0 (earlier ones see none of these tokens)
+  for (int i0 = k0; i0 < a.N; i0 += kTile) {
+    const int cnt = min(kTile, a.N - i0);
+    __syncthreads();
+    {
+      // stage q (scaled to base-2 scores), dout, lse (base 2), delta
+      const int r = threadIdx.x >> 3, part = threadIdx.x & 7;
+      if (r < cnt) {
+        const int64_t qr = (((int64_t)b * a.Hq + hq) * a.n_steps + tl) * a.N + i0 + r;
+        const float4* qs = reinterpret_cast<const float4*>(a.q + qr * kPD + 16 * part);
+        const float4* ds = reinterpret_cast<const float4*>(a.dout + qr * kPD + 16 * part);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float4 x = qs[u];
+          *reinterpret_cast<float4*>(&s_q[r][16 * part + 4 * u]) = make_float4(x.x * sc2, x.y * sc2, x.z * sc2, x.w * sc2);
+          *reinterpret_cast<float4*>(&s_do[r][16 * part + 4 * u]) = ds[u];
+        }
+        if (part == 0) {
+          s_l2[r] = a.lse[qr] * kLog2e;
+          s_dl[r] = a.delta[qr];
+        }
+      }
+    }
+    __syncthreads();
+    for (int qq = 0; qq < cnt; ++qq) {
+      const int i = i0 + qq;
+      const float s = quad_sum(dot_lds(kr, s_q[qq], sub));
+      const float dp = quad_sum(dot_lds(vv, s_do[qq], sub));
+      if (!vk || j > i) continue;
+      const float p = __builtin_amdgcn_exp2f(s - s_l2[qq]);
+      axpy_lds(dv, p, s_do[qq], sub);
+      // d score / d rotated key = scale * q; s_q holds scale * log2(e) * q
+      axpy_lds(dk, p * (dp - s_dl[qq]) * kLn2, s_q[qq], sub);
+    }
+  }
+  // undo the rotation and scatter into the codeword entries
+  if (vk) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int dl = 16 * sub + e, dh = kPH + dl;
+      const float gl = dk.lo[e] * cs[e] + dk.hi[e] * sn[e];
+      const float gh = dk.hi[e] * cs[e] - dk.lo[e] * sn[e];
+      atomicAdd(&s_gk[a.kidx[ir + dl / C] * C + dl % C], gl);
+      atomicAdd(&s_gk[a.kidx[ir + dh / C] * C + dh % C], gh);
+      atomicAdd(&s_gv[a.vidx[ir + dl / C] * C + dl % C], dv.lo[e]);
+      atomicAdd(&s_gv[a.vidx[ir + dh / C] * C + dh % C], dv.hi[e]);
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < a.K * C; e += blockDim.x) {
+    const int r = e / C, i = e - r * C;
+    const int64_t o = cbo + (int64_t)r * a.G + i * a.T_c + m;
+    if (s_gk[e] != 0.f) unsafeAtomicAdd(&a.dkcb[o], s_gk[e]);
+    if (s_gv[e] != 0.f) unsafeAtomicAdd(&a.dvcb[o], s_gv[e]);
+  }
+}
+
+// Query-side backward: dq[b][hq][tl][i] = scale * sum_keys p (dp - delta) k_rot.
+template <int C>
+__global__ __launch_bounds__(256) void prefill_bwd_q_kernel(PrefillArgs a) {
+  extern __shared__ float s_cb[];
+  __shared__ __attribute__((aligned(16))) float s_k[kTile][kLds];
+  __shared__ __attribute__((aligned(16))) float s_v[kTile][kLds];
+  const int row = threadIdx.x >> 2, sub = threadIdx.x & 3;
+  const int hq = blockIdx.y, h = hq / a.gqa;
+  const int b = blockIdx.z / a.n_steps, tl = blockIdx.z - b * a.n_steps;
+  const int t = a.step0 + tl, beta = t / a.T_c, m = t - beta * a.T_c;
+  const int q0 = blockIdx.x * kRows;
+  const int i = q0 + row;
+  const bool vq = i < a.N;
+  float* s_cbk = s_cb;
+  float* s_cbv = s_cb + 256 * C;
+  stage_codebooks<C>(a, h, beta, m, s_cbk, s_cbv);
+
+  const int64_t qr = (((int64_t)b * a.Hq + hq) * a.n_steps + tl) * a.N + (vq ? i : 0);
+  Row32 q, dov, dq;
+  load_row(q, a.q + qr * kPD, sub, a.scale * kLog2e);
+  load_row(dov, a.dout + qr * kPD, sub, 1.f);
+  zero_row(dq);
+  const float l2 = a.lse[qr] * kLog2e, dl = a.delta[qr];
+
+  auto consume = [&](int cnt, int jbase, bool causal) {
+    for (int kk = 0; kk < cnt; ++kk) {
+      const float s = quad_sum(dot_lds(q, s_k[kk], sub));
+      const float dp = quad_sum(dot_lds(dov, s_v[kk], sub));
+      if (!vq || (causal && jbase + kk > i)) continue;
+      const float p = __builtin_amdgcn_exp2f(s - l2);
+      axpy_lds(dq, p * (dp - dl), s_k[kk], sub);
+    }
+  };
+  for (int j0 = 0; j0 < a.n_s; j0 += kTile) {
+    const int cnt = min(kTile, a.n_s - j0);
+    __syncthreads();
+    fill_tile<C>(a, b, h, t, beta, true, j0, cnt, s_cbk, s_cbv, s_k, s_v);
+    __syncthreads();
+    consume(cnt, 0, false);
+  }
+  const int jend = min(a.N, q0 + kRows);
+  for (int j0 = 0; j0 < jend; j0 += kTile) {
+    const int cnt = min(kTile, jend - j0);
+    __syncthreads();
+    fill_tile<C>(a, b, h, t, beta, false, j0, cnt, s_cbk, s_cbv, s_k, s_v);
+    __syncthreads();
+    consume(cnt, j0, true);
+  }
+  if (vq) store_row(dq, a.dq + qr * kPD, sub, a.scale);
+}
+
+hipError_t launch_fill_f32(float* p, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(prefill_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_table_f32(float* tab, int n_pos, int D, double theta, hipStream_t s) {
+  const int64_t n = (int64_t)n_pos * (D / 2);
+  hipLaunchKernelGGL(rope_table_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, tab, n_pos, D, theta);
+  return hipGetLastError();
+}
+
+template <int C>
+static hipError_t prefill_launch(const PrefillArgs& a, bool backward, hipStream_t s) {
+  const dim3 grid((a.N + kRows - 1) / kRows, a.Hq, a.B * a.n_steps);
+  const size_t lds = (size_t)2 * 256 * C * sizeof(float);
+  // dynamic LDS beyond the default allowance (C = 32 takes 64 KiB)
+  for (const void* k : {reinterpret_cast<const void*>(&prefill_fwd_kernel<C>),
+                        reinterpret_cast<const void*>(&prefill_bwd_kv_kernel<C>),
+                        reinterpret_cast<const void*>(&prefill_bwd_q_kernel<C>)}) {
+    const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  if (!backward) {
+    hipLaunchKernelGGL((prefill_fwd_kernel<C>), grid, dim3(256), lds, s, a);
+    return hipGetLastError();
+  }
+  const int64_t rows = (int64_t)a.B * a.Hq * a.n_steps * a.N;
+  hipLaunchKernelGGL(prefill_delta_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, a.out, a.dout,
+                     a.delta, rows);
+  const int64_t ncb = (int64_t)a.H * a.n_blk * a.K * a.G;
+  hipLaunchKernelGGL(prefill_zero_kernel, dim3((unsigned)((ncb + 255) / 256)), dim3(256), 0, s, a.dkcb, ncb);
+  hipLaunchKernelGGL(prefill_zero_kernel, dim3((unsigned)((ncb + 255) / 256)), dim3(256), 0, s, a.dvcb, ncb);
+  hipLaunchKernelGGL((prefill_bwd_kv_kernel<C>), grid, dim3(256), lds, s, a);
+  hipLaunchKernelGGL((prefill_bwd_q_kernel<C>), grid, dim3(256), lds, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill(const PrefillArgs& a, int C, bool backward, hipStream_t s) {
+  switch (C) {
+    case 2: return prefill_launch<2>(a, backward, s);
+    case 4: return prefill_launch<4>(a, backward, s);
+    case 8: return prefill_launch<8>(a, backward, s);
+    case 16: return prefill_launch<16>(a, backward, s);
+    case 32: return prefill_launch<32>(a, backward, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace loopvq

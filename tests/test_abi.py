@@ -18,7 +18,7 @@ def _lib():
 def _header_functions():
     src = open(os.path.join(ROOT, "include", "loopvq.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(loopvq_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(loopvq_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_exports_match_header():
@@ -27,7 +27,7 @@ def test_exports_match_header():
     assert set(names) == set(L.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.loopvq_abi_version() == 3
+    assert lib.loopvq_abi_version() == 4
 
 
 def _geom(L, **kw):
@@ -140,3 +140,44 @@ def test_kmeans_entry_points_reject_bad_arguments():
     assert lib.loopvq_kmeans_finalize(ctypes.byref(g), None, P16, P16, None) == -1
     bad = lv.geom(128, 4, 4, 24, 256, 1, 1)
     assert lib.loopvq_kmeans_finalize(ctypes.byref(bad), P16, P16, P16, None) != 0
+
+
+def test_prefill_entry_points_reject_bad_arguments():
+    import sub_bit_loop_amd as lv
+    _, lib = _lib()
+    g = lv.geom(128, 4, 4, 16, 256, 2, 4)
+    P = ctypes.c_void_p
+    A = P(256)                 # stands in for an aligned device pointer; never dereferenced
+    U = P(258)                 # misaligned
+    # prefill_attn(g, q, step0, n_steps, B, N, kidx, vidx, N_cap, kcb, vcb, sk, sv, n_s, rope, n_pos, out, lse, s)
+    ok = [A, 0, 4, 1, 8, A, A, 8, A, A, A, A, 4, A, 12, A, A, None]
+
+    def fwd(**ch):
+        args = list(ok)
+        names = ["q", "step0", "n_steps", "B", "N", "kidx", "vidx", "N_cap", "kcb", "vcb", "sk", "sv", "n_s",
+                 "rope", "n_pos", "out", "lse", "s"]
+        for k, v in ch.items():
+            args[names.index(k)] = v
+        return lib.loopvq_prefill_attn(ctypes.byref(g), *args)
+    assert fwd(q=None) == -1
+    assert fwd(N=9) == -1                  # N > N_cap
+    assert fwd(n_pos=11) == -1             # rope table shorter than n_s + N
+    assert fwd(step0=1) == -1              # step range beyond T
+    assert fwd(sk=None) == -1              # n_s > 0 without sinks
+    assert fwd(q=U) == -1                  # misaligned
+    assert fwd(lse=None) == -1
+    assert fwd(N=0) == 0                   # nothing to attend: no launch
+    assert fwd(n_s=-1) == -1
+    bad = lv.geom(128, 4, 4, 24, 256, 2, 4)
+    assert lib.loopvq_prefill_attn(ctypes.byref(bad), *ok) != 0
+    size = ctypes.c_size_t(0)
+    assert lib.loopvq_prefill_attn_backward_workspace(ctypes.byref(g), 2, 8, 0, 4, ctypes.byref(size)) == 0
+    assert size.value == 2 * 4 * 4 * 8 * 4
+    # backward: short workspace and NULL gradients are refused before any launch
+    bargs = [A, 0, 4, 1, 8, A, A, 8, A, A, A, A, 4, A, 12, A, A, A, A, A, A, A, 16, None]
+    assert lib.loopvq_prefill_attn_backward(ctypes.byref(g), *bargs) == -4
+    bargs[22] = 1 * 4 * 4 * 8 * 4
+    bargs[19] = None
+    assert lib.loopvq_prefill_attn_backward(ctypes.byref(g), *bargs) == -1
+    assert lib.loopvq_rope_table_f32(1e4, 7, 4, A, None) == -1
+    assert lib.loopvq_rope_table_f32(1e4, 128, 0, A, None) == -1
