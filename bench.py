@@ -16,6 +16,10 @@ oracle's rate on a bounded sample are attached.
 `--config 5` instead runs the 24-layer workload as one flow (prefill encode of
 every layer, then 256 decode calls over all layers with an 8-token page
 encoded per layer every 8 calls) and prints its own JSON line.
+
+`--finetune` times the codebook fine-tuning workload (causal attention over
+the compressed cache and its backward into the codebooks, plus whole Adam
+iterations on the toy looped stack) and prints its own JSON line.
 """
 import argparse
 import hashlib
@@ -95,7 +99,7 @@ def cpu_baseline(cfg, inp, n_tok, n_b):
                          f(inp["v_cb"][h]), f(inp["sink_k"][b, h]), f(inp["sink_v"][b, h]),
                          f(inp["q"][b, hq]), cfg.T_c, cfg.theta))
     cores = len(os.sched_getaffinity(0))
-    workers = max(1, min(cores, len(jobs), 16))
+    workers = max(1, min(cores, len(jobs), 15))      # with the parent, at most 16 processes
     t0 = time.perf_counter()
     with ProcessPoolExecutor(max_workers=workers, mp_context=mp.get_context("spawn")) as ex:
         res = list(ex.map(_oracle_head, jobs))
@@ -281,6 +285,154 @@ def workload5(args, torch, lv, cfg):
     print(json.dumps(res), flush=True)
 
 
+# ----------------------------------------------------------------------------- fine-tuning workload
+
+FP32_VECTOR_PEAK_TFLOPS = 157.3    # published; packed-FP32 FMA (2 per lane per clock)
+
+
+def _oracle_vjp_sample(args):
+    import torch as _t
+    from threadpoolctl import threadpool_limits
+    import oracle as ref
+    q, ki, vi, kc, vc, sk, sv, T_c, dout, theta = args
+    with threadpool_limits(1):
+        _t.set_num_threads(1)
+        t0 = time.perf_counter()
+        ref.attention_vjp(q, ki, vi, kc, vc, sk, sv, T_c, dout, 0, theta)
+        return time.perf_counter() - t0
+
+
+def finetune_flow(args, torch, lv):
+    """Loop-aware codebook fine-tuning (review section 3.2): one calibration
+    sequence per iteration, the toy looped stack over the compressed cache of
+    the 0.5-bit slice's geometry.  Times the compressed-attention forward and
+    backward calls and whole iterations (re-encode, stack forward, KL,
+    backward, Adam).  Prints one JSON line."""
+    from synth import build_inputs, config_by_index, gen_toy_stack
+    from dataclasses import replace
+    from sub_bit_loop_amd import finetune as ft
+    N, vocab = args.ft_tokens, 4096
+    cfg = replace(config_by_index(2), B=1, N=N)
+    inp = build_inputs(cfg, 0, "cuda")
+    g = lv.geom(cfg.D, cfg.T, cfg.T_c, cfg.G, cfg.K, cfg.H_kv, cfg.H_q, cfg.theta)
+    shp = (1, cfg.H_kv, cfg.n_blk, N, cfg.chunks)
+    kidx = torch.empty(shp, dtype=torch.uint8, device="cuda")
+    vidx = torch.empty(shp, dtype=torch.uint8, device="cuda")
+    lv.encode(g, inp["k"], inp["k_cb"], kidx)
+    lv.encode(g, inp["v"], inp["v_cb"], vidx)
+    rope = lv.rope_table_f32(cfg.n_s + N, cfg.D, cfg.theta)
+    gq = torch.Generator(device="cuda").manual_seed(5)
+    q = torch.randn((1, cfg.H_q, cfg.T, N, cfg.D), generator=gq, device="cuda")
+    dout = torch.randn((1, cfg.H_q, cfg.T, N, cfg.D), generator=gq, device="cuda")
+    out = torch.empty_like(q)
+    lse = torch.empty((1, cfg.H_q, cfg.T, N), device="cuda")
+    dq = torch.empty_like(q)
+    dk = torch.empty(inp["k_cb"].shape, device="cuda")
+    dv = torch.empty_like(dk)
+    ws = torch.empty(cfg.H_q * cfg.T * N * 4, dtype=torch.uint8, device="cuda")
+    sk, sv = inp["sink_k"], inp["sink_v"]
+
+    def fwd():
+        lv.prefill_attn(g, q, kidx, vidx, inp["k_cb"], inp["v_cb"], sk, sv, rope, out=out, lse=lse)
+
+    def bwd():
+        lv.prefill_attn_backward(g, q, kidx, vidx, inp["k_cb"], inp["v_cb"], sk, sv, rope, out, lse, dout,
+                                 d_q=dq, d_k_cb=dk, d_v_cb=dv, workspace=ws)
+
+    def timed(fn, reps):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    fwd_ms = timed(fwd, args.steps)
+    bwd_ms = timed(bwd, args.steps)
+    pairs = cfg.H_q * cfg.T * (N * (N + 1) // 2 + N * cfg.n_s)      # (query, key) pairs of one call
+    D = cfg.D
+    fwd_tf = pairs * 4 * D / (fwd_ms * 1e-3) / 1e12
+    bwd_tf = pairs * 8 * D / (bwd_ms * 1e-3) / 1e12
+
+    if bwd_ms >= fwd_ms:
+        dom_name, dom_tf, dom_ms, dom_flop = ("loopvq_prefill_attn_backward (prefill_bwd_kv_kernel + "
+                                              "prefill_bwd_q_kernel + delta)", bwd_tf, bwd_ms, pairs * 8 * D)
+    else:
+        dom_name, dom_tf, dom_ms, dom_flop = "loopvq_prefill_attn (prefill_fwd_kernel)", fwd_tf, fwd_ms, pairs * 4 * D
+
+    toy = gen_toy_stack(cfg, 0, "cuda", vocab=vocab, B=1)
+    stack = ft.ToyLoopedStack(toy["Wq"], toy["Wo"], toy["Wu"], cfg.H_q, cfg.D, cfg.T, cfg.n_s, rope)
+    iters = max(2, args.steps // 2)
+    ft.finetune_codebooks(stack, g, toy["x"], inp["k"], inp["v"], sk, sv, inp["k_cb"], inp["v_cb"], iters=1)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    _, _, Js = ft.finetune_codebooks(stack, g, toy["x"], inp["k"], inp["v"], sk, sv, inp["k_cb"], inp["v_cb"],
+                                     iters=iters)
+    b.record()
+    torch.cuda.synchronize()
+    it_ms = a.elapsed_time(b) / iters
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        # oracle forward + backward (fp64 autograd) of every q-head and loop
+        # step over the first n tokens, one process per q-head
+        from concurrent.futures import ProcessPoolExecutor
+        import multiprocessing as mp
+        n = min(N, args.ft_cpu_tokens)
+        f64 = lambda t: t.detach().cpu().double()
+        jobs = [(f64(q[:, h:h + 1, :, :n]), kidx[:, h:h + 1, :, :n].long().cpu(),
+                 vidx[:, h:h + 1, :, :n].long().cpu(), f64(inp["k_cb"][h:h + 1]), f64(inp["v_cb"][h:h + 1]),
+                 f64(sk[:, h:h + 1]), f64(sv[:, h:h + 1]), cfg.T_c, f64(dout[:, h:h + 1, :, :n]), cfg.theta)
+                for h in range(cfg.H_q)]
+        # each worker imports torch, which opens the GPU device: stay well inside
+        # the per-GPU process limit
+        workers = max(1, min(len(os.sched_getaffinity(0)), len(jobs), 8))
+        t0 = time.perf_counter()
+        with ProcessPoolExecutor(max_workers=workers, mp_context=mp.get_context("spawn")) as ex:
+            list(ex.map(_oracle_vjp_sample, jobs))
+        wall = time.perf_counter() - t0
+        sp = cfg.H_q * cfg.T * (n * (n + 1) // 2 + n * cfg.n_s)
+        cpu = {"value": sp / wall, "unit": "attention (query, key) pairs/s, forward + backward", "cores": workers,
+               "kind": "oracle",
+               "sample": "all %d q-heads and %d loop steps, first %d tokens + %d sinks: fp64 torch causal attention "
+                         "over the rebuilt cache and its autograd backward (%d pairs); one process per q-head, %d "
+                         "at a time, 1 thread each; wall %.1f s" % (cfg.H_q, cfg.T, n, cfg.n_s, sp, workers, wall)}
+    workload = ("codebook fine-tuning (section 3.2): one calibration sequence per iteration, %d kv-heads / %d "
+                "q-heads, D=%d, T=T_c=%d, G=%d, K=%d, %d tokens + %d sinks; toy looped stack d=%d, vocab %d"
+                % (cfg.H_kv, cfg.H_q, cfg.D, cfg.T, cfg.G, cfg.K, N, cfg.n_s, cfg.H_q * cfg.D, vocab))
+    res = {
+        "metric": "codebook fine-tuning: compressed-attention forward + backward (query, key) pairs/s",
+        "value": pairs / ((fwd_ms + bwd_ms) * 1e-3),
+        "unit": "attention (query, key) pairs/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": fwd_ms + bwd_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": workload, "global_batch": 1, "seq_len": N + cfg.n_s,
+                   "step": "loopvq_prefill_attn + loopvq_prefill_attn_backward over every loop step"},
+        "forward": {"ms_per_call": fwd_ms, "tflops": fwd_tf, "flop_per_pair": 4 * D},
+        "backward": {"ms_per_call": bwd_ms, "tflops": bwd_tf, "flop_per_pair": 8 * D},
+        "roofline": {"kernel": dom_name, "bound": "alu", "achieved": dom_tf, "peak": FP32_VECTOR_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": dom_tf / FP32_VECTOR_PEAK_TFLOPS, "traffic": None,
+                     "algorithmic_flop_per_launch": dom_flop, "avg_launch_ms": dom_ms},
+        "iteration": {"ms": it_ms, "objective": Js,
+                      "note": "re-encode K and V, toy stack forward over the rebuilt cache (4 compressed-attention "
+                              "calls), KL against the precise run, backward, Adam (lr 1e-3)"},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
 # ----------------------------------------------------------------------------- GPU leg
 
 def main():
@@ -293,6 +445,10 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=8192, help="context tokens in the oracle sample")
     ap.add_argument("--cpu-batch", type=int, default=2, help="batch entries in the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--finetune", action="store_true",
+                    help="time the codebook fine-tuning workload (compressed-attention forward + backward)")
+    ap.add_argument("--ft-tokens", type=int, default=2048, help="tokens of the fine-tuning sequence")
+    ap.add_argument("--ft-cpu-tokens", type=int, default=1536, help="tokens in the fine-tuning oracle sample")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the LoopVQ path has no multi-GPU step in this build "
@@ -308,8 +464,11 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     lv.lib()
-    cfg = config_by_index(args.config)
     torch.cuda.set_device(0)
+    if args.finetune:
+        finetune_flow(args, torch, lv)
+        return
+    cfg = config_by_index(args.config)
     if cfg.layers != 1:
         workload5(args, torch, lv, cfg)
         return

@@ -10,4 +10,16 @@ Every function is the plain definition from the LoopVQ review (arXiv
 from .loopvq_ref import *  # noqa: F401,F403
 from .tasq_perm import *  # noqa: F401,F403,E402
 from .kmeans_ref import *  # noqa: F401,F403,E402
-from .finetune_ref import *  # noqa: F401,F403,E402
+
+
+def __getattr__(name):
+    # the fine-tuning reference needs torch; it is loaded on first use so that
+    # processes that only encode and decode never import torch
+    import importlib
+    if name.startswith("__"):
+        raise AttributeError(name)
+    mod = importlib.import_module(__name__ + ".finetune_ref")
+    try:
+        return getattr(mod, name)
+    except AttributeError:
+        raise AttributeError("module 'oracle' has no attribute %r" % name) from None

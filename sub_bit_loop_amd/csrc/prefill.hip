@@ -32,11 +32,11 @@ constexpr int kRows = 64;             // rows per workgroup (queries or keys)
 constexpr int kTile = 32;             // keys (or queries) staged per LDS tile
 constexpr int kLds = kPD + 4;         // padded LDS row
 
-__device__ __forceinline__ float quad_sum(float v) {
-  v += __shfl_xor(v, 1);
-  v += __shfl_xor(v, 2);
-  return v;
-}
+__device__ __forceinline__ float quad_sum(float v) { return group_sum<4>(v); }
+
+// Keeps the compiler from holding LDS rows in registers across it (they are
+// read again instead), which bounds register use in the backward loops.
+__device__ __forceinline__ void lds_reload() { asm volatile("" ::: "memory"); }
 
 // Stage step m's slice of the K and V codebooks of (kv-head h, block beta)
 // as fp32 [K][C].
@@ -209,7 +209,8 @@ __global__ __launch_bounds__(256) void prefill_fwd_kernel(PrefillArgs a) {
   const int hq = blockIdx.y, h = hq / a.gqa;
   const int b = blockIdx.z / a.n_steps, tl = blockIdx.z - b * a.n_steps;
   const int t = a.step0 + tl, beta = t / a.T_c, m = t - beta * a.T_c;
-  const int q0 = blockIdx.x * kRows;
+  // the last query tiles attend the most tokens: dispatch them first
+  const int q0 = (gridDim.x - 1 - blockIdx.x) * kRows;
   const int i = q0 + row;
   const bool vq = i < a.N;
   float* s_cbk = s_cb;
@@ -301,30 +302,36 @@ __global__ __launch_bounds__(256) void prefill_bwd_kv_kernel(PrefillArgs a) {
   for (int e = threadIdx.x; e < 2 * 256 * C; e += blockDim.x) s_gd[e] = 0.f;
   __syncthreads();
 
-  // this lane's key (rotated) and value channels, straight from the codebooks
+  // this lane's key (rotated) and value channels, straight from the codebooks;
+  // the index bytes of its channels are kept (NB per half) for the scatter
+  constexpr int NB = C >= 16 ? 1 : 16 / C;
   const int64_t ir = ((((int64_t)b * a.H + h) * a.n_blk + beta) * a.N_cap + (vk ? j : 0)) * (kPD / C);
   const int64_t cbo = ((int64_t)h * a.n_blk + beta) * a.K * a.G;
-  Row32 kr, vv, dk, dv;
-  float cs[16], sn[16];
-  {
-    const int pos = a.n_s + (vk ? j : 0);
-    const float2* rp = reinterpret_cast<const float2*>(a.rope + ((int64_t)pos * kPH + 16 * sub) * 2);
+  const int pos = a.n_s + (vk ? j : 0);
+  const float2* rp = reinterpret_cast<const float2*>(a.rope + ((int64_t)pos * kPH + 16 * sub) * 2);
+  int ikl[NB], ikh[NB], ivl[NB], ivh[NB];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int dl = 16 * sub + e, dh = kPH + dl;
-      // an index byte >= K (never written by the encode) reads the last entry
-      const int rkl = min((int)a.kidx[ir + dl / C], a.K - 1), rkh = min((int)a.kidx[ir + dh / C], a.K - 1);
-      const int rvl = min((int)a.vidx[ir + dl / C], a.K - 1), rvh = min((int)a.vidx[ir + dh / C], a.K - 1);
-      const float xl = bf16_to_f32(a.kcb[cbo + (int64_t)rkl * a.G + (dl % C) * a.T_c + m]);
-      const float xh = bf16_to_f32(a.kcb[cbo + (int64_t)rkh * a.G + (dh % C) * a.T_c + m]);
-      vv.lo[e] = bf16_to_f32(a.vcb[cbo + (int64_t)rvl * a.G + (dl % C) * a.T_c + m]);
-      vv.hi[e] = bf16_to_f32(a.vcb[cbo + (int64_t)rvh * a.G + (dh % C) * a.T_c + m]);
-      const float2 w = rp[e];
-      cs[e] = w.x;
-      sn[e] = w.y;
-      kr.lo[e] = xl * w.x - xh * w.y;
-      kr.hi[e] = xh * w.x + xl * w.y;
-    }
+  for (int u = 0; u < NB; ++u) {
+    const int cl = (16 * sub) / C + u, ch = (kPH + 16 * sub) / C + u;
+    ikl[u] = a.kidx[ir + cl];
+    ikh[u] = a.kidx[ir + ch];
+    ivl[u] = a.vidx[ir + cl];
+    ivh[u] = a.vidx[ir + ch];
+  }
+  Row32 kr, vv, dk, dv;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int u = e / C < NB ? e / C : NB - 1, i = (16 * sub + e) % C;
+    // an index byte >= K (never written by the encode) reads the last entry
+    const int rkl = min(ikl[u], a.K - 1), rkh = min(ikh[u], a.K - 1);
+    const int rvl = min(ivl[u], a.K - 1), rvh = min(ivh[u], a.K - 1);
+    const float xl = bf16_to_f32(a.kcb[cbo + (int64_t)rkl * a.G + i * a.T_c + m]);
+    const float xh = bf16_to_f32(a.kcb[cbo + (int64_t)rkh * a.G + i * a.T_c + m]);
+    vv.lo[e] = bf16_to_f32(a.vcb[cbo + (int64_t)rvl * a.G + i * a.T_c + m]);
+    vv.hi[e] = bf16_to_f32(a.vcb[cbo + (int64_t)rvh * a.G + i * a.T_c + m]);
+    const float2 w = rp[e];
+    kr.lo[e] = xl * w.x - xh * w.y;
+    kr.hi[e] = xh * w.x + xl * w.y;
   }
   zero_row(dk);
   zero_row(dv);
@@ -354,28 +361,32 @@ __global__ __launch_bounds__(256) void prefill_bwd_kv_kernel(PrefillArgs a) {
       }
     }
     __syncthreads();
+#pragma unroll 1
     for (int qq = 0; qq < cnt; ++qq) {
       const int i = i0 + qq;
       const float s = quad_sum(dot_lds(kr, s_q[qq], sub));
       const float dp = quad_sum(dot_lds(vv, s_do[qq], sub));
-      if (!vk || j > i) continue;
-      const float p = __builtin_amdgcn_exp2f(s - s_l2[qq]);
+      // masked pairs contribute zero (no branch: the accumulators stay in place)
+      const float p = (vk && j <= i) ? __builtin_amdgcn_exp2f(s - s_l2[qq]) : 0.f;
+      lds_reload();
       axpy_lds(dv, p, s_do[qq], sub);
       // d score / d rotated key = scale * q; s_q holds scale * log2(e) * q
       axpy_lds(dk, p * (dp - s_dl[qq]) * kLn2, s_q[qq], sub);
     }
   }
-  // undo the rotation and scatter into the codeword entries
+  // undo the rotation (the table is read again) and scatter into the
+  // codeword entries
   if (vk) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const int dl = 16 * sub + e, dh = kPH + dl;
-      const float gl = dk.lo[e] * cs[e] + dk.hi[e] * sn[e];
-      const float gh = dk.hi[e] * cs[e] - dk.lo[e] * sn[e];
-      atomicAdd(&s_gk[a.kidx[ir + dl / C] * C + dl % C], gl);
-      atomicAdd(&s_gk[a.kidx[ir + dh / C] * C + dh % C], gh);
-      atomicAdd(&s_gv[a.vidx[ir + dl / C] * C + dl % C], dv.lo[e]);
-      atomicAdd(&s_gv[a.vidx[ir + dh / C] * C + dh % C], dv.hi[e]);
+      const int u = e / C < NB ? e / C : NB - 1, i = (16 * sub + e) % C;
+      const float2 w = rp[e];
+      const float gl = dk.lo[e] * w.x + dk.hi[e] * w.y;
+      const float gh = dk.hi[e] * w.x - dk.lo[e] * w.y;
+      atomicAdd(&s_gk[ikl[u] * C + i], gl);
+      atomicAdd(&s_gk[ikh[u] * C + i], gh);
+      atomicAdd(&s_gv[ivl[u] * C + i], dv.lo[e]);
+      atomicAdd(&s_gv[ivh[u] * C + i], dv.hi[e]);
     }
   }
   __syncthreads();
@@ -397,7 +408,8 @@ __global__ __launch_bounds__(256) void prefill_bwd_q_kernel(PrefillArgs a) {
   const int hq = blockIdx.y, h = hq / a.gqa;
   const int b = blockIdx.z / a.n_steps, tl = blockIdx.z - b * a.n_steps;
   const int t = a.step0 + tl, beta = t / a.T_c, m = t - beta * a.T_c;
-  const int q0 = blockIdx.x * kRows;
+  // the last query tiles attend the most tokens: dispatch them first
+  const int q0 = (gridDim.x - 1 - blockIdx.x) * kRows;
   const int i = q0 + row;
   const bool vq = i < a.N;
   float* s_cbk = s_cb;
@@ -415,8 +427,9 @@ __global__ __launch_bounds__(256) void prefill_bwd_q_kernel(PrefillArgs a) {
     for (int kk = 0; kk < cnt; ++kk) {
       const float s = quad_sum(dot_lds(q, s_k[kk], sub));
       const float dp = quad_sum(dot_lds(dov, s_v[kk], sub));
-      if (!vq || (causal && jbase + kk > i)) continue;
-      const float p = __builtin_amdgcn_exp2f(s - l2);
+      const bool on = vq && !(causal && jbase + kk > i);
+      const float p = on ? __builtin_amdgcn_exp2f(s - l2) : 0.f;
+      lds_reload();
       axpy_lds(dq, p * (dp - dl), s_k[kk], sub);
     }
   };
