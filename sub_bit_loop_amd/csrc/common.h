@@ -56,6 +56,18 @@ __device__ __forceinline__ uint16_t f64_to_f16_rne(double v) {
   return (uint16_t)(best | sign);
 }
 
+// lo += low fp16 half of w, hi += high half, each with one v_dot2_f32_f16
+// against (1, 0) / (0, 1): the fp16 value is widened exactly and the sum is
+// rounded once, as a convert-then-add would do, in half the instructions.
+// w must hold finite values.
+__device__ __forceinline__ void add_f16x2(uint32_t w, float& lo, float& hi) {
+  typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+  const f16x2_t v = __builtin_bit_cast(f16x2_t, w);
+  const f16x2_t e0 = {(_Float16)1.f, (_Float16)0.f}, e1 = {(_Float16)0.f, (_Float16)1.f};
+  lo = __builtin_amdgcn_fdot2(v, e0, lo, false);
+  hi = __builtin_amdgcn_fdot2(v, e1, hi, false);
+}
+
 // DPP all-reduce sum over aligned groups of L lanes (L in {1,2,4,8,16}).
 // quad_perm [1,0,3,2] = 0xB1, [2,3,0,1] = 0x4E, row_half_mirror = 0x141,
 // row_mirror = 0x140: each pairs every lane with a partner inside the group,

@@ -220,9 +220,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_fast_kernel(DecodeArgs 
         for (int p = 0; p < 2; ++p)
 #pragma unroll
           for (int ip = 0; ip < DW; ++ip) {
-            const h2_t v = as_h2(acc16[ml][k][p][ip]);
-            acc[ml][k][p][2 * ip] += (float)v.x;
-            acc[ml][k][p][2 * ip + 1] += (float)v.y;
+            add_f16x2(acc16[ml][k][p][ip], acc[ml][k][p][2 * ip], acc[ml][k][p][2 * ip + 1]);
             acc16[ml][k][p][ip] = 0u;
           }
   };
@@ -596,9 +594,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(DecodeArgs 
         for (int p = 0; p < 2; ++p)
 #pragma unroll
           for (int ip = 0; ip < DW; ++ip) {
-            const h2_t v = as_h2(acc16[hh][k][p][ip]);
-            acc[hh][k][p][2 * ip] += (float)v.x;
-            acc[hh][k][p][2 * ip + 1] += (float)v.y;
+            add_f16x2(acc16[hh][k][p][ip], acc[hh][k][p][2 * ip], acc[hh][k][p][2 * ip + 1]);
             acc16[hh][k][p][ip] = 0u;
           }
   };

@@ -296,9 +296,7 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
     for (int hh = 0; hh < 4; ++hh)
 #pragma unroll
       for (int ip = 0; ip < 4; ++ip) {
-        const h2g_t v = as_h2g(acc16[hh][ip]);
-        acc[hh][2 * ip] += (float)v.x;
-        acc[hh][2 * ip + 1] += (float)v.y;
+        add_f16x2(acc16[hh][ip], acc[hh][2 * ip], acc[hh][2 * ip + 1]);
         acc16[hh][ip] = 0u;
       }
   };

@@ -253,9 +253,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_tasq_kernel(DecodeArgs 
     for (int ml = 0; ml < 2; ++ml)
 #pragma unroll
       for (int p = 0; p < NPR; ++p) {
-        const h2t_t v = as_h2t(acc16[ml][p]);
-        acc[ml][2 * p] += (float)v.x;
-        acc[ml][2 * p + 1] += (float)v.y;
+        add_f16x2(acc16[ml][p], acc[ml][2 * p], acc[ml][2 * p + 1]);
         acc16[ml][p] = 0u;
       }
   };
