@@ -38,11 +38,12 @@ UNIT = "context tokens/s per loop block"
 
 # Sources whose change invalidates a kernel's committed HBM-traffic figure.
 # The figure is taken on the default workload (one q-head per kv-head, so the
-# decode call runs decode_fast.hip's kernels and decode.hip's merge); the plan
+# decode call runs decode_half.hip's kernel and decode.hip's merge); the plan
 # in loopvq_api.cpp decides that, so it is part of the key too.
 KERNEL_SOURCES = {
     "encode": ("encode.hip", "common.h", "kernels.h", "loopvq_api.cpp", "calib.hip"),
-    "decode": ("decode.hip", "decode_fast.hip", "common.h", "kernels.h", "loopvq_api.cpp", "calib.hip"),
+    "decode": ("decode.hip", "decode_fast.hip", "decode_half.hip", "common.h", "kernels.h", "loopvq_api.cpp",
+               "calib.hip"),
 }
 
 

@@ -1,6 +1,7 @@
 // LoopVQ fused decode attention, specialised for blocks of T_c = 4 loop steps
-// with c = 4 (G = 16, 0.5 bit) or c = 8 (G = 32, 0.25 bit) channels per step
-// per code, D = 128, no channel pre-transform.
+// with c = 8 (G = 32, 0.25 bit) channels per step per code, D = 128, no
+// channel pre-transform (c = 4 has its own layout in decode_half.hip; the
+// kernel template below still covers it), and the single-step variant.
 //
 // LoopVQ review (arXiv 2611.05304), section 3.4 step 3 (codebook on chip,
 // lookup by index, RoPE from a precomputed table after dequant, Flash-
@@ -802,7 +803,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(DecodeArgs 
 hipError_t launch_decode_fast(int G, const DecodeArgs& a, hipStream_t s) {
   dim3 grid(a.n_split, a.Hq, a.B * a.n_blk_serv);
   if (G == 16)
-    hipLaunchKernelGGL(decode_fast_kernel<4>, grid, dim3(kDecodeThreads), 0, s, a);
+    return launch_decode_half(a, s);   // one-instruction index decode (decode_half.hip)
   else if (G == 32)
     hipLaunchKernelGGL(decode_fast_kernel<8>, grid, dim3(kDecodeThreads), 0, s, a);
   else

@@ -129,6 +129,8 @@ constexpr int kDecodeThreads = 256;
 constexpr int kEncodeThreads = 256;
 constexpr int kEncodeTokens = 128;  // tokens per encode workgroup
 
+// fused decode for G = 16, T_c = 4 (c = 4), D = 128, plain keys
+hipError_t launch_decode_half(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_fill_f32(float* p, int64_t n, hipStream_t s);   // p[0..n) = 0
 hipError_t launch_rope_table_f32(float* tab, int n_pos, int D, double theta, hipStream_t s);
 // forward (out, lse) or backward (delta, zeroed then accumulated codebook
