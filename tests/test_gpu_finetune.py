@@ -167,3 +167,36 @@ def test_finetune_loop_lowers_objective():
     _say("  J: %s" % " ".join("%.4g" % j for j in Js))
     assert all(math.isfinite(j) for j in Js)
     assert Js[-1] < Js[0]
+
+
+def test_prefill_full_size_sampled():
+    # the fine-tuning workload bench.py times (16 kv-heads / 16 q-heads, 2048
+    # tokens + 4 sinks, 4 steps in one call); the oracle recomputes two q-heads
+    # (every step and query) and, since MHA gives each kv-head one q-head, the
+    # complete codebook gradients of kv-head 5
+    from dataclasses import replace
+    from synth import config_by_index
+    cfg = replace(config_by_index(2), B=1, N=2048)
+    _say("prefill attention at full size: B=1 H=16 N=2048 T=4")
+    g, inp, kidx, vidx, rope = _setup(cfg)
+    gq = torch.Generator(device="cuda").manual_seed(5)
+    q = torch.randn((1, cfg.H_q, cfg.T, cfg.N, cfg.D), generator=gq, device="cuda")
+    dout = torch.randn((1, cfg.H_q, cfg.T, cfg.N, cfg.D), generator=gq, device="cuda")
+    out, lse = lv.prefill_attn(g, q, kidx, vidx, inp["k_cb"], inp["v_cb"], inp["sink_k"], inp["sink_v"], rope)
+    dq, dk, dv = lv.prefill_attn_backward(g, q, kidx, vidx, inp["k_cb"], inp["v_cb"], inp["sink_k"],
+                                          inp["sink_v"], rope, out, lse, dout)
+    torch.cuda.synchronize()
+    for h in (5, 15):
+        sl = slice(h, h + 1)
+        o_r, l_r, dq_r, dk_r, dv_r = ref.attention_vjp(
+            q[:, sl].double().cpu(), kidx[:, sl, :, :cfg.N].long().cpu(), vidx[:, sl, :, :cfg.N].long().cpu(),
+            inp["k_cb"][sl].double().cpu(), inp["v_cb"][sl].double().cpu(), inp["sink_k"][:, sl].double().cpu(),
+            inp["sink_v"][:, sl].double().cpu(), cfg.T_c, dout[:, sl].double().cpu(), theta=cfg.theta)
+        _row_check(out[:, sl], o_r, 1e-4, "out head %d" % h)
+        dl = float((lse[:, sl].double().cpu() - l_r).abs().max())
+        _say("  lse head %d max err %.3g" % (h, dl))
+        assert dl <= 1e-4
+        _row_check(dq[:, sl], dq_r, 1e-4, "d_q head %d" % h)
+        if h == 5:
+            _tensor_check(dk[sl], dk_r, 1e-4, "d_k_cb kv-head 5")
+            _tensor_check(dv[sl], dv_r, 1e-4, "d_v_cb kv-head 5")
