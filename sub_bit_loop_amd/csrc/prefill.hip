@@ -15,10 +15,11 @@
 // n_s + j).  Everything is fp32; the RoPE table is fp32 (cos, sin) per
 // (position, frequency), computed in fp64.
 //
-// Thread layout (256 threads): a row (a query, or a key in the key-side
-// backward) is served by four lanes; lane `sub` owns the 16 frequencies
-// 16*sub .. 16*sub + 15 and both channels of each RoPE pair (f and f + 64),
-// so rotations stay inside a lane and a dot product is a 4-lane sum.
+// The forward runs on fp32 matrix cores (below).  The backward kernels use the
+// vector units: a row (a key in the key-side backward, a query in the
+// query-side one) is served by four lanes; lane `sub` owns the 16 frequencies
+// 16*sub .. 16*sub + 15 and both channels of each RoPE pair (f and f + 64), so
+// rotations stay inside a lane and a dot product is a 4-lane sum.
 #include "common.h"
 #include "kernels.h"
 
@@ -198,66 +199,202 @@ __global__ __launch_bounds__(256) void rope_table_f32_kernel(float* tab, int n_p
   tab[2 * e + 1] = (float)s;
 }
 
-// Forward: out[b][hq][tl][i] and lse (natural log).  Grid (query tiles of 64,
-// H_q, B * n_steps).
+// Forward on fp32 matrix cores.  Each wave owns 32 queries and computes, per
+// tile of 32 keys, S^T = K_rot Q^T (keys on rows, queries on columns: 64
+// v_mfma_f32_32x32x2f32 over D) and O^T += V^T P^T (16 steps of two keys x 4
+// blocks of 32 channels).  With keys on rows a lane holds 16 of its query's 32
+// scores and its partner lane (lane ^ 32) the other 16, so the softmax needs one
+// exchange, and the probabilities in the score accumulator are already the B
+// operand of the P V product: the key of B row k at step s is the key of
+// accumulator register s in half-wave k.  Keys are staged de-interleaved
+// ([key][(d % 2) * 64 + d / 2]) so a lane's A operands over D are contiguous;
+// values as [key][(d % 32) * 4 + d / 32] so one 16-byte read feeds all four
+// channel blocks.
+typedef float f32x16_pf __attribute__((ext_vector_type(16)));
+constexpr int kMT = 128;              // queries per workgroup (4 waves x 32)
+
 template <int C>
-__global__ __launch_bounds__(256) void prefill_fwd_kernel(PrefillArgs a) {
-  extern __shared__ float s_cb[];                    // [2][K*C] step slices
+__device__ void fill_tile_mfma(const PrefillArgs& a, int b, int h, int t, int beta, bool sinks, int j0, int cnt,
+                               const float* s_cbk, const float* s_cbv, float (*s_k)[kLds], float (*s_v)[kLds]) {
+  const int kk = threadIdx.x >> 3, fs = threadIdx.x & 7;
+  float klo[8], khi[8], vlo[8], vhi[8];
+  if (kk < cnt) {
+    const int j = j0 + kk;
+    int pos;
+    if (sinks) {
+      pos = j;
+      const int64_t ro = ((((int64_t)b * a.H + h) * a.T + t) * a.n_s + j) * kPD;
+      const uint4 xl = *reinterpret_cast<const uint4*>(a.sk + ro + 8 * fs);
+      const uint4 xh = *reinterpret_cast<const uint4*>(a.sk + ro + kPH + 8 * fs);
+      const uint4 yl = *reinterpret_cast<const uint4*>(a.sv + ro + 8 * fs);
+      const uint4 yh = *reinterpret_cast<const uint4*>(a.sv + ro + kPH + 8 * fs);
+      const uint32_t wxl[4] = {xl.x, xl.y, xl.z, xl.w}, wxh[4] = {xh.x, xh.y, xh.z, xh.w};
+      const uint32_t wyl[4] = {yl.x, yl.y, yl.z, yl.w}, wyh[4] = {yh.x, yh.y, yh.z, yh.w};
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        klo[2 * w] = bf16lo(wxl[w]); klo[2 * w + 1] = bf16hi(wxl[w]);
+        khi[2 * w] = bf16lo(wxh[w]); khi[2 * w + 1] = bf16hi(wxh[w]);
+        vlo[2 * w] = bf16lo(wyl[w]); vlo[2 * w + 1] = bf16hi(wyl[w]);
+        vhi[2 * w] = bf16lo(wyh[w]); vhi[2 * w + 1] = bf16hi(wyh[w]);
+      }
+    } else {
+      pos = a.n_s + j;
+      const int64_t ir = ((((int64_t)b * a.H + h) * a.n_blk + beta) * a.N_cap + j) * (kPD / C);
+      const uint8_t* kr = a.kidx + ir;
+      const uint8_t* vr = a.vidx + ir;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int dl = 8 * fs + e, dh = kPH + 8 * fs + e;
+        klo[e] = s_cbk[kr[dl / C] * C + dl % C];
+        khi[e] = s_cbk[kr[dh / C] * C + dh % C];
+        vlo[e] = s_cbv[vr[dl / C] * C + dl % C];
+        vhi[e] = s_cbv[vr[dh / C] * C + dh % C];
+      }
+    }
+    const float4* cs = reinterpret_cast<const float4*>(a.rope + ((int64_t)pos * kPH + 8 * fs) * 2);
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+      const float4 w = cs[e2];
+      const float a0 = klo[2 * e2], b0 = khi[2 * e2], a1 = klo[2 * e2 + 1], b1 = khi[2 * e2 + 1];
+      klo[2 * e2] = a0 * w.x - b0 * w.y;
+      khi[2 * e2] = b0 * w.x + a0 * w.y;
+      klo[2 * e2 + 1] = a1 * w.z - b1 * w.w;
+      khi[2 * e2 + 1] = b1 * w.z + a1 * w.w;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) klo[e] = khi[e] = vlo[e] = vhi[e] = 0.f;
+  }
+  // keys: channel d at (d % 2) * 64 + d / 2 (low channels 8fs + e, high 64 + 8fs + e)
+  *reinterpret_cast<float4*>(&s_k[kk][4 * fs]) = make_float4(klo[0], klo[2], klo[4], klo[6]);
+  *reinterpret_cast<float4*>(&s_k[kk][kPH + 4 * fs]) = make_float4(klo[1], klo[3], klo[5], klo[7]);
+  *reinterpret_cast<float4*>(&s_k[kk][32 + 4 * fs]) = make_float4(khi[0], khi[2], khi[4], khi[6]);
+  *reinterpret_cast<float4*>(&s_k[kk][kPH + 32 + 4 * fs]) = make_float4(khi[1], khi[3], khi[5], khi[7]);
+  // values: channel d at (d % 32) * 4 + d / 32
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int dl = 8 * fs + e, dh = kPH + 8 * fs + e;
+    s_v[kk][(dl & 31) * 4 + (dl >> 5)] = vlo[e];
+    s_v[kk][(dh & 31) * 4 + (dh >> 5)] = vhi[e];
+  }
+}
+
+template <int C>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefill_fwd_mfma_kernel(PrefillArgs a) {
+  extern __shared__ float s_cb[];                    // [2][256*C] step slices
   __shared__ __attribute__((aligned(16))) float s_k[kTile][kLds];
   __shared__ __attribute__((aligned(16))) float s_v[kTile][kLds];
-  const int row = threadIdx.x >> 2, sub = threadIdx.x & 3;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int hh = lane >> 5, col = lane & 31;
   const int hq = blockIdx.y, h = hq / a.gqa;
   const int b = blockIdx.z / a.n_steps, tl = blockIdx.z - b * a.n_steps;
   const int t = a.step0 + tl, beta = t / a.T_c, m = t - beta * a.T_c;
   // the last query tiles attend the most tokens: dispatch them first
-  const int q0 = (gridDim.x - 1 - blockIdx.x) * kRows;
-  const int i = q0 + row;
+  const int q0 = (gridDim.x - 1 - blockIdx.x) * kMT;
+  const int qw0 = q0 + wave * 32;
+  const int i = qw0 + col;
   const bool vq = i < a.N;
   float* s_cbk = s_cb;
   float* s_cbv = s_cb + 256 * C;
   stage_codebooks<C>(a, h, beta, m, s_cbk, s_cbv);
 
+  // B operand of S^T: qreg[s] = q[i][2s + hh], scaled to base-2 scores
   const int64_t qrow = ((((int64_t)b * a.Hq + hq) * a.n_steps + tl) * a.N + (vq ? i : 0)) * kPD;
-  Row32 q, o;
-  load_row(q, a.q + qrow, sub, a.scale * kLog2e);
-  zero_row(o);
+  const float qs = vq ? a.scale * kLog2e : 0.f;
+  float qreg[64];
+  {
+    const float4* qp = reinterpret_cast<const float4*>(a.q + qrow);
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const float4 x = qp[2 * u], y = qp[2 * u + 1];          // channels 8u .. 8u+7
+      qreg[4 * u + 0] = (hh ? x.y : x.x) * qs;
+      qreg[4 * u + 1] = (hh ? x.w : x.z) * qs;
+      qreg[4 * u + 2] = (hh ? y.y : y.x) * qs;
+      qreg[4 * u + 3] = (hh ? y.w : y.z) * qs;
+    }
+  }
+  f32x16_pf o[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
   float mx = -INFINITY, l = 0.f;
 
-  auto consume = [&](int cnt, int jbase, bool causal) {
-    for (int kk = 0; kk < cnt; ++kk) {
-      const float s = quad_sum(dot_lds(q, s_k[kk], sub));
-      if (!vq || (causal && jbase + kk > i)) continue;
-      if (s > mx) {
-        const float al = __builtin_amdgcn_exp2f(mx - s);
-        l *= al;
+  auto consume = [&](int cnt, int j0, bool sinks) {
+    if (!sinks && qw0 + 31 < j0) return;             // every query of the wave precedes the tile
+    f32x16_pf sacc;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) { o.lo[e] *= al; o.hi[e] *= al; }
-        mx = s;
-      }
-      const float p = __builtin_amdgcn_exp2f(s - mx);
-      l += p;
-      axpy_lds(o, p, s_v[kk], sub);
+    for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+#pragma unroll
+    for (int s4 = 0; s4 < 16; ++s4) {
+      const float4 kv = *reinterpret_cast<const float4*>(&s_k[col][hh * kPH + 4 * s4]);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(kv.x, qreg[4 * s4 + 0], sacc, 0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(kv.y, qreg[4 * s4 + 1], sacc, 0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(kv.z, qreg[4 * s4 + 2], sacc, 0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(kv.w, qreg[4 * s4 + 3], sacc, 0, 0, 0);
+    }
+    // register r holds key j0 + 8(r/4) + 4hh + r%4 of query i
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int kr = 8 * (r >> 2) + 4 * hh + (r & 3);
+      const bool ok = vq && kr < cnt && (sinks || j0 + kr <= i);
+      sacc[r] = ok ? sacc[r] : -INFINITY;
+      tmax = fmaxf(tmax, sacc[r]);
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const float mn = fmaxf(mx, tmax);
+    const float al = mx == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mx - mn);
+    float ps = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      sacc[r] = sacc[r] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sacc[r] - mn);
+      ps += sacc[r];
+    }
+    ps += __shfl_xor(ps, 32);
+    l = l * al + ps;
+    mx = mn;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][r] *= al;
+    // O^T += V^T P^T: at step s, B row hh is this lane's register s
+#pragma unroll
+    for (int st = 0; st < 16; ++st) {
+      const int kr = 8 * (st >> 2) + 4 * hh + (st & 3);
+      const float4 vv = *reinterpret_cast<const float4*>(&s_v[kr][col * 4]);
+      o[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv.x, sacc[st], o[0], 0, 0, 0);
+      o[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv.y, sacc[st], o[1], 0, 0, 0);
+      o[2] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv.z, sacc[st], o[2], 0, 0, 0);
+      o[3] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv.w, sacc[st], o[3], 0, 0, 0);
     }
   };
   for (int j0 = 0; j0 < a.n_s; j0 += kTile) {
     const int cnt = min(kTile, a.n_s - j0);
     __syncthreads();
-    fill_tile<C>(a, b, h, t, beta, true, j0, cnt, s_cbk, s_cbv, s_k, s_v);
-    __syncthreads();
-    consume(cnt, 0, false);
-  }
-  const int jend = min(a.N, q0 + kRows);
-  for (int j0 = 0; j0 < jend; j0 += kTile) {
-    const int cnt = min(kTile, jend - j0);
-    __syncthreads();
-    fill_tile<C>(a, b, h, t, beta, false, j0, cnt, s_cbk, s_cbv, s_k, s_v);
+    fill_tile_mfma<C>(a, b, h, t, beta, true, j0, cnt, s_cbk, s_cbv, s_k, s_v);
     __syncthreads();
     consume(cnt, j0, true);
   }
+  const int jend = min(a.N, q0 + kMT);
+  for (int j0 = 0; j0 < jend; j0 += kTile) {
+    const int cnt = min(kTile, jend - j0);
+    __syncthreads();
+    fill_tile_mfma<C>(a, b, h, t, beta, false, j0, cnt, s_cbk, s_cbv, s_k, s_v);
+    __syncthreads();
+    consume(cnt, j0, false);
+  }
   if (vq) {
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    store_row(o, a.out + qrow, sub, inv);
-    if (sub == 0) a.lse[qrow / kPD] = l > 0.f ? (mx + __log2f(l)) * kLn2 : -INFINITY;
+    float* op = a.out + qrow;
+    // O^T register r of block db is channel 32db + 8(r/4) + 4hh + r%4
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        *reinterpret_cast<float4*>(op + 32 * db + 8 * r4 + 4 * hh) =
+            make_float4(o[db][4 * r4] * inv, o[db][4 * r4 + 1] * inv, o[db][4 * r4 + 2] * inv, o[db][4 * r4 + 3] * inv);
+    if (hh == 0) a.lse[qrow / kPD] = l > 0.f ? (mx + __log2f(l)) * kLn2 : -INFINITY;
   }
 }
 
@@ -468,14 +605,15 @@ static hipError_t prefill_launch(const PrefillArgs& a, bool backward, hipStream_
   const dim3 grid((a.N + kRows - 1) / kRows, a.Hq, a.B * a.n_steps);
   const size_t lds = (size_t)2 * 256 * C * sizeof(float);
   // dynamic LDS beyond the default allowance (C = 32 takes 64 KiB)
-  for (const void* k : {reinterpret_cast<const void*>(&prefill_fwd_kernel<C>),
+  for (const void* k : {reinterpret_cast<const void*>(&prefill_fwd_mfma_kernel<C>),
                         reinterpret_cast<const void*>(&prefill_bwd_kv_kernel<C>),
                         reinterpret_cast<const void*>(&prefill_bwd_q_kernel<C>)}) {
     const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
   if (!backward) {
-    hipLaunchKernelGGL((prefill_fwd_kernel<C>), grid, dim3(256), lds, s, a);
+    const dim3 gm((a.N + kMT - 1) / kMT, a.Hq, a.B * a.n_steps);
+    hipLaunchKernelGGL((prefill_fwd_mfma_kernel<C>), gm, dim3(256), lds, s, a);
     return hipGetLastError();
   }
   const int64_t rows = (int64_t)a.B * a.Hq * a.n_steps * a.N;
