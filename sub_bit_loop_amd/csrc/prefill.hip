@@ -213,9 +213,13 @@ __global__ __launch_bounds__(256) void rope_table_f32_kernel(float* tab, int n_p
 typedef float f32x16_pf __attribute__((ext_vector_type(16)));
 constexpr int kMT = 128;              // queries per workgroup (4 waves x 32)
 
-template <int C>
+// Stage cnt keys (rotated) and values for the matrix-core kernels: keys
+// de-interleaved into s_k; values block-interleaved into s_v (V_DEINT: like
+// the keys instead); s_kb, when given, gets a block-interleaved copy of the keys.
+template <int C, bool V_DEINT = false>
 __device__ void fill_tile_mfma(const PrefillArgs& a, int b, int h, int t, int beta, bool sinks, int j0, int cnt,
-                               const float* s_cbk, const float* s_cbv, float (*s_k)[kLds], float (*s_v)[kLds]) {
+                               const float* s_cbk, const float* s_cbv, float (*s_k)[kLds], float (*s_v)[kLds],
+                               float (*s_kb)[kLds] = nullptr) {
   const int kk = threadIdx.x >> 3, fs = threadIdx.x & 7;
   float klo[8], khi[8], vlo[8], vhi[8];
   if (kk < cnt) {
@@ -270,12 +274,27 @@ __device__ void fill_tile_mfma(const PrefillArgs& a, int b, int h, int t, int be
   *reinterpret_cast<float4*>(&s_k[kk][kPH + 4 * fs]) = make_float4(klo[1], klo[3], klo[5], klo[7]);
   *reinterpret_cast<float4*>(&s_k[kk][32 + 4 * fs]) = make_float4(khi[0], khi[2], khi[4], khi[6]);
   *reinterpret_cast<float4*>(&s_k[kk][kPH + 32 + 4 * fs]) = make_float4(khi[1], khi[3], khi[5], khi[7]);
-  // values: channel d at (d % 32) * 4 + d / 32
+  if constexpr (V_DEINT) {
+    *reinterpret_cast<float4*>(&s_v[kk][4 * fs]) = make_float4(vlo[0], vlo[2], vlo[4], vlo[6]);
+    *reinterpret_cast<float4*>(&s_v[kk][kPH + 4 * fs]) = make_float4(vlo[1], vlo[3], vlo[5], vlo[7]);
+    *reinterpret_cast<float4*>(&s_v[kk][32 + 4 * fs]) = make_float4(vhi[0], vhi[2], vhi[4], vhi[6]);
+    *reinterpret_cast<float4*>(&s_v[kk][kPH + 32 + 4 * fs]) = make_float4(vhi[1], vhi[3], vhi[5], vhi[7]);
+  } else {
+    // values: channel d at (d % 32) * 4 + d / 32
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int dl = 8 * fs + e, dh = kPH + 8 * fs + e;
-    s_v[kk][(dl & 31) * 4 + (dl >> 5)] = vlo[e];
-    s_v[kk][(dh & 31) * 4 + (dh >> 5)] = vhi[e];
+    for (int e = 0; e < 8; ++e) {
+      const int dl = 8 * fs + e, dh = kPH + 8 * fs + e;
+      s_v[kk][(dl & 31) * 4 + (dl >> 5)] = vlo[e];
+      s_v[kk][(dh & 31) * 4 + (dh >> 5)] = vhi[e];
+    }
+  }
+  if (s_kb) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int dl = 8 * fs + e, dh = kPH + 8 * fs + e;
+      s_kb[kk][(dl & 31) * 4 + (dl >> 5)] = klo[e];
+      s_kb[kk][(dh & 31) * 4 + (dh >> 5)] = khi[e];
+    }
   }
 }
 
@@ -395,6 +414,121 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         *reinterpret_cast<float4*>(op + 32 * db + 8 * r4 + 4 * hh) =
             make_float4(o[db][4 * r4] * inv, o[db][4 * r4 + 1] * inv, o[db][4 * r4 + 2] * inv, o[db][4 * r4 + 3] * inv);
     if (hh == 0) a.lse[qrow / kPD] = l > 0.f ? (mx + __log2f(l)) * kLn2 : -INFINITY;
+  }
+}
+
+// Query-side backward on fp32 matrix cores (layout as the forward): per tile
+// of 32 keys, S^T = K_rot Q^T and dP^T = V dO^T (keys on rows), dS^T = P^T
+// (dP^T - delta) with P^T = exp(S^T - lse), and dQ^T += K_rot^T dS^T, whose B
+// operand is the dS^T accumulator itself.
+template <int C>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefill_bwd_q_mfma_kernel(
+    PrefillArgs a) {
+  extern __shared__ float s_cb[];
+  __shared__ __attribute__((aligned(16))) float s_k[kTile][kLds];
+  __shared__ __attribute__((aligned(16))) float s_v[kTile][kLds];
+  __shared__ __attribute__((aligned(16))) float s_kb[kTile][kLds];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int hh = lane >> 5, col = lane & 31;
+  const int hq = blockIdx.y, h = hq / a.gqa;
+  const int b = blockIdx.z / a.n_steps, tl = blockIdx.z - b * a.n_steps;
+  const int t = a.step0 + tl, beta = t / a.T_c, m = t - beta * a.T_c;
+  const int q0 = (gridDim.x - 1 - blockIdx.x) * kMT;
+  const int qw0 = q0 + wave * 32;
+  const int i = qw0 + col;
+  const bool vq = i < a.N;
+  float* s_cbk = s_cb;
+  float* s_cbv = s_cb + 256 * C;
+  stage_codebooks<C>(a, h, beta, m, s_cbk, s_cbv);
+
+  const int64_t qr = (((int64_t)b * a.Hq + hq) * a.n_steps + tl) * a.N + (vq ? i : 0);
+  const float qs = vq ? a.scale * kLog2e : 0.f;
+  float qreg[64], dreg[64];
+  {
+    const float4* qp = reinterpret_cast<const float4*>(a.q + qr * kPD);
+    const float4* dp = reinterpret_cast<const float4*>(a.dout + qr * kPD);
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const float4 x = qp[2 * u], y = qp[2 * u + 1];
+      qreg[4 * u + 0] = (hh ? x.y : x.x) * qs;
+      qreg[4 * u + 1] = (hh ? x.w : x.z) * qs;
+      qreg[4 * u + 2] = (hh ? y.y : y.x) * qs;
+      qreg[4 * u + 3] = (hh ? y.w : y.z) * qs;
+      const float4 x2 = dp[2 * u], y2 = dp[2 * u + 1];
+      const float dsc = vq ? 1.f : 0.f;
+      dreg[4 * u + 0] = (hh ? x2.y : x2.x) * dsc;
+      dreg[4 * u + 1] = (hh ? x2.w : x2.z) * dsc;
+      dreg[4 * u + 2] = (hh ? y2.y : y2.x) * dsc;
+      dreg[4 * u + 3] = (hh ? y2.w : y2.z) * dsc;
+    }
+  }
+  const float l2 = a.lse[qr] * kLog2e, dl = a.delta[qr];
+  f32x16_pf dq[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dq[db][r] = 0.f;
+
+  auto consume = [&](int cnt, int j0, bool sinks) {
+    if (!sinks && qw0 + 31 < j0) return;
+    f32x16_pf sacc, pacc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sacc[r] = pacc[r] = 0.f;
+#pragma unroll
+    for (int s4 = 0; s4 < 16; ++s4) {
+      const float4 kv = *reinterpret_cast<const float4*>(&s_k[col][hh * kPH + 4 * s4]);
+      const float4 vv = *reinterpret_cast<const float4*>(&s_v[col][hh * kPH + 4 * s4]);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(kv.x, qreg[4 * s4 + 0], sacc, 0, 0, 0);
+      pacc = __builtin_amdgcn_mfma_f32_32x32x2f32(vv.x, dreg[4 * s4 + 0], pacc, 0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(kv.y, qreg[4 * s4 + 1], sacc, 0, 0, 0);
+      pacc = __builtin_amdgcn_mfma_f32_32x32x2f32(vv.y, dreg[4 * s4 + 1], pacc, 0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(kv.z, qreg[4 * s4 + 2], sacc, 0, 0, 0);
+      pacc = __builtin_amdgcn_mfma_f32_32x32x2f32(vv.z, dreg[4 * s4 + 2], pacc, 0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(kv.w, qreg[4 * s4 + 3], sacc, 0, 0, 0);
+      pacc = __builtin_amdgcn_mfma_f32_32x32x2f32(vv.w, dreg[4 * s4 + 3], pacc, 0, 0, 0);
+    }
+    // dS^T in place of the score accumulator (masked pairs contribute zero)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int kr = 8 * (r >> 2) + 4 * hh + (r & 3);
+      const bool ok = vq && kr < cnt && (sinks || j0 + kr <= i);
+      const float p = ok ? __builtin_amdgcn_exp2f(sacc[r] - l2) : 0.f;
+      sacc[r] = p * (pacc[r] - dl);
+    }
+#pragma unroll
+    for (int st = 0; st < 16; ++st) {
+      const int kr = 8 * (st >> 2) + 4 * hh + (st & 3);
+      const float4 kb = *reinterpret_cast<const float4*>(&s_kb[kr][col * 4]);
+      dq[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(kb.x, sacc[st], dq[0], 0, 0, 0);
+      dq[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(kb.y, sacc[st], dq[1], 0, 0, 0);
+      dq[2] = __builtin_amdgcn_mfma_f32_32x32x2f32(kb.z, sacc[st], dq[2], 0, 0, 0);
+      dq[3] = __builtin_amdgcn_mfma_f32_32x32x2f32(kb.w, sacc[st], dq[3], 0, 0, 0);
+    }
+  };
+  for (int j0 = 0; j0 < a.n_s; j0 += kTile) {
+    const int cnt = min(kTile, a.n_s - j0);
+    __syncthreads();
+    fill_tile_mfma<C, true>(a, b, h, t, beta, true, j0, cnt, s_cbk, s_cbv, s_k, s_v, s_kb);
+    __syncthreads();
+    consume(cnt, j0, true);
+  }
+  const int jend = min(a.N, q0 + kMT);
+  for (int j0 = 0; j0 < jend; j0 += kTile) {
+    const int cnt = min(kTile, jend - j0);
+    __syncthreads();
+    fill_tile_mfma<C, true>(a, b, h, t, beta, false, j0, cnt, s_cbk, s_cbv, s_k, s_v, s_kb);
+    __syncthreads();
+    consume(cnt, j0, false);
+  }
+  if (vq) {
+    float* op = a.dq + qr * kPD;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        *reinterpret_cast<float4*>(op + 32 * db + 8 * r4 + 4 * hh) =
+            make_float4(dq[db][4 * r4] * a.scale, dq[db][4 * r4 + 1] * a.scale, dq[db][4 * r4 + 2] * a.scale,
+                        dq[db][4 * r4 + 3] * a.scale);
   }
 }
 
@@ -607,7 +741,7 @@ static hipError_t prefill_launch(const PrefillArgs& a, bool backward, hipStream_
   // dynamic LDS beyond the default allowance (C = 32 takes 64 KiB)
   for (const void* k : {reinterpret_cast<const void*>(&prefill_fwd_mfma_kernel<C>),
                         reinterpret_cast<const void*>(&prefill_bwd_kv_kernel<C>),
-                        reinterpret_cast<const void*>(&prefill_bwd_q_kernel<C>)}) {
+                        reinterpret_cast<const void*>(&prefill_bwd_q_mfma_kernel<C>)}) {
     const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
@@ -623,7 +757,8 @@ static hipError_t prefill_launch(const PrefillArgs& a, bool backward, hipStream_
   hipLaunchKernelGGL(prefill_zero_kernel, dim3((unsigned)((ncb + 255) / 256)), dim3(256), 0, s, a.dkcb, ncb);
   hipLaunchKernelGGL(prefill_zero_kernel, dim3((unsigned)((ncb + 255) / 256)), dim3(256), 0, s, a.dvcb, ncb);
   hipLaunchKernelGGL((prefill_bwd_kv_kernel<C>), grid, dim3(256), lds, s, a);
-  hipLaunchKernelGGL((prefill_bwd_q_kernel<C>), grid, dim3(256), lds, s, a);
+  const dim3 gm((a.N + kMT - 1) / kMT, a.Hq, a.B * a.n_steps);
+  hipLaunchKernelGGL((prefill_bwd_q_mfma_kernel<C>), gm, dim3(256), lds, s, a);
   return hipGetLastError();
 }
 

@@ -4,9 +4,13 @@ backward pass into the queries and the codebook entries, the gradient of the
 KL objective through the toy looped stack, and a short fine-tuning run.
 
 Tolerances (fp32 kernels against fp64): outputs, per row, max |err| <= 1e-4 *
-||row|| (rows below 1e-3 of the largest use that floor); lse within 1e-4; gradients, per tensor, max |err| <= 1e-4 * max |ref|
-(an fp32 sum of n terms errs by at most ~n * 2^-24 of the sum of magnitudes,
-and the codebook sums add up to a few thousand terms)."""
+||row|| (rows below 1e-3 of the largest use that floor); lse within 1e-4;
+gradients, per tensor, max |err| <= 1e-4 * max |ref| (an fp32 sum of n terms
+errs by at most ~n * 2^-24 of the sum of magnitudes, and the codebook sums add
+up to a few thousand terms).  d_q is checked per row with a floor of 1e-2 of
+the largest row: its terms are P (dP - delta) k with dP and delta each rounded
+in fp32, so a row's error scales with |dP| |k| however much dP - delta cancels,
+and the rows of queries that see one or two keys are small."""
 import math
 
 import numpy as np
@@ -43,14 +47,14 @@ def _oracle_args(cfg, inp, kidx, vidx):
             inp["sink_k"].double().cpu(), inp["sink_v"].double().cpu(), cfg.T_c)
 
 
-def _row_check(got, want, tol, what):
+def _row_check(got, want, tol, what, floor=1e-3):
     g = got.double().cpu().reshape(-1, got.shape[-1])
     w = want.reshape(-1, want.shape[-1])
     err = (g - w).abs().max(dim=1).values
-    # a row whose exact value is zero (query 0 with no sinks has d_q = 0) is
-    # measured against 1e-3 of the largest row
+    # rows far below the largest (query 0 with no sinks has d_q = 0 exactly)
+    # are measured against `floor` times the largest row
     norms = w.norm(dim=1)
-    scale = norms.clamp_min(1e-3 * float(norms.max()))
+    scale = norms.clamp_min(floor * float(norms.max()))
     worst = float((err / scale).max())
     _say("  %s worst rel err %.3g (tolerance %g)" % (what, worst, tol))
     assert worst <= tol, what
@@ -97,7 +101,7 @@ def test_prefill_forward_backward(name, G, T_c, T, H_kv, H_q, B, N, n_s, step0, 
     dl = float((lse.double().cpu() - l_r).abs().max())
     _say("  lse max err %.3g" % dl)
     assert dl <= 1e-4
-    _row_check(dq, dq_r, 1e-4, "d_q")
+    _row_check(dq, dq_r, 1e-4, "d_q", floor=1e-2)
     _tensor_check(dk, dk_r, 1e-4, "d_k_cb")
     _tensor_check(dv, dv_r, 1e-4, "d_v_cb")
     # the forward is deterministic
@@ -196,7 +200,7 @@ def test_prefill_full_size_sampled():
         dl = float((lse[:, sl].double().cpu() - l_r).abs().max())
         _say("  lse head %d max err %.3g" % (h, dl))
         assert dl <= 1e-4
-        _row_check(dq[:, sl], dq_r, 1e-4, "d_q head %d" % h)
+        _row_check(dq[:, sl], dq_r, 1e-4, "d_q head %d" % h, floor=1e-2)
         if h == 5:
             _tensor_check(dk[sl], dk_r, 1e-4, "d_k_cb kv-head 5")
             _tensor_check(dv[sl], dv_r, 1e-4, "d_v_cb kv-head 5")
