@@ -15,11 +15,10 @@
 // n_s + j).  Everything is fp32; the RoPE table is fp32 (cos, sin) per
 // (position, frequency), computed in fp64.
 //
-// The forward runs on fp32 matrix cores (below).  The backward kernels use the
-// vector units: a row (a key in the key-side backward, a query in the
-// query-side one) is served by four lanes; lane `sub` owns the 16 frequencies
-// 16*sub .. 16*sub + 15 and both channels of each RoPE pair (f and f + 64), so
-// rotations stay inside a lane and a dot product is a 4-lane sum.
+// All three products run on fp32 matrix cores (v_mfma_f32_32x32x2f32), so the
+// arithmetic is fp32 as in a vector implementation.  Each wave owns 32 rows
+// (queries, or tokens in the key-side passes) and works on LDS tiles of 32
+// keys or queries; the operand layouts are described with each kernel.
 #include "common.h"
 #include "kernels.h"
 
@@ -29,15 +28,8 @@ namespace {
 
 constexpr int kPD = 128;              // head dimension
 constexpr int kPH = 64;               // RoPE pairs
-constexpr int kRows = 64;             // rows per workgroup (queries or keys)
 constexpr int kTile = 32;             // keys (or queries) staged per LDS tile
 constexpr int kLds = kPD + 4;         // padded LDS row
-
-__device__ __forceinline__ float quad_sum(float v) { return group_sum<4>(v); }
-
-// Keeps the compiler from holding LDS rows in registers across it (they are
-// read again instead), which bounds register use in the backward loops.
-__device__ __forceinline__ void lds_reload() { asm volatile("" ::: "memory"); }
 
 // Stage step m's slice of the K and V codebooks of (kv-head h, block beta)
 // as fp32 [K][C].
@@ -51,134 +43,6 @@ __device__ void stage_codebooks(const PrefillArgs& a, int h, int beta, int m, fl
     s_cbk[e] = r < a.K ? bf16_to_f32(a.kcb[o]) : 0.f;
     s_cbv[e] = r < a.K ? bf16_to_f32(a.vcb[o]) : 0.f;
   }
-}
-
-// Fill an LDS tile with cnt keys (rotated) and values: sinks j0.. (positions
-// j) when `sinks`, else tokens j0.. (positions n_s + j).  Thread (kk, fs)
-// writes frequencies 8*fs .. 8*fs + 7 of key kk and their partners.
-template <int C>
-__device__ void fill_tile(const PrefillArgs& a, int b, int h, int t, int beta, bool sinks, int j0, int cnt,
-                          const float* s_cbk, const float* s_cbv, float (*s_k)[kLds], float (*s_v)[kLds]) {
-  const int kk = threadIdx.x >> 3, fs = threadIdx.x & 7;
-  float klo[8], khi[8], vlo[8], vhi[8];
-  int pos = 0;
-  if (kk < cnt) {
-    const int j = j0 + kk;
-    if (sinks) {
-      pos = j;
-      const int64_t ro = ((((int64_t)b * a.H + h) * a.T + t) * a.n_s + j) * kPD;
-      const uint4 xl = *reinterpret_cast<const uint4*>(a.sk + ro + 8 * fs);
-      const uint4 xh = *reinterpret_cast<const uint4*>(a.sk + ro + kPH + 8 * fs);
-      const uint4 yl = *reinterpret_cast<const uint4*>(a.sv + ro + 8 * fs);
-      const uint4 yh = *reinterpret_cast<const uint4*>(a.sv + ro + kPH + 8 * fs);
-      const uint32_t wxl[4] = {xl.x, xl.y, xl.z, xl.w}, wxh[4] = {xh.x, xh.y, xh.z, xh.w};
-      const uint32_t wyl[4] = {yl.x, yl.y, yl.z, yl.w}, wyh[4] = {yh.x, yh.y, yh.z, yh.w};
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        klo[2 * w] = bf16lo(wxl[w]); klo[2 * w + 1] = bf16hi(wxl[w]);
-        khi[2 * w] = bf16lo(wxh[w]); khi[2 * w + 1] = bf16hi(wxh[w]);
-        vlo[2 * w] = bf16lo(wyl[w]); vlo[2 * w + 1] = bf16hi(wyl[w]);
-        vhi[2 * w] = bf16lo(wyh[w]); vhi[2 * w + 1] = bf16hi(wyh[w]);
-      }
-    } else {
-      pos = a.n_s + j;
-      const int64_t ir = ((((int64_t)b * a.H + h) * a.n_blk + beta) * a.N_cap + j) * (kPD / C);
-      const uint8_t* kr = a.kidx + ir;
-      const uint8_t* vr = a.vidx + ir;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int dl = 8 * fs + e, dh = kPH + 8 * fs + e;
-        klo[e] = s_cbk[kr[dl / C] * C + dl % C];
-        khi[e] = s_cbk[kr[dh / C] * C + dh % C];
-        vlo[e] = s_cbv[vr[dl / C] * C + dl % C];
-        vhi[e] = s_cbv[vr[dh / C] * C + dh % C];
-      }
-    }
-    const float4* cs = reinterpret_cast<const float4*>(a.rope + ((int64_t)pos * kPH + 8 * fs) * 2);
-#pragma unroll
-    for (int e2 = 0; e2 < 4; ++e2) {
-      const float4 w = cs[e2];     // (cos, sin) of two frequencies
-      const float c0 = w.x, s0 = w.y, c1 = w.z, s1 = w.w;
-      const float a0 = klo[2 * e2], b0 = khi[2 * e2], a1 = klo[2 * e2 + 1], b1 = khi[2 * e2 + 1];
-      klo[2 * e2] = a0 * c0 - b0 * s0;
-      khi[2 * e2] = b0 * c0 + a0 * s0;
-      klo[2 * e2 + 1] = a1 * c1 - b1 * s1;
-      khi[2 * e2 + 1] = b1 * c1 + a1 * s1;
-    }
-  } else {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) klo[e] = khi[e] = vlo[e] = vhi[e] = 0.f;
-  }
-#pragma unroll
-  for (int e4 = 0; e4 < 2; ++e4) {
-    *reinterpret_cast<float4*>(&s_k[kk][8 * fs + 4 * e4]) =
-        make_float4(klo[4 * e4], klo[4 * e4 + 1], klo[4 * e4 + 2], klo[4 * e4 + 3]);
-    *reinterpret_cast<float4*>(&s_k[kk][kPH + 8 * fs + 4 * e4]) =
-        make_float4(khi[4 * e4], khi[4 * e4 + 1], khi[4 * e4 + 2], khi[4 * e4 + 3]);
-    *reinterpret_cast<float4*>(&s_v[kk][8 * fs + 4 * e4]) =
-        make_float4(vlo[4 * e4], vlo[4 * e4 + 1], vlo[4 * e4 + 2], vlo[4 * e4 + 3]);
-    *reinterpret_cast<float4*>(&s_v[kk][kPH + 8 * fs + 4 * e4]) =
-        make_float4(vhi[4 * e4], vhi[4 * e4 + 1], vhi[4 * e4 + 2], vhi[4 * e4 + 3]);
-  }
-}
-
-// Row-local load / dot / axpy over a lane's 32 channels of a 128-wide row.
-struct Row32 {
-  float lo[16], hi[16];
-};
-
-__device__ __forceinline__ void load_row(Row32& r, const float* p, int sub, float scale) {
-  const float4* l = reinterpret_cast<const float4*>(p + 16 * sub);
-  const float4* hh = reinterpret_cast<const float4*>(p + kPH + 16 * sub);
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const float4 x = l[u], y = hh[u];
-    r.lo[4 * u] = x.x * scale; r.lo[4 * u + 1] = x.y * scale; r.lo[4 * u + 2] = x.z * scale; r.lo[4 * u + 3] = x.w * scale;
-    r.hi[4 * u] = y.x * scale; r.hi[4 * u + 1] = y.y * scale; r.hi[4 * u + 2] = y.z * scale; r.hi[4 * u + 3] = y.w * scale;
-  }
-}
-
-__device__ __forceinline__ float dot_lds(const Row32& r, const float* row, int sub) {
-  const float4* l = reinterpret_cast<const float4*>(row + 16 * sub);
-  const float4* hh = reinterpret_cast<const float4*>(row + kPH + 16 * sub);
-  float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const float4 x = l[u], y = hh[u];
-    s0 = fmaf(r.lo[4 * u], x.x, s0); s1 = fmaf(r.lo[4 * u + 1], x.y, s1);
-    s0 = fmaf(r.lo[4 * u + 2], x.z, s0); s1 = fmaf(r.lo[4 * u + 3], x.w, s1);
-    s0 = fmaf(r.hi[4 * u], y.x, s0); s1 = fmaf(r.hi[4 * u + 1], y.y, s1);
-    s0 = fmaf(r.hi[4 * u + 2], y.z, s0); s1 = fmaf(r.hi[4 * u + 3], y.w, s1);
-  }
-  return s0 + s1;
-}
-
-__device__ __forceinline__ void axpy_lds(Row32& acc, float p, const float* row, int sub) {
-  const float4* l = reinterpret_cast<const float4*>(row + 16 * sub);
-  const float4* hh = reinterpret_cast<const float4*>(row + kPH + 16 * sub);
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const float4 x = l[u], y = hh[u];
-    acc.lo[4 * u] = fmaf(p, x.x, acc.lo[4 * u]); acc.lo[4 * u + 1] = fmaf(p, x.y, acc.lo[4 * u + 1]);
-    acc.lo[4 * u + 2] = fmaf(p, x.z, acc.lo[4 * u + 2]); acc.lo[4 * u + 3] = fmaf(p, x.w, acc.lo[4 * u + 3]);
-    acc.hi[4 * u] = fmaf(p, y.x, acc.hi[4 * u]); acc.hi[4 * u + 1] = fmaf(p, y.y, acc.hi[4 * u + 1]);
-    acc.hi[4 * u + 2] = fmaf(p, y.z, acc.hi[4 * u + 2]); acc.hi[4 * u + 3] = fmaf(p, y.w, acc.hi[4 * u + 3]);
-  }
-}
-
-__device__ __forceinline__ void store_row(const Row32& r, float* p, int sub, float scale) {
-  float4* l = reinterpret_cast<float4*>(p + 16 * sub);
-  float4* hh = reinterpret_cast<float4*>(p + kPH + 16 * sub);
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    l[u] = make_float4(r.lo[4 * u] * scale, r.lo[4 * u + 1] * scale, r.lo[4 * u + 2] * scale, r.lo[4 * u + 3] * scale);
-    hh[u] = make_float4(r.hi[4 * u] * scale, r.hi[4 * u + 1] * scale, r.hi[4 * u + 2] * scale, r.hi[4 * u + 3] * scale);
-  }
-}
-
-__device__ __forceinline__ void zero_row(Row32& r) {
-#pragma unroll
-  for (int e = 0; e < 16; ++e) r.lo[e] = r.hi[e] = 0.f;
 }
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -532,6 +396,206 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   }
 }
 
+// Key-side backward on fp32 matrix cores, in two passes so that each fits the
+// register file.  A workgroup owns 128 tokens (32 per wave, one per lane
+// column) and walks the tiles of 32 queries that can see them.  With the
+// queries on rows, S = Q K_rot^T has each lane's token in its column, so the
+// token's own rotated key (and value) are the B operands, kept in registers
+// as channels 2s + hh, and the probabilities in the accumulator are the B
+// operand of the next product:
+//   V pass: dV^T += dO^T P;
+//   K pass: dP = dO V^T, dS = P (dP - delta), dK_rot^T += Q^T dS.
+// Query tiles are staged de-interleaved ([q][(d % 2) * 64 + d / 2]) for the A
+// operands over D and block-interleaved ([q][(d % 32) * 4 + d / 32]) for the A
+// operands over the query pairs.  The gradients are added per codeword in LDS,
+// then into the global fp32 gradient.
+
+// Stage tile rows of queries (and dO): thread (r, part) writes channels
+// 16 part .. 16 part + 15 of row r.
+__device__ __forceinline__ void stage_rows(const float* src, float sc, float (*deint)[kLds], float (*blk)[kLds],
+                                           int r, int part) {
+  const float4* p4 = reinterpret_cast<const float4*>(src + 16 * part);
+  float x[16];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const float4 v = p4[u];
+    x[4 * u] = v.x * sc; x[4 * u + 1] = v.y * sc; x[4 * u + 2] = v.z * sc; x[4 * u + 3] = v.w * sc;
+  }
+  if (deint) {
+    *reinterpret_cast<float4*>(&deint[r][8 * part]) = make_float4(x[0], x[2], x[4], x[6]);
+    *reinterpret_cast<float4*>(&deint[r][8 * part + 4]) = make_float4(x[8], x[10], x[12], x[14]);
+    *reinterpret_cast<float4*>(&deint[r][kPH + 8 * part]) = make_float4(x[1], x[3], x[5], x[7]);
+    *reinterpret_cast<float4*>(&deint[r][kPH + 8 * part + 4]) = make_float4(x[9], x[11], x[13], x[15]);
+  }
+  if (blk) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int d = 16 * part + e;
+      blk[r][(d & 31) * 4 + (d >> 5)] = x[e];
+    }
+  }
+}
+
+// This lane's token: rotated key channels kreg[s] = k_rot[2s + hh] and value
+// channels vreg[s] = v[2s + hh] (s < 64), from the codebooks.
+template <int C, bool WITH_V>
+__device__ __forceinline__ void token_regs(const PrefillArgs& a, int64_t ir, int64_t cbo, int m, int pos, int hh,
+                                           float (&kreg)[64], float (&vreg)[64]) {
+  const float2* rp = reinterpret_cast<const float2*>(a.rope + (int64_t)pos * kPH * 2);
+#pragma unroll
+  for (int s = 0; s < 32; ++s) {
+    const int dl = 2 * s + hh, dh = dl + kPH;
+    // an index byte >= K (never written by the encode) reads the last entry
+    const int rl = min((int)a.kidx[ir + dl / C], a.K - 1), rh = min((int)a.kidx[ir + dh / C], a.K - 1);
+    const float xl = bf16_to_f32(a.kcb[cbo + (int64_t)rl * a.G + (dl % C) * a.T_c + m]);
+    const float xh = bf16_to_f32(a.kcb[cbo + (int64_t)rh * a.G + (dh % C) * a.T_c + m]);
+    const float2 w = rp[dl];
+    kreg[s] = xl * w.x - xh * w.y;
+    kreg[s + 32] = xh * w.x + xl * w.y;
+    if constexpr (WITH_V) {
+      const int ul = min((int)a.vidx[ir + dl / C], a.K - 1), uh = min((int)a.vidx[ir + dh / C], a.K - 1);
+      vreg[s] = bf16_to_f32(a.vcb[cbo + (int64_t)ul * a.G + (dl % C) * a.T_c + m]);
+      vreg[s + 32] = bf16_to_f32(a.vcb[cbo + (int64_t)uh * a.G + (dh % C) * a.T_c + m]);
+    }
+  }
+}
+
+template <int C, bool KPASS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefill_bwd_kv_mfma_kernel(
+    PrefillArgs a) {
+  extern __shared__ float s_g[];                      // [256][C] gradient of this step's slice
+  __shared__ __attribute__((aligned(16))) float s_q[kTile][kLds];      // q, de-interleaved, base-2 scaled
+  __shared__ __attribute__((aligned(16))) float s_b[kTile][kLds];      // V pass: dO blocks; K pass: q blocks
+  __shared__ __attribute__((aligned(16))) float s_d[KPASS ? kTile : 1][kLds];   // K pass: dO, de-interleaved
+  __shared__ float s_l2[kTile], s_dl[kTile];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int hh = lane >> 5, col = lane & 31;
+  const int hq = blockIdx.y, h = hq / a.gqa;
+  const int b = blockIdx.z / a.n_steps, tl = blockIdx.z - b * a.n_steps;
+  const int t = a.step0 + tl, beta = t / a.T_c, m = t - beta * a.T_c;
+  const int k0 = blockIdx.x * kMT;
+  const int kw0 = k0 + 32 * wave;
+  const int j = kw0 + col;
+  const bool vk = j < a.N;
+  for (int e = threadIdx.x; e < 256 * C; e += blockDim.x) s_g[e] = 0.f;
+
+  const int64_t ir = ((((int64_t)b * a.H + h) * a.n_blk + beta) * a.N_cap + (vk ? j : 0)) * (kPD / C);
+  const int64_t cbo = ((int64_t)h * a.n_blk + beta) * a.K * a.G;
+  const int pos = a.n_s + (vk ? j : 0);
+  float kreg[64], vreg[64];
+  token_regs<C, KPASS>(a, ir, cbo, m, pos, hh, kreg, vreg);
+  f32x16_pf acc[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+  const float sc2 = a.scale * kLog2e;
+  const int64_t row0 = (((int64_t)b * a.Hq + hq) * a.n_steps + tl) * a.N;
+
+  for (int i0 = k0; i0 < a.N; i0 += kTile) {
+    const int cnt = min(kTile, a.N - i0);
+    __syncthreads();
+    {
+      const int r = threadIdx.x >> 3, part = threadIdx.x & 7;
+      if (r < cnt) {
+        const int64_t qr = row0 + i0 + r;
+        stage_rows(a.q + qr * kPD, sc2, s_q, nullptr, r, part);
+        if constexpr (KPASS) {
+          stage_rows(a.q + qr * kPD, 1.f, nullptr, s_b, r, part);
+          stage_rows(a.dout + qr * kPD, 1.f, s_d, nullptr, r, part);
+        } else {
+          stage_rows(a.dout + qr * kPD, 1.f, nullptr, s_b, r, part);
+        }
+        if (part == 0) {
+          s_l2[r] = a.lse[qr] * kLog2e;
+          s_dl[r] = a.delta[qr];
+        }
+      } else {
+        // rows past the end: zero operands
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          s_q[r][16 * part + e] = 0.f;
+          s_b[r][16 * part + e] = 0.f;
+          if constexpr (KPASS) s_d[r][16 * part + e] = 0.f;
+        }
+        if (part == 0) s_l2[r] = s_dl[r] = 0.f;
+      }
+    }
+    __syncthreads();
+    if (i0 + kTile - 1 < kw0) continue;              // these queries see none of the wave's tokens
+    f32x16_pf sacc, pacc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sacc[r] = pacc[r] = 0.f;
+#pragma unroll
+    for (int s4 = 0; s4 < 16; ++s4) {
+      const float4 qv = *reinterpret_cast<const float4*>(&s_q[col][hh * kPH + 4 * s4]);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(qv.x, kreg[4 * s4 + 0], sacc, 0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(qv.y, kreg[4 * s4 + 1], sacc, 0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(qv.z, kreg[4 * s4 + 2], sacc, 0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(qv.w, kreg[4 * s4 + 3], sacc, 0, 0, 0);
+      if constexpr (KPASS) {
+        const float4 dv = *reinterpret_cast<const float4*>(&s_d[col][hh * kPH + 4 * s4]);
+        pacc = __builtin_amdgcn_mfma_f32_32x32x2f32(dv.x, vreg[4 * s4 + 0], pacc, 0, 0, 0);
+        pacc = __builtin_amdgcn_mfma_f32_32x32x2f32(dv.y, vreg[4 * s4 + 1], pacc, 0, 0, 0);
+        pacc = __builtin_amdgcn_mfma_f32_32x32x2f32(dv.z, vreg[4 * s4 + 2], pacc, 0, 0, 0);
+        pacc = __builtin_amdgcn_mfma_f32_32x32x2f32(dv.w, vreg[4 * s4 + 3], pacc, 0, 0, 0);
+      }
+    }
+    // register r: query i0 + 8(r/4) + 4hh + r%4 of this lane's token j
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int qrl = 8 * (r >> 2) + 4 * hh + (r & 3);
+      const bool ok = vk && qrl < cnt && j <= i0 + qrl;
+      const float p = ok ? __builtin_amdgcn_exp2f(sacc[r] - s_l2[qrl]) : 0.f;
+      if constexpr (KPASS)
+        sacc[r] = p * (pacc[r] - s_dl[qrl]);
+      else
+        sacc[r] = p;
+    }
+#pragma unroll
+    for (int st = 0; st < 16; ++st) {
+      const int qrl = 8 * (st >> 2) + 4 * hh + (st & 3);
+      const float4 bb = *reinterpret_cast<const float4*>(&s_b[qrl][col * 4]);
+      acc[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(bb.x, sacc[st], acc[0], 0, 0, 0);
+      acc[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(bb.y, sacc[st], acc[1], 0, 0, 0);
+      acc[2] = __builtin_amdgcn_mfma_f32_32x32x2f32(bb.z, sacc[st], acc[2], 0, 0, 0);
+      acc[3] = __builtin_amdgcn_mfma_f32_32x32x2f32(bb.w, sacc[st], acc[3], 0, 0, 0);
+    }
+  }
+  // acc[db][r] is the gradient of channel 32db + 8(r/4) + 4hh + r%4 of token j
+  // (K pass: of its rotated key, before the 1/sqrt(D) scale)
+  if (vk) {
+    if constexpr (KPASS) {
+      const float2* rp = reinterpret_cast<const float2*>(a.rope + (int64_t)pos * kPH * 2);
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int dl = 32 * db + 8 * (r >> 2) + 4 * hh + (r & 3), dh = dl + kPH;
+          const float2 w = rp[dl];
+          const float gl = (acc[db][r] * w.x + acc[db + 2][r] * w.y) * a.scale;
+          const float gh = (acc[db + 2][r] * w.x - acc[db][r] * w.y) * a.scale;
+          atomicAdd(&s_g[a.kidx[ir + dl / C] * C + dl % C], gl);
+          atomicAdd(&s_g[a.kidx[ir + dh / C] * C + dh % C], gh);
+        }
+    } else {
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int d = 32 * db + 8 * (r >> 2) + 4 * hh + (r & 3);
+          atomicAdd(&s_g[a.vidx[ir + d / C] * C + d % C], acc[db][r]);
+        }
+    }
+  }
+  __syncthreads();
+  float* g = KPASS ? a.dkcb : a.dvcb;
+  for (int e = threadIdx.x; e < a.K * C; e += blockDim.x) {
+    const int r = e / C, i = e - r * C;
+    if (s_g[e] != 0.f) unsafeAtomicAdd(&g[cbo + (int64_t)r * a.G + i * a.T_c + m], s_g[e]);
+  }
+}
+
 // delta[row] = sum_d dout[row][d] * out[row][d]; one wave per row.
 __global__ __launch_bounds__(256) void prefill_delta_kernel(const float* __restrict__ out,
                                                             const float* __restrict__ dout,
@@ -551,177 +615,6 @@ __global__ __launch_bounds__(256) void prefill_zero_kernel(float* __restrict__ p
   if (e < n) p[e] = 0.f;
 }
 
-// Key-side backward: for 64 tokens of one (b, q-head, step), accumulate the
-// gradients of their rotated keys and values over every query that sees
-// them, undo the rotation, and add them into the codeword entries the
-// tokens use (fp32 atomics).  Grid (token tiles of 64, H_q, B * n_steps).
-template <int C>
-__global__ __launch_bounds__(256) void prefill_bwd_kv_kernel(PrefillArgs a) {
-  extern __shared__ float s_gd[];                    // [2][K*C] gradient accumulators
-  __shared__ __attribute__((aligned(16))) float s_q[kTile][kLds];
-  __shared__ __attribute__((aligned(16))) float s_do[kTile][kLds];
-  __shared__ float s_l2[kTile], s_dl[kTile];
-  const int row = threadIdx.x >> 2, sub = threadIdx.x & 3;
-  const int hq = blockIdx.y, h = hq / a.gqa;
-  const int b = blockIdx.z / a.n_steps, tl = blockIdx.z - b * a.n_steps;
-  const int t = a.step0 + tl, beta = t / a.T_c, m = t - beta * a.T_c;
-  const int k0 = blockIdx.x * kRows;
-  const int j = k0 + row;
-  const bool vk = j < a.N;
-  float* s_gk = s_gd;
-  float* s_gv = s_gd + 256 * C;
-  for (int e = threadIdx.x; e < 2 * 256 * C; e += blockDim.x) s_gd[e] = 0.f;
-  __syncthreads();
-
-  // this lane's key (rotated) and value channels, straight from the codebooks;
-  // the index bytes of its channels are kept (NB per half) for the scatter
-  constexpr int NB = C >= 16 ? 1 : 16 / C;
-  const int64_t ir = ((((int64_t)b * a.H + h) * a.n_blk + beta) * a.N_cap + (vk ? j : 0)) * (kPD / C);
-  const int64_t cbo = ((int64_t)h * a.n_blk + beta) * a.K * a.G;
-  const int pos = a.n_s + (vk ? j : 0);
-  const float2* rp = reinterpret_cast<const float2*>(a.rope + ((int64_t)pos * kPH + 16 * sub) * 2);
-  int ikl[NB], ikh[NB], ivl[NB], ivh[NB];
-#pragma unroll
-  for (int u = 0; u < NB; ++u) {
-    const int cl = (16 * sub) / C + u, ch = (kPH + 16 * sub) / C + u;
-    ikl[u] = a.kidx[ir + cl];
-    ikh[u] = a.kidx[ir + ch];
-    ivl[u] = a.vidx[ir + cl];
-    ivh[u] = a.vidx[ir + ch];
-  }
-  Row32 kr, vv, dk, dv;
-#pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const int u = e / C < NB ? e / C : NB - 1, i = (16 * sub + e) % C;
-    // an index byte >= K (never written by the encode) reads the last entry
-    const int rkl = min(ikl[u], a.K - 1), rkh = min(ikh[u], a.K - 1);
-    const int rvl = min(ivl[u], a.K - 1), rvh = min(ivh[u], a.K - 1);
-    const float xl = bf16_to_f32(a.kcb[cbo + (int64_t)rkl * a.G + i * a.T_c + m]);
-    const float xh = bf16_to_f32(a.kcb[cbo + (int64_t)rkh * a.G + i * a.T_c + m]);
-    vv.lo[e] = bf16_to_f32(a.vcb[cbo + (int64_t)rvl * a.G + i * a.T_c + m]);
-    vv.hi[e] = bf16_to_f32(a.vcb[cbo + (int64_t)rvh * a.G + i * a.T_c + m]);
-    const float2 w = rp[e];
-    kr.lo[e] = xl * w.x - xh * w.y;
-    kr.hi[e] = xh * w.x + xl * w.y;
-  }
-  zero_row(dk);
-  zero_row(dv);
-  const float sc2 = a.scale * kLog2e;
-
-  // queries i >= k0 (earlier ones see none of these tokens)
-  for (int i0 = k0; i0 < a.N; i0 += kTile) {
-    const int cnt = min(kTile, a.N - i0);
-    __syncthreads();
-    {
-      // stage q (scaled to base-2 scores), dout, lse (base 2), delta
-      const int r = threadIdx.x >> 3, part = threadIdx.x & 7;
-      if (r < cnt) {
-        const int64_t qr = (((int64_t)b * a.Hq + hq) * a.n_steps + tl) * a.N + i0 + r;
-        const float4* qs = reinterpret_cast<const float4*>(a.q + qr * kPD + 16 * part);
-        const float4* ds = reinterpret_cast<const float4*>(a.dout + qr * kPD + 16 * part);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const float4 x = qs[u];
-          *reinterpret_cast<float4*>(&s_q[r][16 * part + 4 * u]) = make_float4(x.x * sc2, x.y * sc2, x.z * sc2, x.w * sc2);
-          *reinterpret_cast<float4*>(&s_do[r][16 * part + 4 * u]) = ds[u];
-        }
-        if (part == 0) {
-          s_l2[r] = a.lse[qr] * kLog2e;
-          s_dl[r] = a.delta[qr];
-        }
-      }
-    }
-    __syncthreads();
-#pragma unroll 1
-    for (int qq = 0; qq < cnt; ++qq) {
-      const int i = i0 + qq;
-      const float s = quad_sum(dot_lds(kr, s_q[qq], sub));
-      const float dp = quad_sum(dot_lds(vv, s_do[qq], sub));
-      // masked pairs contribute zero (no branch: the accumulators stay in place)
-      const float p = (vk && j <= i) ? __builtin_amdgcn_exp2f(s - s_l2[qq]) : 0.f;
-      lds_reload();
-      axpy_lds(dv, p, s_do[qq], sub);
-      // d score / d rotated key = scale * q; s_q holds scale * log2(e) * q
-      axpy_lds(dk, p * (dp - s_dl[qq]) * kLn2, s_q[qq], sub);
-    }
-  }
-  // undo the rotation (the table is read again) and scatter into the
-  // codeword entries
-  if (vk) {
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int u = e / C < NB ? e / C : NB - 1, i = (16 * sub + e) % C;
-      const float2 w = rp[e];
-      const float gl = dk.lo[e] * w.x + dk.hi[e] * w.y;
-      const float gh = dk.hi[e] * w.x - dk.lo[e] * w.y;
-      atomicAdd(&s_gk[ikl[u] * C + i], gl);
-      atomicAdd(&s_gk[ikh[u] * C + i], gh);
-      atomicAdd(&s_gv[ivl[u] * C + i], dv.lo[e]);
-      atomicAdd(&s_gv[ivh[u] * C + i], dv.hi[e]);
-    }
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < a.K * C; e += blockDim.x) {
-    const int r = e / C, i = e - r * C;
-    const int64_t o = cbo + (int64_t)r * a.G + i * a.T_c + m;
-    if (s_gk[e] != 0.f) unsafeAtomicAdd(&a.dkcb[o], s_gk[e]);
-    if (s_gv[e] != 0.f) unsafeAtomicAdd(&a.dvcb[o], s_gv[e]);
-  }
-}
-
-// Query-side backward: dq[b][hq][tl][i] = scale * sum_keys p (dp - delta) k_rot.
-template <int C>
-__global__ __launch_bounds__(256) void prefill_bwd_q_kernel(PrefillArgs a) {
-  extern __shared__ float s_cb[];
-  __shared__ __attribute__((aligned(16))) float s_k[kTile][kLds];
-  __shared__ __attribute__((aligned(16))) float s_v[kTile][kLds];
-  const int row = threadIdx.x >> 2, sub = threadIdx.x & 3;
-  const int hq = blockIdx.y, h = hq / a.gqa;
-  const int b = blockIdx.z / a.n_steps, tl = blockIdx.z - b * a.n_steps;
-  const int t = a.step0 + tl, beta = t / a.T_c, m = t - beta * a.T_c;
-  // the last query tiles attend the most tokens: dispatch them first
-  const int q0 = (gridDim.x - 1 - blockIdx.x) * kRows;
-  const int i = q0 + row;
-  const bool vq = i < a.N;
-  float* s_cbk = s_cb;
-  float* s_cbv = s_cb + 256 * C;
-  stage_codebooks<C>(a, h, beta, m, s_cbk, s_cbv);
-
-  const int64_t qr = (((int64_t)b * a.Hq + hq) * a.n_steps + tl) * a.N + (vq ? i : 0);
-  Row32 q, dov, dq;
-  load_row(q, a.q + qr * kPD, sub, a.scale * kLog2e);
-  load_row(dov, a.dout + qr * kPD, sub, 1.f);
-  zero_row(dq);
-  const float l2 = a.lse[qr] * kLog2e, dl = a.delta[qr];
-
-  auto consume = [&](int cnt, int jbase, bool causal) {
-    for (int kk = 0; kk < cnt; ++kk) {
-      const float s = quad_sum(dot_lds(q, s_k[kk], sub));
-      const float dp = quad_sum(dot_lds(dov, s_v[kk], sub));
-      const bool on = vq && !(causal && jbase + kk > i);
-      const float p = on ? __builtin_amdgcn_exp2f(s - l2) : 0.f;
-      lds_reload();
-      axpy_lds(dq, p * (dp - dl), s_k[kk], sub);
-    }
-  };
-  for (int j0 = 0; j0 < a.n_s; j0 += kTile) {
-    const int cnt = min(kTile, a.n_s - j0);
-    __syncthreads();
-    fill_tile<C>(a, b, h, t, beta, true, j0, cnt, s_cbk, s_cbv, s_k, s_v);
-    __syncthreads();
-    consume(cnt, 0, false);
-  }
-  const int jend = min(a.N, q0 + kRows);
-  for (int j0 = 0; j0 < jend; j0 += kTile) {
-    const int cnt = min(kTile, jend - j0);
-    __syncthreads();
-    fill_tile<C>(a, b, h, t, beta, false, j0, cnt, s_cbk, s_cbv, s_k, s_v);
-    __syncthreads();
-    consume(cnt, j0, true);
-  }
-  if (vq) store_row(dq, a.dq + qr * kPD, sub, a.scale);
-}
-
 hipError_t launch_fill_f32(float* p, int64_t n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(prefill_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, n);
@@ -736,11 +629,11 @@ hipError_t launch_rope_table_f32(float* tab, int n_pos, int D, double theta, hip
 
 template <int C>
 static hipError_t prefill_launch(const PrefillArgs& a, bool backward, hipStream_t s) {
-  const dim3 grid((a.N + kRows - 1) / kRows, a.Hq, a.B * a.n_steps);
   const size_t lds = (size_t)2 * 256 * C * sizeof(float);
   // dynamic LDS beyond the default allowance (C = 32 takes 64 KiB)
   for (const void* k : {reinterpret_cast<const void*>(&prefill_fwd_mfma_kernel<C>),
-                        reinterpret_cast<const void*>(&prefill_bwd_kv_kernel<C>),
+                        reinterpret_cast<const void*>(&prefill_bwd_kv_mfma_kernel<C, false>),
+                        reinterpret_cast<const void*>(&prefill_bwd_kv_mfma_kernel<C, true>),
                         reinterpret_cast<const void*>(&prefill_bwd_q_mfma_kernel<C>)}) {
     const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
@@ -756,7 +649,10 @@ static hipError_t prefill_launch(const PrefillArgs& a, bool backward, hipStream_
   const int64_t ncb = (int64_t)a.H * a.n_blk * a.K * a.G;
   hipLaunchKernelGGL(prefill_zero_kernel, dim3((unsigned)((ncb + 255) / 256)), dim3(256), 0, s, a.dkcb, ncb);
   hipLaunchKernelGGL(prefill_zero_kernel, dim3((unsigned)((ncb + 255) / 256)), dim3(256), 0, s, a.dvcb, ncb);
-  hipLaunchKernelGGL((prefill_bwd_kv_kernel<C>), grid, dim3(256), lds, s, a);
+  const dim3 gk((a.N + kMT - 1) / kMT, a.Hq, a.B * a.n_steps);
+  const size_t lds_g = (size_t)256 * C * sizeof(float);
+  hipLaunchKernelGGL((prefill_bwd_kv_mfma_kernel<C, false>), gk, dim3(256), lds_g, s, a);
+  hipLaunchKernelGGL((prefill_bwd_kv_mfma_kernel<C, true>), gk, dim3(256), lds_g, s, a);
   const dim3 gm((a.N + kMT - 1) / kMT, a.Hq, a.B * a.n_steps);
   hipLaunchKernelGGL((prefill_bwd_q_mfma_kernel<C>), gm, dim3(256), lds, s, a);
   return hipGetLastError();
