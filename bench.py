@@ -288,7 +288,7 @@ def workload5(args, torch, lv, cfg):
 
 # ----------------------------------------------------------------------------- fine-tuning workload
 
-FP32_VECTOR_PEAK_TFLOPS = 157.3    # published; packed-FP32 FMA (2 per lane per clock)
+FP32_MATRIX_PEAK_TFLOPS = 157.3    # published dense fp32 matrix-core rate
 
 
 def _oracle_vjp_sample(args):
@@ -360,10 +360,12 @@ def finetune_flow(args, torch, lv):
     bwd_tf = pairs * 8 * D / (bwd_ms * 1e-3) / 1e12
 
     if bwd_ms >= fwd_ms:
-        dom_name, dom_tf, dom_ms, dom_flop = ("loopvq_prefill_attn_backward (prefill_bwd_kv_kernel + "
-                                              "prefill_bwd_q_kernel + delta)", bwd_tf, bwd_ms, pairs * 8 * D)
+        dom_name, dom_tf, dom_ms, dom_flop = ("loopvq_prefill_attn_backward (prefill_bwd_kv_mfma_kernel V and K "
+                                              "passes + prefill_bwd_q_mfma_kernel + delta)", bwd_tf, bwd_ms,
+                                              pairs * 8 * D)
     else:
-        dom_name, dom_tf, dom_ms, dom_flop = "loopvq_prefill_attn (prefill_fwd_kernel)", fwd_tf, fwd_ms, pairs * 4 * D
+        dom_name, dom_tf, dom_ms, dom_flop = ("loopvq_prefill_attn (prefill_fwd_mfma_kernel)", fwd_tf, fwd_ms,
+                                              pairs * 4 * D)
 
     toy = gen_toy_stack(cfg, 0, "cuda", vocab=vocab, B=1)
     stack = ft.ToyLoopedStack(toy["Wq"], toy["Wo"], toy["Wu"], cfg.H_q, cfg.D, cfg.T, cfg.n_s, rope)
@@ -422,10 +424,12 @@ def finetune_flow(args, torch, lv):
         "config": {"workload": workload, "global_batch": 1, "seq_len": N + cfg.n_s,
                    "step": "loopvq_prefill_attn + loopvq_prefill_attn_backward over every loop step"},
         "forward": {"ms_per_call": fwd_ms, "tflops": fwd_tf, "flop_per_pair": 4 * D},
-        "backward": {"ms_per_call": bwd_ms, "tflops": bwd_tf, "flop_per_pair": 8 * D},
-        "roofline": {"kernel": dom_name, "bound": "alu", "achieved": dom_tf, "peak": FP32_VECTOR_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": dom_tf / FP32_VECTOR_PEAK_TFLOPS, "traffic": None,
-                     "algorithmic_flop_per_launch": dom_flop, "avg_launch_ms": dom_ms},
+        "backward": {"ms_per_call": bwd_ms, "tflops": bwd_tf, "flop_per_pair": 8 * D,
+                     "executed_flop_per_pair": 16 * D,
+                     "note": "S = QK^T is recomputed in each of the three backward kernels and dP in two"},
+        "roofline": {"kernel": dom_name, "bound": "mfma", "achieved": dom_tf, "peak": FP32_MATRIX_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": dom_tf / FP32_MATRIX_PEAK_TFLOPS, "traffic": None,
+                     "algorithmic_flop_per_launch": dom_flop, "avg_launch_ms": dom_ms, "dtype": "f32"},
         "iteration": {"ms": it_ms, "objective": Js,
                       "note": "re-encode K and V, toy stack forward over the rebuilt cache (4 compressed-attention "
                               "calls), KL against the precise run, backward, Adam (lr 1e-3)"},
