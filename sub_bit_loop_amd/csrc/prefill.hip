@@ -165,8 +165,9 @@ __device__ void fill_tile_mfma(const PrefillArgs& a, int b, int h, int t, int be
 template <int C>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefill_fwd_mfma_kernel(PrefillArgs a) {
   extern __shared__ float s_cb[];                    // [2][256*C] step slices
-  __shared__ __attribute__((aligned(16))) float s_k[kTile][kLds];
-  __shared__ __attribute__((aligned(16))) float s_v[kTile][kLds];
+  // two tile buffers: the next tile is staged while the current one is used
+  __shared__ __attribute__((aligned(16))) float s_k[2][kTile][kLds];
+  __shared__ __attribute__((aligned(16))) float s_v[2][kTile][kLds];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int hh = lane >> 5, col = lane & 31;
   const int hq = blockIdx.y, h = hq / a.gqa;
@@ -203,14 +204,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
   float mx = -INFINITY, l = 0.f;
 
-  auto consume = [&](int cnt, int j0, bool sinks) {
+  auto consume = [&](int cnt, int j0, bool sinks, int buf) {
     if (!sinks && qw0 + 31 < j0) return;             // every query of the wave precedes the tile
     f32x16_pf sacc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
 #pragma unroll
     for (int s4 = 0; s4 < 16; ++s4) {
-      const float4 kv = *reinterpret_cast<const float4*>(&s_k[col][hh * kPH + 4 * s4]);
+      const float4 kv = *reinterpret_cast<const float4*>(&s_k[buf][col][hh * kPH + 4 * s4]);
       sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(kv.x, qreg[4 * s4 + 0], sacc, 0, 0, 0);
       sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(kv.y, qreg[4 * s4 + 1], sacc, 0, 0, 0);
       sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(kv.z, qreg[4 * s4 + 2], sacc, 0, 0, 0);
@@ -245,27 +246,39 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 #pragma unroll
     for (int st = 0; st < 16; ++st) {
       const int kr = 8 * (st >> 2) + 4 * hh + (st & 3);
-      const float4 vv = *reinterpret_cast<const float4*>(&s_v[kr][col * 4]);
+      const float4 vv = *reinterpret_cast<const float4*>(&s_v[buf][kr][col * 4]);
       o[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv.x, sacc[st], o[0], 0, 0, 0);
       o[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv.y, sacc[st], o[1], 0, 0, 0);
       o[2] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv.z, sacc[st], o[2], 0, 0, 0);
       o[3] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv.w, sacc[st], o[3], 0, 0, 0);
     }
   };
-  for (int j0 = 0; j0 < a.n_s; j0 += kTile) {
-    const int cnt = min(kTile, a.n_s - j0);
-    __syncthreads();
-    fill_tile_mfma<C>(a, b, h, t, beta, true, j0, cnt, s_cbk, s_cbv, s_k, s_v);
-    __syncthreads();
-    consume(cnt, j0, true);
-  }
+  // tiles: the sinks first, then the tokens up to this workgroup's last query
   const int jend = min(a.N, q0 + kMT);
-  for (int j0 = 0; j0 < jend; j0 += kTile) {
-    const int cnt = min(kTile, jend - j0);
-    __syncthreads();
-    fill_tile_mfma<C>(a, b, h, t, beta, false, j0, cnt, s_cbk, s_cbv, s_k, s_v);
-    __syncthreads();
-    consume(cnt, j0, false);
+  const int ns_t = (a.n_s + kTile - 1) / kTile, ntl = ns_t + (jend + kTile - 1) / kTile;
+  auto info = [&](int k, bool& sinks, int& j0, int& cnt) {
+    sinks = k < ns_t;
+    j0 = kTile * (sinks ? k : k - ns_t);
+    cnt = min(kTile, (sinks ? a.n_s : jend) - j0);
+  };
+  __syncthreads();                                   // codebook slices staged
+  if (ntl > 0) {
+    bool sk;
+    int j0, cnt;
+    info(0, sk, j0, cnt);
+    fill_tile_mfma<C>(a, b, h, t, beta, sk, j0, cnt, s_cbk, s_cbv, s_k[0], s_v[0]);
+  }
+  __syncthreads();
+  for (int k = 0; k < ntl; ++k) {
+    bool sk;
+    int j0, cnt;
+    if (k + 1 < ntl) {
+      info(k + 1, sk, j0, cnt);
+      fill_tile_mfma<C>(a, b, h, t, beta, sk, j0, cnt, s_cbk, s_cbv, s_k[(k + 1) & 1], s_v[(k + 1) & 1]);
+    }
+    info(k, sk, j0, cnt);
+    consume(cnt, j0, sk, k & 1);
+    __syncthreads();                                 // tile k+1 staged, tile k no longer read
   }
   if (vq) {
     const float inv = l > 0.f ? 1.f / l : 0.f;
