@@ -62,6 +62,18 @@ def dequant_step_t(idx: torch.Tensor, cb: torch.Tensor, T_c: int, m: int) -> tor
     return e[:, :, m::T_c].reshape(idx.shape[0], -1)
 
 
+def tasq_inverse_t(z: torch.Tensor, w, perm, sigma_bar) -> torch.Tensor:
+    """Keys from the pre-transformed space (section 3.3, appendix B eq. 10):
+    k[..., p(d')] = z[..., d'] * sigma_bar / w[p(d')], differentiable in z.
+    z [..., P, D], w [D], perm [D] (transformed channel d' holds raw channel
+    perm[d']), sigma_bar [P]."""
+    p = torch.as_tensor(perm, dtype=torch.int64)
+    pinv = torch.argsort(p)
+    wv = torch.as_tensor(w, dtype=F64)
+    sg = torch.as_tensor(sigma_bar, dtype=F64)
+    return z[..., pinv] * sg[..., :, None] / wv[None, :]
+
+
 def causal_attention(q, k_tok, v_tok, sink_k, sink_v, theta: float = 1.0e4):
     """Attention of the N positions after the sinks over one step's cache.
 
@@ -86,13 +98,15 @@ def causal_attention(q, k_tok, v_tok, sink_k, sink_v, theta: float = 1.0e4):
 
 
 def compressed_attention(q, k_idx, v_idx, k_cb, v_cb, sink_k, sink_v, T_c: int,
-                         step0: int = 0, theta: float = 1.0e4):
+                         step0: int = 0, theta: float = 1.0e4, tasq=None):
     """All rows of the causal attention over the compressed cache.
 
     q [B, H_q, n_steps, N, D] (steps step0 ..), k_idx / v_idx [B, H_kv, n_blk,
     N, D/c] (int64), k_cb / v_cb [H_kv, n_blk, K, G], sink_k / sink_v
-    [B, H_kv, T, n_s, D].  Returns (o [B, H_q, n_steps, N, D], lse [B, H_q,
-    n_steps, N]); differentiable in q, k_cb and v_cb.
+    [B, H_kv, T, n_s, D].  tasq: None or (w [H_kv, D], perm [H_kv, D],
+    sigma_bar [B, N, T]) for keys coded in the pre-transformed space.
+    Returns (o [B, H_q, n_steps, N, D], lse [B, H_q, n_steps, N]);
+    differentiable in q, k_cb and v_cb.
     """
     B, H_q, n_steps, N, D = q.shape
     H_kv = k_cb.shape[0]
@@ -107,6 +121,8 @@ def compressed_attention(q, k_idx, v_idx, k_cb, v_cb, sink_k, sink_v, T_c: int,
                 t = step0 + tl
                 beta, m = divmod(t, T_c)
                 kq = dequant_step_t(k_idx[b, h, beta, :N], k_cb[h, beta], T_c, m)
+                if tasq is not None:
+                    kq = tasq_inverse_t(kq, tasq[0][h], tasq[1][h], tasq[2][b, :N, t])
                 vq = dequant_step_t(v_idx[b, h, beta, :N], v_cb[h, beta], T_c, m)
                 o, l = causal_attention(q[b, hq, tl], kq, vq, sink_k[b, h, t], sink_v[b, h, t], theta)
                 oh.append(o)
@@ -119,7 +135,7 @@ def compressed_attention(q, k_idx, v_idx, k_cb, v_cb, sink_k, sink_v, T_c: int,
 
 
 def attention_vjp(q, k_idx, v_idx, k_cb, v_cb, sink_k, sink_v, T_c: int, d_out,
-                  step0: int = 0, theta: float = 1.0e4):
+                  step0: int = 0, theta: float = 1.0e4, tasq=None):
     """Gradients of <d_out, o> with respect to q, k_cb and v_cb (backprop
     through dequant, RoPE and the softmax; the indices are constants).
     Returns (o, lse, d_q, d_k_cb, d_v_cb) in fp64."""
@@ -127,7 +143,7 @@ def attention_vjp(q, k_idx, v_idx, k_cb, v_cb, sink_k, sink_v, T_c: int, d_out,
     kc = torch.as_tensor(k_cb, dtype=F64).clone().requires_grad_(True)
     vc = torch.as_tensor(v_cb, dtype=F64).clone().requires_grad_(True)
     o, lse = compressed_attention(qv, k_idx, v_idx, kc, vc, torch.as_tensor(sink_k, dtype=F64),
-                                  torch.as_tensor(sink_v, dtype=F64), T_c, step0, theta)
+                                  torch.as_tensor(sink_v, dtype=F64), T_c, step0, theta, tasq)
     (o * torch.as_tensor(d_out, dtype=F64)).sum().backward()
     return o.detach(), lse.detach(), qv.grad, kc.grad, vc.grad
 

@@ -233,3 +233,44 @@ def test_reference_finetuning_lowers_the_objective():
     Js, kb, vb = ref.finetune_reference(toy, cache, kc, vc, T_c, iters=12, lr=1e-2)
     assert Js[-1] < Js[0]
     assert np.array_equal(ref.bf16_round(kb.numpy()), kb.numpy())
+
+
+def test_pretransformed_keys_in_the_attention():
+    rng = np.random.default_rng(13)
+    D, N, H = 16, 6, 1
+    z = rng.standard_normal((N, D))
+    w = rng.lognormal(0, 0.3, D)
+    perm = rng.permutation(D)
+    sig = rng.uniform(0.5, 2, N)
+    # the torch inverse equals the pinned numpy inverse, and undoes the forward
+    got = ref.tasq_inverse_t(torch.from_numpy(z), w, perm, sig).numpy()
+    assert np.allclose(got, ref.tasq_inverse(z, w, perm, sig), rtol=1e-15, atol=0)
+    k = rng.standard_normal((N, D))
+    back = ref.tasq_inverse_t(torch.from_numpy(ref.tasq_forward(k, w, perm, sig)), w, perm, sig).numpy()
+    assert np.allclose(back, k, rtol=1e-14, atol=1e-14)
+    # identity transform gives the plain attention exactly
+    B, H_q, T, T_c, n_s, K, G = 1, 2, 4, 4, 2, 8, 8
+    cache, kc, vc, ki, vi = _codeword_cache(14, B, H, T, T_c, N, D, n_s, K, G)
+    q = torch.from_numpy(rng.standard_normal((B, H_q, 2, N, D)))
+    args = (q, ki, vi, kc, vc, cache["sink_k"], cache["sink_v"], T_c, 1)
+    o0, l0 = ref.compressed_attention(*args)
+    ident = (np.ones((H, D)), np.tile(np.arange(D), (H, 1)), np.ones((B, N, T)))
+    o1, l1 = ref.compressed_attention(*args, tasq=ident)
+    assert torch.equal(o0, o1) and torch.equal(l0, l1)
+    # gradients through the inverse transform match central differences
+    tq = (rng.lognormal(0, 0.3, (H, D)), np.stack([rng.permutation(D) for _ in range(H)]),
+          rng.uniform(0.5, 2, (B, N, T)))
+    dout = torch.from_numpy(rng.standard_normal(q.shape))
+    _, _, _, dk, _ = ref.attention_vjp(q, ki, vi, kc, vc, cache["sink_k"], cache["sink_v"], T_c, dout, 1,
+                                       tasq=tq)
+
+    def loss(cb):
+        o, _ = ref.compressed_attention(q, ki, vi, cb, vc, cache["sink_k"], cache["sink_v"], T_c, 1, tasq=tq)
+        return float((o * dout).sum())
+    r = int(ki[0, 0, 0, 0, 0])
+    for u in range(3):
+        cp, cm = kc.clone(), kc.clone()
+        cp[0, 0, r, u] += 1e-6
+        cm[0, 0, r, u] -= 1e-6
+        fd = (loss(cp) - loss(cm)) / 2e-6
+        assert abs(fd - dk[0, 0, r, u].item()) <= 1e-6 * max(abs(fd), 1e-3)
