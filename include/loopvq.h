@@ -268,13 +268,17 @@ loopvq_status loopvq_rope_table_f32(float theta, int32_t D, int32_t n_pos, float
  * m = t % T_c: query i (i < N) sits at position n_s + i and attends to the
  * n_s bf16 sinks sink_k[b][h][t][s] (position s) and to the tokens j <= i,
  * whose channel q*c + i' is k_cb[h][beta][k_idx[b][h][beta][j][q]][i'*T_c + m]
- * (section 3.1 eq. 5) at position n_s + j; keys are rotated (RoPE) at their
- * positions, values come from v_idx / v_cb / sink_v; scale 1/sqrt(D).
+ * (section 3.1 eq. 5) at position n_s + j (with pt, the inverse
+ * pre-transform is applied first: raw channel p(d') is coordinate d' times
+ * sigma[b][j][t] / w[h][p(d')]); keys are rotated (RoPE) at their positions,
+ * values come from v_idx / v_cb / sink_v; scale 1/sqrt(D).
  *   q          device fp32 [B][n_q_heads][n_steps][N][D], already rotated
  *   k_idx, v_idx  device uint8 [B][n_kv_heads][n_blk][N_cap][D/c]
  *   k_cb, v_cb device bf16 [n_kv_heads][n_blk][K][G]
  *   sink_k, sink_v  device bf16 [B][n_kv_heads][T][n_s][D], pre-RoPE; may be
  *              NULL when n_s == 0
+ *   pt         keys' pre-transform (reads w, perm and the sigma the encode
+ *              wrote for tokens 0..N-1) or NULL
  *   rope_table device fp32 table of loopvq_rope_table_f32 with
  *              n_pos >= n_s + N positions
  *   out        device fp32 [B][n_q_heads][n_steps][N][D], written
@@ -287,8 +291,8 @@ loopvq_status loopvq_rope_table_f32(float theta, int32_t D, int32_t n_pos, float
 loopvq_status loopvq_prefill_attn(const loopvq_geom* g, const float* q, int32_t step0, int32_t n_steps,
                                   int32_t B, int32_t N, const uint8_t* k_idx, const uint8_t* v_idx,
                                   int32_t N_cap, const void* k_cb, const void* v_cb, const void* sink_k,
-                                  const void* sink_v, int32_t n_s, const float* rope_table, int32_t n_pos,
-                                  float* out, float* lse, void* stream);
+                                  const void* sink_v, int32_t n_s, const loopvq_pretransform* pt,
+                                  const float* rope_table, int32_t n_pos, float* out, float* lse, void* stream);
 
 /* loopvq_prefill_attn_backward_workspace -- bytes of scratch the backward
  * needs: B * n_q_heads * n_steps * N floats. */
@@ -301,7 +305,8 @@ loopvq_status loopvq_prefill_attn_backward_workspace(const loopvq_geom* g, int32
  *   d_k_cb, d_v_cb  device fp32 [n_kv_heads][n_blk][K][G], overwritten with
  *              the gradient with respect to the bf16 codebook entries the
  *              forward read (summed over every batch entry, q-head, step and
- *              token of the call; keys pass back through the rotation)
+ *              token of the call; keys pass back through the rotation and,
+ *              with pt, the inverse pre-transform)
  *   workspace  device scratch of loopvq_prefill_attn_backward_workspace()
  *              bytes, 16-byte aligned
  * Alignment: as the forward, plus out, d_out and d_q 16-byte aligned.
@@ -313,9 +318,9 @@ loopvq_status loopvq_prefill_attn_backward(const loopvq_geom* g, const float* q,
                                            int32_t n_steps, int32_t B, int32_t N, const uint8_t* k_idx,
                                            const uint8_t* v_idx, int32_t N_cap, const void* k_cb,
                                            const void* v_cb, const void* sink_k, const void* sink_v,
-                                           int32_t n_s, const float* rope_table, int32_t n_pos,
-                                           const float* out, const float* lse, const float* d_out, float* d_q,
-                                           float* d_k_cb, float* d_v_cb, void* workspace,
+                                           int32_t n_s, const loopvq_pretransform* pt, const float* rope_table,
+                                           int32_t n_pos, const float* out, const float* lse, const float* d_out,
+                                           float* d_q, float* d_k_cb, float* d_v_cb, void* workspace,
                                            size_t workspace_bytes, void* stream);
 
 /* Thread-local text of the last non-OK status ("" if none). */

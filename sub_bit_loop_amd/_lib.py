@@ -68,12 +68,12 @@ def lib():
     L.loopvq_kmeans_finalize.restype = ctypes.c_int
     L.loopvq_rope_table_f32.argtypes = [ctypes.c_float, I32, I32, P, P]
     L.loopvq_rope_table_f32.restype = ctypes.c_int
-    L.loopvq_prefill_attn.argtypes = [GP, P, I32, I32, I32, I32, P, P, I32, P, P, P, P, I32, P, I32, P, P, P]
+    L.loopvq_prefill_attn.argtypes = [GP, P, I32, I32, I32, I32, P, P, I32, P, P, P, P, I32, PTP, P, I32, P, P, P]
     L.loopvq_prefill_attn.restype = ctypes.c_int
     L.loopvq_prefill_attn_backward_workspace.argtypes = [GP, I32, I32, I32, I32, ctypes.POINTER(SZ)]
     L.loopvq_prefill_attn_backward_workspace.restype = ctypes.c_int
-    L.loopvq_prefill_attn_backward.argtypes = [GP, P, I32, I32, I32, I32, P, P, I32, P, P, P, P, I32, P, I32,
-                                               P, P, P, P, P, P, P, SZ, P]
+    L.loopvq_prefill_attn_backward.argtypes = [GP, P, I32, I32, I32, I32, P, P, I32, P, P, P, P, I32, PTP, P,
+                                               I32, P, P, P, P, P, P, P, SZ, P]
     L.loopvq_prefill_attn_backward.restype = ctypes.c_int
     L.loopvq_last_error.argtypes = []
     L.loopvq_last_error.restype = ctypes.c_char_p

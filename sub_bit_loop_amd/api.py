@@ -225,11 +225,12 @@ def _prefill_common(q, k_idx, v_idx, k_cb, v_cb, sink_k, sink_v, rope):
 
 
 def prefill_attn(g: Geom, q, k_idx, v_idx, k_cb, v_cb, sink_k, sink_v, rope, step0=0, out=None, lse=None,
-                 stream=None):
+                 pt=None, stream=None):
     """Causal attention of the N positions after the sinks over the compressed cache.
     q fp32 [B][Hq][n_steps][N][D] (post-RoPE, query i at position n_s + i); k_idx/v_idx uint8
     [B][H][n_blk][N_cap][D/c]; k_cb/v_cb bf16 [H][n_blk][K][G]; sinks bf16 [B][H][T][n_s][D] or
-    None; rope fp32 table from rope_table_f32().  Returns (out fp32 like q, lse fp32 [B][Hq][n_steps][N])."""
+    None; rope fp32 table from rope_table_f32(); pt the keys' pre-transform (pretransform()) or None.
+    Returns (out fp32 like q, lse fp32 [B][Hq][n_steps][N])."""
     n_s = _prefill_common(q, k_idx, v_idx, k_cb, v_cb, sink_k, sink_v, rope)
     B, Hq, n_steps, N, D = q.shape
     if out is None:
@@ -238,13 +239,13 @@ def prefill_attn(g: Geom, q, k_idx, v_idx, k_cb, v_cb, sink_k, sink_v, rope, ste
         lse = torch.empty((B, Hq, n_steps, N), dtype=torch.float32, device=q.device)
     check(_lib.lib().loopvq_prefill_attn(
         ctypes.byref(g), _ptr(q), step0, n_steps, B, N, _ptr(k_idx), _ptr(v_idx), k_idx.shape[3], _ptr(k_cb),
-        _ptr(v_cb), _ptr(sink_k), _ptr(sink_v), n_s, _ptr(rope), rope.shape[0], _ptr(out), _ptr(lse),
-        _stream(stream)))
+        _ptr(v_cb), _ptr(sink_k), _ptr(sink_v), n_s, ctypes.byref(pt) if pt is not None else None, _ptr(rope),
+        rope.shape[0], _ptr(out), _ptr(lse), _stream(stream)))
     return out, lse
 
 
 def prefill_attn_backward(g: Geom, q, k_idx, v_idx, k_cb, v_cb, sink_k, sink_v, rope, out, lse, d_out,
-                          step0=0, d_q=None, d_k_cb=None, d_v_cb=None, workspace=None, stream=None):
+                          step0=0, d_q=None, d_k_cb=None, d_v_cb=None, workspace=None, pt=None, stream=None):
     """Gradients of prefill_attn: returns (d_q fp32 like q, d_k_cb, d_v_cb fp32 [H][n_blk][K][G]).
     The codebook gradients are overwritten (sums over every q-head, step and token in the call)."""
     n_s = _prefill_common(q, k_idx, v_idx, k_cb, v_cb, sink_k, sink_v, rope)
@@ -266,7 +267,7 @@ def prefill_attn_backward(g: Geom, q, k_idx, v_idx, k_cb, v_cb, sink_k, sink_v, 
         workspace = torch.empty(max(need.value, 16), dtype=torch.uint8, device=q.device)
     check(_lib.lib().loopvq_prefill_attn_backward(
         ctypes.byref(g), _ptr(q), step0, n_steps, B, N, _ptr(k_idx), _ptr(v_idx), k_idx.shape[3], _ptr(k_cb),
-        _ptr(v_cb), _ptr(sink_k), _ptr(sink_v), n_s, _ptr(rope), rope.shape[0], _ptr(out), _ptr(lse),
-        _ptr(d_out), _ptr(d_q), _ptr(d_k_cb), _ptr(d_v_cb), _ptr(workspace),
+        _ptr(v_cb), _ptr(sink_k), _ptr(sink_v), n_s, ctypes.byref(pt) if pt is not None else None, _ptr(rope),
+        rope.shape[0], _ptr(out), _ptr(lse), _ptr(d_out), _ptr(d_q), _ptr(d_k_cb), _ptr(d_v_cb), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
     return d_q, d_k_cb, d_v_cb

@@ -89,6 +89,10 @@ struct PrefillArgs {
   float* dkcb;                // backward: fp32 [H][n_blk][K][G]
   float* dvcb;
   float* delta;               // backward scratch: [B][Hq][n_steps][N]
+  const float* w;             // keys' pre-transform (or null): w [H][D], perm [H][D],
+  const int16_t* perm;        //   sigma fp16 [B][sig_cap][T]
+  const uint16_t* sigma;
+  int32_t sig_cap;
   int32_t B, H, Hq, T, T_c, n_blk, K, G, N, N_cap, n_s, step0, n_steps, gqa;
   float scale;                // 1 / sqrt(D)
 };

@@ -524,8 +524,8 @@ loopvq_status loopvq_rope_table_f32(float theta, int32_t D, int32_t n_pos, float
 static loopvq_status prefill_args(const loopvq_geom* g, const float* q, int32_t step0, int32_t n_steps,
                                   int32_t B, int32_t N, const uint8_t* k_idx, const uint8_t* v_idx,
                                   int32_t N_cap, const void* k_cb, const void* v_cb, const void* sink_k,
-                                  const void* sink_v, int32_t n_s, const float* rope_table, int32_t n_pos,
-                                  loopvq::PrefillArgs& a) {
+                                  const void* sink_v, int32_t n_s, const loopvq_pretransform* pt,
+                                  const float* rope_table, int32_t n_pos, loopvq::PrefillArgs& a) {
   loopvq_status st = check_decode_shape(g, B, N, step0, n_steps);
   if (st != LOOPVQ_OK) return st;
   if (n_s < 0) return fail(LOOPVQ_EINVAL, "n_s=%d must be >= 0", n_s);
@@ -539,7 +539,17 @@ static loopvq_status prefill_args(const loopvq_geom* g, const float* q, int32_t 
   }
   for (const void* p : {(const void*)q, (const void*)rope_table, sink_k, sink_v})
     if (reinterpret_cast<uintptr_t>(p) % 16) return fail(LOOPVQ_EINVAL, "q, rope_table and sinks must be 16-byte aligned");
+  if (pt) {
+    st = check_pt(pt, B, N, false);
+    if (st != LOOPVQ_OK) return st;
+  }
   a = loopvq::PrefillArgs{};
+  if (pt) {
+    a.w = pt->w;
+    a.perm = pt->perm;
+    a.sigma = static_cast<const uint16_t*>(pt->sigma);
+    a.sig_cap = pt->N_cap;
+  }
   a.q = q;
   a.kidx = k_idx;
   a.vidx = v_idx;
@@ -569,12 +579,12 @@ static loopvq_status prefill_args(const loopvq_geom* g, const float* q, int32_t 
 loopvq_status loopvq_prefill_attn(const loopvq_geom* g, const float* q, int32_t step0, int32_t n_steps,
                                   int32_t B, int32_t N, const uint8_t* k_idx, const uint8_t* v_idx,
                                   int32_t N_cap, const void* k_cb, const void* v_cb, const void* sink_k,
-                                  const void* sink_v, int32_t n_s, const float* rope_table, int32_t n_pos,
-                                  float* out, float* lse, void* stream) {
+                                  const void* sink_v, int32_t n_s, const loopvq_pretransform* pt,
+                                  const float* rope_table, int32_t n_pos, float* out, float* lse, void* stream) {
   g_err[0] = 0;
   loopvq::PrefillArgs a;
   loopvq_status st = prefill_args(g, q, step0, n_steps, B, N, k_idx, v_idx, N_cap, k_cb, v_cb, sink_k, sink_v,
-                                  n_s, rope_table, n_pos, a);
+                                  n_s, pt, rope_table, n_pos, a);
   if (st != LOOPVQ_OK) return st;
   if (B == 0 || N == 0) return LOOPVQ_OK;
   if (!out || !lse) return fail(LOOPVQ_EINVAL, "out and lse must not be NULL");
@@ -600,14 +610,14 @@ loopvq_status loopvq_prefill_attn_backward(const loopvq_geom* g, const float* q,
                                            int32_t n_steps, int32_t B, int32_t N, const uint8_t* k_idx,
                                            const uint8_t* v_idx, int32_t N_cap, const void* k_cb,
                                            const void* v_cb, const void* sink_k, const void* sink_v,
-                                           int32_t n_s, const float* rope_table, int32_t n_pos,
-                                           const float* out, const float* lse, const float* d_out, float* d_q,
-                                           float* d_k_cb, float* d_v_cb, void* workspace,
+                                           int32_t n_s, const loopvq_pretransform* pt, const float* rope_table,
+                                           int32_t n_pos, const float* out, const float* lse, const float* d_out,
+                                           float* d_q, float* d_k_cb, float* d_v_cb, void* workspace,
                                            size_t workspace_bytes, void* stream) {
   g_err[0] = 0;
   loopvq::PrefillArgs a;
   loopvq_status st = prefill_args(g, q, step0, n_steps, B, N, k_idx, v_idx, N_cap, k_cb, v_cb, sink_k, sink_v,
-                                  n_s, rope_table, n_pos, a);
+                                  n_s, pt, rope_table, n_pos, a);
   if (st != LOOPVQ_OK) return st;
   if (!d_k_cb || !d_v_cb) return fail(LOOPVQ_EINVAL, "NULL codebook gradient");
   if (B > 0 && N > 0 && (!out || !lse || !d_out || !d_q)) return fail(LOOPVQ_EINVAL, "NULL tensor pointer");

@@ -77,13 +77,34 @@ __global__ __launch_bounds__(256) void rope_table_f32_kernel(float* tab, int n_p
 typedef float f32x16_pf __attribute__((ext_vector_type(16)));
 constexpr int kMT = 128;              // queries per workgroup (4 waves x 32)
 
+// Keys coded in the pre-transformed space (section 3.3, appendix B eq. 10):
+// raw channel d of a key is coordinate p^-1(d) of the rebuilt vector times
+// sigma / w[d].  s_pinv[d] = p^-1(d) (identity without a pre-transform; any
+// perm input stays in bounds), s_rw[d] = 1 / w[d].  Called by every thread.
+__device__ void stage_pretransform(const PrefillArgs& a, int h, int* s_pinv, float* s_rw) {
+  for (int e = threadIdx.x; e < kPD; e += blockDim.x) {
+    s_pinv[e] = e;
+    s_rw[e] = 1.f / a.w[h * kPD + e];
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < kPD; e += blockDim.x) s_pinv[a.perm[h * kPD + e] & (kPD - 1)] = e;
+}
+
+// sigma of token j at step t (pre-transformed keys only)
+__device__ __forceinline__ float key_sigma(const PrefillArgs& a, int b, int j, int t) {
+  const uint16_t hb = a.sigma[((int64_t)b * a.sig_cap + j) * a.T + t];
+  _Float16 hv;
+  __builtin_memcpy(&hv, &hb, 2);
+  return (float)hv;
+}
+
 // Stage cnt keys (rotated) and values for the matrix-core kernels: keys
 // de-interleaved into s_k; values block-interleaved into s_v (V_DEINT: like
 // the keys instead); s_kb, when given, gets a block-interleaved copy of the keys.
-template <int C, bool V_DEINT = false>
+template <int C, bool PT, bool V_DEINT = false>
 __device__ void fill_tile_mfma(const PrefillArgs& a, int b, int h, int t, int beta, bool sinks, int j0, int cnt,
-                               const float* s_cbk, const float* s_cbv, float (*s_k)[kLds], float (*s_v)[kLds],
-                               float (*s_kb)[kLds] = nullptr) {
+                               const float* s_cbk, const float* s_cbv, const int* s_pinv, const float* s_rw,
+                               float (*s_k)[kLds], float (*s_v)[kLds], float (*s_kb)[kLds] = nullptr) {
   const int kk = threadIdx.x >> 3, fs = threadIdx.x & 7;
   float klo[8], khi[8], vlo[8], vhi[8];
   if (kk < cnt) {
@@ -110,11 +131,18 @@ __device__ void fill_tile_mfma(const PrefillArgs& a, int b, int h, int t, int be
       const int64_t ir = ((((int64_t)b * a.H + h) * a.n_blk + beta) * a.N_cap + j) * (kPD / C);
       const uint8_t* kr = a.kidx + ir;
       const uint8_t* vr = a.vidx + ir;
+      const float sg = PT ? key_sigma(a, b, j, t) : 1.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int dl = 8 * fs + e, dh = kPH + 8 * fs + e;
-        klo[e] = s_cbk[kr[dl / C] * C + dl % C];
-        khi[e] = s_cbk[kr[dh / C] * C + dh % C];
+        if constexpr (PT) {
+          const int zl = s_pinv[dl], zh = s_pinv[dh];
+          klo[e] = s_cbk[kr[zl / C] * C + zl % C] * (sg * s_rw[dl]);
+          khi[e] = s_cbk[kr[zh / C] * C + zh % C] * (sg * s_rw[dh]);
+        } else {
+          klo[e] = s_cbk[kr[dl / C] * C + dl % C];
+          khi[e] = s_cbk[kr[dh / C] * C + dh % C];
+        }
         vlo[e] = s_cbv[vr[dl / C] * C + dl % C];
         vhi[e] = s_cbv[vr[dh / C] * C + dh % C];
       }
@@ -162,12 +190,14 @@ __device__ void fill_tile_mfma(const PrefillArgs& a, int b, int h, int t, int be
   }
 }
 
-template <int C>
+template <int C, bool PT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefill_fwd_mfma_kernel(PrefillArgs a) {
   extern __shared__ float s_cb[];                    // [2][256*C] step slices
   // two tile buffers: the next tile is staged while the current one is used
   __shared__ __attribute__((aligned(16))) float s_k[2][kTile][kLds];
   __shared__ __attribute__((aligned(16))) float s_v[2][kTile][kLds];
+  __shared__ int s_pinv[kPD];
+  __shared__ float s_rw[kPD];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int hh = lane >> 5, col = lane & 31;
   const int hq = blockIdx.y, h = hq / a.gqa;
@@ -181,6 +211,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   float* s_cbk = s_cb;
   float* s_cbv = s_cb + 256 * C;
   stage_codebooks<C>(a, h, beta, m, s_cbk, s_cbv);
+  if constexpr (PT) stage_pretransform(a, h, s_pinv, s_rw);
 
   // B operand of S^T: qreg[s] = q[i][2s + hh], scaled to base-2 scores
   const int64_t qrow = ((((int64_t)b * a.Hq + hq) * a.n_steps + tl) * a.N + (vq ? i : 0)) * kPD;
@@ -266,7 +297,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     bool sk;
     int j0, cnt;
     info(0, sk, j0, cnt);
-    fill_tile_mfma<C>(a, b, h, t, beta, sk, j0, cnt, s_cbk, s_cbv, s_k[0], s_v[0]);
+    fill_tile_mfma<C, PT>(a, b, h, t, beta, sk, j0, cnt, s_cbk, s_cbv, s_pinv, s_rw, s_k[0], s_v[0]);
   }
   __syncthreads();
   for (int k = 0; k < ntl; ++k) {
@@ -274,7 +305,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     int j0, cnt;
     if (k + 1 < ntl) {
       info(k + 1, sk, j0, cnt);
-      fill_tile_mfma<C>(a, b, h, t, beta, sk, j0, cnt, s_cbk, s_cbv, s_k[(k + 1) & 1], s_v[(k + 1) & 1]);
+      fill_tile_mfma<C, PT>(a, b, h, t, beta, sk, j0, cnt, s_cbk, s_cbv, s_pinv, s_rw, s_k[(k + 1) & 1], s_v[(k + 1) & 1]);
     }
     info(k, sk, j0, cnt);
     consume(cnt, j0, sk, k & 1);
@@ -298,13 +329,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 // of 32 keys, S^T = K_rot Q^T and dP^T = V dO^T (keys on rows), dS^T = P^T
 // (dP^T - delta) with P^T = exp(S^T - lse), and dQ^T += K_rot^T dS^T, whose B
 // operand is the dS^T accumulator itself.
-template <int C>
+template <int C, bool PT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefill_bwd_q_mfma_kernel(
     PrefillArgs a) {
   extern __shared__ float s_cb[];
   __shared__ __attribute__((aligned(16))) float s_k[kTile][kLds];
   __shared__ __attribute__((aligned(16))) float s_v[kTile][kLds];
   __shared__ __attribute__((aligned(16))) float s_kb[kTile][kLds];
+  __shared__ int s_pinv[kPD];
+  __shared__ float s_rw[kPD];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int hh = lane >> 5, col = lane & 31;
   const int hq = blockIdx.y, h = hq / a.gqa;
@@ -317,6 +350,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   float* s_cbk = s_cb;
   float* s_cbv = s_cb + 256 * C;
   stage_codebooks<C>(a, h, beta, m, s_cbk, s_cbv);
+  if constexpr (PT) stage_pretransform(a, h, s_pinv, s_rw);
 
   const int64_t qr = (((int64_t)b * a.Hq + hq) * a.n_steps + tl) * a.N + (vq ? i : 0);
   const float qs = vq ? a.scale * kLog2e : 0.f;
@@ -385,7 +419,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   for (int j0 = 0; j0 < a.n_s; j0 += kTile) {
     const int cnt = min(kTile, a.n_s - j0);
     __syncthreads();
-    fill_tile_mfma<C, true>(a, b, h, t, beta, true, j0, cnt, s_cbk, s_cbv, s_k, s_v, s_kb);
+    fill_tile_mfma<C, PT, true>(a, b, h, t, beta, true, j0, cnt, s_cbk, s_cbv, s_pinv, s_rw, s_k, s_v, s_kb);
     __syncthreads();
     consume(cnt, j0, true);
   }
@@ -393,7 +427,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   for (int j0 = 0; j0 < jend; j0 += kTile) {
     const int cnt = min(kTile, jend - j0);
     __syncthreads();
-    fill_tile_mfma<C, true>(a, b, h, t, beta, false, j0, cnt, s_cbk, s_cbv, s_k, s_v, s_kb);
+    fill_tile_mfma<C, PT, true>(a, b, h, t, beta, false, j0, cnt, s_cbk, s_cbv, s_pinv, s_rw, s_k, s_v, s_kb);
     __syncthreads();
     consume(cnt, j0, false);
   }
@@ -451,17 +485,20 @@ __device__ __forceinline__ void stage_rows(const float* src, float sc, float (*d
 
 // This lane's token: rotated key channels kreg[s] = k_rot[2s + hh] and value
 // channels vreg[s] = v[2s + hh] (s < 64), from the codebooks.
-template <int C, bool WITH_V>
+template <int C, bool PT, bool WITH_V>
 __device__ __forceinline__ void token_regs(const PrefillArgs& a, int64_t ir, int64_t cbo, int m, int pos, int hh,
-                                           float (&kreg)[64], float (&vreg)[64]) {
+                                           float sg, const int* s_pinv, const float* s_rw, float (&kreg)[64],
+                                           float (&vreg)[64]) {
   const float2* rp = reinterpret_cast<const float2*>(a.rope + (int64_t)pos * kPH * 2);
 #pragma unroll
   for (int s = 0; s < 32; ++s) {
     const int dl = 2 * s + hh, dh = dl + kPH;
+    const int zl = PT ? s_pinv[dl] : dl, zh = PT ? s_pinv[dh] : dh;
+    const float fl = PT ? sg * s_rw[dl] : 1.f, fh = PT ? sg * s_rw[dh] : 1.f;
     // an index byte >= K (never written by the encode) reads the last entry
-    const int rl = min((int)a.kidx[ir + dl / C], a.K - 1), rh = min((int)a.kidx[ir + dh / C], a.K - 1);
-    const float xl = bf16_to_f32(a.kcb[cbo + (int64_t)rl * a.G + (dl % C) * a.T_c + m]);
-    const float xh = bf16_to_f32(a.kcb[cbo + (int64_t)rh * a.G + (dh % C) * a.T_c + m]);
+    const int rl = min((int)a.kidx[ir + zl / C], a.K - 1), rh = min((int)a.kidx[ir + zh / C], a.K - 1);
+    const float xl = bf16_to_f32(a.kcb[cbo + (int64_t)rl * a.G + (zl % C) * a.T_c + m]) * fl;
+    const float xh = bf16_to_f32(a.kcb[cbo + (int64_t)rh * a.G + (zh % C) * a.T_c + m]) * fh;
     const float2 w = rp[dl];
     kreg[s] = xl * w.x - xh * w.y;
     kreg[s + 32] = xh * w.x + xl * w.y;
@@ -473,7 +510,7 @@ __device__ __forceinline__ void token_regs(const PrefillArgs& a, int64_t ir, int
   }
 }
 
-template <int C, bool KPASS>
+template <int C, bool PT, bool KPASS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefill_bwd_kv_mfma_kernel(
     PrefillArgs a) {
   extern __shared__ float s_g[];                      // [256][C] gradient of this step's slice
@@ -481,6 +518,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   __shared__ __attribute__((aligned(16))) float s_b[kTile][kLds];      // V pass: dO blocks; K pass: q blocks
   __shared__ __attribute__((aligned(16))) float s_d[KPASS ? kTile : 1][kLds];   // K pass: dO, de-interleaved
   __shared__ float s_l2[kTile], s_dl[kTile];
+  __shared__ int s_pinv[kPD];
+  __shared__ float s_rw[kPD];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int hh = lane >> 5, col = lane & 31;
   const int hq = blockIdx.y, h = hq / a.gqa;
@@ -491,12 +530,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   const int j = kw0 + col;
   const bool vk = j < a.N;
   for (int e = threadIdx.x; e < 256 * C; e += blockDim.x) s_g[e] = 0.f;
+  if constexpr (PT) stage_pretransform(a, h, s_pinv, s_rw);
+  __syncthreads();
 
   const int64_t ir = ((((int64_t)b * a.H + h) * a.n_blk + beta) * a.N_cap + (vk ? j : 0)) * (kPD / C);
   const int64_t cbo = ((int64_t)h * a.n_blk + beta) * a.K * a.G;
   const int pos = a.n_s + (vk ? j : 0);
+  const float sg = PT ? key_sigma(a, b, vk ? j : 0, t) : 1.f;
   float kreg[64], vreg[64];
-  token_regs<C, KPASS>(a, ir, cbo, m, pos, hh, kreg, vreg);
+  token_regs<C, PT, KPASS>(a, ir, cbo, m, pos, hh, sg, s_pinv, s_rw, kreg, vreg);
   f32x16_pf acc[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db)
@@ -586,10 +628,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         for (int r = 0; r < 16; ++r) {
           const int dl = 32 * db + 8 * (r >> 2) + 4 * hh + (r & 3), dh = dl + kPH;
           const float2 w = rp[dl];
-          const float gl = (acc[db][r] * w.x + acc[db + 2][r] * w.y) * a.scale;
-          const float gh = (acc[db + 2][r] * w.x - acc[db][r] * w.y) * a.scale;
-          atomicAdd(&s_g[a.kidx[ir + dl / C] * C + dl % C], gl);
-          atomicAdd(&s_g[a.kidx[ir + dh / C] * C + dh % C], gh);
+          // undo the rotation, then the pre-transform's scale; raw channel d
+          // came from coordinate p^-1(d) of the rebuilt vector
+          const float gl = (acc[db][r] * w.x + acc[db + 2][r] * w.y) * (PT ? a.scale * sg * s_rw[dl] : a.scale);
+          const float gh = (acc[db + 2][r] * w.x - acc[db][r] * w.y) * (PT ? a.scale * sg * s_rw[dh] : a.scale);
+          const int zl = PT ? s_pinv[dl] : dl, zh = PT ? s_pinv[dh] : dh;
+          atomicAdd(&s_g[a.kidx[ir + zl / C] * C + zl % C], gl);
+          atomicAdd(&s_g[a.kidx[ir + zh / C] * C + zh % C], gh);
         }
     } else {
 #pragma unroll
@@ -640,20 +685,20 @@ hipError_t launch_rope_table_f32(float* tab, int n_pos, int D, double theta, hip
   return hipGetLastError();
 }
 
-template <int C>
+template <int C, bool PT>
 static hipError_t prefill_launch(const PrefillArgs& a, bool backward, hipStream_t s) {
   const size_t lds = (size_t)2 * 256 * C * sizeof(float);
   // dynamic LDS beyond the default allowance (C = 32 takes 64 KiB)
-  for (const void* k : {reinterpret_cast<const void*>(&prefill_fwd_mfma_kernel<C>),
-                        reinterpret_cast<const void*>(&prefill_bwd_kv_mfma_kernel<C, false>),
-                        reinterpret_cast<const void*>(&prefill_bwd_kv_mfma_kernel<C, true>),
-                        reinterpret_cast<const void*>(&prefill_bwd_q_mfma_kernel<C>)}) {
+  for (const void* k : {reinterpret_cast<const void*>(&prefill_fwd_mfma_kernel<C, PT>),
+                        reinterpret_cast<const void*>(&prefill_bwd_kv_mfma_kernel<C, PT, false>),
+                        reinterpret_cast<const void*>(&prefill_bwd_kv_mfma_kernel<C, PT, true>),
+                        reinterpret_cast<const void*>(&prefill_bwd_q_mfma_kernel<C, PT>)}) {
     const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
   if (!backward) {
     const dim3 gm((a.N + kMT - 1) / kMT, a.Hq, a.B * a.n_steps);
-    hipLaunchKernelGGL((prefill_fwd_mfma_kernel<C>), gm, dim3(256), lds, s, a);
+    hipLaunchKernelGGL((prefill_fwd_mfma_kernel<C, PT>), gm, dim3(256), lds, s, a);
     return hipGetLastError();
   }
   const int64_t rows = (int64_t)a.B * a.Hq * a.n_steps * a.N;
@@ -664,20 +709,25 @@ static hipError_t prefill_launch(const PrefillArgs& a, bool backward, hipStream_
   hipLaunchKernelGGL(prefill_zero_kernel, dim3((unsigned)((ncb + 255) / 256)), dim3(256), 0, s, a.dvcb, ncb);
   const dim3 gk((a.N + kMT - 1) / kMT, a.Hq, a.B * a.n_steps);
   const size_t lds_g = (size_t)256 * C * sizeof(float);
-  hipLaunchKernelGGL((prefill_bwd_kv_mfma_kernel<C, false>), gk, dim3(256), lds_g, s, a);
-  hipLaunchKernelGGL((prefill_bwd_kv_mfma_kernel<C, true>), gk, dim3(256), lds_g, s, a);
+  hipLaunchKernelGGL((prefill_bwd_kv_mfma_kernel<C, PT, false>), gk, dim3(256), lds_g, s, a);
+  hipLaunchKernelGGL((prefill_bwd_kv_mfma_kernel<C, PT, true>), gk, dim3(256), lds_g, s, a);
   const dim3 gm((a.N + kMT - 1) / kMT, a.Hq, a.B * a.n_steps);
-  hipLaunchKernelGGL((prefill_bwd_q_mfma_kernel<C>), gm, dim3(256), lds, s, a);
+  hipLaunchKernelGGL((prefill_bwd_q_mfma_kernel<C, PT>), gm, dim3(256), lds, s, a);
   return hipGetLastError();
+}
+
+template <int C>
+static hipError_t prefill_launch_pt(const PrefillArgs& a, bool backward, hipStream_t s) {
+  return a.perm ? prefill_launch<C, true>(a, backward, s) : prefill_launch<C, false>(a, backward, s);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, int C, bool backward, hipStream_t s) {
   switch (C) {
-    case 2: return prefill_launch<2>(a, backward, s);
-    case 4: return prefill_launch<4>(a, backward, s);
-    case 8: return prefill_launch<8>(a, backward, s);
-    case 16: return prefill_launch<16>(a, backward, s);
-    case 32: return prefill_launch<32>(a, backward, s);
+    case 2: return prefill_launch_pt<2>(a, backward, s);
+    case 4: return prefill_launch_pt<4>(a, backward, s);
+    case 8: return prefill_launch_pt<8>(a, backward, s);
+    case 16: return prefill_launch_pt<16>(a, backward, s);
+    case 32: return prefill_launch_pt<32>(a, backward, s);
     default: return hipErrorInvalidValue;
   }
 }

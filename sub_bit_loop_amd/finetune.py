@@ -27,10 +27,10 @@ class _CallState:
     """Per-call constants of CompressedAttention (indices, bf16 codebooks,
     sinks, RoPE table, step)."""
 
-    def __init__(self, g, k_idx, v_idx, k_cb, v_cb, sink_k, sink_v, rope, step):
+    def __init__(self, g, k_idx, v_idx, k_cb, v_cb, sink_k, sink_v, rope, step, pt=None):
         self.g, self.k_idx, self.v_idx = g, k_idx, v_idx
         self.k_cb, self.v_cb = k_cb, v_cb
-        self.sink_k, self.sink_v, self.rope, self.step = sink_k, sink_v, rope, step
+        self.sink_k, self.sink_v, self.rope, self.step, self.pt = sink_k, sink_v, rope, step, pt
 
 
 class CompressedAttention(torch.autograd.Function):
@@ -45,7 +45,7 @@ class CompressedAttention(torch.autograd.Function):
     def forward(ctx, q, k_master, v_master, st):
         q = q.contiguous()
         out, lse = api.prefill_attn(st.g, q, st.k_idx, st.v_idx, st.k_cb, st.v_cb, st.sink_k, st.sink_v,
-                                    st.rope, step0=st.step)
+                                    st.rope, step0=st.step, pt=st.pt)
         ctx.save_for_backward(q, out, lse)
         ctx.st = st
         return out
@@ -56,7 +56,7 @@ class CompressedAttention(torch.autograd.Function):
         st = ctx.st
         d_q, d_k, d_v = api.prefill_attn_backward(st.g, q, st.k_idx, st.v_idx, st.k_cb, st.v_cb, st.sink_k,
                                                   st.sink_v, st.rope, out, lse, d_out.contiguous(),
-                                                  step0=st.step)
+                                                  step0=st.step, pt=st.pt)
         return d_q, d_k, d_v, None
 
 
@@ -123,30 +123,32 @@ def kl_objective(logp, logits_q):
     return (logp.exp() * (logp - lq)).sum(dim=-1).mean(dim=-1).sum()
 
 
-def compressed_logits(stack, g, x, k, v, sink_k, sink_v, k_idx, v_idx, k_master, v_master):
+def compressed_logits(stack, g, x, k, v, sink_k, sink_v, k_idx, v_idx, k_master, v_master, pt=None):
     """The stack's logits over the cache rebuilt from the (bf16-rounded)
-    master codebooks with the given assignment."""
+    master codebooks with the given assignment (pt: the keys' pre-transform,
+    whose sigma the encode wrote)."""
     kb, vb = k_master.detach().to(torch.bfloat16), v_master.detach().to(torch.bfloat16)
 
     def attend(t, Q):
-        st = _CallState(g, k_idx, v_idx, kb, vb, sink_k, sink_v, stack.rope, t)
+        st = _CallState(g, k_idx, v_idx, kb, vb, sink_k, sink_v, stack.rope, t, pt)
         return CompressedAttention.apply(Q[:, :, None], k_master, v_master, st)[:, :, 0]
     return stack.logits(x, attend)
 
 
-def reassign(g, k, v, k_cb, v_cb, k_idx=None, v_idx=None):
-    """Exact assignment of the cache to bf16 codebooks (loopvq_encode)."""
+def reassign(g, k, v, k_cb, v_cb, k_idx=None, v_idx=None, pt=None):
+    """Exact assignment of the cache to bf16 codebooks (loopvq_encode; with pt
+    the keys are coded in the pre-transformed space and sigma is written)."""
     B, H, T, N, D = k.shape
     shp = (B, H, T // g.T_c, N, D // (g.G // g.T_c))
     if k_idx is None:
         k_idx = torch.empty(shp, dtype=torch.uint8, device=k.device)
         v_idx = torch.empty(shp, dtype=torch.uint8, device=k.device)
-    api.encode(g, k, k_cb, k_idx)
+    api.encode(g, k, k_cb, k_idx, pt=pt)
     api.encode(g, v, v_cb, v_idx)
     return k_idx, v_idx
 
 
-def finetune_codebooks(stack, g, x, k, v, sink_k, sink_v, k_cb, v_cb, iters, lr=1.0e-3, callback=None):
+def finetune_codebooks(stack, g, x, k, v, sink_k, sink_v, k_cb, v_cb, iters, lr=1.0e-3, callback=None, pt=None):
     """Fine-tune bf16 codebooks k_cb, v_cb [H][n_blk][K][G] against the
     stack's precise outputs.  Returns (fp32 masters, list of J before each
     step).  callback(it, J) is called after every iteration."""
@@ -159,8 +161,8 @@ def finetune_codebooks(stack, g, x, k, v, sink_k, sink_v, k_cb, v_cb, iters, lr=
     Js = []
     for it in range(iters):
         k_idx, v_idx = reassign(g, k, v, km.detach().to(torch.bfloat16), vm.detach().to(torch.bfloat16),
-                                k_idx, v_idx)
-        J = kl_objective(logp, compressed_logits(stack, g, x, k, v, sink_k, sink_v, k_idx, v_idx, km, vm))
+                                k_idx, v_idx, pt)
+        J = kl_objective(logp, compressed_logits(stack, g, x, k, v, sink_k, sink_v, k_idx, v_idx, km, vm, pt))
         opt.zero_grad(set_to_none=True)
         J.backward()
         opt.step()

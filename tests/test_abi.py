@@ -149,13 +149,14 @@ def test_prefill_entry_points_reject_bad_arguments():
     P = ctypes.c_void_p
     A = P(256)                 # stands in for an aligned device pointer; never dereferenced
     U = P(258)                 # misaligned
-    # prefill_attn(g, q, step0, n_steps, B, N, kidx, vidx, N_cap, kcb, vcb, sk, sv, n_s, rope, n_pos, out, lse, s)
-    ok = [A, 0, 4, 1, 8, A, A, 8, A, A, A, A, 4, A, 12, A, A, None]
+    # prefill_attn(g, q, step0, n_steps, B, N, kidx, vidx, N_cap, kcb, vcb, sk, sv, n_s, pt, rope, n_pos, out,
+    #              lse, s)
+    ok = [A, 0, 4, 1, 8, A, A, 8, A, A, A, A, 4, None, A, 12, A, A, None]
 
     def fwd(**ch):
         args = list(ok)
         names = ["q", "step0", "n_steps", "B", "N", "kidx", "vidx", "N_cap", "kcb", "vcb", "sk", "sv", "n_s",
-                 "rope", "n_pos", "out", "lse", "s"]
+                 "pt", "rope", "n_pos", "out", "lse", "s"]
         for k, v in ch.items():
             args[names.index(k)] = v
         return lib.loopvq_prefill_attn(ctypes.byref(g), *args)
@@ -168,16 +169,19 @@ def test_prefill_entry_points_reject_bad_arguments():
     assert fwd(lse=None) == -1
     assert fwd(N=0) == 0                   # nothing to attend: no launch
     assert fwd(n_s=-1) == -1
+    # a pre-transform with a NULL member is refused
+    bad_pt = lv.pretransform.__globals__["PreTransform"](None, None, None, 8)
+    assert fwd(pt=ctypes.byref(bad_pt)) == -1
     bad = lv.geom(128, 4, 4, 24, 256, 2, 4)
     assert lib.loopvq_prefill_attn(ctypes.byref(bad), *ok) != 0
     size = ctypes.c_size_t(0)
     assert lib.loopvq_prefill_attn_backward_workspace(ctypes.byref(g), 2, 8, 0, 4, ctypes.byref(size)) == 0
     assert size.value == 2 * 4 * 4 * 8 * 4
     # backward: short workspace and NULL gradients are refused before any launch
-    bargs = [A, 0, 4, 1, 8, A, A, 8, A, A, A, A, 4, A, 12, A, A, A, A, A, A, A, 16, None]
+    bargs = [A, 0, 4, 1, 8, A, A, 8, A, A, A, A, 4, None, A, 12, A, A, A, A, A, A, A, 16, None]
     assert lib.loopvq_prefill_attn_backward(ctypes.byref(g), *bargs) == -4
-    bargs[22] = 1 * 4 * 4 * 8 * 4
-    bargs[19] = None
+    bargs[23] = 1 * 4 * 4 * 8 * 4
+    bargs[20] = None
     assert lib.loopvq_prefill_attn_backward(ctypes.byref(g), *bargs) == -1
     assert lib.loopvq_rope_table_f32(1e4, 7, 4, A, None) == -1
     assert lib.loopvq_rope_table_f32(1e4, 128, 0, A, None) == -1

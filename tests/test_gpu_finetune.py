@@ -204,3 +204,43 @@ def test_prefill_full_size_sampled():
         if h == 5:
             _tensor_check(dk[sl], dk_r, 1e-4, "d_k_cb kv-head 5")
             _tensor_check(dv[sl], dv_r, 1e-4, "d_v_cb kv-head 5")
+
+
+@pytest.mark.parametrize("G,H_kv,H_q,N,n_s", [(16, 2, 4, 150, 4), (32, 1, 1, 97, 0)])
+def test_prefill_pretransformed_keys(G, H_kv, H_q, N, n_s):
+    # keys coded in the pre-transformed space (w, perm per kv-head; sigma per
+    # token and step, written by the encode): the kernels rebuild the raw keys
+    # and pass the gradient back through the inverse transform
+    _say("prefill attention with pre-transformed keys G=%d H=%d/%d N=%d" % (G, H_kv, H_q, N))
+    cfg = small_cfg(1, G=G, H_kv=H_kv, H_q=H_q, B=2, N=N, n_s=max(n_s, 1), tasq=True)
+    inp = build_inputs(cfg, 0, "cuda", kmeans=False, cb_seed=5)
+    g = lv.geom(cfg.D, cfg.T, cfg.T_c, cfg.G, cfg.K, cfg.H_kv, cfg.H_q, cfg.theta)
+    shp = (cfg.B, cfg.H_kv, cfg.n_blk, cfg.N, cfg.chunks)
+    kidx = torch.zeros(shp, dtype=torch.uint8, device="cuda")
+    vidx = torch.zeros(shp, dtype=torch.uint8, device="cuda")
+    sigma = torch.zeros((cfg.B, cfg.N, cfg.T), dtype=torch.float16, device="cuda")
+    pt = lv.pretransform(inp["w"], inp["perm"], sigma)
+    lv.encode(g, inp["k"], inp["k_cb"], kidx, pt=pt)
+    lv.encode(g, inp["v"], inp["v_cb"], vidx)
+    rope = lv.rope_table_f32(cfg.n_s + cfg.N, cfg.D, cfg.theta)
+    gq = torch.Generator(device="cpu").manual_seed(21)
+    q = torch.randn((cfg.B, H_q, cfg.T, N, cfg.D), generator=gq).cuda()
+    dout = torch.randn((cfg.B, H_q, cfg.T, N, cfg.D), generator=gq).cuda()
+    sk = inp["sink_k"][:, :, :, :n_s].contiguous() if n_s else None
+    sv = inp["sink_v"][:, :, :, :n_s].contiguous() if n_s else None
+    out, lse = lv.prefill_attn(g, q, kidx, vidx, inp["k_cb"], inp["v_cb"], sk, sv, rope, pt=pt)
+    dq, dk, dv = lv.prefill_attn_backward(g, q, kidx, vidx, inp["k_cb"], inp["v_cb"], sk, sv, rope, out, lse,
+                                          dout, pt=pt)
+    torch.cuda.synchronize()
+    tq = (inp["w"].double().cpu(), inp["perm"].long().cpu() & (cfg.D - 1), sigma.double().cpu())
+    o_r, l_r, dq_r, dk_r, dv_r = ref.attention_vjp(
+        q.double().cpu(), kidx.long().cpu(), vidx.long().cpu(), inp["k_cb"].double().cpu(),
+        inp["v_cb"].double().cpu(), inp["sink_k"][:, :, :, :n_s].double().cpu(),
+        inp["sink_v"][:, :, :, :n_s].double().cpu(), cfg.T_c, dout.double().cpu(), theta=cfg.theta, tasq=tq)
+    _row_check(out, o_r, 1e-4, "out")
+    dl = float((lse.double().cpu() - l_r).abs().max())
+    _say("  lse max err %.3g" % dl)
+    assert dl <= 1e-4
+    _row_check(dq, dq_r, 1e-4, "d_q", floor=1e-2)
+    _tensor_check(dk, dk_r, 1e-4, "d_k_cb")
+    _tensor_check(dv, dv_r, 1e-4, "d_v_cb")
