@@ -6,23 +6,25 @@
 // Decoding split merge) and section 3.1 eq. (5) (step m reads coordinate
 // i*T_c + m of the shared codeword).
 //
-// Four q-heads x four steps give 16 score rows per token, so the scores are a
-// real contraction and run on v_mfma_f32_16x16x32_f16: rows (h, m) = 4h + m,
-// columns = 16 tokens, k = 128 channels in four blocks of 32.  The keys of
-// step m go through their own chain of four MFMAs whose rows of step m are
-// kept (the other rows pair a query with another step's keys and are
-// dropped).  Each wave works on 16 tokens at a time and plays two roles:
-//   * score lanes (token t = lane % 16, quarter q4 = lane / 16): gather the
-//     token's K codewords of the chunks holding channels 32r + 8q4 + j,
-//     rotate them (their RoPE partners are in the same lane) straight into the
-//     MFMA B operand, and receive the scores of head q4 for the four steps;
-//     they keep the online softmax of those rows (the running maximum is
-//     shared by the 16 token lanes of a row through DPP).
-//   * P.V lanes (channel group cg = lane % 16, step m = lane / 16): own the
-//     output of channels 8cg .. 8cg+7 at step m for the four heads; per token
-//     they gather the V codeword slice themselves and read the four
-//     probabilities from a per-wave LDS tile.
-// Every index byte is used once for K and once for V per token, every
+// Four q-heads x four steps give 16 rows rho = 4h + m per token, so both
+// products are real contractions and run on v_mfma_f32_16x16x32_f16:
+//   * scores S^T[token][rho] (A = rotated keys of 16 tokens, B = queries,
+//     k = 128 channels in four blocks of 32).  The keys of step m go through
+//     their own chain of MFMAs; a lane keeps the chain of its row's step.
+//     Key lanes (token t16 = lane % 16, quarter q4 = lane / 16) gather the
+//     token's K codewords of the chunks holding channels 32r + 8q4 + j and
+//     rotate them (RoPE partners sit in the same lane) into the A operand.
+//   * row lanes (rho = lane % 16, group g = lane / 16) receive the scores of
+//     row rho for tokens 4g .. 4g+3 of each 16-token tile, keep the row's
+//     online softmax (the maximum crosses the four groups through permlane
+//     swaps) and hold the row's output O^T[channel][rho] for channels
+//     16b + 4g .. +3 of every 16-channel block b.
+//   * P.V: O^T += V_m^T P_m per step m, with P_m = P masked to the rows of
+//     step m and V_m^T [16 channels][32 tokens] read straight from the LDS
+//     codebook by ds_read_b64_tr_b16: within a 16-lane group, lane (a, j)
+//     fetches four channels 4a .. 4a+3 of token j, and the transposed read
+//     hands every lane one channel of four tokens.
+// Every index byte is used once for K and once for V per token; every
 // codeword gather and key rotation serves all four heads.
 #include "common.h"
 #include "kernels.h"
@@ -32,8 +34,11 @@ namespace loopvq {
 namespace {
 
 typedef _Float16 h2g_t __attribute__((ext_vector_type(2)));
+typedef _Float16 h4g_t __attribute__((ext_vector_type(4)));
 typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 typedef float f4g_t __attribute__((ext_vector_type(4)));
+typedef short s4g_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s4g_t lds_s4_t;
 
 __device__ __forceinline__ h2g_t as_h2g(uint32_t w) { return __builtin_bit_cast(h2g_t, w); }
 
@@ -48,13 +53,25 @@ __device__ __forceinline__ int pow2_shift_g(float max_abs, int lim) {
   return e > lim ? e - lim : 0;
 }
 
-// max over the 16 lanes of a DPP row
-__device__ __forceinline__ float row16_max(float v) {
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, true)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, true)));
-  return v;
+// Four fp16 at an 8-byte aligned LDS byte address, transposed within the
+// lane's 16-lane group (ds_read_b64_tr_b16).
+__device__ __forceinline__ h4g_t lds_tr4(const void* base, uint32_t byte_off) {
+  return __builtin_bit_cast(h4g_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s4_t*)((__attribute__((address_space(3))) char*)(__attribute__((address_space(3))) void*)base + byte_off)));
+}
+
+// max / sum over the four 16-lane groups (lanes l, l ^ 16, l ^ 32, l ^ 48)
+__device__ __forceinline__ float group4_max(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float group4_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // Orders this wave's LDS traffic: writes before the fence are visible to the
@@ -71,31 +88,36 @@ constexpr int kGLag = 3, kGVLim = 7;   // running-max lag and value range, as in
 
 template <int C>
 __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(2))) void decode_gqa_kernel(DecodeArgs a) {
-  constexpr int D = 128, HD = 64, TC = 4, G = C * TC, CPT = D / C;
+  constexpr int D = 128, TC = 4, G = C * TC, CPT = D / C;
   constexpr int CW = G / 8;           // uint4 per codeword (fp16, step-major)
   // Codeword stride in uint4: one pad slot makes it odd, so the step-m slices
-  // of random codewords spread over all LDS bank groups (a stride of 4 slots
-  // would put every step-m read of a wave in the same 4 of 16 groups).
+  // of random codewords spread over all LDS bank groups.
   constexpr int CWS = CW + 1;
   constexpr int DW = C / 2;           // dwords of one step of a codeword
+  constexpr int SOFF = 2 * C;         // bytes of one step of a codeword
   constexpr int RW = CPT / 16;        // uint4 per index row
   constexpr int NW = kDecodeThreads / kWave;
-  constexpr int TOK = 16;             // tokens per wave iteration
-  // K and V codebooks; after the token loops the same memory holds the
-  // per-wave partial rows of the final merge.
-  constexpr int KV_U4 = 2 * 256 * CWS, RED_U4 = (NW * 16 * (D + 2) * 4 + 15) / 16;
-  __shared__ __attribute__((aligned(16))) uint4 s_kv[KV_U4 > RED_U4 ? KV_U4 : RED_U4];
+  constexpr int TILE = 16;            // tokens per score tile; two tiles per wave iteration
+  constexpr int SROW = D + 8;         // fp16 per staged bf16 value row
+  // K and V codebooks; after the quantized tokens the same memory holds the
+  // staged bf16 values, then the per-wave partial rows of the final merge.
+  constexpr int KV_U4 = 2 * 256 * CWS;
+  constexpr int RED_U4 = (NW * 16 * (D + 2) * 4 + 15) / 16;
+  constexpr int STG_U4 = NW * TILE * SROW * 2 / 16;
+  constexpr int U4a = KV_U4 > RED_U4 ? KV_U4 : RED_U4;
+  constexpr int U4 = U4a > STG_U4 ? U4a : STG_U4;
+  __shared__ __attribute__((aligned(16))) uint4 s_kv[U4];
   uint4* const s_k = s_kv;
   uint4* const s_v = s_kv + 256 * CWS;
   float (*const s_red)[16][D + 2] = reinterpret_cast<float (*)[16][D + 2]>(s_kv);
-  __shared__ __attribute__((aligned(16))) uint32_t s_p[NW][TOK][4][4];      // [t][m][h] fp16 pairs (p, p)
-  __shared__ float s_alpha[NW][4][4];                                        // [m][h]
-  __shared__ __attribute__((aligned(16))) uint8_t s_vix[NW][CPT][TOK];      // V index bytes, transposed
+  uint16_t (*const s_stage)[TILE][SROW] = reinterpret_cast<uint16_t (*)[TILE][SROW]>(s_kv);
   __shared__ float s_amax[2][NW];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int t16 = lane & 15, q4 = lane >> 4;     // score role: token, quarter (= head)
-  const int cg = lane & 15, ms = lane >> 4;      // P.V role: channel group, step
+  const int t16 = lane & 15, q4 = lane >> 4;     // key role: token, channel quarter
+  const int rho = lane & 15, grp = lane >> 4;    // row role: row (head rho/4, step rho%4), token group
+  const int mrow = rho & 3;                      // the row's step within the block
+  const int va = lane & 3, vj = (lane >> 2) & 3; // V request role: channel quad, token within the group
   const int split = blockIdx.x;
   const int hq0 = blockIdx.y * 4;
   const int h = hq0 / a.gqa;
@@ -161,12 +183,11 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
     }
   }
 
-  // ---- query operand: row rho = lane % 16 = (head rho/4, step rho%4), k quarter
-  // kq = lane / 16; block r' holds channels 32r' + 8kq .. +7 of the row's step.
+  // ---- query operand (B of the score product): column rho = lane % 16,
+  // k quarter kq = lane / 16; block r' holds channels 32r' + 8kq .. +7.
   h8_t qa[4];
   {
-    const int rho = lane & 15, kq = lane >> 4;
-    const int hh = rho >> 2, m = rho & 3;
+    const int hh = rho >> 2, m = rho & 3, kq = lane >> 4;
     const int t = beta * TC + m;
     const bool act = t >= t_lo && t < t_hi;
     const uint16_t* qr = a.q + (((int64_t)b * a.Hq + hq0 + hh) * a.n_steps + (act ? t - a.step0 : 0)) * D;
@@ -183,24 +204,11 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
   }
   const float sscale = a.qscale * ldexpf(1.f, shk);
 
-  // score-role state: rows (head q4, step i)
-  float Mr[TC], Lr[TC];
+  // row-role state: online softmax of row rho and O^T[16b + 4grp + e][rho]
+  float Mr = -INFINITY, Lr = 0.f;
+  f4g_t oacc[8];
 #pragma unroll
-  for (int i = 0; i < TC; ++i) {
-    Mr[i] = -INFINITY;
-    Lr[i] = 0.f;
-  }
-  // P.V-role state: heads hh, channels 8cg + 2ip, +1 of step ms
-  float acc[4][8];
-  uint32_t acc16[4][4];
-#pragma unroll
-  for (int hh = 0; hh < 4; ++hh)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[hh][e] = 0.f;
-#pragma unroll
-  for (int hh = 0; hh < 4; ++hh)
-#pragma unroll
-    for (int ip = 0; ip < 4; ++ip) acc16[hh][ip] = 0u;
+  for (int bl = 0; bl < 8; ++bl) oacc[bl] = (f4g_t){0.f, 0.f, 0.f, 0.f};
   __syncthreads();
 
   int nb = a.N;
@@ -215,16 +223,16 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
   const uint16_t* rope16 = reinterpret_cast<const uint16_t*>(a.rope);
   const float ksc = ldexpf(1.f, -shk), vsc = ldexpf(1.f, -shv);
 
-  // Score lane data of one token: Kc[m][r'] = 8 channels 32r' + 8q4 .. +7 of
-  // step m as four fp16 pairs (before rotation).  cos/sin: quads 8r + 2q4 and
-  // 8r + 2q4 + 1 for r in {0, 1} (frequencies 32r + 8q4 .. +7).
-  // One accumulator chain per key step m: row (h, m') of chain m holds the
-  // score of q-head h at step m' against the keys of step m, so a lane keeps
-  // element i of chain i (rows 4q4 + i are (head q4, step i)).
-  auto rotate_score = [&](uint32_t (&Kc)[TC][4][4], const uint4 (&CS)[2][2], bool valid, float (&s)[TC]) {
+  // Scores of one 16-token tile.  Key lane data: Kc[m][r'] = 8 channels
+  // 32r' + 8q4 .. +7 of step m as four fp16 pairs (before rotation); cos/sin:
+  // quads 8r + 2q4 and 8r + 2q4 + 1 for r in {0, 1}.  Chain m holds
+  // S^T[token][rho] of every row against the keys of step m; row lanes keep
+  // the chain of their own step: s[e] = score of row rho, token 4grp + e.
+  auto score_tile = [&](uint32_t (&Kc)[TC][4][4], const uint4 (&CS)[2][2], float (&s)[4]) {
+    f4g_t ch[TC];
 #pragma unroll
     for (int m = 0; m < TC; ++m) {
-      f4g_t sacc = {0.f, 0.f, 0.f, 0.f};
+      ch[m] = (f4g_t){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int rr = 0; rr < 2; ++rr) {
         uint32_t o1[4], o2[4];
@@ -238,67 +246,49 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
         }
         const h8_t b1 = __builtin_bit_cast(h8_t, make_uint4(o1[0], o1[1], o1[2], o1[3]));
         const h8_t b2 = __builtin_bit_cast(h8_t, make_uint4(o2[0], o2[1], o2[2], o2[3]));
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[rr], b1, sacc, 0, 0, 0);
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[rr + 2], b2, sacc, 0, 0, 0);
+        ch[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b1, qa[rr], ch[m], 0, 0, 0);
+        ch[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b2, qa[rr + 2], ch[m], 0, 0, 0);
       }
-      s[m] = valid ? sacc[m] * sscale : -INFINITY;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float v01 = (mrow & 1) ? ch[1][e] : ch[0][e];
+      const float v23 = (mrow & 1) ? ch[3][e] : ch[2][e];
+      s[e] = (mrow & 2) ? v23 : v01;
     }
   };
 
-  // Softmax of the score rows, then the P tile and the rescale factors go to
-  // this wave's LDS slots.  Returns true when some row's maximum moved.
-  auto softmax_tile = [&](const float (&s)[TC]) {
+  // Online softmax of row rho over eight scores (invalid ones already
+  // -inf); returns the P operand (fp16, rounded toward zero; the row sum adds
+  // the same rounded values).
+  auto softmax_rows = [&](float (&s)[8]) {
+    float mx = s[0];
+#pragma unroll
+    for (int k = 1; k < 8; ++k) mx = fmaxf(mx, s[k]);
+    mx = group4_max(mx);
+    float alpha = 1.f;
     bool moved = false;
-#pragma unroll
-    for (int i = 0; i < TC; ++i) {
-      const float mx = row16_max(s[i]);
-      float alpha = 1.f;
-      if (mx > Mr[i] + (float)kGLag) {
-        alpha = Mr[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(Mr[i] - mx);
-        Mr[i] = mx;
-        Lr[i] *= alpha;
-        moved = true;
-      }
-      const float p = Mr[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s[i] - Mr[i]);
-      Lr[i] += p;
-      const _Float16 ph = (_Float16)p;
-      s_p[wave][t16][i][q4] = (uint32_t)__builtin_bit_cast(uint16_t, ph) * 0x10001u;
-      if (t16 == 0) s_alpha[wave][i][q4] = alpha;
+    if (mx > Mr + (float)kGLag) {
+      alpha = Mr == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(Mr - mx);
+      Mr = mx;
+      Lr *= alpha;
+      moved = true;
     }
-    return __ballot(moved) != 0;
-  };
-
-  // P.V of one token slot for this lane's (channel group, step); Vw = the
-  // four fp16 pairs of channels 8cg .. 8cg+7 at step ms.
-  auto pv = [&](int t, const uint32_t (&Vw)[4]) {
-    const uint4 p4 = *reinterpret_cast<const uint4*>(&s_p[wave][t][ms][0]);
-    const uint32_t pw[4] = {p4.x, p4.y, p4.z, p4.w};
+    if (__ballot(moved) != 0) {
 #pragma unroll
-    for (int hh = 0; hh < 4; ++hh)
-#pragma unroll
-      for (int ip = 0; ip < 4; ++ip)
-        acc16[hh][ip] = __builtin_bit_cast(uint32_t, as_h2g(Vw[ip]) * as_h2g(pw[hh]) + as_h2g(acc16[hh][ip]));
-  };
-  auto rescale = [&]() {
-    const float4 al = *reinterpret_cast<const float4*>(&s_alpha[wave][ms][0]);
-    const float alv[4] = {al.x, al.y, al.z, al.w};
-#pragma unroll
-    for (int hh = 0; hh < 4; ++hh) {
-      const h2g_t a2 = {(_Float16)alv[hh], (_Float16)alv[hh]};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[hh][e] *= alv[hh];
-#pragma unroll
-      for (int ip = 0; ip < 4; ++ip) acc16[hh][ip] = __builtin_bit_cast(uint32_t, as_h2g(acc16[hh][ip]) * a2);
+      for (int bl = 0; bl < 8; ++bl) oacc[bl] *= alpha;
     }
-  };
-  auto flush = [&]() {
+    uint32_t pk[4];
+    const h2g_t ones = {(_Float16)1.f, (_Float16)1.f};
 #pragma unroll
-    for (int hh = 0; hh < 4; ++hh)
-#pragma unroll
-      for (int ip = 0; ip < 4; ++ip) {
-        add_f16x2(acc16[hh][ip], acc[hh][2 * ip], acc[hh][2 * ip + 1]);
-        acc16[hh][ip] = 0u;
-      }
+    for (int k = 0; k < 4; ++k) {
+      const float p0 = Mr == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s[2 * k] - Mr);
+      const float p1 = Mr == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s[2 * k + 1] - Mr);
+      const h2g_t ph = __builtin_bit_cast(h2g_t, __builtin_amdgcn_cvt_pkrtz(p0, p1));
+      Lr = __builtin_amdgcn_fdot2(ph, ones, Lr, false);
+      pk[k] = __builtin_bit_cast(uint32_t, ph);
+    }
+    return __builtin_bit_cast(h8_t, make_uint4(pk[0], pk[1], pk[2], pk[3]));
   };
   auto load_cs = [&](int pos, uint4 (&CS)[2][2]) {
     const uint4* row = reinterpret_cast<const uint4*>(rope16 + (int64_t)pos * D);
@@ -308,96 +298,33 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
       for (int u = 0; u < 2; ++u) CS[rr][u] = row[8 * rr + 2 * q4 + u];
   };
 
-  // ---- bf16 items: sinks at positions 0..n_s-1, then the recent window at
-  // n_s + N_b + r (split 0 only), 16 per wave iteration
-  for (int base = 0; base < n_bf; base += NW * TOK) {
-    // score role: item base + 16*wave + t16
-    {
-      const int item = base + wave * TOK + t16;
-      const bool valid = item < n_bf;
-      const int it = valid ? item : 0;
-      const bool is_rec = it >= n_sink;
-      const int pos = is_rec ? a.n_s + nb + (it - n_sink) : it;
-      uint32_t Kc[TC][4][4];
-#pragma unroll
-      for (int m = 0; m < TC; ++m) {
-        const uint16_t* kr = is_rec ? a.rk + (rec0 + (int64_t)m * a.r_cap + (it - n_sink)) * D
-                                    : a.sk + (sink0 + (int64_t)m * a.n_s + it) * D;
-#pragma unroll
-        for (int rp = 0; rp < 4; ++rp) {
-          const uint4 w = *reinterpret_cast<const uint4*>(kr + 32 * rp + 8 * q4);
-          const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) Kc[m][rp][e] = pack_h2g(bf16lo(ws[e]) * ksc, bf16hi(ws[e]) * ksc);
-        }
-      }
-      uint4 CS[2][2];
-      load_cs(pos, CS);
-      float s[TC];
-      rotate_score(Kc, CS, valid, s);
-      const bool moved = softmax_tile(s);
-      wave_sync();
-      if (moved) rescale();
-    }
-    // P.V role: the same 16 items, channels 8cg .. 8cg+7 of step ms
-#pragma unroll 1
-    for (int t = 0; t < TOK; ++t) {
-      const int item = base + wave * TOK + t;
-      const int it = item < n_bf ? item : 0;
-      const bool is_rec = it >= n_sink;
-      const uint16_t* vr = is_rec ? a.rv + (rec0 + (int64_t)ms * a.r_cap + (it - n_sink)) * D
-                                  : a.sv + (sink0 + (int64_t)ms * a.n_s + it) * D;
-      const uint4 w = *reinterpret_cast<const uint4*>(vr + 8 * cg);
-      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-      uint32_t Vw[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) Vw[e] = pack_h2g(bf16lo(ws[e]) * vsc, bf16hi(ws[e]) * vsc);
-      pv(t, Vw);   // p = 0 for items past the end
-    }
-    flush();
-    wave_sync();
-  }
-
-  // ---- quantized tokens: 16 per wave iteration, index rows prefetched
+  // ---- quantized tokens: 32 per wave iteration (two score tiles), index
+  // rows of the next iteration loaded while this one is computed
   const int n_tok = max(0, tok_hi - tok_lo);
-  uint4 krow[RW], vrow[RW];
-  uint4 CS[2][2];
-  auto load_rows = [&](int base, int& jj) {
-    const int it = base + wave * TOK + t16;
-    jj = tok_lo + (it < n_tok ? it : n_tok - 1);   // always a real row
-    const uint4* kr = reinterpret_cast<const uint4*>(a.kidx + (irow0 + jj) * CPT);
-    const uint4* vr = reinterpret_cast<const uint4*>(a.vidx + (irow0 + jj) * CPT);
+  uint4 krow[2][RW], vrow[2][RW];
+  auto load_rows = [&](int base, uint4 (&kr)[2][RW], uint4 (&vr)[2][RW]) {
 #pragma unroll
-    for (int u = 0; u < RW; ++u) {
-      krow[u] = kr[u];
-      vrow[u] = vr[u];
+    for (int hf = 0; hf < 2; ++hf) {
+      const int ik = base + wave * 2 * TILE + TILE * hf + t16;
+      const int iv = base + wave * 2 * TILE + TILE * hf + 4 * grp + vj;
+      const int64_t jk = tok_lo + (ik < n_tok ? ik : n_tok - 1);   // always a real row
+      const int64_t jv = tok_lo + (iv < n_tok ? iv : n_tok - 1);
+      const uint4* pk = reinterpret_cast<const uint4*>(a.kidx + (irow0 + jk) * CPT);
+      const uint4* pv = reinterpret_cast<const uint4*>(a.vidx + (irow0 + jv) * CPT);
+#pragma unroll
+      for (int u = 0; u < RW; ++u) {
+        kr[hf][u] = pk[u];
+        vr[hf][u] = pv[u];
+      }
     }
   };
-  if (n_tok > 0) {
-    int jj;
-    load_rows(0, jj);
-    load_cs(a.n_s + jj, CS);
-  }
-  int tiles = 0;
-  for (int base = 0; base < n_tok; base += NW * TOK) {
-    const bool valid = base + wave * TOK + t16 < n_tok;
-    uint32_t kd[4 * RW], vd[4 * RW];
+  // K codewords of the chunks holding channels 32r + 8q4 + j (j < 8)
+  auto gather_k = [&](const uint4 (&kr)[RW], uint32_t (&Kc)[TC][4][4]) {
+    uint32_t kd[4 * RW];
 #pragma unroll
     for (int u = 0; u < RW; ++u) {
-      kd[4 * u] = krow[u].x; kd[4 * u + 1] = krow[u].y; kd[4 * u + 2] = krow[u].z; kd[4 * u + 3] = krow[u].w;
-      vd[4 * u] = vrow[u].x; vd[4 * u + 1] = vrow[u].y; vd[4 * u + 2] = vrow[u].z; vd[4 * u + 3] = vrow[u].w;
+      kd[4 * u] = kr[u].x; kd[4 * u + 1] = kr[u].y; kd[4 * u + 2] = kr[u].z; kd[4 * u + 3] = kr[u].w;
     }
-    // V index bytes of this quarter's chunks, transposed for the P.V lanes:
-    // s_vix[c][t] for c in [q4 * CPT/4, (q4 + 1) * CPT/4).
-#pragma unroll
-    for (int e = 0; e < CPT / 4; ++e) {
-      const int c = q4 * (CPT / 4) + e;
-      s_vix[wave][c][t16] = (uint8_t)__builtin_amdgcn_ubfe(vd[c >> 2], 8 * (c & 3), 8);
-    }
-    int jn;
-    load_rows(base + NW * TOK, jn);
-    // K codewords of the chunks holding channels 32r + 8q4 + j (j < 8)
-    uint32_t Kc[TC][4][4];
 #pragma unroll
     for (int rp = 0; rp < 4; ++rp) {
       if constexpr (C == 8) {
@@ -423,85 +350,168 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
         }
       }
     }
-    float s[TC];
-    rotate_score(Kc, CS, valid, s);
-    load_cs(a.n_s + jn, CS);
-    const bool moved = softmax_tile(s);
-    wave_sync();
-    if (moved) rescale();
-    // P.V lanes: V index bytes of chunk(s) of this channel group for the 16 tokens
+  };
+  // LDS byte offset (from s_v) of this request lane's step-0 slice of the V
+  // codeword of chunk block bl, token of the given index row: channels
+  // 16bl + 4va .. +3.
+  auto v_off = [&](const uint4 (&vr)[RW], int bl) -> uint32_t {
+    uint32_t vd[4 * RW];
+#pragma unroll
+    for (int u = 0; u < RW; ++u) {
+      vd[4 * u] = vr[u].x; vd[4 * u + 1] = vr[u].y; vd[4 * u + 2] = vr[u].z; vd[4 * u + 3] = vr[u].w;
+    }
     if constexpr (C == 8) {
-      const uint4 ix = *reinterpret_cast<const uint4*>(&s_vix[wave][cg][0]);
-      const uint32_t iw[4] = {ix.x, ix.y, ix.z, ix.w};
-#pragma unroll
-      for (int t = 0; t < TOK; ++t) {
-        const uint32_t iv = __builtin_amdgcn_ubfe(iw[t >> 2], 8 * (t & 3), 8);
-        const uint4 y = s_v[iv * CWS + ms];
-        const uint32_t Vw[4] = {y.x, y.y, y.z, y.w};
-        pv(t, Vw);
-      }
+      // chunk 2bl + va/2, byte 2(bl & 1) + va/2 of dword bl/2; half va & 1 of the step slice
+      const uint32_t ix = __builtin_amdgcn_ubfe(vd[bl >> 1], 16 * (bl & 1) + 8 * (va >> 1), 8);
+      return ix * (CWS * 16) + 8 * (va & 1);
     } else {
-      const uint4 ia = *reinterpret_cast<const uint4*>(&s_vix[wave][2 * cg][0]);
-      const uint4 ib = *reinterpret_cast<const uint4*>(&s_vix[wave][2 * cg + 1][0]);
-      const uint32_t wa[4] = {ia.x, ia.y, ia.z, ia.w}, wb[4] = {ib.x, ib.y, ib.z, ib.w};
+      // chunk 4bl + va: byte va of dword bl
+      const uint32_t ix = __builtin_amdgcn_ubfe(vd[bl], 8 * va, 8);
+      return ix * (CWS * 16);
+    }
+  };
+
+  uint4 CS[2][2];
+  if (n_tok > 0) {
+    load_rows(0, krow, vrow);
+    load_cs(a.n_s + tok_lo + min(wave * 2 * TILE + t16, n_tok - 1), CS);
+  }
+  for (int base = 0; base < n_tok; base += NW * 2 * TILE) {
+    const int w0 = base + wave * 2 * TILE;
+    float s[8];
+    {
+      uint32_t Kc[TC][4][4];
+      gather_k(krow[0], Kc);
+      float s0[4];
+      score_tile(Kc, CS, s0);
+      load_cs(a.n_s + tok_lo + min(w0 + TILE + t16, n_tok - 1), CS);
+      gather_k(krow[1], Kc);
+      float s1[4];
+      score_tile(Kc, CS, s1);
+      load_cs(a.n_s + tok_lo + min(w0 + NW * 2 * TILE + t16, n_tok - 1), CS);
 #pragma unroll
-      for (int t = 0; t < TOK; ++t) {
-        const uint32_t va = __builtin_amdgcn_ubfe(wa[t >> 2], 8 * (t & 3), 8);
-        const uint32_t vb = __builtin_amdgcn_ubfe(wb[t >> 2], 8 * (t & 3), 8);
-        // step ms of a 4-channel codeword: dwords 2ms, 2ms+1
-        const uint2 ya = reinterpret_cast<const uint2*>(&s_v[va * CWS])[ms];
-        const uint2 yb = reinterpret_cast<const uint2*>(&s_v[vb * CWS])[ms];
-        const uint32_t Vw[4] = {ya.x, ya.y, yb.x, yb.y};
-        pv(t, Vw);
+      for (int e = 0; e < 4; ++e) {
+        s[e] = w0 + 4 * grp + e < n_tok ? s0[e] * sscale : -INFINITY;
+        s[4 + e] = w0 + TILE + 4 * grp + e < n_tok ? s1[e] * sscale : -INFINITY;
       }
     }
-    // fp16 partials over two tiles (32 tokens): |p| <= 2^kGLag, |v| <= 2^kGVLim,
-    // so a partial stays below 2^15
-    if (++tiles == 2) {
-      flush();
-      tiles = 0;
+    const h8_t P = softmax_rows(s);
+    uint32_t voff[2][8];
+#pragma unroll
+    for (int bl = 0; bl < 8; ++bl) {
+      voff[0][bl] = v_off(vrow[0], bl);
+      voff[1][bl] = v_off(vrow[1], bl);
     }
-    wave_sync();
+    if (base + NW * 2 * TILE < n_tok) load_rows(base + NW * 2 * TILE, krow, vrow);
+#pragma unroll
+    for (int m = 0; m < TC; ++m) {
+      const h8_t Pm = mrow == m ? P : (h8_t){};
+#pragma unroll
+      for (int bl = 0; bl < 8; ++bl) {
+        const h4g_t lo = lds_tr4(s_v, voff[0][bl] + SOFF * m);
+        const h4g_t hi = lds_tr4(s_v, voff[1][bl] + SOFF * m);
+        const h8_t A = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        oacc[bl] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Pm, oacc[bl], 0, 0, 0);
+      }
+    }
   }
-  flush();
 
-  // ---- per-wave row totals, then merge the waves through LDS (the codebook
-  // memory, once every wave is done with it)
+  // ---- bf16 items (split 0): sinks at positions 0..n_s-1, then the recent
+  // window at n_s + N_b + r; 16 per wave iteration, their values staged per
+  // step in this wave's LDS rows (the codebook memory, once every wave is done
+  // with it)
   __syncthreads();
+  for (int base = 0; base < n_bf; base += NW * TILE) {
+    const int w0 = base + wave * TILE;
+    float s[8];
+    {
+      const int item = w0 + t16;
+      const int it = item < n_bf ? item : 0;
+      const bool is_rec = it >= n_sink;
+      const int pos = is_rec ? a.n_s + nb + (it - n_sink) : it;
+      uint32_t Kc[TC][4][4];
 #pragma unroll
-  for (int i = 0; i < TC; ++i) {
-    float l = Lr[i];
-    l += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(l), 0xB1, 0xF, 0xF, true));
-    l += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(l), 0x4E, 0xF, 0xF, true));
-    l += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(l), 0x141, 0xF, 0xF, true));
-    l += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(l), 0x140, 0xF, 0xF, true));
-    if (t16 == 0) {
-      s_red[wave][4 * q4 + i][D] = Mr[i];
-      s_red[wave][4 * q4 + i][D + 1] = l;
+      for (int m = 0; m < TC; ++m) {
+        const uint16_t* kr = is_rec ? a.rk + (rec0 + (int64_t)m * a.r_cap + (it - n_sink)) * D
+                                    : a.sk + (sink0 + (int64_t)m * a.n_s + it) * D;
+#pragma unroll
+        for (int rp = 0; rp < 4; ++rp) {
+          const uint4 w = *reinterpret_cast<const uint4*>(kr + 32 * rp + 8 * q4);
+          const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) Kc[m][rp][e] = pack_h2g(bf16lo(ws[e]) * ksc, bf16hi(ws[e]) * ksc);
+        }
+      }
+      uint4 CSb[2][2];
+      load_cs(pos, CSb);
+      float s0[4];
+      score_tile(Kc, CSb, s0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        s[e] = w0 + 4 * grp + e < n_bf ? s0[e] * sscale : -INFINITY;
+        s[4 + e] = -INFINITY;
+      }
+    }
+    const h8_t P = softmax_rows(s);
+    // staging lane: item w0 + lane/4, channels 32 (lane & 3) .. +31
+    const int si = lane >> 2, sc = 32 * (lane & 3);
+    const int sit = w0 + si < n_bf ? w0 + si : 0;
+    const bool s_rec = sit >= n_sink;
+#pragma unroll 1
+    for (int m = 0; m < TC; ++m) {
+      const uint16_t* vr = s_rec ? a.rv + (rec0 + (int64_t)m * a.r_cap + (sit - n_sink)) * D
+                                 : a.sv + (sink0 + (int64_t)m * a.n_s + sit) * D;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint4 w = *reinterpret_cast<const uint4*>(vr + sc + 8 * u);
+        *reinterpret_cast<uint4*>(&s_stage[wave][si][sc + 8 * u]) =
+            make_uint4(pack_h2g(bf16lo(w.x) * vsc, bf16hi(w.x) * vsc), pack_h2g(bf16lo(w.y) * vsc, bf16hi(w.y) * vsc),
+                       pack_h2g(bf16lo(w.z) * vsc, bf16hi(w.z) * vsc), pack_h2g(bf16lo(w.w) * vsc, bf16hi(w.w) * vsc));
+      }
+      wave_sync();
+      const h8_t Pm = mrow == m ? P : (h8_t){};
+      const uint32_t roff = (uint32_t)((4 * grp + vj) * SROW + 4 * va) * 2;
+#pragma unroll
+      for (int bl = 0; bl < 8; ++bl) {
+        const h4g_t lo = lds_tr4(&s_stage[wave][0][0], roff + 32 * bl);
+        const h8_t A = __builtin_shufflevector(lo, (h4g_t){}, 0, 1, 2, 3, 4, 5, 6, 7);
+        oacc[bl] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Pm, oacc[bl], 0, 0, 0);
+      }
+      wave_sync();
+    }
+  }
+
+  // ---- per-wave row totals, then merge the waves through LDS
+  __syncthreads();
+  {
+    const float l = group4_sum(Lr);
+    if (grp == 0) {
+      s_red[wave][rho][D] = Mr;
+      s_red[wave][rho][D + 1] = l;
     }
   }
 #pragma unroll
-  for (int hh = 0; hh < 4; ++hh)
+  for (int bl = 0; bl < 8; ++bl)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) s_red[wave][4 * hh + ms][8 * cg + e] = acc[hh][e];
+    for (int e = 0; e < 4; ++e) s_red[wave][rho][16 * bl + 4 * grp + e] = oacc[bl][e];
   __syncthreads();
   const float osc = ldexpf(1.f, shv);
   for (int x = tid; x < 16 * D; x += kDecodeThreads) {
-    const int rho = x / D, d = x - rho * D;
-    const int hh = rho >> 2, m = rho & 3;
+    const int rw = x / D, d = x - rw * D;
+    const int hh = rw >> 2, m = rw & 3;
     const int t = beta * TC + m;
     if (t < t_lo || t >= t_hi) continue;
     float mm = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) mm = fmaxf(mm, s_red[w][rho][D]);
+    for (int w = 0; w < NW; ++w) mm = fmaxf(mm, s_red[w][rw][D]);
     float num = 0.f, den = 0.f;
     if (mm != -INFINITY) {
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
-        const float mw = s_red[w][rho][D];
+        const float mw = s_red[w][rw][D];
         const float f = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - mm);
-        num += f * s_red[w][rho][d];
-        den += f * s_red[w][rho][D + 1];
+        num += f * s_red[w][rw][d];
+        den += f * s_red[w][rw][D + 1];
       }
     }
     float* dst = a.ws + ((((int64_t)b * a.Hq + hq0 + hh) * a.n_steps + (t - a.step0)) * a.n_split + split) * (D + 1);
