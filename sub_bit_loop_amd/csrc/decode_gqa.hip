@@ -7,7 +7,9 @@
 // i*T_c + m of the shared codeword).
 //
 // Four q-heads x four steps give 16 rows rho = 4h + m per token, so both
-// products are real contractions and run on v_mfma_f32_16x16x32_f16:
+// products are real contractions and run on v_mfma_f32_16x16x32_f16 (a
+// workgroup may also serve a group of two q-heads: the rows of heads 2 and 3
+// then carry zero queries and are not written):
 //   * scores S^T[token][rho] (A = rotated keys of 16 tokens, B = queries,
 //     k = 128 channels in four blocks of 32).  The keys of step m go through
 //     their own chain of MFMAs; a lane keeps the chain of its row's step.
@@ -86,7 +88,7 @@ constexpr int kGLag = 3, kGVLim = 7;   // running-max lag and value range, as in
 
 }  // namespace
 
-template <int C>
+template <int C, int HPW>
 __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(2))) void decode_gqa_kernel(DecodeArgs a) {
   constexpr int D = 128, TC = 4, G = C * TC, CPT = D / C;
   constexpr int CW = G / 8;           // uint4 per codeword (fp16, step-major)
@@ -119,7 +121,7 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
   const int mrow = rho & 3;                      // the row's step within the block
   const int va = lane & 3, vj = (lane >> 2) & 3; // V request role: channel quad, token within the group
   const int split = blockIdx.x;
-  const int hq0 = blockIdx.y * 4;
+  const int hq0 = blockIdx.y * HPW;
   const int h = hq0 / a.gqa;
   const int b = blockIdx.z / a.n_blk_serv;
   const int beta = a.blk0 + (blockIdx.z - b * a.n_blk_serv);
@@ -189,8 +191,8 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
   {
     const int hh = rho >> 2, m = rho & 3, kq = lane >> 4;
     const int t = beta * TC + m;
-    const bool act = t >= t_lo && t < t_hi;
-    const uint16_t* qr = a.q + (((int64_t)b * a.Hq + hq0 + hh) * a.n_steps + (act ? t - a.step0 : 0)) * D;
+    const bool act = hh < HPW && t >= t_lo && t < t_hi;
+    const uint16_t* qr = a.q + (((int64_t)b * a.Hq + hq0 + (act ? hh : 0)) * a.n_steps + (act ? t - a.step0 : 0)) * D;
 #pragma unroll
     for (int rp = 0; rp < 4; ++rp) {
       const uint4 w = *reinterpret_cast<const uint4*>(qr + 32 * rp + 8 * kq);
@@ -231,10 +233,13 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
   auto score_tile = [&](uint32_t (&Kc)[TC][4][4], const uint4 (&CS)[2][2], float (&s)[4]) {
     f4g_t ch[TC];
 #pragma unroll
-    for (int m = 0; m < TC; ++m) {
-      ch[m] = (f4g_t){0.f, 0.f, 0.f, 0.f};
+    for (int m = 0; m < TC; ++m) ch[m] = (f4g_t){0.f, 0.f, 0.f, 0.f};
+    // the four chains interleave, so no MFMA waits for its predecessor
 #pragma unroll
-      for (int rr = 0; rr < 2; ++rr) {
+    for (int rr = 0; rr < 2; ++rr) {
+      h8_t b1[TC], b2[TC];
+#pragma unroll
+      for (int m = 0; m < TC; ++m) {
         uint32_t o1[4], o2[4];
 #pragma unroll
         for (int ip = 0; ip < 4; ++ip) {
@@ -244,11 +249,13 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
           o1[ip] = __builtin_bit_cast(uint32_t, x1 * c2 - x2 * s2);
           o2[ip] = __builtin_bit_cast(uint32_t, x2 * c2 + x1 * s2);
         }
-        const h8_t b1 = __builtin_bit_cast(h8_t, make_uint4(o1[0], o1[1], o1[2], o1[3]));
-        const h8_t b2 = __builtin_bit_cast(h8_t, make_uint4(o2[0], o2[1], o2[2], o2[3]));
-        ch[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b1, qa[rr], ch[m], 0, 0, 0);
-        ch[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b2, qa[rr + 2], ch[m], 0, 0, 0);
+        b1[m] = __builtin_bit_cast(h8_t, make_uint4(o1[0], o1[1], o1[2], o1[3]));
+        b2[m] = __builtin_bit_cast(h8_t, make_uint4(o2[0], o2[1], o2[2], o2[3]));
       }
+#pragma unroll
+      for (int m = 0; m < TC; ++m) ch[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b1[m], qa[rr], ch[m], 0, 0, 0);
+#pragma unroll
+      for (int m = 0; m < TC; ++m) ch[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b2[m], qa[rr + 2], ch[m], 0, 0, 0);
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -274,7 +281,7 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
       Lr *= alpha;
       moved = true;
     }
-    if (__ballot(moved) != 0) {
+    if (__builtin_expect(__ballot(moved) != 0, 0)) {
 #pragma unroll
       for (int bl = 0; bl < 8; ++bl) oacc[bl] *= alpha;
     }
@@ -500,7 +507,7 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
     const int rw = x / D, d = x - rw * D;
     const int hh = rw >> 2, m = rw & 3;
     const int t = beta * TC + m;
-    if (t < t_lo || t >= t_hi) continue;
+    if (hh >= HPW || t < t_lo || t >= t_hi) continue;
     float mm = -INFINITY;
 #pragma unroll
     for (int w = 0; w < NW; ++w) mm = fmaxf(mm, s_red[w][rw][D]);
@@ -520,15 +527,22 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
   }
 }
 
-hipError_t launch_decode_gqa(int G, const DecodeArgs& a, hipStream_t s) {
-  dim3 grid(a.n_split, a.Hq / 4, a.B * a.n_blk_serv);
-  if (G == 16)
-    hipLaunchKernelGGL(decode_gqa_kernel<4>, grid, dim3(kDecodeThreads), 0, s, a);
-  else if (G == 32)
-    hipLaunchKernelGGL(decode_gqa_kernel<8>, grid, dim3(kDecodeThreads), 0, s, a);
+template <int C>
+static hipError_t launch_gqa_c(int hpw, const DecodeArgs& a, hipStream_t s) {
+  const dim3 grid(a.n_split, a.Hq / hpw, a.B * a.n_blk_serv);
+  if (hpw == 4)
+    hipLaunchKernelGGL((decode_gqa_kernel<C, 4>), grid, dim3(kDecodeThreads), 0, s, a);
+  else if (hpw == 2)
+    hipLaunchKernelGGL((decode_gqa_kernel<C, 2>), grid, dim3(kDecodeThreads), 0, s, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
+}
+
+hipError_t launch_decode_gqa(int G, int hpw, const DecodeArgs& a, hipStream_t s) {
+  if (G == 16) return launch_gqa_c<4>(hpw, a, s);
+  if (G == 32) return launch_gqa_c<8>(hpw, a, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace loopvq

@@ -123,8 +123,9 @@ hipError_t launch_decode_fast(int G, const DecodeArgs& a, hipStream_t s);
 // T_c = 4, no pre-transform; one workgroup per (split, group of hpw q-heads,
 // batch x served step); hpw in {1, 2, 4} divides the GQA group size.
 hipError_t launch_decode_step(int G, int hpw, const DecodeArgs& a, hipStream_t s);
-// T_c = 4, no pre-transform, groups of 4 q-heads; grid (n_split, Hq/4, B x blocks)
-hipError_t launch_decode_gqa(int G, const DecodeArgs& a, hipStream_t s);
+// T_c = 4, no pre-transform, hpw in {2, 4} q-heads of a GQA group per
+// workgroup; grid (n_split, Hq/hpw, B x blocks)
+hipError_t launch_decode_gqa(int G, int hpw, const DecodeArgs& a, hipStream_t s);
 // T_c = 4 with the channel pre-transform (keys); one q-head per workgroup;
 // grid (n_split, Hq, B x served blocks); sigma must be 4-byte aligned.
 hipError_t launch_decode_tasq(int G, const DecodeArgs& a, hipStream_t s);

@@ -79,20 +79,21 @@ DecodePlan plan_decode(const loopvq_geom* g, int B, int N, int step0, int n_step
   p.n_blk_serv = blk1 - p.blk0 + 1;
   const int gqa = g->n_q_heads / g->n_kv_heads;
   p.hpw = gqa % 4 == 0 ? 4 : (gqa % 2 == 0 ? 2 : 1);
-  // Blocks of four steps: GQA groups of four q-heads with several steps served
-  // use the MFMA kernel (16 score rows per token); a single served step, or
-  // other GQA groups, use the single-step kernel (one workgroup per step,
-  // q-heads sharing gathers and rotation); otherwise the multi-step kernel,
-  // which decodes each index row once for all steps of its block.
-  // Pre-transformed keys in blocks of four steps have their own kernel (one
-  // q-head per workgroup); other block lengths use the generic kernel.
+  // Blocks of four steps: GQA groups of two or four q-heads with several steps
+  // served use the MFMA kernel (two or four heads x four steps = 8 or 16
+  // score rows per token); a single served step uses the single-step kernel
+  // (one workgroup per step, q-heads sharing gathers and rotation); other
+  // groups use the multi-step kernel, which decodes each index row once for
+  // all steps of its block.  Pre-transformed keys in blocks of four steps have
+  // their own kernel (one q-head per workgroup); other block lengths use the
+  // generic kernel.
   if (g->T_c != 4)
     p.kernel = DecodeKernel::kGeneric;
   else if (tasq)
     p.kernel = DecodeKernel::kTasq;
-  else if (gqa % 4 == 0 && n_steps > 1)
+  else if (p.hpw > 1 && n_steps > 1)
     p.kernel = DecodeKernel::kGqa;
-  else if (n_steps == 1 || p.hpw > 1)
+  else if (n_steps == 1)
     p.kernel = DecodeKernel::kStep;
   else
     p.kernel = DecodeKernel::kFast;
@@ -104,7 +105,7 @@ DecodePlan plan_decode(const loopvq_geom* g, int B, int N, int step0, int n_step
       target = p.hpw == 1 ? 1024 : 512;   // 95 VGPRs: 4 per CU; more heads: 2
       break;
     case DecodeKernel::kGqa:
-      wgs = (long long)B * (g->n_q_heads / 4) * p.n_blk_serv;
+      wgs = (long long)B * (g->n_q_heads / p.hpw) * p.n_blk_serv;
       target = 512;
       break;
     default:
@@ -493,7 +494,7 @@ loopvq_status loopvq_decode_attn(const loopvq_geom* g, const void* q, int32_t st
   else if (p.kernel == DecodeKernel::kTasq)
     e = loopvq::launch_decode_tasq(g->G, a, s);
   else if (p.kernel == DecodeKernel::kGqa)
-    e = loopvq::launch_decode_gqa(g->G, a, s);
+    e = loopvq::launch_decode_gqa(g->G, p.hpw, a, s);
   else if (p.kernel == DecodeKernel::kStep)
     e = loopvq::launch_decode_step(g->G, p.hpw, a, s);
   else

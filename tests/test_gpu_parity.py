@@ -202,10 +202,12 @@ def test_small_geometries(geo):
 
 
 EDGE_GEOMS = [
-    # name, G, T, H_kv, H_q, pretransform  (the plain multi-step, the GQA MFMA and the
-    # pre-transform kernels; T = 8 gives ranges that cross a block boundary)
+    # name, G, T, H_kv, H_q, pretransform  (the plain multi-step kernel, the GQA MFMA
+    # kernel with four and two q-heads per workgroup, and the pre-transform kernel;
+    # T = 8 gives ranges that cross a block boundary)
     ("mha", 16, 4, 1, 1, False),
     ("gqa4-2blk", 32, 8, 1, 4, False),
+    ("gqa2-2blk", 16, 8, 1, 2, False),
     ("pretransform-2blk", 16, 8, 1, 1, True),
 ]
 
