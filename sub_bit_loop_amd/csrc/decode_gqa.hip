@@ -88,7 +88,7 @@ constexpr int kGLag = 3, kGVLim = 7;   // running-max lag and value range, as in
 
 }  // namespace
 
-template <int C, int HPW>
+template <int C, int HPW, bool ONE>
 __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(2))) void decode_gqa_kernel(DecodeArgs a) {
   constexpr int D = 128, TC = 4, G = C * TC, CPT = D / C;
   constexpr int CW = G / 8;           // uint4 per codeword (fp16, step-major)
@@ -126,6 +126,10 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
   const int b = blockIdx.z / a.n_blk_serv;
   const int beta = a.blk0 + (blockIdx.z - b * a.n_blk_serv);
   const int t_lo = max(a.step0, beta * TC), t_hi = min(a.step0 + a.n_steps, (beta + 1) * TC);
+  // ONE: a single served step m0 of the block; only its codeword slices are
+  // read and rotated, and only its rows carry queries
+  constexpr int NS = ONE ? 1 : TC;
+  const int m0 = ONE ? a.step0 - beta * TC : 0;
 
   // ---- codebooks -> LDS (fp16, step-major), power-of-two range scaling
   const int64_t cbo = ((int64_t)h * a.n_blk + beta) * a.K * G;
@@ -230,16 +234,16 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
   // quads 8r + 2q4 and 8r + 2q4 + 1 for r in {0, 1}.  Chain m holds
   // S^T[token][rho] of every row against the keys of step m; row lanes keep
   // the chain of their own step: s[e] = score of row rho, token 4grp + e.
-  auto score_tile = [&](uint32_t (&Kc)[TC][4][4], const uint4 (&CS)[2][2], float (&s)[4]) {
-    f4g_t ch[TC];
+  auto score_tile = [&](uint32_t (&Kc)[NS][4][4], const uint4 (&CS)[2][2], float (&s)[4]) {
+    f4g_t ch[NS];
 #pragma unroll
-    for (int m = 0; m < TC; ++m) ch[m] = (f4g_t){0.f, 0.f, 0.f, 0.f};
+    for (int m = 0; m < NS; ++m) ch[m] = (f4g_t){0.f, 0.f, 0.f, 0.f};
     // the four chains interleave, so no MFMA waits for its predecessor
 #pragma unroll
     for (int rr = 0; rr < 2; ++rr) {
-      h8_t b1[TC], b2[TC];
+      h8_t b1[NS], b2[NS];
 #pragma unroll
-      for (int m = 0; m < TC; ++m) {
+      for (int m = 0; m < NS; ++m) {
         uint32_t o1[4], o2[4];
 #pragma unroll
         for (int ip = 0; ip < 4; ++ip) {
@@ -253,15 +257,19 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
         b2[m] = __builtin_bit_cast(h8_t, make_uint4(o2[0], o2[1], o2[2], o2[3]));
       }
 #pragma unroll
-      for (int m = 0; m < TC; ++m) ch[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b1[m], qa[rr], ch[m], 0, 0, 0);
+      for (int m = 0; m < NS; ++m) ch[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b1[m], qa[rr], ch[m], 0, 0, 0);
 #pragma unroll
-      for (int m = 0; m < TC; ++m) ch[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b2[m], qa[rr + 2], ch[m], 0, 0, 0);
+      for (int m = 0; m < NS; ++m) ch[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b2[m], qa[rr + 2], ch[m], 0, 0, 0);
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float v01 = (mrow & 1) ? ch[1][e] : ch[0][e];
-      const float v23 = (mrow & 1) ? ch[3][e] : ch[2][e];
-      s[e] = (mrow & 2) ? v23 : v01;
+      if constexpr (ONE) {
+        s[e] = ch[0][e];
+      } else {
+        const float v01 = (mrow & 1) ? ch[1][e] : ch[0][e];
+        const float v23 = (mrow & 1) ? ch[NS - 1][e] : ch[NS - 2][e];
+        s[e] = (mrow & 2) ? v23 : v01;
+      }
     }
   };
 
@@ -326,7 +334,7 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
     }
   };
   // K codewords of the chunks holding channels 32r + 8q4 + j (j < 8)
-  auto gather_k = [&](const uint4 (&kr)[RW], uint32_t (&Kc)[TC][4][4]) {
+  auto gather_k = [&](const uint4 (&kr)[RW], uint32_t (&Kc)[NS][4][4]) {
     uint32_t kd[4 * RW];
 #pragma unroll
     for (int u = 0; u < RW; ++u) {
@@ -339,8 +347,8 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
         const uint32_t ik = __builtin_amdgcn_ubfe(kd[c >> 2], 8 * (c & 3), 8);
         const uint4* cw = &s_k[ik * CWS];
 #pragma unroll
-        for (int m = 0; m < TC; ++m) {
-          const uint4 x = cw[m];                            // step m: 8 channels
+        for (int m = 0; m < NS; ++m) {
+          const uint4 x = cw[ONE ? m0 : m];                 // step m: 8 channels
           Kc[m][rp][0] = x.x; Kc[m][rp][1] = x.y; Kc[m][rp][2] = x.z; Kc[m][rp][3] = x.w;
         }
       } else {
@@ -349,11 +357,16 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
           const int c = 8 * rp + 2 * q4 + half;             // chunk = channels 4c .. 4c+3
           const uint32_t ik = __builtin_amdgcn_ubfe(kd[c >> 2], 8 * (c & 3), 8);
           const uint4* cw = &s_k[ik * CWS];
-          const uint4 x0 = cw[0], x1 = cw[1];               // steps 0-1, 2-3
-          Kc[0][rp][2 * half] = x0.x; Kc[0][rp][2 * half + 1] = x0.y;
-          Kc[1][rp][2 * half] = x0.z; Kc[1][rp][2 * half + 1] = x0.w;
-          Kc[2][rp][2 * half] = x1.x; Kc[2][rp][2 * half + 1] = x1.y;
-          Kc[3][rp][2 * half] = x1.z; Kc[3][rp][2 * half + 1] = x1.w;
+          if constexpr (ONE) {
+            const uint2 x = reinterpret_cast<const uint2*>(cw)[m0];   // step m0: 4 channels
+            Kc[0][rp][2 * half] = x.x; Kc[0][rp][2 * half + 1] = x.y;
+          } else {
+            const uint4 x0 = cw[0], x1 = cw[1];             // steps 0-1, 2-3
+            Kc[0][rp][2 * half] = x0.x; Kc[0][rp][2 * half + 1] = x0.y;
+            Kc[1][rp][2 * half] = x0.z; Kc[1][rp][2 * half + 1] = x0.w;
+            Kc[NS - 2][rp][2 * half] = x1.x; Kc[NS - 2][rp][2 * half + 1] = x1.y;
+            Kc[NS - 1][rp][2 * half] = x1.z; Kc[NS - 1][rp][2 * half + 1] = x1.w;
+          }
         }
       }
     }
@@ -387,7 +400,7 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
     const int w0 = base + wave * 2 * TILE;
     float s[8];
     {
-      uint32_t Kc[TC][4][4];
+      uint32_t Kc[NS][4][4];
       gather_k(krow[0], Kc);
       float s0[4];
       score_tile(Kc, CS, s0);
@@ -411,8 +424,9 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
     }
     if (base + NW * 2 * TILE < n_tok) load_rows(base + NW * 2 * TILE, krow, vrow);
 #pragma unroll
-    for (int m = 0; m < TC; ++m) {
-      const h8_t Pm = mrow == m ? P : (h8_t){};
+    for (int mi = 0; mi < NS; ++mi) {
+      const int m = ONE ? m0 : mi;
+      const h8_t Pm = ONE || mrow == m ? P : (h8_t){};
 #pragma unroll
       for (int bl = 0; bl < 8; ++bl) {
         const h4g_t lo = lds_tr4(s_v, voff[0][bl] + SOFF * m);
@@ -436,9 +450,10 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
       const int it = item < n_bf ? item : 0;
       const bool is_rec = it >= n_sink;
       const int pos = is_rec ? a.n_s + nb + (it - n_sink) : it;
-      uint32_t Kc[TC][4][4];
+      uint32_t Kc[NS][4][4];
 #pragma unroll
-      for (int m = 0; m < TC; ++m) {
+      for (int mi = 0; mi < NS; ++mi) {
+        const int m = ONE ? m0 : mi;
         const uint16_t* kr = is_rec ? a.rk + (rec0 + (int64_t)m * a.r_cap + (it - n_sink)) * D
                                     : a.sk + (sink0 + (int64_t)m * a.n_s + it) * D;
 #pragma unroll
@@ -446,7 +461,7 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
           const uint4 w = *reinterpret_cast<const uint4*>(kr + 32 * rp + 8 * q4);
           const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-          for (int e = 0; e < 4; ++e) Kc[m][rp][e] = pack_h2g(bf16lo(ws[e]) * ksc, bf16hi(ws[e]) * ksc);
+          for (int e = 0; e < 4; ++e) Kc[mi][rp][e] = pack_h2g(bf16lo(ws[e]) * ksc, bf16hi(ws[e]) * ksc);
         }
       }
       uint4 CSb[2][2];
@@ -465,7 +480,8 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
     const int sit = w0 + si < n_bf ? w0 + si : 0;
     const bool s_rec = sit >= n_sink;
 #pragma unroll 1
-    for (int m = 0; m < TC; ++m) {
+    for (int mi = 0; mi < NS; ++mi) {
+      const int m = ONE ? m0 : mi;
       const uint16_t* vr = s_rec ? a.rv + (rec0 + (int64_t)m * a.r_cap + (sit - n_sink)) * D
                                  : a.sv + (sink0 + (int64_t)m * a.n_s + sit) * D;
 #pragma unroll
@@ -476,7 +492,7 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
                        pack_h2g(bf16lo(w.z) * vsc, bf16hi(w.z) * vsc), pack_h2g(bf16lo(w.w) * vsc, bf16hi(w.w) * vsc));
       }
       wave_sync();
-      const h8_t Pm = mrow == m ? P : (h8_t){};
+      const h8_t Pm = ONE || mrow == m ? P : (h8_t){};
       const uint32_t roff = (uint32_t)((4 * grp + vj) * SROW + 4 * va) * 2;
 #pragma unroll
       for (int bl = 0; bl < 8; ++bl) {
@@ -527,21 +543,24 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
   }
 }
 
-template <int C>
+template <int C, bool ONE>
 static hipError_t launch_gqa_c(int hpw, const DecodeArgs& a, hipStream_t s) {
   const dim3 grid(a.n_split, a.Hq / hpw, a.B * a.n_blk_serv);
   if (hpw == 4)
-    hipLaunchKernelGGL((decode_gqa_kernel<C, 4>), grid, dim3(kDecodeThreads), 0, s, a);
+    hipLaunchKernelGGL((decode_gqa_kernel<C, 4, ONE>), grid, dim3(kDecodeThreads), 0, s, a);
   else if (hpw == 2)
-    hipLaunchKernelGGL((decode_gqa_kernel<C, 2>), grid, dim3(kDecodeThreads), 0, s, a);
+    hipLaunchKernelGGL((decode_gqa_kernel<C, 2, ONE>), grid, dim3(kDecodeThreads), 0, s, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
 hipError_t launch_decode_gqa(int G, int hpw, const DecodeArgs& a, hipStream_t s) {
-  if (G == 16) return launch_gqa_c<4>(hpw, a, s);
-  if (G == 32) return launch_gqa_c<8>(hpw, a, s);
+  // one served step: only that step's slices are read (the plan serves it in
+  // a single block)
+  const bool one = a.n_steps == 1;
+  if (G == 16) return one ? launch_gqa_c<4, true>(hpw, a, s) : launch_gqa_c<4, false>(hpw, a, s);
+  if (G == 32) return one ? launch_gqa_c<8, true>(hpw, a, s) : launch_gqa_c<8, false>(hpw, a, s);
   return hipErrorInvalidValue;
 }
 

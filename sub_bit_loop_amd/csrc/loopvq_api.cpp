@@ -79,19 +79,19 @@ DecodePlan plan_decode(const loopvq_geom* g, int B, int N, int step0, int n_step
   p.n_blk_serv = blk1 - p.blk0 + 1;
   const int gqa = g->n_q_heads / g->n_kv_heads;
   p.hpw = gqa % 4 == 0 ? 4 : (gqa % 2 == 0 ? 2 : 1);
-  // Blocks of four steps: GQA groups of two or four q-heads with several steps
-  // served use the MFMA kernel (two or four heads x four steps = 8 or 16
-  // score rows per token); a single served step uses the single-step kernel
-  // (one workgroup per step, q-heads sharing gathers and rotation); other
-  // groups use the multi-step kernel, which decodes each index row once for
-  // all steps of its block.  Pre-transformed keys in blocks of four steps have
+  // Blocks of four steps: GQA groups of two or four q-heads use the MFMA
+  // kernel (two or four heads x the served steps as score rows; a single
+  // served step reads only its own codeword slices); other groups use the
+  // single-step kernel for one served step (one workgroup per step) and
+  // otherwise the multi-step kernel, which decodes each index row once for all
+  // steps of its block.  Pre-transformed keys in blocks of four steps have
   // their own kernel (one q-head per workgroup); other block lengths use the
   // generic kernel.
   if (g->T_c != 4)
     p.kernel = DecodeKernel::kGeneric;
   else if (tasq)
     p.kernel = DecodeKernel::kTasq;
-  else if (p.hpw > 1 && n_steps > 1)
+  else if (p.hpw > 1)
     p.kernel = DecodeKernel::kGqa;
   else if (n_steps == 1)
     p.kernel = DecodeKernel::kStep;
