@@ -448,7 +448,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_fast_kernel(DecodeArgs 
 // and the codeword gathers and the RoPE rotation of a key are shared by the
 // HPW heads.  Lane (g4, s2) owns the chunk pairs (q, q + D/(2c)) for
 // q = g4 + 4 (s2 + 2k).  Used for per-step calls (n_steps = 1, the review's
-// own per-step use) and, one workgroup per step, for GQA groups.
+// own per-step use) with one q-head per workgroup (GQA groups of two or four
+// take the MFMA kernel of decode_gqa.hip).
 template <int C, int HPW>
 __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(DecodeArgs a) {
   constexpr int D = 128, HD = 64, TC = 4, G = C * TC, CPT = D / C;
@@ -811,22 +812,15 @@ hipError_t launch_decode_fast(int G, const DecodeArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int C>
-static hipError_t step_launch(int hpw, const DecodeArgs& a, hipStream_t s) {
-  dim3 grid(a.n_split, a.Hq / hpw, a.B * a.n_steps);
-  switch (hpw) {
-    case 1: hipLaunchKernelGGL((decode_step_kernel<C, 1>), grid, dim3(kDecodeThreads), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((decode_step_kernel<C, 2>), grid, dim3(kDecodeThreads), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((decode_step_kernel<C, 4>), grid, dim3(kDecodeThreads), 0, s, a); break;
-    default: return hipErrorInvalidValue;
-  }
+hipError_t launch_decode_step(int G, const DecodeArgs& a, hipStream_t s) {
+  const dim3 grid(a.n_split, a.Hq, a.B * a.n_steps);
+  if (G == 16)
+    hipLaunchKernelGGL((decode_step_kernel<4, 1>), grid, dim3(kDecodeThreads), 0, s, a);
+  else if (G == 32)
+    hipLaunchKernelGGL((decode_step_kernel<8, 1>), grid, dim3(kDecodeThreads), 0, s, a);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
-}
-
-hipError_t launch_decode_step(int G, int hpw, const DecodeArgs& a, hipStream_t s) {
-  if (G == 16) return step_launch<4>(hpw, a, s);
-  if (G == 32) return step_launch<8>(hpw, a, s);
-  return hipErrorInvalidValue;
 }
 
 }  // namespace loopvq

@@ -120,9 +120,9 @@ hipError_t launch_kmeans_accumulate(const KmeansArgs& a, int B, bool tasq, hipSt
 hipError_t launch_kmeans_finalize(const double* sums, const double* wsum, uint16_t* cb, int64_t n, int G,
                                   hipStream_t s);
 hipError_t launch_decode_fast(int G, const DecodeArgs& a, hipStream_t s);
-// T_c = 4, no pre-transform; one workgroup per (split, group of hpw q-heads,
-// batch x served step); hpw in {1, 2, 4} divides the GQA group size.
-hipError_t launch_decode_step(int G, int hpw, const DecodeArgs& a, hipStream_t s);
+// T_c = 4, no pre-transform; one workgroup per (split, q-head, batch x served
+// step).
+hipError_t launch_decode_step(int G, const DecodeArgs& a, hipStream_t s);
 // T_c = 4, no pre-transform, hpw in {2, 4} q-heads of a GQA group per
 // workgroup; grid (n_split, Hq/hpw, B x blocks)
 hipError_t launch_decode_gqa(int G, int hpw, const DecodeArgs& a, hipStream_t s);

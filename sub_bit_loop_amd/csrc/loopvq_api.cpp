@@ -67,7 +67,7 @@ enum class DecodeKernel { kGeneric, kFast, kStep, kGqa, kTasq };
 
 struct DecodePlan {
   int n_blk_serv, blk0, n_split, tok_per_split;
-  int hpw;              // q-heads per workgroup of the single-step kernel
+  int hpw;              // q-heads per workgroup of the MFMA kernel (2 or 4; 1: other kernels)
   DecodeKernel kernel;
   size_t ws_bytes;
 };
@@ -101,8 +101,8 @@ DecodePlan plan_decode(const loopvq_geom* g, int B, int N, int step0, int n_step
   int target;   // about one resident round of workgroups
   switch (p.kernel) {
     case DecodeKernel::kStep:
-      wgs = (long long)B * (g->n_q_heads / p.hpw) * n_steps;
-      target = p.hpw == 1 ? 1024 : 512;   // 95 VGPRs: 4 per CU; more heads: 2
+      wgs = (long long)B * g->n_q_heads * n_steps;
+      target = 1024;                       // 95 VGPRs: 4 per CU
       break;
     case DecodeKernel::kGqa:
       wgs = (long long)B * (g->n_q_heads / p.hpw) * p.n_blk_serv;
@@ -496,7 +496,7 @@ loopvq_status loopvq_decode_attn(const loopvq_geom* g, const void* q, int32_t st
   else if (p.kernel == DecodeKernel::kGqa)
     e = loopvq::launch_decode_gqa(g->G, p.hpw, a, s);
   else if (p.kernel == DecodeKernel::kStep)
-    e = loopvq::launch_decode_step(g->G, p.hpw, a, s);
+    e = loopvq::launch_decode_step(g->G, a, s);
   else
     e = loopvq::launch_decode_fast(g->G, a, s);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
