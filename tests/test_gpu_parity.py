@@ -154,6 +154,7 @@ GEOMS = [
     ("two-blocks-gqa2", 16, 4, 8, 2, 4, 2, 1000, 4, 256, False),
     ("quarter-bit-gqa4", 32, 4, 4, 2, 8, 2, 701, 4, 256, False),
     ("half-bit-gqa4", 16, 4, 4, 1, 4, 2, 555, 4, 256, False),
+    ("quarter-bit-gqa8", 32, 4, 4, 1, 8, 1, 333, 4, 256, False),
     ("quarter-bit-mha", 32, 4, 4, 2, 2, 2, 650, 4, 256, False),
     ("quarter-bit-2blk-gqa2", 32, 4, 8, 1, 2, 1, 480, 4, 256, False),
     ("pretransform", 16, 4, 4, 2, 2, 2, 777, 4, 256, True),
