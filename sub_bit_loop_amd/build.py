@@ -15,7 +15,8 @@ LIB = os.path.join(HERE, "libloopvq.so")
 CALIB_LIB = os.path.join(HERE, "libloopvq_calib.so")
 CALIB_SOURCES = ["calib.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["encode.hip", "decode.hip", "decode_fast.hip", "decode_half.hip", "decode_gqa.hip", "decode_tasq.hip", "tasq_stats.hip",
+SOURCES = ["encode.hip", "decode.hip", "decode_fast.hip", "decode_half.hip", "decode_gqa.hip", "decode_tasq.hip", "decode_cq.hip",
+           "tasq_stats.hip",
            "kmeans.hip", "prefill.hip", "loopvq_api.cpp"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

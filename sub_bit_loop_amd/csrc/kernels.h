@@ -136,6 +136,9 @@ constexpr int kEncodeTokens = 128;  // tokens per encode workgroup
 
 // fused decode for G = 16, T_c = 4 (c = 4), D = 128, plain keys
 hipError_t launch_decode_half(const DecodeArgs& a, hipStream_t s);
+// T_c = 1, G = 16 (per-step codebooks of 16 channels), no pre-transform; grid
+// (n_split, Hq, B x served steps)
+hipError_t launch_decode_cq(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_fill_f32(float* p, int64_t n, hipStream_t s);   // p[0..n) = 0
 hipError_t launch_rope_table_f32(float* tab, int n_pos, int D, double theta, hipStream_t s);
 // forward (out, lse) or backward (delta, zeroed then accumulated codebook

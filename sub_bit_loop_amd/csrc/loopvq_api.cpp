@@ -63,7 +63,7 @@ loopvq_status check_pt(const loopvq_pretransform* pt, int B, int tok_end, bool n
   return LOOPVQ_OK;
 }
 
-enum class DecodeKernel { kGeneric, kFast, kStep, kGqa, kTasq };
+enum class DecodeKernel { kGeneric, kFast, kStep, kGqa, kTasq, kCq };
 
 struct DecodePlan {
   int n_blk_serv, blk0, n_split, tok_per_split;
@@ -86,8 +86,11 @@ DecodePlan plan_decode(const loopvq_geom* g, int B, int N, int step0, int n_step
   // otherwise the multi-step kernel, which decodes each index row once for all
   // steps of its block.  Pre-transformed keys in blocks of four steps have
   // their own kernel (one q-head per workgroup); other block lengths use the
-  // generic kernel.
-  if (g->T_c != 4)
+  // generic kernel, except per-step codebooks (T_c = 1) of 16 channels, which
+  // have their own kernel.
+  if (g->T_c == 1 && g->G == 16 && !tasq)
+    p.kernel = DecodeKernel::kCq;
+  else if (g->T_c != 4)
     p.kernel = DecodeKernel::kGeneric;
   else if (tasq)
     p.kernel = DecodeKernel::kTasq;
@@ -491,6 +494,8 @@ loopvq_status loopvq_decode_attn(const loopvq_geom* g, const void* q, int32_t st
   hipError_t e;
   if (p.kernel == DecodeKernel::kGeneric)
     e = loopvq::launch_decode(g->G, g->T_c, pt != nullptr, a, s);
+  else if (p.kernel == DecodeKernel::kCq)
+    e = loopvq::launch_decode_cq(a, s);
   else if (p.kernel == DecodeKernel::kTasq)
     e = loopvq::launch_decode_tasq(g->G, a, s);
   else if (p.kernel == DecodeKernel::kGqa)

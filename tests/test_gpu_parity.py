@@ -203,22 +203,23 @@ def test_small_geometries(geo):
 
 
 EDGE_GEOMS = [
-    # name, G, T, H_kv, H_q, pretransform  (the plain multi-step kernel, the GQA MFMA
-    # kernel with four and two q-heads per workgroup, and the pre-transform kernel;
-    # T = 8 gives ranges that cross a block boundary)
-    ("mha", 16, 4, 1, 1, False),
-    ("gqa4-2blk", 32, 8, 1, 4, False),
-    ("gqa2-2blk", 16, 8, 1, 2, False),
-    ("pretransform-2blk", 16, 8, 1, 1, True),
+    # name, G, T, T_c, H_kv, H_q, pretransform  (the plain multi-step kernel, the GQA
+    # MFMA kernel with four and two q-heads per workgroup, the pre-transform kernel and
+    # the per-step-codebook kernel; T = 8 gives ranges that cross a block boundary)
+    ("mha", 16, 4, 4, 1, 1, False),
+    ("gqa4-2blk", 32, 8, 4, 1, 4, False),
+    ("gqa2-2blk", 16, 8, 4, 1, 2, False),
+    ("pretransform-2blk", 16, 8, 4, 1, 1, True),
+    ("per-step-codebooks", 16, 8, 1, 1, 2, False),
 ]
 
 
 @pytest.mark.parametrize("geo", EDGE_GEOMS, ids=[x[0] for x in EDGE_GEOMS])
 def test_edge_cases(geo):
     s = _lib()
-    name, G, T, H, Hq, tasq = geo
+    name, G, T, T_c, H, Hq, tasq = geo
     _say("edge cases", name)
-    cfg = small_cfg(1, G=G, T=T, B=3, N=300, H_kv=H, H_q=Hq, tasq=tasq, rho_k=(0.85,) * (T - 1),
+    cfg = small_cfg(1, G=G, T=T, T_c=T_c, B=3, N=300, H_kv=H, H_q=Hq, tasq=tasq, rho_k=(0.85,) * (T - 1),
                     rho_v=(0.9,) * (T - 1), n_calib=1024, kmeans_iters=5)
     inp = build_inputs(cfg, 0, "cuda")
     kidx, vidx, sigma, pt = _encode_all(s, cfg, inp)
@@ -277,6 +278,7 @@ RECENT = [
     ("half-bit", 16, 4, 4, 2, 2, 2, 600, 64, False),
     ("quarter-bit-gqa", 32, 4, 4, 1, 4, 2, 500, 64, False),
     ("generic-tc2", 16, 2, 4, 1, 1, 2, 300, 24, False),
+    ("per-step-codebooks", 16, 1, 4, 2, 2, 2, 300, 24, False),
     ("pretransform", 16, 4, 4, 2, 2, 1, 400, 32, True),
 ]
 
