@@ -22,6 +22,7 @@ the compressed cache and its backward into the codebooks, plus whole Adam
 iterations on the toy looped stack) and prints its own JSON line.
 """
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -447,6 +448,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=2,
                     help="workload index: 1-4 single layer, 5 the 24-layer prefill + decode flow")
+    ap.add_argument("--tc", type=int, default=None,
+                    help="steps per block T_c override for workloads 1-4 (1: per-step codebooks, as for the "
+                         "layers outside the loop)")
     ap.add_argument("--cpu-tokens", type=int, default=8192, help="context tokens in the oracle sample")
     ap.add_argument("--cpu-batch", type=int, default=2, help="batch entries in the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -474,6 +478,11 @@ def main():
         finetune_flow(args, torch, lv)
         return
     cfg = config_by_index(args.config)
+    if args.tc is not None:
+        if cfg.layers != 1 or args.tc < 1 or cfg.T % args.tc or cfg.G % args.tc:
+            print("--tc needs a single-layer workload and T_c dividing T and G", file=sys.stderr)
+            sys.exit(2)
+        cfg = dataclasses.replace(cfg, T_c=args.tc)
     if cfg.layers != 1:
         workload5(args, torch, lv, cfg)
         return
