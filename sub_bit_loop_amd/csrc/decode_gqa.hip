@@ -1,5 +1,5 @@
-// LoopVQ fused decode attention for GQA groups of four q-heads over blocks of
-// four loop steps (T_c = 4, c = 4 or 8, no pre-transform).
+// LoopVQ fused decode attention for GQA groups of two or four q-heads over
+// blocks of four loop steps (T_c = 4, c = 4 or 8, no pre-transform).
 //
 // LoopVQ review (arXiv 2611.05304), section 3.4 step 3 (codebook on chip,
 // lookup by index, RoPE from a precomputed table after dequant, Flash-
@@ -27,7 +27,9 @@
 //     fetches four channels 4a .. 4a+3 of token j, and the transposed read
 //     hands every lane one channel of four tokens.
 // Every index byte is used once for K and once for V per token; every
-// codeword gather and key rotation serves all four heads.
+// codeword gather and key rotation serves all four heads.  With a single
+// served step (ONE) only that step's key slices are gathered and rotated, one
+// score chain runs and P needs no step mask.
 #include "common.h"
 #include "kernels.h"
 
