@@ -1,7 +1,8 @@
 """GPU parity at the five workloads' full sizes, in the launch configuration
 the benchmark times, checked against the fp64 oracle on sampled slices:
 seeded (batch, kv-head) encode slices over first, last and random tokens, and
-seeded decode rows over the whole context (sinks included)."""
+seeded decode rows over the whole context (sinks included), for the fused call
+over all steps and, on workloads 2 and 3, for a per-step call."""
 import numpy as np
 import pytest
 import torch
@@ -44,16 +45,28 @@ def _run_config(idx, n_enc=3, n_rows=8, layer=0):
     return s, cfg, inp, kidx, vidx, sigma, pt
 
 
+def _per_step_call(s, cfg, inp, kidx, vidx, sigma, pt, t, seed, n_rows=6):
+    """One decode call for loop step t alone (n_steps = 1), the per-step use."""
+    out, lse = _decode(s, cfg, inp, kidx, vidx, pt, N=cfg.N, step0=t, n_steps=1)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(seed)
+    rows = [(int(rng.integers(cfg.B)), int(rng.integers(cfg.H_q)), t) for _ in range(n_rows)]
+    worst = _check_rows(cfg, inp, kidx, vidx, sigma, out, lse, rows, step0=t, N=cfg.N)
+    _say("  per-step call (step %d): decode worst rel err %.3g" % (t, worst))
+
+
 def test_config1_full():
     _run_config(1, n_rows=4)
 
 
 def test_config2_full():
-    _run_config(2)
+    s, cfg, inp, kidx, vidx, sigma, pt = _run_config(2)
+    _per_step_call(s, cfg, inp, kidx, vidx, sigma, pt, 1, 2002)
 
 
 def test_config3_full():
-    _run_config(3)
+    s, cfg, inp, kidx, vidx, sigma, pt = _run_config(3)
+    _per_step_call(s, cfg, inp, kidx, vidx, sigma, pt, 2, 3003)
 
 
 def test_config4_full():
