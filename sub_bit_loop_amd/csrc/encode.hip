@@ -73,6 +73,11 @@ __global__ __launch_bounds__(kEncodeThreads) void encode_kernel(EncodeArgs a) {
   // [nh, nm, nl, 1] (||e||^2 split into three bf16 terms).
   __shared__ __attribute__((aligned(16))) uint16_t s_cb[256 * G];
   __shared__ __attribute__((aligned(16))) uint16_t s_nb[256 * 4];
+  // Codes of this workgroup (token * CPT + chunk) whose two best screened
+  // values lie within the exactness band; they are scored exactly after the
+  // screening loop, one code per wave at a time.
+  __shared__ uint16_t s_tq[kEncodeTokens * CPT];
+  __shared__ int s_tqn;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -105,6 +110,7 @@ __global__ __launch_bounds__(kEncodeThreads) void encode_kernel(EncodeArgs a) {
     uint16_t* nb = s_nb + r * 4;
     nb[0] = nh; nb[1] = nm; nb[2] = nl; nb[3] = one;
   }
+  if (tid == 0) s_tqn = 0;
   __syncthreads();
 
   const int n = lane & 31, hh = lane >> 5;
@@ -380,72 +386,73 @@ __global__ __launch_bounds__(kEncodeThreads) void encode_kernel(EncodeArgs a) {
     // candidate 16t + i of half-wave hh is codebook entry 32t + 8(i/4) + 4hh + i%4
     int res = (int)(((wkey & 0x7cu) << 1) | (wkey & 3u)) | (whalf << 2);
 
-    if (__builtin_expect(__ballot(tie) != 0, 0)) {
-      // Rare path: re-screen and score every candidate inside the band exactly
-      // in fp64 (direct form, step-major positions); lowest index wins exact ties.
-      int jl, q;
-      code_pos(grp, jl, q);
-      const uint16_t* xr = xbase + (int64_t)jl * xs3;
-      double zd[G];
-      if (tie) {
-#pragma unroll
-        for (int p = 0; p < G; ++p) {
-          const int m = p / C, d = q * C + (p % C);
-          if constexpr (!TASQ) {
-            zd[p] = (double)bf16_to_f32(xr[m * xs2 + d]);
-          } else {
-            const int o = ph[d] & (D - 1);
-            const double kv = (double)bf16_to_f32(xr[m * xs2 + o]);
-            const double sg = f16_bits_to_f64(sgb[(int64_t)jl * a.T + m]);
-            zd[p] = ((double)wh[o] * kv) / sg;
-          }
-        }
-      }
-      const float lim = tie ? thr : -1.f;
-      double best = INFINITY;
-      int bi = 0x7fffffff;
-#pragma unroll 1
-      for (int t = 0; t < 8; ++t) {
-        f32x16_t acc = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        const s16x4_t rn = *reinterpret_cast<const s16x4_t*>(&s_nb[(32 * t + n) * 4]);
-        acc = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(rn, bn, acc, 0, 0, 0);
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          const bf16x8_t rv = *reinterpret_cast<const bf16x8_t*>(&s_cb[(32 * t + n) * G + 16 * kk + 8 * hh]);
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rv, cz[kk], acc, 0, 0, 0);
-          if constexpr (TASQ) {
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rv, czlo[kk], acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rv, czlo2[kk], acc, 0, 0, 0);
-          }
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float tv = __uint_as_float(__float_as_uint(acc[i]) & kmask);
-          if (tv <= lim) {
-            const int r = 32 * t + 8 * (i >> 2) + 4 * hh + (i & 3);
-            double dist = 0.0;
-            for (int p = 0; p < G; ++p) {
-              const double e = -0.5 * (double)bf16_to_f32(s_cb[r * G + p]);
-              const double df = zd[p] - e;
-              dist += df * df;
-            }
-            if (r < a.K && (dist < best || (dist == best && r < bi))) {
-              best = dist;
-              bi = r;
-            }
-          }
-        }
-      }
-      // combine the halves: smallest distance, then lowest index
-      const double obest = __shfl_xor(best, 32);
-      const int obi = __shfl_xor(bi, 32);
-      if (obest < best || (obest == best && obi < bi)) {
-        best = obest;
-        bi = obi;
-      }
-      if (tie) res = bi;
+    if (hh == 0) {
+      if (tie)
+        s_tq[atomicAdd(&s_tqn, 1)] = (uint16_t)g;
+      else if (valid)
+        ibase[g] = (uint8_t)res;
     }
-    if (hh == 0 && valid) ibase[g] = (uint8_t)res;
+  }
+
+  // Codes inside the band: every codeword is scored exactly in fp64 (direct
+  // form over the step-major positions) by the 64 lanes of a wave, four
+  // candidates per lane; the smallest distance wins, then the lowest index.
+  __syncthreads();
+  const int nq = s_tqn;
+  for (int e = wave; e < nq; e += WS) {
+    const int gq = s_tq[e];
+    const int jl = gq >> LOG_CPT, q = gq & (CPT - 1);
+    const uint16_t* xr = xbase + (int64_t)jl * xs3;
+    double zd[G];
+#pragma unroll
+    for (int p = 0; p < G; ++p) {
+      const int m = p / C, d = q * C + (p % C);
+      if constexpr (!TASQ) {
+        zd[p] = (double)bf16_to_f32(xr[m * xs2 + d]);
+      } else {
+        const int o = ph[d] & (D - 1);
+        const double kv = (double)bf16_to_f32(xr[m * xs2 + o]);
+        const double sg = f16_bits_to_f64(sgb[(int64_t)jl * a.T + m]);
+        zd[p] = ((double)wh[o] * kv) / sg;
+      }
+    }
+    double best = INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int r = lane + 64 * c;
+      if (r < a.K) {
+        const uint4* cw = reinterpret_cast<const uint4*>(&s_cb[r * G]);
+        double dist = 0.0;
+#pragma unroll
+        for (int c4 = 0; c4 < G / 8; ++c4) {
+          const uint4 w = cw[c4];
+          const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            // s_cb holds -2e, exactly
+            const double d0 = zd[8 * c4 + 2 * k] + 0.5 * (double)bf16lo(ws[k]);
+            const double d1 = zd[8 * c4 + 2 * k + 1] + 0.5 * (double)bf16hi(ws[k]);
+            dist += d0 * d0;
+            dist += d1 * d1;
+          }
+        }
+        if (dist < best) {
+          best = dist;
+          bi = r;
+        }
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const double ob = __shfl_xor(best, off);
+      const int oi = __shfl_xor(bi, off);
+      if (ob < best || (ob == best && oi < bi)) {
+        best = ob;
+        bi = oi;
+      }
+    }
+    if (lane == 0) ibase[gq] = (uint8_t)bi;
   }
 }
 
