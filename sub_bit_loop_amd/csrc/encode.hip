@@ -399,23 +399,8 @@ __global__ __launch_bounds__(kEncodeThreads) void encode_kernel(EncodeArgs a) {
   // candidates per lane; the smallest distance wins, then the lowest index.
   __syncthreads();
   const int nq = s_tqn;
-  for (int e = wave; e < nq; e += WS) {
-    const int gq = s_tq[e];
-    const int jl = gq >> LOG_CPT, q = gq & (CPT - 1);
-    const uint16_t* xr = xbase + (int64_t)jl * xs3;
-    double zd[G];
-#pragma unroll
-    for (int p = 0; p < G; ++p) {
-      const int m = p / C, d = q * C + (p % C);
-      if constexpr (!TASQ) {
-        zd[p] = (double)bf16_to_f32(xr[m * xs2 + d]);
-      } else {
-        const int o = ph[d] & (D - 1);
-        const double kv = (double)bf16_to_f32(xr[m * xs2 + o]);
-        const double sg = f16_bits_to_f64(sgb[(int64_t)jl * a.T + m]);
-        zd[p] = ((double)wh[o] * kv) / sg;
-      }
-    }
+  // exact fp64 scoring of queued code gq with joint vector zd (whole wave)
+  auto score_code = [&](int gq, const double (&zd)[G]) {
     double best = INFINITY;
     int bi = 0x7fffffff;
 #pragma unroll
@@ -453,6 +438,195 @@ __global__ __launch_bounds__(kEncodeThreads) void encode_kernel(EncodeArgs a) {
       }
     }
     if (lane == 0) ibase[gq] = (uint8_t)bi;
+  };
+  if constexpr (!TASQ) {
+    // raw bf16 words of a queued code (positions p = m*C + i: C contiguous
+    // channels per step) as fp64
+    auto load_zd = [&](int gq, double (&zd)[G]) {
+      const int jl = gq >> LOG_CPT, q = gq & (CPT - 1);
+      const uint16_t* xr = xbase + (int64_t)jl * xs3 + q * C;
+      uint32_t zw[G / 2];
+#pragma unroll
+      for (int m = 0; m < TC; ++m) {
+        const uint16_t* pm = xr + m * xs2;
+        if constexpr (C >= 8) {
+#pragma unroll
+          for (int u = 0; u < C / 8; ++u) {
+            const uint4 w = reinterpret_cast<const uint4*>(pm)[u];
+            zw[m * C / 2 + 4 * u] = w.x;
+            zw[m * C / 2 + 4 * u + 1] = w.y;
+            zw[m * C / 2 + 4 * u + 2] = w.z;
+            zw[m * C / 2 + 4 * u + 3] = w.w;
+          }
+        } else if constexpr (C == 4) {
+          const uint2 w = *reinterpret_cast<const uint2*>(pm);
+          zw[2 * m] = w.x;
+          zw[2 * m + 1] = w.y;
+        } else {
+          zw[m] = *reinterpret_cast<const uint32_t*>(pm);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < G / 2; ++k) {
+        zd[2 * k] = (double)bf16lo(zw[k]);
+        zd[2 * k + 1] = (double)bf16hi(zw[k]);
+      }
+    };
+    // exact fp64 distance of zd to codebook row r (s_cb holds -2e, exactly)
+    auto exact_dist = [&](const double (&zd)[G], int r) {
+      const uint4* cw = reinterpret_cast<const uint4*>(&s_cb[r * G]);
+      double dist = 0.0;
+#pragma unroll
+      for (int c4 = 0; c4 < G / 8; ++c4) {
+        const uint4 w = cw[c4];
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const double d0 = zd[8 * c4 + 2 * k] + 0.5 * (double)bf16lo(ws[k]);
+          const double d1 = zd[8 * c4 + 2 * k + 1] + 0.5 * (double)bf16hi(ws[k]);
+          dist += d0 * d0;
+          dist += d1 * d1;
+        }
+      }
+      return dist;
+    };
+    // Batches of 32 queued codes per wave, screened again on the matrix cores
+    // as in the loop above but keeping each half-wave's three best keys: the
+    // band then holds at most its two best candidates, which are scored
+    // exactly; a half with three or more inside the band sends its code to
+    // the full scoring of every codeword.
+    constexpr float kErrQ = (float)(2 * G + 16) * 0x1p-24f;
+    constexpr float kAQ = 1.f + 0x1p-14f + 4.25f * kErrQ, kBQ = 6.11f * kErrQ;
+    for (int bq = wave * 32; bq < nq; bq += WS * 32) {
+      const bool qv = bq + n < nq;
+      const int gq = s_tq[qv ? bq + n : bq];     // lanes past the end repeat a real code
+      bf16x8_t qz[KK];
+      {
+        const int jl = gq >> LOG_CPT, q = gq & (CPT - 1);
+        const uint16_t* xr = xbase + (int64_t)jl * xs3 + q * C;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          const int p0 = 8 * (2 * kk + hh);
+          const uint16_t* pz = xr + (int64_t)(p0 / C) * xs2 + (p0 % C);
+          if constexpr (CW == 8) {
+            qz[kk] = *reinterpret_cast<const bf16x8_t*>(pz);
+          } else {
+            uint32_t w[4];
+#pragma unroll
+            for (int l = 0; l < NL; ++l) {
+              if constexpr (CW == 4) {
+                const uint2 v = *reinterpret_cast<const uint2*>(pz + l * xs2);
+                w[2 * l] = v.x;
+                w[2 * l + 1] = v.y;
+              } else {
+                w[l] = *reinterpret_cast<const uint32_t*>(pz + l * xs2);
+              }
+            }
+            qz[kk] = __builtin_bit_cast(bf16x8_t, (uint4){w[0], w[1], w[2], w[3]});
+          }
+        }
+      }
+      float zq = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const uint4 w = __builtin_bit_cast(uint4, qz[kk]);
+        zq = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.x), __builtin_bit_cast(bf16x2_t, w.x), zq, false);
+        zq = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.y), __builtin_bit_cast(bf16x2_t, w.y), zq, false);
+        zq = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.z), __builtin_bit_cast(bf16x2_t, w.z), zq, false);
+        zq = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.w), __builtin_bit_cast(bf16x2_t, w.w), zq, false);
+      }
+      {
+        const auto zs = __builtin_amdgcn_permlane32_swap(__float_as_uint(zq), __float_as_uint(zq), false, false);
+        zq = __uint_as_float(zs[0]) + __uint_as_float(zs[1]);
+      }
+      const uint32_t zqu = __float_as_uint(fmaf(zq, 1.f + 0x1p-8f, 1e-30f));
+      const uint2 bqw = {bn_lo, ((zqu + 0xffffu) & bn_hmask) | bn_one};
+      const s16x4_t bnq = __builtin_bit_cast(s16x4_t, bqw);
+      float k1 = INFINITY, k2 = INFINITY, k3 = INFINITY;
+      // codeword operands from LDS (a runtime loop keeps the registers of this
+      // rare phase below those of the screening loop)
+#pragma unroll 1
+      for (int t = 0; t < 8; ++t) {
+        f32x16_t acc = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        const s16x4_t rn = *reinterpret_cast<const s16x4_t*>(&s_nb[(32 * t + n) * 4]);
+        acc = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(rn, bnq, acc, 0, 0, 0);
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          const bf16x8_t rv = *reinterpret_cast<const bf16x8_t*>(&s_cb[(32 * t + n) * G + 16 * kk + 8 * hh]);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rv, qz[kk], acc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float key = __uint_as_float(__builtin_amdgcn_perm(__float_as_uint(acc[i]), (uint32_t)(16 * t + i), 0x07060500u));
+          const float n3 = __builtin_amdgcn_fmed3f(k2, k3, key);
+          const float n2 = __builtin_amdgcn_fmed3f(k1, k2, key);
+          k1 = fminf(k1, key);
+          k2 = n2;
+          k3 = n3;
+        }
+      }
+      const auto s1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(k1), __float_as_uint(k1), false, false);
+      const float t1 = fminf(__uint_as_float(s1[0] & kmask), __uint_as_float(s1[1] & kmask));
+      const float thr = fmaf(kAQ, t1, kBQ * zq);
+      const bool in1 = __uint_as_float(__float_as_uint(k1) & kmask) <= thr;
+      const bool in2 = __uint_as_float(__float_as_uint(k2) & kmask) <= thr;
+      const bool wide = __uint_as_float(__float_as_uint(k3) & kmask) <= thr;
+      double zd[G];
+      load_zd(gq, zd);
+      double best = INFINITY;
+      int bi = 0x7fffffff;
+      // candidate number 16t + i of half hh is codebook row 32t + 8(i/4) + 4hh + i%4
+      const uint32_t b1 = __float_as_uint(k1) & 0xffu, b2 = __float_as_uint(k2) & 0xffu;
+      const int r1 = (int)(((b1 & 0x7cu) << 1) | (b1 & 3u)) | (hh << 2);
+      const int r2 = (int)(((b2 & 0x7cu) << 1) | (b2 & 3u)) | (hh << 2);
+      if (in1 && r1 < a.K) {
+        best = exact_dist(zd, r1);
+        bi = r1;
+      }
+      if (in2 && r2 < a.K) {
+        const int r = r2;
+        const double d = exact_dist(zd, r);
+        if (d < best || (d == best && r < bi)) {
+          best = d;
+          bi = r;
+        }
+      }
+      {
+        const double ob = __shfl_xor(best, 32);
+        const int oi = __shfl_xor(bi, 32);
+        if (ob < best || (ob == best && oi < bi)) {
+          best = ob;
+          bi = oi;
+        }
+      }
+      const bool full = wide || __shfl_xor((int)wide, 32) != 0;
+      if (hh == 0 && qv && !full) ibase[gq] = (uint8_t)bi;
+      uint64_t fm = __ballot(hh == 0 && qv && full);
+      while (fm) {
+        const int ln = __builtin_ctzll(fm);
+        fm &= fm - 1;
+        const int gf = __shfl(gq, ln);
+        double zf[G];
+        load_zd(gf, zf);
+        score_code(gf, zf);
+      }
+    }
+  } else {
+    for (int e = wave; e < nq; e += WS) {
+      const int gq = s_tq[e];
+      const int jl = gq >> LOG_CPT, q = gq & (CPT - 1);
+      const uint16_t* xr = xbase + (int64_t)jl * xs3;
+      double zd[G];
+#pragma unroll
+      for (int p = 0; p < G; ++p) {
+        const int m = p / C, d = q * C + (p % C);
+        const int o = ph[d] & (D - 1);
+        const double kv = (double)bf16_to_f32(xr[m * xs2 + o]);
+        const double sg = f16_bits_to_f64(sgb[(int64_t)jl * a.T + m]);
+        zd[p] = ((double)wh[o] * kv) / sg;
+      }
+      score_code(gq, zd);
+    }
   }
 }
 
