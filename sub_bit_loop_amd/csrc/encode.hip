@@ -60,7 +60,7 @@ __device__ __forceinline__ void split3(float x, uint16_t& h, uint16_t& m, uint16
 }
 
 template <int G, int TC, bool TASQ>
-__global__ __launch_bounds__(kEncodeThreads) void encode_kernel(EncodeArgs a) {
+__global__ __launch_bounds__(kEncodeThreads, (G == 16 && !TASQ) ? 4 : 1) void encode_kernel(EncodeArgs a) {
   constexpr int D = 128;
   constexpr int C = G / TC;          // channels per step per code
   constexpr int CPT = D / C;         // codes per token
@@ -69,10 +69,23 @@ __global__ __launch_bounds__(kEncodeThreads) void encode_kernel(EncodeArgs a) {
   constexpr int CW = C < 8 ? C : 8;  // contiguous channels per load
   constexpr int NL = 8 / CW;         // loads per 8-position slot
   static_assert(C >= 2 && (CPT & (CPT - 1)) == 0, "unsupported code shape");
+  // Selection per group of four candidates (plain inputs, G = 16) or per
+  // candidate.  At G = 32 the matrix cores take 1.5x longer per group of
+  // codes and the per-candidate form measured faster.
+  constexpr bool kGroups = !TASQ && G == 16;
   // Per codebook row: -2*e in step-major order (G bf16) and the norm row
-  // [nh, nm, nl, 1] (||e||^2 split into three bf16 terms).
-  __shared__ __attribute__((aligned(16))) uint16_t s_cb[256 * G];
+  // [nh, nm, nl, 1] (||e||^2 split into three bf16 terms).  With group
+  // selection, rows are stored in blocks of four with 16 bytes of padding
+  // after each block, so that the 16-byte reads of the rows 4g .. 4g+3 of 64
+  // random blocks g (one per lane) spread over all LDS banks instead of two
+  // 16-byte slots.
+  constexpr int kCbBlock = kGroups ? 4 * G + 8 : 4 * G;
+  __shared__ __attribute__((aligned(16))) uint16_t s_cb[64 * kCbBlock];
+  auto cbrow = [](int r) { return (r >> 2) * kCbBlock + (r & 3) * G; };
   __shared__ __attribute__((aligned(16))) uint16_t s_nb[256 * 4];
+  // ||e||^2 in fp32 (the value nh + nm + nl), read when a group of four
+  // candidates is scored again after screening.
+  __shared__ __attribute__((aligned(16))) float s_nf[256];
   // Codes of this workgroup (token * CPT + chunk) whose two best screened
   // values lie within the exactness band; they are scored exactly after the
   // screening loop, one code per wave at a time.
@@ -96,16 +109,18 @@ __global__ __launch_bounds__(kEncodeThreads) void encode_kernel(EncodeArgs a) {
         // position p = m*C + i holds joint coordinate i*T_c + m
         const float f = bf16_to_f32(cb[r * G + (p % C) * TC + p / C]);
         s += (double)f * (double)f;
-        s_cb[r * G + p] = (uint16_t)f32_to_bf16_rne(-2.f * f);
+        s_cb[cbrow(r) + p] = (uint16_t)f32_to_bf16_rne(-2.f * f);
       }
       const float nf = (float)s;
       split3(nf, nh, nm, nl);
+      s_nf[r] = nf;
       one = 0x3f80;
     } else {
       // Padding rows never win: a huge norm, zero codeword.
 #pragma unroll
-      for (int p = 0; p < G; ++p) s_cb[r * G + p] = 0;
+      for (int p = 0; p < G; ++p) s_cb[cbrow(r) + p] = 0;
       nh = 0x7f00;   // 2^127
+      s_nf[r] = 0x1p127f;
     }
     uint16_t* nb = s_nb + r * 4;
     nb[0] = nh; nb[1] = nm; nb[2] = nl; nb[3] = one;
@@ -125,7 +140,7 @@ __global__ __launch_bounds__(kEncodeThreads) void encode_kernel(EncodeArgs a) {
     an[t] = *reinterpret_cast<const s16x4_t*>(&s_nb[(32 * t + n) * 4]);
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
-      av[t][kk] = *reinterpret_cast<const bf16x8_t*>(&s_cb[(32 * t + n) * G + 16 * kk + 8 * hh]);
+      av[t][kk] = *reinterpret_cast<const bf16x8_t*>(&s_cb[cbrow(32 * t + n) + 16 * kk + 8 * hh]);
   }
 
   const int j0 = blockIdx.x * kEncodeTokens;
@@ -331,6 +346,7 @@ __global__ __launch_bounds__(kEncodeThreads) void encode_kernel(EncodeArgs a) {
       }
       return acc;
     };
+    // Per candidate: the key of every screened value.
     auto select = [&](const f32x16_t& acc, int t) {
 #pragma unroll
       for (int i = 0; i < 16; i += 2) {
@@ -342,13 +358,34 @@ __global__ __launch_bounds__(kEncodeThreads) void encode_kernel(EncodeArgs a) {
         k2 = fminf(k2, md);
       }
     };
+    // Per group of four: accumulators 4j .. 4j+3 of tile t are
+    // the four consecutive codewords 32t + 8j + 4hh .. +3.  Only the smallest
+    // screened value of a group gets a key (low byte: group number 4t + j);
+    // the winning group is scored again below to find its member.
+    auto select_groups = [&](const f32x16_t& acc, int t) {
+      float gk[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float gm = fminf(fminf(acc[4 * j], acc[4 * j + 1]), fminf(acc[4 * j + 2], acc[4 * j + 3]));
+        gk[j] = __uint_as_float(__builtin_amdgcn_perm(__float_as_uint(gm), (uint32_t)(4 * t + j), 0x07060500u));
+      }
+#pragma unroll
+      for (int j = 0; j < 4; j += 2) {
+        const float md = __builtin_amdgcn_fmed3f(k1, gk[j], gk[j + 1]);
+        k1 = fminf(k1, fminf(gk[j], gk[j + 1]));
+        k2 = fminf(k2, md);
+      }
+    };
     // The norm product of tile t+1 is issued before tile t's selection.
     f32x16_t accn = norms(0);
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const f32x16_t acc = screen(accn, t);
       if (t + 1 < 8) accn = norms(t + 1);
-      select(acc, t);
+      if constexpr (kGroups)
+        select_groups(acc, t);
+      else
+        select(acc, t);
     }
     // Merge the two half-waves (lanes n and n+32 screen different codewords):
     // after the swaps both lanes of a code hold the first half's keys (a*)
@@ -382,9 +419,58 @@ __global__ __launch_bounds__(kEncodeThreads) void encode_kernel(EncodeArgs a) {
     constexpr float kA = TASQ ? 1.f + 0x1p-14f + 12.75f * kErr + 4.25f * 0x1p-21f : 1.f + 0x1p-14f + 4.25f * kErr;
     constexpr float kB = TASQ ? 18.31f * kErr + 6.07f * 0x1p-21f : 6.11f * kErr;
     const float thr = fmaf(kA, t1, kB * zz);
-    const bool tie = valid && !(t2 > thr);
-    // candidate 16t + i of half-wave hh is codebook entry 32t + 8(i/4) + 4hh + i%4
-    int res = (int)(((wkey & 0x7cu) << 1) | (wkey & 3u)) | (whalf << 2);
+    bool tie;
+    int res;
+    if constexpr (!kGroups) {
+      tie = valid && !(t2 > thr);
+      // candidate 16t + i of half-wave hh is codebook entry 32t + 8(i/4) + 4hh + i%4
+      res = (int)(((wkey & 0x7cu) << 1) | (wkey & 3u)) | (whalf << 2);
+    } else {
+      // The winning group (codewords r0 .. r0+3) scored again in fp32 with
+      // the screening's margin u: each half-wave sums its eight positions per
+      // kk, the halves are added.  At most G + 3 roundings, each within
+      // 2^-24 * 2 (||e||^2 + u), so these values obey the screened values'
+      // error bound and the band above applies to them.  The candidate that
+      // gave t1 is re-scored to at most thr, so the group's smallest value
+      // is always inside the band; the code is exact unless another member
+      // (sv) or another group (t2) also reaches it.
+      const uint32_t gid = wkey & 0x1fu;
+      const int r0 = (int)(32 * (gid >> 2) + 8 * (gid & 3u)) + 4 * whalf;
+      const float ub = __uint_as_float((zzu + 0xffffu) & 0xffff0000u);   // u, as the norm product used it
+      const float4 nf4 = *reinterpret_cast<const float4*>(&s_nf[r0]);
+      const float nfv[4] = {nf4.x, nf4.y, nf4.z, nf4.w};
+      float d[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        float part = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          const uint4 w = *reinterpret_cast<const uint4*>(&s_cb[cbrow(r0 + c) + 16 * kk + 8 * hh]);
+          const uint4 z = __builtin_bit_cast(uint4, cz[kk]);
+          part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, z.x), __builtin_bit_cast(bf16x2_t, w.x), part, false);
+          part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, z.y), __builtin_bit_cast(bf16x2_t, w.y), part, false);
+          part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, z.z), __builtin_bit_cast(bf16x2_t, w.z), part, false);
+          part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, z.w), __builtin_bit_cast(bf16x2_t, w.w), part, false);
+        }
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
+        d[c] = (nfv[c] + ub) + (__uint_as_float(sw[0]) + __uint_as_float(sw[1]));
+      }
+      // smallest (lowest member on equal values) and the smallest of the rest
+      float bv = d[0];
+      int bc = 0;
+#pragma unroll
+      for (int c = 1; c < 4; ++c)
+        if (d[c] < bv) {
+          bv = d[c];
+          bc = c;
+        }
+      float sv = INFINITY;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (c != bc) sv = fminf(sv, d[c]);
+      tie = valid && !(t2 > thr && sv > thr);
+      res = r0 + bc;
+    }
 
     if (hh == 0) {
       if (tie)
@@ -407,7 +493,7 @@ __global__ __launch_bounds__(kEncodeThreads) void encode_kernel(EncodeArgs a) {
     for (int c = 0; c < 4; ++c) {
       const int r = lane + 64 * c;
       if (r < a.K) {
-        const uint4* cw = reinterpret_cast<const uint4*>(&s_cb[r * G]);
+        const uint4* cw = reinterpret_cast<const uint4*>(&s_cb[cbrow(r)]);
         double dist = 0.0;
 #pragma unroll
         for (int c4 = 0; c4 < G / 8; ++c4) {
@@ -474,7 +560,7 @@ __global__ __launch_bounds__(kEncodeThreads) void encode_kernel(EncodeArgs a) {
     };
     // exact fp64 distance of zd to codebook row r (s_cb holds -2e, exactly)
     auto exact_dist = [&](const double (&zd)[G], int r) {
-      const uint4* cw = reinterpret_cast<const uint4*>(&s_cb[r * G]);
+      const uint4* cw = reinterpret_cast<const uint4*>(&s_cb[cbrow(r)]);
       double dist = 0.0;
 #pragma unroll
       for (int c4 = 0; c4 < G / 8; ++c4) {
@@ -552,7 +638,7 @@ __global__ __launch_bounds__(kEncodeThreads) void encode_kernel(EncodeArgs a) {
         acc = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(rn, bnq, acc, 0, 0, 0);
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-          const bf16x8_t rv = *reinterpret_cast<const bf16x8_t*>(&s_cb[(32 * t + n) * G + 16 * kk + 8 * hh]);
+          const bf16x8_t rv = *reinterpret_cast<const bf16x8_t*>(&s_cb[cbrow(32 * t + n) + 16 * kk + 8 * hh]);
           acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rv, qz[kk], acc, 0, 0, 0);
         }
 #pragma unroll
