@@ -426,23 +426,25 @@ __global__ __launch_bounds__(kEncodeThreads, (G == 16 && !TASQ) ? 4 : 1) void en
       // candidate 16t + i of half-wave hh is codebook entry 32t + 8(i/4) + 4hh + i%4
       res = (int)(((wkey & 0x7cu) << 1) | (wkey & 3u)) | (whalf << 2);
     } else {
-      // The winning group (codewords r0 .. r0+3) scored again in fp32 with
-      // the screening's margin u: each half-wave sums its eight positions per
-      // kk, the halves are added.  At most G + 3 roundings, each within
-      // 2^-24 * 2 (||e||^2 + u), so these values obey the screened values'
-      // error bound and the band above applies to them.  The candidate that
-      // gave t1 is re-scored to at most thr, so the group's smallest value
-      // is always inside the band; the code is exact unless another member
-      // (sv) or another group (t2) also reaches it.
+      // The winning group (codewords r0 .. r0+3) scored again in fp32: each
+      // half-wave sums its eight positions per kk (the first half starting
+      // from ||e||^2), the halves are added.  At most G + 2 roundings, each
+      // within 2^-24 * 2 (||e||^2 + u), so these values obey the screened
+      // values' error bound; they lack the margin u, so they are compared
+      // with thr - u (one more rounding, within 2^-24 thr, inside the band's
+      // 2^-15 t1 slack).  The candidate that gave t1 is re-scored to at most
+      // thr - u, so the group's smallest value is always inside the band;
+      // the code is exact unless another member (sv) or another group (t2)
+      // also reaches it.
       const uint32_t gid = wkey & 0x1fu;
       const int r0 = (int)(32 * (gid >> 2) + 8 * (gid & 3u)) + 4 * whalf;
-      const float ub = __uint_as_float((zzu + 0xffffu) & 0xffff0000u);   // u, as the norm product used it
+      const float thr_u = thr - __uint_as_float((zzu + 0xffffu) & 0xffff0000u);   // u as the norm product used it
       const float4 nf4 = *reinterpret_cast<const float4*>(&s_nf[r0]);
       const float nfv[4] = {nf4.x, nf4.y, nf4.z, nf4.w};
       float d[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        float part = 0.f;
+        float part = hh == 0 ? nfv[c] : 0.f;
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
           const uint4 w = *reinterpret_cast<const uint4*>(&s_cb[cbrow(r0 + c) + 16 * kk + 8 * hh]);
@@ -453,7 +455,7 @@ __global__ __launch_bounds__(kEncodeThreads, (G == 16 && !TASQ) ? 4 : 1) void en
           part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, z.w), __builtin_bit_cast(bf16x2_t, w.w), part, false);
         }
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
-        d[c] = (nfv[c] + ub) + (__uint_as_float(sw[0]) + __uint_as_float(sw[1]));
+        d[c] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
       }
       // smallest (lowest member on equal values) and the smallest of the rest
       float bv = d[0];
@@ -468,7 +470,7 @@ __global__ __launch_bounds__(kEncodeThreads, (G == 16 && !TASQ) ? 4 : 1) void en
 #pragma unroll
       for (int c = 0; c < 4; ++c)
         if (c != bc) sv = fminf(sv, d[c]);
-      tie = valid && !(t2 > thr && sv > thr);
+      tie = valid && !(t2 > thr && sv > thr_u);
       res = r0 + bc;
     }
 
