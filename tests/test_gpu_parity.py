@@ -174,14 +174,18 @@ def test_small_geometries(geo):
     cfg = small_cfg(1, G=G, T_c=T_c, T=T, H_kv=H, H_q=Hq, B=B, N=N, n_s=n_s, K=K, tasq=tasq,
                     rho_k=(0.85,) * (T - 1), rho_v=(0.9,) * (T - 1), n_calib=1024, kmeans_iters=8)
     inp = build_inputs(cfg, 0, "cuda", kmeans=True)
-    # plant exact codewords (and a duplicate codeword) to exercise exact ties
+    # plant exact codewords and duplicate codewords to exercise exact ties: row
+    # K-1 copies row 3 (another group of four candidates), row 6 copies row 4
+    # (the same group)
     kc = inp["k_cb"]
     kc[:, :, K - 1] = kc[:, :, 3]
+    if K >= 8:
+        kc[:, :, 6] = kc[:, :, 4]
     c = cfg.c
-    for j in range(0, min(N, 40), 7):
-        if tasq:
-            break
-        r = (j * 37) % K
+    planted = [] if tasq else [(j, (j * 37) % K) for j in range(0, min(N, 40), 7)]
+    if not tasq and K >= 8:
+        planted += [(1, 6), (2, 4)]
+    for j, r in planted:
         for beta in range(cfg.n_blk):
             for m in range(T_c):
                 for i in range(c):
@@ -197,6 +201,15 @@ def test_small_geometries(geo):
             fails += rk[2] + rv[2]
             _say("  b%d h%d K exact/tie/fail %s V %s" % (b, h, rk, rv))
     assert fails == 0
+    # a token planted on codeword r encodes every chunk to the lowest index
+    # whose codeword equals row r (the argmin's tie rule)
+    kcc = kc.cpu()
+    kic = kidx.cpu()
+    for j, r in planted:
+        for h in range(H):
+            for beta in range(cfg.n_blk):
+                same = [rr for rr in range(K) if torch.equal(kcc[h, beta, rr], kcc[h, beta, r])]
+                assert bool((kic[:, h, beta, j] == same[0]).all()), (j, r, h, beta, same[0])
     rows = [(b, hq, t) for b in range(B) for hq in range(Hq) for t in range(T)]
     worst = _check_rows(cfg, inp, kidx, vidx, sigma, out, lse, rows)
     _say("  decode worst rel err %.3g over %d rows" % (worst, len(rows)))
