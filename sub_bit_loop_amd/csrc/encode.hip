@@ -14,11 +14,14 @@
 //     s_r = ||e_r||^2 + u - 2 z.e_r    (u ~ ||z||^2, common to all r)
 // for 32 codewords per tile: a v_mfma_f32_32x32x8 for the norm terms and a
 // v_mfma_f32_32x32x16_bf16 for the products (codewords on M, codes on N).
-// Each lane keeps its best and second-best keys (value with the candidate
-// number in the low mantissa byte) with one min3, one med3 and one min per
-// two candidates.  A code whose two best screened values lie within the
-// fp32 error band is re-scored exactly in fp64 (direct form, lowest index on
-// ties), so the written index is the exact argmin.
+// At G = 16 (plain inputs) each lane reduces every four consecutive
+// codewords to their smallest screened value and keys only that value (group
+// number in the low mantissa byte); the winning group is scored again in
+// fp32 after the screening.  Otherwise every screened value gets a key
+// (candidate number in the low byte).  Best and second-best keys cost one
+// min3, one med3 and one min per two keys.  A code whose two best values lie
+// within the fp32 error band is re-scored exactly in fp64 (direct form,
+// lowest index on ties), so the written index is the exact argmin.
 #include "common.h"
 #include "kernels.h"
 
@@ -26,19 +29,26 @@ namespace loopvq {
 
 // Per-(token, step) RMS of the layer's raw keys over all heads and channels,
 // in fp64, rounded to fp16 (review section 3.3 / appendix B).  One wave per
-// token; lane l covers channels 2l, 2l+1 of every head.
+// token; a 16-byte load per lane covers four heads at once: lane l reads
+// channels 8(l % 16) .. +7 of heads l/16, l/16 + 4, ...  (rows are 16-byte
+// aligned: the entry point requires it).
 __global__ __launch_bounds__(256) void sigma_kernel(SigmaArgs a) {
   const int lane = threadIdx.x & 63;
   const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int b = blockIdx.y;
   if (j >= a.N) return;
+  const int h0 = lane >> 4, c8 = 8 * (lane & 15);
   for (int t = 0; t < a.T; ++t) {
     double s = 0.0;
-    for (int h = 0; h < a.H; ++h) {
+    for (int h = h0; h < a.H; h += 4) {
       const uint16_t* row = a.x + b * a.xs0 + h * a.xs1 + t * a.xs2 + (int64_t)j * a.xs3;
-      uint32_t wv = *reinterpret_cast<const uint32_t*>(row + 2 * lane);
-      double lo = bf16lo(wv), hi = bf16hi(wv);
-      s += lo * lo + hi * hi;
+      const uint4 w = *reinterpret_cast<const uint4*>(row + c8);
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const double lo = bf16lo(ws[k]), hi = bf16hi(ws[k]);
+        s += lo * lo + hi * hi;
+      }
     }
     for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
     if (lane == 0) {
