@@ -74,3 +74,26 @@ def test_bf16_round_is_the_library_conversion():
                         [0.0, 1.0, -2.5, 1.00390625, 1.01171875, 3.0e38]]).astype(np.float32)
     want = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
     assert np.array_equal(ref.bf16_round(x.astype(np.float64)), want)
+
+
+def test_objective_hand_worked():
+    # Eq. 3: each vector's squared distance to its nearest codeword, weighted by
+    # its importance.  Two points, one codeword: 2*1^2 + 1*2^2 = 6 (5 unweighted).
+    assert ref.weighted_kmeans_objective(np.array([[0.0], [3.0]]), np.array([2.0, 1.0]),
+                                         np.array([[1.0]])) == 6.0
+    # nearest codeword, not the first: distances 0, 16 (to (3,0)), 49 (to (3,0))
+    z = np.array([[0.0, 0.0], [3.0, 4.0], [10.0, 0.0]])
+    cb = np.array([[0.0, 0.0], [3.0, 0.0]])
+    assert ref.weighted_kmeans_objective(z, np.array([1.0, 2.0, 0.5]), cb) == 56.5
+    # zero weight removes a vector's error entirely
+    assert ref.weighted_kmeans_objective(z, np.array([0.0, 0.0, 1.0]), cb) == 49.0
+
+
+def test_objective_integer_weights_are_repeated_vectors():
+    rng = np.random.default_rng(16)
+    z, init = _clustered(rng, 300, 5, 4)
+    om = rng.integers(0, 4, size=300).astype(np.float64)
+    rep = np.repeat(z, om.astype(np.int64), axis=0)
+    # brute force over the repeated set: min over codewords, summed
+    d = ((rep[:, None, :] - init[None, :, :]) ** 2).sum(axis=-1).min(axis=1).sum()
+    assert ref.weighted_kmeans_objective(z, om, init) == pytest.approx(d, rel=1e-13)

@@ -392,3 +392,27 @@ def test_loop_axis_lowers_nmse():
     ip, _ = ref.encode(test, cbp, 1)
     e_cq = ref.nmse(test, ref.dequant(ip, cbp, 1, cfg.D))
     assert e_loop < e_shared and e_loop < e_cq
+
+
+# --------------------------------------------------------------- NMSE (Fig. 2c's measure)
+
+def test_nmse_closed_forms():
+    """Section 1.2 / Fig. 2c reports reconstruction error as NMSE: squared
+    error over squared signal, pooled over all tokens, steps and channels."""
+    # hand-worked: one channel of (3, 4) lost -> 9 / 25
+    assert ref.nmse(np.array([3.0, 4.0]), np.array([0.0, 4.0])) == 9.0 / 25.0
+    # pooled ratio, not a mean of per-row ratios: (0 + 1) / (25 + 1)
+    x = np.array([[3.0, 4.0], [1.0, 0.0]])
+    assert ref.nmse(x, np.array([[3.0, 4.0], [0.0, 0.0]])) == 1.0 / 26.0
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((4, 7, 16)) + 0.5
+    # reconstructing nothing leaves all the energy
+    assert ref.nmse(x, np.zeros_like(x)) == pytest.approx(1.0, rel=1e-15)
+    # shrinking by (1 - a) leaves a^2 of it
+    for a in (0.5, 0.125, 0.3):
+        assert ref.nmse(x, (1.0 - a) * x) == pytest.approx(a * a, rel=1e-12)
+    # uncentred: a constant signal reconstructed at half its level keeps 1/4
+    assert ref.nmse(np.full(8, 2.0), np.full(8, 1.0)) == 0.25
+    # one-entry codebook at the mean: error / energy = variance / second moment
+    v = rng.standard_normal(5000) * 2.0 + 1.0
+    assert ref.nmse(v, np.full_like(v, v.mean())) == pytest.approx(v.var() / np.mean(v * v), rel=1e-12)

@@ -129,3 +129,29 @@ def test_identity_scaling_is_invariant():
     p1 = ref.pair_grouped_permutation(ref.stacked_covariance(y1)[1], 4, 32, 4)
     p2 = ref.pair_grouped_permutation(ref.stacked_covariance(y2)[1], 4, 32, 4)
     assert np.array_equal(p1, p2)
+
+
+def test_scaled_keys_hand_worked():
+    # Section 3.3 / eq. (10): weights multiply, the token-step scale divides;
+    # sigma differs per token and per step so a swapped or inverted scale fails.
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(__file__), "golden", "tasq_scaled_keys.json")) as f:
+        g = json.load(f)
+    y = ref.tasq_scaled_keys(np.array(g["k"], float), np.array(g["w"], float),
+                             np.array(g["sigma"], float))
+    assert np.array_equal(y, np.array(g["y"], float))
+
+
+def test_scaled_keys_are_the_unpermuted_forward_transform():
+    # With the identity permutation the scaled keys are the encode's
+    # pre-transformed keys (whose hand-worked case is pinned separately).
+    rng = np.random.default_rng(7)
+    T_c, n, D = 4, 9, 16
+    k = rng.standard_normal((T_c, n, D))
+    w = rng.lognormal(0.0, 0.3, size=D)
+    sb = rng.uniform(0.25, 4.0, size=(n, T_c))
+    y = ref.tasq_scaled_keys(k, w, sb)
+    for s in range(T_c):
+        z = ref.tasq_forward(k[s], w, np.arange(D), sb[:, s])
+        assert np.allclose(y[:, s, :], z, rtol=1e-15, atol=0)
