@@ -28,6 +28,33 @@ def _need(t, dtype, name):
         raise ValueError("%s must be a device tensor" % name)
 
 
+def _shape(t, want, name):
+    """want: a tuple of ints or None (any size); raises ValueError on mismatch."""
+    if t.dim() != len(want) or any(w is not None and w != d for w, d in zip(want, t.shape)):
+        shown = tuple("*" if w is None else w for w in want)
+        raise ValueError("%s must have shape %s (got %s)" % (name, shown, tuple(t.shape)))
+
+
+def _dims(g):
+    """(n_blk, chunks per token) of a geometry."""
+    return g.T // g.T_c, g.D // (g.G // g.T_c)
+
+
+def _check_pt(g, pt, B, n_tok):
+    """The pre-transform's tensors against the geometry (B batch entries,
+    n_tok = the highest token position written or read)."""
+    if pt is None:
+        return
+    w, perm, sigma = pt._keep
+    _shape(w, (g.n_kv_heads, g.D), "w")
+    _shape(perm, (g.n_kv_heads, g.D), "perm")
+    for t, n in ((w, "w"), (perm, "perm"), (sigma, "sigma")):
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % n)
+    if sigma.dim() != 3 or sigma.shape[0] < B or sigma.shape[1] < n_tok or sigma.shape[2] != g.T:
+        raise ValueError("sigma must be [>=%d][>=%d][%d] (got %s)" % (B, n_tok, g.T, tuple(sigma.shape)))
+
+
 def _stream(stream):
     s = torch.cuda.current_stream() if stream is None else stream
     return ctypes.c_void_p(s.cuda_stream)
@@ -54,6 +81,13 @@ def encode(g: Geom, x, codebook, idx, tok0=0, pt=None, stream=None):
     if not codebook.is_contiguous() or not idx.is_contiguous():
         raise ValueError("codebook and idx must be contiguous")
     B, _, _, N, _ = x.shape
+    n_blk, cpt = _dims(g)
+    _shape(x, (B, g.n_kv_heads, g.T, N, g.D), "x")
+    _shape(codebook, (g.n_kv_heads, n_blk, g.K, g.G), "codebook")
+    _shape(idx, (B, g.n_kv_heads, n_blk, None, cpt), "idx")
+    if idx.shape[3] < tok0 + N:
+        raise ValueError("idx holds %d tokens, tok0 + N = %d" % (idx.shape[3], tok0 + N))
+    _check_pt(g, pt, B, tok0 + N)
     strides = (ctypes.c_int64 * 4)(*[x.stride(i) for i in range(4)])
     st = _lib.lib().loopvq_encode(ctypes.byref(g), _ptr(x), strides, _ptr(codebook), B, N, tok0,
                                   _ptr(idx), idx.shape[3], ctypes.byref(pt) if pt is not None else None,
@@ -73,6 +107,12 @@ def tasq_covariance(g: Geom, x, w, sigma, mean=None, cov=None, stream=None):
     if x.dim() != 5 or x.stride(4) != 1:
         raise ValueError("x must be [B][H][T][N][D] with contiguous rows")
     B, H, T, N, D = x.shape
+    _shape(x, (B, g.n_kv_heads, g.T, N, g.D), "x")
+    _shape(w, (g.n_kv_heads, g.D), "w")
+    if not w.is_contiguous() or not sigma.is_contiguous():
+        raise ValueError("w and sigma must be contiguous")
+    if sigma.dim() != 3 or sigma.shape[0] < B or sigma.shape[1] < N or sigma.shape[2] != g.T:
+        raise ValueError("sigma must be [>=%d][>=%d][%d] (got %s)" % (B, N, g.T, tuple(sigma.shape)))
     F = g.T_c * g.D
     n_blk = g.T // g.T_c
     if mean is None:
@@ -81,6 +121,10 @@ def tasq_covariance(g: Geom, x, w, sigma, mean=None, cov=None, stream=None):
         cov = torch.empty((H, n_blk, F, F), dtype=torch.float64, device=x.device)
     _need(mean, torch.float64, "mean")
     _need(cov, torch.float64, "cov")
+    _shape(mean, (H, n_blk, F), "mean")
+    _shape(cov, (H, n_blk, F, F), "cov")
+    if not mean.is_contiguous() or not cov.is_contiguous():
+        raise ValueError("mean and cov must be contiguous")
     strides = (ctypes.c_int64 * 4)(*[x.stride(i) for i in range(4)])
     check(_lib.lib().loopvq_tasq_covariance(ctypes.byref(g), _ptr(x), strides, B, N, _ptr(w), _ptr(sigma),
                                             sigma.shape[1], _ptr(mean), _ptr(cov), _stream(stream)))
@@ -118,6 +162,16 @@ def kmeans_accumulate(g: Geom, x, idx, sums, wsum, weight=None, pt=None, stream=
         if not t.is_contiguous():
             raise ValueError("%s must be contiguous" % n)
     B, _, _, N, _ = x.shape
+    n_blk, cpt = _dims(g)
+    _shape(x, (B, g.n_kv_heads, g.T, N, g.D), "x")
+    _shape(idx, (B, g.n_kv_heads, n_blk, None, cpt), "idx")
+    if idx.shape[3] < N:
+        raise ValueError("idx holds %d tokens, x has %d" % (idx.shape[3], N))
+    _shape(sums, (g.n_kv_heads, n_blk, g.K, g.G), "sums")
+    _shape(wsum, (g.n_kv_heads, n_blk, g.K), "wsum")
+    if weight is not None:
+        _shape(weight, (B, g.n_kv_heads, n_blk, N, cpt), "weight")
+    _check_pt(g, pt, B, N)
     strides = (ctypes.c_int64 * 4)(*[x.stride(i) for i in range(4)])
     check(_lib.lib().loopvq_kmeans_accumulate(ctypes.byref(g), _ptr(x), strides, B, N, _ptr(idx), idx.shape[3],
                                               _ptr(weight), ctypes.byref(pt) if pt is not None else None,
@@ -132,6 +186,10 @@ def kmeans_finalize(g: Geom, sums, wsum, codebook, stream=None):
     for t, n in ((sums, "sums"), (wsum, "wsum"), (codebook, "codebook")):
         if not t.is_contiguous():
             raise ValueError("%s must be contiguous" % n)
+    n_blk, _ = _dims(g)
+    _shape(sums, (g.n_kv_heads, n_blk, g.K, g.G), "sums")
+    _shape(wsum, (g.n_kv_heads, n_blk, g.K), "wsum")
+    _shape(codebook, (g.n_kv_heads, n_blk, g.K, g.G), "codebook")
     check(_lib.lib().loopvq_kmeans_finalize(ctypes.byref(g), _ptr(sums), _ptr(wsum), _ptr(codebook),
                                             _stream(stream)))
     return codebook
@@ -167,25 +225,54 @@ def decode_attn(g: Geom, q, k_idx, v_idx, k_cb, v_cb, sink_k, sink_v, rope, N=No
         if not t.is_contiguous():
             raise ValueError("%s must be contiguous" % n)
     B, Hq, n_steps, D = q.shape
+    n_blk, cpt = _dims(g)
+    _shape(q, (B, g.n_q_heads, n_steps, g.D), "q")
+    _shape(k_idx, (B, g.n_kv_heads, n_blk, None, cpt), "k_idx")
+    _shape(v_idx, tuple(k_idx.shape), "v_idx")
+    _shape(k_cb, (g.n_kv_heads, n_blk, g.K, g.G), "k_cb")
+    _shape(v_cb, (g.n_kv_heads, n_blk, g.K, g.G), "v_cb")
+    _shape(rope, (None, g.D // 8, 8), "rope")
     N_cap = k_idx.shape[3]
     N = N_cap if N is None else N
     n_s = 0
+    if (sink_k is None) != (sink_v is None):
+        raise ValueError("sink_k and sink_v must both be given or both be None")
     if sink_k is not None:
         _need(sink_k, torch.bfloat16, "sink_k")
         _need(sink_v, torch.bfloat16, "sink_v")
         n_s = sink_k.shape[3]
+        _shape(sink_k, (B, g.n_kv_heads, g.T, n_s, g.D), "sink_k")
+        _shape(sink_v, (B, g.n_kv_heads, g.T, n_s, g.D), "sink_v")
+        if not sink_k.is_contiguous() or not sink_v.is_contiguous():
+            raise ValueError("sink_k and sink_v must be contiguous")
     if seq_len is not None:
         _need(seq_len, torch.int32, "seq_len")
+        _shape(seq_len, (B,), "seq_len")
+        if not seq_len.is_contiguous():
+            raise ValueError("seq_len must be contiguous")
     R_cap = 0
+    if (recent_k is None) != (recent_v is None):
+        raise ValueError("recent_k and recent_v must both be given or both be None")
     if recent_k is not None:
         _need(recent_k, torch.bfloat16, "recent_k")
         _need(recent_v, torch.bfloat16, "recent_v")
         R_cap = recent_k.shape[3]
+        _shape(recent_k, (B, g.n_kv_heads, g.T, R_cap, g.D), "recent_k")
+        _shape(recent_v, (B, g.n_kv_heads, g.T, R_cap, g.D), "recent_v")
+        if not recent_k.is_contiguous() or not recent_v.is_contiguous():
+            raise ValueError("recent_k and recent_v must be contiguous")
     n_r = R_cap if n_r is None else n_r
+    _check_pt(g, pt, B, N)
     if out is None:
         out = torch.empty((B, Hq, n_steps, D), dtype=torch.float32, device=q.device)
     if lse is None:
         lse = torch.empty((B, Hq, n_steps), dtype=torch.float32, device=q.device)
+    _need(out, torch.float32, "out")
+    _need(lse, torch.float32, "lse")
+    _shape(out, (B, Hq, n_steps, D), "out")
+    _shape(lse, (B, Hq, n_steps), "lse")
+    if not out.is_contiguous() or not lse.is_contiguous():
+        raise ValueError("out and lse must be contiguous")
     need = decode_workspace_bytes(g, B, N, step0, n_steps)
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=q.device)
@@ -206,7 +293,7 @@ def rope_table_f32(n_pos, D=128, theta=1.0e4, device="cuda", stream=None):
     return t
 
 
-def _prefill_common(q, k_idx, v_idx, k_cb, v_cb, sink_k, sink_v, rope):
+def _prefill_common(g, q, k_idx, v_idx, k_cb, v_cb, sink_k, sink_v, rope, pt=None):
     _need(q, torch.float32, "q")
     _need(k_idx, torch.uint8, "k_idx")
     _need(v_idx, torch.uint8, "v_idx")
@@ -216,11 +303,30 @@ def _prefill_common(q, k_idx, v_idx, k_cb, v_cb, sink_k, sink_v, rope):
     for t, n in ((q, "q"), (k_idx, "k_idx"), (v_idx, "v_idx"), (k_cb, "k_cb"), (v_cb, "v_cb"), (rope, "rope")):
         if not t.is_contiguous():
             raise ValueError("%s must be contiguous" % n)
+    if q.dim() != 5:
+        raise ValueError("q must be [B][Hq][n_steps][N][D]")
+    B, _, n_steps, N, _ = q.shape
+    n_blk, cpt = _dims(g)
+    _shape(q, (B, g.n_q_heads, n_steps, N, g.D), "q")
+    _shape(k_idx, (B, g.n_kv_heads, n_blk, None, cpt), "k_idx")
+    _shape(v_idx, tuple(k_idx.shape), "v_idx")
+    if k_idx.shape[3] < N:
+        raise ValueError("k_idx holds %d tokens, q has %d positions" % (k_idx.shape[3], N))
+    _shape(k_cb, (g.n_kv_heads, n_blk, g.K, g.G), "k_cb")
+    _shape(v_cb, (g.n_kv_heads, n_blk, g.K, g.G), "v_cb")
+    _shape(rope, (None, g.D // 2, 2), "rope")
     n_s = 0
+    if (sink_k is None) != (sink_v is None):
+        raise ValueError("sink_k and sink_v must both be given or both be None")
     if sink_k is not None:
         _need(sink_k, torch.bfloat16, "sink_k")
         _need(sink_v, torch.bfloat16, "sink_v")
         n_s = sink_k.shape[3]
+        _shape(sink_k, (B, g.n_kv_heads, g.T, n_s, g.D), "sink_k")
+        _shape(sink_v, (B, g.n_kv_heads, g.T, n_s, g.D), "sink_v")
+        if not sink_k.is_contiguous() or not sink_v.is_contiguous():
+            raise ValueError("sink_k and sink_v must be contiguous")
+    _check_pt(g, pt, B, N)
     return n_s
 
 
@@ -231,7 +337,7 @@ def prefill_attn(g: Geom, q, k_idx, v_idx, k_cb, v_cb, sink_k, sink_v, rope, ste
     [B][H][n_blk][N_cap][D/c]; k_cb/v_cb bf16 [H][n_blk][K][G]; sinks bf16 [B][H][T][n_s][D] or
     None; rope fp32 table from rope_table_f32(); pt the keys' pre-transform (pretransform()) or None.
     Returns (out fp32 like q, lse fp32 [B][Hq][n_steps][N])."""
-    n_s = _prefill_common(q, k_idx, v_idx, k_cb, v_cb, sink_k, sink_v, rope)
+    n_s = _prefill_common(g, q, k_idx, v_idx, k_cb, v_cb, sink_k, sink_v, rope, pt)
     B, Hq, n_steps, N, D = q.shape
     if out is None:
         out = torch.empty_like(q)
@@ -248,12 +354,15 @@ def prefill_attn_backward(g: Geom, q, k_idx, v_idx, k_cb, v_cb, sink_k, sink_v, 
                           step0=0, d_q=None, d_k_cb=None, d_v_cb=None, workspace=None, pt=None, stream=None):
     """Gradients of prefill_attn: returns (d_q fp32 like q, d_k_cb, d_v_cb fp32 [H][n_blk][K][G]).
     The codebook gradients are overwritten (sums over every q-head, step and token in the call)."""
-    n_s = _prefill_common(q, k_idx, v_idx, k_cb, v_cb, sink_k, sink_v, rope)
+    n_s = _prefill_common(g, q, k_idx, v_idx, k_cb, v_cb, sink_k, sink_v, rope, pt)
     for t, n in ((out, "out"), (lse, "lse"), (d_out, "d_out")):
         _need(t, torch.float32, n)
         if not t.is_contiguous():
             raise ValueError("%s must be contiguous" % n)
     B, Hq, n_steps, N, D = q.shape
+    _shape(out, tuple(q.shape), "out")
+    _shape(d_out, tuple(q.shape), "d_out")
+    _shape(lse, (B, Hq, n_steps, N), "lse")
     if d_q is None:
         d_q = torch.empty_like(q)
     if d_k_cb is None:

@@ -290,13 +290,16 @@ __global__ __launch_bounds__(kEncodeThreads, (G == 16 && !TASQ) ? 4 : 1) void en
   const uint32_t bn_one = hh == 0 ? 0x3f80u : 0u;
 
   // The next group's loads are issued before the current group is screened.
+  // A wave with no group of its own (fewer than four groups in this
+  // workgroup) still loads the last group, so every load is of a real row.
   constexpr int WS = kEncodeThreads / kWave;
   bf16x8_t bz[KK];
   uint32_t brk[TASQ ? KK : 1][8], brs[TASQ ? KK : 1][8];
+  const int grp_first = min(wave, ngroups - 1);   // ngroups >= 1: every workgroup has a token
   if constexpr (TASQ)
-    fetch_raw(wave, brk, brs);
+    fetch_raw(grp_first, brk, brs);
   else
-    fetch(wave, bz);
+    fetch(grp_first, bz);
   for (int grp = wave; grp < ngroups; grp += WS) {
     bf16x8_t cz[KK], czlo[KK], czlo2[KK];
     float zz = 0.f;

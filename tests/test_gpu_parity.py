@@ -386,3 +386,42 @@ def test_per_step_decode(geo):
         assert torch.equal(fin, torch.isfinite(lse[:, :, 0]))
         assert torch.allclose(lse[:, :, 0][fin], fused_lse[:, :, t][fin], atol=1e-3, rtol=1e-4)
     _say("  decode worst rel err %.3g over %d steps" % (worst, T))
+
+
+SHORT = [
+    # name, G, pretransform: c = 4 (32 codes per token) and c = 8 (16 per token)
+    ("half-bit", 16, False),
+    ("quarter-bit", 32, False),
+    ("pretransform", 16, True),
+    ("pretransform-quarter-bit", 32, True),
+]
+
+
+@pytest.mark.parametrize("geo", SHORT, ids=[x[0] for x in SHORT])
+def test_encode_exactly_sized_short_inputs(geo):
+    """Encodes of 1, 2, 3, 129 and 130 tokens from tensors holding exactly those
+    tokens (and a sigma buffer of exactly N tokens): the last workgroup has fewer
+    groups of codes than waves, and every load must stay inside the inputs."""
+    s = _lib()
+    name, G, tasq = geo
+    for N in (1, 2, 3, 129, 130):
+        _say("short encode", name, "N=%d" % N)
+        cfg = small_cfg(1, G=G, T_c=4, T=4, H_kv=2, H_q=2, B=2, N=N, n_s=4, tasq=tasq,
+                        n_calib=1024, kmeans_iters=4)
+        inp = build_inputs(cfg, 0, "cuda")
+        x = inp["k"].contiguous()
+        assert x.shape[3] == N
+        g = _geom(s, cfg)
+        kidx = torch.zeros((2, 2, 1, N, cfg.chunks), dtype=torch.uint8, device="cuda")
+        pt = sigma = None
+        if tasq:
+            sigma = torch.zeros((2, N, 4), dtype=torch.float16, device="cuda")
+            pt = s.pretransform(inp["w"], inp["perm"], sigma)
+        vidx = torch.zeros_like(kidx)
+        s.encode(g, x, inp["k_cb"], kidx, pt=pt)
+        s.encode(g, inp["v"].contiguous(), inp["v_cb"], vidx)
+        torch.cuda.synchronize()
+        for b in range(2):
+            for h in range(2):
+                rk, rv = _check_encode_slice(cfg, inp, kidx, vidx, sigma, b, h, slice(None))
+                assert rk[2] == 0 and rv[2] == 0, (N, b, h, rk, rv)
