@@ -143,6 +143,66 @@ def hbm_stream(torch, nbytes=1 << 30):
             "note": "calib_read_kernel / calib_copy_kernel, 16 B per lane, grid-stride; median of 10 / 6 launches"}
 
 
+def onchip_ceilings(torch):
+    """Time the on-chip ceiling kernels of libloopvq_calib.so (LDS reads in
+    the decode kernels' access patterns, vector and matrix arithmetic).
+    Rates per CU per clock assume the 2.4 GHz peak engine clock."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "sub_bit_loop_amd", "libloopvq_calib.so"))
+    lib.loopvq_calib_onchip.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    clk = 2.4e9
+    st = torch.cuda.current_stream().cuda_stream
+    out = {"clock_assumed_GHz": clk / 1e9, "compute_units": n_cu}
+
+    def run(kind, mode, blocks, iters):
+        sink = torch.empty(blocks * 256, dtype=torch.int32, device="cuda")
+
+        def go():
+            if lib.loopvq_calib_onchip(kind, mode, blocks, iters, sink.data_ptr(), st) != 0:
+                raise RuntimeError("calib on-chip launch failed")
+        go()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
+        for a, b in ev:
+            a.record()
+            go()
+            b.record()
+        torch.cuda.synchronize()
+        return _median_ms(ev) * 1e-3
+
+    lds = {0: ("ds_read_b128, conflict-free (lane l reads slot l)", 16),
+           1: ("ds_read_b128, random 16-byte slots", 16),
+           2: ("ds_read_b128, random 48-byte codeword rows, half per wave (c = 4 decode layout)", 16),
+           3: ("ds_read_b64, random 8-byte slots", 8),
+           4: ("ds_read_b64_tr_b16, random 8-byte slots", 8),
+           5: ("ds_read_b128, lane pairs read the two halves of a random 32-byte codeword (pre-transform "
+               "decode layout)", 16),
+           6: ("ds_read_b128, lane pairs read the two halves of a random codeword at a 48-byte stride", 16),
+           7: ("ds_bpermute_b32 from random source lanes", 4)}
+    blocks = 4 * n_cu
+    for mode, (name, width) in lds.items():
+        iters = 4096
+        t = run(0, mode, blocks, iters)
+        out["lds_mode%d" % mode] = {"pattern": name,
+                                    "B_per_clk_per_CU": blocks * 256 * iters * 16 * width / t / n_cu / clk}
+    valu = {0: ("v_pk_fma_f16", 4), 1: ("v_dot2_f32_f16", 4), 2: ("v_fma_f32", 2)}
+    blocks = 8 * n_cu
+    for mode, (name, flop) in valu.items():
+        iters = 8192
+        t = run(1, mode, blocks, iters)
+        ops = blocks * 256 * iters * 16
+        out["valu_mode%d" % mode] = {"instruction": name, "lane_ops_per_clk_per_CU": ops / t / n_cu / clk,
+                                     "TFLOPs": ops * flop / t / 1e12}
+    mfma = {0: ("v_mfma_f32_16x16x32_bf16", 16384), 1: ("v_mfma_f32_32x32x16_bf16", 32768)}
+    for mode, (name, flop) in mfma.items():
+        iters = 8192
+        t = run(2, mode, blocks, iters)
+        out["mfma_mode%d" % mode] = {"instruction": name,
+                                     "TFLOPs": blocks * 4 * iters * 4 * flop / t / 1e12}
+    return out
+
+
 # ----------------------------------------------------------------------------- CPU oracle workers
 # These run in spawned processes that import only NumPy and the oracle.
 
@@ -201,6 +261,7 @@ def workload5(args, torch, lv, cfg):
     N_cap = cfg.N + cfg.page * n_pages
     rope = lv.rope_table(cfg.n_s + N_cap + cfg.page, cfg.D, cfg.theta)
     stream = hbm_stream(torch)
+    ceilings = onchip_ceilings(torch)
 
     def ev():
         return torch.cuda.Event(enable_timing=True)
@@ -358,6 +419,7 @@ def workload5(args, torch, lv, cfg):
         "page_encode": {"events": len(page_ev),
                         "ms_per_event_all_layers_median": statistics.median(page_ms) if page_ms else None},
         "hbm_stream": stream,
+        "onchip_ceilings": ceilings,
         "timed_s": total_ms / 1e3,
         "input_generation_s": gen_s,
     }
@@ -880,14 +942,25 @@ def write_traffic(cfg_index, fetch_dir, write_dir, command):
     def has(name):
         return lambda n, gsz: name in n
 
+    def after(tab, first, name):
+        """Dispatches of `name` launched right after a dispatch of `first`
+        (the merge of one decode call)."""
+        ids = {int(k) + 1 for k, (n, _, _) in tab.items() if first in n}
+        keep = {k for k, (n, _, _) in tab.items() if name in n and int(k) in ids}
+        return keep
+
     entries = {}
+
+    def avg_ids(tab, ids):
+        v = [tab[k][2] for k in ids]
+        return (sum(v) / len(v), len(v)) if v else (None, 0)
 
     def entry(key, kern, label, parts):
         f_kib = w_kib = 0.0
         counts = []
         for fp, wp in parts:
-            fa, nf = avg(fetch, fp)
-            wa, nw = avg(write, wp)
+            fa, nf = avg_ids(fetch, fp) if isinstance(fp, set) else avg(fetch, fp)
+            wa, nw = avg_ids(write, wp) if isinstance(wp, set) else avg(write, wp)
             if fa is None or wa is None:
                 raise SystemExit("no dispatches for %s" % label)
             f_kib += fa
@@ -897,17 +970,18 @@ def write_traffic(cfg_index, fetch_dir, write_dir, command):
                         "write_KiB": w_kib, "dispatches_averaged": counts,
                         "bytes_per_launch": (f_kib * ff + w_kib * wf) * 1024}
 
-    # within one run every merge_kernel launch belongs to that workload's decode calls
     if cfg_index == 5:
         entry("decode_tasq@5", "decode_tasq", "decode_tasq_kernel<4> + merge_kernel (one layer)",
-              [(has("decode_tasq"), has("decode_tasq")), (has("merge_kernel"), has("merge_kernel"))])
+              [(has("decode_tasq"), has("decode_tasq")),
+               (after(fetch, "decode_tasq", "merge_kernel"), after(write, "decode_tasq", "merge_kernel"))])
         entry("encode_prefill_layer@5", "encode", "sigma_kernel + encode_kernel<16,4,true> + "
               "encode_kernel<16,4,false> (one layer's prefill)",
               [(big(fetch, name), big(write, name)) for name in
                ("sigma_kernel", "encode_kernel<16, 4, true>", "encode_kernel<16, 4, false>")])
     elif cfg_index == 2:
         entry("decode_half@2", "decode_half", "decode_half_kernel + merge_kernel",
-              [(has("decode_half"), has("decode_half")), (has("merge_kernel"), has("merge_kernel"))])
+              [(has("decode_half"), has("decode_half")),
+               (after(fetch, "decode_half", "merge_kernel"), after(write, "decode_half", "merge_kernel"))])
         entry("encode@2", "encode", "encode_kernel<16, 4, false>",
               [(big(fetch, "encode_kernel<16, 4, false>"), big(write, "encode_kernel<16, 4, false>"))])
     else:
@@ -917,13 +991,17 @@ def write_traffic(cfg_index, fetch_dir, write_dir, command):
     if os.path.exists(p):
         with open(p) as fh:
             d = json.load(fh)
+    for k in ("command", "fetch_factor", "write_factor"):
+        d.pop(k, None)
+    if not isinstance(d.get("calibration"), dict):
+        d["calibration"] = {}
+    known = {key for _, key in TRAFFIC_ENTRIES.values()}
+    d["kernels"] = {k: v for k, v in d.get("kernels", {}).items() if k in known}
     d.setdefault("kernels", {}).update(entries)
     d.setdefault("commands", {})["workload %d" % cfg_index] = command
     d.setdefault("calibration", {})["workload %d run" % cfg_index] = (
         "calib_read_kernel reads 1 GiB (16 B per lane): FETCH_SIZE %.1f KiB per dispatch -> fetch factor %.4f; "
         "calib_copy_kernel writes 1 GiB: WRITE_SIZE %.1f KiB -> write factor %.4f" % (cf, ff, cw, wf))
-    for k in ("command", "fetch_factor", "write_factor"):
-        d.pop(k, None)
     with open(p, "w") as fh:
         json.dump(d, fh, indent=1)
     print(json.dumps(d, indent=1))

@@ -28,7 +28,8 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
 # The GQA decode kernel keeps its MFMA accumulators in ordinary VGPRs so that
 # it fits two waves per SIMD.
 EXTRA = {"encode.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee", "-mllvm", "-amdgpu-mfma-vgpr-form"],
-         "decode_gqa.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+         "decode_gqa.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "calib.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src):

@@ -17,10 +17,19 @@
 //     a[d'] = q[p(d')] / w[p(d')],
 //     b[d'] = +-q[p(d') +- D/2] / w[p(d')]   (+ for p(d') < D/2),
 // and the dot product is multiplied by the token's sigma.  The permutation
-// separates RoPE partners, so unlike the plain kernels no lane rotates a key:
-// every lane owns contiguous transformed channels and takes the cos/sin of
-// their (scattered) frequencies from a per-wave LDS copy of the token's table
-// row.
+// separates RoPE partners, so unlike the plain kernels no lane rotates a key.
+//
+// Positions: a workgroup iteration serves 16 consecutive tokens at positions
+// P + o, where P is the same for every lane and o (0..15) is fixed per lane.
+// By the angle-sum identity
+//     e[d'](P + o) = A_o[d'] cos(P w_f) + B_o[d'] sin(P w_f),
+//     A_o = a cos(o w_f) + b sin(o w_f),   B_o = b cos(o w_f) - a sin(o w_f),
+// so the per-lane coefficients A_o, B_o are formed once (fp32 angles of
+// o w_f), and per iteration lane f of each wave loads the table entry
+// (cos P w_f, sin P w_f) of frequency f and stores it as word f of the wave's
+// 64-word LDS row; every lane then reads the entries of its 16 channels'
+// frequencies from that row.  The row spans the 64 LDS banks once, so these
+// reads never conflict (lanes reading one word share it).
 //
 // Layout choices:
 //   * Codebooks in LDS as fp16, step-major inside a codeword, first half
@@ -29,9 +38,6 @@
 //     chunks D/c/8 * g .. +D/c/8-1, i.e. the 16 transformed channels
 //     16g .. 16g+15, whose index bytes are one aligned 4-byte word (c = 4) or
 //     half of one (c = 8).
-//   * Per wave iteration each lane copies one quad of its token's RoPE row
-//     into the wave's LDS tile as (cos f, sin f) fp16 pairs; lanes then read
-//     the pairs of their 16 frequencies from it.
 //   * Effective queries, scores and P*V run on packed fp16 (scores summed in
 //     fp32 by v_dot2_f32_f16); P*V partials are flushed into fp32 every
 //     kFlush tokens, with the same range bounds as the plain kernels.
@@ -58,39 +64,47 @@ __device__ __forceinline__ int pow2_shift_t(float max_abs, int lim) {
   return e > lim ? e - lim : 0;
 }
 
-// Orders this wave's LDS traffic: writes before it are visible to the wave's
-// reads after it, and reads before it complete before later writes.
-__device__ __forceinline__ void wave_sync_t() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 constexpr int kTFlush = 16, kTLag = 3, kTVLim = 7;
+// Fourth word of a raw buffer descriptor (32-bit data, no format conversion).
+constexpr int kBufWord3 = 0x00020000;
 constexpr uint32_t kSelLo = 0x05040100u;   // v_perm: low halves of (src1, src0)
 constexpr uint32_t kSelHi = 0x07060302u;   // v_perm: high halves of (src1, src0)
 
 }  // namespace
 
 template <int C>
-__global__ __launch_bounds__(kDecodeThreads) void decode_tasq_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kDecodeThreads, C == 4 ? 3 : 2) void decode_tasq_kernel(DecodeArgs a) {
   constexpr int D = 128, HD = 64, TC = 4, G = C * TC, CPT = D / C;
   constexpr int QW = C / 4;           // uint4 per codeword half (two steps)
   constexpr int DW = C / 2;           // dwords per step of a codeword
   constexpr int LPT = 16, SPW = kWave / LPT, NW = kDecodeThreads / kWave;
+  constexpr int TPI = NW * SPW;       // tokens per workgroup iteration
   constexpr int NCK = CPT / 8;        // chunks per lane (4 or 2)
   constexpr int NCH = NCK * C;        // transformed channels per lane (16)
   constexpr int NPR = NCH / 2;        // channel pairs per lane (8)
-  constexpr int CSR = HD + 4;         // dwords per RoPE tile row (pad spreads the slots over banks)
+  static_assert(TPI == 16 && HD == kWave, "one table frequency per lane");
   __shared__ __attribute__((aligned(16))) uint4 s_k[256 * 2 * QW];
   __shared__ __attribute__((aligned(16))) uint4 s_v[256 * 2 * QW];
-  __shared__ __attribute__((aligned(16))) uint32_t s_cs[NW][SPW][CSR];   // (cos f, sin f) fp16 pairs
-  __shared__ float s_red[NW][TC][D + 2];
+  // One region, three uses in turn: (cos, sin) of o * w_f for o < TPI, f < HD
+  // (fp32) while the coefficients are formed; the fp32 P*V sums of every
+  // lane during the token loop (they live in LDS, not registers, so that
+  // three workgroups fit a CU: quad q of lane t at float4 q * 256 + t, which
+  // consecutive lanes read without bank conflicts); the cross-wave merge of
+  // the partial outputs at the end.
+  constexpr int kAccQ = 2 * NCH / 4;  // float4 sums per lane
+  __shared__ __attribute__((aligned(16))) float4 s_buf[kAccQ * kDecodeThreads];
+  static_assert(NW * TC * (D + 2) <= kAccQ * kDecodeThreads * 4 && TPI * HD * 2 <= kAccQ * kDecodeThreads * 4,
+                "offset table and merge buffer fit the region");
   __shared__ float s_amax[2][NW];
+  __shared__ uint32_t s_row[NW][HD];   // (cos, sin) fp16 pairs of the iteration's table row
+  float (*s_red)[TC][D + 2] = reinterpret_cast<float (*)[TC][D + 2]>(s_buf);
+  float2* s_off = reinterpret_cast<float2*>(s_buf);
+  float4* s_acc = s_buf + threadIdx.x;   // this lane's sums: s_acc[q * kDecodeThreads]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int sl = lane & 15, slot = lane >> 4;
   const int hs = sl >> 3, g = sl & 7;
+  const int my = wave * SPW + slot;   // this lane's token offset o within an iteration
   const int split = blockIdx.x;
   const int hq = blockIdx.y;
   const int h = hq / a.gqa;
@@ -134,6 +148,17 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_tasq_kernel(DecodeArgs 
     s_amax[0][wave] = mk;
     s_amax[1][wave] = mv;
   }
+  // offset angles o * w_f, w_f = theta^(-2f/D), in fp32
+  {
+    const float l2t = log2f(a.theta);
+    for (int x = tid; x < TPI * HD; x += kDecodeThreads) {
+      const int o = x / HD, f = x - o * HD;
+      const float ang = (float)o * exp2f(-(float)(2 * f) / (float)D * l2t);
+      float sn, cs;
+      sincosf(ang, &sn, &cs);
+      s_off[x] = make_float2(cs, sn);
+    }
+  }
   __syncthreads();
   mk = fmaxf(fmaxf(s_amax[0][0], s_amax[0][1]), fmaxf(s_amax[0][2], s_amax[0][3]));
   mv = fmaxf(fmaxf(s_amax[1][0], s_amax[1][1]), fmaxf(s_amax[1][2], s_amax[1][3]));
@@ -155,20 +180,23 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_tasq_kernel(DecodeArgs 
     }
   }
 
-  // ---- effective-query coefficients of this lane's channels d' = 16g + j
-  // for steps 2hs + ml, and the LDS addresses of their (cos, sin) pairs.
+  // ---- effective-query coefficients A_o, B_o of this lane's channels
+  // d' = 16g + j for steps 2hs + ml, and the LDS words of their frequencies
+  // in the wave's table row.
   const int t_lo = max(a.step0, beta * TC), t_hi = min(a.step0 + a.n_steps, (beta + 1) * TC);
   uint32_t A2[2][NPR], B2[2][NPR];
-  const uint32_t* cs_addr[NCH];
+  const uint32_t* rw_addr[NCH];
   {
     int och[NCH];
     float rw[NCH];
+    float2 oc[NCH];
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
       const int o = a.perm[h * D + NCH * g + j] & (D - 1);   // stays in bounds for any input
       och[j] = o;
       rw[j] = 1.f / a.w[h * D + o];
-      cs_addr[j] = &s_cs[wave][slot][o & (HD - 1)];
+      rw_addr[j] = &s_row[wave][o & (HD - 1)];
+      oc[j] = s_off[my * HD + (o & (HD - 1))];
     }
 #pragma unroll
     for (int ml = 0; ml < 2; ++ml) {
@@ -180,11 +208,13 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_tasq_kernel(DecodeArgs 
         float av[2], bv[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          const int o = och[2 * p + u];
+          const int j = 2 * p + u, o = och[j];
           const float qo = bf16_to_f32(qr[o]);
           const float qp = bf16_to_f32(qr[o ^ HD]);
-          av[u] = act ? qo * rw[2 * p + u] : 0.f;
-          bv[u] = act ? (o < HD ? qp : -qp) * rw[2 * p + u] : 0.f;
+          const float aa = qo * rw[j];
+          const float bb = (o < HD ? qp : -qp) * rw[j];
+          av[u] = act ? aa * oc[j].x + bb * oc[j].y : 0.f;
+          bv[u] = act ? bb * oc[j].x - aa * oc[j].y : 0.f;
         }
         A2[ml][p] = pack_h2t(av[0], av[1]);
         B2[ml][p] = pack_h2t(bv[0], bv[1]);
@@ -194,46 +224,52 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_tasq_kernel(DecodeArgs 
   const float sscale = a.qscale * ldexpf(1.f, shk);
 
   float mrow[2] = {-INFINITY, -INFINITY}, lrow[2] = {0.f, 0.f};
-  float acc[2][NCH];
   uint32_t acc16[2][NPR];
 #pragma unroll
-  for (int ml = 0; ml < 2; ++ml) {
-#pragma unroll
-    for (int j = 0; j < NCH; ++j) acc[ml][j] = 0.f;
+  for (int ml = 0; ml < 2; ++ml)
 #pragma unroll
     for (int p = 0; p < NPR; ++p) acc16[ml][p] = 0u;
-  }
-  __syncthreads();
+  __syncthreads();   // codebooks staged; the offset table is no longer read
+#pragma unroll
+  for (int q = 0; q < kAccQ; ++q) s_acc[q * kDecodeThreads] = make_float4(0.f, 0.f, 0.f, 0.f);
 
   int nb = a.N;
   if (a.seq_len) nb = max(0, min(a.seq_len[b], a.N));
   const int tok_lo = split * a.tok_per_split;
   const int tok_hi = min(nb, tok_lo + a.tok_per_split);
   const int n_sink = split == 0 ? a.n_s : 0;
-  const int n_bf = n_sink + (split == 0 ? a.n_r : 0);
+  const int n_rec = split == 0 ? a.n_r : 0;
   const int64_t irow0 = (((int64_t)b * a.H + h) * a.n_blk + beta) * (int64_t)a.N_cap;
   const int64_t sink0 = (((int64_t)b * a.H + h) * a.T + beta * TC) * (int64_t)a.n_s;
   const int64_t rec0 = (((int64_t)b * a.H + h) * a.T + beta * TC) * (int64_t)a.r_cap;
   const uint16_t* rope16 = reinterpret_cast<const uint16_t*>(a.rope);
   const float ksc = ldexpf(1.f, -shk), vsc = ldexpf(1.f, -shv);
 
-  // RoPE quad sl of position pos (4 frequencies) -> the slot's tile row.
-  auto load_quad = [&](int pos) { return reinterpret_cast<const uint4*>(rope16 + (int64_t)pos * D)[sl]; };
-  auto fill = [&](const uint4& qd) {
-    uint4 o;
-    o.x = __builtin_amdgcn_perm(qd.z, qd.x, kSelLo);
-    o.y = __builtin_amdgcn_perm(qd.z, qd.x, kSelHi);
-    o.z = __builtin_amdgcn_perm(qd.w, qd.y, kSelLo);
-    o.w = __builtin_amdgcn_perm(qd.w, qd.y, kSelHi);
-    *reinterpret_cast<uint4*>(&s_cs[wave][slot][4 * sl]) = o;
+  // Per-token loads go through buffer descriptors: the per-lane byte offset
+  // is fixed, the iteration's offset is uniform (a scalar register), and an
+  // offset past the described range reads 0 instead of faulting.
+  const __amdgpu_buffer_rsrc_t rope_rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)a.rope, 0, a.n_pos * D * 2, kBufWord3);
+  const int rope_lane = ((lane >> 2) * 8 + (lane & 3)) * 2;
+  // (cos, sin) of frequency `lane` at position P, from the fp16 quad table
+  auto load_row = [&](int P) {
+    const uint32_t c = __builtin_amdgcn_raw_buffer_load_b16(rope_rs, rope_lane, P * (D * 2), 0);
+    const uint32_t sn = __builtin_amdgcn_raw_buffer_load_b16(rope_rs, rope_lane + 8, P * (D * 2), 0);
+    return c | (sn << 16);
   };
   // Scores of the lane's two steps (summed over the 8 lanes of the token's
   // step half); Kw[k][ml*DW + ip] = channel pair (2ip, 2ip+1) of chunk k.
-  auto scores = [&](const uint32_t (&Kw)[NCK][C], const float (&sg)[2], float (&sc)[2]) {
+  // The row is written and read by this wave only; LDS instructions of one
+  // wave execute in order, so the words read are this iteration's and the
+  // next write follows these reads.
+  auto scores = [&](uint32_t row, const uint32_t (&Kw)[NCK][C], const float (&sg)[2], float (&sc)[2]) {
     uint32_t cs2[NPR], sn2[NPR];
+    s_row[wave][lane] = row;
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int p = 0; p < NPR; ++p) {
-      const uint32_t d0 = *cs_addr[2 * p], d1 = *cs_addr[2 * p + 1];
+      const uint32_t d0 = *rw_addr[2 * p];
+      const uint32_t d1 = *rw_addr[2 * p + 1];
       cs2[p] = __builtin_amdgcn_perm(d1, d0, kSelLo);
       sn2[p] = __builtin_amdgcn_perm(d1, d0, kSelHi);
     }
@@ -248,14 +284,21 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_tasq_kernel(DecodeArgs 
       sc[ml] = group_sum<8>(part) * sg[ml] * sscale;
     }
   };
+  // fp16 partial sums into the fp32 sums in LDS (channel pairs 2p, 2p+1 of
+  // step ml are float4 (ml * NCH + 2p) / 4, components 2p % 4, +1)
   auto flush = [&]() {
+#pragma unroll
+    for (int q = 0; q < kAccQ; ++q) {
+      const int ml = q / (NCH / 4), p0 = 2 * (q % (NCH / 4));
+      float4 v = s_acc[q * kDecodeThreads];
+      add_f16x2(acc16[ml][p0], v.x, v.y);
+      add_f16x2(acc16[ml][p0 + 1], v.z, v.w);
+      s_acc[q * kDecodeThreads] = v;
+    }
 #pragma unroll
     for (int ml = 0; ml < 2; ++ml)
 #pragma unroll
-      for (int p = 0; p < NPR; ++p) {
-        add_f16x2(acc16[ml][p], acc[ml][2 * p], acc[ml][2 * p + 1]);
-        acc16[ml][p] = 0u;
-      }
+      for (int p = 0; p < NPR; ++p) acc16[ml][p] = 0u;
   };
   auto accumulate = [&](const float (&sc)[2], const uint32_t (&Vw)[NCK][C], bool valid) {
     if (!valid) return;
@@ -267,7 +310,14 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_tasq_kernel(DecodeArgs 
         const h2t_t a2 = {(_Float16)alpha, (_Float16)alpha};
         lrow[ml] *= alpha;
 #pragma unroll
-        for (int j = 0; j < NCH; ++j) acc[ml][j] *= alpha;
+        for (int q = ml * (NCH / 4); q < (ml + 1) * (NCH / 4); ++q) {
+          float4 v = s_acc[q * kDecodeThreads];
+          v.x *= alpha;
+          v.y *= alpha;
+          v.z *= alpha;
+          v.w *= alpha;
+          s_acc[q * kDecodeThreads] = v;
+        }
 #pragma unroll
         for (int p = 0; p < NPR; ++p) acc16[ml][p] = __builtin_bit_cast(uint32_t, as_h2t(acc16[ml][p]) * a2);
         mrow[ml] = s;
@@ -282,71 +332,78 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_tasq_kernel(DecodeArgs 
     }
   };
 
-  // ---- bf16 items (split 0): sinks at positions 0..n_s-1, the recent window
-  // at n_s + N_b + r.  Their keys are raw, so they enter the transformed
-  // space as w[p(d')] * k[p(d')] with sigma = 1.
-  for (int base = 0; base < n_bf; base += NW * SPW) {
-    const int item = base + wave * SPW + slot;
-    const bool valid = item < n_bf;
-    const int it = valid ? item : 0;
-    const bool is_rec = it >= n_sink;
-    const int pos = is_rec ? a.n_s + nb + (it - n_sink) : it;
-    fill(load_quad(pos));
-    wave_sync_t();
-    uint32_t Kw[NCK][C], Vw[NCK][C];
+  // ---- bf16 items (split 0): sinks at positions 0..n_s-1, then the recent
+  // window at n_s + N_b + r.  Their keys are raw, so they enter the
+  // transformed space as w[p(d')] * k[p(d')] with sigma = 1.  Item base + o
+  // of a run sits at position P0 + base + o.
+  auto bf16_items = [&](int count, int P0, bool is_rec) {
+    for (int base = 0; base < count; base += TPI) {
+      const int it = base + my;
+      const bool valid = it < count;
+      const int itc = valid ? it : 0;
+      const uint32_t row = load_row(P0 + base);
+      uint32_t Kw[NCK][C], Vw[NCK][C];
 #pragma unroll
-    for (int ml = 0; ml < 2; ++ml) {
-      const int m = 2 * hs + ml;
-      const uint16_t* kr = is_rec ? a.rk + (rec0 + (int64_t)m * a.r_cap + (it - n_sink)) * D
-                                  : a.sk + (sink0 + (int64_t)m * a.n_s + it) * D;
-      const uint16_t* vr = is_rec ? a.rv + (rec0 + (int64_t)m * a.r_cap + (it - n_sink)) * D
-                                  : a.sv + (sink0 + (int64_t)m * a.n_s + it) * D;
+      for (int ml = 0; ml < 2; ++ml) {
+        const int m = 2 * hs + ml;
+        const uint16_t* kr = is_rec ? a.rk + (rec0 + (int64_t)m * a.r_cap + itc) * D
+                                    : a.sk + (sink0 + (int64_t)m * a.n_s + itc) * D;
+        const uint16_t* vr = is_rec ? a.rv + (rec0 + (int64_t)m * a.r_cap + itc) * D
+                                    : a.sv + (sink0 + (int64_t)m * a.n_s + itc) * D;
 #pragma unroll
-      for (int p = 0; p < NPR; ++p) {
-        float z[2];
+        for (int p = 0; p < NPR; ++p) {
+          float z[2];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int o = a.perm[h * D + NCH * g + 2 * p + u] & (D - 1);
-          z[u] = bf16_to_f32(kr[o]) * a.w[h * D + o] * ksc;
+          for (int u = 0; u < 2; ++u) {
+            const int o = a.perm[h * D + NCH * g + 2 * p + u] & (D - 1);
+            z[u] = bf16_to_f32(kr[o]) * a.w[h * D + o] * ksc;
+          }
+          const uint32_t vv = *reinterpret_cast<const uint32_t*>(vr + NCH * g + 2 * p);
+          Kw[p / DW][ml * DW + p % DW] = pack_h2t(z[0], z[1]);
+          Vw[p / DW][ml * DW + p % DW] = pack_h2t(bf16lo(vv) * vsc, bf16hi(vv) * vsc);
         }
-        const uint32_t vv = *reinterpret_cast<const uint32_t*>(vr + NCH * g + 2 * p);
-        Kw[p / DW][ml * DW + p % DW] = pack_h2t(z[0], z[1]);
-        Vw[p / DW][ml * DW + p % DW] = pack_h2t(bf16lo(vv) * vsc, bf16hi(vv) * vsc);
       }
+      const float sg[2] = {1.f, 1.f};
+      float sc[2];
+      scores(row, Kw, sg, sc);
+      accumulate(sc, Vw, valid);
+      flush();
     }
-    const float sg[2] = {1.f, 1.f};
-    float sc[2];
-    scores(Kw, sg, sc);
-    accumulate(sc, Vw, valid);
-    flush();
-    wave_sync_t();
-  }
+  };
+  if (n_sink > 0) bf16_items(n_sink, 0, false);
+  if (n_rec > 0) bf16_items(n_rec, a.n_s + nb, true);
 
-  // ---- quantized tokens, one per lane slot per iteration; index words, sigma
-  // and the RoPE quad of the next iteration are loaded one iteration ahead.
+  // ---- quantized tokens, one per lane slot per iteration; index words,
+  // sigma and the table row of the next iteration are loaded one iteration
+  // ahead.
   const int n_tok = max(0, tok_hi - tok_lo);
-  const int my = wave * SPW + slot;
+  const int P0 = a.n_s + tok_lo;
   // word of the index row holding this lane's index bytes, and their bit offset
   const int kwo = C == 4 ? g : (g >> 1);
   const int kbit = C == 4 ? 0 : 16 * (g & 1);
-  uint32_t kwn = 0, vwn = 0, sgn = 0;
-  uint4 rqn = make_uint4(0, 0, 0, 0);
+  // index rows of this (batch, kv-head, block) and sigma of this batch entry;
+  // a lane past the split's last token reads a later row or 0 (unused)
+  const __amdgpu_buffer_rsrc_t kid_rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(a.kidx + irow0 * CPT), 0, a.N_cap * CPT, kBufWord3);
+  const __amdgpu_buffer_rsrc_t vid_rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(a.vidx + irow0 * CPT), 0, a.N_cap * CPT, kBufWord3);
+  const __amdgpu_buffer_rsrc_t sig_rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.sigma + (int64_t)b * a.sig_cap * a.T), 0, a.sig_cap * a.T * 2, kBufWord3);
+  const int idx_lane = (tok_lo + my) * CPT + 4 * kwo;
+  const int sig_lane = ((tok_lo + my) * a.T + beta * TC + 2 * hs) * 2;
+  uint32_t kwn = 0, vwn = 0, sgn = 0, rown = 0;
   auto load_next = [&](int base) {
-    const int it = base + my;
-    const int jj = tok_lo + (it < n_tok ? it : n_tok - 1);   // always a real row
-    kwn = reinterpret_cast<const uint32_t*>(a.kidx + (irow0 + jj) * CPT)[kwo];
-    vwn = reinterpret_cast<const uint32_t*>(a.vidx + (irow0 + jj) * CPT)[kwo];
-    sgn = *reinterpret_cast<const uint32_t*>(a.sigma + ((int64_t)b * a.sig_cap + jj) * a.T + beta * TC + 2 * hs);
-    rqn = load_quad(a.n_s + jj);
+    kwn = __builtin_amdgcn_raw_buffer_load_b32(kid_rs, idx_lane, base * CPT, 0);
+    vwn = __builtin_amdgcn_raw_buffer_load_b32(vid_rs, idx_lane, base * CPT, 0);
+    sgn = __builtin_amdgcn_raw_buffer_load_b32(sig_rs, sig_lane, base * a.T * 2, 0);
+    rown = load_row(P0 + (base < n_tok ? base : 0));         // a row of this split's tokens
   };
   if (n_tok > 0) load_next(0);
   int since_flush = 0;
-  for (int base = 0; base < n_tok; base += NW * SPW) {
+  for (int base = 0; base < n_tok; base += TPI) {
     const bool valid = base + my < n_tok;
-    const uint32_t kwc = kwn, vwc = vwn, sgc = sgn;
-    fill(rqn);
-    load_next(base + NW * SPW);
-    wave_sync_t();
+    const uint32_t kwc = kwn, vwc = vwn, sgc = sgn, row = rown;
+    load_next(base + TPI);
     uint32_t Kw[NCK][C], Vw[NCK][C];
 #pragma unroll
     for (int k = 0; k < NCK; ++k) {
@@ -363,15 +420,25 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_tasq_kernel(DecodeArgs 
     const h2t_t s16 = as_h2t(sgc);
     const float sg[2] = {(float)s16.x, (float)s16.y};
     float sc[2];
-    scores(Kw, sg, sc);
+    scores(row, Kw, sg, sc);
     accumulate(sc, Vw, valid);
     if (++since_flush == kTFlush) {
       flush();
       since_flush = 0;
     }
-    wave_sync_t();
   }
   flush();
+  float acc[2][NCH];
+#pragma unroll
+  for (int q = 0; q < kAccQ; ++q) {
+    const float4 v = s_acc[q * kDecodeThreads];
+    const int ml = q / (NCH / 4), j0 = 4 * (q % (NCH / 4));
+    acc[ml][j0] = v.x;
+    acc[ml][j0 + 1] = v.y;
+    acc[ml][j0 + 2] = v.z;
+    acc[ml][j0 + 3] = v.w;
+  }
+  __syncthreads();   // every lane holds its sums: the region becomes the merge buffer
 
   // ---- merge the SPW slots of the wave (lanes with equal sl)
 #pragma unroll

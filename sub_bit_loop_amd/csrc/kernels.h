@@ -46,6 +46,8 @@ struct DecodeArgs {
   int32_t B, H, Hq, T, n_blk, K, N, N_cap, n_s, step0, n_steps, n_split, gqa, blk0, n_blk_serv;
   int32_t tok_per_split;
   float qscale;               // log2(e) / sqrt(D)
+  float theta;                // RoPE base the table was made with
+  int32_t n_pos;              // positions in the RoPE table
 };
 
 struct TasqStatsArgs {

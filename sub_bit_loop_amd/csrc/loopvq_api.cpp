@@ -111,6 +111,10 @@ DecodePlan plan_decode(const loopvq_geom* g, int B, int N, int step0, int n_step
       wgs = (long long)B * (g->n_q_heads / p.hpw) * p.n_blk_serv;
       target = 512;
       break;
+    case DecodeKernel::kTasq:
+      wgs = (long long)B * g->n_q_heads * p.n_blk_serv;
+      target = g->G == 16 ? 768 : 512;     // 3 per CU at c = 4 (165 VGPRs, 49 KB LDS), else 2
+      break;
     default:
       wgs = (long long)B * g->n_q_heads * p.n_blk_serv;
       target = 512;                        // 255 VGPRs: 2 per CU
@@ -446,6 +450,12 @@ loopvq_status loopvq_decode_attn(const loopvq_geom* g, const void* q, int32_t st
   const DecodePlan p = plan_decode(g, B, N, step0, n_steps, pt != nullptr);
   if (p.kernel == DecodeKernel::kTasq && reinterpret_cast<uintptr_t>(pt->sigma) % 4)
     return fail(LOOPVQ_EINVAL, "pre-transform sigma must be 4-byte aligned");
+  // byte offsets of the index rows, sigma and the table are 32-bit in the
+  // pre-transform kernel
+  if (p.kernel == DecodeKernel::kTasq &&
+      ((long long)N_cap * (g->D / (g->G / g->T_c)) >= (1ll << 31) || (long long)pt->N_cap * g->T * 2 >= (1ll << 31) ||
+       (long long)n_pos * g->D * 2 >= (1ll << 31)))
+    return fail(LOOPVQ_ENOTSUP, "N_cap=%d or n_pos=%d too large for 32-bit offsets", N_cap, n_pos);
   if (!workspace || workspace_bytes < p.ws_bytes)
     return fail(LOOPVQ_EWORKSPACE, "workspace of %zu bytes needed (got %zu)", p.ws_bytes, workspace_bytes);
 
@@ -488,6 +498,8 @@ loopvq_status loopvq_decode_attn(const loopvq_geom* g, const void* q, int32_t st
   a.n_blk_serv = p.n_blk_serv;
   a.tok_per_split = p.tok_per_split;
   a.qscale = (float)(1.4426950408889634 / std::sqrt((double)g->D));
+  a.theta = g->rope_theta;
+  a.n_pos = n_pos;
   // Blocks of four steps (0.5 and 0.25 bit, with or without the key
   // pre-transform): the specialised kernels chosen by the plan; every other
   // geometry: the generic one.
