@@ -177,6 +177,29 @@ loopvq_status loopvq_decode_attn(const loopvq_geom* g, const void* q, int32_t st
                                  int32_t n_pos, float* out, float* lse, void* workspace,
                                  size_t workspace_bytes, void* stream);
 
+/* loopvq_decode_attn_noalloc -- loopvq_decode_attn for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, results and errors as
+ * loopvq_decode_attn, without the workspace: the split-context partials go
+ * to a static device array of LOOPVQ_NOALLOC_SCRATCH_BYTES, one per GPU,
+ * held until the process ends.  The call allocates nothing (its first call
+ * on a device looks up that device's array with hipGetSymbolAddress).
+ * Every call on one GPU shares that GPU's array: calls that may run at the
+ * same time on one GPU (different streams, or one stream fed by several
+ * host threads without ordering) race and give wrong results.  Nothing in
+ * the array needs clearing: each call writes every partial it reads.
+ * Errors: as loopvq_decode_attn; EWORKSPACE when the shape's partials
+ * (loopvq_decode_attn_workspace) exceed LOOPVQ_NOALLOC_SCRATCH_BYTES. */
+#define LOOPVQ_NOALLOC_SCRATCH_BYTES (8u << 20)
+loopvq_status loopvq_decode_attn_noalloc(const loopvq_geom* g, const void* q, int32_t step0,
+                                         int32_t n_steps, const uint8_t* k_idx, const uint8_t* v_idx,
+                                         int32_t N_cap, const void* k_cb, const void* v_cb,
+                                         const void* sink_k, const void* sink_v, int32_t n_s,
+                                         const void* recent_k, const void* recent_v, int32_t n_r,
+                                         int32_t R_cap, int32_t B, int32_t N, const int32_t* seq_len,
+                                         const loopvq_pretransform* pt, const void* rope_table,
+                                         int32_t n_pos, float* out, float* lse, void* stream);
+
 /* loopvq_tasq_covariance -- statistics for deriving the keys' channel
  * permutation (section 3.3: the permutation is taken from the T_c*D x T_c*D
  * covariance of a block's stacked step keys).  For every (kv-head, block) it

@@ -9,11 +9,12 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libloopvq.so")
 
 OK, EINVAL, ENOTSUP, EHIP, EWORKSPACE = 0, -1, -2, -3, -4
+NOALLOC_SCRATCH_BYTES = 8 << 20     # LOOPVQ_NOALLOC_SCRATCH_BYTES
 STATUS_NAME = {OK: "OK", EINVAL: "EINVAL", ENOTSUP: "ENOTSUP", EHIP: "EHIP", EWORKSPACE: "EWORKSPACE"}
 
 # Names the C header declares; tests check that every one is exported.
 EXPORTS = ("loopvq_encode", "loopvq_rope_table", "loopvq_decode_attn_workspace",
-           "loopvq_decode_attn", "loopvq_tasq_covariance", "loopvq_tasq_pair_permutation",
+           "loopvq_decode_attn", "loopvq_decode_attn_noalloc", "loopvq_tasq_covariance", "loopvq_tasq_pair_permutation",
            "loopvq_kmeans_accumulate", "loopvq_kmeans_finalize", "loopvq_rope_table_f32",
            "loopvq_prefill_attn", "loopvq_prefill_attn_backward_workspace", "loopvq_prefill_attn_backward",
            "loopvq_last_error", "loopvq_abi_version")
@@ -58,6 +59,9 @@ def lib():
     L.loopvq_decode_attn.argtypes = [GP, P, I32, I32, P, P, I32, P, P, P, P, I32, P, P, I32, I32,
                                      I32, I32, P, PTP, P, I32, P, P, P, SZ, P]
     L.loopvq_decode_attn.restype = ctypes.c_int
+    L.loopvq_decode_attn_noalloc.argtypes = [GP, P, I32, I32, P, P, I32, P, P, P, P, I32, P, P, I32, I32,
+                                             I32, I32, P, PTP, P, I32, P, P, P]
+    L.loopvq_decode_attn_noalloc.restype = ctypes.c_int
     L.loopvq_tasq_covariance.argtypes = [GP, P, I64P, I32, I32, P, P, I32, P, P, P]
     L.loopvq_tasq_covariance.restype = ctypes.c_int
     L.loopvq_tasq_pair_permutation.argtypes = [P, I32, I32, I32, P]

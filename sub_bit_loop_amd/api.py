@@ -215,6 +215,22 @@ def decode_attn(g: Geom, q, k_idx, v_idx, k_cb, v_cb, sink_k, sink_v, rope, N=No
     k_cb/v_cb bf16 [H][n_blk][K][G]; sinks bf16 [B][H][T][n_s][D] or None;
     recent window bf16 [B][H][T][R_cap][D] or None (first n_r tokens attended);
     rope fp16 table from rope_table().  Returns (out fp32 [B][Hq][n_steps][D], lse fp32 [B][Hq][n_steps])."""
+    return _decode(g, q, k_idx, v_idx, k_cb, v_cb, sink_k, sink_v, rope, N, step0, seq_len, pt, out, lse,
+                   workspace, stream, recent_k, recent_v, n_r, False)
+
+
+def decode_attn_noalloc(g: Geom, q, k_idx, v_idx, k_cb, v_cb, sink_k, sink_v, rope, N=None, step0=0,
+                        seq_len=None, pt=None, out=None, lse=None, stream=None, recent_k=None, recent_v=None,
+                        n_r=None):
+    """decode_attn without a workspace (loopvq_decode_attn_noalloc: the split
+    partials live in the library's static per-GPU array).  out and lse are
+    allocated here when not given; pass them to keep the call allocation-free."""
+    return _decode(g, q, k_idx, v_idx, k_cb, v_cb, sink_k, sink_v, rope, N, step0, seq_len, pt, out, lse,
+                   None, stream, recent_k, recent_v, n_r, True)
+
+
+def _decode(g, q, k_idx, v_idx, k_cb, v_cb, sink_k, sink_v, rope, N, step0, seq_len, pt, out, lse, workspace,
+            stream, recent_k, recent_v, n_r, noalloc):
     _need(q, torch.bfloat16, "q")
     _need(k_idx, torch.uint8, "k_idx")
     _need(v_idx, torch.uint8, "v_idx")
@@ -273,6 +289,14 @@ def decode_attn(g: Geom, q, k_idx, v_idx, k_cb, v_cb, sink_k, sink_v, rope, N=No
     _shape(lse, (B, Hq, n_steps), "lse")
     if not out.is_contiguous() or not lse.is_contiguous():
         raise ValueError("out and lse must be contiguous")
+    if noalloc:
+        st = _lib.lib().loopvq_decode_attn_noalloc(
+            ctypes.byref(g), _ptr(q), step0, n_steps, _ptr(k_idx), _ptr(v_idx), N_cap, _ptr(k_cb), _ptr(v_cb),
+            _ptr(sink_k), _ptr(sink_v), n_s, _ptr(recent_k), _ptr(recent_v), n_r, R_cap, B, N, _ptr(seq_len),
+            ctypes.byref(pt) if pt is not None else None,
+            _ptr(rope), rope.shape[0], _ptr(out), _ptr(lse), _stream(stream))
+        check(st)
+        return out, lse
     need = decode_workspace_bytes(g, B, N, step0, n_steps)
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=q.device)

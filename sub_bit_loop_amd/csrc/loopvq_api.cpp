@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "../../include/loopvq.h"
@@ -127,6 +128,35 @@ DecodePlan plan_decode(const loopvq_geom* g, int B, int N, int step0, int n_step
   p.tok_per_split = N > 0 ? (N + p.n_split - 1) / p.n_split : 0;
   p.ws_bytes = (size_t)B * g->n_q_heads * n_steps * p.n_split * (g->D + 1) * sizeof(float);
   return p;
+}
+
+// Split partials of loopvq_decode_attn_noalloc: a static device array (one
+// copy per GPU, kept until the process ends).  In host code `scratch` names a
+// host-side stand-in; its device address is taken once per device with
+// hipGetSymbolAddress and only that address is passed to kernels.
+constexpr size_t kScratchBytes = LOOPVQ_NOALLOC_SCRATCH_BYTES;
+static_assert(kScratchBytes % 256 == 0, "scratch size");
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// This device's scratch address (looked up on the first call on a device,
+// with that device current).
+loopvq_status scratch_for_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(LOOPVQ_ENOTSUP, "device %d is beyond the scratch table", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return LOOPVQ_OK;
 }
 
 }  // namespace
@@ -416,15 +446,17 @@ loopvq_status loopvq_decode_attn_workspace(const loopvq_geom* g, int32_t B, int3
   return LOOPVQ_OK;
 }
 
-loopvq_status loopvq_decode_attn(const loopvq_geom* g, const void* q, int32_t step0,
-                                 int32_t n_steps, const uint8_t* k_idx, const uint8_t* v_idx,
-                                 int32_t N_cap, const void* k_cb, const void* v_cb,
-                                 const void* sink_k, const void* sink_v, int32_t n_s,
-                                 const void* recent_k, const void* recent_v, int32_t n_r,
-                                 int32_t R_cap, int32_t B, int32_t N, const int32_t* seq_len,
-                                 const loopvq_pretransform* pt, const void* rope_table,
-                                 int32_t n_pos, float* out, float* lse, void* workspace,
-                                 size_t workspace_bytes, void* stream) {
+// The decode call with the split partials in `workspace`, or (from_scratch)
+// in this device's static scratch array.
+static loopvq_status decode_attn_impl(const loopvq_geom* g, const void* q, int32_t step0,
+                                      int32_t n_steps, const uint8_t* k_idx, const uint8_t* v_idx,
+                                      int32_t N_cap, const void* k_cb, const void* v_cb,
+                                      const void* sink_k, const void* sink_v, int32_t n_s,
+                                      const void* recent_k, const void* recent_v, int32_t n_r,
+                                      int32_t R_cap, int32_t B, int32_t N, const int32_t* seq_len,
+                                      const loopvq_pretransform* pt, const void* rope_table,
+                                      int32_t n_pos, float* out, float* lse, void* workspace,
+                                      size_t workspace_bytes, void* stream, bool from_scratch) {
   g_err[0] = 0;
   loopvq_status st = check_decode_shape(g, B, N, step0, n_steps);
   if (st != LOOPVQ_OK) return st;
@@ -440,7 +472,8 @@ loopvq_status loopvq_decode_attn(const loopvq_geom* g, const void* q, int32_t st
     return fail(LOOPVQ_EINVAL, "rope table has %d positions, need n_s + N + n_r = %lld", n_pos,
                 (long long)n_s + N + n_r);
   {
-    const void* al[] = {q, k_idx, v_idx, k_cb, v_cb, sink_k, sink_v, recent_k, recent_v, rope_table, workspace};
+    const void* al[] = {q, k_idx, v_idx, k_cb, v_cb, sink_k, sink_v, recent_k, recent_v, rope_table,
+                        from_scratch ? nullptr : workspace};
     for (const void* p : al)
       if (reinterpret_cast<uintptr_t>(p) % 16)
         return fail(LOOPVQ_EINVAL, "tensor pointers must be 16-byte aligned");
@@ -456,8 +489,16 @@ loopvq_status loopvq_decode_attn(const loopvq_geom* g, const void* q, int32_t st
       ((long long)N_cap * (g->D / (g->G / g->T_c)) >= (1ll << 31) || (long long)pt->N_cap * g->T * 2 >= (1ll << 31) ||
        (long long)n_pos * g->D * 2 >= (1ll << 31)))
     return fail(LOOPVQ_ENOTSUP, "N_cap=%d or n_pos=%d too large for 32-bit offsets", N_cap, n_pos);
-  if (!workspace || workspace_bytes < p.ws_bytes)
+  if (from_scratch) {
+    if (p.ws_bytes > kScratchBytes)
+      return fail(LOOPVQ_EWORKSPACE, "this shape needs %zu bytes of split partials; the allocation-free call "
+                  "holds at most %zu (use loopvq_decode_attn with a workspace)", p.ws_bytes, kScratchBytes);
+    st = scratch_for_current_device(&workspace);
+    if (st != LOOPVQ_OK) return st;
+    workspace_bytes = kScratchBytes;
+  } else if (!workspace || workspace_bytes < p.ws_bytes) {
     return fail(LOOPVQ_EWORKSPACE, "workspace of %zu bytes needed (got %zu)", p.ws_bytes, workspace_bytes);
+  }
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   loopvq::DecodeArgs a{};
@@ -526,6 +567,33 @@ loopvq_status loopvq_decode_attn(const loopvq_geom* g, const void* q, int32_t st
   e = loopvq::launch_merge(ma, s);
   if (e != hipSuccess) return hip_fail(e, "merge launch");
   return LOOPVQ_OK;
+}
+
+loopvq_status loopvq_decode_attn(const loopvq_geom* g, const void* q, int32_t step0,
+                                 int32_t n_steps, const uint8_t* k_idx, const uint8_t* v_idx,
+                                 int32_t N_cap, const void* k_cb, const void* v_cb,
+                                 const void* sink_k, const void* sink_v, int32_t n_s,
+                                 const void* recent_k, const void* recent_v, int32_t n_r,
+                                 int32_t R_cap, int32_t B, int32_t N, const int32_t* seq_len,
+                                 const loopvq_pretransform* pt, const void* rope_table,
+                                 int32_t n_pos, float* out, float* lse, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  return decode_attn_impl(g, q, step0, n_steps, k_idx, v_idx, N_cap, k_cb, v_cb, sink_k, sink_v, n_s, recent_k,
+                          recent_v, n_r, R_cap, B, N, seq_len, pt, rope_table, n_pos, out, lse, workspace,
+                          workspace_bytes, stream, false);
+}
+
+loopvq_status loopvq_decode_attn_noalloc(const loopvq_geom* g, const void* q, int32_t step0,
+                                         int32_t n_steps, const uint8_t* k_idx, const uint8_t* v_idx,
+                                         int32_t N_cap, const void* k_cb, const void* v_cb,
+                                         const void* sink_k, const void* sink_v, int32_t n_s,
+                                         const void* recent_k, const void* recent_v, int32_t n_r,
+                                         int32_t R_cap, int32_t B, int32_t N, const int32_t* seq_len,
+                                         const loopvq_pretransform* pt, const void* rope_table,
+                                         int32_t n_pos, float* out, float* lse, void* stream) {
+  return decode_attn_impl(g, q, step0, n_steps, k_idx, v_idx, N_cap, k_cb, v_cb, sink_k, sink_v, n_s, recent_k,
+                          recent_v, n_r, R_cap, B, N, seq_len, pt, rope_table, n_pos, out, lse, nullptr, 0, stream,
+                          true);
 }
 
 loopvq_status loopvq_rope_table_f32(float theta, int32_t D, int32_t n_pos, float* table, void* stream) {
