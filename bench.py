@@ -760,7 +760,7 @@ def finetune_flow(args, torch, lv):
     the 0.5-bit slice's geometry.  Times the compressed-attention forward and
     backward calls and whole iterations (re-encode, stack forward, KL,
     backward, Adam).  Returns the JSON line's dict."""
-    from synth import build_inputs, config_by_index, gen_toy_stack
+    from synth import build_inputs, config_by_index, gen_targets, gen_toy_stack
     from dataclasses import replace
     from sub_bit_loop_amd import finetune as ft
     steps = 20 if args.steps is None else args.steps
@@ -822,6 +822,18 @@ def finetune_flow(args, torch, lv):
 
     toy = gen_toy_stack(cfg, 0, "cuda", vocab=vocab, B=1)
     stack = ft.ToyLoopedStack(toy["Wq"], toy["Wo"], toy["Wu"], cfg.H_q, cfg.D, cfg.T, cfg.n_s, rope)
+    # importance weights of the k-means (eq. 3): stack over the precise cache,
+    # next-token loss backward into every cached key and value, weights
+    targets = gen_targets(cfg, 0, "cuda", vocab=vocab, B=1)
+    ft.fisher_importance(stack, g, toy["x"], inp["k"], inp["v"], sk, sv, targets)
+    torch.cuda.synchronize()
+    fev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
+    for a_, b_ in fev:
+        a_.record()
+        ft.fisher_importance(stack, g, toy["x"], inp["k"], inp["v"], sk, sv, targets)
+        b_.record()
+    torch.cuda.synchronize()
+    fisher_ms = _median_ms(fev)
     iters = max(2, steps // 2)
     ft.finetune_codebooks(stack, g, toy["x"], inp["k"], inp["v"], sk, sv, inp["k_cb"], inp["v_cb"], iters=1)
     torch.cuda.synchronize()
@@ -882,6 +894,10 @@ def finetune_flow(args, torch, lv):
         "roofline": {"kernel": dom_name, "bound": "mfma", "achieved": dom_tf, "peak": FP32_MATRIX_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": dom_tf / FP32_MATRIX_PEAK_TFLOPS, "traffic": None,
                      "algorithmic_flop_per_launch": dom_flop, "launch_ms_median": dom_ms, "dtype": "f32"},
+        "fisher_weights": {"ms_per_pass_median": fisher_ms,
+                           "note": "importance weights of every joint vector (eq. 3): toy stack over the precise "
+                                   "cache (4 loopvq_precise_attn calls), next-token loss, backward "
+                                   "(loopvq_precise_attn_backward per step), loopvq_fisher_weights"},
         "iteration": {"ms": it_ms, "objective": Js,
                       "note": "re-encode K and V, toy stack forward over the rebuilt cache (4 compressed-attention "
                               "calls), KL against the precise run, backward, Adam (lr 1e-3)"},

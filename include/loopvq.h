@@ -352,6 +352,54 @@ const char* loopvq_last_error(void);
 /* LOOPVQ_ABI_VERSION of the built library. */
 int32_t loopvq_abi_version(void);
 
+/* loopvq_precise_attn / loopvq_precise_attn_backward -- the same causal
+ * attention as loopvq_prefill_attn (query i of a step at position n_s + i
+ * attends to the sinks and to tokens j <= i) over the PRECISE cache, and its
+ * gradients, for the importance weights of the codebook k-means ("codebook
+ * and calibration", eq. 3: omega_n = ||dL/dz_n||^2 of the precise cache's
+ * joint vectors).
+ *   q             device fp32 [B][n_q_heads][n_steps][N][D], post-RoPE
+ *   k, v          device bf16 [B][n_kv_heads][T][N_x][D], the stored cache
+ *                 (keys pre-RoPE), tokens 0..N-1 attended, N <= N_x
+ *   sink_k, sink_v, rope_table (fp32 table of loopvq_rope_table_f32),
+ *   out, lse      as in loopvq_prefill_attn
+ * Backward: d_q (fp32 like q) is written; the gradients of the loss with
+ * respect to every attended cached key (before RoPE) and value of the served
+ * steps are ADDED into d_k and d_v (fp32 [B][n_kv_heads][T][N_x][D]; zero them
+ * before the first call; q-heads of a GQA group add into their kv-head's
+ * tokens, in an order that may vary in the last bits).  workspace: at least
+ * loopvq_prefill_attn_backward_workspace() bytes.
+ * Errors: EINVAL for NULL pointers, N > N_x, bad geometry or step range, a
+ * short rope table, misaligned tensors (16 bytes for q, k, v, sinks, tables,
+ * out, d_out, d_q); EWORKSPACE for a short workspace. */
+loopvq_status loopvq_precise_attn(const loopvq_geom* g, const float* q, int32_t step0, int32_t n_steps,
+                                  int32_t B, int32_t N, const void* k, const void* v, int32_t N_x,
+                                  const void* sink_k, const void* sink_v, int32_t n_s, const float* rope_table,
+                                  int32_t n_pos, float* out, float* lse, void* stream);
+loopvq_status loopvq_precise_attn_backward(const loopvq_geom* g, const float* q, int32_t step0, int32_t n_steps,
+                                           int32_t B, int32_t N, const void* k, const void* v, int32_t N_x,
+                                           const void* sink_k, const void* sink_v, int32_t n_s,
+                                           const float* rope_table, int32_t n_pos, const float* out,
+                                           const float* lse, const float* d_out, float* d_q, float* d_k,
+                                           float* d_v, void* workspace, size_t workspace_bytes, void* stream);
+
+/* loopvq_fisher_weights -- importance of every joint vector for the weighted
+ * k-means ("codebook and calibration", eq. 3; section 3.1: a loop-axis joint
+ * vector covers T_c steps): omega_n = sum over the G coordinates of z_n of
+ * (dL/dz_n)^2, where coordinate i*T_c + m of chunk q is channel q*c + i at
+ * block step m.  With the keys' pre-transform (pt, section 3.3) the key
+ * vector is z[d'] = w[perm[d']] k[perm[d']] / sigma, so dL/dz[d'] =
+ * d_k[perm[d']] * sigma / w[perm[d']] (sigma fixed, as stored).
+ *   d_k, d_v        device fp32 [B][n_kv_heads][T][N_x][D] (as written by
+ *                   loopvq_precise_attn_backward over every step)
+ *   omega_k, omega_v  device fp32 [B][n_kv_heads][T/T_c][N][D/c], written;
+ *                   the `weight` input of loopvq_kmeans_accumulate
+ * Each omega is summed in fp64 and rounded once to fp32.
+ * Errors: EINVAL for NULL pointers, N > N_x, bad geometry or pre-transform. */
+loopvq_status loopvq_fisher_weights(const loopvq_geom* g, const float* d_k, const float* d_v, int32_t B, int32_t N,
+                                    int32_t N_x, const loopvq_pretransform* pt, float* omega_k, float* omega_v,
+                                    void* stream);
+
 #ifdef __cplusplus
 }
 #endif

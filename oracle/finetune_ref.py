@@ -32,7 +32,14 @@ the design notes of the repository):
     quantized run reads the tokens rebuilt from the codebooks; sinks stay
     bf16 in both;
   * the gradient is taken with respect to the codebook values the forward
-    reads (the bf16 entries); an optimizer keeps its own fp32 master copy.
+    reads (the bf16 entries); an optimizer keeps its own fp32 master copy;
+  * the importance weights of the codebook k-means ("codebook and
+    calibration", eq. 3: omega_n = ||dL/dz_n||^2) take L as the next-token
+    cross-entropy of the toy stack over the precise cache against seeded
+    target tokens (no data exists), summed over the batch entries of the
+    mean over each sequence's N positions; z_n is a joint vector of the
+    precise cache (section 3.1), for pre-transformed keys in the transformed
+    space with sigma held at its stored value.
 """
 import math
 
@@ -287,3 +294,63 @@ def finetune_reference(toy, cache, k_cb0, v_cb0, T_c: int, iters: int, lr: float
         adam_step(kp, gk, st[0], st[1], it, lr)
         adam_step(vp, gv, st[2], st[3], it, lr)
     return Js, torch.from_numpy(bf16_round(kp.numpy())), torch.from_numpy(bf16_round(vp.numpy()))
+
+
+# ----------------------------------------------------------------------------
+# importance weights of the codebook k-means (eq. 3) on the toy stack
+# ----------------------------------------------------------------------------
+
+def next_token_loss(logits: torch.Tensor, targets: torch.Tensor) -> torch.Tensor:
+    """Mean over the rows of -log softmax(logits)[target] (natural log)."""
+    lq = torch.log_softmax(logits, dim=-1)
+    return -lq.gather(-1, targets[:, None]).mean()
+
+
+def precise_cache_loss(toy, cache, targets, theta: float = 1.0e4):
+    """L = sum over batch entries of the mean next-token loss of the toy stack
+    attending to the precise cache (cache["k"], cache["v"] may require grad)."""
+    T = cache["k"].shape[2]
+    n_s = cache["sink_k"].shape[3]
+    D = cache["k"].shape[-1]
+    H_q = cache["H_q"]
+    L = 0.0
+    for b in range(toy["x"].shape[0]):
+        lg = toy_logits(toy["x"][b], toy["Wq"], toy["Wo"], toy["Wu"], H_q, D, T, n_s,
+                        _stack_for(b, cache, 1, theta), theta)
+        L = L + next_token_loss(lg, torch.as_tensor(targets[b], dtype=torch.int64))
+    return L
+
+
+def fisher_importance(toy, cache, targets, T_c: int, G: int, theta: float = 1.0e4, tasq=None):
+    """(L, omega_k, omega_v): eq. 3's weight of every joint vector of the
+    precise cache, omega = ||dL/dz||^2 over its G coordinates, with
+    omega_* [B, H_kv, n_blk, N, D/c] (numpy fp64).
+
+    The gradient with respect to the cached keys and values comes from
+    autograd; z is a coordinate permutation of them (section 3.1), and for
+    pre-transformed keys (tasq = (w [H_kv, D], perm [H_kv, D], sigma_bar
+    [B, N, T])) z[d'] = w[p(d')] k[p(d')] / sigma_bar, so dL/dz[d'] =
+    dL/dk[p(d')] sigma_bar / w[p(d')]."""
+    from .kmeans_ref import fisher_weights
+    from .loopvq_ref import joint_vectors
+    N = cache["N"]
+    c = dict(cache)
+    k = torch.as_tensor(cache["k"][:, :, :, :N], dtype=F64).clone().requires_grad_(True)
+    v = torch.as_tensor(cache["v"][:, :, :, :N], dtype=F64).clone().requires_grad_(True)
+    c["k"], c["v"] = k, v
+    L = precise_cache_loss(toy, c, targets, theta)
+    L.backward()
+    gk = k.grad.numpy()
+    gv = v.grad.numpy()
+    if tasq is not None:
+        w, perm, sb = (np.asarray(x, dtype=np.float64) for x in tasq)
+        perm = perm.astype(np.int64)
+        gz = np.empty_like(gk)
+        for h in range(gk.shape[1]):
+            p = perm[h]
+            # [B, T, N, D'] = dL/dk[..., p(d')] * sigma_bar[b, j, t] / w[p(d')]
+            gz[:, h] = gk[:, h][..., p] * np.transpose(sb, (0, 2, 1))[:, :, :, None] / w[h][p]
+        gk = gz
+    ok = fisher_weights(joint_vectors(gk, T_c, G))
+    ov = fisher_weights(joint_vectors(gv, T_c, G))
+    return float(L.detach()), ok, ov

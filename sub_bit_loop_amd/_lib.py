@@ -17,6 +17,7 @@ EXPORTS = ("loopvq_encode", "loopvq_rope_table", "loopvq_decode_attn_workspace",
            "loopvq_decode_attn", "loopvq_decode_attn_noalloc", "loopvq_tasq_covariance", "loopvq_tasq_pair_permutation",
            "loopvq_kmeans_accumulate", "loopvq_kmeans_finalize", "loopvq_rope_table_f32",
            "loopvq_prefill_attn", "loopvq_prefill_attn_backward_workspace", "loopvq_prefill_attn_backward",
+           "loopvq_precise_attn", "loopvq_precise_attn_backward", "loopvq_fisher_weights",
            "loopvq_last_error", "loopvq_abi_version")
 
 
@@ -79,6 +80,13 @@ def lib():
     L.loopvq_prefill_attn_backward.argtypes = [GP, P, I32, I32, I32, I32, P, P, I32, P, P, P, P, I32, PTP, P,
                                                I32, P, P, P, P, P, P, P, SZ, P]
     L.loopvq_prefill_attn_backward.restype = ctypes.c_int
+    L.loopvq_precise_attn.argtypes = [GP, P, I32, I32, I32, I32, P, P, I32, P, P, I32, P, I32, P, P, P]
+    L.loopvq_precise_attn.restype = ctypes.c_int
+    L.loopvq_precise_attn_backward.argtypes = [GP, P, I32, I32, I32, I32, P, P, I32, P, P, I32, P, I32, P, P, P,
+                                               P, P, P, P, SZ, P]
+    L.loopvq_precise_attn_backward.restype = ctypes.c_int
+    L.loopvq_fisher_weights.argtypes = [GP, P, P, I32, I32, I32, PTP, P, P, P]
+    L.loopvq_fisher_weights.restype = ctypes.c_int
     L.loopvq_last_error.argtypes = []
     L.loopvq_last_error.restype = ctypes.c_char_p
     L.loopvq_abi_version.argtypes = []

@@ -404,3 +404,111 @@ def prefill_attn_backward(g: Geom, q, k_idx, v_idx, k_cb, v_cb, sink_k, sink_v, 
         rope.shape[0], _ptr(out), _ptr(lse), _ptr(d_out), _ptr(d_q), _ptr(d_k_cb), _ptr(d_v_cb), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
     return d_q, d_k_cb, d_v_cb
+
+
+def _precise_common(g, q, k, v, sink_k, sink_v, rope):
+    _need(q, torch.float32, "q")
+    _need(k, torch.bfloat16, "k")
+    _need(v, torch.bfloat16, "v")
+    _need(rope, torch.float32, "rope")
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (rope, "rope")):
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % n)
+    if q.dim() != 5:
+        raise ValueError("q must be [B][Hq][n_steps][N][D]")
+    B, _, n_steps, N, _ = q.shape
+    _shape(q, (B, g.n_q_heads, n_steps, N, g.D), "q")
+    _shape(k, (B, g.n_kv_heads, g.T, None, g.D), "k")
+    _shape(v, tuple(k.shape), "v")
+    if k.shape[3] < N:
+        raise ValueError("the cache holds %d tokens, q has %d positions" % (k.shape[3], N))
+    _shape(rope, (None, g.D // 2, 2), "rope")
+    n_s = 0
+    if (sink_k is None) != (sink_v is None):
+        raise ValueError("sink_k and sink_v must both be given or both be None")
+    if sink_k is not None:
+        _need(sink_k, torch.bfloat16, "sink_k")
+        _need(sink_v, torch.bfloat16, "sink_v")
+        n_s = sink_k.shape[3]
+        _shape(sink_k, (B, g.n_kv_heads, g.T, n_s, g.D), "sink_k")
+        _shape(sink_v, (B, g.n_kv_heads, g.T, n_s, g.D), "sink_v")
+        if not sink_k.is_contiguous() or not sink_v.is_contiguous():
+            raise ValueError("sink_k and sink_v must be contiguous")
+    return n_s
+
+
+def precise_attn(g: Geom, q, k, v, sink_k, sink_v, rope, step0=0, out=None, lse=None, stream=None):
+    """Causal attention of the N positions after the sinks over the precise
+    cache k, v bf16 [B][H][T][N_x][D] (pre-RoPE keys).  q fp32
+    [B][Hq][n_steps][N][D] (post-RoPE); rope fp32 from rope_table_f32().
+    Returns (out fp32 like q, lse fp32 [B][Hq][n_steps][N])."""
+    n_s = _precise_common(g, q, k, v, sink_k, sink_v, rope)
+    B, Hq, n_steps, N, D = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, n_steps, N), dtype=torch.float32, device=q.device)
+    check(_lib.lib().loopvq_precise_attn(
+        ctypes.byref(g), _ptr(q), step0, n_steps, B, N, _ptr(k), _ptr(v), k.shape[3], _ptr(sink_k), _ptr(sink_v),
+        n_s, _ptr(rope), rope.shape[0], _ptr(out), _ptr(lse), _stream(stream)))
+    return out, lse
+
+
+def precise_attn_backward(g: Geom, q, k, v, sink_k, sink_v, rope, out, lse, d_out, d_k, d_v, step0=0, d_q=None,
+                          workspace=None, stream=None):
+    """Gradients of precise_attn: returns d_q (fp32 like q); the gradients of
+    the served steps' cached keys (pre-RoPE) and values are ADDED into d_k,
+    d_v fp32 [B][H][T][N_x][D]."""
+    n_s = _precise_common(g, q, k, v, sink_k, sink_v, rope)
+    for t, n in ((out, "out"), (lse, "lse"), (d_out, "d_out"), (d_k, "d_k"), (d_v, "d_v")):
+        _need(t, torch.float32, n)
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % n)
+    B, Hq, n_steps, N, D = q.shape
+    _shape(out, tuple(q.shape), "out")
+    _shape(d_out, tuple(q.shape), "d_out")
+    _shape(lse, (B, Hq, n_steps, N), "lse")
+    _shape(d_k, tuple(k.shape), "d_k")
+    _shape(d_v, tuple(k.shape), "d_v")
+    if d_q is None:
+        d_q = torch.empty_like(q)
+    need = max(16, B * Hq * n_steps * N * 4)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    check(_lib.lib().loopvq_precise_attn_backward(
+        ctypes.byref(g), _ptr(q), step0, n_steps, B, N, _ptr(k), _ptr(v), k.shape[3], _ptr(sink_k), _ptr(sink_v),
+        n_s, _ptr(rope), rope.shape[0], _ptr(out), _ptr(lse), _ptr(d_out), _ptr(d_q), _ptr(d_k), _ptr(d_v),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return d_q
+
+
+def fisher_weights(g: Geom, d_k, d_v, N=None, pt=None, omega_k=None, omega_v=None, stream=None):
+    """Importance of every joint vector (sum of its squared gradient
+    coordinates) from the cache gradients d_k, d_v fp32 [B][H][T][N_x][D].
+    Returns (omega_k, omega_v) fp32 [B][H][n_blk][N][D/c], the weights of
+    kmeans_accumulate."""
+    _need(d_k, torch.float32, "d_k")
+    _need(d_v, torch.float32, "d_v")
+    if not d_k.is_contiguous() or not d_v.is_contiguous():
+        raise ValueError("d_k and d_v must be contiguous")
+    B = d_k.shape[0]
+    _shape(d_k, (B, g.n_kv_heads, g.T, None, g.D), "d_k")
+    _shape(d_v, tuple(d_k.shape), "d_v")
+    N_x = d_k.shape[3]
+    N = N_x if N is None else N
+    n_blk, cpt = _dims(g)
+    shp = (B, g.n_kv_heads, n_blk, N, cpt)
+    if omega_k is None:
+        omega_k = torch.empty(shp, dtype=torch.float32, device=d_k.device)
+    if omega_v is None:
+        omega_v = torch.empty(shp, dtype=torch.float32, device=d_k.device)
+    for t, n in ((omega_k, "omega_k"), (omega_v, "omega_v")):
+        _need(t, torch.float32, n)
+        _shape(t, shp, n)
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % n)
+    _check_pt(g, pt, B, N)
+    check(_lib.lib().loopvq_fisher_weights(ctypes.byref(g), _ptr(d_k), _ptr(d_v), B, N, N_x,
+                                           ctypes.byref(pt) if pt is not None else None, _ptr(omega_k),
+                                           _ptr(omega_v), _stream(stream)))
+    return omega_k, omega_v

@@ -97,6 +97,13 @@ struct PrefillArgs {
   int32_t sig_cap;
   int32_t B, H, Hq, T, T_c, n_blk, K, G, N, N_cap, n_s, step0, n_steps, gqa;
   float scale;                // 1 / sqrt(D)
+  // precise cache (C = 0): bf16 keys and values [B][H][T][N_x][D], pre-RoPE,
+  // and the fp32 gradients added into dxk (pre-RoPE keys) and dxv, same layout
+  const uint16_t* xk;
+  const uint16_t* xv;
+  int32_t N_x;
+  float* dxk;
+  float* dxv;
 };
 
 struct MergeArgs {
@@ -144,7 +151,23 @@ hipError_t launch_decode_cq(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_fill_f32(float* p, int64_t n, hipStream_t s);   // p[0..n) = 0
 hipError_t launch_rope_table_f32(float* tab, int n_pos, int D, double theta, hipStream_t s);
 // forward (out, lse) or backward (delta, zeroed then accumulated codebook
-// gradients, dq); C = G / T_c in {2, 4, 8, 16, 32}
+// gradients, dq); C = G / T_c in {2, 4, 8, 16, 32}; C = 0: the precise cache
+// (xk, xv), whose backward adds the key and value gradients into dxk, dxv
 hipError_t launch_prefill(const PrefillArgs& a, int C, bool backward, hipStream_t s);
+// omega of every joint vector (sum of the squared gradients of its G
+// coordinates), for keys (with the pre-transform's scale and permutation
+// when a.perm is set) and values
+struct FisherArgs {
+  const float* dk;            // fp32 [B][H][T][N_x][D] gradients of the pre-RoPE keys
+  const float* dv;            // and of the values
+  const float* w;             // keys' pre-transform or null
+  const int16_t* perm;
+  const uint16_t* sigma;      // fp16 [B][sig_cap][T]
+  int32_t sig_cap;
+  float* wk;                  // fp32 [B][H][n_blk][N][D/c]
+  float* wv;
+  int32_t B, H, T, T_c, n_blk, G, N, N_x, D;
+};
+hipError_t launch_fisher(const FisherArgs& a, hipStream_t s);
 
 }  // namespace loopvq

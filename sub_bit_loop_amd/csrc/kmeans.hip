@@ -113,4 +113,58 @@ hipError_t launch_kmeans_finalize(const double* sums, const double* wsum, uint16
   return hipGetLastError();
 }
 
+// Importance weight of every joint vector (eq. 3): omega_n = ||dL/dz_n||^2,
+// summed over the G coordinates of the vector, i.e. over the c channels of its
+// chunk at each of the T_c steps of its block.  The gradient comes per cached
+// element (dk for pre-RoPE keys, dv for values, as the precise-cache attention
+// backward writes them).  With the keys' pre-transform z[d'] = w[p(d')]
+// k[p(d')] / sigma, the chain rule gives dL/dz[d'] = dL/dk[p(d')] sigma /
+// w[p(d')] (sigma is a stored constant, not part of the code).  One thread per
+// (batch, kv-head, block, token, chunk); blockIdx.y picks keys or values.
+__global__ __launch_bounds__(256) void fisher_kernel(FisherArgs a) {
+  const int kv = blockIdx.y;
+  const int C = a.G / a.T_c, CPT = a.D / C;
+  const int64_t n = (int64_t)a.B * a.H * a.n_blk * a.N * CPT;
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= n) return;
+  int64_t r = e;
+  const int q = (int)(r % CPT);
+  r /= CPT;
+  const int j = (int)(r % a.N);
+  r /= a.N;
+  const int beta = (int)(r % a.n_blk);
+  r /= a.n_blk;
+  const int h = (int)(r % a.H);
+  const int b = (int)(r / a.H);
+  const bool tasq = kv == 0 && a.perm != nullptr;
+  const float* g = kv == 0 ? a.dk : a.dv;
+  double acc = 0.0;
+  for (int m = 0; m < a.T_c; ++m) {
+    const int t = beta * a.T_c + m;
+    const float* row = g + ((((int64_t)b * a.H + h) * a.T + t) * a.N_x + j) * a.D;
+    double sg = 1.0;
+    if (tasq) sg = f16_bits_to_f64(a.sigma[((int64_t)b * a.sig_cap + j) * a.T + t]);
+    for (int i = 0; i < C; ++i) {
+      const int dp = q * C + i;
+      double v;
+      if (tasq) {
+        const int o = a.perm[h * a.D + dp] & (a.D - 1);
+        v = (double)row[o] * sg / (double)a.w[h * a.D + o];
+      } else {
+        v = (double)row[dp];
+      }
+      acc += v * v;
+    }
+  }
+  (kv == 0 ? a.wk : a.wv)[e] = (float)acc;
+}
+
+hipError_t launch_fisher(const FisherArgs& a, hipStream_t s) {
+  const int C = a.G / a.T_c;
+  const int64_t n = (int64_t)a.B * a.H * a.n_blk * a.N * (a.D / C);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(fisher_kernel, dim3((unsigned)((n + 255) / 256), 2), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 }  // namespace loopvq

@@ -734,4 +734,132 @@ loopvq_status loopvq_prefill_attn_backward(const loopvq_geom* g, const float* q,
   return LOOPVQ_OK;
 }
 
+static loopvq_status precise_args(const loopvq_geom* g, const float* q, int32_t step0, int32_t n_steps,
+                                  int32_t B, int32_t N, const void* k, const void* v, int32_t N_x,
+                                  const void* sink_k, const void* sink_v, int32_t n_s, const float* rope_table,
+                                  int32_t n_pos, loopvq::PrefillArgs& a) {
+  loopvq_status st = check_decode_shape(g, B, N, step0, n_steps);
+  if (st != LOOPVQ_OK) return st;
+  if (n_s < 0) return fail(LOOPVQ_EINVAL, "n_s=%d must be >= 0", n_s);
+  if (N > N_x) return fail(LOOPVQ_EINVAL, "N=%d exceeds the cache's N_x=%d tokens", N, N_x);
+  if (B > 0 && N > 0) {
+    if (!q || !k || !v || !rope_table) return fail(LOOPVQ_EINVAL, "NULL tensor pointer");
+    if (n_s > 0 && (!sink_k || !sink_v)) return fail(LOOPVQ_EINVAL, "sinks are NULL with n_s=%d", n_s);
+    if ((long long)n_s + N > n_pos) return fail(LOOPVQ_EINVAL, "rope table has %d positions, need %lld", n_pos,
+                                                 (long long)n_s + N);
+  }
+  for (const void* p : {(const void*)q, (const void*)rope_table, sink_k, sink_v, k, v})
+    if (reinterpret_cast<uintptr_t>(p) % 16)
+      return fail(LOOPVQ_EINVAL, "q, k, v, rope_table and sinks must be 16-byte aligned");
+  a = loopvq::PrefillArgs{};
+  a.q = q;
+  a.xk = static_cast<const uint16_t*>(k);
+  a.xv = static_cast<const uint16_t*>(v);
+  a.N_x = N_x;
+  a.sk = static_cast<const uint16_t*>(sink_k);
+  a.sv = static_cast<const uint16_t*>(sink_v);
+  a.rope = rope_table;
+  a.B = B;
+  a.H = g->n_kv_heads;
+  a.Hq = g->n_q_heads;
+  a.T = g->T;
+  a.T_c = g->T_c;
+  a.n_blk = g->T / g->T_c;
+  a.K = g->K;
+  a.G = g->G;
+  a.N = N;
+  a.N_cap = N_x;
+  a.n_s = n_s;
+  a.step0 = step0;
+  a.n_steps = n_steps;
+  a.gqa = g->n_q_heads / g->n_kv_heads;
+  a.scale = (float)(1.0 / std::sqrt((double)g->D));
+  return LOOPVQ_OK;
+}
+
+loopvq_status loopvq_precise_attn(const loopvq_geom* g, const float* q, int32_t step0, int32_t n_steps,
+                                  int32_t B, int32_t N, const void* k, const void* v, int32_t N_x,
+                                  const void* sink_k, const void* sink_v, int32_t n_s, const float* rope_table,
+                                  int32_t n_pos, float* out, float* lse, void* stream) {
+  g_err[0] = 0;
+  loopvq::PrefillArgs a;
+  loopvq_status st = precise_args(g, q, step0, n_steps, B, N, k, v, N_x, sink_k, sink_v, n_s, rope_table, n_pos, a);
+  if (st != LOOPVQ_OK) return st;
+  if (B == 0 || N == 0) return LOOPVQ_OK;
+  if (!out || !lse) return fail(LOOPVQ_EINVAL, "out and lse must not be NULL");
+  if (reinterpret_cast<uintptr_t>(out) % 16) return fail(LOOPVQ_EINVAL, "out must be 16-byte aligned");
+  a.out = out;
+  a.lse = lse;
+  hipError_t e = loopvq::launch_prefill(a, 0, false, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "precise attention launch");
+  return LOOPVQ_OK;
+}
+
+loopvq_status loopvq_precise_attn_backward(const loopvq_geom* g, const float* q, int32_t step0, int32_t n_steps,
+                                           int32_t B, int32_t N, const void* k, const void* v, int32_t N_x,
+                                           const void* sink_k, const void* sink_v, int32_t n_s,
+                                           const float* rope_table, int32_t n_pos, const float* out,
+                                           const float* lse, const float* d_out, float* d_q, float* d_k,
+                                           float* d_v, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  loopvq::PrefillArgs a;
+  loopvq_status st = precise_args(g, q, step0, n_steps, B, N, k, v, N_x, sink_k, sink_v, n_s, rope_table, n_pos, a);
+  if (st != LOOPVQ_OK) return st;
+  if (B == 0 || N == 0) return LOOPVQ_OK;
+  if (!out || !lse || !d_out || !d_q || !d_k || !d_v) return fail(LOOPVQ_EINVAL, "NULL tensor pointer");
+  for (const void* p : {(const void*)out, (const void*)d_out, (const void*)d_q})
+    if (reinterpret_cast<uintptr_t>(p) % 16) return fail(LOOPVQ_EINVAL, "out, d_out and d_q must be 16-byte aligned");
+  const size_t need = (size_t)B * g->n_q_heads * n_steps * N * sizeof(float);
+  if (!workspace || workspace_bytes < need)
+    return fail(LOOPVQ_EWORKSPACE, "workspace of %zu bytes < %zu", workspace_bytes, need);
+  if (reinterpret_cast<uintptr_t>(workspace) % 16) return fail(LOOPVQ_EINVAL, "workspace must be 16-byte aligned");
+  a.out = const_cast<float*>(out);
+  a.lse = const_cast<float*>(lse);
+  a.dout = d_out;
+  a.dq = d_q;
+  a.dxk = d_k;
+  a.dxv = d_v;
+  a.delta = static_cast<float*>(workspace);
+  hipError_t e = loopvq::launch_prefill(a, 0, true, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "precise attention backward launch");
+  return LOOPVQ_OK;
+}
+
+loopvq_status loopvq_fisher_weights(const loopvq_geom* g, const float* d_k, const float* d_v, int32_t B, int32_t N,
+                                    int32_t N_x, const loopvq_pretransform* pt, float* omega_k, float* omega_v,
+                                    void* stream) {
+  g_err[0] = 0;
+  loopvq_status st = check_geom(g);
+  if (st != LOOPVQ_OK) return st;
+  if (B < 0 || N < 0) return fail(LOOPVQ_EINVAL, "B=%d and N=%d must be >= 0", B, N);
+  if (N > N_x) return fail(LOOPVQ_EINVAL, "N=%d exceeds N_x=%d", N, N_x);
+  if (B == 0 || N == 0) return LOOPVQ_OK;
+  if (!d_k || !d_v || !omega_k || !omega_v) return fail(LOOPVQ_EINVAL, "NULL tensor pointer");
+  st = check_pt(pt, B, N, false);
+  if (st != LOOPVQ_OK) return st;
+  loopvq::FisherArgs a{};
+  a.dk = d_k;
+  a.dv = d_v;
+  if (pt) {
+    a.w = pt->w;
+    a.perm = pt->perm;
+    a.sigma = pt->sigma;
+    a.sig_cap = pt->N_cap;
+  }
+  a.wk = omega_k;
+  a.wv = omega_v;
+  a.B = B;
+  a.H = g->n_kv_heads;
+  a.T = g->T;
+  a.T_c = g->T_c;
+  a.n_blk = g->T / g->T_c;
+  a.G = g->G;
+  a.N = N;
+  a.N_x = N_x;
+  a.D = g->D;
+  hipError_t e = loopvq::launch_fisher(a, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "importance weight launch");
+  return LOOPVQ_OK;
+}
+
 }  // extern "C"

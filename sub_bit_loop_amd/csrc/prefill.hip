@@ -15,6 +15,12 @@
 // n_s + j).  Everything is fp32; the RoPE table is fp32 (cos, sin) per
 // (position, frequency), computed in fp64.
 //
+// The same kernels, instantiated with C = 0, read a precise bf16 cache
+// (every step's keys and values as stored) instead of codebook entries, and
+// their key-side backward writes the gradient of every cached key (before
+// RoPE) and value: the gradients the importance weights of the codebook
+// k-means (eq. 3) are made of.
+//
 // All three products run on fp32 matrix cores (v_mfma_f32_32x32x2f32), so the
 // arithmetic is fp32 as in a vector implementation.  Each wave owns 32 rows
 // (queries, or tokens in the key-side passes) and works on LDS tiles of 32
@@ -37,8 +43,9 @@ template <int C>
 __device__ void stage_codebooks(const PrefillArgs& a, int h, int beta, int m, float* s_cbk, float* s_cbv) {
   const int64_t base = ((int64_t)h * a.n_blk + beta) * a.K * a.G;
   // all 256 byte values get a row (zero past K), so any index byte stays in bounds
+  constexpr int CC = C ? C : 1;
   for (int e = threadIdx.x; e < 256 * C; e += blockDim.x) {
-    const int r = e / C, i = e - r * C;
+    const int r = e / CC, i = e - r * CC;
     const int64_t o = base + (int64_t)r * a.G + i * a.T_c + m;
     s_cbk[e] = r < a.K ? bf16_to_f32(a.kcb[o]) : 0.f;
     s_cbv[e] = r < a.K ? bf16_to_f32(a.vcb[o]) : 0.f;
@@ -117,6 +124,23 @@ __device__ void fill_tile_mfma(const PrefillArgs& a, int b, int h, int t, int be
       const uint4 xh = *reinterpret_cast<const uint4*>(a.sk + ro + kPH + 8 * fs);
       const uint4 yl = *reinterpret_cast<const uint4*>(a.sv + ro + 8 * fs);
       const uint4 yh = *reinterpret_cast<const uint4*>(a.sv + ro + kPH + 8 * fs);
+      const uint32_t wxl[4] = {xl.x, xl.y, xl.z, xl.w}, wxh[4] = {xh.x, xh.y, xh.z, xh.w};
+      const uint32_t wyl[4] = {yl.x, yl.y, yl.z, yl.w}, wyh[4] = {yh.x, yh.y, yh.z, yh.w};
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        klo[2 * w] = bf16lo(wxl[w]); klo[2 * w + 1] = bf16hi(wxl[w]);
+        khi[2 * w] = bf16lo(wxh[w]); khi[2 * w + 1] = bf16hi(wxh[w]);
+        vlo[2 * w] = bf16lo(wyl[w]); vlo[2 * w + 1] = bf16hi(wyl[w]);
+        vhi[2 * w] = bf16lo(wyh[w]); vhi[2 * w + 1] = bf16hi(wyh[w]);
+      }
+    } else if constexpr (C == 0) {
+      // precise cache: token j of step t as stored
+      pos = a.n_s + j;
+      const int64_t ro = ((((int64_t)b * a.H + h) * a.T + t) * a.N_x + j) * kPD;
+      const uint4 xl = *reinterpret_cast<const uint4*>(a.xk + ro + 8 * fs);
+      const uint4 xh = *reinterpret_cast<const uint4*>(a.xk + ro + kPH + 8 * fs);
+      const uint4 yl = *reinterpret_cast<const uint4*>(a.xv + ro + 8 * fs);
+      const uint4 yh = *reinterpret_cast<const uint4*>(a.xv + ro + kPH + 8 * fs);
       const uint32_t wxl[4] = {xl.x, xl.y, xl.z, xl.w}, wxh[4] = {xh.x, xh.y, xh.z, xh.w};
       const uint32_t wyl[4] = {yl.x, yl.y, yl.z, yl.w}, wyh[4] = {yh.x, yh.y, yh.z, yh.w};
 #pragma unroll
@@ -490,22 +514,39 @@ __device__ __forceinline__ void token_regs(const PrefillArgs& a, int64_t ir, int
                                            float sg, const int* s_pinv, const float* s_rw, float (&kreg)[64],
                                            float (&vreg)[64]) {
   const float2* rp = reinterpret_cast<const float2*>(a.rope + (int64_t)pos * kPH * 2);
+  if constexpr (C == 0) {
+    // precise cache: ir is the row offset of the token's key and value
+#pragma unroll
+    for (int s = 0; s < 32; ++s) {
+      const int dl = 2 * s + hh, dh = dl + kPH;
+      const float xl = bf16_to_f32(a.xk[ir + dl]), xh = bf16_to_f32(a.xk[ir + dh]);
+      const float2 w = rp[dl];
+      kreg[s] = xl * w.x - xh * w.y;
+      kreg[s + 32] = xh * w.x + xl * w.y;
+      if constexpr (WITH_V) {
+        vreg[s] = bf16_to_f32(a.xv[ir + dl]);
+        vreg[s + 32] = bf16_to_f32(a.xv[ir + dh]);
+      }
+    }
+    return;
+  }
+  constexpr int CC = C ? C : 1;
 #pragma unroll
   for (int s = 0; s < 32; ++s) {
     const int dl = 2 * s + hh, dh = dl + kPH;
     const int zl = PT ? s_pinv[dl] : dl, zh = PT ? s_pinv[dh] : dh;
     const float fl = PT ? sg * s_rw[dl] : 1.f, fh = PT ? sg * s_rw[dh] : 1.f;
     // an index byte >= K (never written by the encode) reads the last entry
-    const int rl = min((int)a.kidx[ir + zl / C], a.K - 1), rh = min((int)a.kidx[ir + zh / C], a.K - 1);
-    const float xl = bf16_to_f32(a.kcb[cbo + (int64_t)rl * a.G + (zl % C) * a.T_c + m]) * fl;
-    const float xh = bf16_to_f32(a.kcb[cbo + (int64_t)rh * a.G + (zh % C) * a.T_c + m]) * fh;
+    const int rl = min((int)a.kidx[ir + zl / CC], a.K - 1), rh = min((int)a.kidx[ir + zh / CC], a.K - 1);
+    const float xl = bf16_to_f32(a.kcb[cbo + (int64_t)rl * a.G + (zl % CC) * a.T_c + m]) * fl;
+    const float xh = bf16_to_f32(a.kcb[cbo + (int64_t)rh * a.G + (zh % CC) * a.T_c + m]) * fh;
     const float2 w = rp[dl];
     kreg[s] = xl * w.x - xh * w.y;
     kreg[s + 32] = xh * w.x + xl * w.y;
     if constexpr (WITH_V) {
-      const int ul = min((int)a.vidx[ir + dl / C], a.K - 1), uh = min((int)a.vidx[ir + dh / C], a.K - 1);
-      vreg[s] = bf16_to_f32(a.vcb[cbo + (int64_t)ul * a.G + (dl % C) * a.T_c + m]);
-      vreg[s + 32] = bf16_to_f32(a.vcb[cbo + (int64_t)uh * a.G + (dh % C) * a.T_c + m]);
+      const int ul = min((int)a.vidx[ir + dl / CC], a.K - 1), uh = min((int)a.vidx[ir + dh / CC], a.K - 1);
+      vreg[s] = bf16_to_f32(a.vcb[cbo + (int64_t)ul * a.G + (dl % CC) * a.T_c + m]);
+      vreg[s + 32] = bf16_to_f32(a.vcb[cbo + (int64_t)uh * a.G + (dh % CC) * a.T_c + m]);
     }
   }
 }
@@ -533,7 +574,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   if constexpr (PT) stage_pretransform(a, h, s_pinv, s_rw);
   __syncthreads();
 
-  const int64_t ir = ((((int64_t)b * a.H + h) * a.n_blk + beta) * a.N_cap + (vk ? j : 0)) * (kPD / C);
+  constexpr int CC = C ? C : 1;
+  // index row of the token (precise cache: row offset of its key and value)
+  const int64_t ir = C ? ((((int64_t)b * a.H + h) * a.n_blk + beta) * a.N_cap + (vk ? j : 0)) * (kPD / CC)
+                       : ((((int64_t)b * a.H + h) * a.T + t) * a.N_x + (vk ? j : 0)) * kPD;
   const int64_t cbo = ((int64_t)h * a.n_blk + beta) * a.K * a.G;
   const int pos = a.n_s + (vk ? j : 0);
   const float sg = PT ? key_sigma(a, b, vk ? j : 0, t) : 1.f;
@@ -619,7 +663,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   }
   // acc[db][r] is the gradient of channel 32db + 8(r/4) + 4hh + r%4 of token j
   // (K pass: of its rotated key, before the 1/sqrt(D) scale)
-  if (vk) {
+  if (vk && C == 0) {
+    // precise cache: the gradient of this token's pre-RoPE key (rotation
+    // undone) or value, added (q-heads of a GQA group share the token)
+    if constexpr (KPASS) {
+      const float2* rp = reinterpret_cast<const float2*>(a.rope + (int64_t)pos * kPH * 2);
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int dl = 32 * db + 8 * (r >> 2) + 4 * hh + (r & 3), dh = dl + kPH;
+          const float2 w = rp[dl];
+          unsafeAtomicAdd(&a.dxk[ir + dl], (acc[db][r] * w.x + acc[db + 2][r] * w.y) * a.scale);
+          unsafeAtomicAdd(&a.dxk[ir + dh], (acc[db + 2][r] * w.x - acc[db][r] * w.y) * a.scale);
+        }
+    } else {
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) unsafeAtomicAdd(&a.dxv[ir + 32 * db + 8 * (r >> 2) + 4 * hh + (r & 3)], acc[db][r]);
+    }
+  } else if (vk) {
     if constexpr (KPASS) {
       const float2* rp = reinterpret_cast<const float2*>(a.rope + (int64_t)pos * kPH * 2);
 #pragma unroll
@@ -633,8 +697,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
           const float gl = (acc[db][r] * w.x + acc[db + 2][r] * w.y) * (PT ? a.scale * sg * s_rw[dl] : a.scale);
           const float gh = (acc[db + 2][r] * w.x - acc[db][r] * w.y) * (PT ? a.scale * sg * s_rw[dh] : a.scale);
           const int zl = PT ? s_pinv[dl] : dl, zh = PT ? s_pinv[dh] : dh;
-          atomicAdd(&s_g[a.kidx[ir + zl / C] * C + zl % C], gl);
-          atomicAdd(&s_g[a.kidx[ir + zh / C] * C + zh % C], gh);
+          atomicAdd(&s_g[a.kidx[ir + zl / CC] * C + zl % CC], gl);
+          atomicAdd(&s_g[a.kidx[ir + zh / CC] * C + zh % CC], gh);
         }
     } else {
 #pragma unroll
@@ -642,14 +706,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int d = 32 * db + 8 * (r >> 2) + 4 * hh + (r & 3);
-          atomicAdd(&s_g[a.vidx[ir + d / C] * C + d % C], acc[db][r]);
+          atomicAdd(&s_g[a.vidx[ir + d / CC] * C + d % CC], acc[db][r]);
         }
     }
   }
   __syncthreads();
   float* g = KPASS ? a.dkcb : a.dvcb;
   for (int e = threadIdx.x; e < a.K * C; e += blockDim.x) {
-    const int r = e / C, i = e - r * C;
+    const int r = e / CC, i = e - r * CC;
     if (s_g[e] != 0.f) unsafeAtomicAdd(&g[cbo + (int64_t)r * a.G + i * a.T_c + m], s_g[e]);
   }
 }
@@ -688,7 +752,8 @@ hipError_t launch_rope_table_f32(float* tab, int n_pos, int D, double theta, hip
 template <int C, bool PT>
 static hipError_t prefill_launch(const PrefillArgs& a, bool backward, hipStream_t s) {
   const size_t lds = (size_t)2 * 256 * C * sizeof(float);
-  // dynamic LDS beyond the default allowance (C = 32 takes 64 KiB)
+  // dynamic LDS beyond the default allowance (C = 32 takes 64 KiB; the
+  // precise cache, C = 0, none)
   for (const void* k : {reinterpret_cast<const void*>(&prefill_fwd_mfma_kernel<C, PT>),
                         reinterpret_cast<const void*>(&prefill_bwd_kv_mfma_kernel<C, PT, false>),
                         reinterpret_cast<const void*>(&prefill_bwd_kv_mfma_kernel<C, PT, true>),
@@ -704,9 +769,11 @@ static hipError_t prefill_launch(const PrefillArgs& a, bool backward, hipStream_
   const int64_t rows = (int64_t)a.B * a.Hq * a.n_steps * a.N;
   hipLaunchKernelGGL(prefill_delta_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, a.out, a.dout,
                      a.delta, rows);
-  const int64_t ncb = (int64_t)a.H * a.n_blk * a.K * a.G;
-  hipLaunchKernelGGL(prefill_zero_kernel, dim3((unsigned)((ncb + 255) / 256)), dim3(256), 0, s, a.dkcb, ncb);
-  hipLaunchKernelGGL(prefill_zero_kernel, dim3((unsigned)((ncb + 255) / 256)), dim3(256), 0, s, a.dvcb, ncb);
+  if constexpr (C != 0) {
+    const int64_t ncb = (int64_t)a.H * a.n_blk * a.K * a.G;
+    hipLaunchKernelGGL(prefill_zero_kernel, dim3((unsigned)((ncb + 255) / 256)), dim3(256), 0, s, a.dkcb, ncb);
+    hipLaunchKernelGGL(prefill_zero_kernel, dim3((unsigned)((ncb + 255) / 256)), dim3(256), 0, s, a.dvcb, ncb);
+  }
   const dim3 gk((a.N + kMT - 1) / kMT, a.Hq, a.B * a.n_steps);
   const size_t lds_g = (size_t)256 * C * sizeof(float);
   hipLaunchKernelGGL((prefill_bwd_kv_mfma_kernel<C, PT, false>), gk, dim3(256), lds_g, s, a);
@@ -723,6 +790,7 @@ static hipError_t prefill_launch_pt(const PrefillArgs& a, bool backward, hipStre
 
 hipError_t launch_prefill(const PrefillArgs& a, int C, bool backward, hipStream_t s) {
   switch (C) {
+    case 0: return prefill_launch<0, false>(a, backward, s);
     case 2: return prefill_launch_pt<2>(a, backward, s);
     case 4: return prefill_launch_pt<4>(a, backward, s);
     case 8: return prefill_launch_pt<8>(a, backward, s);

@@ -15,8 +15,13 @@
   takes KL(p || q) against the precise run's outputs, backpropagates into the
   codebooks and makes one Adam step on fp32 master copies (the kernels read
   their bf16 rounding).
+* PreciseAttention / fisher_importance -- the importance weights of the
+  codebook k-means ("codebook and calibration", eq. 3): the stack attends to
+  the precise cache (loopvq_precise_attn), the next-token loss against the
+  given targets is backpropagated (loopvq_precise_attn_backward adds the
+  gradient of every cached key and value), and loopvq_fisher_weights turns
+  those gradients into omega_n = ||dL/dz_n||^2 per joint vector.
 """
-import math
 
 import torch
 
@@ -93,27 +98,13 @@ class ToyLoopedStack:
         return rms_norm(h) @ self.Wu
 
 
-def precise_attend(k, v, sink_k, sink_v, rope, n_q_heads):
+def precise_attend(g, k, v, sink_k, sink_v, rope):
     """attend() over the stored bf16 cache k, v [B][H][T][N][D] (pre-RoPE keys)
-    with the bf16 sinks: the precise run the codebooks are fitted against."""
-    B, H, T, N, D = k.shape
-    n_s = sink_k.shape[3]
-    gqa = n_q_heads // H
-    pos_cs = rope[:n_s + N]
-    c, s = pos_cs[..., 0], pos_cs[..., 1]
-    mask = torch.ones((N, n_s + N), dtype=torch.bool, device=k.device)
-    mask[:, n_s:] = torch.tril(mask[:, n_s:])
-
+    with the bf16 sinks (loopvq_precise_attn): the precise run the codebooks
+    are fitted against."""
     def attend(t, Q):
-        keys = torch.cat([sink_k[:, :, t], k[:, :, t, :N]], dim=2).float()          # [B, H, n_s+N, D]
-        vals = torch.cat([sink_v[:, :, t], v[:, :, t, :N]], dim=2).float()
-        a, b = keys[..., :D // 2], keys[..., D // 2:]
-        kr = torch.cat([a * c - b * s, b * c + a * s], dim=-1)
-        kr = kr.repeat_interleave(gqa, dim=1)
-        vals = vals.repeat_interleave(gqa, dim=1)
-        sc = (Q @ kr.transpose(-1, -2).contiguous()) / math.sqrt(D)
-        sc = sc.masked_fill(~mask, float("-inf"))
-        return torch.softmax(sc, dim=-1) @ vals
+        out, _ = api.precise_attn(g, Q[:, :, None].contiguous(), k, v, sink_k, sink_v, rope, step0=t)
+        return out[:, :, 0]
     return attend
 
 
@@ -153,7 +144,7 @@ def finetune_codebooks(stack, g, x, k, v, sink_k, sink_v, k_cb, v_cb, iters, lr=
     stack's precise outputs.  Returns (fp32 masters, list of J before each
     step).  callback(it, J) is called after every iteration."""
     with torch.no_grad():
-        logp = torch.log_softmax(stack.logits(x, precise_attend(k, v, sink_k, sink_v, stack.rope, stack.Hq)), -1)
+        logp = torch.log_softmax(stack.logits(x, precise_attend(g, k, v, sink_k, sink_v, stack.rope)), -1)
     km = k_cb.float().clone().requires_grad_(True)
     vm = v_cb.float().clone().requires_grad_(True)
     opt = torch.optim.Adam([km, vm], lr=lr)
@@ -170,3 +161,60 @@ def finetune_codebooks(stack, g, x, k, v, sink_k, sink_v, k_cb, v_cb, iters, lr=
         if callback is not None:
             callback(it, Js[-1])
     return km.detach(), vm.detach(), Js
+
+
+class _PreciseState:
+    """Per-call constants of PreciseAttention and the cache-gradient buffers
+    its backward adds into."""
+
+    def __init__(self, g, k, v, sink_k, sink_v, rope, step, d_k, d_v):
+        self.g, self.k, self.v = g, k, v
+        self.sink_k, self.sink_v, self.rope, self.step = sink_k, sink_v, rope, step
+        self.d_k, self.d_v = d_k, d_v
+
+
+class PreciseAttention(torch.autograd.Function):
+    """o = attention(q, precise cache) for one loop step.  `anchor` is a
+    scalar that requires grad, so that the backward runs even when q does
+    not; the backward returns d_q and adds the step's cache gradients into
+    st.d_k / st.d_v."""
+
+    @staticmethod
+    def forward(ctx, q, anchor, st):
+        q = q.contiguous()
+        out, lse = api.precise_attn(st.g, q, st.k, st.v, st.sink_k, st.sink_v, st.rope, step0=st.step)
+        ctx.save_for_backward(q, out, lse, anchor)
+        ctx.st = st
+        return out
+
+    @staticmethod
+    def backward(ctx, d_out):
+        q, out, lse, anchor = ctx.saved_tensors
+        st = ctx.st
+        d_q = api.precise_attn_backward(st.g, q, st.k, st.v, st.sink_k, st.sink_v, st.rope, out, lse,
+                                        d_out.contiguous(), st.d_k, st.d_v, step0=st.step)
+        return d_q, torch.zeros_like(anchor), None
+
+
+def fisher_importance(stack, g, x, k, v, sink_k, sink_v, targets, pt=None):
+    """Importance weights of every joint vector of the precise cache k, v
+    bf16 [B][H][T][N][D]: L = sum over batch entries of the mean next-token
+    cross-entropy of the stack against targets int64 [B][N]; returns
+    (L, omega_k, omega_v) with omega fp32 [B][H][n_blk][N][D/c] (pt: the keys'
+    pre-transform, whose sigma the encode wrote, to weight key vectors in the
+    transformed space)."""
+    B, N = targets.shape
+    d_k = torch.zeros(k.shape, dtype=torch.float32, device=k.device)
+    d_v = torch.zeros(v.shape, dtype=torch.float32, device=v.device)
+    anchor = torch.zeros((), dtype=torch.float32, device=k.device, requires_grad=True)
+
+    def attend(t, Q):
+        st = _PreciseState(g, k, v, sink_k, sink_v, stack.rope, t, d_k, d_v)
+        return PreciseAttention.apply(Q[:, :, None], anchor, st)[:, :, 0]
+    with torch.enable_grad():
+        logits = stack.logits(x, attend)
+        lq = torch.log_softmax(logits, dim=-1)
+        L = -lq.gather(-1, targets[..., None]).squeeze(-1).mean(dim=-1).sum()
+        L.backward()
+    omega_k, omega_v = api.fisher_weights(g, d_k, d_v, N, pt)
+    return float(L.detach()), omega_k, omega_v

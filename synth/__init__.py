@@ -10,9 +10,9 @@ from .generator import (SeedPlan, gen_kv_layer, gen_queries, gen_sinks,
                         gen_tasq_params, gen_calibration_kv)
 from .codebooks import train_codebooks
 from .inputs import build_inputs, random_codebooks
-from .toy import gen_toy_stack
+from .toy import gen_targets, gen_toy_stack
 
 __all__ = ["CONFIGS", "LoopConfig", "config_by_index", "SeedPlan",
            "gen_kv_layer", "gen_queries", "gen_sinks", "gen_tasq_params",
            "gen_calibration_kv", "train_codebooks", "build_inputs",
-           "random_codebooks", "gen_toy_stack"]
+           "random_codebooks", "gen_toy_stack", "gen_targets"]

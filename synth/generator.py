@@ -23,7 +23,7 @@ from .configs import LoopConfig
 
 ROLE = {"scale_k": 0, "scale_v": 1, "calib_k": 2, "calib_v": 3, "ctx_k": 4,
         "ctx_v": 5, "sinks": 6, "queries": 7, "kmeans": 8, "w": 9, "perm": 10,
-        "toy_x": 11, "toy_w": 12}
+        "toy_x": 11, "toy_w": 12, "toy_y": 13}
 
 
 @dataclass(frozen=True)

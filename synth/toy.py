@@ -15,6 +15,15 @@ from .configs import LoopConfig
 from .generator import SeedPlan
 
 
+def gen_targets(cfg: LoopConfig, layer: int = 0, device="cpu", vocab: int = 256, B=None, N=None):
+    """Next-token targets int64 [B][N], uniform over the vocabulary (no data
+    exists; they stand in for a calibration set's tokens)."""
+    B = cfg.B if B is None else B
+    N = cfg.N if N is None else N
+    g = SeedPlan(cfg.index).gen(layer, "toy_y", "cpu")
+    return torch.randint(0, vocab, (B, N), generator=g, dtype=torch.int64).to(device)
+
+
 def gen_toy_stack(cfg: LoopConfig, layer: int = 0, device="cpu", vocab: int = 256, B=None):
     """dict(x [B][N][d], Wq [d][d], Wo [d][d], Wu [d][vocab]) in fp32 on `device`."""
     B = cfg.B if B is None else B

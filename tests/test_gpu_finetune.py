@@ -145,8 +145,8 @@ def test_finetune_gradient_matches_oracle():
     kidx = kidx[:, :, :, :cfg.N].contiguous()
     vidx = vidx[:, :, :, :cfg.N].contiguous()
     with torch.no_grad():
-        logp = torch.log_softmax(stack.logits(toy["x"], ft.precise_attend(inp["k"], inp["v"], inp["sink_k"],
-                                                                            inp["sink_v"], rope, cfg.H_q)), -1)
+        logp = torch.log_softmax(stack.logits(toy["x"], ft.precise_attend(g, inp["k"], inp["v"], inp["sink_k"],
+                                                                            inp["sink_v"], rope)), -1)
     km = inp["k_cb"].float().clone().requires_grad_(True)
     vm = inp["v_cb"].float().clone().requires_grad_(True)
     J = ft.kl_objective(logp, ft.compressed_logits(stack, g, toy["x"], inp["k"], inp["v"], inp["sink_k"],
