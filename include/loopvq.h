@@ -164,6 +164,12 @@ loopvq_status loopvq_decode_attn_workspace(const loopvq_geom* g, int32_t B, int3
  * workspace must be 16-byte aligned.
  * A row with no keys at all (n_s == 0, N_b == 0 and n_r == 0) yields out = 0 and
  * lse = -inf.
+ * Range: the fast kernels compute in fp16 after power-of-two rescaling of
+ * the queries, of each block's codebooks together with the bf16 sinks and
+ * recent rows, and of the values; the scales are folded back into the fp32
+ * scores and outputs (fp32), so no fp16 value overflows for finite bf16
+ * inputs (with keys pre-transformed, the keys' range is taken after the
+ * weights w, the queries' after division by them).  Inputs must be finite.
  * Errors: EINVAL for NULL pointers, bad geometry, step range outside [0, T),
  * N > N_cap, n_r > R_cap, n_pos too small; EWORKSPACE for a short workspace; ENOTSUP as for
  * loopvq_encode. */

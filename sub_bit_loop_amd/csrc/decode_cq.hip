@@ -16,7 +16,9 @@
 //     (channels 64+16g ..): bytes g of the two index dwords.
 //   * Codewords sit in LDS as fp16 (16 channels, 32 bytes) with a stride of
 //     three 16-byte slots; codebooks are rescaled by powers of two on load
-//     (keys to fit fp16, values below 2^kCVLim), scales folded back later.
+//     (keys to fit fp16, values below 2^kCVLim; the bf16 sinks and recent
+//     rows count in those ranges) and the queries by one of their own; the
+//     scales are folded back later.
 //   * Rotation on packed fp16 pairs, scores as v_dot2_f32_f16 sums, the four
 //     lanes of a token reduce with DPP, online softmax in base 2 whose running
 //     maximum may lag by kCLag, and P*V in packed fp16 flushed into fp32 every
@@ -37,12 +39,6 @@ __device__ __forceinline__ uint32_t pack_hc2(float a, float b) {
   return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
 }
 
-__device__ __forceinline__ int pow2_shift_c(float max_abs, int lim) {
-  if (!(max_abs > 0.f)) return 0;
-  const int e = ilogbf(max_abs) + 1;    // max_abs < 2^e
-  return e > lim ? e - lim : 0;
-}
-
 // fp16 partial sums of P*V: weights <= 2^kCLag, |v| <= 2^kCVLim, kCFlush tokens
 // per lane between flushes keep a partial below 2^(3+7+4) = 16384.
 constexpr int kCFlush = 16, kCLag = 3, kCVLim = 7;
@@ -55,7 +51,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_cq_kernel(DecodeArgs a)
   __shared__ __attribute__((aligned(16))) uint4 s_k[256 * kCQS];
   __shared__ __attribute__((aligned(16))) uint4 s_v[256 * kCQS];
   __shared__ float s_red[NW][D + 2];
-  __shared__ float s_amax[2][NW];
+  __shared__ float s_amax[3][NW];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int slot = lane >> 2, g = lane & 3;
@@ -68,11 +64,15 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_cq_kernel(DecodeArgs a)
 
   // ---- codebooks -> LDS (fp16), power-of-two range scaling
   const int64_t cbo = ((int64_t)h * a.n_blk + beta) * a.K * G;
-  int shk, shv;
+  int shk, shv, shq;
   {
     const int r = tid;   // one row per thread
     float kx[G], vx[G];
-    float mk = 0.f, mv = 0.f;
+    float mq, mk, mv;   // the bf16 sinks and recent rows share the codebooks' scales
+    if (served)
+      decode_input_absmax(a, b, hq, 1, h, beta, beta + 1, split == 0, nullptr, mq, mk, mv);
+    else
+      mq = mk = mv = 0.f;
     if (r < a.K) {
       const uint4* pk = reinterpret_cast<const uint4*>(a.kcb + cbo + r * G);
       const uint4* pv = reinterpret_cast<const uint4*>(a.vcb + cbo + r * G);
@@ -98,18 +98,22 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_cq_kernel(DecodeArgs a)
       for (int u = 0; u < G; ++u) kx[u] = vx[u] = 0.f;
     }
     for (int off = 32; off >= 1; off >>= 1) {
+      mq = fmaxf(mq, __shfl_xor(mq, off));
       mk = fmaxf(mk, __shfl_xor(mk, off));
       mv = fmaxf(mv, __shfl_xor(mv, off));
     }
     if (lane == 0) {
       s_amax[0][wave] = mk;
       s_amax[1][wave] = mv;
+      s_amax[2][wave] = mq;
     }
     __syncthreads();
     mk = fmaxf(fmaxf(s_amax[0][0], s_amax[0][1]), fmaxf(s_amax[0][2], s_amax[0][3]));
     mv = fmaxf(fmaxf(s_amax[1][0], s_amax[1][1]), fmaxf(s_amax[1][2], s_amax[1][3]));
-    shk = pow2_shift_c(mk, 14);
-    shv = pow2_shift_c(mv, kCVLim);
+    mq = fmaxf(fmaxf(s_amax[2][0], s_amax[2][1]), fmaxf(s_amax[2][2], s_amax[2][3]));
+    shq = pow2_range_shift(mq, 14);
+    shk = pow2_range_shift(mk, 14);
+    shv = pow2_range_shift(mv, kCVLim);
     const float sk = ldexpf(1.f, -shk), sv = ldexpf(1.f, -shv);
     uint32_t kw[8], vw[8];
 #pragma unroll
@@ -128,14 +132,15 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_cq_kernel(DecodeArgs a)
   // query of this step: chunk g (channel pairs 16g + 2i) and its partner chunk
   const uint16_t* qr = a.q + (((int64_t)b * a.Hq + hq) * a.n_steps + (served ? beta - a.step0 : 0)) * D;
   uint32_t q1[8], q2[8];
+  const float qsc = ldexpf(1.f, -shq);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const uint32_t w1 = *reinterpret_cast<const uint32_t*>(qr + 16 * g + 2 * i);
     const uint32_t w2 = *reinterpret_cast<const uint32_t*>(qr + HD + 16 * g + 2 * i);
-    q1[i] = served ? pack_hc2(bf16lo(w1), bf16hi(w1)) : 0u;
-    q2[i] = served ? pack_hc2(bf16lo(w2), bf16hi(w2)) : 0u;
+    q1[i] = served ? pack_hc2(bf16lo(w1) * qsc, bf16hi(w1) * qsc) : 0u;
+    q2[i] = served ? pack_hc2(bf16lo(w2) * qsc, bf16hi(w2) * qsc) : 0u;
   }
-  const float sscale = a.qscale * ldexpf(1.f, shk);
+  const float sscale = a.qscale * ldexpf(1.f, shk + shq);
 
   float mrow = -INFINITY, lrow = 0.f;
   float acc[2][16];

@@ -22,8 +22,9 @@
 //     inside a quad, the softmax is online (base 2) and P*V accumulates packed
 //     fp16 pairs that are flushed into fp32 every kFlush tokens.
 //   * Codebooks are rescaled by a power of two on load so that keys fit fp16
-//     and values stay below 2^kVLim; the scales are folded back into scores and
-//     outputs.
+//     and values stay below 2^kVLim (the bf16 sinks and recent rows count in
+//     those ranges), and the queries by one of their own; the scales are
+//     folded back into scores and outputs.
 // One workgroup serves one (batch, q-head, block, context split); q-heads of a
 // GQA group gather the same rows in separate workgroups.
 #include "common.h"
@@ -36,12 +37,6 @@ typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ h2_t as_h2(uint32_t w) { return __builtin_bit_cast(h2_t, w); }
 
 // Power-of-two exponent s >= 0 with max_abs * 2^-s <= 2^lim.
-__device__ __forceinline__ int pow2_shift(float max_abs, int lim) {
-  if (!(max_abs > 0.f)) return 0;
-  const int e = ilogbf(max_abs) + 1;    // max_abs < 2^e
-  return e > lim ? e - lim : 0;
-}
-
 __device__ __forceinline__ uint32_t pack_h2(float a, float b) {
   const _Float16 x = (_Float16)a, y = (_Float16)b;
   return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
@@ -65,7 +60,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_fast_kernel(DecodeArgs 
   __shared__ __attribute__((aligned(16))) uint4 s_k[256 * 2 * QW];
   __shared__ __attribute__((aligned(16))) uint4 s_v[256 * 2 * QW];
   __shared__ float s_red[NW][TC][D + 2];
-  __shared__ float s_amax[2][NW];
+  __shared__ float s_amax[3][NW];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int sl = lane & 7, slot = lane >> 3;
@@ -75,12 +70,14 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_fast_kernel(DecodeArgs 
   const int h = hq / a.gqa;
   const int b = blockIdx.z / a.n_blk_serv;
   const int beta = a.blk0 + (blockIdx.z - b * a.n_blk_serv);
+  const int t_lo = max(a.step0, beta * TC), t_hi = min(a.step0 + a.n_steps, (beta + 1) * TC);
 
   // ---- codebooks -> LDS (fp16, step-major), with power-of-two range scaling
   const int64_t cbo = ((int64_t)h * a.n_blk + beta) * a.K * G;
   const int r = tid;   // one row per thread
   float kx[G], vx[G];
-  float mk = 0.f, mv = 0.f;
+  float mq, mk, mv;   // the bf16 sinks and recent rows share the codebooks' scales
+  decode_input_absmax(a, b, hq, 1, h, t_lo, t_hi, split == 0, nullptr, mq, mk, mv);
   if (r < a.K) {
     const uint4* pk = reinterpret_cast<const uint4*>(a.kcb + cbo + r * G);
     const uint4* pv = reinterpret_cast<const uint4*>(a.vcb + cbo + r * G);
@@ -106,17 +103,21 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_fast_kernel(DecodeArgs 
     for (int u = 0; u < G; ++u) kx[u] = vx[u] = 0.f;
   }
   for (int off = 32; off >= 1; off >>= 1) {
+    mq = fmaxf(mq, __shfl_xor(mq, off));
     mk = fmaxf(mk, __shfl_xor(mk, off));
     mv = fmaxf(mv, __shfl_xor(mv, off));
   }
   if (lane == 0) {
     s_amax[0][wave] = mk;
     s_amax[1][wave] = mv;
+    s_amax[2][wave] = mq;
   }
   __syncthreads();
   mk = fmaxf(fmaxf(s_amax[0][0], s_amax[0][1]), fmaxf(s_amax[0][2], s_amax[0][3]));
   mv = fmaxf(fmaxf(s_amax[1][0], s_amax[1][1]), fmaxf(s_amax[1][2], s_amax[1][3]));
-  const int shk = pow2_shift(mk, 14), shv = pow2_shift(mv, kVLim);
+  mq = fmaxf(fmaxf(s_amax[2][0], s_amax[2][1]), fmaxf(s_amax[2][2], s_amax[2][3]));
+  const int shk = pow2_range_shift(mk, 14), shv = pow2_range_shift(mv, kVLim), shq = pow2_range_shift(mq, 14);
+  const float qsc = ldexpf(1.f, -shq);
   {
     const float sk = ldexpf(1.f, -shk), sv = ldexpf(1.f, -shv);
     uint32_t kw[2 * C], vw[2 * C];   // [m][pair]: step m, channels (2*pair, 2*pair+1)
@@ -137,7 +138,6 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_fast_kernel(DecodeArgs 
   }
 
   // ---- queries of this lane: steps 2hs+ml, chunk pairs k, partner p, channel pair ip
-  const int t_lo = max(a.step0, beta * TC), t_hi = min(a.step0 + a.n_steps, (beta + 1) * TC);
   uint32_t qv[2][NPL][2][DW];
 #pragma unroll
   for (int ml = 0; ml < 2; ++ml) {
@@ -152,12 +152,12 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_fast_kernel(DecodeArgs 
 #pragma unroll
         for (int ip = 0; ip < DW; ++ip) {
           const uint32_t w = *reinterpret_cast<const uint32_t*>(qr + d0 + 2 * ip);
-          qv[ml][k][p][ip] = act ? pack_h2(bf16lo(w), bf16hi(w)) : 0u;
+          qv[ml][k][p][ip] = act ? pack_h2(bf16lo(w) * qsc, bf16hi(w) * qsc) : 0u;
         }
       }
     }
   }
-  const float sscale = a.qscale * ldexpf(1.f, shk);
+  const float sscale = a.qscale * ldexpf(1.f, shk + shq);
 
   float mrow[2] = {-INFINITY, -INFINITY}, lrow[2] = {0.f, 0.f};
   float acc[2][NPL][2][C];
@@ -463,7 +463,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(DecodeArgs 
   __shared__ __attribute__((aligned(16))) uint32_t s_k[256 * DW];
   __shared__ __attribute__((aligned(16))) uint32_t s_v[256 * DW];
   __shared__ float s_red[NW][HPW][D + 2];
-  __shared__ float s_amax[2][NW];
+  __shared__ float s_amax[3][NW];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int sl = lane & 7, slot = lane >> 3;
@@ -480,7 +480,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(DecodeArgs 
   const int64_t cbo = ((int64_t)h * a.n_blk + beta) * a.K * G;
   const int r = tid;   // one row per thread
   float kx[C], vx[C];
-  float mk = 0.f, mv = 0.f;
+  float mq, mk, mv;   // the bf16 sinks and recent rows share the codebooks' scales
+  decode_input_absmax(a, b, hq0, HPW, h, t, t + 1, split == 0, nullptr, mq, mk, mv);
 #pragma unroll
   for (int i = 0; i < C; ++i) kx[i] = vx[i] = 0.f;
   if (r < a.K) {
@@ -494,17 +495,21 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(DecodeArgs 
     }
   }
   for (int off = 32; off >= 1; off >>= 1) {
+    mq = fmaxf(mq, __shfl_xor(mq, off));
     mk = fmaxf(mk, __shfl_xor(mk, off));
     mv = fmaxf(mv, __shfl_xor(mv, off));
   }
   if (lane == 0) {
     s_amax[0][wave] = mk;
     s_amax[1][wave] = mv;
+    s_amax[2][wave] = mq;
   }
   __syncthreads();
   mk = fmaxf(fmaxf(s_amax[0][0], s_amax[0][1]), fmaxf(s_amax[0][2], s_amax[0][3]));
   mv = fmaxf(fmaxf(s_amax[1][0], s_amax[1][1]), fmaxf(s_amax[1][2], s_amax[1][3]));
-  const int shk = pow2_shift(mk, 14), shv = pow2_shift(mv, kVLim);
+  mq = fmaxf(fmaxf(s_amax[2][0], s_amax[2][1]), fmaxf(s_amax[2][2], s_amax[2][3]));
+  const int shk = pow2_range_shift(mk, 14), shv = pow2_range_shift(mv, kVLim), shq = pow2_range_shift(mq, 14);
+  const float qsc = ldexpf(1.f, -shq);
   {
     const float sk = ldexpf(1.f, -shk), sv = ldexpf(1.f, -shv);
 #pragma unroll
@@ -527,11 +532,11 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(DecodeArgs 
 #pragma unroll
         for (int ip = 0; ip < DW; ++ip) {
           const uint32_t w = *reinterpret_cast<const uint32_t*>(qr + d0 + 2 * ip);
-          qv[hh][k][p][ip] = pack_h2(bf16lo(w), bf16hi(w));
+          qv[hh][k][p][ip] = pack_h2(bf16lo(w) * qsc, bf16hi(w) * qsc);
         }
       }
   }
-  const float sscale = a.qscale * ldexpf(1.f, shk);
+  const float sscale = a.qscale * ldexpf(1.f, shk + shq);
 
   float mrow[HPW], lrow[HPW];
   float acc[HPW][NPL][2][C];

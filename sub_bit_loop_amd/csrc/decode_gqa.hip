@@ -51,12 +51,6 @@ __device__ __forceinline__ uint32_t pack_h2g(float a, float b) {
   return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
 }
 
-__device__ __forceinline__ int pow2_shift_g(float max_abs, int lim) {
-  if (!(max_abs > 0.f)) return 0;
-  const int e = ilogbf(max_abs) + 1;
-  return e > lim ? e - lim : 0;
-}
-
 // Four fp16 at an 8-byte aligned LDS byte address, transposed within the
 // lane's 16-lane group (ds_read_b64_tr_b16).
 __device__ __forceinline__ h4g_t lds_tr4(const void* base, uint32_t byte_off) {
@@ -115,7 +109,7 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
   uint4* const s_v = s_kv + 256 * CWS;
   float (*const s_red)[16][D + 2] = reinterpret_cast<float (*)[16][D + 2]>(s_kv);
   uint16_t (*const s_stage)[TILE][SROW] = reinterpret_cast<uint16_t (*)[TILE][SROW]>(s_kv);
-  __shared__ float s_amax[2][NW];
+  __shared__ float s_amax[3][NW];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t16 = lane & 15, q4 = lane >> 4;     // key role: token, channel quarter
@@ -137,7 +131,8 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
   const int64_t cbo = ((int64_t)h * a.n_blk + beta) * a.K * G;
   const int r = tid;
   float kx[G], vx[G];
-  float mk = 0.f, mv = 0.f;
+  float mq, mk, mv;   // the bf16 sinks and recent rows share the codebooks' scales
+  decode_input_absmax(a, b, hq0, HPW, h, t_lo, t_hi, split == 0, nullptr, mq, mk, mv);
   if (r < a.K) {
     const uint4* pk = reinterpret_cast<const uint4*>(a.kcb + cbo + r * G);
     const uint4* pv = reinterpret_cast<const uint4*>(a.vcb + cbo + r * G);
@@ -163,17 +158,20 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
     for (int u = 0; u < G; ++u) kx[u] = vx[u] = 0.f;
   }
   for (int off = 32; off >= 1; off >>= 1) {
+    mq = fmaxf(mq, __shfl_xor(mq, off));
     mk = fmaxf(mk, __shfl_xor(mk, off));
     mv = fmaxf(mv, __shfl_xor(mv, off));
   }
   if (lane == 0) {
     s_amax[0][wave] = mk;
     s_amax[1][wave] = mv;
+    s_amax[2][wave] = mq;
   }
   __syncthreads();
   mk = fmaxf(fmaxf(s_amax[0][0], s_amax[0][1]), fmaxf(s_amax[0][2], s_amax[0][3]));
   mv = fmaxf(fmaxf(s_amax[1][0], s_amax[1][1]), fmaxf(s_amax[1][2], s_amax[1][3]));
-  const int shk = pow2_shift_g(mk, 14), shv = pow2_shift_g(mv, kGVLim);
+  mq = fmaxf(fmaxf(s_amax[2][0], s_amax[2][1]), fmaxf(s_amax[2][2], s_amax[2][3]));
+  const int shk = pow2_range_shift(mk, 14), shv = pow2_range_shift(mv, kGVLim), shq = pow2_range_shift(mq, 14);
   {
     const float sk = ldexpf(1.f, -shk), sv = ldexpf(1.f, -shv);
     uint32_t kw[TC * DW], vw[TC * DW];   // [m][channel pair]
@@ -195,6 +193,7 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
   // k quarter kq = lane / 16; block r' holds channels 32r' + 8kq .. +7.
   h8_t qa[4];
   {
+    const float qsc = ldexpf(1.f, -shq);
     const int hh = rho >> 2, m = rho & 3, kq = lane >> 4;
     const int t = beta * TC + m;
     const bool act = hh < HPW && t >= t_lo && t < t_hi;
@@ -205,12 +204,12 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
       const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        qa[rp][2 * e] = act ? (_Float16)bf16lo(ws[e]) : (_Float16)0.f;
-        qa[rp][2 * e + 1] = act ? (_Float16)bf16hi(ws[e]) : (_Float16)0.f;
+        qa[rp][2 * e] = act ? (_Float16)(bf16lo(ws[e]) * qsc) : (_Float16)0.f;
+        qa[rp][2 * e + 1] = act ? (_Float16)(bf16hi(ws[e]) * qsc) : (_Float16)0.f;
       }
     }
   }
-  const float sscale = a.qscale * ldexpf(1.f, shk);
+  const float sscale = a.qscale * ldexpf(1.f, shk + shq);
 
   // row-role state: online softmax of row rho and O^T[16b + 4grp + e][rho]
   float Mr = -INFINITY, Lr = 0.f;

@@ -20,8 +20,9 @@
 //     stride of three 16-byte slots.  The gathers are random, so they meet
 //     bank conflicts whatever the stride (about 60% of the LDS-active time on
 //     the 0.5-bit workload).  Both codebooks are rescaled by powers of two on
-//     load (keys to fit fp16, values below 2^kHVLim); the scales are folded
-//     back later.
+//     load (keys to fit fp16, values below 2^kHVLim), with the bf16 sinks and
+//     recent rows counted in their ranges; the queries get a power-of-two
+//     scale of their own.  The scales are folded back into scores and outputs.
 //   * Rotation on packed fp16 pairs, scores as v_dot2_f32_f16 sums in fp32,
 //     the four lanes of a token reduce with DPP inside a quad, online softmax
 //     in base 2 whose running maximum may lag by kHLag, and P*V in packed
@@ -43,12 +44,6 @@ __device__ __forceinline__ uint32_t pack_hh2(float a, float b) {
   return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
 }
 
-__device__ __forceinline__ int pow2_shift_h(float max_abs, int lim) {
-  if (!(max_abs > 0.f)) return 0;
-  const int e = ilogbf(max_abs) + 1;    // max_abs < 2^e
-  return e > lim ? e - lim : 0;
-}
-
 // fp16 partial sums of P*V: weights <= 2^kHLag, |v| <= 2^kHVLim, kHFlush tokens
 // per lane between flushes keep a partial below 2^(3+7+4) = 16384.
 constexpr int kHFlush = 16, kHLag = 3, kHVLim = 7;
@@ -65,7 +60,7 @@ __device__ __forceinline__ uint32_t cw_addr(uint32_t w) {
 template <int HS>
 __device__ __forceinline__ void decode_half_body(const DecodeArgs& a, const uint4* s_k, const uint4* s_v,
                                                  float (*s_red)[2][130], int b, int hq, int h, int beta, int split,
-                                                 int shk, int shv) {
+                                                 int shk, int shv, int shq) {
   constexpr int D = 128, HD = 64, TC = 4, C = 4, CPT = D / C;
   constexpr int NW = kDecodeThreads / kWave, SPW = 16;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -77,6 +72,7 @@ __device__ __forceinline__ void decode_half_body(const DecodeArgs& a, const uint
   // queries: steps 2HS + ml; chunk pair k (chunk 4g + k and its partner), channel pair ip
   const int t_lo = max(a.step0, beta * TC), t_hi = min(a.step0 + a.n_steps, (beta + 1) * TC);
   uint32_t qv[2][4][2][2];
+  const float qsc = ldexpf(1.f, -shq);
 #pragma unroll
   for (int ml = 0; ml < 2; ++ml) {
     const int t = beta * TC + 2 * HS + ml;
@@ -89,10 +85,10 @@ __device__ __forceinline__ void decode_half_body(const DecodeArgs& a, const uint
 #pragma unroll
         for (int ip = 0; ip < 2; ++ip) {
           const uint32_t w = *reinterpret_cast<const uint32_t*>(qr + p * HD + 16 * g + 4 * k + 2 * ip);
-          qv[ml][k][p][ip] = act ? pack_hh2(bf16lo(w), bf16hi(w)) : 0u;
+          qv[ml][k][p][ip] = act ? pack_hh2(bf16lo(w) * qsc, bf16hi(w) * qsc) : 0u;
         }
   }
-  const float sscale = a.qscale * ldexpf(1.f, shk);
+  const float sscale = a.qscale * ldexpf(1.f, shk + shq);
 
   float mrow[2] = {-INFINITY, -INFINITY}, lrow[2] = {0.f, 0.f};
   float acc[2][4][2][4];
@@ -334,7 +330,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_half_kernel(DecodeArgs 
   __shared__ __attribute__((aligned(16))) uint4 s_k[256 * kCWS];
   __shared__ __attribute__((aligned(16))) uint4 s_v[256 * kCWS];
   __shared__ float s_red[NW][2][D + 2];
-  __shared__ float s_amax[2][NW];
+  __shared__ float s_amax[3][NW];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int split = blockIdx.x;
@@ -342,12 +338,14 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_half_kernel(DecodeArgs 
   const int h = hq / a.gqa;
   const int b = blockIdx.z / a.n_blk_serv;
   const int beta = a.blk0 + (blockIdx.z - b * a.n_blk_serv);
+  const int t_lo = max(a.step0, beta * TC), t_hi = min(a.step0 + a.n_steps, (beta + 1) * TC);
 
   // ---- codebooks -> LDS (fp16, step-major halves), power-of-two range scaling
   const int64_t cbo = ((int64_t)h * a.n_blk + beta) * a.K * G;
   const int r = tid;   // one row per thread
   float kx[G], vx[G];
-  float mk = 0.f, mv = 0.f;
+  float mq, mk, mv;   // the bf16 sinks and recent rows share the codebooks' scales
+  decode_input_absmax(a, b, hq, 1, h, t_lo, t_hi, split == 0, nullptr, mq, mk, mv);
   if (r < a.K) {
     const uint4* pk = reinterpret_cast<const uint4*>(a.kcb + cbo + r * G);
     const uint4* pv = reinterpret_cast<const uint4*>(a.vcb + cbo + r * G);
@@ -373,17 +371,20 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_half_kernel(DecodeArgs 
     for (int u = 0; u < G; ++u) kx[u] = vx[u] = 0.f;
   }
   for (int off = 32; off >= 1; off >>= 1) {
+    mq = fmaxf(mq, __shfl_xor(mq, off));
     mk = fmaxf(mk, __shfl_xor(mk, off));
     mv = fmaxf(mv, __shfl_xor(mv, off));
   }
   if (lane == 0) {
     s_amax[0][wave] = mk;
     s_amax[1][wave] = mv;
+    s_amax[2][wave] = mq;
   }
   __syncthreads();
   mk = fmaxf(fmaxf(s_amax[0][0], s_amax[0][1]), fmaxf(s_amax[0][2], s_amax[0][3]));
   mv = fmaxf(fmaxf(s_amax[1][0], s_amax[1][1]), fmaxf(s_amax[1][2], s_amax[1][3]));
-  const int shk = pow2_shift_h(mk, 14), shv = pow2_shift_h(mv, kHVLim);
+  mq = fmaxf(fmaxf(s_amax[2][0], s_amax[2][1]), fmaxf(s_amax[2][2], s_amax[2][3]));
+  const int shk = pow2_range_shift(mk, 14), shv = pow2_range_shift(mv, kHVLim), shq = pow2_range_shift(mq, 14);
   {
     const float sk = ldexpf(1.f, -shk), sv = ldexpf(1.f, -shv);
     uint32_t kw[8], vw[8];   // [m][pair]: step m, channels (2*pair, 2*pair+1)
@@ -404,14 +405,13 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_half_kernel(DecodeArgs 
   __syncthreads();
 
   if (wave >> 1)
-    decode_half_body<1>(a, s_k, s_v, s_red, b, hq, h, beta, split, shk, shv);
+    decode_half_body<1>(a, s_k, s_v, s_red, b, hq, h, beta, split, shk, shv, shq);
   else
-    decode_half_body<0>(a, s_k, s_v, s_red, b, hq, h, beta, split, shk, shv);
+    decode_half_body<0>(a, s_k, s_v, s_red, b, hq, h, beta, split, shk, shv, shq);
   __syncthreads();
 
   // ---- merge the two waves of each step half
   const float osc = ldexpf(1.f, shv);
-  const int t_lo = max(a.step0, beta * TC), t_hi = min(a.step0 + a.n_steps, (beta + 1) * TC);
   for (int x = tid; x < TC * D; x += kDecodeThreads) {
     const int m = x / D, d = x - m * D;
     const int t = beta * TC + m;

@@ -58,12 +58,6 @@ __device__ __forceinline__ uint32_t pack_h2t(float a, float b) {
   return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
 }
 
-__device__ __forceinline__ int pow2_shift_t(float max_abs, int lim) {
-  if (!(max_abs > 0.f)) return 0;
-  const int e = ilogbf(max_abs) + 1;
-  return e > lim ? e - lim : 0;
-}
-
 constexpr int kTFlush = 16, kTLag = 3, kTVLim = 7;
 // Fourth word of a raw buffer descriptor (32-bit data, no format conversion).
 constexpr int kBufWord3 = 0x00020000;
@@ -95,7 +89,7 @@ __global__ __launch_bounds__(kDecodeThreads, C == 4 ? 3 : 2) void decode_tasq_ke
   __shared__ __attribute__((aligned(16))) float4 s_buf[kAccQ * kDecodeThreads];
   static_assert(NW * TC * (D + 2) <= kAccQ * kDecodeThreads * 4 && TPI * HD * 2 <= kAccQ * kDecodeThreads * 4,
                 "offset table and merge buffer fit the region");
-  __shared__ float s_amax[2][NW];
+  __shared__ float s_amax[3][NW];
   __shared__ uint32_t s_row[NW][HD];   // (cos, sin) fp16 pairs of the iteration's table row
   float (*s_red)[TC][D + 2] = reinterpret_cast<float (*)[TC][D + 2]>(s_buf);
   float2* s_off = reinterpret_cast<float2*>(s_buf);
@@ -110,12 +104,19 @@ __global__ __launch_bounds__(kDecodeThreads, C == 4 ? 3 : 2) void decode_tasq_ke
   const int h = hq / a.gqa;
   const int b = blockIdx.z / a.n_blk_serv;
   const int beta = a.blk0 + (blockIdx.z - b * a.n_blk_serv);
+  const int t_lo = max(a.step0, beta * TC), t_hi = min(a.step0 + a.n_steps, (beta + 1) * TC);
 
-  // ---- codebooks -> LDS (fp16, step-major), power-of-two range scaling
+  // ---- codebooks -> LDS (fp16, step-major), power-of-two range scaling; the
+  // bf16 sink and recent keys enter the transformed space times w, so their
+  // range counts with that factor.  The effective-query coefficients satisfy
+  // |A_o|, |B_o| <= |a| + |b| <= 2 max_d |q_d| / min(w_d, w_(d^D/2)), the
+  // bound that sets their power-of-two scale.
   const int64_t cbo = ((int64_t)h * a.n_blk + beta) * a.K * G;
   const int r = tid;
   float kx[G], vx[G];
-  float mk = 0.f, mv = 0.f;
+  float mq, mk, mv;
+  decode_input_absmax(a, b, hq, 1, h, t_lo, t_hi, split == 0, a.w + h * D, mq, mk, mv);
+  mq *= 2.f;
   if (r < a.K) {
     const uint4* pk = reinterpret_cast<const uint4*>(a.kcb + cbo + r * G);
     const uint4* pv = reinterpret_cast<const uint4*>(a.vcb + cbo + r * G);
@@ -141,12 +142,14 @@ __global__ __launch_bounds__(kDecodeThreads, C == 4 ? 3 : 2) void decode_tasq_ke
     for (int u = 0; u < G; ++u) kx[u] = vx[u] = 0.f;
   }
   for (int off = 32; off >= 1; off >>= 1) {
+    mq = fmaxf(mq, __shfl_xor(mq, off));
     mk = fmaxf(mk, __shfl_xor(mk, off));
     mv = fmaxf(mv, __shfl_xor(mv, off));
   }
   if (lane == 0) {
     s_amax[0][wave] = mk;
     s_amax[1][wave] = mv;
+    s_amax[2][wave] = mq;
   }
   // offset angles o * w_f, w_f = theta^(-2f/D), in fp32
   {
@@ -162,7 +165,8 @@ __global__ __launch_bounds__(kDecodeThreads, C == 4 ? 3 : 2) void decode_tasq_ke
   __syncthreads();
   mk = fmaxf(fmaxf(s_amax[0][0], s_amax[0][1]), fmaxf(s_amax[0][2], s_amax[0][3]));
   mv = fmaxf(fmaxf(s_amax[1][0], s_amax[1][1]), fmaxf(s_amax[1][2], s_amax[1][3]));
-  const int shk = pow2_shift_t(mk, 14), shv = pow2_shift_t(mv, kTVLim);
+  mq = fmaxf(fmaxf(s_amax[2][0], s_amax[2][1]), fmaxf(s_amax[2][2], s_amax[2][3]));
+  const int shk = pow2_range_shift(mk, 14), shv = pow2_range_shift(mv, kTVLim), shq = pow2_range_shift(mq, 14);
   {
     const float sk = ldexpf(1.f, -shk), sv = ldexpf(1.f, -shv);
     uint32_t kw[2 * C], vw[2 * C];   // [m][pair]
@@ -182,9 +186,9 @@ __global__ __launch_bounds__(kDecodeThreads, C == 4 ? 3 : 2) void decode_tasq_ke
 
   // ---- effective-query coefficients A_o, B_o of this lane's channels
   // d' = 16g + j for steps 2hs + ml, and the LDS words of their frequencies
-  // in the wave's table row.
-  const int t_lo = max(a.step0, beta * TC), t_hi = min(a.step0 + a.n_steps, (beta + 1) * TC);
+  // in the wave's table row.  They enter fp16 times 2^-shq.
   uint32_t A2[2][NPR], B2[2][NPR];
+  const float qsc = ldexpf(1.f, -shq);
   const uint32_t* rw_addr[NCH];
   {
     int och[NCH];
@@ -209,8 +213,8 @@ __global__ __launch_bounds__(kDecodeThreads, C == 4 ? 3 : 2) void decode_tasq_ke
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           const int j = 2 * p + u, o = och[j];
-          const float qo = bf16_to_f32(qr[o]);
-          const float qp = bf16_to_f32(qr[o ^ HD]);
+          const float qo = bf16_to_f32(qr[o]) * qsc;
+          const float qp = bf16_to_f32(qr[o ^ HD]) * qsc;
           const float aa = qo * rw[j];
           const float bb = (o < HD ? qp : -qp) * rw[j];
           av[u] = act ? aa * oc[j].x + bb * oc[j].y : 0.f;
@@ -221,7 +225,7 @@ __global__ __launch_bounds__(kDecodeThreads, C == 4 ? 3 : 2) void decode_tasq_ke
       }
     }
   }
-  const float sscale = a.qscale * ldexpf(1.f, shk);
+  const float sscale = a.qscale * ldexpf(1.f, shk + shq);
 
   float mrow[2] = {-INFINITY, -INFINITY}, lrow[2] = {0.f, 0.f};
   uint32_t acc16[2][NPR];

@@ -50,6 +50,54 @@ struct DecodeArgs {
   int32_t n_pos;              // positions in the RoPE table
 };
 
+// Largest |value| a decode workgroup converts to fp16 besides its codebooks:
+// the queries of q-heads [hq0, hq0 + nh) at steps [t_lo, t_hi) (mq; when kw
+// is given, channel d counts divided by min(kw[d], kw[d ^ D/2])) and, for
+// the split that attends them (with_bf16), the bf16 sink and recent-window
+// keys (mk; channel d multiplied by kw[d] when kw is given) and values (mv)
+// of kv-head h at those steps.  Each thread of the workgroup scans a strided
+// share; the caller reduces across the workgroup.  The kernels turn these
+// into power-of-two range scales (folded back into the scores and outputs),
+// so any finite input stays finite in fp16.
+__device__ inline void decode_input_absmax(const DecodeArgs& a, int b, int hq0, int nh, int h, int t_lo, int t_hi,
+                                           bool with_bf16, const float* kw, float& mq, float& mk, float& mv) {
+  constexpr int D = 128;
+  const int ns = t_hi - t_lo;
+  mq = mk = mv = 0.f;
+  if (ns <= 0) return;
+  const int nq = nh * ns * D;
+  for (int e = threadIdx.x; e < nq; e += blockDim.x) {
+    const int d = e % D, r = e / D, tl = r % ns, hh = r / ns;
+    const uint16_t x = a.q[(((int64_t)b * a.Hq + hq0 + hh) * a.n_steps + (t_lo + tl - a.step0)) * D + d];
+    const float v = fabsf(__uint_as_float((uint32_t)x << 16));
+    mq = fmaxf(mq, kw ? v / fminf(kw[d], kw[d ^ (D / 2)]) : v);
+  }
+  if (!with_bf16) return;
+  const int nsk = a.n_s * ns * D;
+  for (int e = threadIdx.x; e < nsk; e += blockDim.x) {
+    const int d = e % D, r = e / D, s = r % a.n_s, tl = r / a.n_s;
+    const int64_t o = ((((int64_t)b * a.H + h) * a.T + t_lo + tl) * a.n_s + s) * D + d;
+    mk = fmaxf(mk, fabsf(__uint_as_float((uint32_t)a.sk[o] << 16)) * (kw ? kw[d] : 1.f));
+    mv = fmaxf(mv, fabsf(__uint_as_float((uint32_t)a.sv[o] << 16)));
+  }
+  const int nr = a.n_r * ns * D;
+  for (int e = threadIdx.x; e < nr; e += blockDim.x) {
+    const int d = e % D, r = e / D, s = r % a.n_r, tl = r / a.n_r;
+    const int64_t o = ((((int64_t)b * a.H + h) * a.T + t_lo + tl) * a.r_cap + s) * D + d;
+    mk = fmaxf(mk, fabsf(__uint_as_float((uint32_t)a.rk[o] << 16)) * (kw ? kw[d] : 1.f));
+    mv = fmaxf(mv, fabsf(__uint_as_float((uint32_t)a.rv[o] << 16)));
+  }
+}
+
+// Power-of-two range scale of the fp16 decode kernels: the shift s with
+// 2^-s * m in [2^(lim-1), 2^lim) for the largest magnitude m of a set of
+// values (down or up, up by at most 2^64; 0 for m = 0).  The values enter
+// fp16 times 2^-s and 2^s is folded back into the fp32 scores or outputs.
+__device__ inline int pow2_range_shift(float m, int lim) {
+  if (!(m > 0.f)) return 0;
+  return max(ilogbf(m) + 1 - lim, -64);
+}
+
 struct TasqStatsArgs {
   const uint16_t* x;          // bf16 rows of D (raw pre-RoPE keys), strides in elements
   int64_t xs0, xs1, xs2, xs3;

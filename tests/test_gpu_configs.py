@@ -1,8 +1,14 @@
 """GPU parity at the five workloads' full sizes, in the launch configuration
 the benchmark times, checked against the fp64 oracle on sampled slices:
 seeded (batch, kv-head) encode slices over first, last and random tokens, and
-seeded decode rows over the whole context (sinks included), for the fused call
-over all steps and, on workloads 2 and 3, for a per-step call."""
+seeded decode rows over the whole context (sinks included): 64 (batch, q-head)
+pairs x all 4 steps on workload 2, 32 x 4 on workload 3, 16 x all 32 steps
+(every block) on workload 4, 16 x 4 on two layers of workload 5, for the
+fused call and for a per-step call; and small-batch, full-context calls whose
+plans split the context (the log-sum-exp merge at full length)."""
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 import torch
@@ -20,7 +26,27 @@ def _token_sample(N, rng, n=256):
     return toks
 
 
-def _run_config(idx, n_enc=3, n_rows=8, layer=0):
+def _pairs(cfg, rng, n):
+    """n distinct seeded (batch, q-head) pairs, always including the first and last."""
+    allp = [(b, hq) for b in range(cfg.B) for hq in range(cfg.H_q)]
+    pick = rng.choice(len(allp), size=min(n, len(allp)), replace=False)
+    ps = {allp[i] for i in pick}
+    ps.update({(0, 0), (cfg.B - 1, cfg.H_q - 1)})
+    return sorted(ps)
+
+
+def _check_rows_parallel(cfg, inp, kidx, vidx, sigma, out, lse, rows, step0=0, N=None):
+    """_check_rows over many rows, several rows at a time (the oracle's NumPy
+    work releases the interpreter lock)."""
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    chunks = [rows[i::workers] for i in range(workers)]
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        res = list(ex.map(lambda r: _check_rows(cfg, inp, kidx, vidx, sigma, out, lse, r, step0=step0, N=N)
+                          if r else 0.0, chunks))
+    return max(res)
+
+
+def _run_config(idx, n_enc=3, n_rows=8, layer=0, n_pairs=None):
     s = _lib()
     cfg = config_by_index(idx)
     rng = np.random.default_rng(1000 + idx)
@@ -38,21 +64,25 @@ def _run_config(idx, n_enc=3, n_rows=8, layer=0):
         _say("  encode b%d h%d K exact/tie/fail %s V %s" % (b, h, rk, rv))
         fails += rk[2] + rv[2]
     assert fails == 0
-    rows = [(int(rng.integers(cfg.B)), int(rng.integers(cfg.H_q)), int(rng.integers(cfg.T))) for _ in range(n_rows)]
-    rows += [(0, 0, 0), (cfg.B - 1, cfg.H_q - 1, cfg.T - 1)]
-    worst = _check_rows(cfg, inp, kidx, vidx, sigma, out, lse, rows, N=cfg.N)
+    if n_pairs is None:
+        rows = [(int(rng.integers(cfg.B)), int(rng.integers(cfg.H_q)), int(rng.integers(cfg.T)))
+                for _ in range(n_rows)]
+        rows += [(0, 0, 0), (cfg.B - 1, cfg.H_q - 1, cfg.T - 1)]
+    else:
+        rows = [(b, hq, t) for (b, hq) in _pairs(cfg, rng, n_pairs) for t in range(cfg.T)]
+    worst = _check_rows_parallel(cfg, inp, kidx, vidx, sigma, out, lse, rows, N=cfg.N)
     _say("  decode worst rel err %.3g over %d rows (tolerance %g)" % (worst, len(rows), OUT_TOL))
     return s, cfg, inp, kidx, vidx, sigma, pt
 
 
-def _per_step_call(s, cfg, inp, kidx, vidx, sigma, pt, t, seed, n_rows=6):
+def _per_step_call(s, cfg, inp, kidx, vidx, sigma, pt, t, seed, n_pairs=16):
     """One decode call for loop step t alone (n_steps = 1), the per-step use."""
     out, lse = _decode(s, cfg, inp, kidx, vidx, pt, N=cfg.N, step0=t, n_steps=1)
     torch.cuda.synchronize()
     rng = np.random.default_rng(seed)
-    rows = [(int(rng.integers(cfg.B)), int(rng.integers(cfg.H_q)), t) for _ in range(n_rows)]
-    worst = _check_rows(cfg, inp, kidx, vidx, sigma, out, lse, rows, step0=t, N=cfg.N)
-    _say("  per-step call (step %d): decode worst rel err %.3g" % (t, worst))
+    rows = [(b, hq, t) for (b, hq) in _pairs(cfg, rng, n_pairs)]
+    worst = _check_rows_parallel(cfg, inp, kidx, vidx, sigma, out, lse, rows, step0=t, N=cfg.N)
+    _say("  per-step call (step %d): decode worst rel err %.3g over %d rows" % (t, worst, len(rows)))
 
 
 def test_config1_full():
@@ -60,22 +90,46 @@ def test_config1_full():
 
 
 def test_config2_full():
-    s, cfg, inp, kidx, vidx, sigma, pt = _run_config(2)
+    s, cfg, inp, kidx, vidx, sigma, pt = _run_config(2, n_pairs=64)
     _per_step_call(s, cfg, inp, kidx, vidx, sigma, pt, 1, 2002)
 
 
 def test_config3_full():
-    s, cfg, inp, kidx, vidx, sigma, pt = _run_config(3)
+    s, cfg, inp, kidx, vidx, sigma, pt = _run_config(3, n_pairs=32)
     _per_step_call(s, cfg, inp, kidx, vidx, sigma, pt, 2, 3003)
 
 
 def test_config4_full():
-    _run_config(4, n_rows=12)
+    # 16 (batch, q-head) pairs x all 32 steps: every block's codebook
+    s, cfg, inp, kidx, vidx, sigma, pt = _run_config(4, n_pairs=16)
+    _per_step_call(s, cfg, inp, kidx, vidx, sigma, pt, 13, 4004)
+
+
+@pytest.mark.parametrize("idx", [2, 3])
+def test_full_context_small_batch_splits(idx):
+    """Two batch entries at the workload's full context: few workgroups, so the
+    plan splits the context and the log-sum-exp merge runs at full length."""
+    import dataclasses
+    s = _lib()
+    cfg = dataclasses.replace(config_by_index(idx), B=2)
+    g = _geom(s, cfg)
+    n_split = s.decode_workspace_bytes(g, cfg.B, cfg.N, 0, cfg.T) // (cfg.B * cfg.H_q * cfg.T * (cfg.D + 1) * 4)
+    _say("config %d, batch 2: %d context splits" % (idx, n_split))
+    assert n_split > 1
+    inp = build_inputs(cfg, 0, "cuda")
+    kidx, vidx, sigma, pt = _encode_all(s, cfg, inp)
+    out, lse = _decode(s, cfg, inp, kidx, vidx, pt, N=cfg.N)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5000 + idx)
+    rows = [(b, hq, t) for (b, hq) in _pairs(cfg, rng, 8) for t in range(cfg.T)]
+    worst = _check_rows_parallel(cfg, inp, kidx, vidx, sigma, out, lse, rows, N=cfg.N)
+    _say("  decode worst rel err %.3g over %d rows" % (worst, len(rows)))
 
 
 @pytest.mark.parametrize("layer", [0, 23])
 def test_config5_layer_with_page_encode(layer):
-    s, cfg, inp, kidx, vidx, sigma, pt = _run_config(5, n_enc=2, n_rows=6, layer=layer)
+    s, cfg, inp, kidx, vidx, sigma, pt = _run_config(5, n_enc=2, layer=layer, n_pairs=16)
+    _per_step_call(s, cfg, inp, kidx, vidx, sigma, pt, 2, 5005 + layer, n_pairs=8)
     # one decode-time page event: 8 more tokens appended at token N
     from synth.generator import gen_kv_layer
     g = _geom(s, cfg)
