@@ -25,11 +25,14 @@
 //     e[d'](P + o) = A_o[d'] cos(P w_f) + B_o[d'] sin(P w_f),
 //     A_o = a cos(o w_f) + b sin(o w_f),   B_o = b cos(o w_f) - a sin(o w_f),
 // so the per-lane coefficients A_o, B_o are formed once (fp32 angles of
-// o w_f), and per iteration lane f of each wave loads the table entry
-// (cos P w_f, sin P w_f) of frequency f and stores it as word f of the wave's
-// 64-word LDS row; every lane then reads the entries of its 16 channels'
-// frequencies from that row.  The row spans the 64 LDS banks once, so these
-// reads never conflict (lanes reading one word share it).
+// o w_f).  A lane's 16 transformed channels form 8 channel pairs, and the 8
+// lane groups of a token hold 64 pairs in all, so per iteration lane
+// 8p + g of each wave loads the table entries (cos P w_f, sin P w_f) of the
+// two frequencies of pair p of group g and stores them as one 8-byte entry
+// (cos pair, sin pair) of the wave's LDS table; every lane then reads its 8
+// pairs' entries, already packed for the fp16 pair arithmetic.  Both the
+// store and each read cover consecutive entries, so neither meets a bank
+// conflict (lanes reading one entry share it).
 //
 // Layout choices:
 //   * Codebooks in LDS as fp16, step-major inside a codeword, first half
@@ -61,8 +64,6 @@ __device__ __forceinline__ uint32_t pack_h2t(float a, float b) {
 constexpr int kTFlush = 16, kTLag = 3, kTVLim = 7;
 // Fourth word of a raw buffer descriptor (32-bit data, no format conversion).
 constexpr int kBufWord3 = 0x00020000;
-constexpr uint32_t kSelLo = 0x05040100u;   // v_perm: low halves of (src1, src0)
-constexpr uint32_t kSelHi = 0x07060302u;   // v_perm: high halves of (src1, src0)
 
 }  // namespace
 
@@ -76,7 +77,7 @@ __global__ __launch_bounds__(kDecodeThreads, C == 4 ? 3 : 2) void decode_tasq_ke
   constexpr int NCK = CPT / 8;        // chunks per lane (4 or 2)
   constexpr int NCH = NCK * C;        // transformed channels per lane (16)
   constexpr int NPR = NCH / 2;        // channel pairs per lane (8)
-  static_assert(TPI == 16 && HD == kWave, "one table frequency per lane");
+  static_assert(TPI == 16 && NPR * 8 == kWave, "one channel pair of the table per lane");
   __shared__ __attribute__((aligned(16))) uint4 s_k[256 * 2 * QW];
   __shared__ __attribute__((aligned(16))) uint4 s_v[256 * 2 * QW];
   // One region, three uses in turn: (cos, sin) of o * w_f for o < TPI, f < HD
@@ -90,7 +91,9 @@ __global__ __launch_bounds__(kDecodeThreads, C == 4 ? 3 : 2) void decode_tasq_ke
   static_assert(NW * TC * (D + 2) <= kAccQ * kDecodeThreads * 4 && TPI * HD * 2 <= kAccQ * kDecodeThreads * 4,
                 "offset table and merge buffer fit the region");
   __shared__ float s_amax[3][NW];
-  __shared__ uint32_t s_row[NW][HD];   // (cos, sin) fp16 pairs of the iteration's table row
+  // (cos, sin) of the iteration's position for every channel pair: entry
+  // 8p + g holds pair p of lane group g, as (cos of both, sin of both) fp16
+  __shared__ uint2 s_pair[NW][NPR * 8];
   float (*s_red)[TC][D + 2] = reinterpret_cast<float (*)[TC][D + 2]>(s_buf);
   float2* s_off = reinterpret_cast<float2*>(s_buf);
   float4* s_acc = s_buf + threadIdx.x;   // this lane's sums: s_acc[q * kDecodeThreads]
@@ -185,11 +188,9 @@ __global__ __launch_bounds__(kDecodeThreads, C == 4 ? 3 : 2) void decode_tasq_ke
   }
 
   // ---- effective-query coefficients A_o, B_o of this lane's channels
-  // d' = 16g + j for steps 2hs + ml, and the LDS words of their frequencies
-  // in the wave's table row.  They enter fp16 times 2^-shq.
+  // d' = 16g + j for steps 2hs + ml.  They enter fp16 times 2^-shq.
   uint32_t A2[2][NPR], B2[2][NPR];
   const float qsc = ldexpf(1.f, -shq);
-  const uint32_t* rw_addr[NCH];
   {
     int och[NCH];
     float rw[NCH];
@@ -199,7 +200,6 @@ __global__ __launch_bounds__(kDecodeThreads, C == 4 ? 3 : 2) void decode_tasq_ke
       const int o = a.perm[h * D + NCH * g + j] & (D - 1);   // stays in bounds for any input
       och[j] = o;
       rw[j] = 1.f / a.w[h * D + o];
-      rw_addr[j] = &s_row[wave][o & (HD - 1)];
       oc[j] = s_off[my * HD + (o & (HD - 1))];
     }
 #pragma unroll
@@ -254,39 +254,56 @@ __global__ __launch_bounds__(kDecodeThreads, C == 4 ? 3 : 2) void decode_tasq_ke
   // offset past the described range reads 0 instead of faulting.
   const __amdgpu_buffer_rsrc_t rope_rs =
       __builtin_amdgcn_make_buffer_rsrc((void*)a.rope, 0, a.n_pos * D * 2, kBufWord3);
-  const int rope_lane = ((lane >> 2) * 8 + (lane & 3)) * 2;
-  // (cos, sin) of frequency `lane` at position P, from the fp16 quad table
+  // byte offsets in a table row of the cosines of the two frequencies of
+  // the channel pair this lane loads (pair lane / 8 of group lane % 8); each
+  // sine sits 8 bytes after its cosine
+  int rope_a, rope_b;
+  {
+    const int pg = lane & 7, pp = lane >> 3;
+    const int fa = a.perm[h * D + NCH * pg + 2 * pp] & (HD - 1);
+    const int fb = a.perm[h * D + NCH * pg + 2 * pp + 1] & (HD - 1);
+    rope_a = ((fa >> 2) * 8 + (fa & 3)) * 2;
+    rope_b = ((fb >> 2) * 8 + (fb & 3)) * 2;
+  }
+  // (cos pair, sin pair) of this lane's channel pair at position P
   auto load_row = [&](int P) {
-    const uint32_t c = __builtin_amdgcn_raw_buffer_load_b16(rope_rs, rope_lane, P * (D * 2), 0);
-    const uint32_t sn = __builtin_amdgcn_raw_buffer_load_b16(rope_rs, rope_lane + 8, P * (D * 2), 0);
-    return c | (sn << 16);
+    const uint32_t ca = __builtin_amdgcn_raw_buffer_load_b16(rope_rs, rope_a, P * (D * 2), 0);
+    const uint32_t cb = __builtin_amdgcn_raw_buffer_load_b16(rope_rs, rope_b, P * (D * 2), 0);
+    const uint32_t sa = __builtin_amdgcn_raw_buffer_load_b16(rope_rs, rope_a + 8, P * (D * 2), 0);
+    const uint32_t sb = __builtin_amdgcn_raw_buffer_load_b16(rope_rs, rope_b + 8, P * (D * 2), 0);
+    return make_uint2(ca | (cb << 16), sa | (sb << 16));
   };
   // Scores of the lane's two steps (summed over the 8 lanes of the token's
   // step half); Kw[k][ml*DW + ip] = channel pair (2ip, 2ip+1) of chunk k.
   // The row is written and read by this wave only; LDS instructions of one
   // wave execute in order, so the words read are this iteration's and the
   // next write follows these reads.
-  auto scores = [&](uint32_t row, const uint32_t (&Kw)[NCK][C], const float (&sg)[2], float (&sc)[2]) {
+  auto scores = [&](uint2 row, const uint32_t (&Kw)[NCK][C], const float (&sg)[2], float (&sc)[2]) {
     uint32_t cs2[NPR], sn2[NPR];
-    s_row[wave][lane] = row;
+    s_pair[wave][lane] = row;
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int p = 0; p < NPR; ++p) {
-      const uint32_t d0 = *rw_addr[2 * p];
-      const uint32_t d1 = *rw_addr[2 * p + 1];
-      cs2[p] = __builtin_amdgcn_perm(d1, d0, kSelLo);
-      sn2[p] = __builtin_amdgcn_perm(d1, d0, kSelHi);
+      const uint2 e = s_pair[wave][8 * p + g];
+      cs2[p] = e.x;
+      sn2[p] = e.y;
+    }
+    // four independent chains (two steps x even/odd pairs) keep the
+    // dependent pk_mul -> pk_fma -> dot2 sequences overlapped
+    float part[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+#pragma unroll
+    for (int p = 0; p < NPR; ++p) {
+      h2t_t e2[2];
+#pragma unroll
+      for (int ml = 0; ml < 2; ++ml) e2[ml] = as_h2t(A2[ml][p]) * as_h2t(cs2[p]);
+#pragma unroll
+      for (int ml = 0; ml < 2; ++ml) e2[ml] = as_h2t(B2[ml][p]) * as_h2t(sn2[p]) + e2[ml];
+#pragma unroll
+      for (int ml = 0; ml < 2; ++ml)
+        part[ml][p & 1] = __builtin_amdgcn_fdot2(e2[ml], as_h2t(Kw[p / DW][ml * DW + p % DW]), part[ml][p & 1], false);
     }
 #pragma unroll
-    for (int ml = 0; ml < 2; ++ml) {
-      float part = 0.f;
-#pragma unroll
-      for (int p = 0; p < NPR; ++p) {
-        const h2t_t e2 = as_h2t(A2[ml][p]) * as_h2t(cs2[p]) + as_h2t(B2[ml][p]) * as_h2t(sn2[p]);
-        part = __builtin_amdgcn_fdot2(e2, as_h2t(Kw[p / DW][ml * DW + p % DW]), part, false);
-      }
-      sc[ml] = group_sum<8>(part) * sg[ml] * sscale;
-    }
+    for (int ml = 0; ml < 2; ++ml) sc[ml] = group_sum<8>(part[ml][0] + part[ml][1]) * sg[ml] * sscale;
   };
   // fp16 partial sums into the fp32 sums in LDS (channel pairs 2p, 2p+1 of
   // step ml are float4 (ml * NCH + 2p) / 4, components 2p % 4, +1)
@@ -345,7 +362,7 @@ __global__ __launch_bounds__(kDecodeThreads, C == 4 ? 3 : 2) void decode_tasq_ke
       const int it = base + my;
       const bool valid = it < count;
       const int itc = valid ? it : 0;
-      const uint32_t row = load_row(P0 + base);
+      const uint2 row = load_row(P0 + base);
       uint32_t Kw[NCK][C], Vw[NCK][C];
 #pragma unroll
       for (int ml = 0; ml < 2; ++ml) {
@@ -395,7 +412,8 @@ __global__ __launch_bounds__(kDecodeThreads, C == 4 ? 3 : 2) void decode_tasq_ke
       (void*)(a.sigma + (int64_t)b * a.sig_cap * a.T), 0, a.sig_cap * a.T * 2, kBufWord3);
   const int idx_lane = (tok_lo + my) * CPT + 4 * kwo;
   const int sig_lane = ((tok_lo + my) * a.T + beta * TC + 2 * hs) * 2;
-  uint32_t kwn = 0, vwn = 0, sgn = 0, rown = 0;
+  uint32_t kwn = 0, vwn = 0, sgn = 0;
+  uint2 rown = make_uint2(0u, 0u);
   auto load_next = [&](int base) {
     kwn = __builtin_amdgcn_raw_buffer_load_b32(kid_rs, idx_lane, base * CPT, 0);
     vwn = __builtin_amdgcn_raw_buffer_load_b32(vid_rs, idx_lane, base * CPT, 0);
@@ -406,7 +424,8 @@ __global__ __launch_bounds__(kDecodeThreads, C == 4 ? 3 : 2) void decode_tasq_ke
   int since_flush = 0;
   for (int base = 0; base < n_tok; base += TPI) {
     const bool valid = base + my < n_tok;
-    const uint32_t kwc = kwn, vwc = vwn, sgc = sgn, row = rown;
+    const uint32_t kwc = kwn, vwc = vwn, sgc = sgn;
+    const uint2 row = rown;
     load_next(base + TPI);
     uint32_t Kw[NCK][C], Vw[NCK][C];
 #pragma unroll
