@@ -273,13 +273,10 @@ __global__ __launch_bounds__(kDecodeThreads, C == 4 ? 3 : 2) void decode_tasq_ke
     const uint32_t sb = __builtin_amdgcn_raw_buffer_load_b16(rope_rs, rope_b + 8, P * (D * 2), 0);
     return make_uint2(ca | (cb << 16), sa | (sb << 16));
   };
-  // Scores of the lane's two steps (summed over the 8 lanes of the token's
-  // step half); Kw[k][ml*DW + ip] = channel pair (2ip, 2ip+1) of chunk k.
-  // The row is written and read by this wave only; LDS instructions of one
-  // wave execute in order, so the words read are this iteration's and the
-  // next write follows these reads.
-  auto scores = [&](uint2 row, const uint32_t (&Kw)[NCK][C], const float (&sg)[2], float (&sc)[2]) {
-    uint32_t cs2[NPR], sn2[NPR];
+  // The wave's pair table for one position: written and read by this wave
+  // only; LDS instructions of one wave execute in order, so the entries read
+  // are this iteration's and the next write follows these reads.
+  auto pair_table = [&](uint2 row, uint32_t (&cs2)[NPR], uint32_t (&sn2)[NPR]) {
     s_pair[wave][lane] = row;
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
@@ -288,6 +285,11 @@ __global__ __launch_bounds__(kDecodeThreads, C == 4 ? 3 : 2) void decode_tasq_ke
       cs2[p] = e.x;
       sn2[p] = e.y;
     }
+  };
+  // Scores of the lane's two steps (summed over the 8 lanes of the token's
+  // step half); Kw[k][ml*DW + ip] = channel pair (2ip, 2ip+1) of chunk k.
+  auto scores = [&](const uint32_t (&cs2)[NPR], const uint32_t (&sn2)[NPR], const uint32_t (&Kw)[NCK][C],
+                    const float (&sg)[2], float (&sc)[2]) {
     // four independent chains (two steps x even/odd pairs) keep the
     // dependent pk_mul -> pk_fma -> dot2 sequences overlapped
     float part[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
@@ -362,7 +364,8 @@ __global__ __launch_bounds__(kDecodeThreads, C == 4 ? 3 : 2) void decode_tasq_ke
       const int it = base + my;
       const bool valid = it < count;
       const int itc = valid ? it : 0;
-      const uint2 row = load_row(P0 + base);
+      uint32_t cs2[NPR], sn2[NPR];
+      pair_table(load_row(P0 + base), cs2, sn2);
       uint32_t Kw[NCK][C], Vw[NCK][C];
 #pragma unroll
       for (int ml = 0; ml < 2; ++ml) {
@@ -386,7 +389,7 @@ __global__ __launch_bounds__(kDecodeThreads, C == 4 ? 3 : 2) void decode_tasq_ke
       }
       const float sg[2] = {1.f, 1.f};
       float sc[2];
-      scores(row, Kw, sg, sc);
+      scores(cs2, sn2, Kw, sg, sc);
       accumulate(sc, Vw, valid);
       flush();
     }
@@ -427,23 +430,34 @@ __global__ __launch_bounds__(kDecodeThreads, C == 4 ? 3 : 2) void decode_tasq_ke
     const uint32_t kwc = kwn, vwc = vwn, sgc = sgn;
     const uint2 row = rown;
     load_next(base + TPI);
+    // LDS order: the pair table, then the K gathers, then the V gathers, so
+    // the scores can start while the V gathers are in flight
+    uint32_t cs2[NPR], sn2[NPR];
+    pair_table(row, cs2, sn2);
     uint32_t Kw[NCK][C], Vw[NCK][C];
 #pragma unroll
     for (int k = 0; k < NCK; ++k) {
       const uint32_t ik = __builtin_amdgcn_ubfe(kwc, kbit + 8 * k, 8);
-      const uint32_t iv = __builtin_amdgcn_ubfe(vwc, kbit + 8 * k, 8);
 #pragma unroll
       for (int u = 0; u < QW; ++u) {
         const uint4 x = s_k[(2 * ik + hs) * QW + u];
-        const uint4 y = s_v[(2 * iv + hs) * QW + u];
         Kw[k][4 * u] = x.x; Kw[k][4 * u + 1] = x.y; Kw[k][4 * u + 2] = x.z; Kw[k][4 * u + 3] = x.w;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < NCK; ++k) {
+      const uint32_t iv = __builtin_amdgcn_ubfe(vwc, kbit + 8 * k, 8);
+#pragma unroll
+      for (int u = 0; u < QW; ++u) {
+        const uint4 y = s_v[(2 * iv + hs) * QW + u];
         Vw[k][4 * u] = y.x; Vw[k][4 * u + 1] = y.y; Vw[k][4 * u + 2] = y.z; Vw[k][4 * u + 3] = y.w;
       }
     }
+    __builtin_amdgcn_sched_barrier(0);   // keep every gather issued ahead of the arithmetic
     const h2t_t s16 = as_h2t(sgc);
     const float sg[2] = {(float)s16.x, (float)s16.y};
     float sc[2];
-    scores(row, Kw, sg, sc);
+    scores(cs2, sn2, Kw, sg, sc);
     accumulate(sc, Vw, valid);
     if (++since_flush == kTFlush) {
       flush();
