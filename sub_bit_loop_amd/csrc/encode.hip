@@ -14,11 +14,12 @@
 //     s_r = ||e_r||^2 + u - 2 z.e_r    (u ~ ||z||^2, common to all r)
 // for 32 codewords per tile: a v_mfma_f32_32x32x8 for the norm terms and a
 // v_mfma_f32_32x32x16_bf16 for the products (codewords on M, codes on N).
-// At G = 16 (plain inputs) each lane reduces every four consecutive
-// codewords to their smallest screened value and keys only that value (group
-// number in the low mantissa byte); the winning group is scored again in
-// fp32 after the screening.  Otherwise every screened value gets a key
-// (candidate number in the low byte).  Best and second-best keys cost one
+// At G = 16 each lane reduces every four consecutive codewords to their
+// smallest screened value and keys only that value (group number in the low
+// mantissa byte); the winning group is scored again in fp32 after the
+// screening.  At G = 32 every screened value gets a key (candidate number in
+// the low byte).  Pre-transformed keys enter the products as two bf16 terms
+// (hi + lo) of their fp32 value.  Best and second-best keys cost one
 // min3, one med3 and one min per two keys.  A code whose two best values lie
 // within the fp32 error band is re-scored exactly in fp64 (direct form,
 // lowest index on ties), so the written index is the exact argmin.
@@ -79,10 +80,10 @@ __global__ __launch_bounds__(kEncodeThreads, (G == 16 && !TASQ) ? 4 : 1) void en
   constexpr int CW = C < 8 ? C : 8;  // contiguous channels per load
   constexpr int NL = 8 / CW;         // loads per 8-position slot
   static_assert(C >= 2 && (CPT & (CPT - 1)) == 0, "unsupported code shape");
-  // Selection per group of four candidates (plain inputs, G = 16) or per
-  // candidate.  At G = 32 the matrix cores take 1.5x longer per group of
-  // codes and the per-candidate form measured faster.
-  constexpr bool kGroups = !TASQ && G == 16;
+  // Selection per group of four candidates (G = 16) or per candidate.  At
+  // G = 32 the matrix cores take 1.5x longer per group of codes and the
+  // per-candidate form measured faster.
+  constexpr bool kGroups = G == 16;
   // Per codebook row: -2*e in step-major order (G bf16) and the norm row
   // [nh, nm, nl, 1] (||e||^2 split into three bf16 terms).  With group
   // selection, rows are stored in blocks of four with 16 bytes of padding
@@ -237,50 +238,60 @@ __global__ __launch_bounds__(kEncodeThreads, (G == 16 && !TASQ) ? 4 : 1) void en
   // Pre-transformed keys, in two parts so that the loads of the next group
   // are in flight while the current one is screened: the raw bf16 bits of
   // k[p(d)] and the fp16 bits of sigma for each joint position of the lane,
-  // then z = w[p(d)] * k[p(d)] / sigma split into three bf16 terms (the
-  // residuals are exact in fp32, the sum is within 2^-24 |z|; the band below
-  // covers the split, near ties are re-scored from the inputs in fp64).
+  // then z = w[p(d)] * k[p(d)] / sigma split into two bf16 terms hi + lo
+  // (the residual is exact in fp32, the sum is within 2^-16 |z|; the band
+  // below covers the split, near ties are re-scored from the inputs in
+  // fp64).  Sigma is read once per step of the lane's positions and its
+  // reciprocal taken once.
   auto raw_channel = [&](int kk, int e, int q) {
     if constexpr (CPT <= 32) return tof[kk][e];
     // c = 2: the lane's chunk changes between groups
     return ph[q * C + ((16 * kk + 8 * hh + e) % C)] & (D - 1);
   };
-  auto fetch_raw = [&](int grp, uint32_t (&rk)[KK][8], uint32_t (&rs)[KK][8]) {
+  // positions 16kk + 8hh + e of slot kk cover NS steps: step
+  // (16kk + 8hh) / C + e / CW
+  constexpr int NS = 8 / CW;
+  auto fetch_raw = [&](int grp, uint32_t (&rk)[KK][8], uint32_t (&rs)[KK][NS]) {
     int jl, q;
     code_pos(grp, jl, q);
     const uint16_t* xr = xbase + (int64_t)jl * xs3;
     const uint16_t* sg = sgb + (int64_t)jl * a.T;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
+    for (int kk = 0; kk < KK; ++kk) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int m = (16 * kk + 8 * hh) / C + (C <= 8 ? e / C : 0);   // step of position 16kk + 8hh + e
+        const int m = (16 * kk + 8 * hh) / C + e / CW;   // step of position 16kk + 8hh + e
         rk[kk][e] = xr[m * xs2 + raw_channel(kk, e, q)];
-        rs[kk][e] = sg[m];
       }
+#pragma unroll
+      for (int l = 0; l < NS; ++l) rs[kk][l] = sg[(16 * kk + 8 * hh) / C + l];
+    }
   };
-  auto transform = [&](int grp, const uint32_t (&rk)[KK][8], const uint32_t (&rs)[KK][8], bf16x8_t (&zh)[KK],
-                       bf16x8_t (&zl)[KK], bf16x8_t (&zl2)[KK], float& zz) {
+  auto transform = [&](int grp, const uint32_t (&rk)[KK][8], const uint32_t (&rs)[KK][NS], bf16x8_t (&zh)[KK],
+                       bf16x8_t (&zl)[KK], float& zz) {
     int jl, q;
     code_pos(grp, jl, q);
     zz = 0.f;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
+    for (int kk = 0; kk < KK; ++kk) {
+      float rsg[NS];
+#pragma unroll
+      for (int l = 0; l < NS; ++l) {
+        _Float16 sh;
+        const uint16_t sb = (uint16_t)rs[kk][l];
+        __builtin_memcpy(&sh, &sb, 2);
+        rsg[l] = __builtin_amdgcn_rcpf((float)sh);
+      }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float wv = CPT <= 32 ? twt[kk][e] : wh[raw_channel(kk, e, q)];
-        _Float16 sh;
-        const uint16_t sb = (uint16_t)rs[kk][e];
-        __builtin_memcpy(&sh, &sb, 2);
-        const float zf = (wv * bf16_to_f32(rk[kk][e])) * __builtin_amdgcn_rcpf((float)sh);
+        const float zf = (wv * bf16_to_f32(rk[kk][e])) * rsg[e / CW];
         const __bf16 z1 = (__bf16)zf;
-        const float r1 = zf - (float)z1;
-        const __bf16 z2 = (__bf16)r1;
         zz = fmaf(zf, zf, zz);
         zh[kk][e] = z1;
-        zl[kk][e] = z2;
-        zl2[kk][e] = (__bf16)(r1 - (float)z2);
+        zl[kk][e] = (__bf16)(zf - (float)z1);
       }
+    }
   };
 
   // Lane constants of the norm product's B operand (zero in the second
@@ -294,17 +305,17 @@ __global__ __launch_bounds__(kEncodeThreads, (G == 16 && !TASQ) ? 4 : 1) void en
   // workgroup) still loads the last group, so every load is of a real row.
   constexpr int WS = kEncodeThreads / kWave;
   bf16x8_t bz[KK];
-  uint32_t brk[TASQ ? KK : 1][8], brs[TASQ ? KK : 1][8];
+  uint32_t brk[TASQ ? KK : 1][8], brs[TASQ ? KK : 1][NS];
   const int grp_first = min(wave, ngroups - 1);   // ngroups >= 1: every workgroup has a token
   if constexpr (TASQ)
     fetch_raw(grp_first, brk, brs);
   else
     fetch(grp_first, bz);
   for (int grp = wave; grp < ngroups; grp += WS) {
-    bf16x8_t cz[KK], czlo[KK], czlo2[KK];
+    bf16x8_t cz[KK], czlo[KK];
     float zz = 0.f;
     if constexpr (TASQ) {
-      transform(grp, brk, brs, cz, czlo, czlo2, zz);
+      transform(grp, brk, brs, cz, czlo, zz);
       fetch_raw(min(grp + WS, ngroups - 1), brk, brs);
     } else {
 #pragma unroll
@@ -354,7 +365,6 @@ __global__ __launch_bounds__(kEncodeThreads, (G == 16 && !TASQ) ? 4 : 1) void en
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[t][kk], cz[kk], acc, 0, 0, 0);
         if constexpr (TASQ) {
           acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[t][kk], czlo[kk], acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[t][kk], czlo2[kk], acc, 0, 0, 0);
         }
       }
       return acc;
@@ -422,15 +432,16 @@ __global__ __launch_bounds__(kEncodeThreads, (G == 16 && !TASQ) ? 4 : 1) void en
     // With Tb = 1.0625 t1 + ||z||^2 / 64 and nb = 2 (||z||^2 + Tb):
     //   eps = kErr (nb + 1.02 ||z||^2),
     //   thr = t1 (1 + 2^-14) + 2 eps  =  kA t1 + kB ||z||^2.
-    // Pre-transformed keys: the MFMA sums 4 + 3G products (three split
-    // terms), so kErr triples; and the split sum differs from the exact
-    // transformed value by < 2^-21 |z| (2^-24 from the split, ~2^-22 from
+    // Pre-transformed keys: the MFMA sums 4 + 2G products (two split
+    // terms), within 2 kErr; and the split sum differs from the exact
+    // transformed value by < kSplit |z| (2^-16 from the split, ~2^-22 from
     // the fp32 product with the reciprocal of sigma), which moves a screened
-    // value by < 2^-21 (||z||^2 + nb):
-    //   eps = 3 kErr (nb + 1.02 ||z||^2) + 2^-21 (||z||^2 + nb).
+    // value by < kSplit (||z||^2 + nb):
+    //   eps = 2 kErr (nb + 1.02 ||z||^2) + kSplit (||z||^2 + nb).
     constexpr float kErr = (float)(2 * G + 16) * 0x1p-24f;
-    constexpr float kA = TASQ ? 1.f + 0x1p-14f + 12.75f * kErr + 4.25f * 0x1p-21f : 1.f + 0x1p-14f + 4.25f * kErr;
-    constexpr float kB = TASQ ? 18.31f * kErr + 6.07f * 0x1p-21f : 6.11f * kErr;
+    constexpr float kSplit = 0x1.08p-16f;
+    constexpr float kA = TASQ ? 1.f + 0x1p-14f + 8.5f * kErr + 4.25f * kSplit : 1.f + 0x1p-14f + 4.25f * kErr;
+    constexpr float kB = TASQ ? 12.22f * kErr + 6.07f * kSplit : 6.11f * kErr;
     const float thr = fmaf(kA, t1, kB * zz);
     bool tie;
     int res;
@@ -441,7 +452,8 @@ __global__ __launch_bounds__(kEncodeThreads, (G == 16 && !TASQ) ? 4 : 1) void en
     } else {
       // The winning group (codewords r0 .. r0+3) scored again in fp32: each
       // half-wave sums its eight positions per kk (the first half starting
-      // from ||e||^2), the halves are added.  At most G + 2 roundings, each
+      // from ||e||^2; pre-transformed keys add both split terms), the halves
+      // are added.  At most G + 2 roundings (2G + 2 with two terms), each
       // within 2^-24 * 2 (||e||^2 + u), so these values obey the screened
       // values' error bound; they lack the margin u, so they are compared
       // with thr - u (one more rounding, within 2^-24 thr, inside the band's
@@ -466,6 +478,13 @@ __global__ __launch_bounds__(kEncodeThreads, (G == 16 && !TASQ) ? 4 : 1) void en
           part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, z.y), __builtin_bit_cast(bf16x2_t, w.y), part, false);
           part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, z.z), __builtin_bit_cast(bf16x2_t, w.z), part, false);
           part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, z.w), __builtin_bit_cast(bf16x2_t, w.w), part, false);
+          if constexpr (TASQ) {
+            const uint4 zl = __builtin_bit_cast(uint4, czlo[kk]);
+            part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, zl.x), __builtin_bit_cast(bf16x2_t, w.x), part, false);
+            part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, zl.y), __builtin_bit_cast(bf16x2_t, w.y), part, false);
+            part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, zl.z), __builtin_bit_cast(bf16x2_t, w.z), part, false);
+            part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, zl.w), __builtin_bit_cast(bf16x2_t, w.w), part, false);
+          }
         }
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
         d[c] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
