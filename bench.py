@@ -194,12 +194,15 @@ def onchip_ceilings(torch):
         ops = blocks * 256 * iters * 16
         out["valu_mode%d" % mode] = {"instruction": name, "lane_ops_per_clk_per_CU": ops / t / n_cu / clk,
                                      "TFLOPs": ops * flop / t / 1e12}
-    mfma = {0: ("v_mfma_f32_16x16x32_bf16", 16384), 1: ("v_mfma_f32_32x32x16_bf16", 32768)}
+    mfma = {0: ("v_mfma_f32_16x16x32_bf16", 16384), 1: ("v_mfma_f32_32x32x16_bf16", 32768),
+            2: ("v_mfma_f32_32x32x8_bf16", 16384)}
     for mode, (name, flop) in mfma.items():
         iters = 8192
         t = run(2, mode, blocks, iters)
+        per_simd = blocks * 4 * iters * 4 / (n_cu * 4)   # wave instructions issued per SIMD
         out["mfma_mode%d" % mode] = {"instruction": name,
-                                     "TFLOPs": blocks * 4 * iters * 4 * flop / t / 1e12}
+                                     "TFLOPs": blocks * 4 * iters * 4 * flop / t / 1e12,
+                                     "clk_per_instruction_per_SIMD": t * clk / per_simd}
     return out
 
 

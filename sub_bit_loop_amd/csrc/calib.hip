@@ -173,12 +173,29 @@ __global__ __launch_bounds__(256) void calib_mfma_kernel(uint32_t* __restrict__ 
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int e = 0; e < 4; ++e) res ^= __float_as_uint(acc[j][e]);
-  } else {
+  } else if constexpr (MODE == 1) {
     typedef float f16_t __attribute__((ext_vector_type(16)));
     f16_t acc[4] = {};
     for (int it = 0; it < iters; ++it)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[j], 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) res ^= __float_as_uint(acc[j][e]);
+  } else {
+    // the 32x32x8 bf16 product (four bf16 per lane) the encode uses for its
+    // norm terms
+    typedef float f16_t __attribute__((ext_vector_type(16)));
+    typedef short s4_t __attribute__((ext_vector_type(4)));
+    const s4_t a4 = {__builtin_bit_cast(short, a[0]), __builtin_bit_cast(short, a[1]), __builtin_bit_cast(short, a[2]),
+                     __builtin_bit_cast(short, a[3])};
+    const s4_t b4 = {__builtin_bit_cast(short, b[0]), __builtin_bit_cast(short, b[1]), __builtin_bit_cast(short, b[2]),
+                     __builtin_bit_cast(short, b[3])};
+    f16_t acc[4] = {};
+    for (int it = 0; it < iters; ++it)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(a4, b4, acc[j], 0, 0, 0);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -254,6 +271,7 @@ int loopvq_calib_onchip(int kind, int mode, int blocks, int iters, uint32_t* sin
     switch (mode) {
       case 0: hipLaunchKernelGGL(calib_mfma_kernel<0>, g, t, 0, st, sink, iters); break;
       case 1: hipLaunchKernelGGL(calib_mfma_kernel<1>, g, t, 0, st, sink, iters); break;
+      case 2: hipLaunchKernelGGL(calib_mfma_kernel<2>, g, t, 0, st, sink, iters); break;
       default: return -1;
     }
   } else {

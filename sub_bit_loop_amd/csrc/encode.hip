@@ -102,6 +102,13 @@ __global__ __launch_bounds__(kEncodeThreads, (G == 16 && !TASQ) ? 4 : 1) void en
   // screening loop, one code per wave at a time.
   __shared__ uint16_t s_tq[kEncodeTokens * CPT];
   __shared__ int s_tqn;
+  // Pre-transformed keys with CPT <= 32: the rows of a group's tokens (all
+  // T_c steps of its 32 / CPT tokens, 64 G bytes) are read with 16-byte loads
+  // (G / 16 per lane) into the wave's staging area, and every lane picks its
+  // positions' raw channels from there.
+  constexpr bool kStaged = TASQ && CPT <= 32;
+  constexpr int kStageU4 = 4 * G;    // uint4 per wave
+  __shared__ __attribute__((aligned(16))) uint4 s_stage[kStaged ? (kEncodeThreads / kWave) * kStageU4 : 1];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -192,17 +199,19 @@ __global__ __launch_bounds__(kEncodeThreads, (G == 16 && !TASQ) ? 4 : 1) void en
 
   // Pre-transformed keys: this lane's code is always chunk n mod CPT of its
   // token, so the raw channel p(d) and weight w[p(d)] of each of its joint
-  // positions are lane constants.
+  // positions are lane constants; tof holds the element's place in the
+  // staging area (row (token in group) * T_c + step, then the raw channel).
   int tof[TASQ ? KK : 1][8];
   float twt[TASQ ? KK : 1][8];
-  if constexpr (TASQ && CPT <= 32) {
+  if constexpr (kStaged) {
+    const int tk = CPT < 32 ? (n >> LOG_CPT) : 0;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int p = 16 * kk + 8 * hh + e;
         const int o = ph[(n & (CPT - 1)) * C + (p % C)] & (D - 1);
-        tof[kk][e] = o;
+        tof[kk][e] = (tk * TC + p / C) * D + o;
         twt[kk][e] = wh[o];
       }
   }
@@ -237,20 +246,51 @@ __global__ __launch_bounds__(kEncodeThreads, (G == 16 && !TASQ) ? 4 : 1) void en
   };
   // Pre-transformed keys, in two parts so that the loads of the next group
   // are in flight while the current one is screened: the raw bf16 bits of
-  // k[p(d)] and the fp16 bits of sigma for each joint position of the lane,
+  // k[p(d)] (through the staging area when CPT <= 32, else one 2-byte load
+  // per position) and the fp16 bits of sigma for each joint position of the lane,
   // then z = w[p(d)] * k[p(d)] / sigma split into two bf16 terms hi + lo
   // (the residual is exact in fp32, the sum is within 2^-16 |z|; the band
   // below covers the split, near ties are re-scored from the inputs in
   // fp64).  Sigma is read once per step of the lane's positions and its
   // reciprocal taken once.
-  auto raw_channel = [&](int kk, int e, int q) {
-    if constexpr (CPT <= 32) return tof[kk][e];
-    // c = 2: the lane's chunk changes between groups
-    return ph[q * C + ((16 * kk + 8 * hh + e) % C)] & (D - 1);
-  };
+  // raw channel of position 16kk + 8hh + e of chunk q (c = 2, where the
+  // lane's chunk changes between groups and the rows are not staged)
+  auto raw_channel = [&](int kk, int e, int q) { return ph[q * C + ((16 * kk + 8 * hh + e) % C)] & (D - 1); };
   // positions 16kk + 8hh + e of slot kk cover NS steps: step
   // (16kk + 8hh) / C + e / CW
   constexpr int NS = 8 / CW;
+  // staged form: 16-byte chunk lane + 64u of the group's rows (row = token
+  // in group * T_c + step, 16 chunks of 8 channels per row) and sigma
+  uint4 stg[kStaged ? KK : 1];
+  auto fetch_stage = [&](int grp, uint32_t (&rs)[KK][NS]) {
+    int jl, q;
+    code_pos(grp, jl, q);
+    const int jl0 = (grp * 32) >> LOG_CPT;
+#pragma unroll
+    for (int u = 0; u < KK; ++u) {
+      const int c = lane + 64 * u, r = c >> 4;
+      const int tok = min(jl0 + r / TC, ntok - 1);
+      stg[u] = *reinterpret_cast<const uint4*>(xbase + (int64_t)tok * xs3 + (int64_t)(r % TC) * xs2 + 8 * (c & 15));
+    }
+    const uint16_t* sg = sgb + (int64_t)jl * a.T;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+      for (int l = 0; l < NS; ++l) rs[kk][l] = sg[(16 * kk + 8 * hh) / C + l];
+  };
+  // the staged rows through this wave's LDS area into the lane's raw key
+  // elements (LDS instructions of one wave execute in order, so the reads
+  // see this group's rows and the next group's writes follow them)
+  auto pick_stage = [&](uint32_t (&rk)[KK][8]) {
+    uint4* st = s_stage + wave * kStageU4;
+#pragma unroll
+    for (int u = 0; u < KK; ++u) st[lane + 64 * u] = stg[u];
+    const uint16_t* sh = reinterpret_cast<const uint16_t*>(st);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) rk[kk][e] = sh[tof[kk][e]];
+  };
   auto fetch_raw = [&](int grp, uint32_t (&rk)[KK][8], uint32_t (&rs)[KK][NS]) {
     int jl, q;
     code_pos(grp, jl, q);
@@ -307,14 +347,25 @@ __global__ __launch_bounds__(kEncodeThreads, (G == 16 && !TASQ) ? 4 : 1) void en
   bf16x8_t bz[KK];
   uint32_t brk[TASQ ? KK : 1][8], brs[TASQ ? KK : 1][NS];
   const int grp_first = min(wave, ngroups - 1);   // ngroups >= 1: every workgroup has a token
-  if constexpr (TASQ)
+  if constexpr (kStaged)
+    fetch_stage(grp_first, brs);
+  else if constexpr (TASQ)
     fetch_raw(grp_first, brk, brs);
   else
     fetch(grp_first, bz);
   for (int grp = wave; grp < ngroups; grp += WS) {
     bf16x8_t cz[KK], czlo[KK];
     float zz = 0.f;
-    if constexpr (TASQ) {
+    if constexpr (kStaged) {
+      pick_stage(brk);
+      uint32_t crs[KK][NS];
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+        for (int l = 0; l < NS; ++l) crs[kk][l] = brs[kk][l];
+      fetch_stage(min(grp + WS, ngroups - 1), brs);
+      transform(grp, brk, crs, cz, czlo, zz);
+    } else if constexpr (TASQ) {
       transform(grp, brk, brs, cz, czlo, zz);
       fetch_raw(min(grp + WS, ngroups - 1), brk, brs);
     } else {
