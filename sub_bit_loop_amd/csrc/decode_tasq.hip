@@ -113,13 +113,14 @@ __global__ __launch_bounds__(kDecodeThreads, C == 4 ? 3 : 2) void decode_tasq_ke
   // bf16 sink and recent keys enter the transformed space times w, so their
   // range counts with that factor.  The effective-query coefficients satisfy
   // |A_o|, |B_o| <= |a| + |b| <= 2 max_d |q_d| / min(w_d, w_(d^D/2)), the
-  // bound that sets their power-of-two scale.
+  // bound that sets their power-of-two scale (the coefficients carry the
+  // softmax scale log2(e) / sqrt(D) as well).
   const int64_t cbo = ((int64_t)h * a.n_blk + beta) * a.K * G;
   const int r = tid;
   float kx[G], vx[G];
   float mq, mk, mv;
   decode_input_absmax(a, b, hq, 1, h, t_lo, t_hi, split == 0, a.w + h * D, mq, mk, mv);
-  mq *= 2.f;
+  mq *= 2.f * a.qscale;
   if (r < a.K) {
     const uint4* pk = reinterpret_cast<const uint4*>(a.kcb + cbo + r * G);
     const uint4* pv = reinterpret_cast<const uint4*>(a.vcb + cbo + r * G);
@@ -190,7 +191,7 @@ __global__ __launch_bounds__(kDecodeThreads, C == 4 ? 3 : 2) void decode_tasq_ke
   // ---- effective-query coefficients A_o, B_o of this lane's channels
   // d' = 16g + j for steps 2hs + ml.  They enter fp16 times 2^-shq.
   uint32_t A2[2][NPR], B2[2][NPR];
-  const float qsc = ldexpf(1.f, -shq);
+  const float qsc = a.qscale * ldexpf(1.f, -shq);
   {
     int och[NCH];
     float rw[NCH];
@@ -225,9 +226,15 @@ __global__ __launch_bounds__(kDecodeThreads, C == 4 ? 3 : 2) void decode_tasq_ke
       }
     }
   }
-  const float sscale = a.qscale * ldexpf(1.f, shk + shq);
+  // Scores are kept in units of 2^-E (E = shk + shq, the codebook and
+  // coefficient scales): r = (dot product of the fp16 operands) * sigma, and
+  // the true base-2 score is r * 2^E.  The running maximum mr is in the same
+  // units, so score minus maximum is one mixed-precision fma (sigma in fp16)
+  // and 2^E enters only the exponent.
+  const int E = shk + shq;
+  const float lagr = ldexpf((float)kTLag, -E);
 
-  float mrow[2] = {-INFINITY, -INFINITY}, lrow[2] = {0.f, 0.f};
+  float mr[2] = {-INFINITY, -INFINITY}, lrow[2] = {0.f, 0.f};
   uint32_t acc16[2][NPR];
 #pragma unroll
   for (int ml = 0; ml < 2; ++ml)
@@ -286,13 +293,14 @@ __global__ __launch_bounds__(kDecodeThreads, C == 4 ? 3 : 2) void decode_tasq_ke
       sn2[p] = e.y;
     }
   };
-  // Scores of the lane's two steps (summed over the 8 lanes of the token's
-  // step half); Kw[k][ml*DW + ip] = channel pair (2ip, 2ip+1) of chunk k.
+  // Dot products of the lane's two steps (summed over the 8 lanes of the
+  // token's step half, before sigma); Kw[k][ml*DW + ip] = channel pair
+  // (2ip, 2ip+1) of chunk k.
   auto scores = [&](const uint32_t (&cs2)[NPR], const uint32_t (&sn2)[NPR], const uint32_t (&Kw)[NCK][C],
-                    const float (&sg)[2], float (&sc)[2]) {
-    // four independent chains (two steps x even/odd pairs) keep the
-    // dependent pk_mul -> pk_fma -> dot2 sequences overlapped
-    float part[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+                    float (&sc)[2]) {
+    // the two steps' chains interleave, so the dependent pk_mul -> pk_fma
+    // -> dot2 sequences overlap
+    float part[2] = {0.f, 0.f};
 #pragma unroll
     for (int p = 0; p < NPR; ++p) {
       h2t_t e2[2];
@@ -302,10 +310,10 @@ __global__ __launch_bounds__(kDecodeThreads, C == 4 ? 3 : 2) void decode_tasq_ke
       for (int ml = 0; ml < 2; ++ml) e2[ml] = as_h2t(B2[ml][p]) * as_h2t(sn2[p]) + e2[ml];
 #pragma unroll
       for (int ml = 0; ml < 2; ++ml)
-        part[ml][p & 1] = __builtin_amdgcn_fdot2(e2[ml], as_h2t(Kw[p / DW][ml * DW + p % DW]), part[ml][p & 1], false);
+        part[ml] = __builtin_amdgcn_fdot2(e2[ml], as_h2t(Kw[p / DW][ml * DW + p % DW]), part[ml], false);
     }
 #pragma unroll
-    for (int ml = 0; ml < 2; ++ml) sc[ml] = group_sum<8>(part[ml][0] + part[ml][1]) * sg[ml] * sscale;
+    for (int ml = 0; ml < 2; ++ml) sc[ml] = group_sum<8>(part[ml]);
   };
   // fp16 partial sums into the fp32 sums in LDS (channel pairs 2p, 2p+1 of
   // step ml are float4 (ml * NCH + 2p) / 4, components 2p % 4, +1)
@@ -323,13 +331,15 @@ __global__ __launch_bounds__(kDecodeThreads, C == 4 ? 3 : 2) void decode_tasq_ke
 #pragma unroll
       for (int p = 0; p < NPR; ++p) acc16[ml][p] = 0u;
   };
-  auto accumulate = [&](const float (&sc)[2], const uint32_t (&Vw)[NCK][C], bool valid) {
+  // sg: the token's sigma for the two steps (fp16 pair)
+  auto accumulate = [&](const float (&sc)[2], h2t_t sg, const uint32_t (&Vw)[NCK][C], bool valid) {
     if (!valid) return;
 #pragma unroll
     for (int ml = 0; ml < 2; ++ml) {
-      const float s = sc[ml];
-      if (s > mrow[ml] + (float)kTLag) {
-        const float alpha = __builtin_amdgcn_exp2f(mrow[ml] - s);
+      const float sgm = (float)(ml ? sg.y : sg.x);
+      float t = fmaf(sc[ml], sgm, -mr[ml]);   // (score - running maximum) * 2^-E
+      if (t > lagr) {
+        const float alpha = __builtin_amdgcn_exp2f(__builtin_amdgcn_ldexpf(-t, E));
         const h2t_t a2 = {(_Float16)alpha, (_Float16)alpha};
         lrow[ml] *= alpha;
 #pragma unroll
@@ -343,9 +353,10 @@ __global__ __launch_bounds__(kDecodeThreads, C == 4 ? 3 : 2) void decode_tasq_ke
         }
 #pragma unroll
         for (int p = 0; p < NPR; ++p) acc16[ml][p] = __builtin_bit_cast(uint32_t, as_h2t(acc16[ml][p]) * a2);
-        mrow[ml] = s;
+        mr[ml] = sc[ml] * sgm;
+        t = 0.f;
       }
-      const float pr = __builtin_amdgcn_exp2f(s - mrow[ml]);
+      const float pr = __builtin_amdgcn_exp2f(__builtin_amdgcn_ldexpf(t, E));
       lrow[ml] += pr;
       const h2t_t p2 = {(_Float16)pr, (_Float16)pr};
 #pragma unroll
@@ -387,10 +398,10 @@ __global__ __launch_bounds__(kDecodeThreads, C == 4 ? 3 : 2) void decode_tasq_ke
           Vw[p / DW][ml * DW + p % DW] = pack_h2t(bf16lo(vv) * vsc, bf16hi(vv) * vsc);
         }
       }
-      const float sg[2] = {1.f, 1.f};
+      const h2t_t one2 = {(_Float16)1.f, (_Float16)1.f};
       float sc[2];
-      scores(cs2, sn2, Kw, sg, sc);
-      accumulate(sc, Vw, valid);
+      scores(cs2, sn2, Kw, sc);
+      accumulate(sc, one2, Vw, valid);
       flush();
     }
   };
@@ -455,10 +466,9 @@ __global__ __launch_bounds__(kDecodeThreads, C == 4 ? 3 : 2) void decode_tasq_ke
     }
     __builtin_amdgcn_sched_barrier(0);   // keep every gather issued ahead of the arithmetic
     const h2t_t s16 = as_h2t(sgc);
-    const float sg[2] = {(float)s16.x, (float)s16.y};
     float sc[2];
-    scores(cs2, sn2, Kw, sg, sc);
-    accumulate(sc, Vw, valid);
+    scores(cs2, sn2, Kw, sc);
+    accumulate(sc, s16, Vw, valid);
     if (++since_flush == kTFlush) {
       flush();
       since_flush = 0;
@@ -476,6 +486,10 @@ __global__ __launch_bounds__(kDecodeThreads, C == 4 ? 3 : 2) void decode_tasq_ke
     acc[ml][j0 + 3] = v.w;
   }
   __syncthreads();   // every lane holds its sums: the region becomes the merge buffer
+  // running maxima back to base-2 score units
+  float mrow[2];
+#pragma unroll
+  for (int ml = 0; ml < 2; ++ml) mrow[ml] = __builtin_amdgcn_ldexpf(mr[ml], E);
 
   // ---- merge the SPW slots of the wave (lanes with equal sl)
 #pragma unroll
