@@ -56,36 +56,58 @@ struct DecodeArgs {
 // the split that attends them (with_bf16), the bf16 sink and recent-window
 // keys (mk; channel d multiplied by kw[d] when kw is given) and values (mv)
 // of kv-head h at those steps.  Each thread of the workgroup scans a strided
-// share; the caller reduces across the workgroup.  The kernels turn these
+// share of 16-byte chunks; the caller reduces across the workgroup.  The kernels turn these
 // into power-of-two range scales (folded back into the scores and outputs),
 // so any finite input stays finite in fp16.
 __device__ inline void decode_input_absmax(const DecodeArgs& a, int b, int hq0, int nh, int h, int t_lo, int t_hi,
                                            bool with_bf16, const float* kw, float& mq, float& mk, float& mv) {
-  constexpr int D = 128;
+  constexpr int D = 128, CH = D / 8;   // 16-byte chunks per row (rows are 16-byte aligned)
   const int ns = t_hi - t_lo;
   mq = mk = mv = 0.f;
   if (ns <= 0) return;
-  const int nq = nh * ns * D;
-  for (int e = threadIdx.x; e < nq; e += blockDim.x) {
-    const int d = e % D, r = e / D, tl = r % ns, hh = r / ns;
-    const uint16_t x = a.q[(((int64_t)b * a.Hq + hq0 + hh) * a.n_steps + (t_lo + tl - a.step0)) * D + d];
-    const float v = fabsf(__uint_as_float((uint32_t)x << 16));
-    mq = fmaxf(mq, kw ? v / fminf(kw[d], kw[d ^ (D / 2)]) : v);
+  // largest |x| (times the channel factor f(d) when given) over the 8 bf16 of
+  // a 16-byte chunk whose first channel is d0
+  auto chunk_max = [&](const uint16_t* p, int d0, auto f) {
+    const uint4 w = *reinterpret_cast<const uint4*>(p);
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+    float m = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      m = fmaxf(m, fabsf(__uint_as_float(ws[k] << 16)) * f(d0 + 2 * k));
+      m = fmaxf(m, fabsf(__uint_as_float(ws[k] & 0xffff0000u)) * f(d0 + 2 * k + 1));
+    }
+    return m;
+  };
+  auto one = [](int) { return 1.f; };
+  // queries: rows (q-head hh, step tl)
+  for (int e = threadIdx.x; e < nh * ns * CH; e += blockDim.x) {
+    const int r = e / CH, c = e - r * CH, hh = r / ns, tl = r - hh * ns;
+    const uint16_t* row = a.q + (((int64_t)b * a.Hq + hq0 + hh) * a.n_steps + (t_lo + tl - a.step0)) * D;
+    if (kw)
+      mq = fmaxf(mq, chunk_max(row + 8 * c, 8 * c, [&](int d) { return 1.f / fminf(kw[d], kw[d ^ (D / 2)]); }));
+    else
+      mq = fmaxf(mq, chunk_max(row + 8 * c, 8 * c, one));
   }
   if (!with_bf16) return;
-  const int nsk = a.n_s * ns * D;
-  for (int e = threadIdx.x; e < nsk; e += blockDim.x) {
-    const int d = e % D, r = e / D, s = r % a.n_s, tl = r / a.n_s;
-    const int64_t o = ((((int64_t)b * a.H + h) * a.T + t_lo + tl) * a.n_s + s) * D + d;
-    mk = fmaxf(mk, fabsf(__uint_as_float((uint32_t)a.sk[o] << 16)) * (kw ? kw[d] : 1.f));
-    mv = fmaxf(mv, fabsf(__uint_as_float((uint32_t)a.sv[o] << 16)));
+  // sinks: the rows of steps t_lo .. t_hi-1 are contiguous
+  const int64_t s0 = (((int64_t)b * a.H + h) * a.T + t_lo) * a.n_s * D;
+  for (int e = threadIdx.x; e < ns * a.n_s * CH; e += blockDim.x) {
+    const int c = e % CH;
+    if (kw)
+      mk = fmaxf(mk, chunk_max(a.sk + s0 + (int64_t)e * 8, 8 * c, [&](int d) { return kw[d]; }));
+    else
+      mk = fmaxf(mk, chunk_max(a.sk + s0 + (int64_t)e * 8, 8 * c, one));
+    mv = fmaxf(mv, chunk_max(a.sv + s0 + (int64_t)e * 8, 8 * c, one));
   }
-  const int nr = a.n_r * ns * D;
-  for (int e = threadIdx.x; e < nr; e += blockDim.x) {
-    const int d = e % D, r = e / D, s = r % a.n_r, tl = r / a.n_r;
-    const int64_t o = ((((int64_t)b * a.H + h) * a.T + t_lo + tl) * a.r_cap + s) * D + d;
-    mk = fmaxf(mk, fabsf(__uint_as_float((uint32_t)a.rk[o] << 16)) * (kw ? kw[d] : 1.f));
-    mv = fmaxf(mv, fabsf(__uint_as_float((uint32_t)a.rv[o] << 16)));
+  // recent window: rows (step tl, token s < n_r) of capacity r_cap
+  for (int e = threadIdx.x; e < ns * a.n_r * CH; e += blockDim.x) {
+    const int r = e / CH, c = e - r * CH, tl = r / a.n_r, sr = r - tl * a.n_r;
+    const int64_t o = ((((int64_t)b * a.H + h) * a.T + t_lo + tl) * a.r_cap + sr) * D + 8 * c;
+    if (kw)
+      mk = fmaxf(mk, chunk_max(a.rk + o, 8 * c, [&](int d) { return kw[d]; }));
+    else
+      mk = fmaxf(mk, chunk_max(a.rk + o, 8 * c, one));
+    mv = fmaxf(mv, chunk_max(a.rv + o, 8 * c, one));
   }
 }
 
