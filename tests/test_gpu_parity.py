@@ -81,8 +81,9 @@ def _check_encode_slice(cfg, inp, kidx, vidx, sigma, b, h, toks):
     return rk, rv
 
 
-def _check_rows(cfg, inp, kidx, vidx, sigma, out, lse, rows, step0=0, N=None, seq=None, recent=None):
-    """rows: list of (b, hq, t) with t absolute step; out/lse hold steps from step0."""
+def _check_rows(cfg, inp, kidx, vidx, sigma, out, lse, rows, step0=0, N=None, seq=None, recent=None, errs=None):
+    """rows: list of (b, hq, t) with t absolute step; out/lse hold steps from step0.
+    Returns the worst row error; appends every row's error to errs when given."""
     worst = 0.0
     gqa = cfg.H_q // cfg.H_kv
     for (b, hq, t) in rows:
@@ -113,6 +114,8 @@ def _check_rows(cfg, inp, kidx, vidx, sigma, out, lse, rows, step0=0, N=None, se
                                            recent_k=rk, recent_v=rv)
         err = row_error(o_gpu, o_ref)
         worst = max(worst, err)
+        if errs is not None:
+            errs.append(err)
         assert err <= OUT_TOL, "row %s: err %.3g" % ((b, hq, t), err)
         assert abs(lse[b, hq, t - step0].item() - l_ref) < 1e-3 * max(1.0, abs(l_ref))
     return worst
