@@ -353,6 +353,31 @@ def workload5(args, torch, lv, cfg):
     torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1)
 
+    # Per-step usage on layer 0 at the final context (outside the timed flow):
+    # T calls with n_steps = 1, each re-reading the index rows; median of 20.
+    lay0 = layers[0]
+    qs = [lay0["q"][:, :, t:t + 1].contiguous() for t in range(cfg.T)]
+    outs = torch.empty((B, Hq, 1, cfg.D), dtype=torch.float32, device="cuda")
+    lses = torch.empty((B, Hq, 1), dtype=torch.float32, device="cuda")
+
+    def per_step():
+        for t in range(cfg.T):
+            lv.decode_attn(g, qs[t], lay0["kidx"], lay0["vidx"], lay0["k_cb"], lay0["v_cb"], lay0["sk"], lay0["sv"],
+                           rope, N=N, pt=lay0["pt"], step0=t, out=outs, lse=lses, workspace=ws)
+    per_step()
+    fev = [(ev(), ev()) for _ in range(20)]
+    pev = [(ev(), ev()) for _ in range(20)]
+    for (a, b), (c, d) in zip(fev, pev):
+        a.record()
+        decode_layer(lay0, N)
+        b.record()
+        c.record()
+        per_step()
+        d.record()
+    torch.cuda.synchronize()
+    fused_ms = _median_ms(fev)
+    ps_ms = _median_ms(pev)
+
     # per-layer decode calls: median over every (step, layer) call
     lay_ms = [a.elapsed_time(b) for a, b, _ in lay_ev]
     dec_med = statistics.median(lay_ms)
@@ -421,6 +446,10 @@ def workload5(args, torch, lv, cfg):
                            "codes_per_layer": codes_layer},
         "page_encode": {"events": len(page_ev),
                         "ms_per_event_all_layers_median": statistics.median(page_ms) if page_ms else None},
+        "decode_per_step": {"ms_all_steps_median": ps_ms, "calls": cfg.T, "fused_ms_median_same_context": fused_ms,
+                            "vs_fused": ps_ms / fused_ms,
+                            "note": "layer 0 at the final context: one call per loop step (n_steps = 1, the "
+                                    "one-step kernel variant), each re-reading the index rows"},
         "hbm_stream": stream,
         "onchip_ceilings": ceilings,
         "timed_s": total_ms / 1e3,

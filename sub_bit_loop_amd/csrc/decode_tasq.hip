@@ -44,7 +44,10 @@
 //   * Effective queries, scores and P*V run on packed fp16 (scores summed in
 //     fp32 by v_dot2_f32_f16); P*V partials are flushed into fp32 every
 //     kFlush tokens, with the same range bounds as the plain kernels.
-// One workgroup serves one (batch, q-head, block, context split).
+// One workgroup serves one (batch, q-head, block, context split).  A call
+// for one served step (n_steps = 1) takes the variant with one step per lane
+// (NSL = 1): lanes hs = 0 / 1 then serve two tokens instead of two steps, and
+// only the served step's slice of each codeword is read.
 #include "common.h"
 #include "kernels.h"
 
@@ -67,17 +70,22 @@ constexpr int kBufWord3 = 0x00020000;
 
 }  // namespace
 
-template <int C>
-__global__ __launch_bounds__(kDecodeThreads, C == 4 ? 3 : 2) void decode_tasq_kernel(DecodeArgs a) {
+// NSL = 2: every step of the block (lane (hs, g) takes steps 2hs, 2hs+1);
+// NSL = 1: one served step (a call with n_steps = 1): lane (hs, g) then takes
+// that step for tokens of parity hs, so the 16 lanes of a token pair serve
+// two tokens and no lane computes a step that is not served.
+template <int C, int NSL>
+__global__ __launch_bounds__(kDecodeThreads, NSL == 1 ? 4 : (C == 4 ? 3 : 2)) void decode_tasq_kernel(DecodeArgs a) {
   constexpr int D = 128, HD = 64, TC = 4, G = C * TC, CPT = D / C;
   constexpr int QW = C / 4;           // uint4 per codeword half (two steps)
   constexpr int DW = C / 2;           // dwords per step of a codeword
   constexpr int LPT = 16, SPW = kWave / LPT, NW = kDecodeThreads / kWave;
-  constexpr int TPI = NW * SPW;       // tokens per workgroup iteration
+  constexpr int TPI = NW * SPW * (3 - NSL);   // tokens per workgroup iteration (16 or 32)
   constexpr int NCK = CPT / 8;        // chunks per lane (4 or 2)
   constexpr int NCH = NCK * C;        // transformed channels per lane (16)
   constexpr int NPR = NCH / 2;        // channel pairs per lane (8)
-  static_assert(TPI == 16 && NPR * 8 == kWave, "one channel pair of the table per lane");
+  constexpr int KWD = NSL * DW;       // codeword dwords per chunk a lane reads
+  static_assert(NPR * 8 == kWave, "one channel pair of the table per lane");
   __shared__ __attribute__((aligned(16))) uint4 s_k[256 * 2 * QW];
   __shared__ __attribute__((aligned(16))) uint4 s_v[256 * 2 * QW];
   // One region, three uses in turn: (cos, sin) of o * w_f for o < TPI, f < HD
@@ -86,7 +94,7 @@ __global__ __launch_bounds__(kDecodeThreads, C == 4 ? 3 : 2) void decode_tasq_ke
   // three workgroups fit a CU: quad q of lane t at float4 q * 256 + t, which
   // consecutive lanes read without bank conflicts); the cross-wave merge of
   // the partial outputs at the end.
-  constexpr int kAccQ = 2 * NCH / 4;  // float4 sums per lane
+  constexpr int kAccQ = NSL * NCH / 4;   // float4 sums per lane
   __shared__ __attribute__((aligned(16))) float4 s_buf[kAccQ * kDecodeThreads];
   static_assert(NW * TC * (D + 2) <= kAccQ * kDecodeThreads * 4 && TPI * HD * 2 <= kAccQ * kDecodeThreads * 4,
                 "offset table and merge buffer fit the region");
@@ -101,13 +109,17 @@ __global__ __launch_bounds__(kDecodeThreads, C == 4 ? 3 : 2) void decode_tasq_ke
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int sl = lane & 15, slot = lane >> 4;
   const int hs = sl >> 3, g = sl & 7;
-  const int my = wave * SPW + slot;   // this lane's token offset o within an iteration
+  // this lane's token offset o within an iteration
+  const int my = NSL == 2 ? wave * SPW + slot : (wave * SPW + slot) * 2 + hs;
   const int split = blockIdx.x;
   const int hq = blockIdx.y;
   const int h = hq / a.gqa;
   const int b = blockIdx.z / a.n_blk_serv;
   const int beta = a.blk0 + (blockIdx.z - b * a.n_blk_serv);
   const int t_lo = max(a.step0, beta * TC), t_hi = min(a.step0 + a.n_steps, (beta + 1) * TC);
+  const int m0 = a.step0 - beta * TC;   // NSL = 1: the served step (n_steps = 1)
+  // step of the lane's slot ml
+  auto lane_step = [&](int ml) { return NSL == 2 ? 2 * hs + ml : m0; };
 
   // ---- codebooks -> LDS (fp16, step-major), power-of-two range scaling; the
   // bf16 sink and recent keys enter the transformed space times w, so their
@@ -189,8 +201,8 @@ __global__ __launch_bounds__(kDecodeThreads, C == 4 ? 3 : 2) void decode_tasq_ke
   }
 
   // ---- effective-query coefficients A_o, B_o of this lane's channels
-  // d' = 16g + j for steps 2hs + ml.  They enter fp16 times 2^-shq.
-  uint32_t A2[2][NPR], B2[2][NPR];
+  // d' = 16g + j for its steps.  They enter fp16 times 2^-shq.
+  uint32_t A2[NSL][NPR], B2[NSL][NPR];
   const float qsc = a.qscale * ldexpf(1.f, -shq);
   {
     int och[NCH];
@@ -204,8 +216,8 @@ __global__ __launch_bounds__(kDecodeThreads, C == 4 ? 3 : 2) void decode_tasq_ke
       oc[j] = s_off[my * HD + (o & (HD - 1))];
     }
 #pragma unroll
-    for (int ml = 0; ml < 2; ++ml) {
-      const int t = beta * TC + 2 * hs + ml;
+    for (int ml = 0; ml < NSL; ++ml) {
+      const int t = beta * TC + lane_step(ml);
       const bool act = t >= t_lo && t < t_hi;
       const uint16_t* qr = a.q + (((int64_t)b * a.Hq + hq) * a.n_steps + (act ? t - a.step0 : 0)) * D;
 #pragma unroll
@@ -234,12 +246,15 @@ __global__ __launch_bounds__(kDecodeThreads, C == 4 ? 3 : 2) void decode_tasq_ke
   const int E = shk + shq;
   const float lagr = ldexpf((float)kTLag, -E);
 
-  float mr[2] = {-INFINITY, -INFINITY}, lrow[2] = {0.f, 0.f};
-  uint32_t acc16[2][NPR];
+  float mr[NSL], lrow[NSL];
+  uint32_t acc16[NSL][NPR];
 #pragma unroll
-  for (int ml = 0; ml < 2; ++ml)
+  for (int ml = 0; ml < NSL; ++ml) {
+    mr[ml] = -INFINITY;
+    lrow[ml] = 0.f;
 #pragma unroll
     for (int p = 0; p < NPR; ++p) acc16[ml][p] = 0u;
+  }
   __syncthreads();   // codebooks staged; the offset table is no longer read
 #pragma unroll
   for (int q = 0; q < kAccQ; ++q) s_acc[q * kDecodeThreads] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -293,27 +308,29 @@ __global__ __launch_bounds__(kDecodeThreads, C == 4 ? 3 : 2) void decode_tasq_ke
       sn2[p] = e.y;
     }
   };
-  // Dot products of the lane's two steps (summed over the 8 lanes of the
-  // token's step half, before sigma); Kw[k][ml*DW + ip] = channel pair
-  // (2ip, 2ip+1) of chunk k.
-  auto scores = [&](const uint32_t (&cs2)[NPR], const uint32_t (&sn2)[NPR], const uint32_t (&Kw)[NCK][C],
-                    float (&sc)[2]) {
+  // Dot products of the lane's steps (summed over the 8 lanes of the
+  // token's group, before sigma); Kw[k][ml*DW + ip] = channel pair
+  // (2ip, 2ip+1) of chunk k at the lane's step ml.
+  auto scores = [&](const uint32_t (&cs2)[NPR], const uint32_t (&sn2)[NPR], const uint32_t (&Kw)[NCK][KWD],
+                    float (&sc)[NSL]) {
     // the two steps' chains interleave, so the dependent pk_mul -> pk_fma
     // -> dot2 sequences overlap
-    float part[2] = {0.f, 0.f};
+    float part[NSL];
+#pragma unroll
+    for (int ml = 0; ml < NSL; ++ml) part[ml] = 0.f;
 #pragma unroll
     for (int p = 0; p < NPR; ++p) {
-      h2t_t e2[2];
+      h2t_t e2[NSL];
 #pragma unroll
-      for (int ml = 0; ml < 2; ++ml) e2[ml] = as_h2t(A2[ml][p]) * as_h2t(cs2[p]);
+      for (int ml = 0; ml < NSL; ++ml) e2[ml] = as_h2t(A2[ml][p]) * as_h2t(cs2[p]);
 #pragma unroll
-      for (int ml = 0; ml < 2; ++ml) e2[ml] = as_h2t(B2[ml][p]) * as_h2t(sn2[p]) + e2[ml];
+      for (int ml = 0; ml < NSL; ++ml) e2[ml] = as_h2t(B2[ml][p]) * as_h2t(sn2[p]) + e2[ml];
 #pragma unroll
-      for (int ml = 0; ml < 2; ++ml)
+      for (int ml = 0; ml < NSL; ++ml)
         part[ml] = __builtin_amdgcn_fdot2(e2[ml], as_h2t(Kw[p / DW][ml * DW + p % DW]), part[ml], false);
     }
 #pragma unroll
-    for (int ml = 0; ml < 2; ++ml) sc[ml] = group_sum<8>(part[ml]);
+    for (int ml = 0; ml < NSL; ++ml) sc[ml] = group_sum<8>(part[ml]);
   };
   // fp16 partial sums into the fp32 sums in LDS (channel pairs 2p, 2p+1 of
   // step ml are float4 (ml * NCH + 2p) / 4, components 2p % 4, +1)
@@ -327,15 +344,15 @@ __global__ __launch_bounds__(kDecodeThreads, C == 4 ? 3 : 2) void decode_tasq_ke
       s_acc[q * kDecodeThreads] = v;
     }
 #pragma unroll
-    for (int ml = 0; ml < 2; ++ml)
+    for (int ml = 0; ml < NSL; ++ml)
 #pragma unroll
       for (int p = 0; p < NPR; ++p) acc16[ml][p] = 0u;
   };
-  // sg: the token's sigma for the two steps (fp16 pair)
-  auto accumulate = [&](const float (&sc)[2], h2t_t sg, const uint32_t (&Vw)[NCK][C], bool valid) {
+  // sg: the token's sigma for the lane's steps (fp16 pair; NSL = 1 uses .x)
+  auto accumulate = [&](const float (&sc)[NSL], h2t_t sg, const uint32_t (&Vw)[NCK][KWD], bool valid) {
     if (!valid) return;
 #pragma unroll
-    for (int ml = 0; ml < 2; ++ml) {
+    for (int ml = 0; ml < NSL; ++ml) {
       const float sgm = (float)(ml ? sg.y : sg.x);
       float t = fmaf(sc[ml], sgm, -mr[ml]);   // (score - running maximum) * 2^-E
       if (t > lagr) {
@@ -377,10 +394,10 @@ __global__ __launch_bounds__(kDecodeThreads, C == 4 ? 3 : 2) void decode_tasq_ke
       const int itc = valid ? it : 0;
       uint32_t cs2[NPR], sn2[NPR];
       pair_table(load_row(P0 + base), cs2, sn2);
-      uint32_t Kw[NCK][C], Vw[NCK][C];
+      uint32_t Kw[NCK][KWD], Vw[NCK][KWD];
 #pragma unroll
-      for (int ml = 0; ml < 2; ++ml) {
-        const int m = 2 * hs + ml;
+      for (int ml = 0; ml < NSL; ++ml) {
+        const int m = lane_step(ml);
         const uint16_t* kr = is_rec ? a.rk + (rec0 + (int64_t)m * a.r_cap + itc) * D
                                     : a.sk + (sink0 + (int64_t)m * a.n_s + itc) * D;
         const uint16_t* vr = is_rec ? a.rv + (rec0 + (int64_t)m * a.r_cap + itc) * D
@@ -399,7 +416,7 @@ __global__ __launch_bounds__(kDecodeThreads, C == 4 ? 3 : 2) void decode_tasq_ke
         }
       }
       const h2t_t one2 = {(_Float16)1.f, (_Float16)1.f};
-      float sc[2];
+      float sc[NSL];
       scores(cs2, sn2, Kw, sc);
       accumulate(sc, one2, Vw, valid);
       flush();
@@ -425,7 +442,8 @@ __global__ __launch_bounds__(kDecodeThreads, C == 4 ? 3 : 2) void decode_tasq_ke
   const __amdgpu_buffer_rsrc_t sig_rs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(a.sigma + (int64_t)b * a.sig_cap * a.T), 0, a.sig_cap * a.T * 2, kBufWord3);
   const int idx_lane = (tok_lo + my) * CPT + 4 * kwo;
-  const int sig_lane = ((tok_lo + my) * a.T + beta * TC + 2 * hs) * 2;
+  // sigma of the lane's steps: one 4-byte word holds an even step and the next
+  const int sig_lane = ((tok_lo + my) * a.T + beta * TC + (NSL == 2 ? 2 * hs : (m0 & ~1))) * 2;
   uint32_t kwn = 0, vwn = 0, sgn = 0;
   uint2 rown = make_uint2(0u, 0u);
   auto load_next = [&](int base) {
@@ -445,28 +463,35 @@ __global__ __launch_bounds__(kDecodeThreads, C == 4 ? 3 : 2) void decode_tasq_ke
     // the scores can start while the V gathers are in flight
     uint32_t cs2[NPR], sn2[NPR];
     pair_table(row, cs2, sn2);
-    uint32_t Kw[NCK][C], Vw[NCK][C];
+    uint32_t Kw[NCK][KWD], Vw[NCK][KWD];
+    // codeword dwords of the lane's steps: the half hs (both steps), or the
+    // served step's DW dwords inside its half
+    auto gather = [&](const uint4* cb, uint32_t idx, uint32_t (&out)[KWD]) {
+      if constexpr (NSL == 2) {
 #pragma unroll
-    for (int k = 0; k < NCK; ++k) {
-      const uint32_t ik = __builtin_amdgcn_ubfe(kwc, kbit + 8 * k, 8);
-#pragma unroll
-      for (int u = 0; u < QW; ++u) {
-        const uint4 x = s_k[(2 * ik + hs) * QW + u];
-        Kw[k][4 * u] = x.x; Kw[k][4 * u + 1] = x.y; Kw[k][4 * u + 2] = x.z; Kw[k][4 * u + 3] = x.w;
+        for (int u = 0; u < QW; ++u) {
+          const uint4 x = cb[(2 * idx + hs) * QW + u];
+          out[4 * u] = x.x; out[4 * u + 1] = x.y; out[4 * u + 2] = x.z; out[4 * u + 3] = x.w;
+        }
+      } else {
+        const uint32_t* w = reinterpret_cast<const uint32_t*>(cb + (2 * idx + (m0 >> 1)) * QW) + (m0 & 1) * DW;
+        if constexpr (DW == 2) {
+          const uint2 x = *reinterpret_cast<const uint2*>(w);
+          out[0] = x.x; out[1] = x.y;
+        } else {
+          const uint4 x = *reinterpret_cast<const uint4*>(w);
+          out[0] = x.x; out[1] = x.y; out[2] = x.z; out[3] = x.w;
+        }
       }
-    }
+    };
 #pragma unroll
-    for (int k = 0; k < NCK; ++k) {
-      const uint32_t iv = __builtin_amdgcn_ubfe(vwc, kbit + 8 * k, 8);
+    for (int k = 0; k < NCK; ++k) gather(s_k, __builtin_amdgcn_ubfe(kwc, kbit + 8 * k, 8), Kw[k]);
 #pragma unroll
-      for (int u = 0; u < QW; ++u) {
-        const uint4 y = s_v[(2 * iv + hs) * QW + u];
-        Vw[k][4 * u] = y.x; Vw[k][4 * u + 1] = y.y; Vw[k][4 * u + 2] = y.z; Vw[k][4 * u + 3] = y.w;
-      }
-    }
+    for (int k = 0; k < NCK; ++k) gather(s_v, __builtin_amdgcn_ubfe(vwc, kbit + 8 * k, 8), Vw[k]);
     __builtin_amdgcn_sched_barrier(0);   // keep every gather issued ahead of the arithmetic
-    const h2t_t s16 = as_h2t(sgc);
-    float sc[2];
+    h2t_t s16 = as_h2t(sgc);
+    if constexpr (NSL == 1) s16.x = (m0 & 1) ? s16.y : s16.x;
+    float sc[NSL];
     scores(cs2, sn2, Kw, sc);
     accumulate(sc, s16, Vw, valid);
     if (++since_flush == kTFlush) {
@@ -475,7 +500,7 @@ __global__ __launch_bounds__(kDecodeThreads, C == 4 ? 3 : 2) void decode_tasq_ke
     }
   }
   flush();
-  float acc[2][NCH];
+  float acc[NSL][NCH];
 #pragma unroll
   for (int q = 0; q < kAccQ; ++q) {
     const float4 v = s_acc[q * kDecodeThreads];
@@ -487,15 +512,16 @@ __global__ __launch_bounds__(kDecodeThreads, C == 4 ? 3 : 2) void decode_tasq_ke
   }
   __syncthreads();   // every lane holds its sums: the region becomes the merge buffer
   // running maxima back to base-2 score units
-  float mrow[2];
+  float mrow[NSL];
 #pragma unroll
-  for (int ml = 0; ml < 2; ++ml) mrow[ml] = __builtin_amdgcn_ldexpf(mr[ml], E);
+  for (int ml = 0; ml < NSL; ++ml) mrow[ml] = __builtin_amdgcn_ldexpf(mr[ml], E);
 
-  // ---- merge the SPW slots of the wave (lanes with equal sl)
+  // ---- merge the lanes of the wave that hold the same channels and steps
+  // (equal sl; with one served step, equal g)
 #pragma unroll
-  for (int off = LPT; off < kWave; off <<= 1) {
+  for (int off = NSL == 2 ? LPT : LPT / 2; off < kWave; off <<= 1) {
 #pragma unroll
-    for (int ml = 0; ml < 2; ++ml) {
+    for (int ml = 0; ml < NSL; ++ml) {
       const float om = __shfl_xor(mrow[ml], off);
       const float ol = __shfl_xor(lrow[ml], off);
       const float mm = fmaxf(mrow[ml], om);
@@ -510,10 +536,10 @@ __global__ __launch_bounds__(kDecodeThreads, C == 4 ? 3 : 2) void decode_tasq_ke
       mrow[ml] = mm;
     }
   }
-  if (slot == 0) {
+  if (NSL == 2 ? slot == 0 : (lane >> 3) == 0) {
 #pragma unroll
-    for (int ml = 0; ml < 2; ++ml) {
-      const int m = 2 * hs + ml;
+    for (int ml = 0; ml < NSL; ++ml) {
+      const int m = lane_step(ml);
 #pragma unroll
       for (int j = 0; j < NCH; ++j) s_red[wave][m][NCH * g + j] = acc[ml][j];
       if (g == 0) {
@@ -547,12 +573,17 @@ __global__ __launch_bounds__(kDecodeThreads, C == 4 ? 3 : 2) void decode_tasq_ke
   }
 }
 
-hipError_t launch_decode_tasq(int G, const DecodeArgs& a, hipStream_t s) {
+hipError_t launch_decode_tasq(int G, bool one, const DecodeArgs& a, hipStream_t s) {
   dim3 grid(a.n_split, a.Hq, a.B * a.n_blk_serv);
-  if (G == 16)
-    hipLaunchKernelGGL(decode_tasq_kernel<4>, grid, dim3(kDecodeThreads), 0, s, a);
+  if (one && a.n_steps != 1) return hipErrorInvalidValue;
+  if (G == 16 && one)
+    hipLaunchKernelGGL((decode_tasq_kernel<4, 1>), grid, dim3(kDecodeThreads), 0, s, a);
+  else if (G == 16)
+    hipLaunchKernelGGL((decode_tasq_kernel<4, 2>), grid, dim3(kDecodeThreads), 0, s, a);
+  else if (G == 32 && one)
+    hipLaunchKernelGGL((decode_tasq_kernel<8, 1>), grid, dim3(kDecodeThreads), 0, s, a);
   else if (G == 32)
-    hipLaunchKernelGGL(decode_tasq_kernel<8>, grid, dim3(kDecodeThreads), 0, s, a);
+    hipLaunchKernelGGL((decode_tasq_kernel<8, 2>), grid, dim3(kDecodeThreads), 0, s, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

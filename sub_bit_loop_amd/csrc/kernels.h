@@ -206,8 +206,10 @@ hipError_t launch_decode_step(int G, const DecodeArgs& a, hipStream_t s);
 // workgroup; grid (n_split, Hq/hpw, B x blocks)
 hipError_t launch_decode_gqa(int G, int hpw, const DecodeArgs& a, hipStream_t s);
 // T_c = 4 with the channel pre-transform (keys); one q-head per workgroup;
-// grid (n_split, Hq, B x served blocks); sigma must be 4-byte aligned.
-hipError_t launch_decode_tasq(int G, const DecodeArgs& a, hipStream_t s);
+// grid (n_split, Hq, B x served blocks); sigma must be 4-byte aligned.  one:
+// the variant for a single served step (n_steps = 1), which computes only
+// that step.
+hipError_t launch_decode_tasq(int G, bool one, const DecodeArgs& a, hipStream_t s);
 
 constexpr int kDecodeThreads = 256;
 constexpr int kEncodeThreads = 256;

@@ -86,7 +86,8 @@ DecodePlan plan_decode(const loopvq_geom* g, int B, int N, int step0, int n_step
   // single-step kernel for one served step (one workgroup per step) and
   // otherwise the multi-step kernel, which decodes each index row once for all
   // steps of its block.  Pre-transformed keys in blocks of four steps have
-  // their own kernel (one q-head per workgroup); other block lengths use the
+  // their own kernel (one q-head per workgroup; one served step takes its
+  // one-step variant); other block lengths use the
   // generic kernel, except per-step codebooks (T_c = 1) of 16 channels, which
   // have their own kernel.
   if (g->T_c == 1 && g->G == 16 && !tasq)
@@ -114,7 +115,9 @@ DecodePlan plan_decode(const loopvq_geom* g, int B, int N, int step0, int n_step
       break;
     case DecodeKernel::kTasq:
       wgs = (long long)B * g->n_q_heads * p.n_blk_serv;
-      target = g->G == 16 ? 768 : 512;     // 3 per CU at c = 4 (165 VGPRs, 49 KB LDS), else 2
+      // several steps: 3 per CU at c = 4 (166 VGPRs, 51 KB LDS), else 2; one
+      // served step: 4 per CU (at most 128 VGPRs, 35 KB LDS)
+      target = n_steps == 1 ? 1024 : (g->G == 16 ? 768 : 512);
       break;
     default:
       wgs = (long long)B * g->n_q_heads * p.n_blk_serv;
@@ -550,7 +553,7 @@ static loopvq_status decode_attn_impl(const loopvq_geom* g, const void* q, int32
   else if (p.kernel == DecodeKernel::kCq)
     e = loopvq::launch_decode_cq(a, s);
   else if (p.kernel == DecodeKernel::kTasq)
-    e = loopvq::launch_decode_tasq(g->G, a, s);
+    e = loopvq::launch_decode_tasq(g->G, n_steps == 1, a, s);
   else if (p.kernel == DecodeKernel::kGqa)
     e = loopvq::launch_decode_gqa(g->G, p.hpw, a, s);
   else if (p.kernel == DecodeKernel::kStep)

@@ -35,6 +35,8 @@ RANGE_GEOMS = [
     ("gqa4-one-step", 16, 4, 4, 1, 4, False, 1),
     ("pretransform-c4", 16, 4, 4, 1, 1, True, None),
     ("pretransform-c8", 32, 4, 4, 1, 1, True, None),
+    ("pretransform-one-step-c4", 16, 4, 4, 1, 1, True, 1),
+    ("pretransform-one-step-c8", 32, 4, 4, 1, 1, True, 1),
     ("per-step-codebooks", 16, 4, 1, 1, 1, False, None),
     ("generic-tc2", 16, 4, 2, 1, 1, False, None),
 ]
