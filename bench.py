@@ -709,6 +709,33 @@ def single_layer(args, torch, lv, cfg, steps, warmup, with_cpu, stream=None):
         torch.cuda.synchronize()
         ps_ms = _median_ms(pev)
 
+    # A bf16 recent window of 64 tokens per (batch, kv-head, step) in the same
+    # softmax (the tokens not yet converted into a page), against the call
+    # without it; the two alternate, median of 20 each.
+    n_r = 64
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(0x5EED0000 + 1000 * cfg.index + 99)
+    rk = torch.randn((cfg.B, cfg.H_kv, cfg.T, n_r, cfg.D), generator=gen, device="cuda").to(torch.bfloat16)
+    rv = torch.randn((cfg.B, cfg.H_kv, cfg.T, n_r, cfg.D), generator=gen, device="cuda").to(torch.bfloat16)
+    rope_r = lv.rope_table(cfg.n_s + cfg.N + n_r, cfg.D, cfg.theta)
+
+    def dec(recent):
+        lv.decode_attn(g, inp["q"], kidx, vidx, inp["k_cb"], inp["v_cb"], inp["sink_k"], inp["sink_v"], rope_r,
+                       out=out, lse=lse, workspace=ws, recent_k=rk if recent else None,
+                       recent_v=rv if recent else None)
+    dec(True)
+    rev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(20)]
+    for e in rev:
+        e[0].record()
+        dec(False)
+        e[1].record()
+        dec(True)
+        e[2].record()
+    torch.cuda.synchronize()
+    plain_ms = statistics.median(e[0].elapsed_time(e[1]) for e in rev)
+    rec_ms = statistics.median(e[1].elapsed_time(e[2]) for e in rev)
+    del rk, rv
+
     units = cfg.B * cfg.H_kv * cfg.N * cfg.n_blk                  # decode units per call
     codes_per_call = cfg.B * cfg.H_kv * cfg.n_blk * cfg.N * cfg.chunks
     dec_bytes = units * 2 * cfg.chunks                             # K + V index bytes per unit
@@ -755,6 +782,10 @@ def single_layer(args, torch, lv, cfg, steps, warmup, with_cpu, stream=None):
         "decode_per_step": None if ps_ms is None else {
             "ms_all_steps_median": ps_ms, "calls": cfg.T, "vs_fused": ps_ms / dec_ms,
             "note": "one call per loop step (n_steps = 1), each re-reading the index rows"},
+        "decode_recent_window": {"n_r": n_r, "ms_median": rec_ms, "ms_without_median": plain_ms,
+                                 "vs_without": rec_ms / plain_ms,
+                                 "note": "the fused call with 64 bf16 recent tokens per (batch, kv-head, step) "
+                                         "in the same softmax, alternating with the call without them"},
         "roofline": dominant,
         "roofline_decode": roof_dec,
         "roofline_encode": roof_enc,
@@ -1123,6 +1154,7 @@ def main():
         print("single-layer workload 2", file=sys.stderr, flush=True)
         r2 = single_layer(args, torch, lv, config_by_index(2), 20, 3, False)
         sub = {k: r2[k] for k in ("config", "ms_per_step", "value", "decode", "encode", "decode_per_step",
+                                  "decode_recent_window",
                                   "roofline_decode", "roofline_encode")}
     res = workload5(args, torch, lv, cfg)
     res["config2"] = sub
