@@ -58,20 +58,6 @@ __device__ __forceinline__ h4g_t lds_tr4(const void* base, uint32_t byte_off) {
       (lds_s4_t*)((__attribute__((address_space(3))) char*)(__attribute__((address_space(3))) void*)base + byte_off)));
 }
 
-// max / sum over the four 16-lane groups (lanes l, l ^ 16, l ^ 32, l ^ 48)
-__device__ __forceinline__ float group4_max(float v) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ float group4_sum(float v) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
 // Orders this wave's LDS traffic: writes before the fence are visible to the
 // wave's reads after it.
 __device__ __forceinline__ void wave_sync() {

@@ -64,6 +64,9 @@ __device__ __forceinline__ uint32_t pack_h2t(float a, float b) {
   return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
 }
 
+// P*V partial range: at most kTFlush tokens per fp16 partial, weights below
+// 2^kTLag, values below 2^kTVLim (one less where four rows' partials are
+// added before a flush), so a partial stays below 2^14 (2^15 for four rows).
 constexpr int kTFlush = 16, kTLag = 3, kTVLim = 7;
 // Fourth word of a raw buffer descriptor (32-bit data, no format conversion).
 constexpr int kBufWord3 = 0x00020000;
@@ -88,23 +91,29 @@ __global__ __launch_bounds__(kDecodeThreads, NSL == 1 ? 4 : (C == 4 ? 3 : 2)) vo
   static_assert(NPR * 8 == kWave, "one channel pair of the table per lane");
   __shared__ __attribute__((aligned(16))) uint4 s_k[256 * 2 * QW];
   __shared__ __attribute__((aligned(16))) uint4 s_v[256 * 2 * QW];
-  // One region, three uses in turn: (cos, sin) of o * w_f for o < TPI, f < HD
-  // (fp32) while the coefficients are formed; the fp32 P*V sums of every
-  // lane during the token loop (they live in LDS, not registers, so that
-  // three workgroups fit a CU: quad q of lane t at float4 q * 256 + t, which
-  // consecutive lanes read without bank conflicts); the cross-wave merge of
-  // the partial outputs at the end.
-  constexpr int kAccQ = NSL * NCH / 4;   // float4 sums per lane
-  __shared__ __attribute__((aligned(16))) float4 s_buf[kAccQ * kDecodeThreads];
-  static_assert(NW * TC * (D + 2) <= kAccQ * kDecodeThreads * 4 && TPI * HD * 2 <= kAccQ * kDecodeThreads * 4,
-                "offset table and merge buffer fit the region");
+  // fp32 P*V sums.  NSL = 2: the four tokens of a wave iteration (lanes l,
+  // l ^ 16, l ^ 32, l ^ 48, which hold the same channels and steps) share
+  // one running maximum per step, so their fp16 partials add up before a
+  // flush and the wave keeps one set of sums, s_red[wave][step][channel],
+  // which is also the wave's slot of the final merge.  NSL = 1: every lane
+  // keeps its own maximum and sums (quad q of lane t at float4
+  // q * 256 + t, which consecutive lanes read without bank conflicts).
+  // One region, used in turn for (cos, sin) of o * w_f for o < TPI, f < HD
+  // (fp32) while the coefficients are formed, the sums during the token
+  // loop, and the cross-wave merge of the partial outputs at the end.
+  constexpr bool kShared = NSL == 2;
+  constexpr int RW = D + 4;              // merge row: D sums, maximum, sum of weights, padding
+  constexpr int kAccQ = NSL * NCH / 4;   // NSL = 1: float4 sums per lane
+  constexpr int kRedQ = NW * TC * RW / 4, kOffQ = TPI * HD / 2, kLaneQ = kShared ? 0 : kAccQ * kDecodeThreads;
+  constexpr int kBufQ = kRedQ > kOffQ ? (kRedQ > kLaneQ ? kRedQ : kLaneQ) : (kOffQ > kLaneQ ? kOffQ : kLaneQ);
+  __shared__ __attribute__((aligned(16))) float4 s_buf[kBufQ];
   __shared__ float s_amax[3][NW];
   // (cos, sin) of the iteration's position for every channel pair: entry
   // 8p + g holds pair p of lane group g, as (cos of both, sin of both) fp16
   __shared__ uint2 s_pair[NW][NPR * 8];
-  float (*s_red)[TC][D + 2] = reinterpret_cast<float (*)[TC][D + 2]>(s_buf);
+  float (*s_red)[TC][RW] = reinterpret_cast<float (*)[TC][RW]>(s_buf);
   float2* s_off = reinterpret_cast<float2*>(s_buf);
-  float4* s_acc = s_buf + threadIdx.x;   // this lane's sums: s_acc[q * kDecodeThreads]
+  float4* s_acc = s_buf + threadIdx.x;   // NSL = 1: this lane's sums, s_acc[q * kDecodeThreads]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int sl = lane & 15, slot = lane >> 4;
@@ -182,7 +191,7 @@ __global__ __launch_bounds__(kDecodeThreads, NSL == 1 ? 4 : (C == 4 ? 3 : 2)) vo
   mk = fmaxf(fmaxf(s_amax[0][0], s_amax[0][1]), fmaxf(s_amax[0][2], s_amax[0][3]));
   mv = fmaxf(fmaxf(s_amax[1][0], s_amax[1][1]), fmaxf(s_amax[1][2], s_amax[1][3]));
   mq = fmaxf(fmaxf(s_amax[2][0], s_amax[2][1]), fmaxf(s_amax[2][2], s_amax[2][3]));
-  const int shk = pow2_range_shift(mk, 14), shv = pow2_range_shift(mv, kTVLim), shq = pow2_range_shift(mq, 14);
+  const int shk = pow2_range_shift(mk, 14), shv = pow2_range_shift(mv, kShared ? kTVLim - 1 : kTVLim), shq = pow2_range_shift(mq, 14);
   {
     const float sk = ldexpf(1.f, -shk), sv = ldexpf(1.f, -shv);
     uint32_t kw[2 * C], vw[2 * C];   // [m][pair]
@@ -256,8 +265,18 @@ __global__ __launch_bounds__(kDecodeThreads, NSL == 1 ? 4 : (C == 4 ? 3 : 2)) vo
     for (int p = 0; p < NPR; ++p) acc16[ml][p] = 0u;
   }
   __syncthreads();   // codebooks staged; the offset table is no longer read
+  // NSL = 2: the two float4 of the wave's sums that this lane adds into at a
+  // flush: row slot of the wave takes step 2hs + (slot >> 1), channels
+  // 16g + 8(slot & 1) .. +7 (the partials the cross-row reduction leaves
+  // in this lane)
+  float* const s_mine = &s_red[wave][2 * hs + (slot >> 1)][NCH * g + 8 * (slot & 1)];
+  if constexpr (kShared) {
+    reinterpret_cast<float4*>(s_mine)[0] = make_float4(0.f, 0.f, 0.f, 0.f);
+    reinterpret_cast<float4*>(s_mine)[1] = make_float4(0.f, 0.f, 0.f, 0.f);
+  } else {
 #pragma unroll
-  for (int q = 0; q < kAccQ; ++q) s_acc[q * kDecodeThreads] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int q = 0; q < kAccQ; ++q) s_acc[q * kDecodeThreads] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
 
   int nb = a.N;
   if (a.seq_len) nb = max(0, min(a.seq_len[b], a.N));
@@ -332,48 +351,110 @@ __global__ __launch_bounds__(kDecodeThreads, NSL == 1 ? 4 : (C == 4 ? 3 : 2)) vo
 #pragma unroll
     for (int ml = 0; ml < NSL; ++ml) sc[ml] = group_sum<8>(part[ml]);
   };
-  // fp16 partial sums into the fp32 sums in LDS (channel pairs 2p, 2p+1 of
-  // step ml are float4 (ml * NCH + 2p) / 4, components 2p % 4, +1)
+  // fp16 partial sums into the fp32 sums in LDS.  NSL = 2: the four rows'
+  // partials are first summed and scattered by two permlane swaps, after
+  // which row r holds the words of step r >> 1, pairs 4(r & 1) .. +3, and
+  // adds them into its two float4 of the wave's sums.  NSL = 1: channel
+  // pairs 2p, 2p+1 are float4 (2p) / 4 of the lane's own sums, components
+  // 2p % 4, +1.
   auto flush = [&]() {
+    if constexpr (kShared) {
+      uint32_t r1[NPR], f[NPR / 2];
 #pragma unroll
-    for (int q = 0; q < kAccQ; ++q) {
-      const int ml = q / (NCH / 4), p0 = 2 * (q % (NCH / 4));
-      float4 v = s_acc[q * kDecodeThreads];
-      add_f16x2(acc16[ml][p0], v.x, v.y);
-      add_f16x2(acc16[ml][p0 + 1], v.z, v.w);
-      s_acc[q * kDecodeThreads] = v;
+      for (int j = 0; j < NPR; ++j) {
+        const auto x = __builtin_amdgcn_permlane32_swap(acc16[0][j], acc16[1][j], false, false);
+        r1[j] = __builtin_bit_cast(uint32_t, as_h2t(x[0]) + as_h2t(x[1]));
+      }
+#pragma unroll
+      for (int j = 0; j < NPR / 2; ++j) {
+        const auto x = __builtin_amdgcn_permlane16_swap(r1[j], r1[j + NPR / 2], false, false);
+        f[j] = __builtin_bit_cast(uint32_t, as_h2t(x[0]) + as_h2t(x[1]));
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        float4 v = reinterpret_cast<float4*>(s_mine)[u];
+        add_f16x2(f[2 * u], v.x, v.y);
+        add_f16x2(f[2 * u + 1], v.z, v.w);
+        reinterpret_cast<float4*>(s_mine)[u] = v;
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < kAccQ; ++q) {
+        const int ml = q / (NCH / 4), p0 = 2 * (q % (NCH / 4));
+        float4 v = s_acc[q * kDecodeThreads];
+        add_f16x2(acc16[ml][p0], v.x, v.y);
+        add_f16x2(acc16[ml][p0 + 1], v.z, v.w);
+        s_acc[q * kDecodeThreads] = v;
+      }
     }
 #pragma unroll
     for (int ml = 0; ml < NSL; ++ml)
 #pragma unroll
       for (int p = 0; p < NPR; ++p) acc16[ml][p] = 0u;
   };
-  // sg: the token's sigma for the lane's steps (fp16 pair; NSL = 1 uses .x)
+  auto rescale = [&](float4* v, float alpha) {
+    float4 x = *v;
+    x.x *= alpha;
+    x.y *= alpha;
+    x.z *= alpha;
+    x.w *= alpha;
+    *v = x;
+  };
+  // sg: the token's sigma for the lane's steps (fp16 pair; NSL = 1 uses .x).
+  // A token whose score exceeds the running maximum by more than kTLag
+  // raises the maximum (NSL = 2: for the four rows together, in a branch the
+  // whole wave takes) and rescales every sum kept relative to it.
   auto accumulate = [&](const float (&sc)[NSL], h2t_t sg, const uint32_t (&Vw)[NCK][KWD], bool valid) {
-    if (!valid) return;
+    float t[NSL], sgm[NSL];
+    if constexpr (kShared) {
+      bool need = false;
+#pragma unroll
+      for (int ml = 0; ml < NSL; ++ml) {
+        sgm[ml] = (float)(ml ? sg.y : sg.x);
+        t[ml] = fmaf(sc[ml], sgm[ml], -mr[ml]);   // (score - running maximum) * 2^-E
+        need = need || t[ml] > lagr;
+      }
+      if (__builtin_amdgcn_ballot_w64(valid && need) != 0) {
+#pragma unroll
+        for (int ml = 0; ml < NSL; ++ml) {
+          const float nm = fmaxf(mr[ml], group4_max(valid ? sc[ml] * sgm[ml] : -INFINITY));
+          // every row holds a valid token here, so nm is finite
+          const float alpha = __builtin_amdgcn_exp2f(__builtin_amdgcn_ldexpf(mr[ml] - nm, E));
+          const h2t_t a2 = {(_Float16)alpha, (_Float16)alpha};
+          lrow[ml] *= alpha;
+#pragma unroll
+          for (int p = 0; p < NPR; ++p) acc16[ml][p] = __builtin_bit_cast(uint32_t, as_h2t(acc16[ml][p]) * a2);
+          if ((slot >> 1) == ml) {
+            rescale(reinterpret_cast<float4*>(s_mine), alpha);
+            rescale(reinterpret_cast<float4*>(s_mine) + 1, alpha);
+          }
+          mr[ml] = nm;
+          t[ml] = fmaf(sc[ml], sgm[ml], -nm);
+        }
+      }
+      if (!valid) return;
+    } else {
+      if (!valid) return;
+#pragma unroll
+      for (int ml = 0; ml < NSL; ++ml) {
+        sgm[ml] = (float)(ml ? sg.y : sg.x);
+        t[ml] = fmaf(sc[ml], sgm[ml], -mr[ml]);
+        if (t[ml] > lagr) {
+          const float alpha = __builtin_amdgcn_exp2f(__builtin_amdgcn_ldexpf(-t[ml], E));
+          const h2t_t a2 = {(_Float16)alpha, (_Float16)alpha};
+          lrow[ml] *= alpha;
+#pragma unroll
+          for (int q = ml * (NCH / 4); q < (ml + 1) * (NCH / 4); ++q) rescale(&s_acc[q * kDecodeThreads], alpha);
+#pragma unroll
+          for (int p = 0; p < NPR; ++p) acc16[ml][p] = __builtin_bit_cast(uint32_t, as_h2t(acc16[ml][p]) * a2);
+          mr[ml] = sc[ml] * sgm[ml];
+          t[ml] = 0.f;
+        }
+      }
+    }
 #pragma unroll
     for (int ml = 0; ml < NSL; ++ml) {
-      const float sgm = (float)(ml ? sg.y : sg.x);
-      float t = fmaf(sc[ml], sgm, -mr[ml]);   // (score - running maximum) * 2^-E
-      if (t > lagr) {
-        const float alpha = __builtin_amdgcn_exp2f(__builtin_amdgcn_ldexpf(-t, E));
-        const h2t_t a2 = {(_Float16)alpha, (_Float16)alpha};
-        lrow[ml] *= alpha;
-#pragma unroll
-        for (int q = ml * (NCH / 4); q < (ml + 1) * (NCH / 4); ++q) {
-          float4 v = s_acc[q * kDecodeThreads];
-          v.x *= alpha;
-          v.y *= alpha;
-          v.z *= alpha;
-          v.w *= alpha;
-          s_acc[q * kDecodeThreads] = v;
-        }
-#pragma unroll
-        for (int p = 0; p < NPR; ++p) acc16[ml][p] = __builtin_bit_cast(uint32_t, as_h2t(acc16[ml][p]) * a2);
-        mr[ml] = sc[ml] * sgm;
-        t = 0.f;
-      }
-      const float pr = __builtin_amdgcn_exp2f(__builtin_amdgcn_ldexpf(t, E));
+      const float pr = __builtin_amdgcn_exp2f(__builtin_amdgcn_ldexpf(t[ml], E));
       lrow[ml] += pr;
       const h2t_t p2 = {(_Float16)pr, (_Float16)pr};
 #pragma unroll
@@ -500,51 +581,64 @@ __global__ __launch_bounds__(kDecodeThreads, NSL == 1 ? 4 : (C == 4 ? 3 : 2)) vo
     }
   }
   flush();
-  float acc[NSL][NCH];
-#pragma unroll
-  for (int q = 0; q < kAccQ; ++q) {
-    const float4 v = s_acc[q * kDecodeThreads];
-    const int ml = q / (NCH / 4), j0 = 4 * (q % (NCH / 4));
-    acc[ml][j0] = v.x;
-    acc[ml][j0 + 1] = v.y;
-    acc[ml][j0 + 2] = v.z;
-    acc[ml][j0 + 3] = v.w;
-  }
-  __syncthreads();   // every lane holds its sums: the region becomes the merge buffer
-  // running maxima back to base-2 score units
-  float mrow[NSL];
-#pragma unroll
-  for (int ml = 0; ml < NSL; ++ml) mrow[ml] = __builtin_amdgcn_ldexpf(mr[ml], E);
-
-  // ---- merge the lanes of the wave that hold the same channels and steps
-  // (equal sl; with one served step, equal g)
-#pragma unroll
-  for (int off = NSL == 2 ? LPT : LPT / 2; off < kWave; off <<= 1) {
+  if constexpr (kShared) {
+    // the sums are already the wave's merge slot; its maximum is the rows'
+    // common one, its sum of weights the rows' total
 #pragma unroll
     for (int ml = 0; ml < NSL; ++ml) {
-      const float om = __shfl_xor(mrow[ml], off);
-      const float ol = __shfl_xor(lrow[ml], off);
-      const float mm = fmaxf(mrow[ml], om);
-      const float a1 = mrow[ml] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mrow[ml] - mm);
-      const float a2 = om == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(om - mm);
-      lrow[ml] = lrow[ml] * a1 + ol * a2;
-#pragma unroll
-      for (int j = 0; j < NCH; ++j) {
-        const float oa = __shfl_xor(acc[ml][j], off);
-        acc[ml][j] = acc[ml][j] * a1 + oa * a2;
+      const float l = group4_sum(lrow[ml]);
+      if (slot == 0 && g == 0) {
+        s_red[wave][lane_step(ml)][D] = __builtin_amdgcn_ldexpf(mr[ml], E);
+        s_red[wave][lane_step(ml)][D + 1] = l;
       }
-      mrow[ml] = mm;
     }
-  }
-  if (NSL == 2 ? slot == 0 : (lane >> 3) == 0) {
+  } else {
+    float acc[NSL][NCH];
 #pragma unroll
-    for (int ml = 0; ml < NSL; ++ml) {
-      const int m = lane_step(ml);
+    for (int q = 0; q < kAccQ; ++q) {
+      const float4 v = s_acc[q * kDecodeThreads];
+      const int ml = q / (NCH / 4), j0 = 4 * (q % (NCH / 4));
+      acc[ml][j0] = v.x;
+      acc[ml][j0 + 1] = v.y;
+      acc[ml][j0 + 2] = v.z;
+      acc[ml][j0 + 3] = v.w;
+    }
+    __syncthreads();   // every lane holds its sums: the region becomes the merge buffer
+    // running maxima back to base-2 score units
+    float mrow[NSL];
 #pragma unroll
-      for (int j = 0; j < NCH; ++j) s_red[wave][m][NCH * g + j] = acc[ml][j];
-      if (g == 0) {
-        s_red[wave][m][D] = mrow[ml];
-        s_red[wave][m][D + 1] = lrow[ml];
+    for (int ml = 0; ml < NSL; ++ml) mrow[ml] = __builtin_amdgcn_ldexpf(mr[ml], E);
+
+    // ---- merge the lanes of the wave that hold the same channel and step
+    // (equal g)
+#pragma unroll
+    for (int off = LPT / 2; off < kWave; off <<= 1) {
+#pragma unroll
+      for (int ml = 0; ml < NSL; ++ml) {
+        const float om = __shfl_xor(mrow[ml], off);
+        const float ol = __shfl_xor(lrow[ml], off);
+        const float mm = fmaxf(mrow[ml], om);
+        const float a1 = mrow[ml] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mrow[ml] - mm);
+        const float a2 = om == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(om - mm);
+        lrow[ml] = lrow[ml] * a1 + ol * a2;
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) {
+          const float oa = __shfl_xor(acc[ml][j], off);
+          acc[ml][j] = acc[ml][j] * a1 + oa * a2;
+        }
+        mrow[ml] = mm;
+      }
+    }
+    if ((lane >> 3) == 0) {
+#pragma unroll
+      for (int ml = 0; ml < NSL; ++ml) {
+        const int m = lane_step(ml);
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) s_red[wave][m][NCH * g + j] = acc[ml][j];
+        if (g == 0) {
+          s_red[wave][m][D] = mrow[ml];
+          s_red[wave][m][D + 1] = lrow[ml];
+        }
       }
     }
   }
