@@ -310,8 +310,8 @@ __global__ __launch_bounds__(kDecodeThreads, NSL == 1 ? 4 : (C == 4 ? 3 : 2)) vo
   auto load_row = [&](int P) {
     const uint32_t ca = __builtin_amdgcn_raw_buffer_load_b16(rope_rs, rope_a, P * (D * 2), 0);
     const uint32_t cb = __builtin_amdgcn_raw_buffer_load_b16(rope_rs, rope_b, P * (D * 2), 0);
-    const uint32_t sa = __builtin_amdgcn_raw_buffer_load_b16(rope_rs, rope_a + 8, P * (D * 2), 0);
-    const uint32_t sb = __builtin_amdgcn_raw_buffer_load_b16(rope_rs, rope_b + 8, P * (D * 2), 0);
+    const uint32_t sa = __builtin_amdgcn_raw_buffer_load_b16(rope_rs, rope_a, P * (D * 2) + 8, 0);
+    const uint32_t sb = __builtin_amdgcn_raw_buffer_load_b16(rope_rs, rope_b, P * (D * 2) + 8, 0);
     return make_uint2(ca | (cb << 16), sa | (sb << 16));
   };
   // The wave's pair table for one position: written and read by this wave
