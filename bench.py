@@ -1058,9 +1058,15 @@ def write_traffic(cfg_index, fetch_dir, write_dir, command):
               [(big(fetch, name), big(write, name)) for name in
                ("sigma_kernel", "encode_kernel<16, 4, true>", "encode_kernel<16, 4, false>")])
     elif cfg_index == 2:
-        entry("decode_half@2", "decode_half", "decode_half_kernel + merge_kernel",
-              [(has("decode_half"), has("decode_half")),
-               (after(fetch, "decode_half", "merge_kernel"), after(write, "decode_half", "merge_kernel"))])
+        # the step loop's calls (each right after the value encode), not the
+        # recent-window calls timed afterwards
+        def step_calls(tab):
+            dec = after(tab, "encode_kernel", "decode_half")
+            merge = {k for k, (n, _, _) in tab.items() if "merge_kernel" in n and int(k) - 1 in {int(j) for j in dec}}
+            return dec, merge
+        (fd, fm), (wd, wm) = step_calls(fetch), step_calls(write)
+        entry("decode_half@2", "decode_half", "decode_half_kernel + merge_kernel (the step loop's calls)",
+              [(fd, wd), (fm, wm)])
         entry("encode@2", "encode", "encode_kernel<16, 4, false>",
               [(big(fetch, "encode_kernel<16, 4, false>"), big(write, "encode_kernel<16, 4, false>"))])
     else:
