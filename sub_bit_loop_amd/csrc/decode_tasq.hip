@@ -118,6 +118,10 @@ __global__ __launch_bounds__(kDecodeThreads, NSL == 1 ? 4 : (C == 4 ? 3 : 2)) vo
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int sl = lane & 15, slot = lane >> 4;
   const int hs = sl >> 3, g = sl & 7;
+  // NSL = 2: the lane keeps the softmax of its step 2hs + par; lanes g and
+  // 7 - g of a token's group hold the two steps
+  const int par = g >> 2;
+  const uint32_t psel = par ? 0x01000504u : 0x05040100u;   // v_perm: (partner, own) or (own, partner)
   // this lane's token offset o within an iteration
   const int my = NSL == 2 ? wave * SPW + slot : (wave * SPW + slot) * 2 + hs;
   const int split = blockIdx.x;
@@ -255,15 +259,14 @@ __global__ __launch_bounds__(kDecodeThreads, NSL == 1 ? 4 : (C == 4 ? 3 : 2)) vo
   const int E = shk + shq;
   const float lagr = ldexpf((float)kTLag, -E);
 
-  float mr[NSL], lrow[NSL];
+  // running maximum and sum of weights of the lane's one softmax step (the
+  // kept step with NSL = 2, the served step with NSL = 1)
+  float mr[1] = {-INFINITY}, lrow[1] = {0.f};
   uint32_t acc16[NSL][NPR];
 #pragma unroll
-  for (int ml = 0; ml < NSL; ++ml) {
-    mr[ml] = -INFINITY;
-    lrow[ml] = 0.f;
+  for (int ml = 0; ml < NSL; ++ml)
 #pragma unroll
     for (int p = 0; p < NPR; ++p) acc16[ml][p] = 0u;
-  }
   __syncthreads();   // codebooks staged; the offset table is no longer read
   // NSL = 2: the two float4 of the wave's sums that this lane adds into at a
   // flush: row slot of the wave takes step 2hs + (slot >> 1), channels
@@ -348,8 +351,18 @@ __global__ __launch_bounds__(kDecodeThreads, NSL == 1 ? 4 : (C == 4 ? 3 : 2)) vo
       for (int ml = 0; ml < NSL; ++ml)
         part[ml] = __builtin_amdgcn_fdot2(e2[ml], as_h2t(Kw[p / DW][ml * DW + p % DW]), part[ml], false);
     }
+    if constexpr (kShared) {
+      // lanes g and 7 - g trade the step the other keeps, then the four
+      // lanes of each half of the group add up (sc[0]: the kept step)
+      const float keep = par ? part[1] : part[0], give = par ? part[0] : part[1];
+      float x = keep + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(give), 0x141, 0xF, 0xF, true));
+      x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));
+      x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true));
+      sc[0] = x;
+    } else {
 #pragma unroll
-    for (int ml = 0; ml < NSL; ++ml) sc[ml] = group_sum<8>(part[ml]);
+      for (int ml = 0; ml < NSL; ++ml) sc[ml] = group_sum<8>(part[ml]);
+    }
   };
   // fp16 partial sums into the fp32 sums in LDS.  NSL = 2: the four rows'
   // partials are first summed and scattered by two permlane swaps, after
@@ -400,67 +413,67 @@ __global__ __launch_bounds__(kDecodeThreads, NSL == 1 ? 4 : (C == 4 ? 3 : 2)) vo
     x.w *= alpha;
     *v = x;
   };
-  // sg: the token's sigma for the lane's steps (fp16 pair; NSL = 1 uses .x).
   // A token whose score exceeds the running maximum by more than kTLag
-  // raises the maximum (NSL = 2: for the four rows together, in a branch the
-  // whole wave takes) and rescales every sum kept relative to it.
+  // raises the maximum and rescales every sum kept relative to it.
+  // NSL = 2: sg.x is the sigma of the lane's kept step, sc[0] its score; the
+  // maximum is raised for the four rows together, in a branch the whole wave
+  // takes, and the weights of both steps reach the P*V update through the
+  // partner lane 7 - g.  NSL = 1: sg.x is the served step's sigma.
   auto accumulate = [&](const float (&sc)[NSL], h2t_t sg, const uint32_t (&Vw)[NCK][KWD], bool valid) {
-    float t[NSL], sgm[NSL];
+    const float sgm = (float)sg.x;
+    float t = fmaf(sc[0], sgm, -mr[0]);   // (score - running maximum) * 2^-E
     if constexpr (kShared) {
-      bool need = false;
+      if (__builtin_amdgcn_ballot_w64(valid && t > lagr) != 0) {
+        const float nm = fmaxf(mr[0], group4_max(valid ? sc[0] * sgm : -INFINITY));
+        // every row holds a valid token here, so nm is finite
+        const float al = __builtin_amdgcn_exp2f(__builtin_amdgcn_ldexpf(mr[0] - nm, E));
+        const float ao = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(al), 0x141, 0xF, 0xF, true));
+        const float a0 = par ? ao : al, a1 = par ? al : ao;
+        const h2t_t a20 = {(_Float16)a0, (_Float16)a0}, a21 = {(_Float16)a1, (_Float16)a1};
+        lrow[0] *= al;
 #pragma unroll
-      for (int ml = 0; ml < NSL; ++ml) {
-        sgm[ml] = (float)(ml ? sg.y : sg.x);
-        t[ml] = fmaf(sc[ml], sgm[ml], -mr[ml]);   // (score - running maximum) * 2^-E
-        need = need || t[ml] > lagr;
-      }
-      if (__builtin_amdgcn_ballot_w64(valid && need) != 0) {
-#pragma unroll
-        for (int ml = 0; ml < NSL; ++ml) {
-          const float nm = fmaxf(mr[ml], group4_max(valid ? sc[ml] * sgm[ml] : -INFINITY));
-          // every row holds a valid token here, so nm is finite
-          const float alpha = __builtin_amdgcn_exp2f(__builtin_amdgcn_ldexpf(mr[ml] - nm, E));
-          const h2t_t a2 = {(_Float16)alpha, (_Float16)alpha};
-          lrow[ml] *= alpha;
-#pragma unroll
-          for (int p = 0; p < NPR; ++p) acc16[ml][p] = __builtin_bit_cast(uint32_t, as_h2t(acc16[ml][p]) * a2);
-          if ((slot >> 1) == ml) {
-            rescale(reinterpret_cast<float4*>(s_mine), alpha);
-            rescale(reinterpret_cast<float4*>(s_mine) + 1, alpha);
-          }
-          mr[ml] = nm;
-          t[ml] = fmaf(sc[ml], sgm[ml], -nm);
+        for (int p = 0; p < NPR; ++p) {
+          acc16[0][p] = __builtin_bit_cast(uint32_t, as_h2t(acc16[0][p]) * a20);
+          acc16[NSL - 1][p] = __builtin_bit_cast(uint32_t, as_h2t(acc16[NSL - 1][p]) * a21);
         }
+        const float ar = (slot >> 1) ? a1 : a0;
+        rescale(reinterpret_cast<float4*>(s_mine), ar);
+        rescale(reinterpret_cast<float4*>(s_mine) + 1, ar);
+        mr[0] = nm;
+        t = fmaf(sc[0], sgm, -nm);
       }
       if (!valid) return;
+      const float pr = __builtin_amdgcn_exp2f(__builtin_amdgcn_ldexpf(t, E));
+      lrow[0] += pr;
+      const uint32_t p16 = __builtin_bit_cast(uint16_t, (_Float16)pr);
+      const uint32_t o16 = __builtin_amdgcn_mov_dpp(p16, 0x141, 0xF, 0xF, true);
+      const h2t_t pp = as_h2t(__builtin_amdgcn_perm(o16, p16, psel));   // (step 2hs, step 2hs + 1)
+      const h2t_t p0 = {pp.x, pp.x}, p1 = {pp.y, pp.y};
+#pragma unroll
+      for (int p = 0; p < NPR; ++p) {
+        acc16[0][p] = __builtin_bit_cast(uint32_t, as_h2t(Vw[p / DW][p % DW]) * p0 + as_h2t(acc16[0][p]));
+        acc16[NSL - 1][p] = __builtin_bit_cast(
+            uint32_t, as_h2t(Vw[p / DW][(NSL - 1) * DW + p % DW]) * p1 + as_h2t(acc16[NSL - 1][p]));
+      }
     } else {
       if (!valid) return;
+      if (t > lagr) {
+        const float alpha = __builtin_amdgcn_exp2f(__builtin_amdgcn_ldexpf(-t, E));
+        const h2t_t a2 = {(_Float16)alpha, (_Float16)alpha};
+        lrow[0] *= alpha;
 #pragma unroll
-      for (int ml = 0; ml < NSL; ++ml) {
-        sgm[ml] = (float)(ml ? sg.y : sg.x);
-        t[ml] = fmaf(sc[ml], sgm[ml], -mr[ml]);
-        if (t[ml] > lagr) {
-          const float alpha = __builtin_amdgcn_exp2f(__builtin_amdgcn_ldexpf(-t[ml], E));
-          const h2t_t a2 = {(_Float16)alpha, (_Float16)alpha};
-          lrow[ml] *= alpha;
+        for (int q = 0; q < NCH / 4; ++q) rescale(&s_acc[q * kDecodeThreads], alpha);
 #pragma unroll
-          for (int q = ml * (NCH / 4); q < (ml + 1) * (NCH / 4); ++q) rescale(&s_acc[q * kDecodeThreads], alpha);
-#pragma unroll
-          for (int p = 0; p < NPR; ++p) acc16[ml][p] = __builtin_bit_cast(uint32_t, as_h2t(acc16[ml][p]) * a2);
-          mr[ml] = sc[ml] * sgm[ml];
-          t[ml] = 0.f;
-        }
+        for (int p = 0; p < NPR; ++p) acc16[0][p] = __builtin_bit_cast(uint32_t, as_h2t(acc16[0][p]) * a2);
+        mr[0] = sc[0] * sgm;
+        t = 0.f;
       }
-    }
-#pragma unroll
-    for (int ml = 0; ml < NSL; ++ml) {
-      const float pr = __builtin_amdgcn_exp2f(__builtin_amdgcn_ldexpf(t[ml], E));
-      lrow[ml] += pr;
+      const float pr = __builtin_amdgcn_exp2f(__builtin_amdgcn_ldexpf(t, E));
+      lrow[0] += pr;
       const h2t_t p2 = {(_Float16)pr, (_Float16)pr};
 #pragma unroll
       for (int p = 0; p < NPR; ++p)
-        acc16[ml][p] = __builtin_bit_cast(uint32_t,
-                                          as_h2t(Vw[p / DW][ml * DW + p % DW]) * p2 + as_h2t(acc16[ml][p]));
+        acc16[0][p] = __builtin_bit_cast(uint32_t, as_h2t(Vw[p / DW][p % DW]) * p2 + as_h2t(acc16[0][p]));
     }
   };
 
@@ -524,13 +537,18 @@ __global__ __launch_bounds__(kDecodeThreads, NSL == 1 ? 4 : (C == 4 ? 3 : 2)) vo
       (void*)(a.sigma + (int64_t)b * a.sig_cap * a.T), 0, a.sig_cap * a.T * 2, kBufWord3);
   const int idx_lane = (tok_lo + my) * CPT + 4 * kwo;
   // sigma of the lane's steps: one 4-byte word holds an even step and the next
-  const int sig_lane = ((tok_lo + my) * a.T + beta * TC + (NSL == 2 ? 2 * hs : (m0 & ~1))) * 2;
+  // sigma: NSL = 2, the lane's kept step (2 bytes); NSL = 1, the 4-byte word
+  // holding the served step and its even/odd neighbour
+  const int sig_lane = ((tok_lo + my) * a.T + beta * TC + (NSL == 2 ? 2 * hs + par : (m0 & ~1))) * 2;
   uint32_t kwn = 0, vwn = 0, sgn = 0;
   uint2 rown = make_uint2(0u, 0u);
   auto load_next = [&](int base) {
     kwn = __builtin_amdgcn_raw_buffer_load_b32(kid_rs, idx_lane, base * CPT, 0);
     vwn = __builtin_amdgcn_raw_buffer_load_b32(vid_rs, idx_lane, base * CPT, 0);
-    sgn = __builtin_amdgcn_raw_buffer_load_b32(sig_rs, sig_lane, base * a.T * 2, 0);
+    if constexpr (NSL == 2)
+      sgn = __builtin_amdgcn_raw_buffer_load_b16(sig_rs, sig_lane, base * a.T * 2, 0);
+    else
+      sgn = __builtin_amdgcn_raw_buffer_load_b32(sig_rs, sig_lane, base * a.T * 2, 0);
     rown = load_row(P0 + (base < n_tok ? base : 0));         // a row of this split's tokens
   };
   if (n_tok > 0) load_next(0);
@@ -583,14 +601,12 @@ __global__ __launch_bounds__(kDecodeThreads, NSL == 1 ? 4 : (C == 4 ? 3 : 2)) vo
   flush();
   if constexpr (kShared) {
     // the sums are already the wave's merge slot; its maximum is the rows'
-    // common one, its sum of weights the rows' total
-#pragma unroll
-    for (int ml = 0; ml < NSL; ++ml) {
-      const float l = group4_sum(lrow[ml]);
-      if (slot == 0 && g == 0) {
-        s_red[wave][lane_step(ml)][D] = __builtin_amdgcn_ldexpf(mr[ml], E);
-        s_red[wave][lane_step(ml)][D + 1] = l;
-      }
+    // common one, its sum of weights the rows' total (lanes g = 0 and 4 of
+    // row 0 hold steps 2hs and 2hs + 1)
+    const float l = group4_sum(lrow[0]);
+    if (slot == 0 && (g & 3) == 0) {
+      s_red[wave][2 * hs + par][D] = __builtin_amdgcn_ldexpf(mr[0], E);
+      s_red[wave][2 * hs + par][D + 1] = l;
     }
   } else {
     float acc[NSL][NCH];
