@@ -425,7 +425,8 @@ __global__ __launch_bounds__(kDecodeThreads, NSL == 1 ? 4 : (C == 4 ? 3 : 2)) vo
     if constexpr (kShared) {
       if (__builtin_amdgcn_ballot_w64(valid && t > lagr) != 0) {
         const float nm = fmaxf(mr[0], group4_max(valid ? sc[0] * sgm : -INFINITY));
-        // every row holds a valid token here, so nm is finite
+        // some row holds a valid token here (the rows of a lane set are the
+        // wave's four tokens, valid alike for every lane set), so nm is finite
         const float al = __builtin_amdgcn_exp2f(__builtin_amdgcn_ldexpf(mr[0] - nm, E));
         const float ao = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(al), 0x141, 0xF, 0xF, true));
         const float a0 = par ? ao : al, a1 = par ? al : ao;
