@@ -115,8 +115,9 @@ DecodePlan plan_decode(const loopvq_geom* g, int B, int N, int step0, int n_step
       break;
     case DecodeKernel::kTasq:
       wgs = (long long)B * g->n_q_heads * p.n_blk_serv;
-      // several steps: 3 per CU at c = 4 (166 VGPRs, 51 KB LDS), else 2; one
-      // served step: 4 per CU (at most 128 VGPRs, 35 KB LDS)
+      // several steps: 3 per CU at c = 4 (166 VGPRs, 27 KB LDS); at c = 8 two
+      // (three fit, and measured slower); one served step: 4 per CU (at most
+      // 128 VGPRs, 35 KB LDS)
       target = n_steps == 1 ? 1024 : (g->G == 16 ? 768 : 512);
       break;
     default:
