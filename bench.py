@@ -39,6 +39,10 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
+# Packed-fp16 vector peak: 256 CUs x 2.4 GHz x one wave64 instruction per CU
+# per clock x 64 lanes x 2 FMA (4 flop) = 157.3 TFLOP/s (the fp32 vector figure
+# counts the same packed issue).
+F16_VALU_PEAK_TFLOPS = 157.3
 METRIC = "decode-attn context tokens/s per loop block + % HBM peak; encode codes/s"
 UNIT = "context tokens/s per loop block"
 OUT_TOL = 2e-3                      # max-abs error per output row, relative to the row's L2 norm
@@ -95,6 +99,21 @@ def host_cpu():
     except OSError:
         pass
     return cores, model
+
+
+def valu_roofline(units, T_c, D, gqa, ms, kernel):
+    """The decode's arithmetic against the packed-fp16 vector peak (the unit
+    the decode kernels are bound by at GQA 1): per (token, step, channel) of a
+    unit, the key rotation (2 multiplies + 1 add, shared by the q-heads of a
+    GQA group), the score product and the P.V product (2 flop each per
+    q-head)."""
+    flop = units * T_c * D * (3 + 4 * gqa)
+    tf = flop / (ms * 1e-3) / 1e12
+    return {"kernel": kernel, "bound": "alu", "achieved": tf, "peak": F16_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": tf / F16_VALU_PEAK_TFLOPS, "algorithmic_flop_per_launch": flop,
+            "algorithmic": "T_c * D * (3 + 4 * gqa) flop per (token, kv-head, block) unit: key rotation 3, "
+                           "score 2 and P.V 2 per q-head, per step and channel",
+            "note": "secondary view; the metric's roofline is the HBM one"}
 
 
 def _median_ms(pairs):
@@ -437,6 +456,8 @@ def workload5(args, torch, lv, cfg):
                    "step": "one decode-attention call per layer over all %d layers (all 4 loop steps), plus a "
                            "page encode per layer after every %d steps" % (L, cfg.page)},
         "roofline": roof_dec,
+        "roofline_decode_valu": valu_roofline(units_mean, cfg.T_c, cfg.D, Hq // H, dec_med,
+                                              "decode_tasq_kernel<4> (+ merge_kernel), one layer per launch"),
         "roofline_encode": roof_enc,
         "decode": {"ms_per_layer_call_median": dec_med,
                    "context_tokens_per_s_per_block": B * units_mean / (B * H) / (dec_med * 1e-3),
@@ -788,6 +809,8 @@ def single_layer(args, torch, lv, cfg, steps, warmup, with_cpu, stream=None):
                                          "in the same softmax, alternating with the call without them"},
         "roofline": dominant,
         "roofline_decode": roof_dec,
+        "roofline_decode_valu": valu_roofline(units, cfg.T_c, cfg.D, cfg.H_q // cfg.H_kv, dec_ms,
+                                              roof_dec["kernel"]),
         "roofline_encode": roof_enc,
         "hbm_stream": stream,
         "input_generation_s": t_gen,
@@ -1161,7 +1184,7 @@ def main():
         r2 = single_layer(args, torch, lv, config_by_index(2), 20, 3, False)
         sub = {k: r2[k] for k in ("config", "ms_per_step", "value", "decode", "encode", "decode_per_step",
                                   "decode_recent_window",
-                                  "roofline_decode", "roofline_encode")}
+                                  "roofline_decode", "roofline_decode_valu", "roofline_encode")}
     res = workload5(args, torch, lv, cfg)
     res["config2"] = sub
     print(json.dumps(res), flush=True)
