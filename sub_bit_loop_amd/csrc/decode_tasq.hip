@@ -19,8 +19,9 @@
 // and the dot product is multiplied by the token's sigma.  The permutation
 // separates RoPE partners, so unlike the plain kernels no lane rotates a key.
 //
-// Positions: a workgroup iteration serves 16 consecutive tokens at positions
-// P + o, where P is the same for every lane and o (0..15) is fixed per lane.
+// Positions: a workgroup iteration serves 16 consecutive tokens (32 with one
+// served step) at positions P + o, where P is the same for every lane and o
+// is fixed per lane.
 // By the angle-sum identity
 //     e[d'](P + o) = A_o[d'] cos(P w_f) + B_o[d'] sin(P w_f),
 //     A_o = a cos(o w_f) + b sin(o w_f),   B_o = b cos(o w_f) - a sin(o w_f),
@@ -43,7 +44,13 @@
 //     half of one (c = 8).
 //   * Effective queries, scores and P*V run on packed fp16 (scores summed in
 //     fp32 by v_dot2_f32_f16); P*V partials are flushed into fp32 every
-//     kFlush tokens, with the same range bounds as the plain kernels.
+//     kTFlush tokens, with the same kind of range bounds as the plain kernels.
+//   * Online softmax (all steps, NSL = 2): the four tokens of a wave
+//     iteration share one running maximum per step, raised in a branch the
+//     whole wave takes, so their fp16 partials add up across the four rows
+//     before a flush and the wave keeps one set of fp32 sums in LDS; of the
+//     two lanes g and 7 - g that hold the same steps, each keeps the softmax
+//     of one step and hands its weight to the other through DPP.
 // One workgroup serves one (batch, q-head, block, context split).  A call
 // for one served step (n_steps = 1) takes the variant with one step per lane
 // (NSL = 1): lanes hs = 0 / 1 then serve two tokens instead of two steps, and
@@ -118,10 +125,11 @@ __global__ __launch_bounds__(kDecodeThreads, NSL == 1 ? 4 : (C == 4 ? 3 : 2)) vo
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int sl = lane & 15, slot = lane >> 4;
   const int hs = sl >> 3, g = sl & 7;
-  // NSL = 2: the lane keeps the softmax of its step 2hs + par; lanes g and
-  // 7 - g of a token's group hold the two steps
+  // NSL = 2: lanes g and 7 - g of a token's group hold the same two steps
+  // 2hs, 2hs + 1; the lane keeps the softmax of step 2hs + par, and psel
+  // orders its own and its partner's fp16 weight as (step 2hs, step 2hs + 1)
   const int par = g >> 2;
-  const uint32_t psel = par ? 0x01000504u : 0x05040100u;   // v_perm: (partner, own) or (own, partner)
+  const uint32_t psel = par ? 0x01000504u : 0x05040100u;
   // this lane's token offset o within an iteration
   const int my = NSL == 2 ? wave * SPW + slot : (wave * SPW + slot) * 2 + hs;
   const int split = blockIdx.x;
