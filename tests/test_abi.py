@@ -122,6 +122,15 @@ def test_decode_workspace_and_errors():
     assert call(ws_bytes=need.value - 1) == -4
     assert call(ws=P(0)) == -4
     assert call(B=0) == 0                     # nothing to do
+    # pre-transformed keys: the kernel's index-row, sigma and table offsets are
+    # 32-bit, so a capacity of 2^26 tokens of 32-byte rows (2^31 bytes) is refused
+    big = 1 << 26
+    pt = L.PreTransform(16, 16, 16, big)
+    wide = ctypes.c_size_t(0)
+    assert lib.loopvq_decode_attn_workspace(ctypes.byref(g), 2, 100, 0, 4, ctypes.byref(wide)) == 0
+    assert call(N_cap=big, pt=ctypes.byref(pt), ws_bytes=wide.value) == -2
+    assert "32-bit" in lib.loopvq_last_error().decode()
+    assert call(N_cap=big - 1, pt=ctypes.byref(pt), ws_bytes=wide.value, q=P(0)) == -1   # plain argument errors first
 
 
 def test_kmeans_entry_points_reject_bad_arguments():
