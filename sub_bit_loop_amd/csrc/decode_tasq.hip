@@ -58,6 +58,8 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <type_traits>
+
 namespace loopvq {
 
 namespace {
@@ -65,6 +67,27 @@ namespace {
 typedef _Float16 h2t_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ h2t_t as_h2t(uint32_t w) { return __builtin_bit_cast(h2t_t, w); }
+
+// a.x * b.x + a.y * b.y in fp32, the first product of a chain: the VOP3
+// form takes the zero addend as a constant (the compiler's accumulating form
+// would first move a zero into a register)
+__device__ __forceinline__ float dot2_first(h2t_t a, h2t_t b) {
+  float r;
+  asm("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
+// w16 * S + add, w16 the 16-bit half H of w (op_sel picks the high half):
+// the byte offset of a codeword from an index spread into a 16-bit half
+template <int H, int S>
+__device__ __forceinline__ uint32_t mad_half(uint32_t w, uint32_t add) {
+  uint32_t r;
+  if constexpr (H == 0)
+    asm("v_mad_u32_u16 %0, %1, %2, %3" : "=v"(r) : "v"(w), "i"(S), "v"(add));
+  else
+    asm("v_mad_u32_u16 %0, %1, %2, %3 op_sel:[1,0,0,0]" : "=v"(r) : "v"(w), "i"(S), "v"(add));
+  return r;
+}
 
 __device__ __forceinline__ uint32_t pack_h2t(float a, float b) {
   const _Float16 x = (_Float16)a, y = (_Float16)b;
@@ -96,6 +119,7 @@ __global__ __launch_bounds__(kDecodeThreads, NSL == 1 ? 4 : (C == 4 ? 3 : 2)) vo
   constexpr int NPR = NCH / 2;        // channel pairs per lane (8)
   constexpr int KWD = NSL * DW;       // codeword dwords per chunk a lane reads
   static_assert(NPR * 8 == kWave, "one channel pair of the table per lane");
+  static_assert((kTFlush * TPI & (kTFlush * TPI - 1)) == 0, "flush period is a power of two");
   __shared__ __attribute__((aligned(16))) uint4 s_k[256 * 2 * QW];
   __shared__ __attribute__((aligned(16))) uint4 s_v[256 * 2 * QW];
   // fp32 P*V sums.  NSL = 2: the four tokens of a wave iteration (lanes l,
@@ -130,6 +154,13 @@ __global__ __launch_bounds__(kDecodeThreads, NSL == 1 ? 4 : (C == 4 ? 3 : 2)) vo
   // orders its own and its partner's fp16 weight as (step 2hs, step 2hs + 1)
   const int par = g >> 2;
   const uint32_t psel = par ? 0x01000504u : 0x05040100u;
+  // NSL = 2: lanes (0, g) and (1, g) of a token read the same pair-table
+  // entries, so each reads half of them (its pairs rot .. rot + 3, rot = 4 hs)
+  // and takes the other half from the other lane through DPP.  The lane then
+  // keeps its channel pairs in slot order, slot s holding pair (s + rot) mod 8,
+  // for the coefficients, the gathered codeword chunks and the P*V sums alike.
+  const int rot = kShared ? 4 * hs : 0;
+  auto pair_of = [&](int s) { return (s + rot) & (NPR - 1); };
   // this lane's token offset o within an iteration
   const int my = NSL == 2 ? wave * SPW + slot : (wave * SPW + slot) * 2 + hs;
   const int split = blockIdx.x;
@@ -231,7 +262,8 @@ __global__ __launch_bounds__(kDecodeThreads, NSL == 1 ? 4 : (C == 4 ? 3 : 2)) vo
     float2 oc[NCH];
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
-      const int o = a.perm[h * D + NCH * g + j] & (D - 1);   // stays in bounds for any input
+      // pair slot j / 2; the index stays in bounds for any input
+      const int o = a.perm[h * D + NCH * g + 2 * pair_of(j >> 1) + (j & 1)] & (D - 1);
       och[j] = o;
       rw[j] = 1.f / a.w[h * D + o];
       oc[j] = s_off[my * HD + (o & (HD - 1))];
@@ -277,10 +309,10 @@ __global__ __launch_bounds__(kDecodeThreads, NSL == 1 ? 4 : (C == 4 ? 3 : 2)) vo
     for (int p = 0; p < NPR; ++p) acc16[ml][p] = 0u;
   __syncthreads();   // codebooks staged; the offset table is no longer read
   // NSL = 2: the two float4 of the wave's sums that this lane adds into at a
-  // flush: row slot of the wave takes step 2hs + (slot >> 1), channels
-  // 16g + 8(slot & 1) .. +7 (the partials the cross-row reduction leaves
-  // in this lane)
-  float* const s_mine = &s_red[wave][2 * hs + (slot >> 1)][NCH * g + 8 * (slot & 1)];
+  // flush: row slot of the wave takes step 2hs + (slot >> 1), pair slots
+  // 4(slot & 1) .. +3, i.e. channels 16g + 8((slot & 1) ^ hs) .. +7 (the
+  // partials the cross-row reduction leaves in this lane)
+  float* const s_mine = &s_red[wave][2 * hs + (slot >> 1)][NCH * g + 8 * ((slot & 1) ^ hs)];
   if constexpr (kShared) {
     reinterpret_cast<float4*>(s_mine)[0] = make_float4(0.f, 0.f, 0.f, 0.f);
     reinterpret_cast<float4*>(s_mine)[1] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -306,24 +338,29 @@ __global__ __launch_bounds__(kDecodeThreads, NSL == 1 ? 4 : (C == 4 ? 3 : 2)) vo
   // offset past the described range reads 0 instead of faulting.
   const __amdgpu_buffer_rsrc_t rope_rs =
       __builtin_amdgcn_make_buffer_rsrc((void*)a.rope, 0, a.n_pos * D * 2, kBufWord3);
-  // byte offsets in a table row of the cosines of the two frequencies of
-  // the channel pair this lane loads (pair lane / 8 of group lane % 8); each
-  // sine sits 8 bytes after its cosine
+  // byte offsets in a table row of the aligned 4-byte words holding the
+  // cosines of the two frequencies of the channel pair this lane loads (pair
+  // lane / 8 of group lane % 8), each sine sitting 8 bytes after its cosine,
+  // and the byte selector that packs the two fp16 values (a low, b high) out
+  // of the two words
   int rope_a, rope_b;
+  uint32_t rope_sel;
   {
     const int pg = lane & 7, pp = lane >> 3;
     const int fa = a.perm[h * D + NCH * pg + 2 * pp] & (HD - 1);
     const int fb = a.perm[h * D + NCH * pg + 2 * pp + 1] & (HD - 1);
-    rope_a = ((fa >> 2) * 8 + (fa & 3)) * 2;
-    rope_b = ((fb >> 2) * 8 + (fb & 3)) * 2;
+    rope_a = (fa >> 1) * 4 + (fa >> 2) * 8;   // = ((fa >> 2) * 8 + (fa & 3)) * 2, rounded down to 4
+    rope_b = (fb >> 1) * 4 + (fb >> 2) * 8;
+    const uint32_t ba = 2 * (fa & 1), bb = 4 + 2 * (fb & 1);
+    rope_sel = ba | (ba + 1) << 8 | bb << 16 | (bb + 1) << 24;
   }
   // (cos pair, sin pair) of this lane's channel pair at position P
   auto load_row = [&](int P) {
-    const uint32_t ca = __builtin_amdgcn_raw_buffer_load_b16(rope_rs, rope_a, P * (D * 2), 0);
-    const uint32_t cb = __builtin_amdgcn_raw_buffer_load_b16(rope_rs, rope_b, P * (D * 2), 0);
-    const uint32_t sa = __builtin_amdgcn_raw_buffer_load_b16(rope_rs, rope_a, P * (D * 2) + 8, 0);
-    const uint32_t sb = __builtin_amdgcn_raw_buffer_load_b16(rope_rs, rope_b, P * (D * 2) + 8, 0);
-    return make_uint2(ca | (cb << 16), sa | (sb << 16));
+    const uint32_t ca = __builtin_amdgcn_raw_buffer_load_b32(rope_rs, rope_a, P * (D * 2), 0);
+    const uint32_t cb = __builtin_amdgcn_raw_buffer_load_b32(rope_rs, rope_b, P * (D * 2), 0);
+    const uint32_t sa = __builtin_amdgcn_raw_buffer_load_b32(rope_rs, rope_a, P * (D * 2) + 8, 0);
+    const uint32_t sb = __builtin_amdgcn_raw_buffer_load_b32(rope_rs, rope_b, P * (D * 2) + 8, 0);
+    return make_uint2(__builtin_amdgcn_perm(cb, ca, rope_sel), __builtin_amdgcn_perm(sb, sa, rope_sel));
   };
   // The wave's pair table for one position: written and read by this wave
   // only; LDS instructions of one wave execute in order, so the entries read
@@ -331,23 +368,34 @@ __global__ __launch_bounds__(kDecodeThreads, NSL == 1 ? 4 : (C == 4 ? 3 : 2)) vo
   auto pair_table = [&](uint2 row, uint32_t (&cs2)[NPR], uint32_t (&sn2)[NPR]) {
     s_pair[wave][lane] = row;
     __builtin_amdgcn_wave_barrier();
+    if constexpr (kShared) {
+      // slots s < 4 from the table, s + 4 from lane (1 - hs, g), 8 lanes over
+      // in the same row of 16 (a row rotation by 8)
 #pragma unroll
-    for (int p = 0; p < NPR; ++p) {
-      const uint2 e = s_pair[wave][8 * p + g];
-      cs2[p] = e.x;
-      sn2[p] = e.y;
+      for (int q = 0; q < NPR / 2; ++q) {
+        const uint2 e = s_pair[wave][8 * (rot + q) + g];
+        cs2[q] = e.x;
+        sn2[q] = e.y;
+        cs2[q + NPR / 2] = __builtin_amdgcn_mov_dpp(e.x, 0x128, 0xF, 0xF, true);
+        sn2[q + NPR / 2] = __builtin_amdgcn_mov_dpp(e.y, 0x128, 0xF, 0xF, true);
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < NPR; ++q) {
+        const uint2 e = s_pair[wave][8 * q + g];
+        cs2[q] = e.x;
+        sn2[q] = e.y;
+      }
     }
   };
   // Dot products of the lane's steps (summed over the 8 lanes of the
-  // token's group, before sigma); Kw[k][ml*DW + ip] = channel pair
-  // (2ip, 2ip+1) of chunk k at the lane's step ml.
+  // token's group, before sigma); Kw[k][ml*DW + ip] = pair slot k*DW + ip
+  // (a channel pair of chunk slot k) at the lane's step ml.
   auto scores = [&](const uint32_t (&cs2)[NPR], const uint32_t (&sn2)[NPR], const uint32_t (&Kw)[NCK][KWD],
                     float (&sc)[NSL]) {
     // the two steps' chains interleave, so the dependent pk_mul -> pk_fma
     // -> dot2 sequences overlap
     float part[NSL];
-#pragma unroll
-    for (int ml = 0; ml < NSL; ++ml) part[ml] = 0.f;
 #pragma unroll
     for (int p = 0; p < NPR; ++p) {
       h2t_t e2[NSL];
@@ -356,8 +404,10 @@ __global__ __launch_bounds__(kDecodeThreads, NSL == 1 ? 4 : (C == 4 ? 3 : 2)) vo
 #pragma unroll
       for (int ml = 0; ml < NSL; ++ml) e2[ml] = as_h2t(B2[ml][p]) * as_h2t(sn2[p]) + e2[ml];
 #pragma unroll
-      for (int ml = 0; ml < NSL; ++ml)
-        part[ml] = __builtin_amdgcn_fdot2(e2[ml], as_h2t(Kw[p / DW][ml * DW + p % DW]), part[ml], false);
+      for (int ml = 0; ml < NSL; ++ml) {
+        const h2t_t k2 = as_h2t(Kw[p / DW][ml * DW + p % DW]);
+        part[ml] = p == 0 ? dot2_first(e2[ml], k2) : __builtin_amdgcn_fdot2(e2[ml], k2, part[ml], false);
+      }
     }
     if constexpr (kShared) {
       // lanes g and 7 - g trade the step the other keeps, then the four
@@ -510,10 +560,10 @@ __global__ __launch_bounds__(kDecodeThreads, NSL == 1 ? 4 : (C == 4 ? 3 : 2)) vo
           float z[2];
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
-            const int o = a.perm[h * D + NCH * g + 2 * p + u] & (D - 1);
+            const int o = a.perm[h * D + NCH * g + 2 * pair_of(p) + u] & (D - 1);
             z[u] = bf16_to_f32(kr[o]) * a.w[h * D + o] * ksc;
           }
-          const uint32_t vv = *reinterpret_cast<const uint32_t*>(vr + NCH * g + 2 * p);
+          const uint32_t vv = *reinterpret_cast<const uint32_t*>(vr + NCH * g + 2 * pair_of(p));
           Kw[p / DW][ml * DW + p % DW] = pack_h2t(z[0], z[1]);
           Vw[p / DW][ml * DW + p % DW] = pack_h2t(bf16lo(vv) * vsc, bf16hi(vv) * vsc);
         }
@@ -536,6 +586,18 @@ __global__ __launch_bounds__(kDecodeThreads, NSL == 1 ? 4 : (C == 4 ? 3 : 2)) vo
   // word of the index row holding this lane's index bytes, and their bit offset
   const int kwo = C == 4 ? g : (g >> 1);
   const int kbit = C == 4 ? 0 : 16 * (g & 1);
+  // Byte selectors spreading the lane's index bytes into 16-bit halves in
+  // chunk-slot order: chunk slot k holds chunk (k + rotc) mod NCK, the chunk
+  // of the pairs its slots hold.  c = 4: isel0 takes slots 0, 2, isel1 slots
+  // 1, 3; c = 8: isel takes the lane's two bytes (of its 4-byte word) for
+  // slots 0, 1.
+  const int rotc = rot * NCK / NPR;
+  auto bsel = [&](int k0, int k1) {
+    return (uint32_t)k0 | 0x0C00u | (uint32_t)k1 << 16 | 0x0C000000u;
+  };
+  const uint32_t isel0 = bsel(rotc & 3, (2 + rotc) & 3), isel1 = bsel((1 + rotc) & 3, (3 + rotc) & 3);
+  const uint32_t isel = bsel(kbit / 8 + (rotc & 1), kbit / 8 + ((1 + rotc) & 1));
+  const uint32_t hsb = hs * QW * 16;   // byte offset of half hs inside a codeword
   // index rows of this (batch, kv-head, block) and sigma of this batch entry;
   // a lane past the split's last token reads a later row or 0 (unused)
   const __amdgpu_buffer_rsrc_t kid_rs =
@@ -549,39 +611,76 @@ __global__ __launch_bounds__(kDecodeThreads, NSL == 1 ? 4 : (C == 4 ? 3 : 2)) vo
   // sigma: NSL = 2, the lane's kept step (2 bytes); NSL = 1, the 4-byte word
   // holding the served step and its even/odd neighbour
   const int sig_lane = ((tok_lo + my) * a.T + beta * TC + (NSL == 2 ? 2 * hs + par : (m0 & ~1))) * 2;
-  uint32_t kwn = 0, vwn = 0, sgn = 0;
-  uint2 rown = make_uint2(0u, 0u);
-  auto load_next = [&](int base) {
-    kwn = __builtin_amdgcn_raw_buffer_load_b32(kid_rs, idx_lane, base * CPT, 0);
-    vwn = __builtin_amdgcn_raw_buffer_load_b32(vid_rs, idx_lane, base * CPT, 0);
-    if constexpr (NSL == 2)
-      sgn = __builtin_amdgcn_raw_buffer_load_b16(sig_rs, sig_lane, base * a.T * 2, 0);
-    else
-      sgn = __builtin_amdgcn_raw_buffer_load_b32(sig_rs, sig_lane, base * a.T * 2, 0);
-    rown = load_row(P0 + (base < n_tok ? base : 0));         // a row of this split's tokens
+  // what one iteration loads ahead: index words, sigma and the table row
+  struct Ahead {
+    uint32_t kw, vw, sg;
+    uint2 row;
   };
-  if (n_tok > 0) load_next(0);
-  int since_flush = 0;
-  for (int base = 0; base < n_tok; base += TPI) {
-    const bool valid = base + my < n_tok;
-    const uint32_t kwc = kwn, vwc = vwn, sgc = sgn;
-    const uint2 row = rown;
-    load_next(base + TPI);
+  auto load_ahead = [&](int base) {
+    Ahead x;
+    x.kw = __builtin_amdgcn_raw_buffer_load_b32(kid_rs, idx_lane, base * CPT, 0);
+    x.vw = __builtin_amdgcn_raw_buffer_load_b32(vid_rs, idx_lane, base * CPT, 0);
+    if constexpr (NSL == 2)
+      x.sg = __builtin_amdgcn_raw_buffer_load_b16(sig_rs, sig_lane, base * a.T * 2, 0);
+    else
+      x.sg = __builtin_amdgcn_raw_buffer_load_b32(sig_rs, sig_lane, base * a.T * 2, 0);
+    x.row = load_row(P0 + (base < n_tok ? base : 0));         // a row of this split's tokens
+    return x;
+  };
+  auto iteration = [&](int base, const Ahead& cur) {
+    const bool valid = my < n_tok - base;   // one compare with a scalar bound
     // LDS order: the pair table, then the K gathers, then the V gathers, so
     // the scores can start while the V gathers are in flight
     uint32_t cs2[NPR], sn2[NPR];
-    pair_table(row, cs2, sn2);
+    pair_table(cur.row, cs2, sn2);
     uint32_t Kw[NCK][KWD], Vw[NCK][KWD];
     // codeword dwords of the lane's steps: the half hs (both steps), or the
-    // served step's DW dwords inside its half
-    auto gather = [&](const uint4* cb, uint32_t idx, uint32_t (&out)[KWD]) {
-      if constexpr (NSL == 2) {
+    // served step's dwords
+    if constexpr (NSL == 2) {
+      // The lane's index bytes are spread into 16-bit halves of two words
+      // (c = 4: the bytes of chunk slots 0, 2 and 1, 3; c = 8: its two bytes
+      // in one word), so each codeword's byte offset, idx * 32 QW + the half's
+      // 16 QW hs, is one multiply-add on a half.
+      auto spread = [&](uint32_t w, uint32_t (&h)[2]) {
+        if constexpr (C == 4) {
+          h[0] = __builtin_amdgcn_perm(w, w, isel0);
+          h[1] = __builtin_amdgcn_perm(w, w, isel1);
+        } else {
+          h[0] = __builtin_amdgcn_perm(w, w, isel);
+          h[1] = 0u;
+        }
+      };
+      uint32_t kh[2], vh[2];
+      spread(cur.kw, kh);
+      spread(cur.vw, vh);
+      auto gather = [&](const uint4* cb, uint32_t off, uint32_t (&out)[KWD]) {
+        const uint4* x = reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(cb) + off);
 #pragma unroll
         for (int u = 0; u < QW; ++u) {
-          const uint4 x = cb[(2 * idx + hs) * QW + u];
-          out[4 * u] = x.x; out[4 * u + 1] = x.y; out[4 * u + 2] = x.z; out[4 * u + 3] = x.w;
+          const uint4 y = x[u];
+          out[4 * u] = y.x; out[4 * u + 1] = y.y; out[4 * u + 2] = y.z; out[4 * u + 3] = y.w;
         }
-      } else {
+      };
+      auto offset = [&](const uint32_t (&h)[2], auto kc) {
+        constexpr int k = decltype(kc)::value;
+        constexpr int wsel = C == 4 ? (k & 1) : 0, hsel = C == 4 ? (k >> 1) : k;
+        return mad_half<hsel, 32 * QW>(h[wsel], hsb);
+      };
+      gather(s_k, offset(kh, std::integral_constant<int, 0>{}), Kw[0]);
+      gather(s_k, offset(kh, std::integral_constant<int, 1>{}), Kw[1]);
+      if constexpr (NCK == 4) {
+        gather(s_k, offset(kh, std::integral_constant<int, 2>{}), Kw[2]);
+        gather(s_k, offset(kh, std::integral_constant<int, 3>{}), Kw[3]);
+      }
+      gather(s_v, offset(vh, std::integral_constant<int, 0>{}), Vw[0]);
+      gather(s_v, offset(vh, std::integral_constant<int, 1>{}), Vw[1]);
+      if constexpr (NCK == 4) {
+        gather(s_v, offset(vh, std::integral_constant<int, 2>{}), Vw[2]);
+        gather(s_v, offset(vh, std::integral_constant<int, 3>{}), Vw[3]);
+      }
+    } else {
+      // the served step's DW dwords inside its half
+      auto gather = [&](const uint4* cb, uint32_t idx, uint32_t (&out)[KWD]) {
         const uint32_t* w = reinterpret_cast<const uint32_t*>(cb + (2 * idx + (m0 >> 1)) * QW) + (m0 & 1) * DW;
         if constexpr (DW == 2) {
           const uint2 x = *reinterpret_cast<const uint2*>(w);
@@ -590,21 +689,32 @@ __global__ __launch_bounds__(kDecodeThreads, NSL == 1 ? 4 : (C == 4 ? 3 : 2)) vo
           const uint4 x = *reinterpret_cast<const uint4*>(w);
           out[0] = x.x; out[1] = x.y; out[2] = x.z; out[3] = x.w;
         }
-      }
-    };
+      };
 #pragma unroll
-    for (int k = 0; k < NCK; ++k) gather(s_k, __builtin_amdgcn_ubfe(kwc, kbit + 8 * k, 8), Kw[k]);
+      for (int k = 0; k < NCK; ++k) gather(s_k, __builtin_amdgcn_ubfe(cur.kw, kbit + 8 * k, 8), Kw[k]);
 #pragma unroll
-    for (int k = 0; k < NCK; ++k) gather(s_v, __builtin_amdgcn_ubfe(vwc, kbit + 8 * k, 8), Vw[k]);
+      for (int k = 0; k < NCK; ++k) gather(s_v, __builtin_amdgcn_ubfe(cur.vw, kbit + 8 * k, 8), Vw[k]);
+    }
     __builtin_amdgcn_sched_barrier(0);   // keep every gather issued ahead of the arithmetic
-    h2t_t s16 = as_h2t(sgc);
+    h2t_t s16 = as_h2t(cur.sg);
     if constexpr (NSL == 1) s16.x = (m0 & 1) ? s16.y : s16.x;
     float sc[NSL];
     scores(cs2, sn2, Kw, sc);
     accumulate(sc, s16, Vw, valid);
-    if (++since_flush == kTFlush) {
-      flush();
-      since_flush = 0;
+    // every kTFlush iterations (base is the same in every lane)
+    if ((base & (kTFlush * TPI - 1)) == (kTFlush - 1) * TPI) flush();
+  };
+  // two iterations per trip, loading into alternate register sets, so that
+  // nothing loaded ahead is copied from one set to the other
+  if (n_tok > 0) {
+    Ahead x0 = load_ahead(0), x1;
+    for (int base = 0;; base += 2 * TPI) {
+      x1 = load_ahead(base + TPI);
+      iteration(base, x0);
+      if (base + TPI >= n_tok) break;
+      x0 = load_ahead(base + 2 * TPI);
+      iteration(base + TPI, x1);
+      if (base + 2 * TPI >= n_tok) break;
     }
   }
   flush();
