@@ -19,9 +19,9 @@
 // and the dot product is multiplied by the token's sigma.  The permutation
 // separates RoPE partners, so unlike the plain kernels no lane rotates a key.
 //
-// Positions: a workgroup iteration serves 16 consecutive tokens (32 with one
-// served step) at positions P + o, where P is the same for every lane and o
-// is fixed per lane.
+// Positions: a workgroup iteration serves 4 consecutive tokens per wave (8
+// with one served step) at positions P + o, where P is the same for every
+// lane and o is fixed per lane.
 // By the angle-sum identity
 //     e[d'](P + o) = A_o[d'] cos(P w_f) + B_o[d'] sin(P w_f),
 //     A_o = a cos(o w_f) + b sin(o w_f),   B_o = b cos(o w_f) - a sin(o w_f),
@@ -38,6 +38,9 @@
 // Layout choices:
 //   * Codebooks in LDS as fp16, step-major inside a codeword, first half
 //     steps 0-1, second half steps 2-3 (as in the plain multi-step kernel).
+//     With c = 4 and every step served, eight copies, one per lane group, so
+//     that the gathers meet no bank conflicts (a workgroup of 12 waves then
+//     fills a CU's LDS).
 //   * 16 lanes serve a token: lane (hs, g) takes steps {2hs, 2hs+1} and the
 //     chunks D/c/8 * g .. +D/c/8-1, i.e. the 16 transformed channels
 //     16g .. 16g+15, whose index bytes are one aligned 4-byte word (c = 4) or
@@ -79,13 +82,21 @@ __device__ __forceinline__ float dot2_first(h2t_t a, h2t_t b) {
 
 // w16 * S + add, w16 the 16-bit half H of w (op_sel picks the high half):
 // the byte offset of a codeword from an index spread into a 16-bit half
+// (S up to 64 is an inline constant; a larger one sits in a scalar register)
 template <int H, int S>
 __device__ __forceinline__ uint32_t mad_half(uint32_t w, uint32_t add) {
   uint32_t r;
-  if constexpr (H == 0)
-    asm("v_mad_u32_u16 %0, %1, %2, %3" : "=v"(r) : "v"(w), "i"(S), "v"(add));
-  else
-    asm("v_mad_u32_u16 %0, %1, %2, %3 op_sel:[1,0,0,0]" : "=v"(r) : "v"(w), "i"(S), "v"(add));
+  if constexpr (S <= 64) {
+    if constexpr (H == 0)
+      asm("v_mad_u32_u16 %0, %1, %2, %3" : "=v"(r) : "v"(w), "i"(S), "v"(add));
+    else
+      asm("v_mad_u32_u16 %0, %1, %2, %3 op_sel:[1,0,0,0]" : "=v"(r) : "v"(w), "i"(S), "v"(add));
+  } else {
+    if constexpr (H == 0)
+      asm("v_mad_u32_u16 %0, %1, %2, %3" : "=v"(r) : "v"(w), "s"(S), "v"(add));
+    else
+      asm("v_mad_u32_u16 %0, %1, %2, %3 op_sel:[1,0,0,0]" : "=v"(r) : "v"(w), "s"(S), "v"(add));
+  }
   return r;
 }
 
@@ -108,20 +119,33 @@ constexpr int kBufWord3 = 0x00020000;
 // that step for tokens of parity hs, so the 16 lanes of a token pair serve
 // two tokens and no lane computes a step that is not served.
 template <int C, int NSL>
-__global__ __launch_bounds__(kDecodeThreads, NSL == 1 ? 4 : (C == 4 ? 3 : 2)) void decode_tasq_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(tasq_threads(C, NSL), C == 4 && NSL == 2 ? 1 : (NSL == 1 ? 4 : 2)) void decode_tasq_kernel(
+    DecodeArgs a) {
   constexpr int D = 128, HD = 64, TC = 4, G = C * TC, CPT = D / C;
   constexpr int QW = C / 4;           // uint4 per codeword half (two steps)
   constexpr int DW = C / 2;           // dwords per step of a codeword
-  constexpr int LPT = 16, SPW = kWave / LPT, NW = kDecodeThreads / kWave;
-  constexpr int TPI = NW * SPW * (3 - NSL);   // tokens per workgroup iteration (16 or 32)
+  // kRep (c = 4, every step): one workgroup of 12 waves per CU, with eight
+  // copies of each codebook, one per lane group g: row r (512 bytes) holds
+  // the K codeword r of copy j at bytes 32 j .. 32 j + 31 and the V codeword
+  // at 256 + 32 j, so the 16 lanes of a token, which read 8 codewords (a half
+  // each), meet 8 disjoint sets of banks and a gather has no bank conflict
+  // (and the V half of a row stays within an instruction's 16-bit offset).
+  // Otherwise one copy of each codebook, codeword r at 32 QW r, and
+  // workgroups of 4 waves.
+  constexpr bool kRep = C == 4 && NSL == 2;
+  constexpr int NTH = tasq_threads(C, NSL);
+  constexpr int LPT = 16, SPW = kWave / LPT, NW = NTH / kWave;
+  constexpr int TPI = NW * SPW * (3 - NSL);   // tokens per workgroup iteration (48, 16 or 32)
   constexpr int NCK = CPT / 8;        // chunks per lane (4 or 2)
   constexpr int NCH = NCK * C;        // transformed channels per lane (16)
   constexpr int NPR = NCH / 2;        // channel pairs per lane (8)
   constexpr int KWD = NSL * DW;       // codeword dwords per chunk a lane reads
   static_assert(NPR * 8 == kWave, "one channel pair of the table per lane");
-  static_assert((kTFlush * TPI & (kTFlush * TPI - 1)) == 0, "flush period is a power of two");
-  __shared__ __attribute__((aligned(16))) uint4 s_k[256 * 2 * QW];
-  __shared__ __attribute__((aligned(16))) uint4 s_v[256 * 2 * QW];
+  constexpr int kRowQ = kRep ? 32 : 2 * QW;   // uint4 per codebook row in LDS
+  __shared__ __attribute__((aligned(16))) uint4 s_k[256 * kRowQ];
+  __shared__ __attribute__((aligned(16))) uint4 s_v[kRep ? 1 : 256 * kRowQ];   // kRep: rows of s_k
+  uint4* const cbk = s_k;
+  uint4* const cbv = kRep ? s_k + 16 : s_v;
   // fp32 P*V sums.  NSL = 2: the four tokens of a wave iteration (lanes l,
   // l ^ 16, l ^ 32, l ^ 48, which hold the same channels and steps) share
   // one running maximum per step, so their fp16 partials add up before a
@@ -135,7 +159,7 @@ __global__ __launch_bounds__(kDecodeThreads, NSL == 1 ? 4 : (C == 4 ? 3 : 2)) vo
   constexpr bool kShared = NSL == 2;
   constexpr int RW = D + 4;              // merge row: D sums, maximum, sum of weights, padding
   constexpr int kAccQ = NSL * NCH / 4;   // NSL = 1: float4 sums per lane
-  constexpr int kRedQ = NW * TC * RW / 4, kOffQ = TPI * HD / 2, kLaneQ = kShared ? 0 : kAccQ * kDecodeThreads;
+  constexpr int kRedQ = NW * TC * RW / 4, kOffQ = TPI * HD / 2, kLaneQ = kShared ? 0 : kAccQ * NTH;
   constexpr int kBufQ = kRedQ > kOffQ ? (kRedQ > kLaneQ ? kRedQ : kLaneQ) : (kOffQ > kLaneQ ? kOffQ : kLaneQ);
   __shared__ __attribute__((aligned(16))) float4 s_buf[kBufQ];
   __shared__ float s_amax[3][NW];
@@ -144,16 +168,14 @@ __global__ __launch_bounds__(kDecodeThreads, NSL == 1 ? 4 : (C == 4 ? 3 : 2)) vo
   __shared__ uint2 s_pair[NW][NPR * 8];
   float (*s_red)[TC][RW] = reinterpret_cast<float (*)[TC][RW]>(s_buf);
   float2* s_off = reinterpret_cast<float2*>(s_buf);
-  float4* s_acc = s_buf + threadIdx.x;   // NSL = 1: this lane's sums, s_acc[q * kDecodeThreads]
+  float4* s_acc = s_buf + threadIdx.x;   // NSL = 1: this lane's sums, s_acc[q * NTH]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int sl = lane & 15, slot = lane >> 4;
   const int hs = sl >> 3, g = sl & 7;
   // NSL = 2: lanes g and 7 - g of a token's group hold the same two steps
-  // 2hs, 2hs + 1; the lane keeps the softmax of step 2hs + par, and psel
-  // orders its own and its partner's fp16 weight as (step 2hs, step 2hs + 1)
+  // 2hs, 2hs + 1; the lane keeps the softmax of step 2hs + par
   const int par = g >> 2;
-  const uint32_t psel = par ? 0x01000504u : 0x05040100u;
   // NSL = 2: lanes (0, g) and (1, g) of a token read the same pair-table
   // entries, so each reads half of them (its pairs rot .. rot + 3, rot = 4 hs)
   // and takes the other half from the other lane through DPP.  The lane then
@@ -222,7 +244,7 @@ __global__ __launch_bounds__(kDecodeThreads, NSL == 1 ? 4 : (C == 4 ? 3 : 2)) vo
   // offset angles o * w_f, w_f = theta^(-2f/D), in fp32
   {
     const float l2t = log2f(a.theta);
-    for (int x = tid; x < TPI * HD; x += kDecodeThreads) {
+    for (int x = tid; x < TPI * HD; x += NTH) {
       const int o = x / HD, f = x - o * HD;
       const float ang = (float)o * exp2f(-(float)(2 * f) / (float)D * l2t);
       float sn, cs;
@@ -231,9 +253,15 @@ __global__ __launch_bounds__(kDecodeThreads, NSL == 1 ? 4 : (C == 4 ? 3 : 2)) vo
     }
   }
   __syncthreads();
-  mk = fmaxf(fmaxf(s_amax[0][0], s_amax[0][1]), fmaxf(s_amax[0][2], s_amax[0][3]));
-  mv = fmaxf(fmaxf(s_amax[1][0], s_amax[1][1]), fmaxf(s_amax[1][2], s_amax[1][3]));
-  mq = fmaxf(fmaxf(s_amax[2][0], s_amax[2][1]), fmaxf(s_amax[2][2], s_amax[2][3]));
+  mk = s_amax[0][0];
+  mv = s_amax[1][0];
+  mq = s_amax[2][0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) {
+    mk = fmaxf(mk, s_amax[0][w]);
+    mv = fmaxf(mv, s_amax[1][w]);
+    mq = fmaxf(mq, s_amax[2][w]);
+  }
   const int shk = pow2_range_shift(mk, 14), shv = pow2_range_shift(mv, kShared ? kTVLim - 1 : kTVLim), shq = pow2_range_shift(mq, 14);
   {
     const float sk = ldexpf(1.f, -shk), sv = ldexpf(1.f, -shv);
@@ -245,10 +273,26 @@ __global__ __launch_bounds__(kDecodeThreads, NSL == 1 ? 4 : (C == 4 ? 3 : 2)) vo
         kw[m * DW + ip] = pack_h2t(kx[(2 * ip) * TC + m] * sk, kx[(2 * ip + 1) * TC + m] * sk);
         vw[m * DW + ip] = pack_h2t(vx[(2 * ip) * TC + m] * sv, vx[(2 * ip + 1) * TC + m] * sv);
       }
+    if constexpr (kRep) {
+      if (r < 256) {
+        // the eight copies, stored in a lane-rotated order to spread the
+        // stores over the banks
 #pragma unroll
-    for (int u = 0; u < 2 * QW; ++u) {
-      s_k[r * 2 * QW + u] = make_uint4(kw[4 * u], kw[4 * u + 1], kw[4 * u + 2], kw[4 * u + 3]);
-      s_v[r * 2 * QW + u] = make_uint4(vw[4 * u], vw[4 * u + 1], vw[4 * u + 2], vw[4 * u + 3]);
+        for (int j0 = 0; j0 < 8; ++j0) {
+          const int j = (j0 + r) & 7;
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            cbk[r * kRowQ + 2 * j + u] = make_uint4(kw[4 * u], kw[4 * u + 1], kw[4 * u + 2], kw[4 * u + 3]);
+            cbv[r * kRowQ + 2 * j + u] = make_uint4(vw[4 * u], vw[4 * u + 1], vw[4 * u + 2], vw[4 * u + 3]);
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < 2 * QW; ++u) {
+        cbk[r * kRowQ + u] = make_uint4(kw[4 * u], kw[4 * u + 1], kw[4 * u + 2], kw[4 * u + 3]);
+        cbv[r * kRowQ + u] = make_uint4(vw[4 * u], vw[4 * u + 1], vw[4 * u + 2], vw[4 * u + 3]);
+      }
     }
   }
 
@@ -318,7 +362,7 @@ __global__ __launch_bounds__(kDecodeThreads, NSL == 1 ? 4 : (C == 4 ? 3 : 2)) vo
     reinterpret_cast<float4*>(s_mine)[1] = make_float4(0.f, 0.f, 0.f, 0.f);
   } else {
 #pragma unroll
-    for (int q = 0; q < kAccQ; ++q) s_acc[q * kDecodeThreads] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int q = 0; q < kAccQ; ++q) s_acc[q * NTH] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
 
   int nb = a.N;
@@ -452,10 +496,10 @@ __global__ __launch_bounds__(kDecodeThreads, NSL == 1 ? 4 : (C == 4 ? 3 : 2)) vo
 #pragma unroll
       for (int q = 0; q < kAccQ; ++q) {
         const int ml = q / (NCH / 4), p0 = 2 * (q % (NCH / 4));
-        float4 v = s_acc[q * kDecodeThreads];
+        float4 v = s_acc[q * NTH];
         add_f16x2(acc16[ml][p0], v.x, v.y);
         add_f16x2(acc16[ml][p0 + 1], v.z, v.w);
-        s_acc[q * kDecodeThreads] = v;
+        s_acc[q * NTH] = v;
       }
     }
 #pragma unroll
@@ -506,7 +550,11 @@ __global__ __launch_bounds__(kDecodeThreads, NSL == 1 ? 4 : (C == 4 ? 3 : 2)) vo
       lrow[0] += pr;
       const uint32_t p16 = __builtin_bit_cast(uint16_t, (_Float16)pr);
       const uint32_t o16 = __builtin_amdgcn_mov_dpp(p16, 0x141, 0xF, 0xF, true);
-      const h2t_t pp = as_h2t(__builtin_amdgcn_perm(o16, p16, psel));   // (step 2hs, step 2hs + 1)
+      // (own, partner's) is the order (step 2hs, step 2hs + 1) for lanes
+      // g < 4; lanes g >= 4 (banks 1 and 3 of each row of 16) take their
+      // partner's word instead
+      const uint32_t x = __builtin_amdgcn_perm(o16, p16, 0x05040100u);
+      const h2t_t pp = as_h2t(__builtin_amdgcn_update_dpp(x, x, 0x141, 0xF, 0xA, false));
       const h2t_t p0 = {pp.x, pp.x}, p1 = {pp.y, pp.y};
 #pragma unroll
       for (int p = 0; p < NPR; ++p) {
@@ -521,7 +569,7 @@ __global__ __launch_bounds__(kDecodeThreads, NSL == 1 ? 4 : (C == 4 ? 3 : 2)) vo
         const h2t_t a2 = {(_Float16)alpha, (_Float16)alpha};
         lrow[0] *= alpha;
 #pragma unroll
-        for (int q = 0; q < NCH / 4; ++q) rescale(&s_acc[q * kDecodeThreads], alpha);
+        for (int q = 0; q < NCH / 4; ++q) rescale(&s_acc[q * NTH], alpha);
 #pragma unroll
         for (int p = 0; p < NPR; ++p) acc16[0][p] = __builtin_bit_cast(uint32_t, as_h2t(acc16[0][p]) * a2);
         mr[0] = sc[0] * sgm;
@@ -597,7 +645,10 @@ __global__ __launch_bounds__(kDecodeThreads, NSL == 1 ? 4 : (C == 4 ? 3 : 2)) vo
   };
   const uint32_t isel0 = bsel(rotc & 3, (2 + rotc) & 3), isel1 = bsel((1 + rotc) & 3, (3 + rotc) & 3);
   const uint32_t isel = bsel(kbit / 8 + (rotc & 1), kbit / 8 + ((1 + rotc) & 1));
-  const uint32_t hsb = hs * QW * 16;   // byte offset of half hs inside a codeword
+  // byte offset of the lane's half inside a codeword row: half hs of its
+  // group's copy (kRep) or of the one copy
+  const uint32_t hsb = kRep ? g * 32 + hs * 16 : hs * QW * 16;
+  constexpr int kRow = kRowQ * 16;   // bytes per codeword row in LDS
   // index rows of this (batch, kv-head, block) and sigma of this batch entry;
   // a lane past the split's last token reads a later row or 0 (unused)
   const __amdgpu_buffer_rsrc_t kid_rs =
@@ -627,7 +678,7 @@ __global__ __launch_bounds__(kDecodeThreads, NSL == 1 ? 4 : (C == 4 ? 3 : 2)) vo
     x.row = load_row(P0 + (base < n_tok ? base : 0));         // a row of this split's tokens
     return x;
   };
-  auto iteration = [&](int base, const Ahead& cur) {
+  auto iteration = [&](int base, int it, const Ahead& cur) {
     const bool valid = my < n_tok - base;   // one compare with a scalar bound
     // LDS order: the pair table, then the K gathers, then the V gathers, so
     // the scores can start while the V gathers are in flight
@@ -664,19 +715,19 @@ __global__ __launch_bounds__(kDecodeThreads, NSL == 1 ? 4 : (C == 4 ? 3 : 2)) vo
       auto offset = [&](const uint32_t (&h)[2], auto kc) {
         constexpr int k = decltype(kc)::value;
         constexpr int wsel = C == 4 ? (k & 1) : 0, hsel = C == 4 ? (k >> 1) : k;
-        return mad_half<hsel, 32 * QW>(h[wsel], hsb);
+        return mad_half<hsel, kRow>(h[wsel], hsb);
       };
-      gather(s_k, offset(kh, std::integral_constant<int, 0>{}), Kw[0]);
-      gather(s_k, offset(kh, std::integral_constant<int, 1>{}), Kw[1]);
+      gather(cbk, offset(kh, std::integral_constant<int, 0>{}), Kw[0]);
+      gather(cbk, offset(kh, std::integral_constant<int, 1>{}), Kw[1]);
       if constexpr (NCK == 4) {
-        gather(s_k, offset(kh, std::integral_constant<int, 2>{}), Kw[2]);
-        gather(s_k, offset(kh, std::integral_constant<int, 3>{}), Kw[3]);
+        gather(cbk, offset(kh, std::integral_constant<int, 2>{}), Kw[2]);
+        gather(cbk, offset(kh, std::integral_constant<int, 3>{}), Kw[3]);
       }
-      gather(s_v, offset(vh, std::integral_constant<int, 0>{}), Vw[0]);
-      gather(s_v, offset(vh, std::integral_constant<int, 1>{}), Vw[1]);
+      gather(cbv, offset(vh, std::integral_constant<int, 0>{}), Vw[0]);
+      gather(cbv, offset(vh, std::integral_constant<int, 1>{}), Vw[1]);
       if constexpr (NCK == 4) {
-        gather(s_v, offset(vh, std::integral_constant<int, 2>{}), Vw[2]);
-        gather(s_v, offset(vh, std::integral_constant<int, 3>{}), Vw[3]);
+        gather(cbv, offset(vh, std::integral_constant<int, 2>{}), Vw[2]);
+        gather(cbv, offset(vh, std::integral_constant<int, 3>{}), Vw[3]);
       }
     } else {
       // the served step's DW dwords inside its half
@@ -691,9 +742,9 @@ __global__ __launch_bounds__(kDecodeThreads, NSL == 1 ? 4 : (C == 4 ? 3 : 2)) vo
         }
       };
 #pragma unroll
-      for (int k = 0; k < NCK; ++k) gather(s_k, __builtin_amdgcn_ubfe(cur.kw, kbit + 8 * k, 8), Kw[k]);
+      for (int k = 0; k < NCK; ++k) gather(cbk, __builtin_amdgcn_ubfe(cur.kw, kbit + 8 * k, 8), Kw[k]);
 #pragma unroll
-      for (int k = 0; k < NCK; ++k) gather(s_v, __builtin_amdgcn_ubfe(cur.vw, kbit + 8 * k, 8), Vw[k]);
+      for (int k = 0; k < NCK; ++k) gather(cbv, __builtin_amdgcn_ubfe(cur.vw, kbit + 8 * k, 8), Vw[k]);
     }
     __builtin_amdgcn_sched_barrier(0);   // keep every gather issued ahead of the arithmetic
     h2t_t s16 = as_h2t(cur.sg);
@@ -701,19 +752,19 @@ __global__ __launch_bounds__(kDecodeThreads, NSL == 1 ? 4 : (C == 4 ? 3 : 2)) vo
     float sc[NSL];
     scores(cs2, sn2, Kw, sc);
     accumulate(sc, s16, Vw, valid);
-    // every kTFlush iterations (base is the same in every lane)
-    if ((base & (kTFlush * TPI - 1)) == (kTFlush - 1) * TPI) flush();
+    // every kTFlush iterations (it is the same in every lane)
+    if ((it & (kTFlush - 1)) == kTFlush - 1) flush();
   };
   // two iterations per trip, loading into alternate register sets, so that
   // nothing loaded ahead is copied from one set to the other
   if (n_tok > 0) {
     Ahead x0 = load_ahead(0), x1;
-    for (int base = 0;; base += 2 * TPI) {
+    for (int base = 0, it = 0;; base += 2 * TPI, it += 2) {
       x1 = load_ahead(base + TPI);
-      iteration(base, x0);
+      iteration(base, it, x0);
       if (base + TPI >= n_tok) break;
       x0 = load_ahead(base + 2 * TPI);
-      iteration(base + TPI, x1);
+      iteration(base + TPI, it + 1, x1);
       if (base + 2 * TPI >= n_tok) break;
     }
   }
@@ -731,7 +782,7 @@ __global__ __launch_bounds__(kDecodeThreads, NSL == 1 ? 4 : (C == 4 ? 3 : 2)) vo
     float acc[NSL][NCH];
 #pragma unroll
     for (int q = 0; q < kAccQ; ++q) {
-      const float4 v = s_acc[q * kDecodeThreads];
+      const float4 v = s_acc[q * NTH];
       const int ml = q / (NCH / 4), j0 = 4 * (q % (NCH / 4));
       acc[ml][j0] = v.x;
       acc[ml][j0 + 1] = v.y;
@@ -779,7 +830,7 @@ __global__ __launch_bounds__(kDecodeThreads, NSL == 1 ? 4 : (C == 4 ? 3 : 2)) vo
   }
   __syncthreads();
   const float osc = ldexpf(1.f, shv);
-  for (int x = tid; x < TC * D; x += kDecodeThreads) {
+  for (int x = tid; x < TC * D; x += NTH) {
     const int m = x / D, d = x - m * D;
     const int t = beta * TC + m;
     if (t < t_lo || t >= t_hi) continue;
@@ -806,13 +857,13 @@ hipError_t launch_decode_tasq(int G, bool one, const DecodeArgs& a, hipStream_t 
   dim3 grid(a.n_split, a.Hq, a.B * a.n_blk_serv);
   if (one && a.n_steps != 1) return hipErrorInvalidValue;
   if (G == 16 && one)
-    hipLaunchKernelGGL((decode_tasq_kernel<4, 1>), grid, dim3(kDecodeThreads), 0, s, a);
+    hipLaunchKernelGGL((decode_tasq_kernel<4, 1>), grid, dim3(tasq_threads(4, 1)), 0, s, a);
   else if (G == 16)
-    hipLaunchKernelGGL((decode_tasq_kernel<4, 2>), grid, dim3(kDecodeThreads), 0, s, a);
+    hipLaunchKernelGGL((decode_tasq_kernel<4, 2>), grid, dim3(tasq_threads(4, 2)), 0, s, a);
   else if (G == 32 && one)
-    hipLaunchKernelGGL((decode_tasq_kernel<8, 1>), grid, dim3(kDecodeThreads), 0, s, a);
+    hipLaunchKernelGGL((decode_tasq_kernel<8, 1>), grid, dim3(tasq_threads(8, 1)), 0, s, a);
   else if (G == 32)
-    hipLaunchKernelGGL((decode_tasq_kernel<8, 2>), grid, dim3(kDecodeThreads), 0, s, a);
+    hipLaunchKernelGGL((decode_tasq_kernel<8, 2>), grid, dim3(tasq_threads(8, 2)), 0, s, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

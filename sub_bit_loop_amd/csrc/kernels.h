@@ -212,6 +212,10 @@ hipError_t launch_decode_gqa(int G, int hpw, const DecodeArgs& a, hipStream_t s)
 hipError_t launch_decode_tasq(int G, bool one, const DecodeArgs& a, hipStream_t s);
 
 constexpr int kDecodeThreads = 256;
+// threads per workgroup of decode_tasq_kernel<C, NSL>: c = 4 with every step
+// of the block served runs one workgroup of 12 waves per CU (its codebook
+// copies fill the LDS), the other variants workgroups of 4 waves
+constexpr int tasq_threads(int C, int NSL) { return C == 4 && NSL == 2 ? 768 : kDecodeThreads; }
 constexpr int kEncodeThreads = 256;
 constexpr int kEncodeTokens = 128;  // tokens per encode workgroup
 
