@@ -61,8 +61,6 @@
 #include "common.h"
 #include "kernels.h"
 
-#include <type_traits>
-
 namespace loopvq {
 
 namespace {
@@ -125,11 +123,12 @@ __global__ __launch_bounds__(tasq_threads(C, NSL), C == 4 && NSL == 2 ? 1 : (NSL
   constexpr int QW = C / 4;           // uint4 per codeword half (two steps)
   constexpr int DW = C / 2;           // dwords per step of a codeword
   // kRep (c = 4, every step): one workgroup of 12 waves per CU, with eight
-  // copies of each codebook, one per lane group g: row r (512 bytes) holds
-  // the K codeword r of copy j at bytes 32 j .. 32 j + 31 and the V codeword
-  // at 256 + 32 j, so the 16 lanes of a token, which read 8 codewords (a half
-  // each), meet 8 disjoint sets of banks and a gather has no bank conflict
-  // (and the V half of a row stays within an instruction's 16-bit offset).
+  // copies of each codebook, one per lane group g: row r (256 bytes) holds
+  // codeword r of copy j at bytes 32 j .. 32 j + 31, so the 16 lanes of a
+  // token, which read 8 codewords (a half each), meet 8 disjoint sets of
+  // banks and a gather has no bank conflict.  The V rows follow the K rows
+  // 64 KB further on, so the byte offset of a codeword half, idx * 256 +
+  // 32 g + 16 hs (+ 65536 for V), is assembled by one byte permute.
   // Otherwise one copy of each codebook, codeword r at 32 QW r, and
   // workgroups of 4 waves.
   constexpr bool kRep = C == 4 && NSL == 2;
@@ -141,11 +140,11 @@ __global__ __launch_bounds__(tasq_threads(C, NSL), C == 4 && NSL == 2 ? 1 : (NSL
   constexpr int NPR = NCH / 2;        // channel pairs per lane (8)
   constexpr int KWD = NSL * DW;       // codeword dwords per chunk a lane reads
   static_assert(NPR * 8 == kWave, "one channel pair of the table per lane");
-  constexpr int kRowQ = kRep ? 32 : 2 * QW;   // uint4 per codebook row in LDS
-  __shared__ __attribute__((aligned(16))) uint4 s_k[256 * kRowQ];
-  __shared__ __attribute__((aligned(16))) uint4 s_v[kRep ? 1 : 256 * kRowQ];   // kRep: rows of s_k
+  constexpr int kRowQ = kRep ? 16 : 2 * QW;   // uint4 per codebook row in LDS
+  __shared__ __attribute__((aligned(16))) uint4 s_k[256 * kRowQ * (kRep ? 2 : 1)];
+  __shared__ __attribute__((aligned(16))) uint4 s_v[kRep ? 1 : 256 * kRowQ];   // kRep: the second half of s_k
   uint4* const cbk = s_k;
-  uint4* const cbv = kRep ? s_k + 16 : s_v;
+  uint4* const cbv = kRep ? s_k + 256 * kRowQ : s_v;
   // fp32 P*V sums.  NSL = 2: the four tokens of a wave iteration (lanes l,
   // l ^ 16, l ^ 32, l ^ 48, which hold the same channels and steps) share
   // one running maximum per step, so their fp16 partials add up before a
@@ -176,13 +175,6 @@ __global__ __launch_bounds__(tasq_threads(C, NSL), C == 4 && NSL == 2 ? 1 : (NSL
   // NSL = 2: lanes g and 7 - g of a token's group hold the same two steps
   // 2hs, 2hs + 1; the lane keeps the softmax of step 2hs + par
   const int par = g >> 2;
-  // NSL = 2: lanes (0, g) and (1, g) of a token read the same pair-table
-  // entries, so each reads half of them (its pairs rot .. rot + 3, rot = 4 hs)
-  // and takes the other half from the other lane through DPP.  The lane then
-  // keeps its channel pairs in slot order, slot s holding pair (s + rot) mod 8,
-  // for the coefficients, the gathered codeword chunks and the P*V sums alike.
-  const int rot = kShared ? 4 * hs : 0;
-  auto pair_of = [&](int s) { return (s + rot) & (NPR - 1); };
   // this lane's token offset o within an iteration
   const int my = NSL == 2 ? wave * SPW + slot : (wave * SPW + slot) * 2 + hs;
   const int split = blockIdx.x;
@@ -306,8 +298,7 @@ __global__ __launch_bounds__(tasq_threads(C, NSL), C == 4 && NSL == 2 ? 1 : (NSL
     float2 oc[NCH];
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
-      // pair slot j / 2; the index stays in bounds for any input
-      const int o = a.perm[h * D + NCH * g + 2 * pair_of(j >> 1) + (j & 1)] & (D - 1);
+      const int o = a.perm[h * D + NCH * g + j] & (D - 1);   // stays in bounds for any input
       och[j] = o;
       rw[j] = 1.f / a.w[h * D + o];
       oc[j] = s_off[my * HD + (o & (HD - 1))];
@@ -353,10 +344,10 @@ __global__ __launch_bounds__(tasq_threads(C, NSL), C == 4 && NSL == 2 ? 1 : (NSL
     for (int p = 0; p < NPR; ++p) acc16[ml][p] = 0u;
   __syncthreads();   // codebooks staged; the offset table is no longer read
   // NSL = 2: the two float4 of the wave's sums that this lane adds into at a
-  // flush: row slot of the wave takes step 2hs + (slot >> 1), pair slots
-  // 4(slot & 1) .. +3, i.e. channels 16g + 8((slot & 1) ^ hs) .. +7 (the
-  // partials the cross-row reduction leaves in this lane)
-  float* const s_mine = &s_red[wave][2 * hs + (slot >> 1)][NCH * g + 8 * ((slot & 1) ^ hs)];
+  // flush: row slot of the wave takes step 2hs + (slot >> 1), channels
+  // 16g + 8(slot & 1) .. +7 (the partials the cross-row reduction leaves
+  // in this lane)
+  float* const s_mine = &s_red[wave][2 * hs + (slot >> 1)][NCH * g + 8 * (slot & 1)];
   if constexpr (kShared) {
     reinterpret_cast<float4*>(s_mine)[0] = make_float4(0.f, 0.f, 0.f, 0.f);
     reinterpret_cast<float4*>(s_mine)[1] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -412,24 +403,11 @@ __global__ __launch_bounds__(tasq_threads(C, NSL), C == 4 && NSL == 2 ? 1 : (NSL
   auto pair_table = [&](uint2 row, uint32_t (&cs2)[NPR], uint32_t (&sn2)[NPR]) {
     s_pair[wave][lane] = row;
     __builtin_amdgcn_wave_barrier();
-    if constexpr (kShared) {
-      // slots s < 4 from the table, s + 4 from lane (1 - hs, g), 8 lanes over
-      // in the same row of 16 (a row rotation by 8)
 #pragma unroll
-      for (int q = 0; q < NPR / 2; ++q) {
-        const uint2 e = s_pair[wave][8 * (rot + q) + g];
-        cs2[q] = e.x;
-        sn2[q] = e.y;
-        cs2[q + NPR / 2] = __builtin_amdgcn_mov_dpp(e.x, 0x128, 0xF, 0xF, true);
-        sn2[q + NPR / 2] = __builtin_amdgcn_mov_dpp(e.y, 0x128, 0xF, 0xF, true);
-      }
-    } else {
-#pragma unroll
-      for (int q = 0; q < NPR; ++q) {
-        const uint2 e = s_pair[wave][8 * q + g];
-        cs2[q] = e.x;
-        sn2[q] = e.y;
-      }
+    for (int p = 0; p < NPR; ++p) {
+      const uint2 e = s_pair[wave][8 * p + g];
+      cs2[p] = e.x;
+      sn2[p] = e.y;
     }
   };
   // Dot products of the lane's steps (summed over the 8 lanes of the
@@ -608,10 +586,10 @@ __global__ __launch_bounds__(tasq_threads(C, NSL), C == 4 && NSL == 2 ? 1 : (NSL
           float z[2];
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
-            const int o = a.perm[h * D + NCH * g + 2 * pair_of(p) + u] & (D - 1);
+            const int o = a.perm[h * D + NCH * g + 2 * p + u] & (D - 1);
             z[u] = bf16_to_f32(kr[o]) * a.w[h * D + o] * ksc;
           }
-          const uint32_t vv = *reinterpret_cast<const uint32_t*>(vr + NCH * g + 2 * pair_of(p));
+          const uint32_t vv = *reinterpret_cast<const uint32_t*>(vr + NCH * g + 2 * p);
           Kw[p / DW][ml * DW + p % DW] = pack_h2t(z[0], z[1]);
           Vw[p / DW][ml * DW + p % DW] = pack_h2t(bf16lo(vv) * vsc, bf16hi(vv) * vsc);
         }
@@ -634,21 +612,13 @@ __global__ __launch_bounds__(tasq_threads(C, NSL), C == 4 && NSL == 2 ? 1 : (NSL
   // word of the index row holding this lane's index bytes, and their bit offset
   const int kwo = C == 4 ? g : (g >> 1);
   const int kbit = C == 4 ? 0 : 16 * (g & 1);
-  // Byte selectors spreading the lane's index bytes into 16-bit halves in
-  // chunk-slot order: chunk slot k holds chunk (k + rotc) mod NCK, the chunk
-  // of the pairs its slots hold.  c = 4: isel0 takes slots 0, 2, isel1 slots
-  // 1, 3; c = 8: isel takes the lane's two bytes (of its 4-byte word) for
-  // slots 0, 1.
-  const int rotc = rot * NCK / NPR;
-  auto bsel = [&](int k0, int k1) {
-    return (uint32_t)k0 | 0x0C00u | (uint32_t)k1 << 16 | 0x0C000000u;
-  };
-  const uint32_t isel0 = bsel(rotc & 3, (2 + rotc) & 3), isel1 = bsel((1 + rotc) & 3, (3 + rotc) & 3);
-  const uint32_t isel = bsel(kbit / 8 + (rotc & 1), kbit / 8 + ((1 + rotc) & 1));
+  // c = 8: byte selector spreading the lane's two index bytes into 16-bit halves
+  const uint32_t isel = (uint32_t)(kbit / 8) | 0x0C00u | (uint32_t)(kbit / 8 + 1) << 16 | 0x0C000000u;
   // byte offset of the lane's half inside a codeword row: half hs of its
   // group's copy (kRep) or of the one copy
   const uint32_t hsb = kRep ? g * 32 + hs * 16 : hs * QW * 16;
   constexpr int kRow = kRowQ * 16;   // bytes per codeword row in LDS
+  const uint32_t hsbv = hsb + 65536u;   // kRep: the V rows follow 64 KB on
   // index rows of this (batch, kv-head, block) and sigma of this batch entry;
   // a lane past the split's last token reads a later row or 0 (unused)
   const __amdgpu_buffer_rsrc_t kid_rs =
@@ -687,23 +657,24 @@ __global__ __launch_bounds__(tasq_threads(C, NSL), C == 4 && NSL == 2 ? 1 : (NSL
     uint32_t Kw[NCK][KWD], Vw[NCK][KWD];
     // codeword dwords of the lane's steps: the half hs (both steps), or the
     // served step's dwords
-    if constexpr (NSL == 2) {
-      // The lane's index bytes are spread into 16-bit halves of two words
-      // (c = 4: the bytes of chunk slots 0, 2 and 1, 3; c = 8: its two bytes
-      // in one word), so each codeword's byte offset, idx * 32 QW + the half's
-      // 16 QW hs, is one multiply-add on a half.
-      auto spread = [&](uint32_t w, uint32_t (&h)[2]) {
-        if constexpr (C == 4) {
-          h[0] = __builtin_amdgcn_perm(w, w, isel0);
-          h[1] = __builtin_amdgcn_perm(w, w, isel1);
-        } else {
-          h[0] = __builtin_amdgcn_perm(w, w, isel);
-          h[1] = 0u;
-        }
+    if constexpr (kRep) {
+      // offset of the codeword half: bytes (hsb byte 0, index byte k, hsb
+      // byte 2, 0), hsbv for V
+      auto gather = [&](uint32_t w, uint32_t base, int k, uint32_t (&out)[KWD]) {
+        const uint32_t o = __builtin_amdgcn_perm(w, base, 0x0C020000u | (uint32_t)(4 + k) << 8);
+        const uint4 y = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(s_k) + o);
+        out[0] = y.x; out[1] = y.y; out[2] = y.z; out[3] = y.w;
       };
-      uint32_t kh[2], vh[2];
-      spread(cur.kw, kh);
-      spread(cur.vw, vh);
+#pragma unroll
+      for (int k = 0; k < NCK; ++k) gather(cur.kw, hsb, k, Kw[k]);
+#pragma unroll
+      for (int k = 0; k < NCK; ++k) gather(cur.vw, hsbv, k, Vw[k]);
+    } else if constexpr (NSL == 2) {
+      // (c = 8) The lane's two index bytes are spread into the 16-bit halves
+      // of one word, so each codeword's byte offset, idx * 32 QW + the half's
+      // 16 QW hs, is one multiply-add on a half.
+      const uint32_t kh[2] = {__builtin_amdgcn_perm(cur.kw, cur.kw, isel), 0u};
+      const uint32_t vh[2] = {__builtin_amdgcn_perm(cur.vw, cur.vw, isel), 0u};
       auto gather = [&](const uint4* cb, uint32_t off, uint32_t (&out)[KWD]) {
         const uint4* x = reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(cb) + off);
 #pragma unroll
@@ -712,23 +683,11 @@ __global__ __launch_bounds__(tasq_threads(C, NSL), C == 4 && NSL == 2 ? 1 : (NSL
           out[4 * u] = y.x; out[4 * u + 1] = y.y; out[4 * u + 2] = y.z; out[4 * u + 3] = y.w;
         }
       };
-      auto offset = [&](const uint32_t (&h)[2], auto kc) {
-        constexpr int k = decltype(kc)::value;
-        constexpr int wsel = C == 4 ? (k & 1) : 0, hsel = C == 4 ? (k >> 1) : k;
-        return mad_half<hsel, kRow>(h[wsel], hsb);
-      };
-      gather(cbk, offset(kh, std::integral_constant<int, 0>{}), Kw[0]);
-      gather(cbk, offset(kh, std::integral_constant<int, 1>{}), Kw[1]);
-      if constexpr (NCK == 4) {
-        gather(cbk, offset(kh, std::integral_constant<int, 2>{}), Kw[2]);
-        gather(cbk, offset(kh, std::integral_constant<int, 3>{}), Kw[3]);
-      }
-      gather(cbv, offset(vh, std::integral_constant<int, 0>{}), Vw[0]);
-      gather(cbv, offset(vh, std::integral_constant<int, 1>{}), Vw[1]);
-      if constexpr (NCK == 4) {
-        gather(cbv, offset(vh, std::integral_constant<int, 2>{}), Vw[2]);
-        gather(cbv, offset(vh, std::integral_constant<int, 3>{}), Vw[3]);
-      }
+      static_assert(NCK == 2, "the spread form serves c = 8");
+      gather(cbk, mad_half<0, kRow>(kh[0], hsb), Kw[0]);
+      gather(cbk, mad_half<1, kRow>(kh[0], hsb), Kw[1]);
+      gather(cbv, mad_half<0, kRow>(vh[0], hsb), Vw[0]);
+      gather(cbv, mad_half<1, kRow>(vh[0], hsb), Vw[1]);
     } else {
       // the served step's DW dwords inside its half
       auto gather = [&](const uint4* cb, uint32_t idx, uint32_t (&out)[KWD]) {
