@@ -117,7 +117,7 @@ constexpr int kBufWord3 = 0x00020000;
 // that step for tokens of parity hs, so the 16 lanes of a token pair serve
 // two tokens and no lane computes a step that is not served.
 template <int C, int NSL>
-__global__ __launch_bounds__(tasq_threads(C, NSL), C == 4 && NSL == 2 ? 1 : (NSL == 1 ? 4 : 2)) void decode_tasq_kernel(
+__global__ __launch_bounds__(tasq_threads(C, NSL), C == 4 ? 1 : (NSL == 1 ? 4 : 2)) void decode_tasq_kernel(
     DecodeArgs a) {
   constexpr int D = 128, HD = 64, TC = 4, G = C * TC, CPT = D / C;
   constexpr int QW = C / 4;           // uint4 per codeword half (two steps)
@@ -129,22 +129,30 @@ __global__ __launch_bounds__(tasq_threads(C, NSL), C == 4 && NSL == 2 ? 1 : (NSL
   // banks and a gather has no bank conflict.  The V rows follow the K rows
   // 64 KB further on, so the byte offset of a codeword half, idx * 256 +
   // 32 g + 16 hs (+ 65536 for V), is assembled by one byte permute.
-  // Otherwise one copy of each codebook, codeword r at 32 QW r, and
+  // kSlice (c = 4, one served step m0): one workgroup of 16 waves per CU,
+  // whose LDS holds only step m0's 8-byte slice of each codeword, 16 copies:
+  // row r (256 bytes) holds the K slice of copy j at bytes 8 j and the V
+  // slice at 128 + 8 j, and lane l reads copy l mod 16, so the 16 lanes of a
+  // token pair meet disjoint banks; a slice's offset, idx * 256 + 8 (l mod
+  // 16) (+ 128 for V), is again one byte permute.
+  // Otherwise (c = 8) one copy of each codebook, codeword r at 32 QW r, and
   // workgroups of 4 waves.
   constexpr bool kRep = C == 4 && NSL == 2;
+  constexpr bool kSlice = C == 4 && NSL == 1;
   constexpr int NTH = tasq_threads(C, NSL);
   constexpr int LPT = 16, SPW = kWave / LPT, NW = NTH / kWave;
-  constexpr int TPI = NW * SPW * (3 - NSL);   // tokens per workgroup iteration (48, 16 or 32)
+  constexpr int TPI = NW * SPW * (3 - NSL);   // tokens per workgroup iteration (48, 128, 16 or 32)
   constexpr int NCK = CPT / 8;        // chunks per lane (4 or 2)
   constexpr int NCH = NCK * C;        // transformed channels per lane (16)
   constexpr int NPR = NCH / 2;        // channel pairs per lane (8)
   constexpr int KWD = NSL * DW;       // codeword dwords per chunk a lane reads
   static_assert(NPR * 8 == kWave, "one channel pair of the table per lane");
-  constexpr int kRowQ = kRep ? 16 : 2 * QW;   // uint4 per codebook row in LDS
+  constexpr int kRowQ = kRep || kSlice ? 16 : 2 * QW;   // uint4 per codebook row in LDS
   __shared__ __attribute__((aligned(16))) uint4 s_k[256 * kRowQ * (kRep ? 2 : 1)];
-  __shared__ __attribute__((aligned(16))) uint4 s_v[kRep ? 1 : 256 * kRowQ];   // kRep: the second half of s_k
+  // kRep: the V rows are the second half of s_k; kSlice: the second half of each row
+  __shared__ __attribute__((aligned(16))) uint4 s_v[kRep || kSlice ? 1 : 256 * kRowQ];
   uint4* const cbk = s_k;
-  uint4* const cbv = kRep ? s_k + 256 * kRowQ : s_v;
+  uint4* const cbv = kRep ? s_k + 256 * kRowQ : (kSlice ? s_k + 8 : s_v);
   // fp32 P*V sums.  NSL = 2: the four tokens of a wave iteration (lanes l,
   // l ^ 16, l ^ 32, l ^ 48, which hold the same channels and steps) share
   // one running maximum per step, so their fp16 partials add up before a
@@ -277,6 +285,21 @@ __global__ __launch_bounds__(tasq_threads(C, NSL), C == 4 && NSL == 2 ? 1 : (NSL
             cbk[r * kRowQ + 2 * j + u] = make_uint4(kw[4 * u], kw[4 * u + 1], kw[4 * u + 2], kw[4 * u + 3]);
             cbv[r * kRowQ + 2 * j + u] = make_uint4(vw[4 * u], vw[4 * u + 1], vw[4 * u + 2], vw[4 * u + 3]);
           }
+        }
+      }
+    } else if constexpr (kSlice) {
+      if (r < 256) {
+        // step m0's slice of codeword r (DW = 2 dwords), sixteen copies
+        auto pick = [&](const uint32_t (&x)[2 * C], int ip) {
+          return m0 == 0 ? x[ip] : m0 == 1 ? x[DW + ip] : m0 == 2 ? x[2 * DW + ip] : x[3 * DW + ip];
+        };
+        const uint2 ks = make_uint2(pick(kw, 0), pick(kw, 1)), vs = make_uint2(pick(vw, 0), pick(vw, 1));
+        uint2* row = reinterpret_cast<uint2*>(s_k + r * kRowQ);
+#pragma unroll
+        for (int j0 = 0; j0 < 16; ++j0) {
+          const int j = (j0 + r) & 15;
+          row[j] = ks;
+          row[16 + j] = vs;
         }
       }
     } else {
@@ -619,6 +642,7 @@ __global__ __launch_bounds__(tasq_threads(C, NSL), C == 4 && NSL == 2 ? 1 : (NSL
   const uint32_t hsb = kRep ? g * 32 + hs * 16 : hs * QW * 16;
   constexpr int kRow = kRowQ * 16;   // bytes per codeword row in LDS
   const uint32_t hsbv = hsb + 65536u;   // kRep: the V rows follow 64 KB on
+  const uint32_t slb = 8u * sl;          // kSlice: the lane's copy of a K slice
   // index rows of this (batch, kv-head, block) and sigma of this batch entry;
   // a lane past the split's last token reads a later row or 0 (unused)
   const __amdgpu_buffer_rsrc_t kid_rs =
@@ -669,6 +693,18 @@ __global__ __launch_bounds__(tasq_threads(C, NSL), C == 4 && NSL == 2 ? 1 : (NSL
       for (int k = 0; k < NCK; ++k) gather(cur.kw, hsb, k, Kw[k]);
 #pragma unroll
       for (int k = 0; k < NCK; ++k) gather(cur.vw, hsbv, k, Vw[k]);
+    } else if constexpr (kSlice) {
+      // offset of the step slice: bytes (8 (lane mod 16) (+ 128 for V), index
+      // byte k, 0, 0)
+      auto gather = [&](uint32_t w, uint32_t base, int k, uint32_t (&out)[KWD]) {
+        const uint32_t o = __builtin_amdgcn_perm(w, base, 0x0C0C0000u | (uint32_t)(4 + k) << 8);
+        const uint2 y = *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(s_k) + o);
+        out[0] = y.x; out[1] = y.y;
+      };
+#pragma unroll
+      for (int k = 0; k < NCK; ++k) gather(cur.kw, slb, k, Kw[k]);
+#pragma unroll
+      for (int k = 0; k < NCK; ++k) gather(cur.vw, slb + 128u, k, Vw[k]);
     } else if constexpr (NSL == 2) {
       // (c = 8) The lane's two index bytes are spread into the 16-bit halves
       // of one word, so each codeword's byte offset, idx * 32 QW + the half's

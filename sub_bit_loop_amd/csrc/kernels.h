@@ -212,10 +212,10 @@ hipError_t launch_decode_gqa(int G, int hpw, const DecodeArgs& a, hipStream_t s)
 hipError_t launch_decode_tasq(int G, bool one, const DecodeArgs& a, hipStream_t s);
 
 constexpr int kDecodeThreads = 256;
-// threads per workgroup of decode_tasq_kernel<C, NSL>: c = 4 with every step
-// of the block served runs one workgroup of 12 waves per CU (its codebook
-// copies fill the LDS), the other variants workgroups of 4 waves
-constexpr int tasq_threads(int C, int NSL) { return C == 4 && NSL == 2 ? 768 : kDecodeThreads; }
+// threads per workgroup of decode_tasq_kernel<C, NSL>: at c = 4 one workgroup
+// per CU, whose codebook copies fill most of the LDS (12 waves with every step
+// of the block served, 16 with one served step); at c = 8 workgroups of 4 waves
+constexpr int tasq_threads(int C, int NSL) { return C == 4 ? (NSL == 2 ? 768 : 1024) : kDecodeThreads; }
 constexpr int kEncodeThreads = 256;
 constexpr int kEncodeTokens = 128;  // tokens per encode workgroup
 

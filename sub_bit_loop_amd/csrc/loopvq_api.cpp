@@ -115,11 +115,11 @@ DecodePlan plan_decode(const loopvq_geom* g, int B, int N, int step0, int n_step
       break;
     case DecodeKernel::kTasq:
       wgs = (long long)B * g->n_q_heads * p.n_blk_serv;
-      // several steps: at c = 4 one workgroup of 12 waves per CU (its eight
-      // codebook copies take 159 KB of LDS); at c = 8 two of 4 waves (three
-      // fit, and measured slower); one served step: 4 of 4 waves per CU (at
-      // most 128 VGPRs, 35 KB LDS)
-      target = n_steps == 1 ? 1024 : (g->G == 16 ? 256 : 512);
+      // c = 4: one workgroup per CU (its codebook copies fill most of the
+      // LDS: 12 waves for several steps, 16 for one); c = 8: several steps two
+      // workgroups of 4 waves per CU (three fit, and measured slower), one
+      // served step four (at most 128 VGPRs, 35 KB LDS)
+      target = g->G == 16 ? 256 : (n_steps == 1 ? 1024 : 512);
       break;
     default:
       wgs = (long long)B * g->n_q_heads * p.n_blk_serv;
