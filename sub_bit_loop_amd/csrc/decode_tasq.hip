@@ -21,7 +21,11 @@
 //
 // Positions: a workgroup iteration serves 4 consecutive tokens per wave (8
 // with one served step) at positions P + o, where P is the same for every
-// lane and o is fixed per lane.
+// lane and o is fixed per lane.  The waves run their iterations without
+// waiting for each other; the issue arbitration favours older waves, so every
+// 16 iterations a wave that has done fewer than the workgroup's average
+// raises its priority (s_setprio) until it catches up, and the waves finish
+// together (each token still goes to the same lane in the same order).
 // By the angle-sum identity
 //     e[d'](P + o) = A_o[d'] cos(P w_f) + B_o[d'] sin(P w_f),
 //     A_o = a cos(o w_f) + b sin(o w_f),   B_o = b cos(o w_f) - a sin(o w_f),
@@ -170,6 +174,7 @@ __global__ __launch_bounds__(tasq_threads(C, NSL), C == 4 ? 1 : (NSL == 1 ? 4 : 
   constexpr int kBufQ = kRedQ > kOffQ ? (kRedQ > kLaneQ ? kRedQ : kLaneQ) : (kOffQ > kLaneQ ? kOffQ : kLaneQ);
   __shared__ __attribute__((aligned(16))) float4 s_buf[kBufQ];
   __shared__ float s_amax[3][NW];
+  __shared__ int s_prog;   // blocks of kTFlush iterations done by the workgroup's waves
   // (cos, sin) of the iteration's position for every channel pair: entry
   // 8p + g holds pair p of lane group g, as (cos of both, sin of both) fp16
   __shared__ uint2 s_pair[NW][NPR * 8];
@@ -241,6 +246,7 @@ __global__ __launch_bounds__(tasq_threads(C, NSL), C == 4 ? 1 : (NSL == 1 ? 4 : 
     s_amax[1][wave] = mv;
     s_amax[2][wave] = mq;
   }
+  if (tid == 0) s_prog = 0;   // read only after the next barrier
   // offset angles o * w_f, w_f = theta^(-2f/D), in fp32
   {
     const float l2t = log2f(a.theta);
@@ -747,8 +753,18 @@ __global__ __launch_bounds__(tasq_threads(C, NSL), C == 4 ? 1 : (NSL == 1 ? 4 : 
     float sc[NSL];
     scores(cs2, sn2, Kw, sc);
     accumulate(sc, s16, Vw, valid);
-    // every kTFlush iterations (it is the same in every lane)
-    if ((it & (kTFlush - 1)) == kTFlush - 1) flush();
+    // every kTFlush iterations (it is the same in every lane): the flush, and
+    // the wave's priority from its progress against the workgroup's
+    if ((it & (kTFlush - 1)) == kTFlush - 1) {
+      flush();
+      int tot = 0;
+      if (lane == 0) tot = atomicAdd(&s_prog, 1) + 1;
+      tot = __builtin_amdgcn_readfirstlane(tot);
+      if (((it + 1) / kTFlush) * NW < tot)
+        __builtin_amdgcn_s_setprio(2);
+      else
+        __builtin_amdgcn_s_setprio(0);
+    }
   };
   // two iterations per trip, loading into alternate register sets, so that
   // nothing loaded ahead is copied from one set to the other
@@ -763,6 +779,7 @@ __global__ __launch_bounds__(tasq_threads(C, NSL), C == 4 ? 1 : (NSL == 1 ? 4 : 
       if (base + 2 * TPI >= n_tok) break;
     }
   }
+  __builtin_amdgcn_s_setprio(0);
   flush();
   if constexpr (kShared) {
     // the sums are already the wave's merge slot; its maximum is the rows'
