@@ -205,14 +205,20 @@ def onchip_ceilings(torch):
         t = run(0, mode, blocks, iters)
         out["lds_mode%d" % mode] = {"pattern": name,
                                     "B_per_clk_per_CU": blocks * 256 * iters * 16 * width / t / n_cu / clk}
-    valu = {0: ("v_pk_fma_f16", 4), 1: ("v_dot2_f32_f16", 4), 2: ("v_fma_f32", 2)}
+    valu = {0: ("v_pk_fma_f16", 4), 1: ("v_dot2_f32_f16", 4), 2: ("v_fma_f32", 2), 3: ("v_min3_f32", None),
+            4: ("v_med3_f32", None), 5: ("v_perm_b32", None), 6: ("v_mov_b32_dpp (row shuffle)", None),
+            7: ("v_exp_f32", None), 8: ("v_add_f32", 1)}
     blocks = 8 * n_cu
     for mode, (name, flop) in valu.items():
-        iters = 8192
+        iters = 8192 if mode < 3 else 4096
         t = run(1, mode, blocks, iters)
         ops = blocks * 256 * iters * 16
-        out["valu_mode%d" % mode] = {"instruction": name, "lane_ops_per_clk_per_CU": ops / t / n_cu / clk,
-                                     "TFLOPs": ops * flop / t / 1e12}
+        e = {"instruction": name, "lane_ops_per_clk_per_CU": ops / t / n_cu / clk,
+             # wave instructions issued per SIMD, at the assumed clock
+             "clk_per_wave_instruction_per_SIMD": t * clk / (ops / 64 / (n_cu * 4))}
+        if flop:
+            e["TFLOPs"] = ops * flop / t / 1e12
+        out["valu_mode%d" % mode] = e
     mfma = {0: ("v_mfma_f32_16x16x32_bf16", 16384), 1: ("v_mfma_f32_32x32x16_bf16", 32768),
             2: ("v_mfma_f32_32x32x8_bf16", 16384)}
     for mode, (name, flop) in mfma.items():

@@ -112,6 +112,10 @@ __global__ __launch_bounds__(256) void calib_lds_kernel(uint32_t* __restrict__ s
 //   mode 0: v_pk_fma_f16 (two fp16 FMAs per lane per instruction);
 //   mode 1: v_dot2_f32_f16 (two fp16 products summed into fp32);
 //   mode 2: v_fma_f32.
+//   modes 3-8 (instruction issue rates of the selection and softmax steps;
+//   each instruction written out so the compiler cannot substitute another):
+//   v_min3_f32, v_med3_f32, v_perm_b32, v_mov_b32 with a DPP row shuffle,
+//   v_exp_f32, v_add_f32.
 template <int MODE>
 __global__ __launch_bounds__(256) void calib_valu_kernel(uint32_t* __restrict__ sink, int iters) {
   typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
@@ -137,7 +141,7 @@ __global__ __launch_bounds__(256) void calib_valu_kernel(uint32_t* __restrict__ 
       for (int j = 0; j < 16; ++j) acc[j] = __builtin_amdgcn_fdot2(a, b, acc[j], false);
 #pragma unroll
     for (int j = 0; j < 16; ++j) res ^= __float_as_uint(acc[j]);
-  } else {
+  } else if constexpr (MODE == 2) {
     float acc[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) acc[j] = f * j;
@@ -146,6 +150,29 @@ __global__ __launch_bounds__(256) void calib_valu_kernel(uint32_t* __restrict__ 
       for (int j = 0; j < 16; ++j) acc[j] = fmaf(acc[j], 0.5f, f);
 #pragma unroll
     for (int j = 0; j < 16; ++j) res ^= __float_as_uint(acc[j]);
+  } else {
+    uint32_t acc[16];
+    const uint32_t b = __float_as_uint(f), c = __float_as_uint(0.5f * f);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[j] = __float_as_uint(f * (float)(j + 1));
+    for (int it = 0; it < iters; ++it)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        if constexpr (MODE == 3)
+          asm volatile("v_min3_f32 %0, %0, %1, %2" : "+v"(acc[j]) : "v"(b), "v"(c));
+        else if constexpr (MODE == 4)
+          asm volatile("v_med3_f32 %0, %0, %1, %2" : "+v"(acc[j]) : "v"(b), "v"(c));
+        else if constexpr (MODE == 5)
+          asm volatile("v_perm_b32 %0, %0, %1, %2" : "+v"(acc[j]) : "v"(b), "v"(c));
+        else if constexpr (MODE == 6)
+          asm volatile("v_mov_b32_dpp %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf" : "+v"(acc[j]));
+        else if constexpr (MODE == 7)
+          asm volatile("v_exp_f32 %0, %0" : "+v"(acc[j]));
+        else
+          asm volatile("v_add_f32 %0, %0, %1" : "+v"(acc[j]) : "v"(b));
+      }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) res ^= acc[j];
   }
   sink[(uint64_t)blockIdx.x * 256 + threadIdx.x] = res;
 }
@@ -239,8 +266,8 @@ int loopvq_calib_read(const void* src, uint64_t bytes, uint32_t* sink, void* str
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
-// On-chip ceiling kernels.  kind: 0 LDS (mode 0-4), 1 vector unit (mode 0-2),
-// 2 matrix cores (mode 0-1).  blocks workgroups of 256 threads, iters loop
+// On-chip ceiling kernels.  kind: 0 LDS (mode 0-7), 1 vector unit (mode 0-8),
+// 2 matrix cores (mode 0-2).  blocks workgroups of 256 threads, iters loop
 // iterations of 16 (LDS, vector) or 4 (matrix) operations per lane or wave;
 // sink holds blocks * 256 words.  Returns 0, -1 for bad arguments, -3 for a
 // launch error.
@@ -265,6 +292,12 @@ int loopvq_calib_onchip(int kind, int mode, int blocks, int iters, uint32_t* sin
       case 0: hipLaunchKernelGGL(calib_valu_kernel<0>, g, t, 0, st, sink, iters); break;
       case 1: hipLaunchKernelGGL(calib_valu_kernel<1>, g, t, 0, st, sink, iters); break;
       case 2: hipLaunchKernelGGL(calib_valu_kernel<2>, g, t, 0, st, sink, iters); break;
+      case 3: hipLaunchKernelGGL(calib_valu_kernel<3>, g, t, 0, st, sink, iters); break;
+      case 4: hipLaunchKernelGGL(calib_valu_kernel<4>, g, t, 0, st, sink, iters); break;
+      case 5: hipLaunchKernelGGL(calib_valu_kernel<5>, g, t, 0, st, sink, iters); break;
+      case 6: hipLaunchKernelGGL(calib_valu_kernel<6>, g, t, 0, st, sink, iters); break;
+      case 7: hipLaunchKernelGGL(calib_valu_kernel<7>, g, t, 0, st, sink, iters); break;
+      case 8: hipLaunchKernelGGL(calib_valu_kernel<8>, g, t, 0, st, sink, iters); break;
       default: return -1;
     }
   } else if (kind == 2) {

@@ -842,6 +842,9 @@ __global__ __launch_bounds__(tasq_threads(C, NSL), C == 4 ? 1 : (NSL == 1 ? 4 : 
   }
   __syncthreads();
   const float osc = ldexpf(1.f, shv);
+  // one split (out set): the rows go straight to out / lse, since the merge
+  // of a single partial returns it unchanged
+  const bool direct = a.out != nullptr;
   for (int x = tid; x < TC * D; x += NTH) {
     const int m = x / D, d = x - m * D;
     const int t = beta * TC + m;
@@ -859,9 +862,17 @@ __global__ __launch_bounds__(tasq_threads(C, NSL), C == 4 ? 1 : (NSL == 1 ? 4 : 
         den += f * s_red[w][m][D + 1];
       }
     }
-    float* dst = a.ws + ((((int64_t)b * a.Hq + hq) * a.n_steps + (t - a.step0)) * a.n_split + split) * (D + 1);
-    dst[d] = den > 0.f ? num / den * osc : 0.f;
-    if (d == 0) dst[D] = den > 0.f ? (mm + __log2f(den)) * 0.69314718055994531f : -INFINITY;
+    const int64_t row = ((int64_t)b * a.Hq + hq) * a.n_steps + (t - a.step0);
+    const float o = den > 0.f ? num / den * osc : 0.f;
+    const float l = den > 0.f ? (mm + __log2f(den)) * 0.69314718055994531f : -INFINITY;
+    if (direct) {
+      a.out[row * D + d] = o;
+      if (d == 0 && a.lse) a.lse[row] = l;
+    } else {
+      float* dst = a.ws + (row * a.n_split + split) * (D + 1);
+      dst[d] = o;
+      if (d == 0) dst[D] = l;
+    }
   }
 }
 

@@ -546,6 +546,10 @@ static loopvq_status decode_attn_impl(const loopvq_geom* g, const void* q, int32
   a.qscale = (float)(1.4426950408889634 / std::sqrt((double)g->D));
   a.theta = g->rope_theta;
   a.n_pos = n_pos;
+  if (p.kernel == DecodeKernel::kTasq && p.n_split == 1) {
+    a.out = out;
+    a.lse = lse;
+  }
   // Blocks of four steps (0.5 and 0.25 bit, with or without the key
   // pre-transform): the specialised kernels chosen by the plan; every other
   // geometry: the generic one.
@@ -563,6 +567,8 @@ static loopvq_status decode_attn_impl(const loopvq_geom* g, const void* q, int32
   else
     e = loopvq::launch_decode_fast(g->G, a, s);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
+  // one split of the pre-transform kernel: the kernel wrote out / lse
+  if (p.kernel == DecodeKernel::kTasq && p.n_split == 1) return LOOPVQ_OK;
   loopvq::MergeArgs ma{};
   ma.ws = a.ws;
   ma.out = out;

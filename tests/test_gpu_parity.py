@@ -164,6 +164,8 @@ GEOMS = [
     ("pretransform-quarter-bit", 32, 4, 4, 2, 2, 1, 600, 4, 256, True),
     ("pretransform-2blk-gqa2", 16, 4, 8, 1, 2, 2, 500, 4, 256, True),
     ("pretransform-k200-nosink", 16, 4, 4, 1, 1, 2, 333, 0, 200, True),
+    # one context split: the pre-transform kernel writes out / lse itself
+    ("pretransform-one-split", 16, 4, 4, 2, 2, 2, 200, 4, 256, True),
     ("tc2-k200-nosink", 16, 2, 4, 1, 1, 1, 300, 0, 200, False),
     ("tc1-channel-vq", 16, 1, 2, 1, 2, 1, 129, 3, 64, False),
     ("tc8", 32, 8, 8, 1, 1, 1, 200, 2, 256, False),
