@@ -51,7 +51,7 @@
 //     half of one (c = 8).
 //   * Effective queries, scores and P*V run on packed fp16 (scores summed in
 //     fp32 by v_dot2_f32_f16); P*V partials are flushed into fp32 every
-//     kTFlush tokens, with the same kind of range bounds as the plain kernels.
+//     kTFlush(NSL) tokens, with the same kind of range bounds as the plain kernels.
 //   * Online softmax (all steps, NSL = 2): the four tokens of a wave
 //     iteration share one running maximum per step, raised in a branch the
 //     whole wave takes, so their fp16 partials add up across the four rows
@@ -107,10 +107,14 @@ __device__ __forceinline__ uint32_t pack_h2t(float a, float b) {
   return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
 }
 
-// P*V partial range: at most kTFlush tokens per fp16 partial, weights below
-// 2^kTLag, values below 2^kTVLim (one less where four rows' partials are
-// added before a flush), so a partial stays below 2^14 (2^15 for four rows).
-constexpr int kTFlush = 16, kTLag = 3, kTVLim = 7;
+// P*V partial range: weights below 2^kTLag; a lane's fp16 partial sums at
+// most kTFlush(NSL) tokens before it is flushed into fp32, with values below
+// 2^kTVLim(NSL), so a partial stays below 2^14, and below 2^15 where four
+// rows' partials are added before a flush (NSL = 2: 32 tokens, values below
+// 2^5; NSL = 1: 16 tokens, values below 2^7).
+constexpr int kTLag = 3;
+constexpr int kTFlush(int nsl) { return nsl == 2 ? 32 : 16; }
+constexpr int kTVLim(int nsl) { return nsl == 2 ? 5 : 7; }
 // Fourth word of a raw buffer descriptor (32-bit data, no format conversion).
 constexpr int kBufWord3 = 0x00020000;
 
@@ -141,6 +145,7 @@ __global__ __launch_bounds__(tasq_threads(C, NSL), C == 4 ? 1 : (NSL == 1 ? 4 : 
   // 16) (+ 128 for V), is again one byte permute.
   // Otherwise (c = 8) one copy of each codebook, codeword r at 32 QW r, and
   // workgroups of 4 waves.
+  constexpr int kFl = kTFlush(NSL);
   constexpr bool kRep = C == 4 && NSL == 2;
   constexpr bool kSlice = C == 4 && NSL == 1;
   constexpr int NTH = tasq_threads(C, NSL);
@@ -174,7 +179,7 @@ __global__ __launch_bounds__(tasq_threads(C, NSL), C == 4 ? 1 : (NSL == 1 ? 4 : 
   constexpr int kBufQ = kRedQ > kOffQ ? (kRedQ > kLaneQ ? kRedQ : kLaneQ) : (kOffQ > kLaneQ ? kOffQ : kLaneQ);
   __shared__ __attribute__((aligned(16))) float4 s_buf[kBufQ];
   __shared__ float s_amax[3][NW];
-  __shared__ int s_prog;   // blocks of kTFlush iterations done by the workgroup's waves
+  __shared__ int s_prog;   // blocks of kTFlush(NSL) iterations done by the workgroup's waves
   // (cos, sin) of the iteration's position for every channel pair: entry
   // 8p + g holds pair p of lane group g, as (cos of both, sin of both) fp16
   __shared__ uint2 s_pair[NW][NPR * 8];
@@ -268,7 +273,7 @@ __global__ __launch_bounds__(tasq_threads(C, NSL), C == 4 ? 1 : (NSL == 1 ? 4 : 
     mv = fmaxf(mv, s_amax[1][w]);
     mq = fmaxf(mq, s_amax[2][w]);
   }
-  const int shk = pow2_range_shift(mk, 14), shv = pow2_range_shift(mv, kShared ? kTVLim - 1 : kTVLim), shq = pow2_range_shift(mq, 14);
+  const int shk = pow2_range_shift(mk, 14), shv = pow2_range_shift(mv, kTVLim(NSL)), shq = pow2_range_shift(mq, 14);
   {
     const float sk = ldexpf(1.f, -shk), sv = ldexpf(1.f, -shv);
     uint32_t kw[2 * C], vw[2 * C];   // [m][pair]
@@ -753,14 +758,14 @@ __global__ __launch_bounds__(tasq_threads(C, NSL), C == 4 ? 1 : (NSL == 1 ? 4 : 
     float sc[NSL];
     scores(cs2, sn2, Kw, sc);
     accumulate(sc, s16, Vw, valid);
-    // every kTFlush iterations (it is the same in every lane): the flush, and
+    // every kFl iterations (it is the same in every lane): the flush, and
     // the wave's priority from its progress against the workgroup's
-    if ((it & (kTFlush - 1)) == kTFlush - 1) {
+    if ((it & (kFl - 1)) == kFl - 1) {
       flush();
       int tot = 0;
       if (lane == 0) tot = atomicAdd(&s_prog, 1) + 1;
       tot = __builtin_amdgcn_readfirstlane(tot);
-      if (((it + 1) / kTFlush) * NW < tot)
+      if (((it + 1) / kFl) * NW < tot)
         __builtin_amdgcn_s_setprio(2);
       else
         __builtin_amdgcn_s_setprio(0);
