@@ -299,7 +299,7 @@ def workload5(args, torch, lv, cfg):
     heads = (0, 1)
     n_enc = min(cfg.N, args.cpu_tokens)
     keep = {}
-    layers, enc_k, enc_v, gen_s = [], [], [], 0.0
+    layers, enc_k, enc_v, enc_k1, enc_v1, gen_s = [], [], [], [], [], 0.0
     for layer in range(L):
         t = time.time()
         inp = build_inputs(cfg, layer, "cuda")
@@ -312,15 +312,20 @@ def workload5(args, torch, lv, cfg):
                    vidx=torch.zeros(shp, dtype=torch.uint8, device="cuda"),
                    sigma=torch.zeros((B, N_cap, cfg.T), dtype=torch.float16, device="cuda"))
         lay["pt"] = lv.pretransform(lay["w"], lay["perm"], lay["sigma"])
-        e0, e1, e2 = ev(), ev(), ev()
-        e0.record()
-        lv.encode(g, inp["k"], lay["k_cb"], lay["kidx"], pt=lay["pt"])
-        e1.record()
-        lv.encode(g, inp["v"], lay["v_cb"], lay["vidx"])
-        e2.record()
-        torch.cuda.synchronize()
-        enc_k.append(e0.elapsed_time(e1))
-        enc_v.append(e1.elapsed_time(e2))
+        # The layer's prefill encode runs twice with the same inputs (the
+        # second writes the same indices and sigma): the first launch after the
+        # input generation runs 10-14% slower than any later one, so the kernel
+        # time is the second call's; the first call's is reported beside it.
+        for rep in range(2):
+            e0, e1, e2 = ev(), ev(), ev()
+            e0.record()
+            lv.encode(g, inp["k"], lay["k_cb"], lay["kidx"], pt=lay["pt"])
+            e1.record()
+            lv.encode(g, inp["v"], lay["v_cb"], lay["vidx"])
+            e2.record()
+            torch.cuda.synchronize()
+            (enc_k1 if rep == 0 else enc_k).append(e0.elapsed_time(e1))
+            (enc_v1 if rep == 0 else enc_v).append(e1.elapsed_time(e2))
         # the page source: the layer's last 8 tokens (their content does not change the timing)
         lay["page_k"] = inp["k"][:, :, :, -cfg.page:].clone()
         lay["page_v"] = inp["v"][:, :, :, -cfg.page:].clone()
@@ -332,8 +337,8 @@ def workload5(args, torch, lv, cfg):
         del inp
         torch.cuda.empty_cache()
         layers.append(lay)
-        print("layer %d encoded (K %.2f ms, V %.2f ms); generation so far %.0f s"
-              % (layer, enc_k[-1], enc_v[-1], gen_s), file=sys.stderr, flush=True)
+        print("layer %d encoded (K %.2f ms, V %.2f ms; first call %.2f, %.2f); generation so far %.0f s"
+              % (layer, enc_k[-1], enc_v[-1], enc_k1[-1], enc_v1[-1], gen_s), file=sys.stderr, flush=True)
 
     ws = torch.empty(max(4, lv.decode_workspace_bytes(g, B, N_cap, 0, cfg.T)), dtype=torch.uint8, device="cuda")
     out = torch.empty((B, Hq, cfg.T, cfg.D), dtype=torch.float32, device="cuda")
@@ -443,6 +448,8 @@ def workload5(args, torch, lv, cfg):
                                "for sigma, 2 B of sigma per (token, step)",
                 "launch_ms_median": enc_med, "keys_ms_median": statistics.median(enc_k),
                 "values_ms_median": statistics.median(enc_v),
+                "timing": "second call of each layer's prefill encode (same inputs); median over the layers",
+                "first_call_ms_median": statistics.median([a + b for a, b in zip(enc_k1, enc_v1)]),
                 "codes_per_s": codes_layer / (enc_med * 1e-3),
                 "mfma_tflops": enc_tf, "mfma_frac_of_bf16_peak": enc_tf / BF16_MFMA_PEAK_TFLOPS}
     res = {
@@ -470,7 +477,12 @@ def workload5(args, torch, lv, cfg):
                    "units_per_s": units_mean / (dec_med * 1e-3), "index_GBps": dec_gbs,
                    "hbm_frac_index_bytes": dec_gbs / HBM_PEAK_GBS},
         "prefill_encode": {"ms_per_layer_median": enc_med, "codes_per_s": codes_layer / (enc_med * 1e-3),
-                           "codes_per_layer": codes_layer},
+                           "codes_per_layer": codes_layer,
+                           "keys_with_sigma_ms_median": statistics.median(enc_k),
+                           "values_ms_median": statistics.median(enc_v),
+                           "first_call_ms_per_layer_median": statistics.median([a + b for a, b in zip(enc_k1, enc_v1)]),
+                           "note": "the second of two identical calls per layer; the first launch after the input "
+                                   "generation is reported as first_call"},
         "page_encode": {"events": len(page_ev),
                         "ms_per_event_all_layers_median": statistics.median(page_ms) if page_ms else None},
         "decode_per_step": {"ms_all_steps_median": ps_ms, "calls": cfg.T, "fused_ms_median_same_context": fused_ms,
