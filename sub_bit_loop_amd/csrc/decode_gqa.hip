@@ -524,9 +524,19 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
         den += f * s_red[w][rw][D + 1];
       }
     }
-    float* dst = a.ws + ((((int64_t)b * a.Hq + hq0 + hh) * a.n_steps + (t - a.step0)) * a.n_split + split) * (D + 1);
-    dst[d] = den > 0.f ? num / den * osc : 0.f;
-    if (d == 0) dst[D] = den > 0.f ? (mm + __log2f(den)) * 0.69314718055994531f : -INFINITY;
+    const int64_t row = ((int64_t)b * a.Hq + hq0 + hh) * a.n_steps + (t - a.step0);
+    const float o = den > 0.f ? num / den * osc : 0.f;
+    const float l = den > 0.f ? (mm + __log2f(den)) * 0.69314718055994531f : -INFINITY;
+    if (a.out) {
+      // one split: the rows go straight to out / lse (the merge of a single
+      // partial returns it unchanged)
+      a.out[row * D + d] = o;
+      if (d == 0 && a.lse) a.lse[row] = l;
+    } else {
+      float* dst = a.ws + (row * a.n_split + split) * (D + 1);
+      dst[d] = o;
+      if (d == 0) dst[D] = l;
+    }
   }
 }
 

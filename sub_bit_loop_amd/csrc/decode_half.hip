@@ -426,9 +426,19 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_half_kernel(DecodeArgs 
       num = f0 * s_red[w0][ml][d] + f1 * s_red[w0 + 1][ml][d];
       den = f0 * s_red[w0][ml][D + 1] + f1 * s_red[w0 + 1][ml][D + 1];
     }
-    float* dst = a.ws + ((((int64_t)b * a.Hq + hq) * a.n_steps + (t - a.step0)) * a.n_split + split) * (D + 1);
-    dst[d] = den > 0.f ? num / den * osc : 0.f;
-    if (d == 0) dst[D] = den > 0.f ? (mm + __log2f(den)) * 0.69314718055994531f : -INFINITY;
+    const int64_t row = ((int64_t)b * a.Hq + hq) * a.n_steps + (t - a.step0);
+    const float o = den > 0.f ? num / den * osc : 0.f;
+    const float l = den > 0.f ? (mm + __log2f(den)) * 0.69314718055994531f : -INFINITY;
+    if (a.out) {
+      // one split: the rows go straight to out / lse (the merge of a single
+      // partial returns it unchanged)
+      a.out[row * D + d] = o;
+      if (d == 0 && a.lse) a.lse[row] = l;
+    } else {
+      float* dst = a.ws + (row * a.n_split + split) * (D + 1);
+      dst[d] = o;
+      if (d == 0) dst[D] = l;
+    }
   }
 }
 

@@ -48,12 +48,12 @@ struct DecodeArgs {
   float qscale;               // log2(e) / sqrt(D)
   float theta;                // RoPE base the table was made with
   int32_t n_pos;              // positions in the RoPE table
-  // One context split (pre-transform kernel): with out set, a workgroup
-  // writes its rows of out / lse itself and no merge kernel runs (the merge
-  // of a single partial returns it unchanged).  Several splits always go
-  // through merge_kernel: a merge inside the kernel needs device-scope fences
-  // (an L2 write-back and invalidate per workgroup), which cost more than the
-  // merge launch.
+  // One context split (pre-transform, GQA and c = 4 multi-step kernels):
+  // with out set, a workgroup writes its rows of out / lse itself and no
+  // merge kernel runs (the merge of a single partial returns it unchanged).
+  // Several splits always go through merge_kernel: a merge inside the kernel
+  // needs device-scope fences (an L2 write-back and invalidate per
+  // workgroup), which cost more than the merge launch.
   float* out;                 // fp32 [B][Hq][n_steps][D] or null (partials)
   float* lse;                 // fp32 [B][Hq][n_steps] or null
 };

@@ -546,7 +546,11 @@ static loopvq_status decode_attn_impl(const loopvq_geom* g, const void* q, int32
   a.qscale = (float)(1.4426950408889634 / std::sqrt((double)g->D));
   a.theta = g->rope_theta;
   a.n_pos = n_pos;
-  if (p.kernel == DecodeKernel::kTasq && p.n_split == 1) {
+  // One context split: the pre-transform, GQA and c = 4 multi-step kernels
+  // write out / lse themselves and no merge kernel runs.
+  const bool direct = p.n_split == 1 && (p.kernel == DecodeKernel::kTasq || p.kernel == DecodeKernel::kGqa ||
+                                         (p.kernel == DecodeKernel::kFast && g->G == 16));
+  if (direct) {
     a.out = out;
     a.lse = lse;
   }
@@ -567,8 +571,7 @@ static loopvq_status decode_attn_impl(const loopvq_geom* g, const void* q, int32
   else
     e = loopvq::launch_decode_fast(g->G, a, s);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
-  // one split of the pre-transform kernel: the kernel wrote out / lse
-  if (p.kernel == DecodeKernel::kTasq && p.n_split == 1) return LOOPVQ_OK;
+  if (direct) return LOOPVQ_OK;   // the kernel wrote out / lse
   loopvq::MergeArgs ma{};
   ma.ws = a.ws;
   ma.out = out;
